@@ -1,0 +1,771 @@
+// Host side of the C-ABI library: validation, the sidecar onto the card
+// (repacked into the kernels' tile layouts), the context store and its
+// position rule, and the launch sequences of the settle and block passes.
+//
+// Definitions followed (docs.rs page "cortiq_engine/dflash.rs",
+// cortiq-engine 0.8.78): `Geometry::of` (what a geometry must satisfy),
+// `queue_context` / `truncate` (the position rule), `settle_rows` (the
+// context rows, 256 at a time as the CUDA block takes them), `block_dev`
+// (each layer's context range), `Drafter::block`, `select_with`.
+#include "dflash.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <functional>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+constexpr int kSettleRows = 256;     // rows one settle pass takes
+constexpr int kTargetBlocks = 768;   // workgroups a GEMM launch aims for (256 CUs)
+constexpr int kMaxChunks = 64;       // context chunks per kv head in the attention
+constexpr int kF16R = 2;             // row tiles per wave of the f16 GEMM
+constexpr int kI4R = 1;              // row tiles per wave of the int4 GEMM
+
+thread_local std::string g_create_error;
+
+struct Split {
+  int S, per;
+};
+
+// K splits for a GEMM of `ntiles` row tiles with R tiles per wave, `steps`
+// K steps (32 columns for f16, 128 for int4) and `mblocks` 16-row blocks.
+Split split_for(int ntiles, int R, int steps, int mblocks) {
+  const long groups = (ntiles + 4L * R - 1) / (4L * R);
+  const long have = groups * mblocks;
+  long S = (kTargetBlocks + have - 1) / have;
+  S = std::max(1L, std::min<long>(S, steps));
+  const int per = (int)((steps + S - 1) / S);
+  return {(int)((steps + per - 1) / per), per};
+}
+
+void parallel_for(long n, const std::function<void(long)>& f) {
+  unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  if (n < 64) nt = 1;
+  std::vector<std::thread> th;
+  for (unsigned t = 0; t < nt; ++t)
+    th.emplace_back([&, t] {
+      for (long i = t; i < n; i += nt) f(i);
+    });
+  for (auto& x : th) x.join();
+}
+
+// Dense f16 [N][K] → F16T with rows padded to a multiple of 16 (zeros).
+std::vector<uint16_t> repack_f16(const uint16_t* src, int N, int K) {
+  const int KS = K / 32, NT = (N + 15) / 16;
+  std::vector<uint16_t> dst((size_t)NT * 16 * K);
+  parallel_for(NT, [&](long t) {
+    for (int s = 0; s < KS; ++s)
+      for (int l = 0; l < 64; ++l) {
+        const int j = l >> 4, n = l & 15;
+        const long row = 16 * t + n;
+        uint16_t* d = dst.data() + (((size_t)t * KS + s) * 64 + l) * 8;
+        if (row < N)
+          std::memcpy(d, src + (size_t)row * K + 32 * s + 8 * j, 16);
+        else
+          std::memset(d, 0, 16);
+      }
+  });
+  return dst;
+}
+
+// int4 [N][K] → I4T tiles written at tile offset `t_off` of codes/scales.
+void repack_i4(const dflash_i4& m, int N, int K, uint8_t* codes, uint16_t* scales, long t_off) {
+  const int KT = K / 128, NT = N / 16;
+  parallel_for(NT, [&](long t) {
+    const long tt = t + t_off;
+    for (int p = 0; p < KT; ++p)
+      for (int l = 0; l < 64; ++l) {
+        const int j = l >> 4, n = l & 15;
+        const long row = 16 * t + n;
+        const uint8_t* qr = m.q + (size_t)row * (K / 2);
+        for (int u = 0; u < 4; ++u) {
+          uint32_t word = 0;
+          for (int e = 0; e < 8; ++e) {
+            const int k = 128 * p + 32 * u + 8 * j + e;
+            const uint32_t nib = (k & 1) ? (qr[k / 2] >> 4) : (qr[k / 2] & 15);
+            const int pos = (e & 1) ? 16 + 2 * (e - 1) : 2 * e;
+            word |= (nib ^ 8u) << pos;
+          }
+          std::memcpy(codes + (((size_t)tt * KT + p) * 64 + l) * 16 + 4 * u, &word, 4);
+          if (j == 0) scales[(((size_t)tt * KT + p) * 16 + n) * 4 + u] = m.scale[(size_t)row * (K / 32) + 4 * p + u];
+        }
+      }
+  });
+}
+
+}  // namespace
+
+struct I4Set {  // one int4 product of every layer, tiles [layer][tiles][K/128]
+  uint8_t* codes = nullptr;
+  uint16_t* scales = nullptr;
+  int tiles = 0, K = 0;
+  long layer_tiles() const { return tiles; }
+};
+
+struct dflash {
+  // geometry
+  int hs, ffn, L, nh, kv, hd, V, B, mask, gs, kn, rank, top, ntaps, tw, qd, kd, G, P;
+  std::vector<int> windows, rot;
+  double theta;
+  float eps;
+  long cap;
+  hipStream_t st;
+  // weights
+  uint16_t *fc = nullptr, *sel = nullptr, *pbook = nullptr, *cbook = nullptr, *embed = nullptr,
+           *head = nullptr, *attn_kproj = nullptr, *mlp_kproj = nullptr;
+  float *hidden_norm = nullptr, *norm = nullptr, *in_norm = nullptr, *post_norm = nullptr,
+        *q_norm = nullptr, *k_norm = nullptr, *attn_base = nullptr, *mlp_base = nullptr,
+        *inv = nullptr;
+  int* rot_dev = nullptr;
+  I4Set qkv, o, gu, down;
+  int ptiles;  // kernel-projection row tiles
+  // context store
+  float *sk = nullptr, *sv = nullptr;
+  long first = 0, len = 0;
+  // block scratch
+  float *h = nullptr, *x = nullptr, *dsum_a = nullptr, *dsum_m = nullptr, *kb = nullptr,
+        *vb = nullptr, *pacc = nullptr, *pml = nullptr, *part = nullptr, *logits = nullptr,
+        *hp = nullptr, *cv = nullptr;
+  int* ci = nullptr;
+  uint16_t *xa = nullptr, *xca = nullptr, *qa = nullptr, *ya = nullptr, *ma = nullptr;
+  // settle scratch
+  uint16_t *taps_a = nullptr, *t_a = nullptr;
+  long part_floats = 0;
+  int stage_cols = 0;  // widest activation the staging buffer holds
+  int last_k = 0;
+  std::vector<void*> allocs;
+  std::string err;
+};
+
+namespace {
+
+int fail(dflash* d, int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (d)
+    d->err = buf;
+  else
+    g_create_error = buf;
+  return code;
+}
+
+int hip_check(dflash* d, hipError_t e, const char* what) {
+  if (e == hipSuccess) return DFLASH_OK;
+  return fail(d, e == hipErrorOutOfMemory ? DFLASH_ENOMEM : DFLASH_EHIP, "%s: %s", what,
+              hipGetErrorString(e));
+}
+
+template <class T>
+int dev_alloc(dflash* d, T** p, size_t count, const char* what) {
+  void* q = nullptr;
+  const hipError_t e = hipMalloc(&q, std::max<size_t>(count * sizeof(T), 16));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(nullptr, DFLASH_ENOMEM, "device memory for %s (%zu bytes): %s", what,
+                count * sizeof(T), hipGetErrorString(e));
+  }
+  d->allocs.push_back(q);
+  *p = static_cast<T*>(q);
+  return hipMemset(q, 0, std::max<size_t>(count * sizeof(T), 16)) == hipSuccess
+             ? DFLASH_OK
+             : fail(nullptr, DFLASH_EHIP, "clearing %s", what);
+}
+
+template <class T>
+int upload(dflash* d, T** p, const T* src, size_t count, const char* what) {
+  int rc = dev_alloc(d, p, count, what);
+  if (rc) return rc;
+  if (hipMemcpy(*p, src, count * sizeof(T), hipMemcpyHostToDevice) != hipSuccess)
+    return fail(nullptr, DFLASH_EHIP, "copying %s to the device", what);
+  return DFLASH_OK;
+}
+
+int launch_check(dflash* d, const char* what) {
+  return hip_check(d, hipGetLastError(), what);
+}
+
+const char* validate(const dflash_geometry* g, const dflash_weights* w) {
+  if (!g || !w) return "null geometry or weights";
+  if (g->layers <= 0) return "layers must be > 0";
+  if (g->block < 2 || g->block > 16) return "block must be in [2, 16]";
+  if (g->n_taps <= 0) return "n_taps must be > 0";
+  if (g->kv_heads <= 0 || g->heads <= 0 || g->heads % g->kv_heads) return "heads % kv_heads";
+  if (g->head_dim != 64 && g->head_dim != 128 && g->head_dim != 256)
+    return "head_dim must be 64, 128 or 256";
+  if (g->conv_group <= 0 || g->hidden % g->conv_group) return "hidden % conv_group";
+  if (g->conv_kernel < 1 || g->conv_kernel > g->block) return "conv_kernel must be in [1, block]";
+  if (g->hidden <= 0 || g->hidden % 128) return "hidden must be a multiple of 128";
+  if (g->intermediate <= 0 || g->intermediate % 128) return "intermediate must be a multiple of 128";
+  if ((g->heads * g->head_dim) % 128) return "heads*head_dim must be a multiple of 128";
+  if (2L * g->conv_kernel * (g->hidden / g->conv_group) > 16384)
+    return "2*conv_kernel*hidden/conv_group must be at most 16384";
+  if (g->selector_top < 1 || g->selector_top > 32 || g->selector_top > g->vocab)
+    return "selector_top must be in [1, min(32, vocab)]";
+  if (g->selector_rank < 1 || g->selector_rank > 256) return "selector_rank must be in [1, 256]";
+  if (g->mask_token < 0 || g->mask_token >= g->vocab) return "mask_token outside the vocabulary";
+  if (g->max_context < 1) return "max_context must be >= 1";
+  if (!g->windows || !g->rotary) return "null windows or rotary";
+  for (int l = 0; l < g->layers; ++l)
+    if (g->windows[l] < 0) return "negative window";
+  if (!w->fc || !w->hidden_norm || !w->norm || !w->sel_proj || !w->pred_book || !w->succ_book ||
+      !w->embed || !w->head || !w->layer)
+    return "null weight pointer";
+  for (int l = 0; l < g->layers; ++l) {
+    const dflash_layer_w& x = w->layer[l];
+    if (!x.in_norm || !x.post_norm || !x.q_norm || !x.k_norm || !x.attn_base || !x.mlp_base ||
+        !x.attn_kproj || !x.mlp_kproj)
+      return "null layer weight pointer";
+    for (const dflash_i4* m : {&x.q, &x.k, &x.v, &x.o, &x.gate, &x.up, &x.down})
+      if (!m->q || !m->scale) return "null int4 matrix";
+  }
+  return nullptr;
+}
+
+int alloc_i4(dflash* d, I4Set& s, int tiles, int K, const char* what) {
+  s.tiles = tiles;
+  s.K = K;
+  const size_t n = (size_t)d->L * tiles * (K / 128);
+  int rc = dev_alloc(d, &s.codes, n * 64 * 16, what);
+  if (!rc) rc = dev_alloc(d, &s.scales, n * 16 * 4, what);
+  return rc;
+}
+
+int upload_i4(dflash* d, I4Set& s, int l, std::initializer_list<std::pair<const dflash_i4*, int>> parts) {
+  const int KT = s.K / 128;
+  std::vector<uint8_t> codes((size_t)s.tiles * KT * 64 * 16);
+  std::vector<uint16_t> scales((size_t)s.tiles * KT * 16 * 4);
+  long t_off = 0;
+  for (auto& pr : parts) {
+    repack_i4(*pr.first, pr.second, s.K, codes.data(), scales.data(), t_off);
+    t_off += pr.second / 16;
+  }
+  const size_t lc = codes.size(), ls = scales.size();
+  if (hipMemcpy(s.codes + (size_t)l * lc, codes.data(), lc, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(s.scales + (size_t)l * ls, scales.data(), ls * 2, hipMemcpyHostToDevice) != hipSuccess)
+    return fail(nullptr, DFLASH_EHIP, "copying int4 weights to the device");
+  return DFLASH_OK;
+}
+
+// Largest GEMM partial buffer (floats) any call can need.
+long partial_need(const dflash* d) {
+  long need = 0;
+  auto f16 = [&](int N, int K, int mb) {
+    const Split s = split_for((N + 15) / 16, kF16R, K / 32, mb);
+    need = std::max(need, (long)s.S * mb * 16 * N);
+  };
+  auto i4 = [&](int N, int K, int mb) {
+    const Split s = split_for(N / 16, kI4R, K / 128, mb);
+    need = std::max(need, (long)s.S * mb * 16 * N);
+  };
+  for (int mb = 1; mb <= kSettleRows / 16; ++mb) {
+    f16(d->hs, d->tw, mb);
+    f16(d->P, d->hs, mb);
+    f16(d->rank, d->hs, mb);
+    i4(d->L * 2 * d->kd, d->hs, mb);
+    i4(d->qd + 2 * d->kd, d->hs, mb);
+    i4(d->hs, d->qd, mb);
+    i4(2 * d->ffn, d->hs, mb);
+    i4(d->hs, d->ffn, mb);
+  }
+  return need;
+}
+
+int topk_slices(int width, int top, int* slice) {
+  int ns = (width + 4095) / 4096;
+  ns = std::min(ns, std::max(1, 4096 / top));
+  *slice = (width + ns - 1) / ns;
+  return ns;
+}
+
+void layer_range(const dflash* d, int l, long a, long* lo, long* n) {
+  // `block_dev`: base = first (the store keeps every settled row);
+  // hi = min(a, first+len), never below base; a window w > 0 starts the
+  // layer at a+1−w, clamped into [base, hi].
+  const long base = d->first;
+  long hi = std::min(a, d->first + d->len);
+  hi = std::max(hi, base);
+  long l0 = base;
+  const int w = d->windows[l];
+  if (w > 0) l0 = std::min(std::max(std::max(a + 1 - w, 0L), base), hi);
+  *lo = l0;
+  *n = hi - l0;
+}
+
+int attn_chunk(long n, int* nchunks) {
+  if (n <= 0) {
+    *nchunks = 0;
+    return 32;
+  }
+  long c = std::max(128L, (n + kMaxChunks - 1) / kMaxChunks);
+  c = (c + 31) / 32 * 32;
+  *nchunks = (int)((n + c - 1) / c);
+  return (int)c;
+}
+
+}  // namespace
+
+// ====================================================================== API
+
+extern "C" {
+
+const char* dflash_last_error(const dflash_t* d) {
+  return d ? d->err.c_str() : g_create_error.c_str();
+}
+
+void dflash_destroy(dflash_t* d) {
+  if (!d) return;
+  (void)hipStreamSynchronize(d->st);
+  for (void* p : d->allocs) (void)hipFree(p);
+  delete d;
+}
+
+int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* stream,
+                  dflash_t** out) {
+  if (!out) return fail(nullptr, DFLASH_EINVAL, "null output handle");
+  *out = nullptr;
+  g_create_error.clear();
+  if (const char* why = validate(g, w)) return fail(nullptr, DFLASH_EINVAL, "geometry: %s", why);
+  dflash* d = new dflash();
+  d->hs = g->hidden;
+  d->ffn = g->intermediate;
+  d->L = g->layers;
+  d->nh = g->heads;
+  d->kv = g->kv_heads;
+  d->hd = g->head_dim;
+  d->V = g->vocab;
+  d->B = g->block;
+  d->mask = g->mask_token;
+  d->gs = g->conv_group;
+  d->kn = g->conv_kernel;
+  d->rank = g->selector_rank;
+  d->top = g->selector_top;
+  d->ntaps = g->n_taps;
+  d->tw = g->n_taps * g->hidden;
+  d->qd = d->nh * d->hd;
+  d->kd = d->kv * d->hd;
+  d->G = d->hs / d->gs;
+  d->P = 2 * d->kn * d->G;
+  d->theta = g->rope_theta;
+  d->eps = (float)g->eps;
+  d->cap = g->max_context;
+  d->st = static_cast<hipStream_t>(stream);
+  d->windows.assign(g->windows, g->windows + d->L);
+  for (int l = 0; l < d->L; ++l) d->rot.push_back(g->rotary[l] ? 1 : 0);
+  d->ptiles = (d->P + 15) / 16;
+
+  auto done = [&](int rc) {
+    if (rc) {
+      if (g_create_error.empty()) g_create_error = "create failed";
+      dflash_destroy(d);
+      return rc;
+    }
+    *out = d;
+    return DFLASH_OK;
+  };
+  int rc = DFLASH_OK;
+  const int hs = d->hs, L = d->L;
+  // ---- dense f16 matrices, repacked
+  {
+    auto fc = repack_f16(w->fc, hs, d->tw);
+    rc = upload(d, &d->fc, fc.data(), fc.size(), "fc");
+  }
+  if (!rc) {
+    auto s = repack_f16(w->sel_proj, d->rank, hs);
+    rc = upload(d, &d->sel, s.data(), s.size(), "selector projection");
+  }
+  if (!rc) {
+    auto h = repack_f16(w->head, d->V, hs);
+    rc = upload(d, &d->head, h.data(), h.size(), "head");
+  }
+  if (!rc) rc = upload(d, &d->embed, w->embed, (size_t)d->V * hs, "embedding");
+  if (!rc) rc = upload(d, &d->pbook, w->pred_book, (size_t)d->V * d->rank, "predecessor codebook");
+  if (!rc) rc = upload(d, &d->cbook, w->succ_book, (size_t)d->V * d->rank, "successor codebook");
+  if (!rc) rc = upload(d, &d->hidden_norm, w->hidden_norm, hs, "hidden_norm");
+  if (!rc) rc = upload(d, &d->norm, w->norm, hs, "norm");
+  // ---- per-layer vectors and kernel projections, [layer][...]
+  const size_t kp_layer = (size_t)d->ptiles * 16 * hs;
+  if (!rc) rc = dev_alloc(d, &d->attn_kproj, L * kp_layer, "attention kernel projections");
+  if (!rc) rc = dev_alloc(d, &d->mlp_kproj, L * kp_layer, "MLP kernel projections");
+  std::vector<float> in_n, post_n, q_n, k_n, ab, mb;
+  for (int l = 0; l < L && !rc; ++l) {
+    const dflash_layer_w& x = w->layer[l];
+    in_n.insert(in_n.end(), x.in_norm, x.in_norm + hs);
+    post_n.insert(post_n.end(), x.post_norm, x.post_norm + hs);
+    q_n.insert(q_n.end(), x.q_norm, x.q_norm + d->hd);
+    k_n.insert(k_n.end(), x.k_norm, x.k_norm + d->hd);
+    ab.insert(ab.end(), x.attn_base, x.attn_base + 2 * d->kn * hs);
+    mb.insert(mb.end(), x.mlp_base, x.mlp_base + 2 * d->kn * hs);
+    auto a = repack_f16(x.attn_kproj, d->P, hs);
+    auto m = repack_f16(x.mlp_kproj, d->P, hs);
+    if (hipMemcpy(d->attn_kproj + l * kp_layer, a.data(), a.size() * 2, hipMemcpyHostToDevice) ||
+        hipMemcpy(d->mlp_kproj + l * kp_layer, m.data(), m.size() * 2, hipMemcpyHostToDevice))
+      rc = fail(nullptr, DFLASH_EHIP, "copying kernel projections");
+  }
+  if (!rc) rc = upload(d, &d->in_norm, in_n.data(), in_n.size(), "input norms");
+  if (!rc) rc = upload(d, &d->post_norm, post_n.data(), post_n.size(), "post-attention norms");
+  if (!rc) rc = upload(d, &d->q_norm, q_n.data(), q_n.size(), "q norms");
+  if (!rc) rc = upload(d, &d->k_norm, k_n.data(), k_n.size(), "k norms");
+  if (!rc) rc = upload(d, &d->attn_base, ab.data(), ab.size(), "attention conv base");
+  if (!rc) rc = upload(d, &d->mlp_base, mb.data(), mb.size(), "MLP conv base");
+  // ---- int4 products: [q|k|v], o, [gate|up], down
+  if (!rc) rc = alloc_i4(d, d->qkv, (d->qd + 2 * d->kd) / 16, hs, "q/k/v");
+  if (!rc) rc = alloc_i4(d, d->o, hs / 16, d->qd, "o");
+  if (!rc) rc = alloc_i4(d, d->gu, 2 * d->ffn / 16, hs, "gate/up");
+  if (!rc) rc = alloc_i4(d, d->down, hs / 16, d->ffn, "down");
+  for (int l = 0; l < L && !rc; ++l) {
+    const dflash_layer_w& x = w->layer[l];
+    rc = upload_i4(d, d->qkv, l, {{&x.q, d->qd}, {&x.k, d->kd}, {&x.v, d->kd}});
+    if (!rc) rc = upload_i4(d, d->o, l, {{&x.o, hs}});
+    if (!rc) rc = upload_i4(d, d->gu, l, {{&x.gate, d->ffn}, {&x.up, d->ffn}});
+    if (!rc) rc = upload_i4(d, d->down, l, {{&x.down, hs}});
+  }
+  // ---- rotary frequencies: θ^(−2i/hd) in binary64, kept as binary32
+  if (!rc) {
+    std::vector<float> inv(d->hd / 2);
+    for (int i = 0; i < d->hd / 2; ++i) inv[i] = (float)std::pow(d->theta, -(2.0 * i) / d->hd);
+    rc = upload(d, &d->inv, inv.data(), inv.size(), "rotary frequencies");
+  }
+  if (!rc) rc = upload(d, &d->rot_dev, d->rot.data(), d->rot.size(), "rotary flags");
+  // ---- context store
+  const size_t store = (size_t)L * d->cap * d->kd;
+  if (!rc) rc = dev_alloc(d, &d->sk, store, "context keys");
+  if (!rc) rc = dev_alloc(d, &d->sv, store, "context values");
+  // ---- scratch
+  const int rep = d->nh / d->kv;
+  const size_t slots = (size_t)d->kv * (kMaxChunks + 1) * rep;
+  d->part_floats = partial_need(d);
+  int slice = 0;
+  const int ns = topk_slices(d->V, d->top, &slice);
+  if (!rc) rc = dev_alloc(d, &d->h, 16 * hs, "scratch");
+  if (!rc) rc = dev_alloc(d, &d->x, 16 * hs, "scratch");
+  if (!rc) rc = dev_alloc(d, &d->dsum_a, 16 * d->P, "scratch");
+  if (!rc) rc = dev_alloc(d, &d->dsum_m, 16 * d->P, "scratch");
+  if (!rc) rc = dev_alloc(d, &d->kb, 16 * d->kd, "scratch");
+  if (!rc) rc = dev_alloc(d, &d->vb, 16 * d->kd, "scratch");
+  if (!rc) rc = dev_alloc(d, &d->pacc, slots * 16 * d->hd, "attention partials");
+  if (!rc) rc = dev_alloc(d, &d->pml, slots * 16 * 2, "attention partials");
+  if (!rc) rc = dev_alloc(d, &d->part, d->part_floats, "GEMM partials");
+  if (!rc) rc = dev_alloc(d, &d->logits, (size_t)16 * d->V, "logits");
+  if (!rc) rc = dev_alloc(d, &d->hp, 16 * d->rank, "selector projection");
+  if (!rc) rc = dev_alloc(d, &d->cv, (size_t)16 * ns * d->top, "candidates");
+  if (!rc) rc = dev_alloc(d, &d->ci, (size_t)16 * ns * d->top, "candidates");
+  if (!rc) rc = dev_alloc(d, &d->xa, 16 * hs, "scratch");
+  if (!rc) rc = dev_alloc(d, &d->xca, 16 * hs, "scratch");
+  if (!rc) rc = dev_alloc(d, &d->qa, (size_t)d->nh * 16 * d->hd, "scratch");
+  if (!rc) rc = dev_alloc(d, &d->ya, 16 * d->qd, "scratch");
+  if (!rc) rc = dev_alloc(d, &d->ma, 16 * d->ffn, "scratch");
+  d->stage_cols = std::max(std::max(d->tw, d->ffn), std::max(d->qd, hs));
+  if (!rc) rc = dev_alloc(d, &d->taps_a, (size_t)kSettleRows * d->stage_cols, "settle scratch");
+  if (!rc) rc = dev_alloc(d, &d->t_a, (size_t)kSettleRows * hs, "settle scratch");
+  if (!rc) rc = hip_check(nullptr, hipDeviceSynchronize(), "create");
+  return done(rc);
+}
+
+int dflash_sync(dflash_t* d) {
+  if (!d) return DFLASH_EINVAL;
+  return hip_check(d, hipStreamSynchronize(d->st), "stream synchronize");
+}
+
+int dflash_span(const dflash_t* d, int64_t* first, int64_t* end) {
+  if (!d || !first || !end) return DFLASH_EINVAL;
+  *first = d->first;
+  *end = d->first + d->len;
+  return DFLASH_OK;
+}
+
+int dflash_truncate(dflash_t* d, int64_t pos) {
+  if (!d) return DFLASH_EINVAL;
+  d->len = std::max(0L, std::min(d->len, (long)pos - d->first));
+  return DFLASH_OK;
+}
+
+// One settle pass of m ≤ 256 rows at store row `row0`, positions pos0.. .
+static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0) {
+  hipStream_t st = d->st;
+  const int mb = (m + 15) / 16;
+  dfl::to_a(st, taps, d->tw, m, d->tw, d->taps_a);
+  // t = fc · taps (f32 partials), then rms by hidden_norm into A-layout
+  const Split sf = split_for(d->hs / 16, kF16R, d->tw / 32, mb);
+  const long ssf = (long)mb * 16 * d->hs;
+  dfl::gemm_f16(st, d->taps_a, d->tw, mb, d->fc, dfl::TileMap{d->hs / 16, d->hs / 16, 0, 0}, d->hs,
+                sf.S, sf.per, d->part, ssf);
+  dfl::sum_norm(st, d->part, sf.S, ssf, m, d->hs, d->hidden_norm, d->eps, d->t_a);
+  // K and V of every layer: the k and v tiles of each layer's q/k/v set
+  const int kvt = 2 * d->kd / 16;
+  const int N = d->L * 2 * d->kd;
+  const Split sk = split_for(d->L * kvt, kI4R, d->hs / 128, mb);
+  const long ssk = (long)mb * 16 * N;
+  dfl::TileMap map{d->L * kvt, kvt, d->qkv.tiles, d->qd / 16};
+  dfl::gemm_i4(st, d->t_a, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per, d->part,
+               ssk);
+  dfl::settle_kv(st, d->part, sk.S, ssk, m, d->L, d->kv, d->hd, d->k_norm, d->inv, d->rot_dev,
+                 pos0, d->eps, d->sk, d->sv, d->cap, row0);
+  return launch_check(d, "settle");
+}
+
+int dflash_settle(dflash_t* d, int64_t first_pos, int32_t n, const float* taps) {
+  if (!d) return DFLASH_EINVAL;
+  if (n < 0 || first_pos < 0) return fail(d, DFLASH_EINVAL, "settle: n and first_pos must be >= 0");
+  if (n > 0 && !taps) return fail(d, DFLASH_EINVAL, "settle: null taps");
+  // position rule of `queue_context`
+  long first = d->first, len = d->len;
+  if (len == 0 || first_pos > first + len || first_pos < first) {
+    first = first_pos;
+    len = 0;
+  } else {
+    len = first_pos - first;
+  }
+  if (len + (long)n > d->cap)
+    return fail(d, DFLASH_ENOMEM, "settle: %ld rows do not fit the store (max_context %ld)",
+                len + (long)n, d->cap);
+  d->first = first;
+  d->len = len;
+  for (int done = 0; done < n; done += kSettleRows) {
+    const int m = std::min(kSettleRows, n - done);
+    const int rc = settle_pass(d, taps + (size_t)done * d->tw, m, first_pos + done, len + done);
+    if (rc) return rc;
+    d->len = len + done + m;
+  }
+  return DFLASH_OK;
+}
+
+int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t width, float* logits,
+                 int32_t* cand, float* unary, float* score, int32_t* chosen) {
+  if (!d) return DFLASH_EINVAL;
+  if (k < 1 || k >= d->B) return fail(d, DFLASH_EINVAL, "block: k must be in [1, block)");
+  if (width < d->top || width > d->V)
+    return fail(d, DFLASH_EINVAL, "block: width must be in [selector_top, vocab]");
+  if (anchor < 0 || anchor >= d->V) return fail(d, DFLASH_EINVAL, "block: anchor outside the vocabulary");
+  if (a < 0) return fail(d, DFLASH_EINVAL, "block: a must be >= 0");
+  if (!cand || !unary || !score || !chosen) return fail(d, DFLASH_EINVAL, "block: null output");
+  hipStream_t st = d->st;
+  const int hs = d->hs, B = d->B;
+  const float scale = std::pow((float)d->hd, -0.5f);
+  const long ssd = 16L * d->P, ssq = 16L * (d->qd + 2 * d->kd), ssh = 16L * hs;
+  const Split spk = split_for(d->ptiles, kF16R, hs / 32, 1);
+  const Split sqk = split_for(d->qkv.tiles, kI4R, hs / 128, 1);
+  const Split so = split_for(hs / 16, kI4R, d->qd / 128, 1);
+  const Split sdn = split_for(hs / 16, kI4R, d->ffn / 128, 1);
+  const size_t kp_layer = (size_t)d->ptiles * 16 * hs;
+  const size_t i4l_qkv = (size_t)d->qkv.tiles * (hs / 128);
+  const size_t i4l_o = (size_t)d->o.tiles * (d->qd / 128);
+  const size_t i4l_gu = (size_t)d->gu.tiles * (hs / 128);
+  const size_t i4l_dn = (size_t)d->down.tiles * (d->ffn / 128);
+
+  dfl::embed_norm(st, d->embed, anchor, d->mask, B, hs, d->in_norm, d->eps, d->h, d->x, d->xa);
+  for (int l = 0; l < d->L; ++l) {
+    const float* ab = d->attn_base + (size_t)l * 2 * d->kn * hs;
+    const float* mbase = d->mlp_base + (size_t)l * 2 * d->kn * hs;
+    // attention: conv_in, q/k/v, norms + rotary
+    dfl::gemm_f16(st, d->xa, hs, 1, d->attn_kproj + l * kp_layer,
+                  dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, spk.S, spk.per, d->part, ssd);
+    dfl::conv0(st, d->x, d->part, spk.S, ssd, ab, B, hs, d->gs, d->kn, d->xca, d->dsum_a);
+    dfl::gemm_i4(st, d->xca, hs, 1, d->qkv.codes + i4l_qkv * 1024 * l, d->qkv.scales + i4l_qkv * 64 * l,
+                 dfl::TileMap{d->qkv.tiles, d->qkv.tiles, 0, 0}, d->qd + 2 * d->kd, sqk.S, sqk.per,
+                 d->part, ssq);
+    dfl::qkv_post(st, d->part, sqk.S, ssq, B, d->nh, d->kv, d->hd, d->q_norm + (size_t)l * d->hd,
+                  d->k_norm + (size_t)l * d->hd, d->inv, a, d->rot[l], d->eps, d->qa, d->kb, d->vb);
+    // attention over the layer's context range and the block's rows
+    long lo, n;
+    layer_range(d, l, a, &lo, &n);
+    int nchunks = 0;
+    const int chunk = attn_chunk(n, &nchunks);
+    const size_t lrow = (size_t)l * d->cap + (lo - d->first);
+    dfl::attention(st, d->qa, d->sk + lrow * d->kd, d->sv + lrow * d->kd, d->kb, d->vb, B, d->nh,
+                   d->kv, d->hd, (int)n, lo, a, d->windows[l], chunk, nchunks, scale, d->pacc,
+                   d->pml);
+    dfl::attn_merge(st, d->pacc, d->pml, d->nh, d->kv, d->hd, nchunks, B, d->ya);
+    // o, conv_out into the residual, post-attention norm
+    dfl::gemm_i4(st, d->ya, d->qd, 1, d->o.codes + i4l_o * 1024 * l, d->o.scales + i4l_o * 64 * l,
+                 dfl::TileMap{d->o.tiles, d->o.tiles, 0, 0}, hs, so.S, so.per, d->part, ssh);
+    dfl::conv1_norm(st, d->h, d->part, so.S, ssh, d->dsum_a, ab, B, hs, d->gs, d->kn,
+                    d->post_norm + (size_t)l * hs, d->eps, d->x, d->xa);
+    // MLP, wrapped the same way
+    dfl::gemm_f16(st, d->xa, hs, 1, d->mlp_kproj + l * kp_layer,
+                  dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, spk.S, spk.per, d->part, ssd);
+    dfl::conv0(st, d->x, d->part, spk.S, ssd, mbase, B, hs, d->gs, d->kn, d->xca, d->dsum_m);
+    dfl::gemm_glu(st, d->xca, hs, d->gu.codes + i4l_gu * 1024 * l, d->gu.scales + i4l_gu * 64 * l,
+                  d->ffn / 16, d->ma);
+    dfl::gemm_i4(st, d->ma, d->ffn, 1, d->down.codes + i4l_dn * 1024 * l,
+                 d->down.scales + i4l_dn * 64 * l, dfl::TileMap{d->down.tiles, d->down.tiles, 0, 0},
+                 hs, sdn.S, sdn.per, d->part, ssh);
+    const float* next = l + 1 < d->L ? d->in_norm + (size_t)(l + 1) * hs : d->norm;
+    dfl::conv1_norm(st, d->h, d->part, sdn.S, ssh, d->dsum_m, mbase, B, hs, d->gs, d->kn, next,
+                    d->eps, d->x, d->xa);
+  }
+  // head over rows 1..k and the selector projection
+  float* lg = logits ? logits : d->logits;
+  dfl::head_sel(st, d->xa, hs, d->head, width, k, lg, d->sel, d->rank, d->hp);
+  int slice = 0;
+  const int ns = topk_slices(width, d->top, &slice);
+  dfl::topk_slice(st, lg, k, width, d->top, slice, ns, d->cv, d->ci);
+  dfl::topk_merge(st, d->cv, d->ci, k, ns * d->top, d->top, cand, unary);
+  dfl::select_chain(st, cand, unary, d->hp + d->rank, k, d->top, d->rank, d->pbook, d->cbook,
+                    d->V, anchor, nullptr, score, chosen);
+  d->last_k = k;
+  return launch_check(d, "block");
+}
+
+// --------------------------------------------------------------- debug
+
+static int matrix_of(dflash* d, int layer, int which, bool* is_i4, const void** codes,
+                     const uint16_t** scales, dfl::TileMap* map, int* rows, int* cols) {
+  if (which < DFLASH_W_FC && (layer < 0 || layer >= d->L))
+    return fail(d, DFLASH_EINVAL, "debug: layer out of range");
+  const int hs = d->hs;
+  auto i4 = [&](const I4Set& s, int K, int t_off, int ntiles) {
+    const size_t per_layer = (size_t)s.tiles * (K / 128);
+    *is_i4 = true;
+    *codes = s.codes + per_layer * 1024 * layer;
+    *scales = s.scales + per_layer * 64 * layer;
+    *map = dfl::TileMap{ntiles, ntiles, 0, t_off};
+    *rows = ntiles * 16;
+    *cols = K;
+  };
+  auto f16 = [&](const uint16_t* w, int N, int K) {
+    *is_i4 = false;
+    *codes = w;
+    *scales = nullptr;
+    *map = dfl::TileMap{(N + 15) / 16, (N + 15) / 16, 0, 0};
+    *rows = N;
+    *cols = K;
+  };
+  const size_t kp_layer = (size_t)d->ptiles * 16 * hs;
+  switch (which) {
+    case DFLASH_W_Q: i4(d->qkv, hs, 0, d->qd / 16); break;
+    case DFLASH_W_K: i4(d->qkv, hs, d->qd / 16, d->kd / 16); break;
+    case DFLASH_W_V: i4(d->qkv, hs, (d->qd + d->kd) / 16, d->kd / 16); break;
+    case DFLASH_W_O: i4(d->o, d->qd, 0, hs / 16); break;
+    case DFLASH_W_GATE: i4(d->gu, hs, 0, d->ffn / 16); break;
+    case DFLASH_W_UP: i4(d->gu, hs, d->ffn / 16, d->ffn / 16); break;
+    case DFLASH_W_DOWN: i4(d->down, d->ffn, 0, hs / 16); break;
+    case DFLASH_W_ATTN_KPROJ: f16(d->attn_kproj + kp_layer * layer, d->P, hs); break;
+    case DFLASH_W_MLP_KPROJ: f16(d->mlp_kproj + kp_layer * layer, d->P, hs); break;
+    case DFLASH_W_FC: f16(d->fc, hs, d->tw); break;
+    case DFLASH_W_HEAD: f16(d->head, d->V, hs); break;
+    case DFLASH_W_SEL: f16(d->sel, d->rank, hs); break;
+    default: return fail(d, DFLASH_EINVAL, "debug: unknown matrix id %d", which);
+  }
+  return DFLASH_OK;
+}
+
+int dflash_debug_dequant(dflash_t* d, int32_t layer, int32_t which, float* out) {
+  if (!d || !out) return DFLASH_EINVAL;
+  if (which > DFLASH_W_DOWN) return fail(d, DFLASH_EINVAL, "dequant: not an int4 matrix");
+  bool is_i4;
+  const void* codes;
+  const uint16_t* scales;
+  dfl::TileMap map;
+  int rows, cols;
+  int rc = matrix_of(d, layer, which, &is_i4, &codes, &scales, &map, &rows, &cols);
+  if (rc) return rc;
+  dfl::dequant_i4(d->st, static_cast<const uint8_t*>(codes), scales, map, rows, cols, out);
+  return launch_check(d, "dequant");
+}
+
+int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* x, int32_t m,
+                        float* y) {
+  if (!d || !x || !y) return DFLASH_EINVAL;
+  if (m < 1 || m > kSettleRows) return fail(d, DFLASH_EINVAL, "matvec: m must be in [1, 256]");
+  bool is_i4;
+  const void* codes;
+  const uint16_t* scales;
+  dfl::TileMap map;
+  int rows, cols;
+  int rc = matrix_of(d, layer, which, &is_i4, &codes, &scales, &map, &rows, &cols);
+  if (rc) return rc;
+  if (cols > d->stage_cols) return fail(d, DFLASH_EINVAL, "matvec: matrix wider than the staging buffer");
+  const int mb = (m + 15) / 16;
+  dfl::to_a(d->st, x, cols, m, cols, d->taps_a);
+  const Split s = is_i4 ? split_for(map.ntiles, kI4R, cols / 128, mb)
+                        : split_for(map.ntiles, kF16R, cols / 32, mb);
+  const long ss = (long)mb * 16 * rows;
+  if ((long)s.S * ss > d->part_floats) return fail(d, DFLASH_EINVAL, "matvec: partials too large");
+  if (is_i4)
+    dfl::gemm_i4(d->st, d->taps_a, cols, mb, static_cast<const uint8_t*>(codes), scales, map, rows,
+                 s.S, s.per, d->part, ss);
+  else
+    dfl::gemm_f16(d->st, d->taps_a, cols, mb, static_cast<const uint16_t*>(codes), map, rows, s.S,
+                  s.per, d->part, ss);
+  dfl::sum_rows(d->st, d->part, s.S, ss, m, rows, y);
+  return launch_check(d, "matvec");
+}
+
+int dflash_debug_read_store(dflash_t* d, int32_t layer, int64_t row0, int64_t n, float* k_out,
+                            float* v_out) {
+  if (!d || !k_out || !v_out) return DFLASH_EINVAL;
+  if (layer < 0 || layer >= d->L || row0 < 0 || n < 0 || row0 + n > d->cap)
+    return fail(d, DFLASH_EINVAL, "read_store: range outside the store");
+  const size_t off = ((size_t)layer * d->cap + row0) * d->kd, bytes = (size_t)n * d->kd * 4;
+  int rc = hip_check(d, hipMemcpyAsync(k_out, d->sk + off, bytes, hipMemcpyDeviceToDevice, d->st),
+                     "read_store");
+  if (!rc)
+    rc = hip_check(d, hipMemcpyAsync(v_out, d->sv + off, bytes, hipMemcpyDeviceToDevice, d->st),
+                   "read_store");
+  return rc;
+}
+
+int dflash_debug_load_store(dflash_t* d, int64_t first, int64_t len, const float* const* k,
+                            const float* const* v) {
+  if (!d || !k || !v) return DFLASH_EINVAL;
+  if (first < 0 || len < 0 || len > d->cap) return fail(d, DFLASH_EINVAL, "load_store: bad range");
+  for (int l = 0; l < d->L; ++l) {
+    if (len && (!k[l] || !v[l])) return fail(d, DFLASH_EINVAL, "load_store: null layer pointer");
+  }
+  const size_t bytes = (size_t)len * d->kd * 4;
+  for (int l = 0; l < d->L && len; ++l) {
+    const size_t off = (size_t)l * d->cap * d->kd;
+    int rc = hip_check(d, hipMemcpyAsync(d->sk + off, k[l], bytes, hipMemcpyDeviceToDevice, d->st),
+                       "load_store");
+    if (!rc)
+      rc = hip_check(d, hipMemcpyAsync(d->sv + off, v[l], bytes, hipMemcpyDeviceToDevice, d->st),
+                     "load_store");
+    if (rc) return rc;
+  }
+  d->first = first;
+  d->len = len;
+  return DFLASH_OK;
+}
+
+int dflash_debug_last_block(dflash_t* d, float* hidden, float* hp) {
+  if (!d) return DFLASH_EINVAL;
+  int rc = DFLASH_OK;
+  if (hidden)
+    rc = hip_check(d, hipMemcpyAsync(hidden, d->x, (size_t)d->B * d->hs * 4, hipMemcpyDeviceToDevice,
+                                     d->st),
+                   "last_block");
+  if (!rc && hp && d->last_k)
+    rc = hip_check(d, hipMemcpyAsync(hp, d->hp + d->rank, (size_t)d->last_k * d->rank * 4,
+                                     hipMemcpyDeviceToDevice, d->st),
+                   "last_block");
+  return rc;
+}
+
+int dflash_debug_select(dflash_t* d, const float* logits, const float* hp, int32_t k,
+                        int32_t width, int32_t anchor, const int32_t* forced_prev, int32_t* cand,
+                        float* unary, float* score, int32_t* chosen) {
+  if (!d || !logits || !hp || !cand || !unary || !score || !chosen) return DFLASH_EINVAL;
+  if (k < 1 || k >= 16) return fail(d, DFLASH_EINVAL, "select: k must be in [1, 15]");
+  if (width < d->top || width > d->V) return fail(d, DFLASH_EINVAL, "select: bad width");
+  if (anchor < 0 || anchor >= d->V) return fail(d, DFLASH_EINVAL, "select: bad anchor");
+  int slice = 0;
+  const int ns = topk_slices(width, d->top, &slice);
+  dfl::topk_slice(d->st, logits, k, width, d->top, slice, ns, d->cv, d->ci);
+  dfl::topk_merge(d->st, d->cv, d->ci, k, ns * d->top, d->top, cand, unary);
+  dfl::select_chain(d->st, cand, unary, hp, k, d->top, d->rank, d->pbook, d->cbook, d->V,
+                    anchor, forced_prev, score, chosen);
+  return launch_check(d, "select");
+}
+
+}  // extern "C"

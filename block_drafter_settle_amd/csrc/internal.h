@@ -1,0 +1,89 @@
+// Shared declarations between the host orchestration (dflash.cpp) and the
+// gfx950 kernels (kernels.hip). Layouts used by both sides:
+//
+// A-layout (activation operand of every GEMM, f16): an activation matrix of
+// M rows and K columns (K % 32 == 0) is cut into 16-row blocks; inside a
+// block, element (m, k) sits at half index
+//     ((k/32)·64 + ((k/8)%4)·16 + m)·8 + k%8,
+// so one 16x16x32 MFMA step s reads the contiguous 1 KB [s·64·8, (s+1)·64·8)
+// and lane l gets row l%16, columns 32s + 8(l/16) .. +7. Rows past M are 0.
+//
+// F16T (dense f16 weights [N][K]): 16-row tiles, each tile 32 columns at a
+// time: tile t, step s, lane l holds W[16t + l%16][32s + 8(l/16) .. +7] at
+// half index ((t·KS + s)·64 + l)·8, KS = K/32.
+//
+// I4T (int4 weights [N][K], K % 128 == 0): tile t, span p (128 columns),
+// lane l owns 16 bytes at ((t·KT + p)·64 + l)·16, KT = K/128: four 32-bit
+// words, word u holding row 16t + l%16, columns 128p + 32u + 8(l/16) + e for
+// e = 0..7 as offset-binary nibbles (code + 8); e even at bit 2e, e odd at
+// bit 16 + 2(e−1). Scales: 4 f16 per (tile, span, row) at
+// ((t·KT + p)·16 + l%16)·4 + u, the scale of column group 4p + u.
+//
+// Tile maps: GEMM tile t (0 .. ntiles−1) reads stored tile
+//     (t / seg)·seg_stride + seg_off + t % seg,
+// which lets one launch walk the same rows of every layer (the settle's
+// keys and values) or a row range of a fused matrix.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dfl {
+
+struct TileMap {
+  int ntiles;     // tiles in the product (output columns / 16, rounded up)
+  int seg;        // tiles per segment
+  long seg_stride;  // stored tiles between segments
+  long seg_off;   // stored tile of the product's tile 0
+};
+
+// GEMM launches: out[split][mb·16 + m][col] partial sums (f32), col < N.
+void gemm_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
+              TileMap map, int N, int splits, int steps_per_split, float* out, long split_stride);
+void gemm_i4(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint8_t* codes,
+             const uint16_t* scales, TileMap map, int N, int splits, int spans_per_split,
+             float* out, long split_stride);
+// gate/up with the SwiGLU epilogue: gate tiles [0, ftiles), up tiles
+// [ftiles, 2·ftiles) of one stored matrix; writes silu(g)·u in A-layout.
+void gemm_glu(hipStream_t st, const uint16_t* xa, int K, const uint8_t* codes,
+              const uint16_t* scales, int ftiles, uint16_t* ma);
+// Logits of rows 1..k over head tiles [0, ceil(width/16)) and the selector
+// projection hp [16][rank] of all rows, in one launch.
+void head_sel(hipStream_t st, const uint16_t* xa, int K, const uint16_t* head, int width,
+              int k, float* logits, const uint16_t* sel, int rank, float* hp);
+
+void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa);
+void sum_norm(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,
+              const float* w, float eps, uint16_t* xa);
+void embed_norm(hipStream_t st, const uint16_t* embed, int anchor, int mask, int rows, int hs,
+                const float* w, float eps, float* h, float* x, uint16_t* xa);
+void conv0(hipStream_t st, const float* x, const float* dpart, int splits, long split_stride,
+           const float* base, int rows, int hs, int gs, int kn, uint16_t* xca, float* dsum);
+void conv1_norm(hipStream_t st, float* h, const float* opart, int splits, long split_stride,
+                const float* dsum, const float* base, int rows, int hs, int gs, int kn,
+                const float* w, float eps, float* x, uint16_t* xa);
+void qkv_post(hipStream_t st, const float* part, int splits, long split_stride, int rows, int nh,
+              int kv, int hd, const float* q_norm, const float* k_norm, const float* inv_freq,
+              long pos0, int rot, float eps, uint16_t* qa, float* kb, float* vb);
+void settle_kv(hipStream_t st, const float* part, int splits, long split_stride, int rows,
+               int layers, int kv, int hd, const float* k_norm, const float* inv_freq,
+               const int* rot, long pos0, float eps, float* store_k, float* store_v, long cap,
+               long row0);
+void attention(hipStream_t st, const uint16_t* qa, const float* sk, const float* sv,
+               const float* kb, const float* vb, int B, int nh, int kv, int hd, int n,
+               long lo_pos, long a, int window, int chunk, int nchunks, float scale,
+               float* pacc, float* pml);
+void attn_merge(hipStream_t st, const float* pacc, const float* pml, int nh, int kv, int hd,
+                int nchunks, int B, uint16_t* ya);
+void topk_slice(hipStream_t st, const float* logits, int k, int width, int top, int slice,
+                int nslices, float* cv, int* ci);
+void topk_merge(hipStream_t st, const float* cv, const int* ci, int k, int cnt, int top,
+                int* cand, float* unary);
+void select_chain(hipStream_t st, const int* cand, const float* unary, const float* hp, int k,
+                  int top, int rank, const uint16_t* pbook, const uint16_t* cbook, int vocab,
+                  int anchor, const int* forced_prev, float* score, int* chosen);
+void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,
+                int rows, int K, float* out);
+void sum_rows(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,
+              float* out);
+
+}  // namespace dfl

@@ -1,0 +1,199 @@
+/*
+ * dflash.h — the DFlash 2 drafter's forward pass on one AMD MI355X (gfx950).
+ *
+ * The drafter and its two passes are defined on the docs.rs page
+ * "cortiq_engine/dflash.rs" (cortiq-engine 0.8.78): the module overview (the
+ * context, block and token formulas), `Geometry`, `settle_rows`,
+ * `Drafter::block`, `block_dev` (the per-layer context ranges and the head
+ * width), `select_with` and `top_k`. The device interface it replaces is the
+ * CUDA block on the page "src/gpu_cuda/hyb/dflash.rs" (cortiq-engine
+ * 0.8.72): `Dev::new` (the sidecar onto the card), `Dev::settle` and
+ * `Dev::block`.
+ *
+ * Conventions for every entry point:
+ *   - Return 0 on success or a negative code: DFLASH_EINVAL (-1) for an
+ *     invalid argument or geometry, DFLASH_ENOMEM (-2) for device memory or
+ *     store capacity (max_context) exhausted, DFLASH_EHIP (-3) for a HIP
+ *     runtime error. The message is kept for dflash_last_error. Arguments
+ *     are checked before any launch, and a call that fails changes no state.
+ *   - "dev" pointers are device memory the caller owns (e.g. torch tensors'
+ *     data_ptr on the same GPU); "host" pointers are host memory.
+ *   - Work is enqueued on the stream given at create and is asynchronous:
+ *     outputs are valid once that stream has been synchronised
+ *     (dflash_sync, or the caller's own stream sync). Calls on one handle
+ *     must not overlap from several host threads.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_OK 0
+#define DFLASH_EINVAL (-1)
+#define DFLASH_ENOMEM (-2)
+#define DFLASH_EHIP (-3)
+
+typedef struct dflash dflash_t; /* opaque; owns every device buffer it uses */
+
+/* A matrix of symmetric int4 weights with one f16 scale per 32 consecutive
+   columns of a row: element (r, c) = q(r, c) · scale[r][c/32].
+   q: [rows][cols/2] bytes, column 2j in the low nibble of byte j and column
+   2j+1 in the high nibble, two's complement (−8..7).
+   scale: [rows][cols/32] IEEE binary16 bit patterns. */
+typedef struct {
+  const uint8_t* q;
+  const uint16_t* scale;
+} dflash_i4;
+
+/* One draft layer (host pointers; the names are the sidecar's tensors of
+   `Drafter::new`). f16 arrays hold IEEE binary16 bit patterns. */
+typedef struct {
+  const float *in_norm, *post_norm; /* [hidden] input / post-attention RMSNorm gains */
+  const float *q_norm, *k_norm;     /* [head_dim] per-head query / key norm gains */
+  const float *attn_base, *mlp_base; /* [2][conv_kernel][hidden] conv base kernels,
+                                        stage 0 (before the sub-layer) then stage 1 */
+  const uint16_t *attn_kproj, *mlp_kproj; /* f16 [2*conv_kernel*(hidden/conv_group)][hidden]
+                                             kernel projections; output row
+                                             (stage*kn + o)*groups + g */
+  dflash_i4 q, k, v; /* [heads*head_dim | kv_heads*head_dim | kv_heads*head_dim][hidden] */
+  dflash_i4 o;       /* [hidden][heads*head_dim] */
+  dflash_i4 gate, up; /* [intermediate][hidden] */
+  dflash_i4 down;    /* [hidden][intermediate] */
+} dflash_layer_w;
+
+/* `Geometry` of the page, plus the store's capacity. Accepted when: layers
+   > 0, block in [2, 16], n_taps > 0, kv_heads > 0, heads % kv_heads == 0,
+   head_dim in {64, 128, 256}, conv_group > 0, hidden % conv_group == 0,
+   conv_kernel in [1, block], hidden, intermediate and heads*head_dim
+   multiples of 128, 1 ≤ selector_top ≤ 32, selector_top ≤ vocab,
+   selector_rank in [1, 256], 0 ≤ mask_token < vocab, every window ≥ 0,
+   max_context ≥ 1. */
+typedef struct {
+  int32_t hidden, intermediate, layers, heads, kv_heads, head_dim, vocab, block, mask_token,
+      conv_group, conv_kernel, selector_rank, selector_top, n_taps;
+  const int32_t* windows; /* host [layers]: positions a block row sees back, 0 = all */
+  const uint8_t* rotary;  /* host [layers]: 1 = rotary queries and keys, 0 = `no_rope` */
+  double rope_theta, eps;
+  int64_t max_context; /* rows the context store holds (positions first .. first+max_context) */
+} dflash_geometry;
+
+typedef struct {
+  const uint16_t* fc;         /* f16 [hidden][n_taps*hidden] */
+  const float* hidden_norm;   /* [hidden] */
+  const float* norm;          /* [hidden] the final norm */
+  const uint16_t* sel_proj;   /* f16 [selector_rank][hidden] selector hidden projection */
+  const uint16_t* pred_book;  /* f16 [vocab][selector_rank] predecessor codebook P */
+  const uint16_t* succ_book;  /* f16 [vocab][selector_rank] successor codebook C */
+  const uint16_t* embed;      /* f16 [vocab][hidden] the target's embedding */
+  const uint16_t* head;       /* f16 [vocab][hidden] the target's head (may equal embed) */
+  const dflash_layer_w* layer; /* [layers] */
+} dflash_weights;
+
+/* Build a drafter: validate the geometry, copy every weight to device memory
+   (int4 and f16 matrices repacked into the kernels' tile layouts), allocate
+   the f32 context store ([layer][max_context][kv_heads][head_dim], keys and
+   values) and all scratch. Synchronous: the caller may free every host array
+   once it returns. `stream` is a hipStream_t (NULL = the null stream) that
+   every later call enqueues on. On failure *out is NULL and
+   dflash_last_error(NULL) has the message. */
+int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* stream,
+                  dflash_t** out);
+
+/* Context settle (`settle_rows`; `Dev::settle`): n joined tap rows
+   (dev f32 [n][n_taps*hidden], row r = position first_pos + r, taps in the
+   order of the geometry's taps) become context: t = rms(fc·row, hidden_norm);
+   per layer K = rot(rms(Wk·t per kv head, k_norm), position) (no rotation
+   on a no-rope layer), V = Wv·t, stored f32.
+   Position rule (`queue_context`): with first ≤ first_pos ≤ first+len the
+   context is cut at first_pos and the rows appended; otherwise (an empty
+   context, a gap, or first_pos < first) it restarts at first_pos. n = 0 only
+   applies the rule. Fails with DFLASH_ENOMEM if the rows would not fit
+   max_context. Any n is accepted and taken 256 rows at a time. */
+int dflash_settle(dflash_t* d, int64_t first_pos, int32_t n, const float* taps);
+
+/* Block pass (`Drafter::block` + the head + `select_with`): rows
+   [embed[anchor_token], embed[mask_token] × (block−1)] at positions a, a+1, …
+   through every layer, attending to the settled context positions the
+   layer's range allows (per-layer range of `block_dev`; row r also hides
+   positions below a+r+1−window) and to all block rows. Rows 1..k after the
+   final norm give
+     logits  dev f32 [k][width], head rows 0..width−1 (NULL: not written),
+   and, after the selector (top `selector_top` candidates of each row by
+   logit, larger first and the smaller index first among equals, re-scored
+   as logit + Σ_r (P[prev]·hp)[r]·C[cand][r], prev = anchor for row 0 and
+   the chosen token of the row before otherwise):
+     cand    dev int32 [k][selector_top] candidate tokens, in top-k order
+     unary   dev f32   [k][selector_top] their logits
+     score   dev f32   [k][selector_top] their selector scores
+     chosen  dev int32 [k] the first candidate with the largest score.
+   Requires 1 ≤ k < block, selector_top ≤ width ≤ vocab,
+   0 ≤ anchor_token < vocab, a ≥ 0. */
+int dflash_block(dflash_t* d, int32_t anchor_token, int64_t a, int32_t k, int32_t width,
+                 float* logits, int32_t* cand, float* unary, float* score, int32_t* chosen);
+
+/* Forget the context from position pos on (`truncate`). */
+int dflash_truncate(dflash_t* d, int64_t pos);
+
+/* The settled span: *first and one past the last settled position. */
+int dflash_span(const dflash_t* d, int64_t* first, int64_t* end);
+
+/* Wait for every call enqueued so far. */
+int dflash_sync(dflash_t* d);
+
+/* Release every device buffer (after finishing the enqueued work). */
+void dflash_destroy(dflash_t* d);
+
+/* The message of the handle's last failure ("" if none); NULL handle: the
+   last failure of dflash_create on this thread. */
+const char* dflash_last_error(const dflash_t* d);
+
+/* ---- test entry points: each kernel on caller buffers ---------------------- */
+
+/* Matrix ids for the debug entry points (`layer` is ignored for the
+   sidecar-wide ones). */
+enum {
+  DFLASH_W_Q = 0, DFLASH_W_K, DFLASH_W_V, DFLASH_W_O, DFLASH_W_GATE, DFLASH_W_UP,
+  DFLASH_W_DOWN, DFLASH_W_ATTN_KPROJ, DFLASH_W_MLP_KPROJ, DFLASH_W_FC, DFLASH_W_HEAD,
+  DFLASH_W_SEL
+};
+
+/* The int4 matrix `which` (Q..DOWN) of `layer` as the device holds it,
+   dequantised: dev f32 [rows][cols], element q·scale. */
+int dflash_debug_dequant(dflash_t* d, int32_t layer, int32_t which, float* out);
+
+/* y = W·x with the product path's GEMM kernels: x dev f32 [m][cols]
+   (rounded to f16 like every activation operand), y dev f32 [m][rows],
+   m in [1, 256]. */
+int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* x, int32_t m,
+                        float* y);
+
+/* Copy rows [row0, row0+n) of layer's store (row i = position first+i):
+   k_out, v_out dev f32 [n][kv_heads*head_dim]. */
+int dflash_debug_read_store(dflash_t* d, int32_t layer, int64_t row0, int64_t n, float* k_out,
+                            float* v_out);
+
+/* Replace the context with `len` given rows at positions first..first+len−1:
+   k[l], v[l] (host array of `layers` dev pointers) dev f32 [len][kv*hd]. */
+int dflash_debug_load_store(dflash_t* d, int64_t first, int64_t len, const float* const* k,
+                            const float* const* v);
+
+/* From the last dflash_block: every row after the final norm, dev f32
+   [block][hidden], and the selector projection of rows 1..k, dev f32
+   [k][selector_rank] (either may be NULL). */
+int dflash_debug_last_block(dflash_t* d, float* hidden, float* hp);
+
+/* The selector alone on given logits (dev f32 [k][width]) and projections
+   hp (dev f32 [k][rank]); forced_prev (dev int32 [k] or NULL) replaces prev
+   of every row j ≥ 1. Outputs as dflash_block. */
+int dflash_debug_select(dflash_t* d, const float* logits, const float* hp, int32_t k,
+                        int32_t width, int32_t anchor_token, const int32_t* forced_prev,
+                        int32_t* cand, float* unary, float* score, int32_t* chosen);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

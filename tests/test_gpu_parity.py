@@ -1,0 +1,298 @@
+"""GPU path against the CPU oracle, on the same seeded inputs, through the
+C-ABI. Floating-point outputs must satisfy max|err| ≤ 2e-3·max|ref| per
+tensor and call; integer and index work is compared exactly (candidates and
+chosen tokens where the oracle's margin exceeds that tolerance)."""
+import numpy as np
+import pytest
+import torch
+
+import block_drafter_settle_amd as pkg
+from block_drafter_settle_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL = 2e-3
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return torch.device("cuda:0")
+
+
+def close(got, ref, what, rel=REL):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    tol = rel * np.abs(ref).max()
+    err = np.abs(got - ref).max()
+    print(f"{what}: max|err| {err:.3e} tol {tol:.3e}", flush=True)
+    assert err <= tol, f"{what}: max|err| {err:.3e} > {tol:.3e}"
+
+
+def make(g, seed, max_context):
+    w = synth.make_weights(g, seed=seed)
+    stream = torch.cuda.current_stream(_dev()).cuda_stream
+    return w, pkg.Drafter(g, w, max_context=max_context, stream=stream)
+
+
+def run_block(d, g, anchor, a, k, width):
+    dev = _dev()
+    top = g["selector_top"]
+    out = dict(logits=torch.empty(k, width, device=dev),
+               cand=torch.empty(k, top, dtype=torch.int32, device=dev),
+               unary=torch.empty(k, top, device=dev), score=torch.empty(k, top, device=dev),
+               chosen=torch.empty(k, dtype=torch.int32, device=dev),
+               hidden=torch.empty(g["block"], g["hidden"], device=dev),
+               hp=torch.empty(k, g["selector_rank"], device=dev))
+    d.block(anchor, a, k, width, out["logits"].data_ptr(), out["cand"].data_ptr(),
+            out["unary"].data_ptr(), out["score"].data_ptr(), out["chosen"].data_ptr())
+    d.debug_last_block(out["hidden"].data_ptr(), out["hp"].data_ptr())
+    d.sync()
+    return {n: t.cpu().numpy() for n, t in out.items()}
+
+
+def check_selection(got, ref_logits, ref_sel, what):
+    """Candidates where the oracle's neighbouring gaps exceed τ; chosen
+    tokens and scores along the chain while it agrees."""
+    tau = REL * np.abs(ref_logits).max()
+    k, top = ref_sel["cand"].shape
+    for j in range(k):
+        row = np.sort(ref_logits[j])[::-1]
+        for t in range(top):
+            lo_gap = row[t] - row[t + 1] if t + 1 < row.size else np.inf
+            hi_gap = row[t - 1] - row[t] if t > 0 else np.inf
+            if lo_gap > tau and hi_gap > tau:
+                assert got["cand"][j, t] == ref_sel["cand"][j, t], (what, j, t)
+    # the chain: compare while every earlier chosen token agrees
+    stau = REL * np.abs(ref_sel["score"]).max()
+    for j in range(k):
+        if not np.array_equal(got["cand"][j], ref_sel["cand"][j]):
+            break
+        err = np.abs(got["score"][j] - ref_sel["score"][j]).max()
+        assert err <= stau, f"{what} score row {j}: max|err| {err:.3e} > {stau:.3e}"
+        s = np.sort(ref_sel["score"][j])[::-1]
+        if s.size < 2 or s[0] - s[1] > stau:
+            assert got["chosen"][j] == ref_sel["chosen"][j], (what, "chosen", j)
+        if got["chosen"][j] != ref_sel["chosen"][j]:
+            break
+
+
+# ------------------------------------------------------------------ pieces
+
+@pytest.fixture(scope="module")
+def small():
+    g = synth.small_geometry(windows=[0, 5], no_rope=[1])
+    w, d = make(g, seed=1, max_context=600)
+    yield g, w, d
+    d.close()
+
+
+def test_dequant_bit_exact(small, orc):
+    g, w, d = small
+    dev = _dev()
+    names = ["q", "k", "v", "o", "gate", "up", "down"]
+    for l in range(g["layers"]):
+        for which, name in enumerate(names):
+            codes, scale = w["layers"][l][name]
+            ref = orc.dequant_q4(codes, scale).astype(np.float32)
+            out = torch.empty(ref.shape, device=dev)
+            d.debug_dequant(l, which, out.data_ptr())
+            d.sync()
+            assert np.array_equal(out.cpu().numpy(), ref), (l, name)
+
+
+@pytest.mark.parametrize("m", [1, 7, 16, 37])
+def test_matvec_parity(small, orc, m):
+    g, w, d = small
+    dev = _dev()
+    names = ["q", "k", "v", "o", "gate", "up", "down"]
+    rng = np.random.default_rng(m)
+    cases = []
+    for which, name in enumerate(names):
+        codes, scale = w["layers"][1][name]
+        cases.append((1, which, ("q4", codes, scale)))
+    cases.append((0, pkg.W_ATTN_KPROJ, ("f16", w["layers"][0]["attn_kproj"])))
+    cases.append((1, pkg.W_MLP_KPROJ, ("f16", w["layers"][1]["mlp_kproj"])))
+    cases.append((0, pkg.W_FC, ("f16", w["fc"])))
+    cases.append((0, pkg.W_SEL, ("f16", w["sel_proj"])))
+    if m <= 16:
+        cases.append((0, pkg.W_HEAD, ("f16", w["head"])))
+    for layer, which, mat in cases:
+        if mat[0] == "q4":
+            rows, cols = mat[1].shape[0], mat[1].shape[1] * 2
+        else:
+            rows, cols = mat[1].shape
+        x = rng.standard_normal((m, cols)).astype(np.float32)
+        ref = orc.apply_q4(mat[1], mat[2], x) if mat[0] == "q4" else orc.apply_f16(mat[1], x)
+        xd = torch.tensor(x, device=dev)
+        y = torch.empty(m, rows, device=dev)
+        d.debug_matvec(layer, which, xd.data_ptr(), m, y.data_ptr())
+        d.sync()
+        close(y.cpu().numpy(), ref, f"matvec {which} m={m}")
+
+
+# ------------------------------------------------------------------ settle
+
+def _read_store(d, g, rows, row0=0):
+    dev = _dev()
+    kd = g["kv_heads"] * g["head_dim"]
+    out = []
+    for l in range(g["layers"]):
+        k = torch.empty(rows, kd, device=dev)
+        v = torch.empty(rows, kd, device=dev)
+        d.debug_read_store(l, row0, rows, k.data_ptr(), v.data_ptr())
+        out.append((k, v))
+    d.sync()
+    return [(k.cpu().numpy(), v.cpu().numpy()) for k, v in out]
+
+
+@pytest.mark.parametrize("n,first", [(1, 0), (40, 100), (300, 7)])
+def test_settle_parity(small, orc, n, first):
+    g, w, d = small
+    dev = _dev()
+    taps = synth.make_taps(g, n, seed=n)
+    d.settle(first, n, taps.to(dev).data_ptr())
+    assert d.span() == (first, first + n)
+    got = _read_store(d, g, n)
+    K, V = orc.Model(g, w).settle(taps.numpy(), first)
+    for l in range(g["layers"]):
+        close(got[l][0], K[l], f"settle K layer {l}")
+        close(got[l][1], V[l], f"settle V layer {l}")
+
+
+def test_settle_position_rule(small):
+    g, w, d = small
+    dev = _dev()
+    taps = synth.make_taps(g, 30, seed=5).to(dev)
+    d.truncate(0)                                   # empty context
+    d.settle(50, 20, taps.data_ptr())               # an empty context restarts at first_pos
+    assert d.span() == (50, 70)
+    d.settle(70, 5, taps[20:].data_ptr())           # append
+    assert d.span() == (50, 75)
+    d.settle(60, 3, taps[10:].data_ptr())           # rewind to 60, then append
+    assert d.span() == (50, 63)
+    d.settle(90, 2, taps.data_ptr())                # gap: restart
+    assert d.span() == (90, 92)
+    d.settle(10, 1, taps.data_ptr())                # before first: restart
+    assert d.span() == (10, 11)
+    d.truncate(10)
+    assert d.span() == (10, 10)
+    with pytest.raises(pkg.DflashError) as e:
+        d.settle(10, 601, taps.data_ptr())          # over max_context: no state change
+    assert e.value.code == pkg.DFLASH_ENOMEM and d.span() == (10, 10)
+
+
+def test_rewind_resettle_equals_fresh(small):
+    g, w, d = small
+    dev = _dev()
+    taps = synth.make_taps(g, 24, seed=8).to(dev)
+    other = synth.make_taps(g, 24, seed=9).to(dev)
+    d.settle(0, 24, taps.data_ptr())
+    fresh = _read_store(d, g, 24)
+    d.settle(0, 24, other.data_ptr())
+    d.settle(10, 14, taps[10:].data_ptr())
+    mixed = _read_store(d, g, 24)
+    for l in range(g["layers"]):
+        assert np.array_equal(fresh[l][0][10:], mixed[l][0][10:])
+        assert np.array_equal(fresh[l][1][10:], mixed[l][1][10:])
+
+
+# ------------------------------------------------------------------- block
+
+BLOCK_CASES = [
+    # geometry overrides, context (first, length), anchor offset from the end, k, width
+    (dict(windows=[0, 0], no_rope=[]), (0, 64), 0, 7, 1000),
+    (dict(windows=[0, 5], no_rope=[1]), (100, 40), 0, 7, 1000),
+    (dict(windows=[3, 33], no_rope=[0]), (20, 150), 0, 3, 1000),
+    (dict(windows=[0, 2], no_rope=[]), (0, 0), 0, 7, 1000),          # empty context
+    (dict(windows=[0, 0], no_rope=[]), (30, 90), -25, 1, 8),         # anchor inside, min width
+    (dict(windows=[0, 0], no_rope=[], block=16), (0, 200), 0, 15, 1000),
+    (dict(windows=[0, 0], no_rope=[], kv_heads=4), (5, 70), 3, 7, 999),
+    (dict(windows=[0, 0], no_rope=[], heads=8, kv_heads=1, head_dim=128), (0, 300), 0, 7, 1000),
+]
+
+
+@pytest.mark.parametrize("case", BLOCK_CASES)
+def test_block_parity(orc, case):
+    over, (first, length), da, k, width = case
+    g = synth.small_geometry(**over)
+    w, d = make(g, seed=2, max_context=max(length, 1) + 8)
+    try:
+        dev = _dev()
+        m = orc.Model(g, w)
+        if length:
+            taps = synth.make_taps(g, length, seed=3)
+            d.settle(first, length, taps.to(dev).data_ptr())
+            K, V = m.settle(taps.numpy(), first)
+            store = [(K[l], V[l]) for l in range(g["layers"])]
+        else:
+            store = [(np.zeros((1, g["kv_heads"] * g["head_dim"]), np.float32),) * 2
+                     for _ in range(g["layers"])]
+        a = first + length + da
+        anchor = 123
+        got = run_block(d, g, anchor, a, k, width)
+        ref = m.block(store, first, length, anchor, a, k, width)
+        close(got["hidden"], ref["hidden"], "hidden")
+        close(got["logits"], ref["logits"], "logits")
+        close(got["hp"], ref["hp"], "hp")
+        sel = m.select(ref["logits"], ref["hp"], anchor)
+        check_selection(got, ref["logits"], sel, "block")
+    finally:
+        d.close()
+
+
+def test_block_is_deterministic(small):
+    g, w, d = small
+    dev = _dev()
+    taps = synth.make_taps(g, 50, seed=4)
+    d.settle(0, 50, taps.to(dev).data_ptr())
+    a = run_block(d, g, 9, 50, 7, 1000)
+    b = run_block(d, g, 9, 50, 7, 1000)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+
+
+# ----------------------------------------------------------------- select
+
+@pytest.mark.parametrize("strong", [False, True])
+def test_select_parity(orc, strong):
+    g = synth.small_geometry(vocab=5000, mask_token=4999, selector_top=16, selector_rank=32)
+    w, d = make(g, seed=6, max_context=8)
+    try:
+        dev = _dev()
+        if strong:  # codebooks large enough for the selector to reorder
+            rng = np.random.default_rng(1)
+            w["pred_book"] = (rng.standard_normal(w["pred_book"].shape) * 0.5).astype(
+                np.float16).view(np.uint16)
+            w["succ_book"] = (rng.standard_normal(w["succ_book"].shape) * 0.5).astype(
+                np.float16).view(np.uint16)
+            d.close()
+            d = pkg.Drafter(g, w, max_context=8, stream=torch.cuda.current_stream(dev).cuda_stream)
+        rng = np.random.default_rng(2)
+        k, width = 7, 4093
+        logits = rng.integers(-30, 30, (k, width)).astype(np.float32) / 4  # many exact ties
+        hp = rng.standard_normal((k, g["selector_rank"])).astype(np.float32)
+        top = g["selector_top"]
+        ld, hd_ = torch.tensor(logits, device=dev), torch.tensor(hp, device=dev)
+        cand = torch.empty(k, top, dtype=torch.int32, device=dev)
+        unary = torch.empty(k, top, device=dev)
+        score = torch.empty(k, top, device=dev)
+        chosen = torch.empty(k, dtype=torch.int32, device=dev)
+        d.debug_select(ld.data_ptr(), hd_.data_ptr(), k, width, 77, None, cand.data_ptr(),
+                       unary.data_ptr(), score.data_ptr(), chosen.data_ptr())
+        d.sync()
+        ref = orc.Model(g, w).select(logits, hp, 77)
+        assert np.array_equal(cand.cpu().numpy(), ref["cand"])       # same f32 inputs: exact
+        assert np.array_equal(unary.cpu().numpy(), ref["unary"].astype(np.float32))
+        got = dict(cand=cand.cpu().numpy(), score=score.cpu().numpy(),
+                   chosen=chosen.cpu().numpy())
+        check_selection(got, logits, ref, "select")
+        # forced predecessors: every row scored against the oracle's chain
+        fp = torch.tensor(np.concatenate([[77], ref["chosen"][:-1]]).astype(np.int32), device=dev)
+        d.debug_select(ld.data_ptr(), hd_.data_ptr(), k, width, 77, fp.data_ptr(),
+                       cand.data_ptr(), unary.data_ptr(), score.data_ptr(), chosen.data_ptr())
+        d.sync()
+        close(score.cpu().numpy(), ref["score"], "forced scores")
+    finally:
+        d.close()
