@@ -1,0 +1,266 @@
+#!/usr/bin/env python
+"""Throughput of the DFlash 2 drafter's forward pass on one MI355X.
+
+Workload (synthetic, seeded; weights random-init of the 27B-target-shaped
+sidecar: hidden 5120, intermediate 17408, 5 layers, 32/8 heads, head_dim
+128, vocab 248320, block 16, 5 taps (tap width 25600), windows
+[2048 x4, 0], layer 4 without rotary; int4 q/k/v/o/gate/up/down, f16 fc,
+kernel projections, head, selector):
+
+  stream  32768 context positions settled first (untimed); then each step
+          settles the next 8 tap rows and runs one block at the next anchor
+          (k = 15 draft rows, head width = the vocabulary, a uniform anchor
+          token). `value` = steps per second = draft blocks per second,
+          the 8-row settle included.
+  settle  16384 tap rows (N(0,1), 1 % of the channels x20) settled in 64
+          calls of 256 rows: settle rows per second.
+
+One JSON line on stdout; progress on stderr. Inputs are resident in device
+memory before any timed region. The per-kernel rooflines come from the
+library's stage timers (hipEvents on its stream) in a separate timed pass.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+F16_MFMA_PEAK_TFS = 2500.0   # MI355X dense f16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-calls", type=int, default=64)
+    ap.add_argument("--timing-steps", type=int, default=50)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the drafter's path runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_drafter_settle_amd as pkg
+    from block_drafter_settle_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    g = synth.geometry("t27b")
+    hs, V, tw, L = g["hidden"], g["vocab"], synth.tap_width(g), g["layers"]
+    kd = g["kv_heads"] * g["head_dim"]
+    k, width, per_step = g["block"] - 1, g["vocab"], 8
+    ctx0 = 32768
+    steps, warm = args.steps, args.warmup
+    cap = max(ctx0 + per_step * (warm + steps + args.timing_steps) + 16, 16384 + 256)
+
+    t0 = time.time()
+    w = synth.make_weights(g, seed=0, device=dev)
+    log(f"weights generated in {time.time() - t0:.1f}s")
+    t0 = time.time()
+    d = pkg.Drafter(g, w, max_context=cap, stream=stream)
+    log(f"drafter created in {time.time() - t0:.1f}s (store capacity {cap} rows)")
+
+    # ------------------------------------------------ settle-bound workload
+    n_set = 256 * args.settle_calls
+    taps4 = synth.make_taps(g, n_set, seed=0, name="settle_taps", outliers=True, device=dev)
+    for i in range(4):
+        d.settle(0, 256, taps4[256 * i:].data_ptr())
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.settle_calls):
+        d.settle(256 * i, 256, taps4[256 * i:].data_ptr())
+    ev1.record()
+    torch.cuda.synchronize()
+    settle_s = ev0.elapsed_time(ev1) / 1e3
+    settle_rows_s = n_set / settle_s
+    log(f"settle: {n_set} rows in {settle_s * 1e3:.2f} ms -> {settle_rows_s / 1e6:.3f} M rows/s")
+    d.set_timing(True)
+    for i in range(8):
+        d.settle(256 * i, 256, taps4[256 * i:].data_ptr())
+    st_settle, _, n_settles = d.stage_times()
+    d.set_timing(False)
+    del taps4
+
+    # ------------------------------------------------------ stream workload
+    t0 = time.time()
+    for c in range(ctx0 // 256):
+        tp = synth.make_taps(g, 256, seed=0, name=f"context.{c}", device=dev)
+        d.settle(256 * c, 256, tp.data_ptr())
+    torch.cuda.synchronize()
+    log(f"context of {ctx0} positions settled in {time.time() - t0:.1f}s")
+    total = warm + steps + args.timing_steps
+    stream_taps = synth.make_taps(g, per_step * total, seed=0, name="stream", device=dev)
+    anchors = synth.uniform_tokens(g, total, seed=0)
+    top = g["selector_top"]
+    out = dict(logits=torch.empty(k, width, device=dev),
+               cand=torch.empty(k, top, dtype=torch.int32, device=dev),
+               unary=torch.empty(k, top, device=dev), score=torch.empty(k, top, device=dev),
+               chosen=torch.empty(k, dtype=torch.int32, device=dev))
+    ptrs = [out[n].data_ptr() for n in ("logits", "cand", "unary", "score", "chosen")]
+    pos = ctx0
+
+    def step(i):
+        nonlocal pos
+        d.settle(pos, per_step, stream_taps[per_step * i:].data_ptr())
+        pos += per_step
+        d.block(anchors[i], pos, k, width, *ptrs)
+
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warm, warm + steps):
+        step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    value = steps / dt
+    log(f"stream: {steps} steps in {dt * 1e3:.1f} ms -> {value:.1f} blocks/s")
+
+    # stage timers over a further stretch of the stream
+    d.set_timing(True)
+    for i in range(warm + steps, total):
+        step(i)
+    st_stream, n_blocks, n_str_settles = d.stage_times()
+    d.set_timing(False)
+    block_stages = ("kproj", "conv_norm", "qkv", "qk_post", "attention", "o", "gate_up", "down",
+                    "head", "select")
+    block_us = sum(st_stream[s][0] for s in block_stages) / n_blocks
+    head_us = st_stream["head"][0] / st_stream["head"][1]
+    # algorithmic bytes of one head launch: head rows and selector rows (f16)
+    # read once, the logits written once
+    head_bytes = width * hs * 2 + g["selector_rank"] * hs * 2 + k * width * 4
+    head_gbs = head_bytes / (head_us * 1e-6) / 1e9
+    # whole block: int4 weights + scales, f16 kernel projections, head,
+    # selector, visible context K/V, gathered codebook rows, embedding rows
+    qd = g["heads"] * g["head_dim"]
+    ffn = g["intermediate"]
+    i4 = L * (qd * hs + 2 * kd * hs + hs * qd + 3 * ffn * hs) * (0.5 + 2 / 32)
+    kproj = L * 2 * (2 * g["conv_kernel"] * hs // g["conv_group"]) * hs * 2
+    a_end = pos
+    kv_rows = 0
+    for l in range(L):
+        wdw = g["windows"][l]
+        hi = a_end
+        lo = max(0, a_end + 1 - wdw) if wdw > 0 else 0
+        kv_rows += hi - lo
+    block_bytes = (i4 + kproj + head_bytes + kv_rows * kd * 4 * 2 +
+                   k * (1 + top) * g["selector_rank"] * 2 + 2 * hs * 2)
+    # settle: the fc GEMM's flops per 256-row launch
+    fc_us = st_settle["settle_fc"][0] / st_settle["settle_fc"][1]
+    fc_flops = 2.0 * 256 * tw * hs
+    settle_flops = 2.0 * 256 * (tw * hs + L * 2 * kd * hs)
+    settle_call_us = sum(v[0] for n, v in st_settle.items() if n.startswith("settle")) / n_settles
+
+    stages = {n: round(st_stream[n][0] / n_blocks, 2) for n in block_stages}
+    stages.update({n: round(st_settle[n][0] / n_settles, 2) for n in st_settle
+                   if n.startswith("settle")})
+    res = {
+        "metric": "draft blocks/s + settle rows/s (27B-shaped sidecar), % of HBM/MFMA roofline",
+        "value": round(value, 2),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(dt * 1e3 / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "27b_stream: 27B-target-shaped drafter (hidden 5120, ffn 17408, 5 layers, "
+                        "32/8 heads, hd 128, vocab 248320, block 16, tap width 25600, windows "
+                        "[2048x4,0], layer 4 no_rope), 32768 settled positions, each step settles "
+                        "8 new tap rows then drafts one block (k=15, width=vocab) at the next anchor",
+            "weights": "int4 g32 f16-scale q/k/v/o/gate/up/down; f16 fc/kproj/head/selector; "
+                       "f32 context KV; f16 MFMA operands, f32 accumulate",
+            "block_rows": g["block"], "k": k, "width": width, "context": ctx0,
+            "settle_rows_per_step": per_step,
+        },
+        "block_only": {
+            "blocks_per_s": round(1e6 / block_us, 1),
+            "us_per_block": round(block_us, 1),
+            "algorithmic_bytes": int(block_bytes),
+            "hbm_frac": round(block_bytes / (block_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "roofline": {
+            "kernel": "k_head (head logits over the vocabulary + selector projection)",
+            "bound": "hbm",
+            "achieved": round(head_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(head_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "us_per_launch": round(head_us, 2),
+            "bytes_per_launch": int(head_bytes),
+        },
+        "settle": {
+            "workload": "27b_settle: 16384 tap rows (1% channels x20) in 64 calls of 256 rows",
+            "rows_per_s": round(settle_rows_s, 1),
+            "us_per_call": round(settle_call_us, 2),
+            "mfma_frac_call": round(settle_flops / (settle_call_us * 1e-6) / 1e12 /
+                                    F16_MFMA_PEAK_TFS, 4),
+            "roofline": {
+                "kernel": "k_gemm_f16 (fc, 256 rows)",
+                "bound": "mfma",
+                "achieved": round(fc_flops / (fc_us * 1e-6) / 1e12, 2),
+                "peak": F16_MFMA_PEAK_TFS,
+                "unit": "TFLOP/s",
+                "frac": round(fc_flops / (fc_us * 1e-6) / 1e12 / F16_MFMA_PEAK_TFS, 4),
+                "traffic": None,
+                "us_per_launch": round(fc_us, 2),
+            },
+        },
+        "stages_us": stages,
+    }
+
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(g, w, synth)
+    d.close()
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(g, w, synth):
+    """The CPU oracle on a bounded sample of the stream: one step (8 tap
+    rows settled + one block over a 32768-row context) on the host cores."""
+    import numpy as np
+
+    from oracle import oracle
+
+    oracle.build()
+    log("cpu baseline: oracle, one stream step ...")
+    m = oracle.Model(g, w)
+    store = [(k.numpy(), v.numpy()) for k, v in synth.make_store(g, 32768, seed=0)]
+    taps = synth.make_taps(g, 8, seed=0, name="stream").numpy()
+    t0 = time.perf_counter()
+    m.settle(taps, 32768)
+    t1 = time.perf_counter()
+    r = m.block(store, 0, 32768, 5, 32768, g["block"] - 1, g["vocab"])
+    m.select(r["logits"], r["hp"], 5)
+    t2 = time.perf_counter()
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count()))
+    log(f"cpu baseline: settle 8 rows {t1 - t0:.1f}s, block {t2 - t1:.1f}s")
+    return {"value": round(1.0 / (t2 - t0), 4), "unit": "blocks/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "one stream step of the same workload: 8 tap rows settled + one block "
+                      "(32768-position synthetic context, k=15, width=vocab) + selection",
+            "settle_s": round(t1 - t0, 2), "block_s": round(t2 - t1, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -64,6 +64,8 @@ _SIGS = {
     "dflash_sync": ([C.c_void_p], C.c_int),
     "dflash_destroy": ([C.c_void_p], None),
     "dflash_last_error": ([C.c_void_p], C.c_char_p),
+    "dflash_set_timing": ([C.c_void_p, C.c_int], C.c_int),
+    "dflash_stage_times": ([C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
     "dflash_debug_dequant": ([C.c_void_p, C.c_int32, C.c_int32, C.c_void_p], C.c_int),
     "dflash_debug_matvec": ([C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int32,
                              C.c_void_p], C.c_int),
@@ -77,6 +79,10 @@ _SIGS = {
 }
 
 EXPORTS = tuple(_SIGS)
+
+# stage order of the library's timers (include/dflash.h, DFLASH_ST_*)
+STAGES = ("kproj", "conv_norm", "qkv", "qk_post", "attention", "o", "gate_up", "down", "head",
+          "select", "settle_taps", "settle_fc", "settle_norm", "settle_kv", "settle_store")
 
 
 def lib():
@@ -139,6 +145,7 @@ class Drafter:
 
     def __init__(self, g: dict, w: dict, max_context: int, stream: int = 0):
         self.g = g
+        self.h = None
         keep = []
 
         def arr(a, dt):
@@ -209,6 +216,16 @@ class Drafter:
 
     def sync(self):
         _check(lib().dflash_sync(self.h), self.h)
+
+    def set_timing(self, on: bool):
+        _check(lib().dflash_set_timing(self.h, 1 if on else 0), self.h)
+
+    def stage_times(self):
+        us = (C.c_double * len(STAGES))()
+        n = (C.c_int64 * len(STAGES))()
+        b, s = C.c_int64(), C.c_int64()
+        _check(lib().dflash_stage_times(self.h, us, n, C.byref(b), C.byref(s)), self.h)
+        return {name: (us[i], n[i]) for i, name in enumerate(STAGES)}, b.value, s.value
 
     def debug_dequant(self, layer, which, out_ptr):
         _check(lib().dflash_debug_dequant(self.h, layer, which, out_ptr), self.h)

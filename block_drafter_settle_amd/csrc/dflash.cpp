@@ -24,10 +24,16 @@
 namespace {
 
 constexpr int kSettleRows = 256;     // rows one settle pass takes
-constexpr int kTargetBlocks = 768;   // workgroups a GEMM launch aims for (256 CUs)
+constexpr int kTargetBlocks = 512;   // workgroups a GEMM launch aims for (256 CUs)
 constexpr int kMaxChunks = 64;       // context chunks per kv head in the attention
-constexpr int kF16R = 2;             // row tiles per wave of the f16 GEMM
-constexpr int kI4R = 1;              // row tiles per wave of the int4 GEMM
+// Row tiles per wave of each product (a workgroup covers 4·R tiles of 16).
+constexpr int kRKproj = 2;   // kernel projections, f16
+constexpr int kRFc = 2;      // settle's fc, f16
+constexpr int kRQkv = 2;     // q/k/v, int4
+constexpr int kRO = 2;       // o, int4
+constexpr int kRDown = 2;    // down, int4
+constexpr int kRKv = 2;      // settle's k/v of every layer, int4
+constexpr int kRDebug = 2;   // the debug matvec
 
 thread_local std::string g_create_error;
 
@@ -36,12 +42,13 @@ struct Split {
 };
 
 // K splits for a GEMM of `ntiles` row tiles with R tiles per wave, `steps`
-// K steps (32 columns for f16, 128 for int4) and `mblocks` 16-row blocks.
-Split split_for(int ntiles, int R, int steps, int mblocks) {
+// K steps (32 columns for f16, 128 for int4) and `mblocks` 16-row blocks;
+// every split keeps at least `min_per` steps.
+Split split_for(int ntiles, int R, int steps, int mblocks, int min_per) {
   const long groups = (ntiles + 4L * R - 1) / (4L * R);
   const long have = groups * mblocks;
   long S = (kTargetBlocks + have - 1) / have;
-  S = std::max(1L, std::min<long>(S, steps));
+  S = std::max(1L, std::min<long>(S, std::max(1, steps / min_per)));
   const int per = (int)((steps + S - 1) / S);
   return {(int)((steps + per - 1) / per), per};
 }
@@ -136,13 +143,24 @@ struct dflash {
         *hp = nullptr, *cv = nullptr;
   int* ci = nullptr;
   uint16_t *xa = nullptr, *xca = nullptr, *qa = nullptr, *ya = nullptr, *ma = nullptr;
+  float *sqp = nullptr, *tab = nullptr;
   // settle scratch
   uint16_t *taps_a = nullptr, *t_a = nullptr;
+  float* tbuf = nullptr;
   long part_floats = 0;
   int stage_cols = 0;  // widest activation the staging buffer holds
   int last_k = 0;
   std::vector<void*> allocs;
   std::string err;
+  struct Timing {
+    bool on = false;
+    std::vector<hipEvent_t> ev;            // event pool, grown on demand
+    int used = 0;
+    std::vector<std::pair<int, int>> marks;  // (stage, event) after each launch
+    double us[DFLASH_STAGES] = {};
+    int64_t launches[DFLASH_STAGES] = {};
+    int64_t blocks = 0, settles = 0;
+  } tm;
 };
 
 namespace {
@@ -195,6 +213,44 @@ int launch_check(dflash* d, const char* what) {
   return hip_check(d, hipGetLastError(), what);
 }
 
+// ---- stage timers: an event after every launch, resolved at the call's end
+void tm_record(dflash* d) {
+  auto& t = d->tm;
+  if (t.used == (int)t.ev.size()) {
+    hipEvent_t e;
+    (void)hipEventCreate(&e);
+    t.ev.push_back(e);
+  }
+  (void)hipEventRecord(t.ev[t.used++], d->st);
+}
+
+void tm_begin(dflash* d) {
+  if (!d->tm.on) return;
+  d->tm.used = 0;
+  d->tm.marks.clear();
+  tm_record(d);
+}
+
+void tm_mark(dflash* d, int stage) {
+  if (!d->tm.on) return;
+  tm_record(d);
+  d->tm.marks.emplace_back(stage, d->tm.used - 1);
+}
+
+void tm_end(dflash* d) {
+  auto& t = d->tm;
+  if (!t.on || t.used == 0) return;
+  (void)hipEventSynchronize(t.ev[t.used - 1]);
+  int prev = 0;
+  for (auto& m : t.marks) {
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, t.ev[prev], t.ev[m.second]);
+    t.us[m.first] += 1000.0 * ms;
+    t.launches[m.first] += 1;
+    prev = m.second;
+  }
+}
+
 const char* validate(const dflash_geometry* g, const dflash_weights* w) {
   if (!g || !w) return "null geometry or weights";
   if (g->layers <= 0) return "layers must be > 0";
@@ -213,6 +269,7 @@ const char* validate(const dflash_geometry* g, const dflash_weights* w) {
   if (g->selector_top < 1 || g->selector_top > 32 || g->selector_top > g->vocab)
     return "selector_top must be in [1, min(32, vocab)]";
   if (g->selector_rank < 1 || g->selector_rank > 256) return "selector_rank must be in [1, 256]";
+  if ((long)g->vocab * g->selector_top > 8388608L) return "vocab*selector_top must be at most 2^23";
   if (g->mask_token < 0 || g->mask_token >= g->vocab) return "mask_token outside the vocabulary";
   if (g->max_context < 1) return "max_context must be >= 1";
   if (!g->windows || !g->rotary) return "null windows or rotary";
@@ -260,32 +317,28 @@ int upload_i4(dflash* d, I4Set& s, int l, std::initializer_list<std::pair<const 
 // Largest GEMM partial buffer (floats) any call can need.
 long partial_need(const dflash* d) {
   long need = 0;
-  auto f16 = [&](int N, int K, int mb) {
-    const Split s = split_for((N + 15) / 16, kF16R, K / 32, mb);
+  auto f16 = [&](int N, int K, int mb, int R) {
+    const Split s = split_for((N + 15) / 16, R, K / 32, mb, 16);
     need = std::max(need, (long)s.S * mb * 16 * N);
   };
-  auto i4 = [&](int N, int K, int mb) {
-    const Split s = split_for(N / 16, kI4R, K / 128, mb);
+  auto i4 = [&](int N, int K, int mb, int R) {
+    const Split s = split_for(N / 16, R, K / 128, mb, 4);
     need = std::max(need, (long)s.S * mb * 16 * N);
   };
+  f16(d->P, d->hs, 1, kRKproj);
+  i4(d->qd + 2 * d->kd, d->hs, 1, kRQkv);
+  i4(d->hs, d->qd, 1, kRO);
+  i4(d->hs, d->ffn, 1, kRDown);
   for (int mb = 1; mb <= kSettleRows / 16; ++mb) {
-    f16(d->hs, d->tw, mb);
-    f16(d->P, d->hs, mb);
-    f16(d->rank, d->hs, mb);
-    i4(d->L * 2 * d->kd, d->hs, mb);
-    i4(d->qd + 2 * d->kd, d->hs, mb);
-    i4(d->hs, d->qd, mb);
-    i4(2 * d->ffn, d->hs, mb);
-    i4(d->hs, d->ffn, mb);
+    f16(d->hs, d->tw, mb, kRFc);
+    i4(d->L * 2 * d->kd, d->hs, mb, kRKv);
+    for (int N : {d->hs, d->P, d->rank}) f16(N, d->hs, mb, kRDebug);
+    f16(d->hs, d->tw, mb, kRDebug);
+    for (int N : {d->qd, d->kd, d->ffn}) i4(N, d->hs, mb, kRDebug);
+    i4(d->hs, d->qd, mb, kRDebug);
+    i4(d->hs, d->ffn, mb, kRDebug);
   }
   return need;
-}
-
-int topk_slices(int width, int top, int* slice) {
-  int ns = (width + 4095) / 4096;
-  ns = std::min(ns, std::max(1, 4096 / top));
-  *slice = (width + ns - 1) / ns;
-  return ns;
 }
 
 void layer_range(const dflash* d, int l, long a, long* lo, long* n) {
@@ -326,6 +379,7 @@ const char* dflash_last_error(const dflash_t* d) {
 void dflash_destroy(dflash_t* d) {
   if (!d) return;
   (void)hipStreamSynchronize(d->st);
+  for (hipEvent_t e : d->tm.ev) (void)hipEventDestroy(e);
   for (void* p : d->allocs) (void)hipFree(p);
   delete d;
 }
@@ -445,8 +499,7 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   const int rep = d->nh / d->kv;
   const size_t slots = (size_t)d->kv * (kMaxChunks + 1) * rep;
   d->part_floats = partial_need(d);
-  int slice = 0;
-  const int ns = topk_slices(d->V, d->top, &slice);
+  const int ns = dfl::topk_slices(d->V);
   if (!rc) rc = dev_alloc(d, &d->h, 16 * hs, "scratch");
   if (!rc) rc = dev_alloc(d, &d->x, 16 * hs, "scratch");
   if (!rc) rc = dev_alloc(d, &d->dsum_a, 16 * d->P, "scratch");
@@ -468,8 +521,36 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   d->stage_cols = std::max(std::max(d->tw, d->ffn), std::max(d->qd, hs));
   if (!rc) rc = dev_alloc(d, &d->taps_a, (size_t)kSettleRows * d->stage_cols, "settle scratch");
   if (!rc) rc = dev_alloc(d, &d->t_a, (size_t)kSettleRows * hs, "settle scratch");
+  if (!rc) rc = dev_alloc(d, &d->tbuf, (size_t)kSettleRows * hs, "settle scratch");
+  if (!rc) rc = dev_alloc(d, &d->sqp, (size_t)kSettleRows * ((hs + 255) / 256), "norm scratch");
+  if (!rc) rc = dev_alloc(d, &d->tab, (size_t)d->top * (1 + 15 * d->top), "selector table");
   if (!rc) rc = hip_check(nullptr, hipDeviceSynchronize(), "create");
   return done(rc);
+}
+
+int dflash_set_timing(dflash_t* d, int on) {
+  if (!d) return DFLASH_EINVAL;
+  int rc = hip_check(d, hipStreamSynchronize(d->st), "set_timing");
+  auto& t = d->tm;
+  t.on = on != 0;
+  t.used = 0;
+  t.marks.clear();
+  std::fill(t.us, t.us + DFLASH_STAGES, 0.0);
+  std::fill(t.launches, t.launches + DFLASH_STAGES, 0);
+  t.blocks = t.settles = 0;
+  return rc;
+}
+
+int dflash_stage_times(const dflash_t* d, double* us, int64_t* launches, int64_t* blocks,
+                       int64_t* settles) {
+  if (!d) return DFLASH_EINVAL;
+  for (int i = 0; i < DFLASH_STAGES; ++i) {
+    if (us) us[i] = d->tm.us[i];
+    if (launches) launches[i] = d->tm.launches[i];
+  }
+  if (blocks) *blocks = d->tm.blocks;
+  if (settles) *settles = d->tm.settles;
+  return DFLASH_OK;
 }
 
 int dflash_sync(dflash_t* d) {
@@ -495,22 +576,29 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
   hipStream_t st = d->st;
   const int mb = (m + 15) / 16;
   dfl::to_a(st, taps, d->tw, m, d->tw, d->taps_a);
+  tm_mark(d, DFLASH_ST_S_TAPS);
   // t = fc · taps (f32 partials), then rms by hidden_norm into A-layout
-  const Split sf = split_for(d->hs / 16, kF16R, d->tw / 32, mb);
+  const Split sf = split_for(d->hs / 16, kRFc, d->tw / 32, mb, 16);
   const long ssf = (long)mb * 16 * d->hs;
-  dfl::gemm_f16(st, d->taps_a, d->tw, mb, d->fc, dfl::TileMap{d->hs / 16, d->hs / 16, 0, 0}, d->hs,
+  dfl::gemm_f16(st, kRFc, d->taps_a, d->tw, mb, d->fc, dfl::TileMap{d->hs / 16, d->hs / 16, 0, 0}, d->hs,
                 sf.S, sf.per, d->part, ssf);
-  dfl::sum_norm(st, d->part, sf.S, ssf, m, d->hs, d->hidden_norm, d->eps, d->t_a);
+  tm_mark(d, DFLASH_ST_S_FC);
+  dfl::rowsum_sq(st, d->part, sf.S, ssf, m, d->hs, d->tbuf, d->sqp);
+  tm_mark(d, DFLASH_ST_S_NORM);
+  dfl::norm_apply(st, d->tbuf, d->sqp, m, d->hs, d->hidden_norm, d->eps, nullptr, d->t_a);
+  tm_mark(d, DFLASH_ST_S_NORM);
   // K and V of every layer: the k and v tiles of each layer's q/k/v set
   const int kvt = 2 * d->kd / 16;
   const int N = d->L * 2 * d->kd;
-  const Split sk = split_for(d->L * kvt, kI4R, d->hs / 128, mb);
+  const Split sk = split_for(d->L * kvt, kRKv, d->hs / 128, mb, 4);
   const long ssk = (long)mb * 16 * N;
   dfl::TileMap map{d->L * kvt, kvt, d->qkv.tiles, d->qd / 16};
-  dfl::gemm_i4(st, d->t_a, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per, d->part,
+  dfl::gemm_i4(st, kRKv, d->t_a, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per, d->part,
                ssk);
+  tm_mark(d, DFLASH_ST_S_KV);
   dfl::settle_kv(st, d->part, sk.S, ssk, m, d->L, d->kv, d->hd, d->k_norm, d->inv, d->rot_dev,
                  pos0, d->eps, d->sk, d->sv, d->cap, row0);
+  tm_mark(d, DFLASH_ST_S_STORE);
   return launch_check(d, "settle");
 }
 
@@ -531,12 +619,16 @@ int dflash_settle(dflash_t* d, int64_t first_pos, int32_t n, const float* taps) 
                 len + (long)n, d->cap);
   d->first = first;
   d->len = len;
+  if (n == 0) return DFLASH_OK;
+  tm_begin(d);
   for (int done = 0; done < n; done += kSettleRows) {
     const int m = std::min(kSettleRows, n - done);
     const int rc = settle_pass(d, taps + (size_t)done * d->tw, m, first_pos + done, len + done);
     if (rc) return rc;
     d->len = len + done + m;
   }
+  tm_end(d);
+  d->tm.settles += d->tm.on;
   return DFLASH_OK;
 }
 
@@ -553,29 +645,37 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
   const int hs = d->hs, B = d->B;
   const float scale = std::pow((float)d->hd, -0.5f);
   const long ssd = 16L * d->P, ssq = 16L * (d->qd + 2 * d->kd), ssh = 16L * hs;
-  const Split spk = split_for(d->ptiles, kF16R, hs / 32, 1);
-  const Split sqk = split_for(d->qkv.tiles, kI4R, hs / 128, 1);
-  const Split so = split_for(hs / 16, kI4R, d->qd / 128, 1);
-  const Split sdn = split_for(hs / 16, kI4R, d->ffn / 128, 1);
+  const Split spk = split_for(d->ptiles, kRKproj, hs / 32, 1, 16);
+  const Split sqk = split_for(d->qkv.tiles, kRQkv, hs / 128, 1, 4);
+  const Split so = split_for(hs / 16, kRO, d->qd / 128, 1, 4);
+  const Split sdn = split_for(hs / 16, kRDown, d->ffn / 128, 1, 4);
   const size_t kp_layer = (size_t)d->ptiles * 16 * hs;
   const size_t i4l_qkv = (size_t)d->qkv.tiles * (hs / 128);
   const size_t i4l_o = (size_t)d->o.tiles * (d->qd / 128);
   const size_t i4l_gu = (size_t)d->gu.tiles * (hs / 128);
   const size_t i4l_dn = (size_t)d->down.tiles * (d->ffn / 128);
 
-  dfl::embed_norm(st, d->embed, anchor, d->mask, B, hs, d->in_norm, d->eps, d->h, d->x, d->xa);
+  tm_begin(d);
+  dfl::embed(st, d->embed, anchor, d->mask, B, hs, d->h, d->sqp);
+  tm_mark(d, DFLASH_ST_CONV);
+  dfl::norm_apply(st, d->h, d->sqp, B, hs, d->in_norm, d->eps, d->x, d->xa);
+  tm_mark(d, DFLASH_ST_CONV);
   for (int l = 0; l < d->L; ++l) {
     const float* ab = d->attn_base + (size_t)l * 2 * d->kn * hs;
     const float* mbase = d->mlp_base + (size_t)l * 2 * d->kn * hs;
     // attention: conv_in, q/k/v, norms + rotary
-    dfl::gemm_f16(st, d->xa, hs, 1, d->attn_kproj + l * kp_layer,
+    dfl::gemm_f16(st, kRKproj, d->xa, hs, 1, d->attn_kproj + l * kp_layer,
                   dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, spk.S, spk.per, d->part, ssd);
+    tm_mark(d, DFLASH_ST_KPROJ);
     dfl::conv0(st, d->x, d->part, spk.S, ssd, ab, B, hs, d->gs, d->kn, d->xca, d->dsum_a);
-    dfl::gemm_i4(st, d->xca, hs, 1, d->qkv.codes + i4l_qkv * 1024 * l, d->qkv.scales + i4l_qkv * 64 * l,
+    tm_mark(d, DFLASH_ST_CONV);
+    dfl::gemm_i4(st, kRQkv, d->xca, hs, 1, d->qkv.codes + i4l_qkv * 1024 * l, d->qkv.scales + i4l_qkv * 64 * l,
                  dfl::TileMap{d->qkv.tiles, d->qkv.tiles, 0, 0}, d->qd + 2 * d->kd, sqk.S, sqk.per,
                  d->part, ssq);
+    tm_mark(d, DFLASH_ST_QKV);
     dfl::qkv_post(st, d->part, sqk.S, ssq, B, d->nh, d->kv, d->hd, d->q_norm + (size_t)l * d->hd,
                   d->k_norm + (size_t)l * d->hd, d->inv, a, d->rot[l], d->eps, d->qa, d->kb, d->vb);
+    tm_mark(d, DFLASH_ST_QKPOST);
     // attention over the layer's context range and the block's rows
     long lo, n;
     layer_range(d, l, a, &lo, &n);
@@ -585,36 +685,48 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     dfl::attention(st, d->qa, d->sk + lrow * d->kd, d->sv + lrow * d->kd, d->kb, d->vb, B, d->nh,
                    d->kv, d->hd, (int)n, lo, a, d->windows[l], chunk, nchunks, scale, d->pacc,
                    d->pml);
+    tm_mark(d, DFLASH_ST_ATTN);
     dfl::attn_merge(st, d->pacc, d->pml, d->nh, d->kv, d->hd, nchunks, B, d->ya);
+    tm_mark(d, DFLASH_ST_ATTN);
     // o, conv_out into the residual, post-attention norm
-    dfl::gemm_i4(st, d->ya, d->qd, 1, d->o.codes + i4l_o * 1024 * l, d->o.scales + i4l_o * 64 * l,
+    dfl::gemm_i4(st, kRO, d->ya, d->qd, 1, d->o.codes + i4l_o * 1024 * l, d->o.scales + i4l_o * 64 * l,
                  dfl::TileMap{d->o.tiles, d->o.tiles, 0, 0}, hs, so.S, so.per, d->part, ssh);
-    dfl::conv1_norm(st, d->h, d->part, so.S, ssh, d->dsum_a, ab, B, hs, d->gs, d->kn,
-                    d->post_norm + (size_t)l * hs, d->eps, d->x, d->xa);
+    tm_mark(d, DFLASH_ST_O);
+    dfl::conv1(st, d->h, d->part, so.S, ssh, d->dsum_a, ab, B, hs, d->gs, d->kn, d->sqp);
+    tm_mark(d, DFLASH_ST_CONV);
+    dfl::norm_apply(st, d->h, d->sqp, B, hs, d->post_norm + (size_t)l * hs, d->eps, d->x, d->xa);
+    tm_mark(d, DFLASH_ST_CONV);
     // MLP, wrapped the same way
-    dfl::gemm_f16(st, d->xa, hs, 1, d->mlp_kproj + l * kp_layer,
+    dfl::gemm_f16(st, kRKproj, d->xa, hs, 1, d->mlp_kproj + l * kp_layer,
                   dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, spk.S, spk.per, d->part, ssd);
+    tm_mark(d, DFLASH_ST_KPROJ);
     dfl::conv0(st, d->x, d->part, spk.S, ssd, mbase, B, hs, d->gs, d->kn, d->xca, d->dsum_m);
+    tm_mark(d, DFLASH_ST_CONV);
     dfl::gemm_glu(st, d->xca, hs, d->gu.codes + i4l_gu * 1024 * l, d->gu.scales + i4l_gu * 64 * l,
                   d->ffn / 16, d->ma);
-    dfl::gemm_i4(st, d->ma, d->ffn, 1, d->down.codes + i4l_dn * 1024 * l,
+    tm_mark(d, DFLASH_ST_GLU);
+    dfl::gemm_i4(st, kRDown, d->ma, d->ffn, 1, d->down.codes + i4l_dn * 1024 * l,
                  d->down.scales + i4l_dn * 64 * l, dfl::TileMap{d->down.tiles, d->down.tiles, 0, 0},
                  hs, sdn.S, sdn.per, d->part, ssh);
+    tm_mark(d, DFLASH_ST_DOWN);
     const float* next = l + 1 < d->L ? d->in_norm + (size_t)(l + 1) * hs : d->norm;
-    dfl::conv1_norm(st, d->h, d->part, sdn.S, ssh, d->dsum_m, mbase, B, hs, d->gs, d->kn, next,
-                    d->eps, d->x, d->xa);
+    dfl::conv1(st, d->h, d->part, sdn.S, ssh, d->dsum_m, mbase, B, hs, d->gs, d->kn, d->sqp);
+    tm_mark(d, DFLASH_ST_CONV);
+    dfl::norm_apply(st, d->h, d->sqp, B, hs, next, d->eps, d->x, d->xa);
+    tm_mark(d, DFLASH_ST_CONV);
   }
   // head over rows 1..k and the selector projection
   float* lg = logits ? logits : d->logits;
   dfl::head_sel(st, d->xa, hs, d->head, width, k, lg, d->sel, d->rank, d->hp);
-  int slice = 0;
-  const int ns = topk_slices(width, d->top, &slice);
-  dfl::topk_slice(st, lg, k, width, d->top, slice, ns, d->cv, d->ci);
-  dfl::topk_merge(st, d->cv, d->ci, k, ns * d->top, d->top, cand, unary);
-  dfl::select_chain(st, cand, unary, d->hp + d->rank, k, d->top, d->rank, d->pbook, d->cbook,
-                    d->V, anchor, nullptr, score, chosen);
+  tm_mark(d, DFLASH_ST_HEAD);
+  dfl::select_all(st, lg, k, width, d->top, d->hp + d->rank, d->rank, d->pbook, d->cbook, d->V,
+                  anchor, nullptr, d->cv, d->ci, d->tab, cand, unary, score, chosen);
+  tm_mark(d, DFLASH_ST_SELECT);
   d->last_k = k;
-  return launch_check(d, "block");
+  const int rc = launch_check(d, "block");
+  tm_end(d);
+  d->tm.blocks += d->tm.on;
+  return rc;
 }
 
 // --------------------------------------------------------------- debug
@@ -688,15 +800,15 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
   if (cols > d->stage_cols) return fail(d, DFLASH_EINVAL, "matvec: matrix wider than the staging buffer");
   const int mb = (m + 15) / 16;
   dfl::to_a(d->st, x, cols, m, cols, d->taps_a);
-  const Split s = is_i4 ? split_for(map.ntiles, kI4R, cols / 128, mb)
-                        : split_for(map.ntiles, kF16R, cols / 32, mb);
+  const Split s = is_i4 ? split_for(map.ntiles, kRDebug, cols / 128, mb, 4)
+                        : split_for(map.ntiles, kRDebug, cols / 32, mb, 16);
   const long ss = (long)mb * 16 * rows;
   if ((long)s.S * ss > d->part_floats) return fail(d, DFLASH_EINVAL, "matvec: partials too large");
   if (is_i4)
-    dfl::gemm_i4(d->st, d->taps_a, cols, mb, static_cast<const uint8_t*>(codes), scales, map, rows,
+    dfl::gemm_i4(d->st, kRDebug, d->taps_a, cols, mb, static_cast<const uint8_t*>(codes), scales, map, rows,
                  s.S, s.per, d->part, ss);
   else
-    dfl::gemm_f16(d->st, d->taps_a, cols, mb, static_cast<const uint16_t*>(codes), map, rows, s.S,
+    dfl::gemm_f16(d->st, kRDebug, d->taps_a, cols, mb, static_cast<const uint16_t*>(codes), map, rows, s.S,
                   s.per, d->part, ss);
   dfl::sum_rows(d->st, d->part, s.S, ss, m, rows, y);
   return launch_check(d, "matvec");
@@ -759,12 +871,8 @@ int dflash_debug_select(dflash_t* d, const float* logits, const float* hp, int32
   if (k < 1 || k >= 16) return fail(d, DFLASH_EINVAL, "select: k must be in [1, 15]");
   if (width < d->top || width > d->V) return fail(d, DFLASH_EINVAL, "select: bad width");
   if (anchor < 0 || anchor >= d->V) return fail(d, DFLASH_EINVAL, "select: bad anchor");
-  int slice = 0;
-  const int ns = topk_slices(width, d->top, &slice);
-  dfl::topk_slice(d->st, logits, k, width, d->top, slice, ns, d->cv, d->ci);
-  dfl::topk_merge(d->st, d->cv, d->ci, k, ns * d->top, d->top, cand, unary);
-  dfl::select_chain(d->st, cand, unary, hp, k, d->top, d->rank, d->pbook, d->cbook, d->V,
-                    anchor, forced_prev, score, chosen);
+  dfl::select_all(d->st, logits, k, width, d->top, hp, d->rank, d->pbook, d->cbook, d->V, anchor,
+                  forced_prev, d->cv, d->ci, d->tab, cand, unary, score, chosen);
   return launch_check(d, "select");
 }
 

@@ -37,9 +37,10 @@ struct TileMap {
 };
 
 // GEMM launches: out[split][mb·16 + m][col] partial sums (f32), col < N.
-void gemm_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
+// R = row tiles per wave (1, 2 or 4); a workgroup covers 4·R tiles.
+void gemm_f16(hipStream_t st, int R, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
               TileMap map, int N, int splits, int steps_per_split, float* out, long split_stride);
-void gemm_i4(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint8_t* codes,
+void gemm_i4(hipStream_t st, int R, const uint16_t* xa, int K, int mblocks, const uint8_t* codes,
              const uint16_t* scales, TileMap map, int N, int splits, int spans_per_split,
              float* out, long split_stride);
 // gate/up with the SwiGLU epilogue: gate tiles [0, ftiles), up tiles
@@ -52,15 +53,17 @@ void head_sel(hipStream_t st, const uint16_t* xa, int K, const uint16_t* head, i
               int k, float* logits, const uint16_t* sel, int rank, float* hp);
 
 void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa);
-void sum_norm(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,
-              const float* w, float eps, uint16_t* xa);
-void embed_norm(hipStream_t st, const uint16_t* embed, int anchor, int mask, int rows, int hs,
-                const float* w, float eps, float* h, float* x, uint16_t* xa);
+// Row kernels: sqp holds each (row, 256-channel chunk)'s sum of squares.
+void rowsum_sq(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,
+               float* out, float* sqp);
+void norm_apply(hipStream_t st, const float* h, const float* sqp, int rows, int N, const float* w,
+                float eps, float* x, uint16_t* xa);
+void embed(hipStream_t st, const uint16_t* emb, int anchor, int mask, int rows, int hs, float* h,
+           float* sqp);
 void conv0(hipStream_t st, const float* x, const float* dpart, int splits, long split_stride,
            const float* base, int rows, int hs, int gs, int kn, uint16_t* xca, float* dsum);
-void conv1_norm(hipStream_t st, float* h, const float* opart, int splits, long split_stride,
-                const float* dsum, const float* base, int rows, int hs, int gs, int kn,
-                const float* w, float eps, float* x, uint16_t* xa);
+void conv1(hipStream_t st, float* h, const float* opart, int splits, long split_stride,
+           const float* dsum, const float* base, int rows, int hs, int gs, int kn, float* sqp);
 void qkv_post(hipStream_t st, const float* part, int splits, long split_stride, int rows, int nh,
               int kv, int hd, const float* q_norm, const float* k_norm, const float* inv_freq,
               long pos0, int rot, float eps, uint16_t* qa, float* kb, float* vb);
@@ -74,13 +77,14 @@ void attention(hipStream_t st, const uint16_t* qa, const float* sk, const float*
                float* pacc, float* pml);
 void attn_merge(hipStream_t st, const float* pacc, const float* pml, int nh, int kv, int hd,
                 int nchunks, int B, uint16_t* ya);
-void topk_slice(hipStream_t st, const float* logits, int k, int width, int top, int slice,
-                int nslices, float* cv, int* ci);
-void topk_merge(hipStream_t st, const float* cv, const int* ci, int k, int cnt, int top,
-                int* cand, float* unary);
-void select_chain(hipStream_t st, const int* cand, const float* unary, const float* hp, int k,
-                  int top, int rank, const uint16_t* pbook, const uint16_t* cbook, int vocab,
-                  int anchor, const int* forced_prev, float* score, int* chosen);
+// Selection (`top_k` + `select_with`) on logits [k][width] and hp rows
+// [k][rank]: per-slice candidates (cv/ci scratch [k][topk_slices(width)][top]),
+// then cand/unary, the score table (tab) and the chain (score, chosen).
+int topk_slices(int width);
+void select_all(hipStream_t st, const float* logits, int k, int width, int top, const float* hp,
+                int rank, const uint16_t* pbook, const uint16_t* cbook, int vocab, int anchor,
+                const int* forced, float* cv, int* ci, float* tab, int* cand, float* unary,
+                float* score, int* chosen);
 void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,
                 int rows, int K, float* out);
 void sum_rows(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,

@@ -12,6 +12,7 @@
 // dequantised weight q·s is used exactly. Accumulation is f32 throughout.
 #include "internal.h"
 
+#include <algorithm>
 #include <climits>
 #include <math.h>
 
@@ -56,6 +57,21 @@ __device__ float block_sum(float v, float* red) {
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
   return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Σ_s p[s·ss] over the K splits of a GEMM, four independent chains so the
+// loads are in flight together (fixed order: the same splits give the same sum).
+__device__ __forceinline__ float sum_splits(const float* __restrict__ p, int splits, long ss) {
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int s = 0;
+  for (; s + 4 <= splits; s += 4) {
+    a0 += p[(size_t)s * ss];
+    a1 += p[(size_t)(s + 1) * ss];
+    a2 += p[(size_t)(s + 2) * ss];
+    a3 += p[(size_t)(s + 3) * ss];
+  }
+  for (; s < splits; ++s) a0 += p[(size_t)s * ss];
+  return (a0 + a1) + (a2 + a3);
 }
 
 // Eight int4 codes of one I4T word → eight f16 integers in column order.
@@ -211,55 +227,60 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa
 }
 
 // gate/up over the full K, SwiGLU in the epilogue (`mlp`: silu(g)·u with
-// silu(a) = a/(1+e^−a)). Block b: waves 0, 1 take gate tiles 2b, 2b+1;
-// waves 2, 3 the up tiles of the same rows.
+// silu(a) = a/(1+e^−a)). Each wave owns one ffn tile: gate tile ft and up
+// tile ffn_tiles + ft of the stored matrix, so g and u meet in registers.
 __global__ __launch_bounds__(kThreads) void k_gemm_glu(const f16* __restrict__ xa, int K,
                                                        const uint4* __restrict__ codes,
                                                        const uint2* __restrict__ scales,
                                                        int ftiles, f16* __restrict__ ma) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int KT = K >> 7;
-  const int ft = 2 * blockIdx.x + (wave & 1);
-  const long st = wave < 2 ? ft : ftiles + ft;
+  const int ft = blockIdx.x * 4 + wave;
+  if (ft >= ftiles) return;
   const h8* xp = reinterpret_cast<const h8*>(xa) + lane;
-  const uint4* cp = codes + (size_t)st * KT * 64 + lane;
-  const uint2* scp = scales + (size_t)st * KT * 16 + (lane & 15);
-  f4 acc[1] = {(f4){0.f, 0.f, 0.f, 0.f}};
+  const uint4* cp[2] = {codes + (size_t)ft * KT * 64 + lane,
+                        codes + (size_t)(ftiles + ft) * KT * 64 + lane};
+  const uint2* scp[2] = {scales + (size_t)ft * KT * 16 + (lane & 15),
+                         scales + (size_t)(ftiles + ft) * KT * 16 + (lane & 15)};
+  f4 acc[2] = {(f4){0.f, 0.f, 0.f, 0.f}, (f4){0.f, 0.f, 0.f, 0.f}};
   int p = 0;
   for (; p + 2 <= KT; p += 2) {
-    uint4 c0[1] = {cp[(size_t)p * 64]}, c1[1] = {cp[(size_t)(p + 1) * 64]};
-    uint2 s0[1] = {scp[(size_t)p * 16]}, s1[1] = {scp[(size_t)(p + 1) * 16]};
+    uint4 c0[2], c1[2];
+    uint2 s0[2], s1[2];
     h8 a0[4], a1[4];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      c0[r] = cp[r][(size_t)p * 64];
+      c1[r] = cp[r][(size_t)(p + 1) * 64];
+      s0[r] = scp[r][(size_t)p * 16];
+      s1[r] = scp[r][(size_t)(p + 1) * 16];
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       a0[u] = xp[(size_t)(4 * p + u) * 64];
       a1[u] = xp[(size_t)(4 * p + 4 + u) * 64];
     }
-    i4_span<1>(c0, s0, a0, acc);
-    i4_span<1>(c1, s1, a1, acc);
+    i4_span<2>(c0, s0, a0, acc);
+    i4_span<2>(c1, s1, a1, acc);
   }
   if (p < KT) {
-    uint4 c0[1] = {cp[(size_t)p * 64]};
-    uint2 s0[1] = {scp[(size_t)p * 16]};
+    uint4 c0[2];
+    uint2 s0[2];
     h8 a0[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) a0[u] = xp[(size_t)(4 * p + u) * 64];
-    i4_span<1>(c0, s0, a0, acc);
-  }
-  __shared__ float up[2][16][17];
-  const int j = lane >> 4, n = lane & 15;
-  if (wave >= 2)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) up[wave - 2][4 * j + v][n] = acc[0][v];
-  __syncthreads();
-  if (wave < 2) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 4 * j + v;
-      const float g = acc[0][v];
-      const float val = g / (1.f + expf(-g)) * up[wave][m][n];
-      ma[a_idx(m, ft * 16 + n)] = (f16)val;
+    for (int r = 0; r < 2; ++r) {
+      c0[r] = cp[r][(size_t)p * 64];
+      s0[r] = scp[r][(size_t)p * 16];
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a0[u] = xp[(size_t)(4 * p + u) * 64];
+    i4_span<2>(c0, s0, a0, acc);
+  }
+  const int j = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float g = acc[0][v];
+    ma[a_idx(4 * j + v, ft * 16 + n)] = (f16)(g / (1.f + expf(-g)) * acc[1][v]);
   }
 }
 
@@ -344,119 +365,119 @@ __global__ __launch_bounds__(kThreads) void k_to_a(const float* __restrict__ x, 
   reinterpret_cast<h8*>(xa + (size_t)mb * 16 * K)[t] = v;
 }
 
-// `rms` of the split-summed rows → A-layout f16 (the settle's hidden norm).
-__global__ __launch_bounds__(kThreads) void k_sum_norm(const float* __restrict__ part, int splits,
-                                                       long ss, int N, const float* __restrict__ w,
-                                                       float eps, f16* __restrict__ xa) {
+// The row kernels below split each row into chunks of kChunk channels, one
+// workgroup per (chunk, row). A norm is two launches: the producer writes
+// the rows and each chunk's sum of squares, `k_norm_apply` finishes `rms`.
+static constexpr int kChunk = 256;
+
+// Split-summed rows (the settle's t = fc·taps) and each chunk's Σv².
+__global__ __launch_bounds__(kThreads) void k_rowsum_sq(const float* __restrict__ part, int splits,
+                                                        long ss, int N, float* __restrict__ out,
+                                                        float* __restrict__ sqp, int nchunk) {
   __shared__ float red[4];
-  const int row = blockIdx.x;
-  const float* pr = part + (size_t)row * N;
-  float sq = 0.f;
-  for (int i = threadIdx.x; i < N; i += kThreads) {
-    float v = 0.f;
-    for (int s = 0; s < splits; ++s) v += pr[(size_t)s * ss + i];
-    sq += v * v;
+  const int r = blockIdx.y, c = blockIdx.x, i = c * kChunk + threadIdx.x;
+  float v = 0.f;
+  if (i < N) {
+    v = sum_splits(part + (size_t)r * N + i, splits, ss);
+    out[(size_t)r * N + i] = v;
   }
-  sq = block_sum(sq, red);
-  const float scale = 1.f / sqrtf(sq / N + eps);
-  f16* out = xa + (size_t)(row >> 4) * 16 * N;
-  for (int i = threadIdx.x; i < N; i += kThreads) {
-    float v = 0.f;
-    for (int s = 0; s < splits; ++s) v += pr[(size_t)s * ss + i];
-    out[a_idx(row & 15, i)] = (f16)(v * scale * w[i]);
-  }
+  const float sq = block_sum(v * v, red);
+  if (threadIdx.x == 0) sqp[(size_t)r * nchunk + c] = sq;
 }
 
-// Rows [E[anchor], E[mask]…] and their `rms` by the first layer's gain.
-__global__ __launch_bounds__(kThreads) void k_embed_norm(const f16* __restrict__ embed, int anchor,
-                                                         int mask, int hs,
+// `rms`: y = h·(1/sqrt(Σh²/N + eps))·w for one chunk of row r, the row's
+// Σh² gathered from its chunks; y to f32 (if x) and to A-layout f16.
+__global__ __launch_bounds__(kThreads) void k_norm_apply(const float* __restrict__ h,
+                                                         const float* __restrict__ sqp,
+                                                         int nchunk, int N,
                                                          const float* __restrict__ w, float eps,
-                                                         float* __restrict__ h,
                                                          float* __restrict__ x,
                                                          f16* __restrict__ xa) {
-  __shared__ float red[4];
-  const int r = blockIdx.x;
-  const f16* e = embed + (size_t)(r == 0 ? anchor : mask) * hs;
-  float sq = 0.f;
-  for (int i = threadIdx.x; i < hs; i += kThreads) {
-    const float v = (float)e[i];
-    h[(size_t)r * hs + i] = v;
-    sq += v * v;
-  }
-  sq = block_sum(sq, red);
-  const float scale = 1.f / sqrtf(sq / hs + eps);
-  for (int i = threadIdx.x; i < hs; i += kThreads) {
-    const float y = (float)e[i] * scale * w[i];
-    x[(size_t)r * hs + i] = y;
-    xa[a_idx(r, i)] = (f16)y;
-  }
+  __shared__ float part[kThreads];
+  const int r = blockIdx.y, c = blockIdx.x, i = c * kChunk + threadIdx.x;
+  if (threadIdx.x < nchunk) part[threadIdx.x] = sqp[(size_t)r * nchunk + threadIdx.x];
+  __syncthreads();
+  float ss = 0.f;
+  for (int q = 0; q < nchunk; ++q) ss += part[q];
+  const float scale = 1.f / sqrtf(ss / N + eps);
+  if (i >= N) return;
+  const float y = h[(size_t)r * N + i] * scale * w[i];
+  if (x) x[(size_t)r * N + i] = y;
+  xa[(size_t)(r >> 4) * 16 * N + a_idx(r & 15, i)] = (f16)y;
 }
 
-// Conv stage 0 of row r (`conv`): xc[r][i] = Σ_{o ≤ min(kn−1, r)}
-// (base[0][o][i] + d[r][0][o][i/gs])·x[r−o][i]. Also keeps row r's summed
-// kernel projection (both stages) for stage 1.
+// The block's rows [E[anchor], E[mask]…] (f16 → f32) and each chunk's Σh².
+__global__ __launch_bounds__(kThreads) void k_embed(const f16* __restrict__ embed, int anchor,
+                                                    int mask, int hs, float* __restrict__ h,
+                                                    float* __restrict__ sqp, int nchunk) {
+  __shared__ float red[4];
+  const int r = blockIdx.y, c = blockIdx.x, i = c * kChunk + threadIdx.x;
+  float v = 0.f;
+  if (i < hs) {
+    v = (float)embed[(size_t)(r == 0 ? anchor : mask) * hs + i];
+    h[(size_t)r * hs + i] = v;
+  }
+  const float sq = block_sum(v * v, red);
+  if (threadIdx.x == 0) sqp[(size_t)r * nchunk + c] = sq;
+}
+
+// Conv stage 0 (`conv`) of row r over a run of whole channel groups:
+// xc[r][i] = Σ_{o ≤ min(kn−1, r)} (base[0][o][i] + d[r][0][o][i/gs])·x[r−o][i].
+// The split-summed kernel projection of these groups, both stages, is kept
+// for stage 1.
 __global__ __launch_bounds__(kThreads) void k_conv0(const float* __restrict__ x,
                                                     const float* __restrict__ dpart, int splits,
                                                     long ss, const float* __restrict__ base,
-                                                    int hs, int gs, int kn, f16* __restrict__ xca,
+                                                    int hs, int gs, int kn, int gpw,
+                                                    f16* __restrict__ xca,
                                                     float* __restrict__ dsum) {
-  extern __shared__ float dl[];
-  const int r = blockIdx.x;
+  extern __shared__ float dl[];  // [2·kn][ng]
+  const int r = blockIdx.y;
   const int G = hs / gs, P = 2 * kn * G;
-  for (int i = threadIdx.x; i < P; i += kThreads) {
-    float v = 0.f;
-    for (int s = 0; s < splits; ++s) v += dpart[(size_t)s * ss + (size_t)r * P + i];
-    dl[i] = v;
-    dsum[(size_t)r * P + i] = v;
+  const int g0 = blockIdx.x * gpw, ng = min(G, g0 + gpw) - g0;
+  for (int e = threadIdx.x; e < 2 * kn * ng; e += kThreads) {
+    const int idx = (e / ng) * G + g0 + e % ng;
+    const float v = sum_splits(dpart + (size_t)r * P + idx, splits, ss);
+    dl[e] = v;
+    dsum[(size_t)r * P + idx] = v;
   }
   __syncthreads();
   const int taps = min(kn, r + 1);
-  for (int i = threadIdx.x; i < hs; i += kThreads) {
-    const int g = i / gs;
+  for (int i = g0 * gs + threadIdx.x; i < (g0 + ng) * gs; i += kThreads) {
+    const int g = i / gs - g0;
     float acc = 0.f;
     for (int o = 0; o < taps; ++o)
-      acc += (base[(size_t)o * hs + i] + dl[o * G + g]) * x[(size_t)(r - o) * hs + i];
+      acc += (base[(size_t)o * hs + i] + dl[o * ng + g]) * x[(size_t)(r - o) * hs + i];
     xca[a_idx(r, i)] = (f16)acc;
   }
 }
 
-// Conv stage 1 of the sub-layer's output into the residual, then the next
-// `rms`: h[r] += Σ_o (base[1][o] + d[r][1][o][g])·out[r−o]; x = rms(h[r], w).
-__global__ __launch_bounds__(kThreads) void k_conv1_norm(float* __restrict__ h,
-                                                         const float* __restrict__ opart,
-                                                         int splits, long ss,
-                                                         const float* __restrict__ dsum,
-                                                         const float* __restrict__ base, int hs,
-                                                         int gs, int kn,
-                                                         const float* __restrict__ w, float eps,
-                                                         float* __restrict__ x,
-                                                         f16* __restrict__ xa) {
+// Conv stage 1 of the sub-layer's output into the residual:
+// h[r][i] += Σ_o (base[1][o][i] + d[r][1][o][i/gs])·out[r−o][i], out being
+// the split-summed GEMM output; each chunk's Σh² of the new rows.
+__global__ __launch_bounds__(kThreads) void k_conv1(float* __restrict__ h,
+                                                    const float* __restrict__ opart, int splits,
+                                                    long ss, const float* __restrict__ dsum,
+                                                    const float* __restrict__ base, int hs,
+                                                    int gs, int kn, float* __restrict__ sqp,
+                                                    int nchunk) {
   __shared__ float red[4];
-  const int r = blockIdx.x;
+  const int r = blockIdx.y, c = blockIdx.x, i = c * kChunk + threadIdx.x;
   const int G = hs / gs, P = 2 * kn * G;
-  const int taps = min(kn, r + 1);
-  const float* b1 = base + (size_t)kn * hs;
-  const float* d1 = dsum + (size_t)r * P + (size_t)kn * G;
-  float sq = 0.f;
-  for (int i = threadIdx.x; i < hs; i += kThreads) {
-    const int g = i / gs;
+  float hn = 0.f;
+  if (i < hs) {
+    const int taps = min(kn, r + 1), g = i / gs;
+    const float* b1 = base + (size_t)kn * hs;
+    const float* d1 = dsum + (size_t)r * P + (size_t)kn * G;
+    float ov[16];
+    for (int o = 0; o < taps; ++o) ov[o] = sum_splits(opart + (size_t)(r - o) * hs + i, splits, ss);
     float acc = 0.f;
-    for (int o = 0; o < taps; ++o) {
-      float ov = 0.f;
-      for (int s = 0; s < splits; ++s) ov += opart[(size_t)s * ss + (size_t)(r - o) * hs + i];
-      acc += (b1[(size_t)o * hs + i] + d1[o * G + g]) * ov;
-    }
-    const float hn = h[(size_t)r * hs + i] + acc;
+    for (int o = 0; o < taps; ++o) acc += (b1[(size_t)o * hs + i] + d1[o * G + g]) * ov[o];
+    hn = h[(size_t)r * hs + i] + acc;
     h[(size_t)r * hs + i] = hn;
-    sq += hn * hn;
   }
-  sq = block_sum(sq, red);
-  const float scale = 1.f / sqrtf(sq / hs + eps);
-  for (int i = threadIdx.x; i < hs; i += kThreads) {
-    const float y = h[(size_t)r * hs + i] * scale * w[i];
-    x[(size_t)r * hs + i] = y;
-    xa[a_idx(r, i)] = (f16)y;
-  }
+  const float sq = block_sum(hn * hn, red);
+  if (threadIdx.x == 0) sqp[(size_t)r * nchunk + c] = sq;
 }
 
 // One head of one row: split-summed values at columns col0 + i and
@@ -472,11 +493,10 @@ __device__ __forceinline__ Pairs load_pairs(const float* part, int splits, long 
   for (int c = 0; c < 2; ++c) {
     const int i = threadIdx.x + 64 * c;
     p.lo[c] = p.hi[c] = 0.f;
-    if (i < half)
-      for (int s = 0; s < splits; ++s) {
-        p.lo[c] += part[(size_t)s * ss + base + i];
-        p.hi[c] += part[(size_t)s * ss + base + i + half];
-      }
+    if (i < half) {
+      p.lo[c] = sum_splits(part + base + i, splits, ss);
+      p.hi[c] = sum_splits(part + base + i + half, splits, ss);
+    }
   }
   return p;
 }
@@ -702,172 +722,213 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa,
   if (j == 0) pml[slot * 16 + r] = make_float2(m_run, l_run);
 }
 
-// Softmax-merge of the chunks of one (q head, row) → y in A-layout f16.
-__global__ void k_attn_merge(const float* __restrict__ pacc, const float2* __restrict__ pml,
-                             int nh, int kv, int hd, int nchunks, f16* __restrict__ ya) {
-  const int hq = blockIdx.x, r = blockIdx.y, d = threadIdx.x;
-  const int rep = nh / kv, g = hq / rep, qi = hq % rep;
-  float M = -INFINITY;
-  for (int c = 0; c <= nchunks; ++c)
-    M = fmaxf(M, pml[(((size_t)g * (nchunks + 1) + c) * rep + qi) * 16 + r].x);
-  float L = 0.f, y = 0.f;
-  for (int c = 0; c <= nchunks; ++c) {
-    const size_t slot = ((size_t)g * (nchunks + 1) + c) * rep + qi;
-    const float2 ml = pml[slot * 16 + r];
-    if (ml.x == -INFINITY) continue;
-    const float f = expf(ml.x - M);
-    L += ml.y * f;
-    y += pacc[(slot * 16 + r) * hd + d] * f;
+// Softmax-merge of the chunks of one (q head, row) → y in A-layout f16:
+// y = Σ_c acc_c·e^{m_c − M} / Σ_c l_c·e^{m_c − M}, M the largest chunk max.
+// One thread per chunk forms the weights, one thread per dimension sums.
+__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pacc,
+                                                    const float2* __restrict__ pml, int nh,
+                                                    int kv, int hd, int nchunks,
+                                                    f16* __restrict__ ya) {
+  __shared__ float fw[256], red[4], redl[4];
+  const int hq = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
+  const int rep = nh / kv, g = hq / rep, qi = hq % rep, nc = nchunks + 1;
+  const size_t slot0 = (size_t)g * nc * rep + qi;  // chunk c is slot slot0 + c·rep
+  float2 ml = make_float2(-INFINITY, 0.f);
+  if (t < nc) ml = pml[(slot0 + (size_t)t * rep) * 16 + r];
+  float m = ml.x;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  float M = red[0];
+  for (int w = 1; w < nw; ++w) M = fmaxf(M, red[w]);
+  const float f = (t < nc && ml.x != -INFINITY) ? expf(ml.x - M) : 0.f;
+  if (t < nc) fw[t] = f;
+  const float l = wave_sum(ml.y * f);
+  if (lane == 0) redl[wave] = l;
+  __syncthreads();
+  float L = 0.f;
+  for (int w = 0; w < nw; ++w) L += redl[w];
+  if (t >= hd) return;
+  float y0 = 0.f, y1 = 0.f;
+  int c = 0;
+  for (; c + 2 <= nc; c += 2) {
+    y0 += pacc[((slot0 + (size_t)c * rep) * 16 + r) * hd + t] * fw[c];
+    y1 += pacc[((slot0 + (size_t)(c + 1) * rep) * 16 + r) * hd + t] * fw[c + 1];
   }
-  ya[a_idx(r, hq * hd + d)] = (f16)(y / L);
+  if (c < nc) y0 += pacc[((slot0 + (size_t)c * rep) * 16 + r) * hd + t] * fw[c];
+  ya[a_idx(r, hq * hd + t)] = (f16)((y0 + y1) / L);
 }
 
 // ------------------------------------------------------- top-k, selector
 
+// `top_k`'s order: the larger value first, the smaller index among equals.
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
-// Exact top-`top` (value desc, index asc) of cnt pairs in LDS; the taken
-// entry is retired each round. 256 threads. Writes out_v/out_i[0..top).
-__device__ void block_topk(float* sv, int* si, int cnt, int top, float* out_v, int* out_i) {
-  __shared__ float rv[4];
-  __shared__ int ri[4], ro[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float bv = -INFINITY;
-  int bi = INT_MAX, bslot = -1;
+// Exact first `want` entries in `top_k` order of up to 64·VPL (value, index)
+// pairs held VPL per lane (entry u of lane l is pair l + 64u), by `want`
+// rounds of a wave-wide arg-best in which the winning lane retires its entry.
+// Lane 0 writes the results to out_v/out_i.
+template <int VPL>
+__device__ void wave_select(float (&v)[VPL], int (&ix)[VPL], int want, float* out_v,
+                            int* out_i) {
+  const int lane = threadIdx.x & 63;
+  uint64_t taken = 0;
+  float bv;
+  int bi, bs;
   auto rescan = [&]() {
     bv = -INFINITY;
     bi = INT_MAX;
-    bslot = -1;
-    for (int e = tid; e < cnt; e += kThreads)
-      if (better(sv[e], si[e], bv, bi)) {
-        bv = sv[e];
-        bi = si[e];
-        bslot = e;
+    bs = -1;
+#pragma unroll
+    for (int u = 0; u < VPL; ++u)
+      if (!((taken >> u) & 1) && better(v[u], ix[u], bv, bi)) {
+        bv = v[u];
+        bi = ix[u];
+        bs = u;
       }
   };
   rescan();
-  for (int it = 0; it < top; ++it) {
-    float v = bv;
-    int i = bi, ow = tid;
+  for (int it = 0; it < want; ++it) {
+    float wv = bv;
+    int wi = bi, wl = lane;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-      const float v2 = __shfl_xor(v, o, 64);
-      const int i2 = __shfl_xor(i, o, 64), ow2 = __shfl_xor(ow, o, 64);
-      if (better(v2, i2, v, i)) {
-        v = v2;
-        i = i2;
-        ow = ow2;
+      const float v2 = __shfl_xor(wv, o, 64);
+      const int i2 = __shfl_xor(wi, o, 64), l2 = __shfl_xor(wl, o, 64);
+      if (better(v2, i2, wv, wi) || (v2 == wv && i2 == wi && l2 < wl)) {
+        wv = v2;
+        wi = i2;
+        wl = l2;
       }
     }
     if (lane == 0) {
-      rv[wave] = v;
-      ri[wave] = i;
-      ro[wave] = ow;
+      out_v[it] = wv;
+      out_i[it] = wi;
     }
-    __syncthreads();
-    float V = rv[0];
-    int I = ri[0], OW = ro[0];
-    for (int w = 1; w < 4; ++w)
-      if (better(rv[w], ri[w], V, I)) {
-        V = rv[w];
-        I = ri[w];
-        OW = ro[w];
-      }
-    if (tid == 0) {
-      out_v[it] = V;
-      out_i[it] = I;
-    }
-    if (tid == OW && bslot >= 0) {
-      sv[bslot] = -INFINITY;
-      si[bslot] = INT_MAX;
+    if (lane == wl && bs >= 0) {
+      taken |= 1ull << bs;
       rescan();
     }
-    __syncthreads();
   }
 }
+
+// Each wave takes a slice of 64·kSliceVPL logits of one row and writes its
+// exact top `top` candidates (value, index) for the merge.
+static constexpr int kSliceVPL = 32;
 
 __global__ __launch_bounds__(kThreads) void k_topk_slice(const float* __restrict__ logits,
-                                                         int width, int top, int slice,
-                                                         int nslices, float* __restrict__ cv,
+                                                         int width, int top, int nslices,
+                                                         float* __restrict__ cv,
                                                          int* __restrict__ ci) {
-  extern __shared__ float lds[];
-  float* sv = lds;
-  int* si = reinterpret_cast<int*>(lds + slice);
-  const int j = blockIdx.y, sl = blockIdx.x;
-  const int b0 = sl * slice, cnt = max(0, min(slice, width - b0));
-  const float* row = logits + (size_t)j * width + b0;
-  for (int e = threadIdx.x; e < cnt; e += kThreads) {
-    sv[e] = row[e];
-    si[e] = b0 + e;
+  const int lane = threadIdx.x & 63, j = blockIdx.y;
+  const int sl = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (sl >= nslices) return;
+  const int b0 = sl * 64 * kSliceVPL;
+  const float* row = logits + (size_t)j * width;
+  float v[kSliceVPL];
+  int ix[kSliceVPL];
+#pragma unroll
+  for (int u = 0; u < kSliceVPL; ++u) {
+    const int e = b0 + lane + 64 * u;
+    v[u] = e < width ? row[e] : -INFINITY;
+    ix[u] = e < width ? e : INT_MAX;
   }
-  __syncthreads();
   const size_t o = ((size_t)j * nslices + sl) * top;
-  block_topk(sv, si, cnt, top, cv + o, ci + o);
+  wave_select<kSliceVPL>(v, ix, top, cv + o, ci + o);
 }
 
-__global__ __launch_bounds__(kThreads) void k_topk_merge(const float* __restrict__ cv,
-                                                         const int* __restrict__ ci, int cnt,
-                                                         int top, int* __restrict__ cand,
-                                                         float* __restrict__ unary) {
-  extern __shared__ float lds[];
-  float* sv = lds;
-  int* si = reinterpret_cast<int*>(lds + cnt);
-  const int j = blockIdx.x;
-  for (int e = threadIdx.x; e < cnt; e += kThreads) {
-    sv[e] = cv[(size_t)j * cnt + e];
-    si[e] = ci[(size_t)j * cnt + e];
+// Row j's candidates: the exact top `top` of the slices' candidates (wave 0),
+// and row j−1's (wave 1, j ≥ 1); then the scores of row j's candidates
+// under row j−1's candidate tp (or the anchor, or forced[j]) as predecessor,
+// `select_with`: unary + Σ_q (P[prev][q]·hp[j][q])·C[tok][q]. Block (j, tp);
+// block (j, 0) also writes cand and unary of row j.
+static constexpr int kMergeVPL = 64;
+
+__global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ cv,
+                                               const int* __restrict__ ci, int cnt, int top,
+                                               const float* __restrict__ hp, int rank,
+                                               const f16* __restrict__ pbook,
+                                               const f16* __restrict__ cbook, int vocab, int anchor,
+                                               const int* __restrict__ forced,
+                                               int* __restrict__ cand, float* __restrict__ unary,
+                                               float* __restrict__ tab) {
+  __shared__ float uv[2][32];
+  __shared__ int uc[2][32];
+  const int j = blockIdx.x, tp = blockIdx.y, tpn = gridDim.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (j == 0 && tp > 0) return;
+  const int row = j - wave;  // wave 0: row j, wave 1: row j−1
+  const bool need = wave == 0 || (j > 0 && !forced);
+  if (need) {
+    float v[kMergeVPL];
+    int ix[kMergeVPL];
+#pragma unroll
+    for (int u = 0; u < kMergeVPL; ++u) {
+      const int e = lane + 64 * u;
+      v[u] = e < cnt ? cv[(size_t)row * cnt + e] : -INFINITY;
+      ix[u] = e < cnt ? ci[(size_t)row * cnt + e] : INT_MAX;
+    }
+    wave_select<kMergeVPL>(v, ix, wave == 0 ? top : tp + 1, uv[wave], uc[wave]);
   }
   __syncthreads();
-  block_topk(sv, si, cnt, top, unary + (size_t)j * top, cand + (size_t)j * top);
+  if (wave == 0 && tp == 0 && lane < top) {
+    cand[(size_t)j * top + lane] = uc[0][lane];
+    unary[(size_t)j * top + lane] = uv[0][lane];
+  }
+  if (wave != 0) return;
+  const int prev = j == 0 ? anchor : (forced ? forced[j] : uc[1][tp]);
+  const bool okp = prev >= 0 && prev < vocab;
+  float pc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int q = lane + 64 * c;
+    pc[c] = (okp && q < rank) ? (float)pbook[(size_t)prev * rank + q] * hp[(size_t)j * rank + q] : 0.f;
+  }
+  float* out = tab + (j == 0 ? 0 : top + ((size_t)(j - 1) * tpn + tp) * top);
+  for (int t0 = 0; t0 < top; t0 += 8) {
+    float part[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = t0 + u;
+      const int tok = t < top ? uc[0][t] : -1;
+      const bool ok = okp && tok >= 0 && tok < vocab;
+      part[u] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int q = lane + 64 * c;
+        if (ok && q < rank) part[u] += pc[c] * (float)cbook[(size_t)tok * rank + q];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = t0 + u;
+      const float dot = wave_sum(part[u]);
+      if (lane == 0 && t < top) {
+        const int tok = uc[0][t];
+        out[t] = (okp && tok >= 0 && tok < vocab) ? uv[0][t] + dot : -INFINITY;
+      }
+    }
+  }
 }
 
-// `select_with`'s chain. Every (row j, predecessor candidate tp, candidate t)
-// score unary + Σ_r (P[prev]·hp[j])[r]·C[tok][r] is formed in parallel (the
-// predecessor of row j ≥ 1 is one of row j−1's candidates), then one thread
-// walks the rows keeping the first strict maximum.
-__global__ __launch_bounds__(kThreads) void k_select(const int* __restrict__ cand,
-                                                     const float* __restrict__ unary,
-                                                     const float* __restrict__ hp, int k, int top,
-                                                     int rank, const f16* __restrict__ pbook,
-                                                     const f16* __restrict__ cbook, int vocab,
-                                                     int anchor, const int* __restrict__ forced,
-                                                     float* __restrict__ score,
-                                                     int* __restrict__ chosen) {
-  extern __shared__ float tab[];
-  const int tpn = forced ? 1 : top;
+// The chain: row by row, the first candidate with the largest score under
+// the predecessor chosen before it.
+__global__ __launch_bounds__(kThreads) void k_chain(const float* __restrict__ tab,
+                                                    const int* __restrict__ cand, int k, int top,
+                                                    int tpn, float* __restrict__ score,
+                                                    int* __restrict__ chosen) {
+  extern __shared__ float lt[];
   const int total = top + (k - 1) * tpn * top;
-  for (int e = threadIdx.x; e < total; e += kThreads) {
-    int j, tp, t;
-    if (e < top) {
-      j = 0;
-      tp = 0;
-      t = e;
-    } else {
-      const int f = e - top;
-      j = 1 + f / (tpn * top);
-      tp = (f / top) % tpn;
-      t = f % top;
-    }
-    const int prev = j == 0 ? anchor : (forced ? forced[j] : cand[(size_t)(j - 1) * top + tp]);
-    const int tok = cand[(size_t)j * top + t];
-    if (prev < 0 || prev >= vocab || tok < 0 || tok >= vocab) {  // no such token: never chosen
-      tab[e] = -INFINITY;
-      continue;
-    }
-    const f16* P = pbook + (size_t)prev * rank;
-    const f16* C = cbook + (size_t)tok * rank;
-    const float* H = hp + (size_t)j * rank;
-    float dot = 0.f;
-    for (int q = 0; q < rank; ++q) dot += ((float)P[q] * H[q]) * (float)C[q];
-    tab[e] = unary[(size_t)j * top + t] + dot;
-  }
+  for (int e = threadIdx.x; e < total; e += kThreads) lt[e] = tab[e];
   __syncthreads();
   if (threadIdx.x != 0) return;
   int tp = 0;
   for (int j = 0; j < k; ++j) {
-    const float* row = tab + (j == 0 ? 0 : top + (size_t)(j - 1) * tpn * top + (size_t)tp * top);
+    const float* row = lt + (j == 0 ? 0 : top + ((size_t)(j - 1) * tpn + tp) * top);
     float best = -INFINITY;
     int bt = 0;
     for (int t = 0; t < top; ++t) {
@@ -878,7 +939,7 @@ __global__ __launch_bounds__(kThreads) void k_select(const int* __restrict__ can
       }
     }
     chosen[j] = cand[(size_t)j * top + bt];
-    tp = forced ? 0 : bt;
+    tp = tpn == 1 ? 0 : bt;
   }
 }
 
@@ -903,9 +964,7 @@ __global__ void k_sum_rows(const float* __restrict__ part, int splits, long ss, 
                            float* __restrict__ out) {
   const long idx = (long)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= (long)rows * N) return;
-  float v = 0.f;
-  for (int s = 0; s < splits; ++s) v += part[(size_t)s * ss + idx];
-  out[idx] = v;
+  out[idx] = sum_splits(part + idx, splits, ss);
 }
 
 // ------------------------------------------------------------- launchers
@@ -920,27 +979,44 @@ static void launch_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, c
                                            reinterpret_cast<const f16*>(w), map, N, sps, out, ss);
 }
 
-void gemm_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
+void gemm_f16(hipStream_t st, int R, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
               TileMap map, int N, int splits, int sps, float* out, long ss) {
-  launch_f16<2>(st, xa, K, mblocks, w, map, N, splits, sps, out, ss);
+  if (R == 1)
+    launch_f16<1>(st, xa, K, mblocks, w, map, N, splits, sps, out, ss);
+  else if (R == 2)
+    launch_f16<2>(st, xa, K, mblocks, w, map, N, splits, sps, out, ss);
+  else
+    launch_f16<4>(st, xa, K, mblocks, w, map, N, splits, sps, out, ss);
 }
 
-void gemm_i4(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint8_t* codes,
-             const uint16_t* scales, TileMap map, int N, int splits, int pps, float* out,
-             long ss) {
-  dim3 grid(cdiv(map.ntiles, 4), splits, mblocks);
-  k_gemm_i4<1><<<grid, kThreads, 0, st>>>(reinterpret_cast<const f16*>(xa), K,
+template <int R>
+static void launch_i4(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint8_t* codes,
+                      const uint16_t* scales, TileMap map, int N, int splits, int pps, float* out,
+                      long ss) {
+  dim3 grid(cdiv(map.ntiles, 4 * R), splits, mblocks);
+  k_gemm_i4<R><<<grid, kThreads, 0, st>>>(reinterpret_cast<const f16*>(xa), K,
                                           reinterpret_cast<const uint4*>(codes),
                                           reinterpret_cast<const uint2*>(scales), map, N, pps, out,
                                           ss);
 }
 
+void gemm_i4(hipStream_t st, int R, const uint16_t* xa, int K, int mblocks, const uint8_t* codes,
+             const uint16_t* scales, TileMap map, int N, int splits, int pps, float* out,
+             long ss) {
+  if (R == 1)
+    launch_i4<1>(st, xa, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
+  else if (R == 2)
+    launch_i4<2>(st, xa, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
+  else
+    launch_i4<4>(st, xa, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
+}
+
 void gemm_glu(hipStream_t st, const uint16_t* xa, int K, const uint8_t* codes,
               const uint16_t* scales, int ftiles, uint16_t* ma) {
-  k_gemm_glu<<<ftiles / 2, kThreads, 0, st>>>(reinterpret_cast<const f16*>(xa), K,
-                                              reinterpret_cast<const uint4*>(codes),
-                                              reinterpret_cast<const uint2*>(scales), ftiles,
-                                              reinterpret_cast<f16*>(ma));
+  k_gemm_glu<<<cdiv(ftiles, 4), kThreads, 0, st>>>(reinterpret_cast<const f16*>(xa), K,
+                                                   reinterpret_cast<const uint4*>(codes),
+                                                   reinterpret_cast<const uint2*>(scales), ftiles,
+                                                   reinterpret_cast<f16*>(ma));
 }
 
 void head_sel(hipStream_t st, const uint16_t* xa, int K, const uint16_t* head, int width, int k,
@@ -957,29 +1033,39 @@ void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa) {
   k_to_a<<<grid, kThreads, 0, st>>>(x, ld, m, K, reinterpret_cast<f16*>(xa));
 }
 
-void sum_norm(hipStream_t st, const float* part, int splits, long ss, int rows, int N,
-              const float* w, float eps, uint16_t* xa) {
-  k_sum_norm<<<rows, kThreads, 0, st>>>(part, splits, ss, N, w, eps, reinterpret_cast<f16*>(xa));
+void rowsum_sq(hipStream_t st, const float* part, int splits, long ss, int rows, int N,
+               float* out, float* sqp) {
+  const int nch = cdiv(N, kChunk);
+  k_rowsum_sq<<<dim3(nch, rows), kThreads, 0, st>>>(part, splits, ss, N, out, sqp, nch);
 }
 
-void embed_norm(hipStream_t st, const uint16_t* embed, int anchor, int mask, int rows, int hs,
-                const float* w, float eps, float* h, float* x, uint16_t* xa) {
-  k_embed_norm<<<rows, kThreads, 0, st>>>(reinterpret_cast<const f16*>(embed), anchor, mask, hs, w,
-                                          eps, h, x, reinterpret_cast<f16*>(xa));
+void norm_apply(hipStream_t st, const float* h, const float* sqp, int rows, int N, const float* w,
+                float eps, float* x, uint16_t* xa) {
+  const int nch = cdiv(N, kChunk);
+  k_norm_apply<<<dim3(nch, rows), kThreads, 0, st>>>(h, sqp, nch, N, w, eps, x,
+                                                     reinterpret_cast<f16*>(xa));
+}
+
+void embed(hipStream_t st, const uint16_t* emb, int anchor, int mask, int rows, int hs, float* h,
+           float* sqp) {
+  const int nch = cdiv(hs, kChunk);
+  k_embed<<<dim3(nch, rows), kThreads, 0, st>>>(reinterpret_cast<const f16*>(emb), anchor, mask,
+                                                hs, h, sqp, nch);
 }
 
 void conv0(hipStream_t st, const float* x, const float* dpart, int splits, long ss,
            const float* base, int rows, int hs, int gs, int kn, uint16_t* xca, float* dsum) {
-  const size_t lds = sizeof(float) * 2 * kn * (hs / gs);
-  k_conv0<<<rows, kThreads, lds, st>>>(x, dpart, splits, ss, base, hs, gs, kn,
-                                       reinterpret_cast<f16*>(xca), dsum);
+  const int G = hs / gs, gpw = std::max(1, kChunk / gs);
+  const size_t lds = sizeof(float) * 2 * kn * gpw;
+  k_conv0<<<dim3(cdiv(G, gpw), rows), kThreads, lds, st>>>(x, dpart, splits, ss, base, hs, gs, kn,
+                                                          gpw, reinterpret_cast<f16*>(xca), dsum);
 }
 
-void conv1_norm(hipStream_t st, float* h, const float* opart, int splits, long ss,
-                const float* dsum, const float* base, int rows, int hs, int gs, int kn,
-                const float* w, float eps, float* x, uint16_t* xa) {
-  k_conv1_norm<<<rows, kThreads, 0, st>>>(h, opart, splits, ss, dsum, base, hs, gs, kn, w, eps, x,
-                                          reinterpret_cast<f16*>(xa));
+void conv1(hipStream_t st, float* h, const float* opart, int splits, long ss, const float* dsum,
+           const float* base, int rows, int hs, int gs, int kn, float* sqp) {
+  const int nch = cdiv(hs, kChunk);
+  k_conv1<<<dim3(nch, rows), kThreads, 0, st>>>(h, opart, splits, ss, dsum, base, hs, gs, kn, sqp,
+                                                nch);
 }
 
 void qkv_post(hipStream_t st, const float* part, int splits, long ss, int rows, int nh, int kv,
@@ -1024,26 +1110,21 @@ void attn_merge(hipStream_t st, const float* pacc, const float* pml, int nh, int
                                     reinterpret_cast<f16*>(ya));
 }
 
-void topk_slice(hipStream_t st, const float* logits, int k, int width, int top, int slice,
-                int nslices, float* cv, int* ci) {
-  dim3 grid(nslices, k);
-  k_topk_slice<<<grid, kThreads, (size_t)slice * 8, st>>>(logits, width, top, slice, nslices, cv, ci);
-}
+int topk_slices(int width) { return cdiv(width, 64 * kSliceVPL); }
 
-void topk_merge(hipStream_t st, const float* cv, const int* ci, int k, int cnt, int top, int* cand,
-                float* unary) {
-  k_topk_merge<<<k, kThreads, (size_t)cnt * 8, st>>>(cv, ci, cnt, top, cand, unary);
-}
-
-void select_chain(hipStream_t st, const int* cand, const float* unary, const float* hp, int k,
-                  int top, int rank, const uint16_t* pbook, const uint16_t* cbook, int vocab,
-                  int anchor, const int* forced, float* score, int* chosen) {
+void select_all(hipStream_t st, const float* logits, int k, int width, int top, const float* hp,
+                int rank, const uint16_t* pbook, const uint16_t* cbook, int vocab, int anchor,
+                const int* forced, float* cv, int* ci, float* tab, int* cand, float* unary,
+                float* score, int* chosen) {
+  const int ns = topk_slices(width);
+  k_topk_slice<<<dim3(cdiv(ns, 4), k), kThreads, 0, st>>>(logits, width, top, ns, cv, ci);
   const int tpn = forced ? 1 : top;
+  k_pairs<<<dim3(k, tpn), 128, 0, st>>>(cv, ci, ns * top, top, hp, rank,
+                                        reinterpret_cast<const f16*>(pbook),
+                                        reinterpret_cast<const f16*>(cbook), vocab, anchor,
+                                        forced, cand, unary, tab);
   const size_t lds = sizeof(float) * (size_t)(top + (k - 1) * tpn * top);
-  k_select<<<1, kThreads, lds, st>>>(cand, unary, hp, k, top, rank,
-                                     reinterpret_cast<const f16*>(pbook),
-                                     reinterpret_cast<const f16*>(cbook), vocab, anchor, forced,
-                                     score, chosen);
+  k_chain<<<1, kThreads, lds, st>>>(tab, cand, k, top, tpn, score, chosen);
 }
 
 void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,

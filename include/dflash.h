@@ -151,6 +151,41 @@ void dflash_destroy(dflash_t* d);
    last failure of dflash_create on this thread. */
 const char* dflash_last_error(const dflash_t* d);
 
+/* ---- stage timers -------------------------------------------------------- */
+
+/* Per-stage device time, in the manner of the page's `CMF_DFLASH_TIME`
+   stage timers (`stage`, `stage_report`): with timing on, every launch of a
+   settle or block call is bracketed by hipEvents on the handle's stream and
+   each call waits for its last event, so the totals are exact device times
+   (and the calls no longer overlap the host). Stages, in order: */
+enum {
+  DFLASH_ST_KPROJ = 0,  /* kernel projections (both conv sets), f16 GEMM */
+  DFLASH_ST_CONV,       /* embedding, row convolutions, norms */
+  DFLASH_ST_QKV,        /* q/k/v int4 GEMM */
+  DFLASH_ST_QKPOST,     /* q/k norms + rotary */
+  DFLASH_ST_ATTN,       /* attention chunks + merge */
+  DFLASH_ST_O,          /* o int4 GEMM */
+  DFLASH_ST_GLU,        /* gate/up int4 GEMM with SwiGLU */
+  DFLASH_ST_DOWN,       /* down int4 GEMM */
+  DFLASH_ST_HEAD,       /* head (+ selector projection) f16 GEMM */
+  DFLASH_ST_SELECT,     /* top-k + selector chain */
+  DFLASH_ST_S_TAPS,     /* settle: tap rows to f16 */
+  DFLASH_ST_S_FC,       /* settle: fc f16 GEMM */
+  DFLASH_ST_S_NORM,     /* settle: hidden norm */
+  DFLASH_ST_S_KV,       /* settle: all layers' K/V int4 GEMM */
+  DFLASH_ST_S_STORE,    /* settle: k norm + rotary + store append */
+  DFLASH_STAGES
+};
+
+/* Turn the timers on (1) or off (0); either way the totals restart. */
+int dflash_set_timing(dflash_t* d, int on);
+
+/* Totals since the last dflash_set_timing: us[s] microseconds and
+   launches[s] kernel launches of stage s (arrays of DFLASH_STAGES), and the
+   number of block and settle calls timed (any pointer may be NULL). */
+int dflash_stage_times(const dflash_t* d, double* us, int64_t* launches, int64_t* blocks,
+                       int64_t* settles);
+
 /* ---- test entry points: each kernel on caller buffers ---------------------- */
 
 /* Matrix ids for the debug entry points (`layer` is ignored for the
