@@ -140,10 +140,10 @@ struct dflash {
   // block scratch
   float *h = nullptr, *x = nullptr, *dsum_a = nullptr, *dsum_m = nullptr, *kb = nullptr,
         *vb = nullptr, *pacc = nullptr, *pml = nullptr, *part = nullptr, *logits = nullptr,
-        *hp = nullptr, *cv = nullptr;
-  int* ci = nullptr;
+        *hp = nullptr;
   uint16_t *xa = nullptr, *xca = nullptr, *qa = nullptr, *ya = nullptr, *ma = nullptr;
-  float *sqp = nullptr, *tab = nullptr;
+  float* sqp = nullptr;
+  dfl::SelectScratch sel_sc{};
   // settle scratch
   uint16_t *taps_a = nullptr, *t_a = nullptr;
   float* tbuf = nullptr;
@@ -269,7 +269,7 @@ const char* validate(const dflash_geometry* g, const dflash_weights* w) {
   if (g->selector_top < 1 || g->selector_top > 32 || g->selector_top > g->vocab)
     return "selector_top must be in [1, min(32, vocab)]";
   if (g->selector_rank < 1 || g->selector_rank > 256) return "selector_rank must be in [1, 256]";
-  if ((long)g->vocab * g->selector_top > 8388608L) return "vocab*selector_top must be at most 2^23";
+  if (g->vocab > 262144) return "vocab must be at most 262144";
   if (g->mask_token < 0 || g->mask_token >= g->vocab) return "mask_token outside the vocabulary";
   if (g->max_context < 1) return "max_context must be >= 1";
   if (!g->windows || !g->rotary) return "null windows or rotary";
@@ -499,7 +499,7 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   const int rep = d->nh / d->kv;
   const size_t slots = (size_t)d->kv * (kMaxChunks + 1) * rep;
   d->part_floats = partial_need(d);
-  const int ns = dfl::topk_slices(d->V);
+  const size_t sel_cap = (size_t)dfl::topk_cap(d->V, d->top);
   if (!rc) rc = dev_alloc(d, &d->h, 16 * hs, "scratch");
   if (!rc) rc = dev_alloc(d, &d->x, 16 * hs, "scratch");
   if (!rc) rc = dev_alloc(d, &d->dsum_a, 16 * d->P, "scratch");
@@ -511,8 +511,11 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   if (!rc) rc = dev_alloc(d, &d->part, d->part_floats, "GEMM partials");
   if (!rc) rc = dev_alloc(d, &d->logits, (size_t)16 * d->V, "logits");
   if (!rc) rc = dev_alloc(d, &d->hp, 16 * d->rank, "selector projection");
-  if (!rc) rc = dev_alloc(d, &d->cv, (size_t)16 * ns * d->top, "candidates");
-  if (!rc) rc = dev_alloc(d, &d->ci, (size_t)16 * ns * d->top, "candidates");
+  if (!rc) rc = dev_alloc(d, &d->sel_sc.gmax, (size_t)16 * ((d->V + 255) / 256), "selection");
+  if (!rc) rc = dev_alloc(d, &d->sel_sc.thr, 16, "selection");
+  if (!rc) rc = dev_alloc(d, &d->sel_sc.counters, 16, "selection");
+  if (!rc) rc = dev_alloc(d, &d->sel_sc.lv, 16 * sel_cap, "selection candidates");
+  if (!rc) rc = dev_alloc(d, &d->sel_sc.li, 16 * sel_cap, "selection candidates");
   if (!rc) rc = dev_alloc(d, &d->xa, 16 * hs, "scratch");
   if (!rc) rc = dev_alloc(d, &d->xca, 16 * hs, "scratch");
   if (!rc) rc = dev_alloc(d, &d->qa, (size_t)d->nh * 16 * d->hd, "scratch");
@@ -523,7 +526,7 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   if (!rc) rc = dev_alloc(d, &d->t_a, (size_t)kSettleRows * hs, "settle scratch");
   if (!rc) rc = dev_alloc(d, &d->tbuf, (size_t)kSettleRows * hs, "settle scratch");
   if (!rc) rc = dev_alloc(d, &d->sqp, (size_t)kSettleRows * ((hs + 255) / 256), "norm scratch");
-  if (!rc) rc = dev_alloc(d, &d->tab, (size_t)d->top * (1 + 15 * d->top), "selector table");
+  if (!rc) rc = dev_alloc(d, &d->sel_sc.tab, (size_t)d->top * (1 + 15 * d->top), "selector table");
   if (!rc) rc = hip_check(nullptr, hipDeviceSynchronize(), "create");
   return done(rc);
 }
@@ -717,10 +720,10 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
   }
   // head over rows 1..k and the selector projection
   float* lg = logits ? logits : d->logits;
-  dfl::head_sel(st, d->xa, hs, d->head, width, k, lg, d->sel, d->rank, d->hp);
+  dfl::head_sel(st, d->xa, hs, d->head, width, k, lg, d->sel, d->rank, d->hp, d->sel_sc);
   tm_mark(d, DFLASH_ST_HEAD);
-  dfl::select_all(st, lg, k, width, d->top, d->hp + d->rank, d->rank, d->pbook, d->cbook, d->V,
-                  anchor, nullptr, d->cv, d->ci, d->tab, cand, unary, score, chosen);
+  dfl::select_all(st, lg, true, k, width, d->top, d->hp + d->rank, d->rank, d->pbook, d->cbook,
+                  d->V, anchor, nullptr, d->sel_sc, cand, unary, score, chosen);
   tm_mark(d, DFLASH_ST_SELECT);
   d->last_k = k;
   const int rc = launch_check(d, "block");
@@ -871,8 +874,8 @@ int dflash_debug_select(dflash_t* d, const float* logits, const float* hp, int32
   if (k < 1 || k >= 16) return fail(d, DFLASH_EINVAL, "select: k must be in [1, 15]");
   if (width < d->top || width > d->V) return fail(d, DFLASH_EINVAL, "select: bad width");
   if (anchor < 0 || anchor >= d->V) return fail(d, DFLASH_EINVAL, "select: bad anchor");
-  dfl::select_all(d->st, logits, k, width, d->top, hp, d->rank, d->pbook, d->cbook, d->V, anchor,
-                  forced_prev, d->cv, d->ci, d->tab, cand, unary, score, chosen);
+  dfl::select_all(d->st, logits, false, k, width, d->top, hp, d->rank, d->pbook, d->cbook, d->V,
+                  anchor, forced_prev, d->sel_sc, cand, unary, score, chosen);
   return launch_check(d, "select");
 }
 

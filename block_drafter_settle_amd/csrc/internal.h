@@ -47,10 +47,23 @@ void gemm_i4(hipStream_t st, int R, const uint16_t* xa, int K, int mblocks, cons
 // [ftiles, 2·ftiles) of one stored matrix; writes silu(g)·u in A-layout.
 void gemm_glu(hipStream_t st, const uint16_t* xa, int K, const uint8_t* codes,
               const uint16_t* scales, int ftiles, uint16_t* ma);
+// Scratch of the selection: gmax [k][ceil(width/256)] column-group maxima,
+// thr [k], counters [16], the candidate lists lv/li [k][topk_cap], and the
+// score table tab [top·(1 + 15·top)].
+struct SelectScratch {
+  float* gmax;
+  float* thr;
+  int* counters;
+  float* lv;
+  int* li;
+  float* tab;
+};
+
 // Logits of rows 1..k over head tiles [0, ceil(width/16)) and the selector
-// projection hp [16][rank] of all rows, in one launch.
+// projection hp [16][rank] of all rows, in one launch; also the selection's
+// column-group maxima.
 void head_sel(hipStream_t st, const uint16_t* xa, int K, const uint16_t* head, int width,
-              int k, float* logits, const uint16_t* sel, int rank, float* hp);
+              int k, float* logits, const uint16_t* sel, int rank, float* hp, SelectScratch sc);
 
 void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa);
 // Row kernels: sqp holds each (row, 256-channel chunk)'s sum of squares.
@@ -78,13 +91,14 @@ void attention(hipStream_t st, const uint16_t* qa, const float* sk, const float*
 void attn_merge(hipStream_t st, const float* pacc, const float* pml, int nh, int kv, int hd,
                 int nchunks, int B, uint16_t* ya);
 // Selection (`top_k` + `select_with`) on logits [k][width] and hp rows
-// [k][rank]: per-slice candidates (cv/ci scratch [k][topk_slices(width)][top]),
-// then cand/unary, the score table (tab) and the chain (score, chosen).
+// [k][rank]: cand/unary, the score table and the chain (score, chosen).
+// have_gmax: the head kernel already wrote the column-group maxima.
 int topk_slices(int width);
-void select_all(hipStream_t st, const float* logits, int k, int width, int top, const float* hp,
-                int rank, const uint16_t* pbook, const uint16_t* cbook, int vocab, int anchor,
-                const int* forced, float* cv, int* ci, float* tab, int* cand, float* unary,
-                float* score, int* chosen);
+int topk_cap(int width, int top);
+void select_all(hipStream_t st, const float* logits, bool have_gmax, int k, int width, int top,
+                const float* hp, int rank, const uint16_t* pbook, const uint16_t* cbook,
+                int vocab, int anchor, const int* forced, SelectScratch sc, int* cand,
+                float* unary, float* score, int* chosen);
 void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,
                 int rows, int K, float* out);
 void sum_rows(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,

@@ -286,13 +286,18 @@ __global__ __launch_bounds__(kThreads) void k_gemm_glu(const f16* __restrict__ x
 
 // The head over rows 1..k (logits [k][width]) and, in blocks past
 // head_groups, the selector projection of all 16 rows (hp [16][rank]).
+// Head blocks also record, per draft row, the largest logit of each 256
+// columns (gmax [k][head_groups]) for the selection's threshold, and block
+// 0 clears the selection's candidate counters.
 __global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, int K,
                                                    const f16* __restrict__ head, int wtiles,
                                                    int width, int k, float* __restrict__ logits,
                                                    const f16* __restrict__ sel, int stiles,
                                                    int rank, float* __restrict__ hp,
-                                                   int head_groups) {
+                                                   int head_groups, float* __restrict__ gmax,
+                                                   int* __restrict__ counters) {
   constexpr int R = 4;
+  __shared__ float wm[4][16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool is_sel = (int)blockIdx.x >= head_groups;
   const f16* w = is_sel ? sel : head;
@@ -300,35 +305,37 @@ __global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, i
   const int grp = is_sel ? blockIdx.x - head_groups : blockIdx.x;
   const int KS = K >> 5;
   const int t0 = (grp * 4 + wave) * R;
-  if (t0 >= ntiles) return;
-  const h8* xp = reinterpret_cast<const h8*>(xa) + lane;
-  const h8* wp[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-    wp[r] = reinterpret_cast<const h8*>(w) + (size_t)min(t0 + r, ntiles - 1) * KS * 64 + lane;
   f4 acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = (f4){0.f, 0.f, 0.f, 0.f};
-  int s = 0;
-  for (; s + 4 <= KS; s += 4) {
-    h8 a[4], b[4][R];
+  if (t0 < ntiles) {
+    const h8* xp = reinterpret_cast<const h8*>(xa) + lane;
+    const h8* wp[R];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a[u] = xp[(size_t)(s + u) * 64];
+    for (int r = 0; r < R; ++r)
+      wp[r] = reinterpret_cast<const h8*>(w) + (size_t)min(t0 + r, ntiles - 1) * KS * 64 + lane;
+    int s = 0;
+    for (; s + 4 <= KS; s += 4) {
+      h8 a[4], b[4][R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) b[u][r] = wp[r][(size_t)(s + u) * 64];
+      for (int u = 0; u < 4; ++u) {
+        a[u] = xp[(size_t)(s + u) * 64];
+#pragma unroll
+        for (int r = 0; r < R; ++r) b[u][r] = wp[r][(size_t)(s + u) * 64];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = mfma16(a[u], b[u][r], acc[r]);
     }
+    for (; s < KS; ++s) {
+      const h8 a = xp[(size_t)s * 64];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = mfma16(a[u], b[u][r], acc[r]);
-  }
-  for (; s < KS; ++s) {
-    const h8 a = xp[(size_t)s * 64];
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = mfma16(a, wp[r][(size_t)s * 64], acc[r]);
+      for (int r = 0; r < R; ++r) acc[r] = mfma16(a, wp[r][(size_t)s * 64], acc[r]);
+    }
   }
   const int j = lane >> 4, n = lane & 15;
+  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int t = t0 + r, col = t * 16 + n;
@@ -338,10 +345,26 @@ __global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, i
       const int m = 4 * j + v;
       if (is_sel) {
         if (col < rank) hp[(size_t)m * rank + col] = acc[r][v];
-      } else if (m >= 1 && m <= k && col < width) {
-        logits[(size_t)(m - 1) * width + col] = acc[r][v];
+      } else if (col < width) {
+        if (m >= 1 && m <= k) logits[(size_t)(m - 1) * width + col] = acc[r][v];
+        mx[v] = fmaxf(mx[v], acc[r][v]);
       }
     }
+  }
+  if (is_sel) return;  // uniform per block
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) mx[v] = fmaxf(mx[v], __shfl_xor(mx[v], o, 64));
+  if (n == 0)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wm[wave][4 * j + v] = mx[v];
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int m = threadIdx.x;
+    const float g = fmaxf(fmaxf(wm[0][m], wm[1][m]), fmaxf(wm[2][m], wm[3][m]));
+    if (m >= 1 && m <= k) gmax[(size_t)(m - 1) * head_groups + blockIdx.x] = g;
+    if (blockIdx.x == 0) counters[m] = 0;
   }
 }
 
@@ -763,6 +786,12 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 
 // ------------------------------------------------------- top-k, selector
 
+// Orders this wave's LDS accesses (lane 0's writes before every lane's reads).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
+
 // `top_k`'s order: the larger value first, the smaller index among equals.
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
@@ -816,40 +845,159 @@ __device__ void wave_select(float (&v)[VPL], int (&ix)[VPL], int want, float* ou
   }
 }
 
-// Each wave takes a slice of 64·kSliceVPL logits of one row and writes its
-// exact top `top` candidates (value, index) for the merge.
-static constexpr int kSliceVPL = 32;
+// Selection of the top `top` logits of a row, exactly, in three steps:
+//   k_thresh   T = the top-th largest of the row's 256-column maxima; at
+//              least `top` logits are ≥ T, and only the < top column groups
+//              whose maximum exceeds T can hold logits > T;
+//   k_collect  every logit > T, and of the logits equal to T the first `top`
+//              by index in each 2048-column slice, into the row's list;
+//   k_pairs    the exact top `top` of that list (it holds the row's top
+//              `top` by construction), then the selector's scores.
+static constexpr int kSliceVPL = 32;  // a collect wave covers 64·32 = 2048 columns
 
-__global__ __launch_bounds__(kThreads) void k_topk_slice(const float* __restrict__ logits,
-                                                         int width, int top, int nslices,
-                                                         float* __restrict__ cv,
-                                                         int* __restrict__ ci) {
+// The row maxima of 256-column groups (for the selector entry point, whose
+// logits do not come from the head kernel); block (0, 0) clears the counters.
+__global__ __launch_bounds__(kThreads) void k_rowmax(const float* __restrict__ logits, int width,
+                                                     int ngroups, float* __restrict__ gmax,
+                                                     int* __restrict__ counters) {
+  __shared__ float red[4];
+  const int g = blockIdx.x, j = blockIdx.y, c = g * 256 + threadIdx.x;
+  float v = c < width ? logits[(size_t)j * width + c] : -INFINITY;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    gmax[(size_t)j * ngroups + g] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (g == 0 && j == 0 && threadIdx.x < 16) counters[threadIdx.x] = 0;
+}
+
+// T of each row: one wave per row over its ngroups maxima (≤ 64·16).
+__global__ __launch_bounds__(64) void k_thresh(const float* __restrict__ gmax, int ngroups, int top,
+                                               float* __restrict__ thr) {
+  __shared__ float ov[32];
+  __shared__ int oi[32];
+  const int j = blockIdx.x, lane = threadIdx.x;
+  float v[16];
+  int ix[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int e = lane + 64 * u;
+    v[u] = e < ngroups ? gmax[(size_t)j * ngroups + e] : -INFINITY;
+    ix[u] = e < ngroups ? e : INT_MAX;
+  }
+  wave_select<16>(v, ix, top, ov, oi);
+  __syncthreads();
+  if (lane == 0) thr[j] = ov[top - 1];
+}
+
+// Append (value, index) for the lanes with `take`, in lane order, to row j's list.
+__device__ __forceinline__ void append(bool take, float v, int idx, int* counter, float* lv,
+                                       int* li, int cap) {
+  const uint64_t mask = __ballot(take);
+  if (!mask) return;
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  if (lane == 0) base = atomicAdd(counter, __popcll(mask));
+  base = __shfl(base, 0, 64);
+  const int pos = base + __popcll(mask & ((1ull << lane) - 1));
+  if (take && pos < cap) {
+    lv[pos] = v;
+    li[pos] = idx;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_collect(const float* __restrict__ logits, int width,
+                                                      int top, int nslices,
+                                                      const float* __restrict__ thr,
+                                                      int* __restrict__ counters,
+                                                      float* __restrict__ lv, int* __restrict__ li,
+                                                      int cap) {
   const int lane = threadIdx.x & 63, j = blockIdx.y;
   const int sl = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (sl >= nslices) return;
+  const float T = thr[j];
   const int b0 = sl * 64 * kSliceVPL;
   const float* row = logits + (size_t)j * width;
   float v[kSliceVPL];
-  int ix[kSliceVPL];
 #pragma unroll
   for (int u = 0; u < kSliceVPL; ++u) {
     const int e = b0 + lane + 64 * u;
     v[u] = e < width ? row[e] : -INFINITY;
-    ix[u] = e < width ? e : INT_MAX;
   }
-  const size_t o = ((size_t)j * nslices + sl) * top;
-  wave_select<kSliceVPL>(v, ix, top, cv + o, ci + o);
+  float* rv = lv + (size_t)j * cap;
+  int* ri = li + (size_t)j * cap;
+#pragma unroll
+  for (int u = 0; u < kSliceVPL; ++u) append(v[u] > T, v[u], b0 + lane + 64 * u, counters + j, rv, ri, cap);
+  // ties at T: the first `top` of this slice in index order (u major, lane minor)
+  int taken = 0;
+  for (int u = 0; u < kSliceVPL && taken < top; ++u) {
+    const int e = b0 + lane + 64 * u;
+    const bool eq = e < width && v[u] == T;
+    const uint64_t mask = __ballot(eq);
+    const int rank_in = __popcll(mask & ((1ull << lane) - 1));
+    const bool take = eq && rank_in < top - taken;
+    append(take, v[u], e, counters + j, rv, ri, cap);
+    taken += min(__popcll(mask), top - taken);
+  }
 }
 
-// Row j's candidates: the exact top `top` of the slices' candidates (wave 0),
-// and row j−1's (wave 1, j ≥ 1); then the scores of row j's candidates
-// under row j−1's candidate tp (or the anchor, or forced[j]) as predecessor,
-// `select_with`: unary + Σ_q (P[prev][q]·hp[j][q])·C[tok][q]. Block (j, tp);
-// block (j, 0) also writes cand and unary of row j.
-static constexpr int kMergeVPL = 64;
+// The exact top `want` of row's list (count entries), in `top_k` order, into
+// out_v/out_i (LDS, ≥ 32 + 64 entries): passes of up to 64·VPL entries,
+// each pass re-selecting from the best so far plus new entries.
+template <int VPL>
+__device__ void list_pass(const float* rv, const int* ri, int e0, int n_new, float* best_v,
+                          int* best_i, int nbest, int want) {
+  const int lane = threadIdx.x & 63;
+  float v[VPL];
+  int ix[VPL];
+#pragma unroll
+  for (int u = 0; u < VPL; ++u) {
+    const int e = lane + 64 * u;  // entries [0, nbest) are the best so far
+    if (e < nbest) {
+      v[u] = best_v[e];
+      ix[u] = best_i[e];
+    } else if (e < nbest + n_new) {
+      v[u] = rv[e0 + e - nbest];
+      ix[u] = ri[e0 + e - nbest];
+    } else {
+      v[u] = -INFINITY;
+      ix[u] = INT_MAX;
+    }
+  }
+  wave_lds_sync();
+  wave_select<VPL>(v, ix, want, best_v, best_i);
+  wave_lds_sync();
+}
 
-__global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ cv,
-                                               const int* __restrict__ ci, int cnt, int top,
+__device__ void select_list(const float* rv, const int* ri, int count, int want, float* best_v,
+                            int* best_i) {
+  int nbest = 0, e0 = 0;
+  do {
+    const int room = 64 * 64 - nbest;
+    const int n_new = min(count - e0, room);
+    const int tot = nbest + n_new;
+    if (tot <= 64)
+      list_pass<1>(rv, ri, e0, n_new, best_v, best_i, nbest, want);
+    else if (tot <= 256)
+      list_pass<4>(rv, ri, e0, n_new, best_v, best_i, nbest, want);
+    else if (tot <= 1024)
+      list_pass<16>(rv, ri, e0, n_new, best_v, best_i, nbest, want);
+    else
+      list_pass<64>(rv, ri, e0, n_new, best_v, best_i, nbest, want);
+    nbest = want;
+    e0 += n_new;
+  } while (e0 < count);
+}
+
+// Row j's top candidates (wave 0) and row j−1's (wave 1, j ≥ 1, to know the
+// predecessor tp); then the scores of row j's candidates under that
+// predecessor (or the anchor for j = 0, or forced[j]), `select_with`:
+// unary + Σ_q (P[prev][q]·hp[j][q])·C[tok][q]. Block (j, tp); block (j, 0)
+// also writes cand and unary of row j.
+__global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
+                                               const int* __restrict__ li,
+                                               const int* __restrict__ counters, int cap, int top,
                                                const float* __restrict__ hp, int rank,
                                                const f16* __restrict__ pbook,
                                                const f16* __restrict__ cbook, int vocab, int anchor,
@@ -864,15 +1012,9 @@ __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ cv,
   const int row = j - wave;  // wave 0: row j, wave 1: row j−1
   const bool need = wave == 0 || (j > 0 && !forced);
   if (need) {
-    float v[kMergeVPL];
-    int ix[kMergeVPL];
-#pragma unroll
-    for (int u = 0; u < kMergeVPL; ++u) {
-      const int e = lane + 64 * u;
-      v[u] = e < cnt ? cv[(size_t)row * cnt + e] : -INFINITY;
-      ix[u] = e < cnt ? ci[(size_t)row * cnt + e] : INT_MAX;
-    }
-    wave_select<kMergeVPL>(v, ix, wave == 0 ? top : tp + 1, uv[wave], uc[wave]);
+    const int count = min(counters[row], cap);
+    select_list(lv + (size_t)row * cap, li + (size_t)row * cap, count, wave == 0 ? top : tp + 1,
+                uv[wave], uc[wave]);
   }
   __syncthreads();
   if (wave == 0 && tp == 0 && lane < top) {
@@ -917,13 +1059,14 @@ __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ cv,
 
 // The chain: row by row, the first candidate with the largest score under
 // the predecessor chosen before it.
-__global__ __launch_bounds__(kThreads) void k_chain(const float* __restrict__ tab,
-                                                    const int* __restrict__ cand, int k, int top,
-                                                    int tpn, float* __restrict__ score,
-                                                    int* __restrict__ chosen) {
+__global__ __launch_bounds__(1024) void k_chain(const float* __restrict__ tab,
+                                                const int* __restrict__ cand, int k, int top,
+                                                int tpn, float* __restrict__ score,
+                                                int* __restrict__ chosen) {
   extern __shared__ float lt[];
   const int total = top + (k - 1) * tpn * top;
-  for (int e = threadIdx.x; e < total; e += kThreads) lt[e] = tab[e];
+#pragma unroll 4
+  for (int e = threadIdx.x; e < total; e += 1024) lt[e] = tab[e];
   __syncthreads();
   if (threadIdx.x != 0) return;
   int tp = 0;
@@ -1020,12 +1163,13 @@ void gemm_glu(hipStream_t st, const uint16_t* xa, int K, const uint8_t* codes,
 }
 
 void head_sel(hipStream_t st, const uint16_t* xa, int K, const uint16_t* head, int width, int k,
-              float* logits, const uint16_t* sel, int rank, float* hp) {
+              float* logits, const uint16_t* sel, int rank, float* hp, SelectScratch sc) {
   const int wtiles = cdiv(width, 16), stiles = cdiv(rank, 16);
   const int hg = cdiv(wtiles, 16), sg = cdiv(stiles, 16);
   k_head<<<hg + sg, kThreads, 0, st>>>(reinterpret_cast<const f16*>(xa), K,
                                        reinterpret_cast<const f16*>(head), wtiles, width, k, logits,
-                                       reinterpret_cast<const f16*>(sel), stiles, rank, hp, hg);
+                                       reinterpret_cast<const f16*>(sel), stiles, rank, hp, hg,
+                                       sc.gmax, sc.counters);
 }
 
 void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa) {
@@ -1112,19 +1256,28 @@ void attn_merge(hipStream_t st, const float* pacc, const float* pml, int nh, int
 
 int topk_slices(int width) { return cdiv(width, 64 * kSliceVPL); }
 
-void select_all(hipStream_t st, const float* logits, int k, int width, int top, const float* hp,
-                int rank, const uint16_t* pbook, const uint16_t* cbook, int vocab, int anchor,
-                const int* forced, float* cv, int* ci, float* tab, int* cand, float* unary,
-                float* score, int* chosen) {
-  const int ns = topk_slices(width);
-  k_topk_slice<<<dim3(cdiv(ns, 4), k), kThreads, 0, st>>>(logits, width, top, ns, cv, ci);
+int topk_cap(int width, int top) {
+  // logits > T lie in < top column groups of 256; ties add ≤ top a slice
+  return ((top - 1) * 256 + top * topk_slices(width) + 63) / 64 * 64;
+}
+
+void select_all(hipStream_t st, const float* logits, bool have_gmax, int k, int width, int top,
+                const float* hp, int rank, const uint16_t* pbook, const uint16_t* cbook,
+                int vocab, int anchor, const int* forced, SelectScratch sc, int* cand,
+                float* unary, float* score, int* chosen) {
+  const int ngroups = cdiv(width, 256), ns = topk_slices(width), cap = topk_cap(width, top);
+  if (!have_gmax)
+    k_rowmax<<<dim3(ngroups, k), kThreads, 0, st>>>(logits, width, ngroups, sc.gmax, sc.counters);
+  k_thresh<<<k, 64, 0, st>>>(sc.gmax, ngroups, top, sc.thr);
+  k_collect<<<dim3(cdiv(ns, 4), k), kThreads, 0, st>>>(logits, width, top, ns, sc.thr, sc.counters,
+                                                       sc.lv, sc.li, cap);
   const int tpn = forced ? 1 : top;
-  k_pairs<<<dim3(k, tpn), 128, 0, st>>>(cv, ci, ns * top, top, hp, rank,
+  k_pairs<<<dim3(k, tpn), 128, 0, st>>>(sc.lv, sc.li, sc.counters, cap, top, hp, rank,
                                         reinterpret_cast<const f16*>(pbook),
                                         reinterpret_cast<const f16*>(cbook), vocab, anchor,
-                                        forced, cand, unary, tab);
+                                        forced, cand, unary, sc.tab);
   const size_t lds = sizeof(float) * (size_t)(top + (k - 1) * tpn * top);
-  k_chain<<<1, kThreads, lds, st>>>(tab, cand, k, top, tpn, score, chosen);
+  k_chain<<<1, 1024, lds, st>>>(sc.tab, cand, k, top, tpn, score, chosen);
 }
 
 void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,

@@ -70,7 +70,7 @@ typedef struct {
    head_dim in {64, 128, 256}, conv_group > 0, hidden % conv_group == 0,
    conv_kernel in [1, block], hidden, intermediate and heads*head_dim
    multiples of 128, 1 ≤ selector_top ≤ 32, selector_top ≤ vocab,
-   selector_rank in [1, 256], 0 ≤ mask_token < vocab, every window ≥ 0,
+   vocab ≤ 262144, selector_rank in [1, 256], 0 ≤ mask_token < vocab, every window ≥ 0,
    max_context ≥ 1. */
 typedef struct {
   int32_t hidden, intermediate, layers, heads, kv_heads, head_dim, vocab, block, mask_token,

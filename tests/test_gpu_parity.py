@@ -296,3 +296,29 @@ def test_select_parity(orc, strong):
         close(score.cpu().numpy(), ref["score"], "forced scores")
     finally:
         d.close()
+
+
+def test_block_ties_everywhere(orc):
+    """A zero head makes every logit exactly 0: the candidates are the first
+    `top` token ids in order and every unary is 0 (exact tie-break path)."""
+    g = synth.small_geometry(vocab=3000, mask_token=2999)
+    w = synth.make_weights(g, seed=7)
+    w["head"] = np.zeros_like(w["head"])
+    stream = torch.cuda.current_stream(_dev()).cuda_stream
+    d = pkg.Drafter(g, w, max_context=40, stream=stream)
+    try:
+        taps = synth.make_taps(g, 30, seed=1)
+        d.settle(0, 30, taps.to(_dev()).data_ptr())
+        got = run_block(d, g, 5, 30, 7, 3000)
+        top = g["selector_top"]
+        assert np.all(got["logits"] == 0)
+        assert np.array_equal(got["cand"], np.tile(np.arange(top), (7, 1)))
+        assert np.all(got["unary"] == 0)
+        m = orc.Model(g, w)
+        K, V = m.settle(taps.numpy(), 0)
+        ref = m.block([(K[l], V[l]) for l in range(g["layers"])], 0, 30, 5, 30, 7, 3000)
+        sel = m.select(ref["logits"], ref["hp"], 5)
+        assert np.array_equal(sel["cand"], got["cand"])
+        check_selection(got, np.ones_like(ref["logits"]), sel, "ties")
+    finally:
+        d.close()
