@@ -53,6 +53,15 @@ Split split_for(int ntiles, int R, int steps, int mblocks, int min_per) {
   return {(int)((steps + per - 1) / per), per};
 }
 
+// K splits of the many-row f16 GEMM (16 weight tiles a block): about one
+// block per CU, every split keeping at least 16 steps (512 columns).
+Split split_big(int ntiles, int steps) {
+  const long groups = (ntiles + 15) / 16;
+  long S = std::max(1L, std::min<long>(256 / groups, steps / 16));
+  const int per = (int)((steps + S - 1) / S);
+  return {(int)((steps + per - 1) / per), per};
+}
+
 void parallel_for(long n, const std::function<void(long)>& f) {
   unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
   if (n < 64) nt = 1;
@@ -329,6 +338,14 @@ long partial_need(const dflash* d) {
   i4(d->qd + 2 * d->kd, d->hs, 1, kRQkv);
   i4(d->hs, d->qd, 1, kRO);
   i4(d->hs, d->ffn, 1, kRDown);
+  for (int mb = 2; mb <= kSettleRows / 16; ++mb)
+    for (int N : {d->hs, d->P, d->rank}) {
+      const int K = N == d->hs ? d->tw : d->hs;
+      const Split s = split_big((N + 15) / 16, K / 32);
+      need = std::max(need, (long)s.S * mb * 16 * N);
+      const Split s2 = split_big((N + 15) / 16, d->hs / 32);
+      need = std::max(need, (long)s2.S * mb * 16 * N);
+    }
   for (int mb = 1; mb <= kSettleRows / 16; ++mb) {
     f16(d->hs, d->tw, mb, kRFc);
     i4(d->L * 2 * d->kd, d->hs, mb, kRKv);
@@ -581,10 +598,14 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
   dfl::to_a(st, taps, d->tw, m, d->tw, d->taps_a);
   tm_mark(d, DFLASH_ST_S_TAPS);
   // t = fc · taps (f32 partials), then rms by hidden_norm into A-layout
-  const Split sf = split_for(d->hs / 16, kRFc, d->tw / 32, mb, 16);
+  const dfl::TileMap fmap{d->hs / 16, d->hs / 16, 0, 0};
+  const Split sf = mb > 1 ? split_big(d->hs / 16, d->tw / 32)
+                          : split_for(d->hs / 16, kRFc, d->tw / 32, mb, 16);
   const long ssf = (long)mb * 16 * d->hs;
-  dfl::gemm_f16(st, kRFc, d->taps_a, d->tw, mb, d->fc, dfl::TileMap{d->hs / 16, d->hs / 16, 0, 0}, d->hs,
-                sf.S, sf.per, d->part, ssf);
+  if (mb > 1)
+    dfl::gemm_big_f16(st, d->taps_a, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part, ssf);
+  else
+    dfl::gemm_f16(st, kRFc, d->taps_a, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part, ssf);
   tm_mark(d, DFLASH_ST_S_FC);
   dfl::rowsum_sq(st, d->part, sf.S, ssf, m, d->hs, d->tbuf, d->sqp);
   tm_mark(d, DFLASH_ST_S_NORM);
@@ -804,12 +825,16 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
   const int mb = (m + 15) / 16;
   dfl::to_a(d->st, x, cols, m, cols, d->taps_a);
   const Split s = is_i4 ? split_for(map.ntiles, kRDebug, cols / 128, mb, 4)
-                        : split_for(map.ntiles, kRDebug, cols / 32, mb, 16);
+                  : mb > 1 ? split_big(map.ntiles, cols / 32)
+                           : split_for(map.ntiles, kRDebug, cols / 32, mb, 16);
   const long ss = (long)mb * 16 * rows;
   if ((long)s.S * ss > d->part_floats) return fail(d, DFLASH_EINVAL, "matvec: partials too large");
   if (is_i4)
     dfl::gemm_i4(d->st, kRDebug, d->taps_a, cols, mb, static_cast<const uint8_t*>(codes), scales, map, rows,
                  s.S, s.per, d->part, ss);
+  else if (mb > 1)
+    dfl::gemm_big_f16(d->st, d->taps_a, cols, mb, static_cast<const uint16_t*>(codes), map, rows,
+                      s.S, s.per, d->part, ss);
   else
     dfl::gemm_f16(d->st, kRDebug, d->taps_a, cols, mb, static_cast<const uint16_t*>(codes), map, rows, s.S,
                   s.per, d->part, ss);

@@ -43,6 +43,11 @@ void gemm_f16(hipStream_t st, int R, const uint16_t* xa, int K, int mblocks, con
 void gemm_i4(hipStream_t st, int R, const uint16_t* xa, int K, int mblocks, const uint8_t* codes,
              const uint16_t* scales, TileMap map, int N, int splits, int spans_per_split,
              float* out, long split_stride);
+// Many-row f16 GEMM (mblocks ≤ 16 row blocks at once, 8 weight tiles per
+// block, LDS double buffered); out as gemm_f16.
+void gemm_big_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
+                  TileMap map, int N, int splits, int steps_per_split, float* out,
+                  long split_stride);
 // gate/up with the SwiGLU epilogue: gate tiles [0, ftiles), up tiles
 // [ftiles, 2·ftiles) of one stored matrix; writes silu(g)·u in A-layout.
 void gemm_glu(hipStream_t st, const uint16_t* xa, int K, const uint8_t* codes,
