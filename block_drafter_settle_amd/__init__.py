@@ -74,6 +74,7 @@ _SIGS = {
     "dflash_debug_load_store": ([C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p],
                                 C.c_int),
     "dflash_debug_last_block": ([C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
+    "dflash_debug_set_trace": ([C.c_void_p, C.c_void_p], C.c_int),
     "dflash_debug_select": ([C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
                              C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
 }
@@ -243,6 +244,9 @@ class Drafter:
 
     def debug_last_block(self, hidden_ptr, hp_ptr):
         _check(lib().dflash_debug_last_block(self.h, hidden_ptr, hp_ptr), self.h)
+
+    def debug_set_trace(self, trace_ptr):
+        _check(lib().dflash_debug_set_trace(self.h, trace_ptr), self.h)
 
     def debug_select(self, logits_ptr, hp_ptr, k, width, anchor, forced_ptr, cand_ptr, unary_ptr,
                      score_ptr, chosen_ptr):

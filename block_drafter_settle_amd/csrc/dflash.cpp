@@ -159,6 +159,7 @@ struct dflash {
   long part_floats = 0;
   int stage_cols = 0;  // widest activation the staging buffer holds
   int last_k = 0;
+  float* trace = nullptr;  // per-layer residual copies (debug)
   std::vector<void*> allocs;
   std::string err;
   struct Timing {
@@ -533,11 +534,12 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   if (!rc) rc = dev_alloc(d, &d->sel_sc.counters, 16, "selection");
   if (!rc) rc = dev_alloc(d, &d->sel_sc.lv, 16 * sel_cap, "selection candidates");
   if (!rc) rc = dev_alloc(d, &d->sel_sc.li, 16 * sel_cap, "selection candidates");
-  if (!rc) rc = dev_alloc(d, &d->xa, 16 * hs, "scratch");
-  if (!rc) rc = dev_alloc(d, &d->xca, 16 * hs, "scratch");
-  if (!rc) rc = dev_alloc(d, &d->qa, (size_t)d->nh * 16 * d->hd, "scratch");
-  if (!rc) rc = dev_alloc(d, &d->ya, 16 * d->qd, "scratch");
-  if (!rc) rc = dev_alloc(d, &d->ma, 16 * d->ffn, "scratch");
+  // the block's activation operands, two planes each
+  if (!rc) rc = dev_alloc(d, &d->xa, 2 * 16 * hs, "scratch");
+  if (!rc) rc = dev_alloc(d, &d->xca, 2 * 16 * hs, "scratch");
+  if (!rc) rc = dev_alloc(d, &d->qa, 2 * (size_t)d->nh * 16 * d->hd, "scratch");
+  if (!rc) rc = dev_alloc(d, &d->ya, 2 * 16 * d->qd, "scratch");
+  if (!rc) rc = dev_alloc(d, &d->ma, 2 * 16 * d->ffn, "scratch");
   d->stage_cols = std::max(std::max(d->tw, d->ffn), std::max(d->qd, hs));
   if (!rc) rc = dev_alloc(d, &d->taps_a, (size_t)kSettleRows * d->stage_cols, "settle scratch");
   if (!rc) rc = dev_alloc(d, &d->t_a, (size_t)kSettleRows * hs, "settle scratch");
@@ -595,7 +597,7 @@ int dflash_truncate(dflash_t* d, int64_t pos) {
 static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0) {
   hipStream_t st = d->st;
   const int mb = (m + 15) / 16;
-  dfl::to_a(st, taps, d->tw, m, d->tw, d->taps_a);
+  dfl::to_a(st, taps, d->tw, m, d->tw, d->taps_a, 0);
   tm_mark(d, DFLASH_ST_S_TAPS);
   // t = fc · taps (f32 partials), then rms by hidden_norm into A-layout
   const dfl::TileMap fmap{d->hs / 16, d->hs / 16, 0, 0};
@@ -605,11 +607,12 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
   if (mb > 1)
     dfl::gemm_big_f16(st, d->taps_a, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part, ssf);
   else
-    dfl::gemm_f16(st, kRFc, d->taps_a, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part, ssf);
+    dfl::gemm_f16(st, kRFc, d->taps_a, 0, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part,
+                  ssf);
   tm_mark(d, DFLASH_ST_S_FC);
   dfl::rowsum_sq(st, d->part, sf.S, ssf, m, d->hs, d->tbuf, d->sqp);
   tm_mark(d, DFLASH_ST_S_NORM);
-  dfl::norm_apply(st, d->tbuf, d->sqp, m, d->hs, d->hidden_norm, d->eps, nullptr, d->t_a);
+  dfl::norm_apply(st, d->tbuf, d->sqp, m, d->hs, d->hidden_norm, d->eps, nullptr, d->t_a, 0);
   tm_mark(d, DFLASH_ST_S_NORM);
   // K and V of every layer: the k and v tiles of each layer's q/k/v set
   const int kvt = 2 * d->kd / 16;
@@ -617,7 +620,7 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
   const Split sk = split_for(d->L * kvt, kRKv, d->hs / 128, mb, 4);
   const long ssk = (long)mb * 16 * N;
   dfl::TileMap map{d->L * kvt, kvt, d->qkv.tiles, d->qd / 16};
-  dfl::gemm_i4(st, kRKv, d->t_a, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per, d->part,
+  dfl::gemm_i4(st, kRKv, d->t_a, 0, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per, d->part,
                ssk);
   tm_mark(d, DFLASH_ST_S_KV);
   dfl::settle_kv(st, d->part, sk.S, ssk, m, d->L, d->kv, d->hd, d->k_norm, d->inv, d->rot_dev,
@@ -678,27 +681,29 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
   const size_t i4l_o = (size_t)d->o.tiles * (d->qd / 128);
   const size_t i4l_gu = (size_t)d->gu.tiles * (hs / 128);
   const size_t i4l_dn = (size_t)d->down.tiles * (d->ffn / 128);
+  // plane strides (halves) of the two-plane operands
+  const long psh = 16L * hs, psq = 16L * d->nh * d->hd, psy = 16L * d->qd, psm = 16L * d->ffn;
 
   tm_begin(d);
   dfl::embed(st, d->embed, anchor, d->mask, B, hs, d->h, d->sqp);
   tm_mark(d, DFLASH_ST_CONV);
-  dfl::norm_apply(st, d->h, d->sqp, B, hs, d->in_norm, d->eps, d->x, d->xa);
+  dfl::norm_apply(st, d->h, d->sqp, B, hs, d->in_norm, d->eps, d->x, d->xa, psh);
   tm_mark(d, DFLASH_ST_CONV);
   for (int l = 0; l < d->L; ++l) {
     const float* ab = d->attn_base + (size_t)l * 2 * d->kn * hs;
     const float* mbase = d->mlp_base + (size_t)l * 2 * d->kn * hs;
     // attention: conv_in, q/k/v, norms + rotary
-    dfl::gemm_f16(st, kRKproj, d->xa, hs, 1, d->attn_kproj + l * kp_layer,
+    dfl::gemm_f16(st, kRKproj, d->xa, psh, hs, 1, d->attn_kproj + l * kp_layer,
                   dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, spk.S, spk.per, d->part, ssd);
     tm_mark(d, DFLASH_ST_KPROJ);
-    dfl::conv0(st, d->x, d->part, spk.S, ssd, ab, B, hs, d->gs, d->kn, d->xca, d->dsum_a);
+    dfl::conv0(st, d->x, d->part, spk.S, ssd, ab, B, hs, d->gs, d->kn, d->xca, psh, d->dsum_a);
     tm_mark(d, DFLASH_ST_CONV);
-    dfl::gemm_i4(st, kRQkv, d->xca, hs, 1, d->qkv.codes + i4l_qkv * 1024 * l, d->qkv.scales + i4l_qkv * 64 * l,
+    dfl::gemm_i4(st, kRQkv, d->xca, psh, hs, 1, d->qkv.codes + i4l_qkv * 1024 * l, d->qkv.scales + i4l_qkv * 64 * l,
                  dfl::TileMap{d->qkv.tiles, d->qkv.tiles, 0, 0}, d->qd + 2 * d->kd, sqk.S, sqk.per,
                  d->part, ssq);
     tm_mark(d, DFLASH_ST_QKV);
     dfl::qkv_post(st, d->part, sqk.S, ssq, B, d->nh, d->kv, d->hd, d->q_norm + (size_t)l * d->hd,
-                  d->k_norm + (size_t)l * d->hd, d->inv, a, d->rot[l], d->eps, d->qa, d->kb, d->vb);
+                  d->k_norm + (size_t)l * d->hd, d->inv, a, d->rot[l], d->eps, d->qa, psq, d->kb, d->vb);
     tm_mark(d, DFLASH_ST_QKPOST);
     // attention over the layer's context range and the block's rows
     long lo, n;
@@ -706,42 +711,47 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     int nchunks = 0;
     const int chunk = attn_chunk(n, &nchunks);
     const size_t lrow = (size_t)l * d->cap + (lo - d->first);
-    dfl::attention(st, d->qa, d->sk + lrow * d->kd, d->sv + lrow * d->kd, d->kb, d->vb, B, d->nh,
+    dfl::attention(st, d->qa, psq, d->sk + lrow * d->kd, d->sv + lrow * d->kd, d->kb, d->vb, B, d->nh,
                    d->kv, d->hd, (int)n, lo, a, d->windows[l], chunk, nchunks, scale, d->pacc,
                    d->pml);
     tm_mark(d, DFLASH_ST_ATTN);
-    dfl::attn_merge(st, d->pacc, d->pml, d->nh, d->kv, d->hd, nchunks, B, d->ya);
+    dfl::attn_merge(st, d->pacc, d->pml, d->nh, d->kv, d->hd, nchunks, B, d->ya, psy);
     tm_mark(d, DFLASH_ST_ATTN);
     // o, conv_out into the residual, post-attention norm
-    dfl::gemm_i4(st, kRO, d->ya, d->qd, 1, d->o.codes + i4l_o * 1024 * l, d->o.scales + i4l_o * 64 * l,
+    dfl::gemm_i4(st, kRO, d->ya, psy, d->qd, 1, d->o.codes + i4l_o * 1024 * l, d->o.scales + i4l_o * 64 * l,
                  dfl::TileMap{d->o.tiles, d->o.tiles, 0, 0}, hs, so.S, so.per, d->part, ssh);
     tm_mark(d, DFLASH_ST_O);
     dfl::conv1(st, d->h, d->part, so.S, ssh, d->dsum_a, ab, B, hs, d->gs, d->kn, d->sqp);
     tm_mark(d, DFLASH_ST_CONV);
-    dfl::norm_apply(st, d->h, d->sqp, B, hs, d->post_norm + (size_t)l * hs, d->eps, d->x, d->xa);
+    dfl::norm_apply(st, d->h, d->sqp, B, hs, d->post_norm + (size_t)l * hs, d->eps, d->x, d->xa,
+                    psh);
     tm_mark(d, DFLASH_ST_CONV);
     // MLP, wrapped the same way
-    dfl::gemm_f16(st, kRKproj, d->xa, hs, 1, d->mlp_kproj + l * kp_layer,
+    dfl::gemm_f16(st, kRKproj, d->xa, psh, hs, 1, d->mlp_kproj + l * kp_layer,
                   dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, spk.S, spk.per, d->part, ssd);
     tm_mark(d, DFLASH_ST_KPROJ);
-    dfl::conv0(st, d->x, d->part, spk.S, ssd, mbase, B, hs, d->gs, d->kn, d->xca, d->dsum_m);
+    dfl::conv0(st, d->x, d->part, spk.S, ssd, mbase, B, hs, d->gs, d->kn, d->xca, psh,
+               d->dsum_m);
     tm_mark(d, DFLASH_ST_CONV);
-    dfl::gemm_glu(st, d->xca, hs, d->gu.codes + i4l_gu * 1024 * l, d->gu.scales + i4l_gu * 64 * l,
-                  d->ffn / 16, d->ma);
+    dfl::gemm_glu(st, d->xca, psh, hs, d->gu.codes + i4l_gu * 1024 * l,
+                  d->gu.scales + i4l_gu * 64 * l, d->ffn / 16, d->ma, psm);
     tm_mark(d, DFLASH_ST_GLU);
-    dfl::gemm_i4(st, kRDown, d->ma, d->ffn, 1, d->down.codes + i4l_dn * 1024 * l,
+    dfl::gemm_i4(st, kRDown, d->ma, psm, d->ffn, 1, d->down.codes + i4l_dn * 1024 * l,
                  d->down.scales + i4l_dn * 64 * l, dfl::TileMap{d->down.tiles, d->down.tiles, 0, 0},
                  hs, sdn.S, sdn.per, d->part, ssh);
     tm_mark(d, DFLASH_ST_DOWN);
     const float* next = l + 1 < d->L ? d->in_norm + (size_t)(l + 1) * hs : d->norm;
     dfl::conv1(st, d->h, d->part, sdn.S, ssh, d->dsum_m, mbase, B, hs, d->gs, d->kn, d->sqp);
     tm_mark(d, DFLASH_ST_CONV);
-    dfl::norm_apply(st, d->h, d->sqp, B, hs, next, d->eps, d->x, d->xa);
+    dfl::norm_apply(st, d->h, d->sqp, B, hs, next, d->eps, d->x, d->xa, psh);
     tm_mark(d, DFLASH_ST_CONV);
+    if (d->trace)
+      (void)hipMemcpyAsync(d->trace + (size_t)l * B * hs, d->h, sizeof(float) * B * hs,
+                           hipMemcpyDeviceToDevice, st);
   }
   // head over rows 1..k and the selector projection
   float* lg = logits ? logits : d->logits;
-  dfl::head_sel(st, d->xa, hs, d->head, width, k, lg, d->sel, d->rank, d->hp, d->sel_sc);
+  dfl::head_sel(st, d->xa, psh, hs, d->head, width, k, lg, d->sel, d->rank, d->hp, d->sel_sc);
   tm_mark(d, DFLASH_ST_HEAD);
   dfl::select_all(st, lg, true, k, width, d->top, d->hp + d->rank, d->rank, d->pbook, d->cbook,
                   d->V, anchor, nullptr, d->sel_sc, cand, unary, score, chosen);
@@ -823,20 +833,22 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
   if (rc) return rc;
   if (cols > d->stage_cols) return fail(d, DFLASH_EINVAL, "matvec: matrix wider than the staging buffer");
   const int mb = (m + 15) / 16;
-  dfl::to_a(d->st, x, cols, m, cols, d->taps_a);
+  // the block's operands (m ≤ 16) carry two planes, the settle's one
+  const long ps = m <= 16 ? 16L * cols : 0;
+  dfl::to_a(d->st, x, cols, m, cols, d->taps_a, ps);
   const Split s = is_i4 ? split_for(map.ntiles, kRDebug, cols / 128, mb, 4)
                   : mb > 1 ? split_big(map.ntiles, cols / 32)
                            : split_for(map.ntiles, kRDebug, cols / 32, mb, 16);
   const long ss = (long)mb * 16 * rows;
   if ((long)s.S * ss > d->part_floats) return fail(d, DFLASH_EINVAL, "matvec: partials too large");
   if (is_i4)
-    dfl::gemm_i4(d->st, kRDebug, d->taps_a, cols, mb, static_cast<const uint8_t*>(codes), scales, map, rows,
+    dfl::gemm_i4(d->st, kRDebug, d->taps_a, ps, cols, mb, static_cast<const uint8_t*>(codes), scales, map, rows,
                  s.S, s.per, d->part, ss);
   else if (mb > 1)
     dfl::gemm_big_f16(d->st, d->taps_a, cols, mb, static_cast<const uint16_t*>(codes), map, rows,
                       s.S, s.per, d->part, ss);
   else
-    dfl::gemm_f16(d->st, kRDebug, d->taps_a, cols, mb, static_cast<const uint16_t*>(codes), map, rows, s.S,
+    dfl::gemm_f16(d->st, kRDebug, d->taps_a, ps, cols, mb, static_cast<const uint16_t*>(codes), map, rows, s.S,
                   s.per, d->part, ss);
   dfl::sum_rows(d->st, d->part, s.S, ss, m, rows, y);
   return launch_check(d, "matvec");
@@ -890,6 +902,12 @@ int dflash_debug_last_block(dflash_t* d, float* hidden, float* hp) {
                                      hipMemcpyDeviceToDevice, d->st),
                    "last_block");
   return rc;
+}
+
+int dflash_debug_set_trace(dflash_t* d, float* trace) {
+  if (!d) return DFLASH_EINVAL;
+  d->trace = trace;
+  return DFLASH_OK;
 }
 
 int dflash_debug_select(dflash_t* d, const float* logits, const float* hp, int32_t k,

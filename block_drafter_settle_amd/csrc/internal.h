@@ -8,6 +8,12 @@
 // so one 16x16x32 MFMA step s reads the contiguous 1 KB [s·64·8, (s+1)·64·8)
 // and lane l gets row l%16, columns 32s + 8(l/16) .. +7. Rows past M are 0.
 //
+// Planes: an operand may carry a second A-layout array ("plane 1") at
+// `ps` halves past the first, holding f16(v − f16(v)) of each value v.
+// GEMMs then add both planes' products, which carries the f32 activation
+// with about 22 significant bits instead of f16's 11. ps = 0 means a single
+// plane. Writers of A-layout take the same ps.
+//
 // F16T (dense f16 weights [N][K]): 16-row tiles, each tile 32 columns at a
 // time: tile t, step s, lane l holds W[16t + l%16][32s + 8(l/16) .. +7] at
 // half index ((t·KS + s)·64 + l)·8, KS = K/32.
@@ -38,20 +44,22 @@ struct TileMap {
 
 // GEMM launches: out[split][mb·16 + m][col] partial sums (f32), col < N.
 // R = row tiles per wave (1, 2 or 4); a workgroup covers 4·R tiles.
-void gemm_f16(hipStream_t st, int R, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
-              TileMap map, int N, int splits, int steps_per_split, float* out, long split_stride);
-void gemm_i4(hipStream_t st, int R, const uint16_t* xa, int K, int mblocks, const uint8_t* codes,
-             const uint16_t* scales, TileMap map, int N, int splits, int spans_per_split,
-             float* out, long split_stride);
-// Many-row f16 GEMM (mblocks ≤ 16 row blocks at once, 8 weight tiles per
-// block, LDS double buffered); out as gemm_f16.
+void gemm_f16(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblocks,
+              const uint16_t* w, TileMap map, int N, int splits, int steps_per_split, float* out,
+              long split_stride);
+void gemm_i4(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblocks,
+             const uint8_t* codes, const uint16_t* scales, TileMap map, int N, int splits,
+             int spans_per_split, float* out, long split_stride);
+// Many-row f16 GEMM (mblocks ≤ 16 row blocks at once, 16 weight tiles per
+// block, async copies into a 4-stage LDS ring; one plane); out as gemm_f16.
 void gemm_big_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
                   TileMap map, int N, int splits, int steps_per_split, float* out,
                   long split_stride);
 // gate/up with the SwiGLU epilogue: gate tiles [0, ftiles), up tiles
-// [ftiles, 2·ftiles) of one stored matrix; writes silu(g)·u in A-layout.
-void gemm_glu(hipStream_t st, const uint16_t* xa, int K, const uint8_t* codes,
-              const uint16_t* scales, int ftiles, uint16_t* ma);
+// [ftiles, 2·ftiles) of one stored matrix; writes silu(g)·u in A-layout
+// planes (ma, mps).
+void gemm_glu(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
+              const uint16_t* scales, int ftiles, uint16_t* ma, long mps);
 // Scratch of the selection: gmax [k][ceil(width/256)] column-group maxima,
 // thr [k], counters [16], the candidate lists lv/li [k][topk_cap], and the
 // score table tab [top·(1 + 15·top)].
@@ -67,34 +75,36 @@ struct SelectScratch {
 // Logits of rows 1..k over head tiles [0, ceil(width/16)) and the selector
 // projection hp [16][rank] of all rows, in one launch; also the selection's
 // column-group maxima.
-void head_sel(hipStream_t st, const uint16_t* xa, int K, const uint16_t* head, int width,
-              int k, float* logits, const uint16_t* sel, int rank, float* hp, SelectScratch sc);
+void head_sel(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t* head,
+              int width, int k, float* logits, const uint16_t* sel, int rank, float* hp,
+              SelectScratch sc);
 
-void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa);
+void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa, long ps);
 // Row kernels: sqp holds each (row, 256-channel chunk)'s sum of squares.
 void rowsum_sq(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,
                float* out, float* sqp);
 void norm_apply(hipStream_t st, const float* h, const float* sqp, int rows, int N, const float* w,
-                float eps, float* x, uint16_t* xa);
+                float eps, float* x, uint16_t* xa, long ps);
 void embed(hipStream_t st, const uint16_t* emb, int anchor, int mask, int rows, int hs, float* h,
            float* sqp);
 void conv0(hipStream_t st, const float* x, const float* dpart, int splits, long split_stride,
-           const float* base, int rows, int hs, int gs, int kn, uint16_t* xca, float* dsum);
+           const float* base, int rows, int hs, int gs, int kn, uint16_t* xca, long ps,
+           float* dsum);
 void conv1(hipStream_t st, float* h, const float* opart, int splits, long split_stride,
            const float* dsum, const float* base, int rows, int hs, int gs, int kn, float* sqp);
 void qkv_post(hipStream_t st, const float* part, int splits, long split_stride, int rows, int nh,
               int kv, int hd, const float* q_norm, const float* k_norm, const float* inv_freq,
-              long pos0, int rot, float eps, uint16_t* qa, float* kb, float* vb);
+              long pos0, int rot, float eps, uint16_t* qa, long qps, float* kb, float* vb);
 void settle_kv(hipStream_t st, const float* part, int splits, long split_stride, int rows,
                int layers, int kv, int hd, const float* k_norm, const float* inv_freq,
                const int* rot, long pos0, float eps, float* store_k, float* store_v, long cap,
                long row0);
-void attention(hipStream_t st, const uint16_t* qa, const float* sk, const float* sv,
+void attention(hipStream_t st, const uint16_t* qa, long qps, const float* sk, const float* sv,
                const float* kb, const float* vb, int B, int nh, int kv, int hd, int n,
                long lo_pos, long a, int window, int chunk, int nchunks, float scale,
                float* pacc, float* pml);
 void attn_merge(hipStream_t st, const float* pacc, const float* pml, int nh, int kv, int hd,
-                int nchunks, int B, uint16_t* ya);
+                int nchunks, int B, uint16_t* ya, long ps);
 // Selection (`top_k` + `select_with`) on logits [k][width] and hp rows
 // [k][rank]: cand/unary, the score table and the chain (score, chosen).
 // have_gmax: the head kernel already wrote the column-group maxima.

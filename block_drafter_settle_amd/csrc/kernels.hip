@@ -6,10 +6,13 @@
 // `top_k`. Operand layouts (A-layout, F16T, I4T, tile maps) are described
 // in internal.h.
 //
-// Every matrix product runs on v_mfma_f32_16x16x32_f16: activations are
-// rounded to f16, int4 codes enter the MFMA as exact small integers and
-// each 32-column group's partial is scaled by its f16 scale in f32, so the
-// dequantised weight q·s is used exactly. Accumulation is f32 throughout.
+// Every matrix product runs on v_mfma_f32_16x16x32_f16. An activation
+// operand is one or two f16 planes (internal.h): with two, the product is
+// the sum of both planes' products, so the f32 activation enters with about
+// 22 significant bits. int4 codes enter the MFMA as exact small integers
+// and each 32-column group's partial is scaled by its f16 scale in f32, so
+// the dequantised weight q·s is used exactly. Accumulation is f32
+// throughout.
 #include "internal.h"
 
 #include <algorithm>
@@ -33,6 +36,14 @@ __device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
 // A-layout half index of (m, k) inside one 16-row block.
 __device__ __forceinline__ size_t a_idx(int m, int k) {
   return ((size_t)(k >> 5) * 64 + ((k >> 3) & 3) * 16 + (m & 15)) * 8 + (k & 7);
+}
+
+// Stores v at A-layout index idx: plane 0 its f16 rounding and, when ps (the
+// plane stride in halves) is nonzero, plane 1 the f16 rounding of what is left.
+__device__ __forceinline__ void put_a(f16* xa, long ps, size_t idx, float v) {
+  const f16 hi = (f16)v;
+  xa[idx] = hi;
+  if (ps) xa[ps + idx] = (f16)(v - (float)hi);
 }
 
 __device__ __forceinline__ long map_tile(const TileMap& mp, int t) {
@@ -90,9 +101,10 @@ __device__ __forceinline__ h8 unpack_i4(uint32_t w) {
 
 // ------------------------------------------------------------------ GEMMs
 
-// Skinny GEMM, f16 weights: each wave owns R row tiles over its K split.
-template <int R>
-__global__ __launch_bounds__(kThreads) void k_gemm_f16(const f16* __restrict__ xa, int K,
+// Skinny GEMM, f16 weights: each wave owns R row tiles over its K split;
+// PL activation planes, plane 1 at xa + ps.
+template <int R, int PL>
+__global__ __launch_bounds__(kThreads) void k_gemm_f16(const f16* __restrict__ xa, long ps, int K,
                                                        const f16* __restrict__ w, TileMap mp,
                                                        int N, int sps, float* __restrict__ out,
                                                        long split_stride) {
@@ -103,6 +115,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_f16(const f16* __restrict__ x
   const int t0 = (blockIdx.x * 4 + wave) * R;
   if (t0 >= mp.ntiles) return;
   const h8* xp = reinterpret_cast<const h8*>(xa + (size_t)mb * 16 * K) + lane;
+  const h8* xq = reinterpret_cast<const h8*>(xa + ps * (PL - 1) + (size_t)mb * 16 * K) + lane;
   const h8* wp[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -114,22 +127,32 @@ __global__ __launch_bounds__(kThreads) void k_gemm_f16(const f16* __restrict__ x
   for (int r = 0; r < R; ++r) acc[r] = (f4){0.f, 0.f, 0.f, 0.f};
   int s = s0;
   for (; s + 4 <= s1; s += 4) {
-    h8 a[4], b[4][R];
+    h8 a[4], a2[4], b[4][R];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       a[u] = xp[(size_t)(s + u) * 64];
+      if (PL == 2) a2[u] = xq[(size_t)(s + u) * 64];
 #pragma unroll
       for (int r = 0; r < R; ++r) b[u][r] = wp[r][(size_t)(s + u) * 64];
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = mfma16(a[u], b[u][r], acc[r]);
+      for (int r = 0; r < R; ++r) {
+        acc[r] = mfma16(a[u], b[u][r], acc[r]);
+        if (PL == 2) acc[r] = mfma16(a2[u], b[u][r], acc[r]);
+      }
   }
   for (; s < s1; ++s) {
     const h8 a = xp[(size_t)s * 64];
+    h8 a2;
+    if (PL == 2) a2 = xq[(size_t)s * 64];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = mfma16(a, wp[r][(size_t)s * 64], acc[r]);
+    for (int r = 0; r < R; ++r) {
+      const h8 b = wp[r][(size_t)s * 64];
+      acc[r] = mfma16(a, b, acc[r]);
+      if (PL == 2) acc[r] = mfma16(a2, b, acc[r]);
+    }
   }
   float* o = out + (size_t)sp * split_stride + (size_t)mb * 16 * N;
   const int j = lane >> 4, n = lane & 15;
@@ -244,9 +267,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big_f16(const f16* __restr
   }
 }
 
-// One 128-column span of R int4 tiles against four A-layout steps.
-template <int R>
-__device__ __forceinline__ void i4_span(const uint4* c, const uint2* sc, const h8* a, f4* acc) {
+// One 128-column span of R int4 tiles against four A-layout steps of PL
+// planes (a, a2).
+template <int R, int PL>
+__device__ __forceinline__ void i4_span(const uint4* c, const uint2* sc, const h8* a, const h8* a2,
+                                        f4* acc) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -254,14 +279,26 @@ __device__ __forceinline__ void i4_span(const uint4* c, const uint2* sc, const h
       const uint32_t word = u == 0 ? c[r].x : u == 1 ? c[r].y : u == 2 ? c[r].z : c[r].w;
       const uint32_t sb = u < 2 ? sc[r].x : sc[r].y;
       const float s = half_bits((u & 1) ? (sb >> 16) : sb);
-      const f4 t = mfma16(a[u], unpack_i4(word), (f4){0.f, 0.f, 0.f, 0.f});
+      const h8 q = unpack_i4(word);
+      f4 t = mfma16(a[u], q, (f4){0.f, 0.f, 0.f, 0.f});
+      if (PL == 2) t = mfma16(a2[u], q, t);
       acc[r] += s * t;
     }
   }
 }
 
-template <int R>
-__global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa, int K,
+// The A fragments of span p: four steps of each plane.
+template <int PL>
+__device__ __forceinline__ void load_span(const h8* xp, const h8* xq, int p, h8* a, h8* a2) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    a[u] = xp[(size_t)(4 * p + u) * 64];
+    if (PL == 2) a2[u] = xq[(size_t)(4 * p + u) * 64];
+  }
+}
+
+template <int R, int PL>
+__global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa, long ps, int K,
                                                       const uint4* __restrict__ codes,
                                                       const uint2* __restrict__ scales,
                                                       TileMap mp, int N, int pps,
@@ -273,6 +310,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa
   const int t0 = (blockIdx.x * 4 + wave) * R;
   if (t0 >= mp.ntiles) return;
   const h8* xp = reinterpret_cast<const h8*>(xa + (size_t)mb * 16 * K) + lane;
+  const h8* xq = reinterpret_cast<const h8*>(xa + ps * (PL - 1) + (size_t)mb * 16 * K) + lane;
   const uint4* cp[R];
   const uint2* scp[R];
 #pragma unroll
@@ -288,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa
   for (; p + 2 <= p1; p += 2) {
     uint4 c0[R], c1[R];
     uint2 s0[R], s1[R];
-    h8 a0[4], a1[4];
+    h8 a0[4], a1[4], b0[4], b1[4];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       c0[r] = cp[r][(size_t)p * 64];
@@ -296,26 +334,22 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa
       s0[r] = scp[r][(size_t)p * 16];
       s1[r] = scp[r][(size_t)(p + 1) * 16];
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a0[u] = xp[(size_t)(4 * p + u) * 64];
-      a1[u] = xp[(size_t)(4 * p + 4 + u) * 64];
-    }
-    i4_span<R>(c0, s0, a0, acc);
-    i4_span<R>(c1, s1, a1, acc);
+    load_span<PL>(xp, xq, p, a0, b0);
+    load_span<PL>(xp, xq, p + 1, a1, b1);
+    i4_span<R, PL>(c0, s0, a0, b0, acc);
+    i4_span<R, PL>(c1, s1, a1, b1, acc);
   }
   if (p < p1) {
     uint4 c0[R];
     uint2 s0[R];
-    h8 a0[4];
+    h8 a0[4], b0[4];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       c0[r] = cp[r][(size_t)p * 64];
       s0[r] = scp[r][(size_t)p * 16];
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) a0[u] = xp[(size_t)(4 * p + u) * 64];
-    i4_span<R>(c0, s0, a0, acc);
+    load_span<PL>(xp, xq, p, a0, b0);
+    i4_span<R, PL>(c0, s0, a0, b0, acc);
   }
   float* o = out + (size_t)sp * split_stride + (size_t)mb * 16 * N;
   const int j = lane >> 4, n = lane & 15;
@@ -331,15 +365,19 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa
 // gate/up over the full K, SwiGLU in the epilogue (`mlp`: silu(g)·u with
 // silu(a) = a/(1+e^−a)). Each wave owns one ffn tile: gate tile ft and up
 // tile ffn_tiles + ft of the stored matrix, so g and u meet in registers.
-__global__ __launch_bounds__(kThreads) void k_gemm_glu(const f16* __restrict__ xa, int K,
+// Input of PL planes (xa, ps); the output in A-layout planes (ma, mps).
+template <int PL>
+__global__ __launch_bounds__(kThreads) void k_gemm_glu(const f16* __restrict__ xa, long ps, int K,
                                                        const uint4* __restrict__ codes,
                                                        const uint2* __restrict__ scales,
-                                                       int ftiles, f16* __restrict__ ma) {
+                                                       int ftiles, f16* __restrict__ ma,
+                                                       long mps) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int KT = K >> 7;
   const int ft = blockIdx.x * 4 + wave;
   if (ft >= ftiles) return;
   const h8* xp = reinterpret_cast<const h8*>(xa) + lane;
+  const h8* xq = reinterpret_cast<const h8*>(xa + ps * (PL - 1)) + lane;
   const uint4* cp[2] = {codes + (size_t)ft * KT * 64 + lane,
                         codes + (size_t)(ftiles + ft) * KT * 64 + lane};
   const uint2* scp[2] = {scales + (size_t)ft * KT * 16 + (lane & 15),
@@ -349,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_glu(const f16* __restrict__ x
   for (; p + 2 <= KT; p += 2) {
     uint4 c0[2], c1[2];
     uint2 s0[2], s1[2];
-    h8 a0[4], a1[4];
+    h8 a0[4], a1[4], b0[4], b1[4];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       c0[r] = cp[r][(size_t)p * 64];
@@ -357,32 +395,28 @@ __global__ __launch_bounds__(kThreads) void k_gemm_glu(const f16* __restrict__ x
       s0[r] = scp[r][(size_t)p * 16];
       s1[r] = scp[r][(size_t)(p + 1) * 16];
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a0[u] = xp[(size_t)(4 * p + u) * 64];
-      a1[u] = xp[(size_t)(4 * p + 4 + u) * 64];
-    }
-    i4_span<2>(c0, s0, a0, acc);
-    i4_span<2>(c1, s1, a1, acc);
+    load_span<PL>(xp, xq, p, a0, b0);
+    load_span<PL>(xp, xq, p + 1, a1, b1);
+    i4_span<2, PL>(c0, s0, a0, b0, acc);
+    i4_span<2, PL>(c1, s1, a1, b1, acc);
   }
   if (p < KT) {
     uint4 c0[2];
     uint2 s0[2];
-    h8 a0[4];
+    h8 a0[4], b0[4];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       c0[r] = cp[r][(size_t)p * 64];
       s0[r] = scp[r][(size_t)p * 16];
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) a0[u] = xp[(size_t)(4 * p + u) * 64];
-    i4_span<2>(c0, s0, a0, acc);
+    load_span<PL>(xp, xq, p, a0, b0);
+    i4_span<2, PL>(c0, s0, a0, b0, acc);
   }
   const int j = lane >> 4, n = lane & 15;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const float g = acc[0][v];
-    ma[a_idx(4 * j + v, ft * 16 + n)] = (f16)(g / (1.f + expf(-g)) * acc[1][v]);
+    put_a(ma, mps, a_idx(4 * j + v, ft * 16 + n), g / (1.f + expf(-g)) * acc[1][v]);
   }
 }
 
@@ -391,7 +425,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_glu(const f16* __restrict__ x
 // Head blocks also record, per draft row, the largest logit of each 256
 // columns (gmax [k][head_groups]) for the selection's threshold, and block
 // 0 clears the selection's candidate counters.
-__global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, int K,
+template <int PL>
+__global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, long ps, int K,
                                                    const f16* __restrict__ head, int wtiles,
                                                    int width, int k, float* __restrict__ logits,
                                                    const f16* __restrict__ sel, int stiles,
@@ -412,28 +447,39 @@ __global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, i
   for (int r = 0; r < R; ++r) acc[r] = (f4){0.f, 0.f, 0.f, 0.f};
   if (t0 < ntiles) {
     const h8* xp = reinterpret_cast<const h8*>(xa) + lane;
+    const h8* xq = reinterpret_cast<const h8*>(xa + ps * (PL - 1)) + lane;
     const h8* wp[R];
 #pragma unroll
     for (int r = 0; r < R; ++r)
       wp[r] = reinterpret_cast<const h8*>(w) + (size_t)min(t0 + r, ntiles - 1) * KS * 64 + lane;
     int s = 0;
     for (; s + 4 <= KS; s += 4) {
-      h8 a[4], b[4][R];
+      h8 a[4], a2[4], b[4][R];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         a[u] = xp[(size_t)(s + u) * 64];
+        if (PL == 2) a2[u] = xq[(size_t)(s + u) * 64];
 #pragma unroll
         for (int r = 0; r < R; ++r) b[u][r] = wp[r][(size_t)(s + u) * 64];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = mfma16(a[u], b[u][r], acc[r]);
+        for (int r = 0; r < R; ++r) {
+          acc[r] = mfma16(a[u], b[u][r], acc[r]);
+          if (PL == 2) acc[r] = mfma16(a2[u], b[u][r], acc[r]);
+        }
     }
     for (; s < KS; ++s) {
       const h8 a = xp[(size_t)s * 64];
+      h8 a2;
+      if (PL == 2) a2 = xq[(size_t)s * 64];
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = mfma16(a, wp[r][(size_t)s * 64], acc[r]);
+      for (int r = 0; r < R; ++r) {
+        const h8 b = wp[r][(size_t)s * 64];
+        acc[r] = mfma16(a, b, acc[r]);
+        if (PL == 2) acc[r] = mfma16(a2, b, acc[r]);
+      }
     }
   }
   const int j = lane >> 4, n = lane & 15;
@@ -472,22 +518,31 @@ __global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, i
 
 // ----------------------------------------------------------- row kernels
 
-// f32 rows → A-layout f16; one thread per 8 columns of one row.
+// f32 rows → A-layout f16 (plane 1 at xa + ps when ps is nonzero); one
+// thread per 8 columns of one row.
 __global__ __launch_bounds__(kThreads) void k_to_a(const float* __restrict__ x, long ld, int m,
-                                                   int K, f16* __restrict__ xa) {
+                                                   int K, f16* __restrict__ xa, long ps) {
   const int mb = blockIdx.y;
   const long t = (long)blockIdx.x * kThreads + threadIdx.x;
   if (t >= (long)(K >> 3) * 16) return;
   const int i = t & 15, j = (t >> 4) & 3;
   const long s = t >> 6;
   const int row = mb * 16 + i;
-  h8 v = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+  float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (row < m) {
     const float4* p = reinterpret_cast<const float4*>(x + (size_t)row * ld + s * 32 + j * 8);
     const float4 lo = p[0], hi = p[1];
-    v = (h8){(f16)lo.x, (f16)lo.y, (f16)lo.z, (f16)lo.w, (f16)hi.x, (f16)hi.y, (f16)hi.z, (f16)hi.w};
+    f[0] = lo.x, f[1] = lo.y, f[2] = lo.z, f[3] = lo.w;
+    f[4] = hi.x, f[5] = hi.y, f[6] = hi.z, f[7] = hi.w;
+  }
+  h8 v, r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    v[e] = (f16)f[e];
+    r[e] = (f16)(f[e] - (float)v[e]);
   }
   reinterpret_cast<h8*>(xa + (size_t)mb * 16 * K)[t] = v;
+  if (ps) reinterpret_cast<h8*>(xa + ps + (size_t)mb * 16 * K)[t] = r;
 }
 
 // The row kernels below split each row into chunks of kChunk channels, one
@@ -517,7 +572,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_apply(const float* __restrict
                                                          int nchunk, int N,
                                                          const float* __restrict__ w, float eps,
                                                          float* __restrict__ x,
-                                                         f16* __restrict__ xa) {
+                                                         f16* __restrict__ xa, long ps) {
   __shared__ float part[kThreads];
   const int r = blockIdx.y, c = blockIdx.x, i = c * kChunk + threadIdx.x;
   if (threadIdx.x < nchunk) part[threadIdx.x] = sqp[(size_t)r * nchunk + threadIdx.x];
@@ -528,7 +583,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_apply(const float* __restrict
   if (i >= N) return;
   const float y = h[(size_t)r * N + i] * scale * w[i];
   if (x) x[(size_t)r * N + i] = y;
-  xa[(size_t)(r >> 4) * 16 * N + a_idx(r & 15, i)] = (f16)y;
+  put_a(xa, ps, (size_t)(r >> 4) * 16 * N + a_idx(r & 15, i), y);
 }
 
 // The block's rows [E[anchor], E[mask]…] (f16 → f32) and each chunk's Σh².
@@ -554,7 +609,7 @@ __global__ __launch_bounds__(kThreads) void k_conv0(const float* __restrict__ x,
                                                     const float* __restrict__ dpart, int splits,
                                                     long ss, const float* __restrict__ base,
                                                     int hs, int gs, int kn, int gpw,
-                                                    f16* __restrict__ xca,
+                                                    f16* __restrict__ xca, long ps,
                                                     float* __restrict__ dsum) {
   extern __shared__ float dl[];  // [2·kn][ng]
   const int r = blockIdx.y;
@@ -573,7 +628,7 @@ __global__ __launch_bounds__(kThreads) void k_conv0(const float* __restrict__ x,
     float acc = 0.f;
     for (int o = 0; o < taps; ++o)
       acc += (base[(size_t)o * hs + i] + dl[o * ng + g]) * x[(size_t)(r - o) * hs + i];
-    xca[a_idx(r, i)] = (f16)acc;
+    put_a(xca, ps, a_idx(r, i), acc);
   }
 }
 
@@ -664,7 +719,8 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ part,
                                                  const float* __restrict__ kn,
                                                  const float* __restrict__ inv, long pos0,
                                                  int rot, float eps, f16* __restrict__ qa,
-                                                 float* __restrict__ kb, float* __restrict__ vb) {
+                                                 long qps, float* __restrict__ kb,
+                                                 float* __restrict__ vb) {
   const int r = blockIdx.x, hh = blockIdx.y;
   const int qd = nh * hd, kd = kv * hd, N = qd + 2 * kd, half = hd >> 1;
   const int col0 = hh < nh ? hh * hd : (hh < nh + kv ? qd + (hh - nh) * hd : qd + kd + (hh - nh - kv) * hd);
@@ -676,8 +732,8 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ part,
     if (i >= half) continue;
     if (hh < nh) {
       f16* q = qa + (size_t)hh * 16 * hd;
-      q[a_idx(r, i)] = (f16)p.lo[c];
-      q[a_idx(r, i + half)] = (f16)p.hi[c];
+      put_a(q, qps, a_idx(r, i), p.lo[c]);
+      put_a(q, qps, a_idx(r, i + half), p.hi[c]);
     } else {
       float* dst = hh < nh + kv ? kb + (size_t)r * kd + (hh - nh) * hd
                                 : vb + (size_t)r * kd + (hh - nh - kv) * hd;
@@ -718,11 +774,14 @@ __global__ __launch_bounds__(64) void k_settle_kv(const float* __restrict__ part
 // kv head g, its q heads 4z..4z+3, and key chunk c — context keys
 // [c·chunk, min(n, (c+1)·chunk)) of the layer's range, or for c == nchunks
 // the block's own B keys. Each wave keeps one q head's 16 query rows and an
-// online softmax over 32-key steps: S^T = K·Q^T and O^T += V^T·P^T on MFMA,
-// K and V converted to f16 in LDS. Writes the chunk's (max, sum, O) for the
+// online softmax over 32-key steps: S^T = K·Q^T and O^T += V^T·P^T on MFMA.
+// Every operand is an f16 pair (hi, lo = f16 of the rest): q's two A-layout
+// planes (plane 1 at qa + qps), K and V split into two LDS planes, P split
+// in registers; each product takes hi·hi + hi·lo + lo·hi, the dropped lo·lo
+// term lying below f32 rounding. Writes the chunk's (max, sum, O) for the
 // merge.
 template <int HD>
-__global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa,
+__global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, long qps,
                                                    const float* __restrict__ sk,
                                                    const float* __restrict__ sv,
                                                    const float* __restrict__ kb,
@@ -734,8 +793,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa,
   constexpr int KST = HD + 8;   // LDS row stride of K (halfs)
   constexpr int VST = 32 + 8;   // LDS row stride of V^T (halfs)
   constexpr int EPT = HD / 8;   // staged elements per thread per 32 keys
-  __shared__ f16 Ks[32 * KST];
-  __shared__ f16 Vt[HD * VST];
+  __shared__ f16 Ks[2][32 * KST];
+  __shared__ f16 Vt[2][HD * VST];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = blockIdx.x, g = blockIdx.y;
   const int rep = nh / kv;
@@ -750,10 +809,13 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa,
   const float* vbase = blk ? vb + (size_t)g * HD : sv + (size_t)k_first * kd + (size_t)g * HD;
   const long pos_base = lo_pos + k_first;
 
-  h8 qf[HD / 32];
+  h8 qf[HD / 32], ql[HD / 32];
 #pragma unroll
-  for (int s = 0; s < HD / 32; ++s)
-    qf[s] = *reinterpret_cast<const h8*>(qa + (size_t)hq * 16 * HD + ((size_t)s * 64 + lane) * 8);
+  for (int s = 0; s < HD / 32; ++s) {
+    const size_t off = (size_t)hq * 16 * HD + ((size_t)s * 64 + lane) * 8;
+    qf[s] = *reinterpret_cast<const h8*>(qa + off);
+    ql[s] = *reinterpret_cast<const h8*>(qa + qps + off);
+  }
 
   const int r = lane & 15, j = lane >> 4;
   const long lim = window > 0 ? a + r + 1 - window : LONG_MIN;
@@ -780,13 +842,19 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa,
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < EPT / 4; ++e) {
-      const float4 kk = kreg[e], vv = vreg[e];
-      *reinterpret_cast<h4*>(&Ks[skey * KST + sd0 + 4 * e]) =
-          (h4){(f16)kk.x, (f16)kk.y, (f16)kk.z, (f16)kk.w};
-      Vt[(sd0 + 4 * e + 0) * VST + skey] = (f16)vv.x;
-      Vt[(sd0 + 4 * e + 1) * VST + skey] = (f16)vv.y;
-      Vt[(sd0 + 4 * e + 2) * VST + skey] = (f16)vv.z;
-      Vt[(sd0 + 4 * e + 3) * VST + skey] = (f16)vv.w;
+      const float kf[4] = {kreg[e].x, kreg[e].y, kreg[e].z, kreg[e].w};
+      const float vf[4] = {vreg[e].x, vreg[e].y, vreg[e].z, vreg[e].w};
+      h4 khi, klo;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        khi[q] = (f16)kf[q];
+        klo[q] = (f16)(kf[q] - (float)khi[q]);
+        const f16 vh = (f16)vf[q];
+        Vt[0][(sd0 + 4 * e + q) * VST + skey] = vh;
+        Vt[1][(sd0 + 4 * e + q) * VST + skey] = (f16)(vf[q] - (float)vh);
+      }
+      *reinterpret_cast<h4*>(&Ks[0][skey * KST + sd0 + 4 * e]) = khi;
+      *reinterpret_cast<h4*>(&Ks[1][skey * KST + sd0 + 4 * e]) = klo;
     }
     __syncthreads();
     if (k0 + 32 < count) fetch(k0 + 32);
@@ -798,8 +866,12 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa,
       st[hb] = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < HD / 32; ++s) {
-        const h8 ka = *reinterpret_cast<const h8*>(&Ks[(16 * hb + (lane & 15)) * KST + 32 * s + 8 * j]);
+        const int off = (16 * hb + (lane & 15)) * KST + 32 * s + 8 * j;
+        const h8 ka = *reinterpret_cast<const h8*>(&Ks[0][off]);
+        const h8 kl = *reinterpret_cast<const h8*>(&Ks[1][off]);
         st[hb] = mfma16(ka, qf[s], st[hb]);
+        st[hb] = mfma16(ka, ql[s], st[hb]);
+        st[hb] = mfma16(kl, qf[s], st[hb]);
       }
     }
     float p[8];
@@ -826,15 +898,24 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa,
     ps += __shfl_xor(ps, 32, 64);
     l_run = l_run * corr + ps;
     m_run = m_new;
-    const h8 pb = (h8){(f16)p[0], (f16)p[1], (f16)p[2], (f16)p[3],
-                       (f16)p[4], (f16)p[5], (f16)p[6], (f16)p[7]};
+    h8 pb, pl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pb[e] = (f16)p[e];
+      pl[e] = (f16)(p[e] - (float)pb[e]);
+    }
 #pragma unroll
     for (int d = 0; d < HD / 16; ++d) {
-      const f16* vrow = &Vt[(16 * d + (lane & 15)) * VST];
-      const h4 v0 = *reinterpret_cast<const h4*>(vrow + 4 * j);
-      const h4 v1 = *reinterpret_cast<const h4*>(vrow + 16 + 4 * j);
+      const int off = (16 * d + (lane & 15)) * VST + 4 * j;
+      const h4 v0 = *reinterpret_cast<const h4*>(&Vt[0][off]);
+      const h4 v1 = *reinterpret_cast<const h4*>(&Vt[0][off + 16]);
+      const h4 w0 = *reinterpret_cast<const h4*>(&Vt[1][off]);
+      const h4 w1 = *reinterpret_cast<const h4*>(&Vt[1][off + 16]);
       const h8 va = (h8){v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      acc[d] = mfma16(va, pb, acc[d] * corr);
+      const h8 vl = (h8){w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      f4 t = mfma16(va, pb, acc[d] * corr);
+      t = mfma16(va, pl, t);
+      acc[d] = mfma16(vl, pb, t);
     }
   }
   if (!active) return;
@@ -853,7 +934,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa,
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pacc,
                                                     const float2* __restrict__ pml, int nh,
                                                     int kv, int hd, int nchunks,
-                                                    f16* __restrict__ ya) {
+                                                    f16* __restrict__ ya, long ps) {
   __shared__ float fw[256], red[4], redl[4];
   const int hq = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
@@ -883,7 +964,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
     y1 += pacc[((slot0 + (size_t)(c + 1) * rep) * 16 + r) * hd + t] * fw[c + 1];
   }
   if (c < nc) y0 += pacc[((slot0 + (size_t)c * rep) * 16 + r) * hd + t] * fw[c];
-  ya[a_idx(r, hq * hd + t)] = (f16)((y0 + y1) / L);
+  put_a(ya, ps, a_idx(r, hq * hd + t), (y0 + y1) / L);
 }
 
 // ------------------------------------------------------- top-k, selector
@@ -1216,22 +1297,34 @@ __global__ void k_sum_rows(const float* __restrict__ part, int splits, long ss, 
 
 static inline unsigned cdiv(long a, long b) { return (unsigned)((a + b - 1) / b); }
 
-template <int R>
-static void launch_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
-                       TileMap map, int N, int splits, int sps, float* out, long ss) {
+template <int R, int PL>
+static void launch_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks,
+                       const uint16_t* w, TileMap map, int N, int splits, int sps, float* out,
+                       long ss) {
   dim3 grid(cdiv(map.ntiles, 4 * R), splits, mblocks);
-  k_gemm_f16<R><<<grid, kThreads, 0, st>>>(reinterpret_cast<const f16*>(xa), K,
-                                           reinterpret_cast<const f16*>(w), map, N, sps, out, ss);
+  k_gemm_f16<R, PL><<<grid, kThreads, 0, st>>>(reinterpret_cast<const f16*>(xa), ps, K,
+                                               reinterpret_cast<const f16*>(w), map, N, sps, out,
+                                               ss);
 }
 
-void gemm_f16(hipStream_t st, int R, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
-              TileMap map, int N, int splits, int sps, float* out, long ss) {
+template <int PL>
+static void pick_f16(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblocks,
+                     const uint16_t* w, TileMap map, int N, int splits, int sps, float* out,
+                     long ss) {
   if (R == 1)
-    launch_f16<1>(st, xa, K, mblocks, w, map, N, splits, sps, out, ss);
+    launch_f16<1, PL>(st, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
   else if (R == 2)
-    launch_f16<2>(st, xa, K, mblocks, w, map, N, splits, sps, out, ss);
+    launch_f16<2, PL>(st, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
   else
-    launch_f16<4>(st, xa, K, mblocks, w, map, N, splits, sps, out, ss);
+    launch_f16<4, PL>(st, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
+}
+
+void gemm_f16(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblocks,
+              const uint16_t* w, TileMap map, int N, int splits, int sps, float* out, long ss) {
+  if (ps)
+    pick_f16<2>(st, R, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
+  else
+    pick_f16<1>(st, R, xa, 0, K, mblocks, w, map, N, splits, sps, out, ss);
 }
 
 void gemm_big_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
@@ -1243,49 +1336,68 @@ void gemm_big_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const 
                                                 sps, out, ss);
 }
 
-template <int R>
-static void launch_i4(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint8_t* codes,
-                      const uint16_t* scales, TileMap map, int N, int splits, int pps, float* out,
-                      long ss) {
+template <int R, int PL>
+static void launch_i4(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks,
+                      const uint8_t* codes, const uint16_t* scales, TileMap map, int N, int splits,
+                      int pps, float* out, long ss) {
   dim3 grid(cdiv(map.ntiles, 4 * R), splits, mblocks);
-  k_gemm_i4<R><<<grid, kThreads, 0, st>>>(reinterpret_cast<const f16*>(xa), K,
-                                          reinterpret_cast<const uint4*>(codes),
-                                          reinterpret_cast<const uint2*>(scales), map, N, pps, out,
-                                          ss);
+  k_gemm_i4<R, PL><<<grid, kThreads, 0, st>>>(reinterpret_cast<const f16*>(xa), ps, K,
+                                              reinterpret_cast<const uint4*>(codes),
+                                              reinterpret_cast<const uint2*>(scales), map, N, pps,
+                                              out, ss);
 }
 
-void gemm_i4(hipStream_t st, int R, const uint16_t* xa, int K, int mblocks, const uint8_t* codes,
-             const uint16_t* scales, TileMap map, int N, int splits, int pps, float* out,
-             long ss) {
+template <int PL>
+static void pick_i4(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblocks,
+                    const uint8_t* codes, const uint16_t* scales, TileMap map, int N, int splits,
+                    int pps, float* out, long ss) {
   if (R == 1)
-    launch_i4<1>(st, xa, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
+    launch_i4<1, PL>(st, xa, ps, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
   else if (R == 2)
-    launch_i4<2>(st, xa, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
+    launch_i4<2, PL>(st, xa, ps, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
   else
-    launch_i4<4>(st, xa, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
+    launch_i4<4, PL>(st, xa, ps, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
 }
 
-void gemm_glu(hipStream_t st, const uint16_t* xa, int K, const uint8_t* codes,
-              const uint16_t* scales, int ftiles, uint16_t* ma) {
-  k_gemm_glu<<<cdiv(ftiles, 4), kThreads, 0, st>>>(reinterpret_cast<const f16*>(xa), K,
-                                                   reinterpret_cast<const uint4*>(codes),
-                                                   reinterpret_cast<const uint2*>(scales), ftiles,
-                                                   reinterpret_cast<f16*>(ma));
+void gemm_i4(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblocks,
+             const uint8_t* codes, const uint16_t* scales, TileMap map, int N, int splits, int pps,
+             float* out, long ss) {
+  if (ps)
+    pick_i4<2>(st, R, xa, ps, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
+  else
+    pick_i4<1>(st, R, xa, 0, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
 }
 
-void head_sel(hipStream_t st, const uint16_t* xa, int K, const uint16_t* head, int width, int k,
-              float* logits, const uint16_t* sel, int rank, float* hp, SelectScratch sc) {
+void gemm_glu(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
+              const uint16_t* scales, int ftiles, uint16_t* ma, long mps) {
+  const f16* x = reinterpret_cast<const f16*>(xa);
+  const uint4* c = reinterpret_cast<const uint4*>(codes);
+  const uint2* sc = reinterpret_cast<const uint2*>(scales);
+  f16* m = reinterpret_cast<f16*>(ma);
+  if (ps)
+    k_gemm_glu<2><<<cdiv(ftiles, 4), kThreads, 0, st>>>(x, ps, K, c, sc, ftiles, m, mps);
+  else
+    k_gemm_glu<1><<<cdiv(ftiles, 4), kThreads, 0, st>>>(x, 0, K, c, sc, ftiles, m, mps);
+}
+
+void head_sel(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t* head, int width,
+              int k, float* logits, const uint16_t* sel, int rank, float* hp, SelectScratch sc) {
   const int wtiles = cdiv(width, 16), stiles = cdiv(rank, 16);
   const int hg = cdiv(wtiles, 16), sg = cdiv(stiles, 16);
-  k_head<<<hg + sg, kThreads, 0, st>>>(reinterpret_cast<const f16*>(xa), K,
-                                       reinterpret_cast<const f16*>(head), wtiles, width, k, logits,
-                                       reinterpret_cast<const f16*>(sel), stiles, rank, hp, hg,
-                                       sc.gmax, sc.counters);
+  const f16* x = reinterpret_cast<const f16*>(xa);
+  const f16* hw = reinterpret_cast<const f16*>(head);
+  const f16* sw = reinterpret_cast<const f16*>(sel);
+  if (ps)
+    k_head<2><<<hg + sg, kThreads, 0, st>>>(x, ps, K, hw, wtiles, width, k, logits, sw, stiles,
+                                            rank, hp, hg, sc.gmax, sc.counters);
+  else
+    k_head<1><<<hg + sg, kThreads, 0, st>>>(x, 0, K, hw, wtiles, width, k, logits, sw, stiles,
+                                            rank, hp, hg, sc.gmax, sc.counters);
 }
 
-void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa) {
+void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa, long ps) {
   dim3 grid(cdiv((long)(K / 8) * 16, kThreads), cdiv(m, 16));
-  k_to_a<<<grid, kThreads, 0, st>>>(x, ld, m, K, reinterpret_cast<f16*>(xa));
+  k_to_a<<<grid, kThreads, 0, st>>>(x, ld, m, K, reinterpret_cast<f16*>(xa), ps);
 }
 
 void rowsum_sq(hipStream_t st, const float* part, int splits, long ss, int rows, int N,
@@ -1295,10 +1407,10 @@ void rowsum_sq(hipStream_t st, const float* part, int splits, long ss, int rows,
 }
 
 void norm_apply(hipStream_t st, const float* h, const float* sqp, int rows, int N, const float* w,
-                float eps, float* x, uint16_t* xa) {
+                float eps, float* x, uint16_t* xa, long ps) {
   const int nch = cdiv(N, kChunk);
   k_norm_apply<<<dim3(nch, rows), kThreads, 0, st>>>(h, sqp, nch, N, w, eps, x,
-                                                     reinterpret_cast<f16*>(xa));
+                                                     reinterpret_cast<f16*>(xa), ps);
 }
 
 void embed(hipStream_t st, const uint16_t* emb, int anchor, int mask, int rows, int hs, float* h,
@@ -1309,11 +1421,13 @@ void embed(hipStream_t st, const uint16_t* emb, int anchor, int mask, int rows, 
 }
 
 void conv0(hipStream_t st, const float* x, const float* dpart, int splits, long ss,
-           const float* base, int rows, int hs, int gs, int kn, uint16_t* xca, float* dsum) {
+           const float* base, int rows, int hs, int gs, int kn, uint16_t* xca, long ps,
+           float* dsum) {
   const int G = hs / gs, gpw = std::max(1, kChunk / gs);
   const size_t lds = sizeof(float) * 2 * kn * gpw;
   k_conv0<<<dim3(cdiv(G, gpw), rows), kThreads, lds, st>>>(x, dpart, splits, ss, base, hs, gs, kn,
-                                                          gpw, reinterpret_cast<f16*>(xca), dsum);
+                                                          gpw, reinterpret_cast<f16*>(xca), ps,
+                                                          dsum);
 }
 
 void conv1(hipStream_t st, float* h, const float* opart, int splits, long ss, const float* dsum,
@@ -1325,10 +1439,10 @@ void conv1(hipStream_t st, float* h, const float* opart, int splits, long ss, co
 
 void qkv_post(hipStream_t st, const float* part, int splits, long ss, int rows, int nh, int kv,
               int hd, const float* q_norm, const float* k_norm, const float* inv, long pos0,
-              int rot, float eps, uint16_t* qa, float* kb, float* vb) {
+              int rot, float eps, uint16_t* qa, long qps, float* kb, float* vb) {
   dim3 grid(rows, nh + 2 * kv);
   k_qkv_post<<<grid, 64, 0, st>>>(part, splits, ss, nh, kv, hd, q_norm, k_norm, inv, pos0, rot, eps,
-                                  reinterpret_cast<f16*>(qa), kb, vb);
+                                  reinterpret_cast<f16*>(qa), qps, kb, vb);
 }
 
 void settle_kv(hipStream_t st, const float* part, int splits, long ss, int rows, int layers,
@@ -1339,7 +1453,7 @@ void settle_kv(hipStream_t st, const float* part, int splits, long ss, int rows,
                                    sk, sv, cap, row0);
 }
 
-void attention(hipStream_t st, const uint16_t* qa, const float* sk, const float* sv,
+void attention(hipStream_t st, const uint16_t* qa, long qps, const float* sk, const float* sv,
                const float* kb, const float* vb, int B, int nh, int kv, int hd, int n,
                long lo_pos, long a, int window, int chunk, int nchunks, float scale, float* pacc,
                float* pml) {
@@ -1348,21 +1462,21 @@ void attention(hipStream_t st, const uint16_t* qa, const float* sk, const float*
   const f16* q = reinterpret_cast<const f16*>(qa);
   float2* ml = reinterpret_cast<float2*>(pml);
   if (hd == 64)
-    k_attn<64><<<grid, kThreads, 0, st>>>(q, sk, sv, kb, vb, B, nh, kv, n, lo_pos, a, window,
+    k_attn<64><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, kb, vb, B, nh, kv, n, lo_pos, a, window,
                                           chunk, nchunks, scale, pacc, ml);
   else if (hd == 128)
-    k_attn<128><<<grid, kThreads, 0, st>>>(q, sk, sv, kb, vb, B, nh, kv, n, lo_pos, a, window,
+    k_attn<128><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, kb, vb, B, nh, kv, n, lo_pos, a, window,
                                            chunk, nchunks, scale, pacc, ml);
   else
-    k_attn<256><<<grid, kThreads, 0, st>>>(q, sk, sv, kb, vb, B, nh, kv, n, lo_pos, a, window,
+    k_attn<256><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, kb, vb, B, nh, kv, n, lo_pos, a, window,
                                            chunk, nchunks, scale, pacc, ml);
 }
 
 void attn_merge(hipStream_t st, const float* pacc, const float* pml, int nh, int kv, int hd,
-                int nchunks, int B, uint16_t* ya) {
+                int nchunks, int B, uint16_t* ya, long ps) {
   dim3 grid(nh, B);
   k_attn_merge<<<grid, hd, 0, st>>>(pacc, reinterpret_cast<const float2*>(pml), nh, kv, hd, nchunks,
-                                    reinterpret_cast<f16*>(ya));
+                                    reinterpret_cast<f16*>(ya), ps);
 }
 
 int topk_slices(int width) { return cdiv(width, 64 * kSliceVPL); }

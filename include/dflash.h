@@ -200,9 +200,10 @@ enum {
    dequantised: dev f32 [rows][cols], element q·scale. */
 int dflash_debug_dequant(dflash_t* d, int32_t layer, int32_t which, float* out);
 
-/* y = W·x with the product path's GEMM kernels: x dev f32 [m][cols]
-   (rounded to f16 like every activation operand), y dev f32 [m][rows],
-   m in [1, 256]. */
+/* y = W·x with the product path's GEMM kernels: x dev f32 [m][cols],
+   y dev f32 [m][rows], m in [1, 256]. x enters as the block pass's
+   operands do for m <= 16 (two f16 planes, hi and the rest) and as the
+   settle's do above (one f16 plane). */
 int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* x, int32_t m,
                         float* y);
 
@@ -220,6 +221,10 @@ int dflash_debug_load_store(dflash_t* d, int64_t first, int64_t len, const float
    [block][hidden], and the selector projection of rows 1..k, dev f32
    [k][selector_rank] (either may be NULL). */
 int dflash_debug_last_block(dflash_t* d, float* hidden, float* hp);
+
+/* With trace non-NULL, later blocks also copy the residual rows after each
+   layer into trace, dev f32 [layers][block][hidden]; NULL stops it. */
+int dflash_debug_set_trace(dflash_t* d, float* trace);
 
 /* The selector alone on given logits (dev f32 [k][width]) and projections
    hp (dev f32 [k][rank]); forced_prev (dev int32 [k] or NULL) replaces prev

@@ -1,0 +1,125 @@
+"""Parity at the full sidecar sizes, in the launch configuration the
+benchmark times, on outputs the CPU oracle can afford: whole blocks over a
+synthetic context store (loaded through the debug entry, so no oracle input
+comes from the GPU), and sampled rows of 256-row and 8-row settles (each
+settled row depends only on its tap row and position)."""
+import numpy as np
+import pytest
+import torch
+
+import block_drafter_settle_amd as pkg
+from block_drafter_settle_amd import synth
+
+from test_gpu_parity import REL, check_selection, close, run_block
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return torch.device("cuda:0")
+
+
+_cache = {}
+
+
+def sidecar(name):
+    """Weights drawn on the GPU (fast) and held as host arrays, once per session."""
+    if name not in _cache:
+        g = synth.geometry(name)
+        w = synth.make_weights(g, seed=0, device=_dev())
+        _cache.clear()
+        _cache[name] = (g, w)
+    return _cache[name]
+
+
+def drafter(g, w, cap):
+    return pkg.Drafter(g, w, max_context=cap, stream=torch.cuda.current_stream(_dev()).cuda_stream)
+
+
+@pytest.mark.parametrize("name,ctx,k", [("t27b", 32768, 15), ("qwen3_4b", 4096, 15),
+                                        ("t27b_long", 131072, 15)])
+def test_full_block_over_synthetic_store(orc, name, ctx, k):
+    g, w = sidecar(name)
+    dev = _dev()
+    store = synth.make_store(g, ctx, seed=1, device=dev)
+    d = drafter(g, w, ctx + 16)
+    try:
+        first = 5
+        d.debug_load_store(first, ctx, [s[0].data_ptr() for s in store],
+                           [s[1].data_ptr() for s in store])
+        a = first + ctx
+        anchor = synth.uniform_tokens(g, 1, seed=3)[0]
+        width = g["vocab"]
+        print(f"{name}: block at a={a} over {ctx} positions, width {width}", flush=True)
+        trace = torch.zeros(g["layers"], g["block"], g["hidden"], device=dev)
+        d.debug_set_trace(trace.data_ptr())
+        got = run_block(d, g, anchor, a, k, width)
+        d.debug_set_trace(None)
+        host_store = [(s[0].cpu().numpy(), s[1].cpu().numpy()) for s in store]
+        del store
+        m = orc.Model(g, w)
+        ref = m.block(host_store, first, ctx, anchor, a, k, width, trace=True)
+        tr = trace.cpu().numpy()
+        for l in range(g["layers"]):
+            e = np.abs(tr[l] - ref["trace"][l])
+            print(f"{name} layer {l}: residual max|ref| {np.abs(ref['trace'][l]).max():.3e} "
+                  f"max|err| {e.max():.3e} rows {np.round(e.max(axis=1) / np.abs(ref['trace'][l]).max(), 5).tolist()}",
+                  flush=True)
+        close(got["hidden"], ref["hidden"], f"{name} hidden")
+        close(got["logits"], ref["logits"], f"{name} logits")
+        close(got["hp"], ref["hp"], f"{name} hp")
+        sel = m.select(ref["logits"], ref["hp"], anchor)
+        check_selection(got, ref["logits"], sel, name)
+    finally:
+        d.close()
+
+
+@pytest.mark.parametrize("name", ["t27b", "qwen3_4b"])
+def test_full_settle_sampled_rows(orc, name):
+    g, w = sidecar(name)
+    dev = _dev()
+    kd = g["kv_heads"] * g["head_dim"]
+    d = drafter(g, w, 300)
+    try:
+        m = orc.Model(g, w)
+        for n, first, outl in ((256, 32768, True), (8, 40000, False)):
+            taps = synth.make_taps(g, n, seed=n, outliers=outl, device=dev)
+            d.settle(first, n, taps.data_ptr())
+            ks = [torch.empty(n, kd, device=dev) for _ in range(g["layers"])]
+            vs = [torch.empty(n, kd, device=dev) for _ in range(g["layers"])]
+            for l in range(g["layers"]):
+                d.debug_read_store(l, 0, n, ks[l].data_ptr(), vs[l].data_ptr())
+            d.sync()
+            rows = sorted({0, n // 2, n - 1})
+            host_taps = taps.cpu().numpy()
+            print(f"{name}: settle of {n} rows at {first}, oracle rows {rows}", flush=True)
+            for r in rows:
+                K, V = m.settle(host_taps[r:r + 1], first + r)
+                for l in range(g["layers"]):
+                    close(ks[l][r].cpu().numpy(), K[l, 0], f"{name} K l{l} row {r}")
+                    close(vs[l][r].cpu().numpy(), V[l, 0], f"{name} V l{l} row {r}")
+    finally:
+        d.close()
+
+
+def test_tiny_sidecar_end_to_end(orc):
+    """The tiny fp32 sidecar: 128 settled positions then one block at 128,
+    the oracle settling its own context."""
+    g = synth.geometry("tiny")
+    w = synth.make_weights(g, seed=0)
+    d = drafter(g, w, 144)
+    try:
+        taps = synth.make_taps(g, 128, seed=0)
+        d.settle(0, 128, taps.to(_dev()).data_ptr())
+        m = orc.Model(g, w)
+        K, V = m.settle(taps.numpy(), 0)
+        anchor, k = 17, g["block"] - 1
+        got = run_block(d, g, anchor, 128, k, g["vocab"])
+        ref = m.block([(K[l], V[l]) for l in range(g["layers"])], 0, 128, anchor, 128, k,
+                      g["vocab"])
+        close(got["logits"], ref["logits"], "tiny logits")
+        close(got["hp"], ref["hp"], "tiny hp")
+        check_selection(got, ref["logits"], m.select(ref["logits"], ref["hp"], anchor), "tiny")
+    finally:
+        d.close()
