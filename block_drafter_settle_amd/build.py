@@ -3,26 +3,26 @@ from __future__ import annotations
 
 import os
 import subprocess
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdflash.so")
-SOURCES = ["kernels.hip", "dflash.cpp"]
+# source, extra flags: the block pass's int4 kernels keep MFMA results in
+# VGPRs (their results are scaled in VALU at once)
+SOURCES = [("kernels.hip", []), ("skinny.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+           ("dflash.cpp", [])]
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed fp32 VALU ops in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = ["hipcc", *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-x", "hip", *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     out = subprocess.run(cmd, capture_output=True, text=True)
@@ -33,6 +33,19 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed:\n{msg}")
     if verbose and msg.strip():
         print(msg)
+
+
+def build(verbose: bool = False) -> str:
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    with tempfile.TemporaryDirectory() as tmpdir:
+        objs = []
+        for src, extra in SOURCES:
+            obj = os.path.join(tmpdir, src + ".o")
+            _run(["hipcc", *FLAGS, *extra, *inc, "-c", "-x", "hip", os.path.join(CSRC, src),
+                  "-o", obj], verbose)
+            objs.append(obj)
+        tmp = LIB + ".tmp"
+        _run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -29,9 +29,9 @@ constexpr int kMaxChunks = 64;       // context chunks per kv head in the attent
 // Row tiles per wave of each product (a workgroup covers 4·R tiles of 16).
 constexpr int kRKproj = 2;   // kernel projections, f16
 constexpr int kRFc = 2;      // settle's fc, f16
-constexpr int kRQkv = 2;     // q/k/v, int4
-constexpr int kRO = 2;       // o, int4
-constexpr int kRDown = 2;    // down, int4
+constexpr int kKsQkv = 2;    // q/k/v, int4: spans (128 columns) per split
+constexpr int kKsO = 2;      // o, int4
+constexpr int kKsDown = 4;   // down, int4
 constexpr int kRKv = 2;      // settle's k/v of every layer, int4
 constexpr int kRDebug = 2;   // the debug matvec
 
@@ -336,9 +336,15 @@ long partial_need(const dflash* d) {
     need = std::max(need, (long)s.S * mb * 16 * N);
   };
   f16(d->P, d->hs, 1, kRKproj);
-  i4(d->qd + 2 * d->kd, d->hs, 1, kRQkv);
-  i4(d->hs, d->qd, 1, kRO);
-  i4(d->hs, d->ffn, 1, kRDown);
+  auto i4b = [&](int N, int K, int ks) {
+    need = std::max(need, (long)dfl::i4_block_splits(K, ks) * 16 * N);
+  };
+  i4b(d->qd + 2 * d->kd, d->hs, kKsQkv);
+  i4b(d->hs, d->qd, kKsO);
+  i4b(d->hs, d->ffn, kKsDown);
+  for (int N : {d->qd, d->kd, d->ffn}) i4b(N, d->hs, 2);
+  i4b(d->hs, d->qd, 2);
+  i4b(d->hs, d->ffn, 2);
   for (int mb = 2; mb <= kSettleRows / 16; ++mb)
     for (int N : {d->hs, d->P, d->rank}) {
       const int K = N == d->hs ? d->tw : d->hs;
@@ -673,9 +679,9 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
   const float scale = std::pow((float)d->hd, -0.5f);
   const long ssd = 16L * d->P, ssq = 16L * (d->qd + 2 * d->kd), ssh = 16L * hs;
   const Split spk = split_for(d->ptiles, kRKproj, hs / 32, 1, 16);
-  const Split sqk = split_for(d->qkv.tiles, kRQkv, hs / 128, 1, 4);
-  const Split so = split_for(hs / 16, kRO, d->qd / 128, 1, 4);
-  const Split sdn = split_for(hs / 16, kRDown, d->ffn / 128, 1, 4);
+  const Split sqk = {dfl::i4_block_splits(hs, kKsQkv), kKsQkv};
+  const Split so = {dfl::i4_block_splits(d->qd, kKsO), kKsO};
+  const Split sdn = {dfl::i4_block_splits(d->ffn, kKsDown), kKsDown};
   const size_t kp_layer = (size_t)d->ptiles * 16 * hs;
   const size_t i4l_qkv = (size_t)d->qkv.tiles * (hs / 128);
   const size_t i4l_o = (size_t)d->o.tiles * (d->qd / 128);
@@ -698,9 +704,10 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     tm_mark(d, DFLASH_ST_KPROJ);
     dfl::conv0(st, d->x, d->part, spk.S, ssd, ab, B, hs, d->gs, d->kn, d->xca, psh, d->dsum_a);
     tm_mark(d, DFLASH_ST_CONV);
-    dfl::gemm_i4(st, kRQkv, d->xca, psh, hs, 1, d->qkv.codes + i4l_qkv * 1024 * l, d->qkv.scales + i4l_qkv * 64 * l,
-                 dfl::TileMap{d->qkv.tiles, d->qkv.tiles, 0, 0}, d->qd + 2 * d->kd, sqk.S, sqk.per,
-                 d->part, ssq);
+    dfl::gemm_i4_block(st, d->xca, psh, hs, d->qkv.codes + i4l_qkv * 1024 * l,
+                       d->qkv.scales + i4l_qkv * 64 * l,
+                       dfl::TileMap{d->qkv.tiles, d->qkv.tiles, 0, 0}, d->qd + 2 * d->kd, sqk.per,
+                       d->part, ssq);
     tm_mark(d, DFLASH_ST_QKV);
     dfl::qkv_post(st, d->part, sqk.S, ssq, B, d->nh, d->kv, d->hd, d->q_norm + (size_t)l * d->hd,
                   d->k_norm + (size_t)l * d->hd, d->inv, a, d->rot[l], d->eps, d->qa, psq, d->kb, d->vb);
@@ -718,8 +725,9 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     dfl::attn_merge(st, d->pacc, d->pml, d->nh, d->kv, d->hd, nchunks, B, d->ya, psy);
     tm_mark(d, DFLASH_ST_ATTN);
     // o, conv_out into the residual, post-attention norm
-    dfl::gemm_i4(st, kRO, d->ya, psy, d->qd, 1, d->o.codes + i4l_o * 1024 * l, d->o.scales + i4l_o * 64 * l,
-                 dfl::TileMap{d->o.tiles, d->o.tiles, 0, 0}, hs, so.S, so.per, d->part, ssh);
+    dfl::gemm_i4_block(st, d->ya, psy, d->qd, d->o.codes + i4l_o * 1024 * l,
+                       d->o.scales + i4l_o * 64 * l, dfl::TileMap{d->o.tiles, d->o.tiles, 0, 0},
+                       hs, so.per, d->part, ssh);
     tm_mark(d, DFLASH_ST_O);
     dfl::conv1(st, d->h, d->part, so.S, ssh, d->dsum_a, ab, B, hs, d->gs, d->kn, d->sqp);
     tm_mark(d, DFLASH_ST_CONV);
@@ -736,9 +744,9 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     dfl::gemm_glu(st, d->xca, psh, hs, d->gu.codes + i4l_gu * 1024 * l,
                   d->gu.scales + i4l_gu * 64 * l, d->ffn / 16, d->ma, psm);
     tm_mark(d, DFLASH_ST_GLU);
-    dfl::gemm_i4(st, kRDown, d->ma, psm, d->ffn, 1, d->down.codes + i4l_dn * 1024 * l,
-                 d->down.scales + i4l_dn * 64 * l, dfl::TileMap{d->down.tiles, d->down.tiles, 0, 0},
-                 hs, sdn.S, sdn.per, d->part, ssh);
+    dfl::gemm_i4_block(st, d->ma, psm, d->ffn, d->down.codes + i4l_dn * 1024 * l,
+                       d->down.scales + i4l_dn * 64 * l,
+                       dfl::TileMap{d->down.tiles, d->down.tiles, 0, 0}, hs, sdn.per, d->part, ssh);
     tm_mark(d, DFLASH_ST_DOWN);
     const float* next = l + 1 < d->L ? d->in_norm + (size_t)(l + 1) * hs : d->norm;
     dfl::conv1(st, d->h, d->part, sdn.S, ssh, d->dsum_m, mbase, B, hs, d->gs, d->kn, d->sqp);
@@ -836,12 +844,17 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
   // the block's operands (m ≤ 16) carry two planes, the settle's one
   const long ps = m <= 16 ? 16L * cols : 0;
   dfl::to_a(d->st, x, cols, m, cols, d->taps_a, ps);
-  const Split s = is_i4 ? split_for(map.ntiles, kRDebug, cols / 128, mb, 4)
-                  : mb > 1 ? split_big(map.ntiles, cols / 32)
-                           : split_for(map.ntiles, kRDebug, cols / 32, mb, 16);
+  // at m ≤ 16 an int4 matrix takes the block pass's kernel (two-span splits)
+  const Split s = is_i4 && mb == 1 ? Split{dfl::i4_block_splits(cols, 2), 2}
+                  : is_i4          ? split_for(map.ntiles, kRDebug, cols / 128, mb, 4)
+                  : mb > 1         ? split_big(map.ntiles, cols / 32)
+                                   : split_for(map.ntiles, kRDebug, cols / 32, mb, 16);
   const long ss = (long)mb * 16 * rows;
   if ((long)s.S * ss > d->part_floats) return fail(d, DFLASH_EINVAL, "matvec: partials too large");
-  if (is_i4)
+  if (is_i4 && mb == 1)
+    dfl::gemm_i4_block(d->st, d->taps_a, ps, cols, static_cast<const uint8_t*>(codes), scales, map,
+                       rows, 2, d->part, ss);
+  else if (is_i4)
     dfl::gemm_i4(d->st, kRDebug, d->taps_a, ps, cols, mb, static_cast<const uint8_t*>(codes), scales, map, rows,
                  s.S, s.per, d->part, ss);
   else if (mb > 1)

@@ -55,9 +55,16 @@ void gemm_i4(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblo
 void gemm_big_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
                   TileMap map, int N, int splits, int steps_per_split, float* out,
                   long split_stride);
-// gate/up with the SwiGLU epilogue: gate tiles [0, ftiles), up tiles
-// [ftiles, 2·ftiles) of one stored matrix; writes silu(g)·u in A-layout
-// planes (ma, mps).
+// The block pass's 16-row int4 GEMM (two planes, ps ≠ 0; skinny.hip):
+// splits of `ks` spans (128 columns) each, i4_block_splits(K, ks) of them;
+// out as gemm_i4. ks is 2 or 4.
+int i4_block_splits(int K, int ks);
+void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
+                   const uint16_t* scales, TileMap map, int N, int ks, float* out,
+                   long split_stride);
+// gate/up with the SwiGLU epilogue at 16 rows, two planes in (xa, ps):
+// gate tiles [0, ftiles), up tiles [ftiles, 2·ftiles) of one stored
+// matrix; writes silu(g)·u in A-layout planes (ma, mps).
 void gemm_glu(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
               const uint16_t* scales, int ftiles, uint16_t* ma, long mps);
 // Scratch of the selection: gmax [k][ceil(width/256)] column-group maxima,

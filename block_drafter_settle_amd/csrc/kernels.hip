@@ -13,6 +13,7 @@
 // and each 32-column group's partial is scaled by its f16 scale in f32, so
 // the dequantised weight q·s is used exactly. Accumulation is f32
 // throughout.
+#include "device.h"
 #include "internal.h"
 
 #include <algorithm>
@@ -20,84 +21,6 @@
 #include <math.h>
 
 namespace dfl {
-
-typedef _Float16 f16;
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-static constexpr int kThreads = 256;
-
-__device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// A-layout half index of (m, k) inside one 16-row block.
-__device__ __forceinline__ size_t a_idx(int m, int k) {
-  return ((size_t)(k >> 5) * 64 + ((k >> 3) & 3) * 16 + (m & 15)) * 8 + (k & 7);
-}
-
-// Stores v at A-layout index idx: plane 0 its f16 rounding and, when ps (the
-// plane stride in halves) is nonzero, plane 1 the f16 rounding of what is left.
-__device__ __forceinline__ void put_a(f16* xa, long ps, size_t idx, float v) {
-  const f16 hi = (f16)v;
-  xa[idx] = hi;
-  if (ps) xa[ps + idx] = (f16)(v - (float)hi);
-}
-
-__device__ __forceinline__ long map_tile(const TileMap& mp, int t) {
-  return (long)(t / mp.seg) * mp.seg_stride + mp.seg_off + t % mp.seg;
-}
-
-__device__ __forceinline__ float half_bits(uint32_t b) {
-  return (float)__builtin_bit_cast(f16, (uint16_t)(b & 0xffffu));
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-// Sum over a 256-thread block; every thread gets the total (fixed order).
-__device__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
-}
-
-// Σ_s p[s·ss] over the K splits of a GEMM, four independent chains so the
-// loads are in flight together (fixed order: the same splits give the same sum).
-__device__ __forceinline__ float sum_splits(const float* __restrict__ p, int splits, long ss) {
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  int s = 0;
-  for (; s + 4 <= splits; s += 4) {
-    a0 += p[(size_t)s * ss];
-    a1 += p[(size_t)(s + 1) * ss];
-    a2 += p[(size_t)(s + 2) * ss];
-    a3 += p[(size_t)(s + 3) * ss];
-  }
-  for (; s < splits; ++s) a0 += p[(size_t)s * ss];
-  return (a0 + a1) + (a2 + a3);
-}
-
-// Eight int4 codes of one I4T word → eight f16 integers in column order.
-// A nibble u' at bits 0–3 of a half over the exponent pattern of 1024 reads
-// 1024 + u'; at bits 4–7 it reads 1024 + 16·u'. Both map exactly to
-// q = u' − 8.
-__device__ __forceinline__ h8 unpack_i4(uint32_t w) {
-  const uint32_t M = 0x64006400u;
-  const uint32_t w2 = w >> 8;
-  const h2 q0 = __builtin_bit_cast(h2, (w & 0x000F000Fu) | M) - (h2){1032, 1032};
-  const h2 q1 = __builtin_bit_cast(h2, (w & 0x00F000F0u) | M) * (h2){0.0625, 0.0625} - (h2){72, 72};
-  const h2 q2 = __builtin_bit_cast(h2, (w2 & 0x000F000Fu) | M) - (h2){1032, 1032};
-  const h2 q3 = __builtin_bit_cast(h2, (w2 & 0x00F000F0u) | M) * (h2){0.0625, 0.0625} - (h2){72, 72};
-  return (h8){q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
-}
 
 // ------------------------------------------------------------------ GEMMs
 
@@ -178,11 +101,6 @@ static constexpr int kBigFrags = 16 + kBigNT;      // fragments a step
 static constexpr int kBigPerWave = kBigFrags / 4;  // async loads a wave issues a step
 static_assert(kBigFrags % 4 == 0, "fragments split evenly over the waves");
 
-template <int N_OUT>
-__device__ __forceinline__ void wait_vm() {
-  // s_waitcnt vmcnt(N_OUT) with expcnt/lgkmcnt left at their maxima (gfx9 encoding)
-  __builtin_amdgcn_s_waitcnt((N_OUT & 15) | (7 << 4) | (15 << 8) | ((N_OUT >> 4) << 14));
-}
 
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_big_f16(const f16* __restrict__ xa, int K,
                                                              int mblocks,
@@ -267,36 +185,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big_f16(const f16* __restr
   }
 }
 
-// One 128-column span of R int4 tiles against four A-layout steps of PL
-// planes (a, a2).
-template <int R, int PL>
-__device__ __forceinline__ void i4_span(const uint4* c, const uint2* sc, const h8* a, const h8* a2,
-                                        f4* acc) {
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint32_t word = u == 0 ? c[r].x : u == 1 ? c[r].y : u == 2 ? c[r].z : c[r].w;
-      const uint32_t sb = u < 2 ? sc[r].x : sc[r].y;
-      const float s = half_bits((u & 1) ? (sb >> 16) : sb);
-      const h8 q = unpack_i4(word);
-      f4 t = mfma16(a[u], q, (f4){0.f, 0.f, 0.f, 0.f});
-      if (PL == 2) t = mfma16(a2[u], q, t);
-      acc[r] += s * t;
-    }
-  }
-}
-
-// The A fragments of span p: four steps of each plane.
-template <int PL>
-__device__ __forceinline__ void load_span(const h8* xp, const h8* xq, int p, h8* a, h8* a2) {
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    a[u] = xp[(size_t)(4 * p + u) * 64];
-    if (PL == 2) a2[u] = xq[(size_t)(4 * p + u) * 64];
-  }
-}
-
 template <int R, int PL>
 __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa, long ps, int K,
                                                       const uint4* __restrict__ codes,
@@ -359,64 +247,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa
     if (t < mp.ntiles && col < N)
 #pragma unroll
       for (int v = 0; v < 4; ++v) o[(size_t)(4 * j + v) * N + col] = acc[r][v];
-  }
-}
-
-// gate/up over the full K, SwiGLU in the epilogue (`mlp`: silu(g)·u with
-// silu(a) = a/(1+e^−a)). Each wave owns one ffn tile: gate tile ft and up
-// tile ffn_tiles + ft of the stored matrix, so g and u meet in registers.
-// Input of PL planes (xa, ps); the output in A-layout planes (ma, mps).
-template <int PL>
-__global__ __launch_bounds__(kThreads) void k_gemm_glu(const f16* __restrict__ xa, long ps, int K,
-                                                       const uint4* __restrict__ codes,
-                                                       const uint2* __restrict__ scales,
-                                                       int ftiles, f16* __restrict__ ma,
-                                                       long mps) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int KT = K >> 7;
-  const int ft = blockIdx.x * 4 + wave;
-  if (ft >= ftiles) return;
-  const h8* xp = reinterpret_cast<const h8*>(xa) + lane;
-  const h8* xq = reinterpret_cast<const h8*>(xa + ps * (PL - 1)) + lane;
-  const uint4* cp[2] = {codes + (size_t)ft * KT * 64 + lane,
-                        codes + (size_t)(ftiles + ft) * KT * 64 + lane};
-  const uint2* scp[2] = {scales + (size_t)ft * KT * 16 + (lane & 15),
-                         scales + (size_t)(ftiles + ft) * KT * 16 + (lane & 15)};
-  f4 acc[2] = {(f4){0.f, 0.f, 0.f, 0.f}, (f4){0.f, 0.f, 0.f, 0.f}};
-  int p = 0;
-  for (; p + 2 <= KT; p += 2) {
-    uint4 c0[2], c1[2];
-    uint2 s0[2], s1[2];
-    h8 a0[4], a1[4], b0[4], b1[4];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      c0[r] = cp[r][(size_t)p * 64];
-      c1[r] = cp[r][(size_t)(p + 1) * 64];
-      s0[r] = scp[r][(size_t)p * 16];
-      s1[r] = scp[r][(size_t)(p + 1) * 16];
-    }
-    load_span<PL>(xp, xq, p, a0, b0);
-    load_span<PL>(xp, xq, p + 1, a1, b1);
-    i4_span<2, PL>(c0, s0, a0, b0, acc);
-    i4_span<2, PL>(c1, s1, a1, b1, acc);
-  }
-  if (p < KT) {
-    uint4 c0[2];
-    uint2 s0[2];
-    h8 a0[4], b0[4];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      c0[r] = cp[r][(size_t)p * 64];
-      s0[r] = scp[r][(size_t)p * 16];
-    }
-    load_span<PL>(xp, xq, p, a0, b0);
-    i4_span<2, PL>(c0, s0, a0, b0, acc);
-  }
-  const int j = lane >> 4, n = lane & 15;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const float g = acc[0][v];
-    put_a(ma, mps, a_idx(4 * j + v, ft * 16 + n), g / (1.f + expf(-g)) * acc[1][v]);
   }
 }
 
@@ -1366,18 +1196,6 @@ void gemm_i4(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblo
     pick_i4<2>(st, R, xa, ps, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
   else
     pick_i4<1>(st, R, xa, 0, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
-}
-
-void gemm_glu(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
-              const uint16_t* scales, int ftiles, uint16_t* ma, long mps) {
-  const f16* x = reinterpret_cast<const f16*>(xa);
-  const uint4* c = reinterpret_cast<const uint4*>(codes);
-  const uint2* sc = reinterpret_cast<const uint2*>(scales);
-  f16* m = reinterpret_cast<f16*>(ma);
-  if (ps)
-    k_gemm_glu<2><<<cdiv(ftiles, 4), kThreads, 0, st>>>(x, ps, K, c, sc, ftiles, m, mps);
-  else
-    k_gemm_glu<1><<<cdiv(ftiles, 4), kThreads, 0, st>>>(x, 0, K, c, sc, ftiles, m, mps);
 }
 
 void head_sel(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t* head, int width,

@@ -1,0 +1,210 @@
+// The block pass's int4 projections (q/k/v, o, down and the gate/up pair
+// with SwiGLU) at 16 rows with two activation planes.
+//
+// These kernels are compiled on their own with MFMA results in VGPRs
+// (-mllvm -amdgpu-mfma-vgpr-form): every MFMA result is scaled by its
+// group's f16 scale in VALU right away, which in the accumulator-register
+// form costs a v_accvgpr_read per element.
+//
+// `mlp` (silu(a) = a/(1+e^−a), the product with up) and the projections
+// are defined on the docs.rs page "cortiq_engine/dflash.rs" (cortiq-engine
+// 0.8.78), `Drafter::block`.
+#include "device.h"
+#include "internal.h"
+
+#include <algorithm>
+
+namespace dfl {
+
+// A 16-row int4 GEMM against two activation planes. Workgroup (g, sp): NW
+// waves × R row tiles (tile group g) over spans [sp·KS, sp·KS + KS) of K.
+// The workgroup copies the two planes' A fragments of its spans into LDS
+// once; every wave issues all of its weight loads before the copy's wait,
+// so a wave's whole share is in flight at once. Writes partial sums
+// out[sp][m][col].
+template <int R, int NW, int KS>
+__global__ __launch_bounds__(64 * NW) void k_i4_block(const f16* __restrict__ xa, long ps, int K,
+                                                      const uint4* __restrict__ codes,
+                                                      const uint2* __restrict__ scales,
+                                                      TileMap mp, int N, float* __restrict__ out,
+                                                      long split_stride) {
+  constexpr int kSteps = KS * 4;                 // 32-column steps a workgroup covers
+  constexpr int kFrags = 2 * kSteps * 64;        // h8 fragments of both planes
+  constexpr int kPer = (kFrags + 64 * NW - 1) / (64 * NW);
+  __shared__ h8 al[2][kSteps][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int KT = K >> 7;
+  const int sp = blockIdx.y;
+  const int p0 = sp * KS, np = min(KS, KT - p0);
+  const int t0 = (blockIdx.x * NW + wave) * R;
+  // the A copy: fragment e = (plane, step, lane)
+  const h8* x0 = reinterpret_cast<const h8*>(xa);
+  const h8* x1 = reinterpret_cast<const h8*>(xa + ps);
+  h8 areg[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = threadIdx.x + i * 64 * NW;
+    const int pl = e / (kSteps * 64), st = (e / 64) % kSteps;
+    if (e < kFrags && st < np * 4) areg[i] = (pl ? x1 : x0)[(size_t)(p0 * 4 + st) * 64 + (e & 63)];
+  }
+  uint4 c[KS][R];
+  uint2 s[KS][R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const long st = map_tile(mp, min(t0 + r, mp.ntiles - 1));
+    const uint4* cp = codes + (size_t)st * KT * 64 + lane;
+    const uint2* scp = scales + (size_t)st * KT * 16 + (lane & 15);
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+      const int p = p0 + min(u, np - 1);
+      c[u][r] = cp[(size_t)p * 64];
+      s[u][r] = scp[(size_t)p * 16];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = threadIdx.x + i * 64 * NW;
+    const int pl = e / (kSteps * 64), st = (e / 64) % kSteps;
+    if (e < kFrags && st < np * 4) al[pl][st][e & 63] = areg[i];
+  }
+  // LDS writes done, then a bare s_barrier: a __syncthreads here would also
+  // wait for the weight loads still in flight
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  asm volatile("s_barrier" ::: "memory");
+  f4 acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < KS; ++u) {
+    if (u < np) {
+      h8 a[4], b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[q] = al[0][u * 4 + q][lane];
+        b[q] = al[1][u * 4 + q][lane];
+      }
+      i4_span<R, 2>(c[u], s[u], a, b, acc);
+    }
+  }
+  if (t0 >= mp.ntiles) return;
+  float* o = out + (size_t)sp * split_stride;
+  const int j = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = t0 + r, col = t * 16 + n;
+    if (t < mp.ntiles && col < N)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[(size_t)(4 * j + v) * N + col] = acc[r][v];
+  }
+}
+
+// gate/up over the full K with SwiGLU in the epilogue: workgroup g owns
+// ffn tiles [FP·g, FP·g + FP), i.e. FP gate tiles and the FP up tiles
+// (ftiles further on in the stored matrix); its NW waves split K, and their
+// partial sums meet in LDS, where wave 0 finishes silu(g)·u into the A-layout
+// planes of the down projection (ma, mps).
+template <int FP, int NW>
+__global__ __launch_bounds__(64 * NW) void k_glu_block(const f16* __restrict__ xa, long ps, int K,
+                                                       const uint4* __restrict__ codes,
+                                                       const uint2* __restrict__ scales,
+                                                       int ftiles, f16* __restrict__ ma,
+                                                       long mps) {
+  constexpr int R = 2 * FP;
+  __shared__ f4 red[NW - 1][R][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int KT = K >> 7;
+  const int ft0 = blockIdx.x * FP;
+  const int per = (KT + NW - 1) / NW;
+  const int p0 = wave * per, p1 = min(KT, p0 + per);
+  const h8* xp = reinterpret_cast<const h8*>(xa) + lane;
+  const h8* xq = reinterpret_cast<const h8*>(xa + ps) + lane;
+  const uint4* cp[R];
+  const uint2* scp[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int f = min(ft0 + (r % FP), ftiles - 1);
+    const long st = r < FP ? f : ftiles + f;
+    cp[r] = codes + (size_t)st * KT * 64 + lane;
+    scp[r] = scales + (size_t)st * KT * 16 + (lane & 15);
+  }
+  f4 acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = (f4){0.f, 0.f, 0.f, 0.f};
+  int p = p0;
+  for (; p + 2 <= p1; p += 2) {
+    uint4 c0[R], c1[R];
+    uint2 s0[R], s1[R];
+    h8 a0[4], a1[4], b0[4], b1[4];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      c0[r] = cp[r][(size_t)p * 64];
+      c1[r] = cp[r][(size_t)(p + 1) * 64];
+      s0[r] = scp[r][(size_t)p * 16];
+      s1[r] = scp[r][(size_t)(p + 1) * 16];
+    }
+    load_span<2>(xp, xq, p, a0, b0);
+    load_span<2>(xp, xq, p + 1, a1, b1);
+    i4_span<R, 2>(c0, s0, a0, b0, acc);
+    i4_span<R, 2>(c1, s1, a1, b1, acc);
+  }
+  if (p < p1) {
+    uint4 c0[R];
+    uint2 s0[R];
+    h8 a0[4], b0[4];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      c0[r] = cp[r][(size_t)p * 64];
+      s0[r] = scp[r][(size_t)p * 16];
+    }
+    load_span<2>(xp, xq, p, a0, b0);
+    i4_span<R, 2>(c0, s0, a0, b0, acc);
+  }
+  if (wave > 0)
+#pragma unroll
+    for (int r = 0; r < R; ++r) red[wave - 1][r][lane] = acc[r];
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < NW - 1; ++w)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] += red[w][r][lane];
+  const int j = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int f = 0; f < FP; ++f) {
+    if (ft0 + f >= ftiles) break;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float g = acc[f][v];
+      put_a(ma, mps, a_idx(4 * j + v, (ft0 + f) * 16 + n), g / (1.f + expf(-g)) * acc[FP + f][v]);
+    }
+  }
+}
+
+static inline unsigned cdiv(long a, long b) { return (unsigned)((a + b - 1) / b); }
+
+// tiles per workgroup and spans per split of k_i4_block
+static constexpr int kBlkR = 2, kBlkNW = 4;
+
+int i4_block_splits(int K, int ks) { return (int)cdiv(K / 128, ks); }
+
+void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
+                   const uint16_t* scales, TileMap map, int N, int ks, float* out, long ss) {
+  const dim3 grid(cdiv(map.ntiles, kBlkR * kBlkNW), i4_block_splits(K, ks));
+  const f16* x = reinterpret_cast<const f16*>(xa);
+  const uint4* c = reinterpret_cast<const uint4*>(codes);
+  const uint2* s = reinterpret_cast<const uint2*>(scales);
+  if (ks == 2)
+    k_i4_block<kBlkR, kBlkNW, 2><<<grid, 64 * kBlkNW, 0, st>>>(x, ps, K, c, s, map, N, out, ss);
+  else
+    k_i4_block<kBlkR, kBlkNW, 4><<<grid, 64 * kBlkNW, 0, st>>>(x, ps, K, c, s, map, N, out, ss);
+}
+
+void gemm_glu(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
+              const uint16_t* scales, int ftiles, uint16_t* ma, long mps) {
+  constexpr int FP = 2, NW = 4;
+  k_glu_block<FP, NW><<<cdiv(ftiles, FP), 64 * NW, 0, st>>>(
+      reinterpret_cast<const f16*>(xa), ps, K, reinterpret_cast<const uint4*>(codes),
+      reinterpret_cast<const uint2*>(scales), ftiles, reinterpret_cast<f16*>(ma), mps);
+}
+
+}  // namespace dfl
