@@ -27,7 +27,6 @@ constexpr int kSettleRows = 256;     // rows one settle pass takes
 constexpr int kTargetBlocks = 512;   // workgroups a GEMM launch aims for (256 CUs)
 constexpr int kMaxChunks = 64;       // context chunks per kv head in the attention
 // Row tiles per wave of each product (a workgroup covers 4·R tiles of 16).
-constexpr int kRKproj = 2;   // kernel projections, f16
 constexpr int kRFc = 2;      // settle's fc, f16
 constexpr int kKsQkv = 2;    // q/k/v, int4: spans (128 columns) per split
 constexpr int kKsO = 2;      // o, int4
@@ -335,7 +334,12 @@ long partial_need(const dflash* d) {
     const Split s = split_for(N / 16, R, K / 128, mb, 4);
     need = std::max(need, (long)s.S * mb * 16 * N);
   };
-  f16(d->P, d->hs, 1, kRKproj);
+  auto f16b = [&](int N, int K) {
+    need = std::max(need, (long)dfl::f16_block_splits(K) * 16 * N);
+  };
+  f16b(d->P, d->hs);
+  for (int N : {d->hs, d->P, d->rank}) f16b(N, d->hs);
+  f16b(d->hs, d->tw);
   auto i4b = [&](int N, int K, int ks) {
     need = std::max(need, (long)dfl::i4_block_splits(K, ks) * 16 * N);
   };
@@ -618,7 +622,7 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
   tm_mark(d, DFLASH_ST_S_FC);
   dfl::rowsum_sq(st, d->part, sf.S, ssf, m, d->hs, d->tbuf, d->sqp);
   tm_mark(d, DFLASH_ST_S_NORM);
-  dfl::norm_apply(st, d->tbuf, d->sqp, m, d->hs, d->hidden_norm, d->eps, nullptr, d->t_a, 0);
+  dfl::norm_apply(st, d->tbuf, d->sqp, dfl::row_chunks(d->hs), m, d->hs, d->hidden_norm, d->eps, nullptr, d->t_a, 0);
   tm_mark(d, DFLASH_ST_S_NORM);
   // K and V of every layer: the k and v tiles of each layer's q/k/v set
   const int kvt = 2 * d->kd / 16;
@@ -678,7 +682,7 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
   const int hs = d->hs, B = d->B;
   const float scale = std::pow((float)d->hd, -0.5f);
   const long ssd = 16L * d->P, ssq = 16L * (d->qd + 2 * d->kd), ssh = 16L * hs;
-  const Split spk = split_for(d->ptiles, kRKproj, hs / 32, 1, 16);
+  const Split spk = {dfl::f16_block_splits(hs), 0};
   const Split sqk = {dfl::i4_block_splits(hs, kKsQkv), kKsQkv};
   const Split so = {dfl::i4_block_splits(d->qd, kKsO), kKsO};
   const Split sdn = {dfl::i4_block_splits(d->ffn, kKsDown), kKsDown};
@@ -688,19 +692,20 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
   const size_t i4l_gu = (size_t)d->gu.tiles * (hs / 128);
   const size_t i4l_dn = (size_t)d->down.tiles * (d->ffn / 128);
   // plane strides (halves) of the two-plane operands
+  const int nc1 = dfl::conv1_chunks(hs);  // sums of squares per row after conv1
   const long psh = 16L * hs, psq = 16L * d->nh * d->hd, psy = 16L * d->qd, psm = 16L * d->ffn;
 
   tm_begin(d);
   dfl::embed(st, d->embed, anchor, d->mask, B, hs, d->h, d->sqp);
   tm_mark(d, DFLASH_ST_CONV);
-  dfl::norm_apply(st, d->h, d->sqp, B, hs, d->in_norm, d->eps, d->x, d->xa, psh);
+  dfl::norm_apply(st, d->h, d->sqp, dfl::row_chunks(hs), B, hs, d->in_norm, d->eps, d->x, d->xa, psh);
   tm_mark(d, DFLASH_ST_CONV);
   for (int l = 0; l < d->L; ++l) {
     const float* ab = d->attn_base + (size_t)l * 2 * d->kn * hs;
     const float* mbase = d->mlp_base + (size_t)l * 2 * d->kn * hs;
     // attention: conv_in, q/k/v, norms + rotary
-    dfl::gemm_f16(st, kRKproj, d->xa, psh, hs, 1, d->attn_kproj + l * kp_layer,
-                  dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, spk.S, spk.per, d->part, ssd);
+    dfl::gemm_f16_block(st, d->xa, psh, hs, d->attn_kproj + l * kp_layer,
+                        dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, d->part, ssd);
     tm_mark(d, DFLASH_ST_KPROJ);
     dfl::conv0(st, d->x, d->part, spk.S, ssd, ab, B, hs, d->gs, d->kn, d->xca, psh, d->dsum_a);
     tm_mark(d, DFLASH_ST_CONV);
@@ -731,12 +736,12 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     tm_mark(d, DFLASH_ST_O);
     dfl::conv1(st, d->h, d->part, so.S, ssh, d->dsum_a, ab, B, hs, d->gs, d->kn, d->sqp);
     tm_mark(d, DFLASH_ST_CONV);
-    dfl::norm_apply(st, d->h, d->sqp, B, hs, d->post_norm + (size_t)l * hs, d->eps, d->x, d->xa,
+    dfl::norm_apply(st, d->h, d->sqp, nc1, B, hs, d->post_norm + (size_t)l * hs, d->eps, d->x, d->xa,
                     psh);
     tm_mark(d, DFLASH_ST_CONV);
     // MLP, wrapped the same way
-    dfl::gemm_f16(st, kRKproj, d->xa, psh, hs, 1, d->mlp_kproj + l * kp_layer,
-                  dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, spk.S, spk.per, d->part, ssd);
+    dfl::gemm_f16_block(st, d->xa, psh, hs, d->mlp_kproj + l * kp_layer,
+                        dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, d->part, ssd);
     tm_mark(d, DFLASH_ST_KPROJ);
     dfl::conv0(st, d->x, d->part, spk.S, ssd, mbase, B, hs, d->gs, d->kn, d->xca, psh,
                d->dsum_m);
@@ -751,7 +756,7 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     const float* next = l + 1 < d->L ? d->in_norm + (size_t)(l + 1) * hs : d->norm;
     dfl::conv1(st, d->h, d->part, sdn.S, ssh, d->dsum_m, mbase, B, hs, d->gs, d->kn, d->sqp);
     tm_mark(d, DFLASH_ST_CONV);
-    dfl::norm_apply(st, d->h, d->sqp, B, hs, next, d->eps, d->x, d->xa, psh);
+    dfl::norm_apply(st, d->h, d->sqp, nc1, B, hs, next, d->eps, d->x, d->xa, psh);
     tm_mark(d, DFLASH_ST_CONV);
     if (d->trace)
       (void)hipMemcpyAsync(d->trace + (size_t)l * B * hs, d->h, sizeof(float) * B * hs,
@@ -846,6 +851,7 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
   dfl::to_a(d->st, x, cols, m, cols, d->taps_a, ps);
   // at m ≤ 16 an int4 matrix takes the block pass's kernel (two-span splits)
   const Split s = is_i4 && mb == 1 ? Split{dfl::i4_block_splits(cols, 2), 2}
+                  : mb == 1        ? Split{dfl::f16_block_splits(cols), 0}
                   : is_i4          ? split_for(map.ntiles, kRDebug, cols / 128, mb, 4)
                   : mb > 1         ? split_big(map.ntiles, cols / 32)
                                    : split_for(map.ntiles, kRDebug, cols / 32, mb, 16);
@@ -861,8 +867,8 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
     dfl::gemm_big_f16(d->st, d->taps_a, cols, mb, static_cast<const uint16_t*>(codes), map, rows,
                       s.S, s.per, d->part, ss);
   else
-    dfl::gemm_f16(d->st, kRDebug, d->taps_a, ps, cols, mb, static_cast<const uint16_t*>(codes), map, rows, s.S,
-                  s.per, d->part, ss);
+    dfl::gemm_f16_block(d->st, d->taps_a, ps, cols, static_cast<const uint16_t*>(codes), map, rows,
+                        d->part, ss);
   dfl::sum_rows(d->st, d->part, s.S, ss, m, rows, y);
   return launch_check(d, "matvec");
 }

@@ -62,6 +62,11 @@ int i4_block_splits(int K, int ks);
 void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
                    const uint16_t* scales, TileMap map, int N, int ks, float* out,
                    long split_stride);
+// The block pass's 16-row f16 GEMM (two planes, ps ≠ 0): f16_block_splits(K)
+// splits of 512 columns; out as gemm_f16.
+int f16_block_splits(int K);
+void gemm_f16_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t* w,
+                    TileMap map, int N, float* out, long split_stride);
 // gate/up with the SwiGLU epilogue at 16 rows, two planes in (xa, ps):
 // gate tiles [0, ftiles), up tiles [ftiles, 2·ftiles) of one stored
 // matrix; writes silu(g)·u in A-layout planes (ma, mps).
@@ -87,11 +92,15 @@ void head_sel(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t
               SelectScratch sc);
 
 void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa, long ps);
-// Row kernels: sqp holds each (row, 256-channel chunk)'s sum of squares.
+// Row kernels: sqp holds partial sums of squares of each row, row_chunks(N)
+// per row from rowsum_sq and embed (256 channels each), conv1_chunks(hs)
+// per row from conv1; norm_apply takes the producer's count.
+int row_chunks(int N);
+int conv1_chunks(int hs);
 void rowsum_sq(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,
                float* out, float* sqp);
-void norm_apply(hipStream_t st, const float* h, const float* sqp, int rows, int N, const float* w,
-                float eps, float* x, uint16_t* xa, long ps);
+void norm_apply(hipStream_t st, const float* h, const float* sqp, int nchunk, int rows, int N,
+                const float* w, float eps, float* x, uint16_t* xa, long ps);
 void embed(hipStream_t st, const uint16_t* emb, int anchor, int mask, int rows, int hs, float* h,
            float* sqp);
 void conv0(hipStream_t st, const float* x, const float* dpart, int splits, long split_stride,

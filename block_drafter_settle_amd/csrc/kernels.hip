@@ -395,20 +395,21 @@ __global__ __launch_bounds__(kThreads) void k_rowsum_sq(const float* __restrict_
   if (threadIdx.x == 0) sqp[(size_t)r * nchunk + c] = sq;
 }
 
-// `rms`: y = h·(1/sqrt(Σh²/N + eps))·w for one chunk of row r, the row's
-// Σh² gathered from its chunks; y to f32 (if x) and to A-layout f16.
+// `rms`: y = h·(1/sqrt(Σh²/N + eps))·w for one 256-channel chunk of row r,
+// the row's Σh² gathered from the producer's `nchunk` partial sums (in a
+// fixed order, so every chunk of a row gets the same scale); y to f32 (if
+// x) and to A-layout f16 planes.
 __global__ __launch_bounds__(kThreads) void k_norm_apply(const float* __restrict__ h,
                                                          const float* __restrict__ sqp,
                                                          int nchunk, int N,
                                                          const float* __restrict__ w, float eps,
                                                          float* __restrict__ x,
                                                          f16* __restrict__ xa, long ps) {
-  __shared__ float part[kThreads];
+  __shared__ float red[4];
   const int r = blockIdx.y, c = blockIdx.x, i = c * kChunk + threadIdx.x;
-  if (threadIdx.x < nchunk) part[threadIdx.x] = sqp[(size_t)r * nchunk + threadIdx.x];
-  __syncthreads();
-  float ss = 0.f;
-  for (int q = 0; q < nchunk; ++q) ss += part[q];
+  float part = 0.f;
+  for (int q = threadIdx.x; q < nchunk; q += kThreads) part += sqp[(size_t)r * nchunk + q];
+  const float ss = block_sum(part, red);
   const float scale = 1.f / sqrtf(ss / N + eps);
   if (i >= N) return;
   const float y = h[(size_t)r * N + i] * scale * w[i];
@@ -464,30 +465,38 @@ __global__ __launch_bounds__(kThreads) void k_conv0(const float* __restrict__ x,
 
 // Conv stage 1 of the sub-layer's output into the residual:
 // h[r][i] += Σ_o (base[1][o][i] + d[r][1][o][i/gs])·out[r−o][i], out being
-// the split-summed GEMM output; each chunk's Σh² of the new rows.
-__global__ __launch_bounds__(kThreads) void k_conv1(float* __restrict__ h,
+// the split-summed GEMM output. One workgroup per kC1 channels and all
+// rows: thread (c, r) split-sums out[r] at its channel once, and the taps
+// read those sums from LDS. Also each (row, kC1 channels)'s Σh² of the new
+// rows, sqp[r][blockIdx.x].
+static constexpr int kC1 = 32;
+__global__ __launch_bounds__(kC1 * 16) void k_conv1(float* __restrict__ h,
                                                     const float* __restrict__ opart, int splits,
                                                     long ss, const float* __restrict__ dsum,
-                                                    const float* __restrict__ base, int hs,
-                                                    int gs, int kn, float* __restrict__ sqp,
-                                                    int nchunk) {
-  __shared__ float red[4];
-  const int r = blockIdx.y, c = blockIdx.x, i = c * kChunk + threadIdx.x;
-  const int G = hs / gs, P = 2 * kn * G;
+                                                    const float* __restrict__ base, int rows,
+                                                    int hs, int gs, int kn,
+                                                    float* __restrict__ sqp, int nchunk) {
+  __shared__ float v[16][kC1];
+  const int c = threadIdx.x % kC1, r = threadIdx.x / kC1;
+  const int i = blockIdx.x * kC1 + c;
+  const bool live = r < rows && i < hs;
+  v[r][c] = live ? sum_splits(opart + (size_t)r * hs + i, splits, ss) : 0.f;
+  __syncthreads();
   float hn = 0.f;
-  if (i < hs) {
-    const int taps = min(kn, r + 1), g = i / gs;
+  if (live) {
+    const int G = hs / gs, P = 2 * kn * G, taps = min(kn, r + 1), g = i / gs;
     const float* b1 = base + (size_t)kn * hs;
     const float* d1 = dsum + (size_t)r * P + (size_t)kn * G;
-    float ov[16];
-    for (int o = 0; o < taps; ++o) ov[o] = sum_splits(opart + (size_t)(r - o) * hs + i, splits, ss);
     float acc = 0.f;
-    for (int o = 0; o < taps; ++o) acc += (b1[(size_t)o * hs + i] + d1[o * G + g]) * ov[o];
+    for (int o = 0; o < taps; ++o) acc += (b1[(size_t)o * hs + i] + d1[o * G + g]) * v[r - o][c];
     hn = h[(size_t)r * hs + i] + acc;
     h[(size_t)r * hs + i] = hn;
   }
-  const float sq = block_sum(hn * hn, red);
-  if (threadIdx.x == 0) sqp[(size_t)r * nchunk + c] = sq;
+  // Σh² over the kC1 channels of row r: the kC1 lanes that hold them
+  float sq = hn * hn;
+#pragma unroll
+  for (int o = kC1 / 2; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+  if (c == 0 && r < rows) sqp[(size_t)r * nchunk + blockIdx.x] = sq;
 }
 
 // One head of one row: split-summed values at columns col0 + i and
@@ -885,23 +894,72 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const float* __restrict__ l
   if (g == 0 && j == 0 && threadIdx.x < 16) counters[threadIdx.x] = 0;
 }
 
-// T of each row: one wave per row over its ngroups maxima (≤ 64·16).
-__global__ __launch_bounds__(64) void k_thresh(const float* __restrict__ gmax, int ngroups, int top,
-                                               float* __restrict__ thr) {
-  __shared__ float ov[32];
-  __shared__ int oi[32];
-  const int j = blockIdx.x, lane = threadIdx.x;
-  float v[16];
-  int ix[16];
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int e = lane + 64 * u;
-    v[u] = e < ngroups ? gmax[(size_t)j * ngroups + e] : -INFINITY;
-    ix[u] = e < ngroups ? e : INT_MAX;
+// An unsigned key whose order is the order of the floats (−0 below +0; NaN
+// is not produced by the head).
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// T of each row: the top-th largest of its ngroups column-group maxima, by a
+// radix select over the maxima's order keys, eight bits a pass from the top:
+// each pass counts the candidates still matching the chosen prefix per
+// next byte, and a suffix scan over the 256 counts picks the byte holding
+// the top-th largest. One workgroup per row.
+static constexpr int kThreshPer = 8;  // maxima per thread: ngroups ≤ 2048
+__global__ __launch_bounds__(kThreads) void k_thresh(const float* __restrict__ gmax, int ngroups,
+                                                     int top, float* __restrict__ thr) {
+  __shared__ int hist[256];
+  __shared__ int wsum[4];
+  __shared__ uint32_t sel[2];  // chosen byte, rank still wanted inside it
+  const int j = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (ngroups < top) {  // fewer groups than candidates: every logit is one
+    if (t == 0) thr[j] = -INFINITY;
+    return;
   }
-  wave_select<16>(v, ix, top, ov, oi);
-  __syncthreads();
-  if (lane == 0) thr[j] = ov[top - 1];
+  uint32_t key[kThreshPer];
+#pragma unroll
+  for (int u = 0; u < kThreshPer; ++u) {
+    const int e = t + kThreads * u;
+    key[u] = e < ngroups ? order_key(gmax[(size_t)j * ngroups + e]) : 0u;
+  }
+  uint32_t prefix = 0, mask = 0;
+  int want = top;  // rank (1-based) of the wanted key among those matching prefix
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[t] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kThreshPer; ++u)
+      if (t + kThreads * u < ngroups && (key[u] & mask) == prefix)
+        atomicAdd(&hist[(key[u] >> shift) & 255], 1);
+    __syncthreads();
+    // suffix sums over bytes: thread t holds byte 255 − t, so an inclusive
+    // prefix scan over t is the count of keys with byte ≥ 255 − t
+    const int c = hist[255 - t];
+    int inc = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) inc += wsum[w];
+    const int above = inc - c;  // keys with a larger byte
+    if (above < want && inc >= want) {
+      sel[0] = 255 - t;
+      sel[1] = want - above;
+    }
+    __syncthreads();
+    prefix |= sel[0] << shift;
+    mask |= 255u << shift;
+    want = (int)sel[1];
+    __syncthreads();
+  }
+  if (t == 0) thr[j] = key_float(prefix);
 }
 
 // Append (value, index) for the lanes with `take`, in lane order, to row j's list.
@@ -1003,11 +1061,38 @@ __device__ void select_list(const float* rv, const int* ri, int count, int want,
   } while (e0 < count);
 }
 
-// Row j's top candidates (wave 0) and row j−1's (wave 1, j ≥ 1, to know the
-// predecessor tp); then the scores of row j's candidates under that
-// predecessor (or the anchor for j = 0, or forced[j]), `select_with`:
+// The first `want` entries in `top_k` order of a row's list of n ≤ kRankMax
+// entries, by rank: an entry's rank is the number of entries better than
+// it (a strict order, indices being distinct), so the entry of rank q < want
+// lands at out[q]. The list is staged in LDS (sv, si); all threads of the
+// block take part.
+static constexpr int kRankMax = 1024;
+__device__ void rank_select(const float* rv, const int* ri, int n, int want, float* sv, int* si,
+                            float* out_v, int* out_i) {
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    sv[e] = rv[e];
+    si[e] = ri[e];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const float v = sv[e];
+    const int i = si[e];
+    int rank = 0;
+    for (int f = 0; f < n; ++f) rank += better(sv[f], si[f], v, i);
+    if (rank < want) {
+      out_v[rank] = v;
+      out_i[rank] = i;
+    }
+  }
+  __syncthreads();
+}
+
+// Row j's top candidates and row j−1's (j ≥ 1, to know the predecessor tp);
+// then the scores of row j's candidates under that predecessor (or the
+// anchor for j = 0, or forced[j]), `select_with`:
 // unary + Σ_q (P[prev][q]·hp[j][q])·C[tok][q]. Block (j, tp); block (j, 0)
-// also writes cand and unary of row j.
+// also writes cand and unary of row j. Lists longer than kRankMax take
+// wave_select passes instead.
 __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
                                                const int* __restrict__ li,
                                                const int* __restrict__ counters, int cap, int top,
@@ -1017,19 +1102,28 @@ __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
                                                const int* __restrict__ forced,
                                                int* __restrict__ cand, float* __restrict__ unary,
                                                float* __restrict__ tab) {
-  __shared__ float uv[2][32];
-  __shared__ int uc[2][32];
+  __shared__ float uv[2][32 + 64];
+  __shared__ int uc[2][32 + 64];
+  __shared__ float sv[kRankMax];
+  __shared__ int si[kRankMax];
   const int j = blockIdx.x, tp = blockIdx.y, tpn = gridDim.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (j == 0 && tp > 0) return;
-  const int row = j - wave;  // wave 0: row j, wave 1: row j−1
-  const bool need = wave == 0 || (j > 0 && !forced);
-  if (need) {
-    const int count = min(counters[row], cap);
-    select_list(lv + (size_t)row * cap, li + (size_t)row * cap, count, wave == 0 ? top : tp + 1,
-                uv[wave], uc[wave]);
+  const int n0 = min(counters[j], cap);
+  const bool prev_row = j > 0 && !forced;
+  const int n1 = prev_row ? min(counters[j - 1], cap) : 0;
+  if (n0 <= kRankMax && n1 <= kRankMax) {
+    rank_select(lv + (size_t)j * cap, li + (size_t)j * cap, n0, top, sv, si, uv[0], uc[0]);
+    if (prev_row)
+      rank_select(lv + (size_t)(j - 1) * cap, li + (size_t)(j - 1) * cap, n1, tp + 1, sv, si,
+                  uv[1], uc[1]);
+  } else {
+    const int row = j - wave;  // wave 0: row j, wave 1: row j−1
+    if (wave == 0 || prev_row)
+      select_list(lv + (size_t)row * cap, li + (size_t)row * cap, wave == 0 ? n0 : n1,
+                  wave == 0 ? top : tp + 1, uv[wave], uc[wave]);
+    __syncthreads();
   }
-  __syncthreads();
   if (wave == 0 && tp == 0 && lane < top) {
     cand[(size_t)j * top + lane] = uc[0][lane];
     unary[(size_t)j * top + lane] = uv[0][lane];
@@ -1071,31 +1165,34 @@ __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
 }
 
 // The chain: row by row, the first candidate with the largest score under
-// the predecessor chosen before it.
-__global__ __launch_bounds__(1024) void k_chain(const float* __restrict__ tab,
-                                                const int* __restrict__ cand, int k, int top,
-                                                int tpn, float* __restrict__ score,
-                                                int* __restrict__ chosen) {
-  extern __shared__ float lt[];
-  const int total = top + (k - 1) * tpn * top;
-#pragma unroll 4
-  for (int e = threadIdx.x; e < total; e += 1024) lt[e] = tab[e];
-  __syncthreads();
-  if (threadIdx.x != 0) return;
+// the predecessor chosen before it. One wave; lane t holds candidate t of
+// the current row (top ≤ 64), and an arg-max over the lanes (the smaller
+// candidate index among equal scores) picks the row's choice.
+__global__ __launch_bounds__(64) void k_chain(const float* __restrict__ tab,
+                                              const int* __restrict__ cand, int k, int top,
+                                              int tpn, float* __restrict__ score,
+                                              int* __restrict__ chosen) {
+  const int lane = threadIdx.x;
   int tp = 0;
   for (int j = 0; j < k; ++j) {
-    const float* row = lt + (j == 0 ? 0 : top + ((size_t)(j - 1) * tpn + tp) * top);
-    float best = -INFINITY;
-    int bt = 0;
-    for (int t = 0; t < top; ++t) {
-      score[(size_t)j * top + t] = row[t];
-      if (row[t] > best) {
-        best = row[t];
-        bt = t;
+    const float* row = tab + (j == 0 ? 0 : top + ((size_t)(j - 1) * tpn + tp) * top);
+    const float v = lane < top ? row[lane] : -INFINITY;
+    if (lane < top) score[(size_t)j * top + lane] = v;
+    // first strictly largest: compare (v, lane) with the smaller lane winning ties;
+    // lanes ≥ top never win (candidate 0 wins an all −∞ row)
+    float bv = v;
+    int bl = lane < top ? lane : 64;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float v2 = __shfl_xor(bv, o, 64);
+      const int l2 = __shfl_xor(bl, o, 64);
+      if (v2 > bv || (v2 == bv && l2 < bl)) {
+        bv = v2;
+        bl = l2;
       }
     }
-    chosen[j] = cand[(size_t)j * top + bt];
-    tp = tpn == 1 ? 0 : bt;
+    if (lane == 0) chosen[j] = cand[(size_t)j * top + bl];
+    tp = tpn == 1 ? 0 : bl;
   }
 }
 
@@ -1224,11 +1321,13 @@ void rowsum_sq(hipStream_t st, const float* part, int splits, long ss, int rows,
   k_rowsum_sq<<<dim3(nch, rows), kThreads, 0, st>>>(part, splits, ss, N, out, sqp, nch);
 }
 
-void norm_apply(hipStream_t st, const float* h, const float* sqp, int rows, int N, const float* w,
-                float eps, float* x, uint16_t* xa, long ps) {
-  const int nch = cdiv(N, kChunk);
-  k_norm_apply<<<dim3(nch, rows), kThreads, 0, st>>>(h, sqp, nch, N, w, eps, x,
-                                                     reinterpret_cast<f16*>(xa), ps);
+int row_chunks(int N) { return cdiv(N, kChunk); }
+int conv1_chunks(int hs) { return cdiv(hs, kC1); }
+
+void norm_apply(hipStream_t st, const float* h, const float* sqp, int nchunk, int rows, int N,
+                const float* w, float eps, float* x, uint16_t* xa, long ps) {
+  k_norm_apply<<<dim3(cdiv(N, kChunk), rows), kThreads, 0, st>>>(h, sqp, nchunk, N, w, eps, x,
+                                                                 reinterpret_cast<f16*>(xa), ps);
 }
 
 void embed(hipStream_t st, const uint16_t* emb, int anchor, int mask, int rows, int hs, float* h,
@@ -1250,9 +1349,8 @@ void conv0(hipStream_t st, const float* x, const float* dpart, int splits, long 
 
 void conv1(hipStream_t st, float* h, const float* opart, int splits, long ss, const float* dsum,
            const float* base, int rows, int hs, int gs, int kn, float* sqp) {
-  const int nch = cdiv(hs, kChunk);
-  k_conv1<<<dim3(nch, rows), kThreads, 0, st>>>(h, opart, splits, ss, dsum, base, hs, gs, kn, sqp,
-                                                nch);
+  const int nch = conv1_chunks(hs);
+  k_conv1<<<nch, kC1 * 16, 0, st>>>(h, opart, splits, ss, dsum, base, rows, hs, gs, kn, sqp, nch);
 }
 
 void qkv_post(hipStream_t st, const float* part, int splits, long ss, int rows, int nh, int kv,
@@ -1311,7 +1409,7 @@ void select_all(hipStream_t st, const float* logits, bool have_gmax, int k, int 
   const int ngroups = cdiv(width, 256), ns = topk_slices(width), cap = topk_cap(width, top);
   if (!have_gmax)
     k_rowmax<<<dim3(ngroups, k), kThreads, 0, st>>>(logits, width, ngroups, sc.gmax, sc.counters);
-  k_thresh<<<k, 64, 0, st>>>(sc.gmax, ngroups, top, sc.thr);
+  k_thresh<<<k, kThreads, 0, st>>>(sc.gmax, ngroups, top, sc.thr);
   k_collect<<<dim3(cdiv(ns, 4), k), kThreads, 0, st>>>(logits, width, top, ns, sc.thr, sc.counters,
                                                        sc.lv, sc.li, cap);
   const int tpn = forced ? 1 : top;
@@ -1319,8 +1417,7 @@ void select_all(hipStream_t st, const float* logits, bool have_gmax, int k, int 
                                         reinterpret_cast<const f16*>(pbook),
                                         reinterpret_cast<const f16*>(cbook), vocab, anchor,
                                         forced, cand, unary, sc.tab);
-  const size_t lds = sizeof(float) * (size_t)(top + (k - 1) * tpn * top);
-  k_chain<<<1, 1024, lds, st>>>(sc.tab, cand, k, top, tpn, score, chosen);
+  k_chain<<<1, 64, 0, st>>>(sc.tab, cand, k, top, tpn, score, chosen);
 }
 
 void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,

@@ -98,6 +98,73 @@ __global__ __launch_bounds__(64 * NW) void k_i4_block(const f16* __restrict__ xa
   }
 }
 
+// The 16-row f16 GEMM of the kernel projections, two activation planes:
+// as k_i4_block with f16 weight tiles, KS 32-column steps a split. Each
+// wave holds all KS·R weight fragments of its share in registers.
+template <int R, int NW, int KS>
+__global__ __launch_bounds__(64 * NW) void k_f16_block(const f16* __restrict__ xa, long ps, int K,
+                                                       const f16* __restrict__ w, TileMap mp,
+                                                       int N, float* __restrict__ out,
+                                                       long split_stride) {
+  constexpr int kFrags = 2 * KS * 64;
+  constexpr int kPer = (kFrags + 64 * NW - 1) / (64 * NW);
+  __shared__ h8 al[2][KS][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int KST = K >> 5;
+  const int sp = blockIdx.y;
+  const int s0 = sp * KS, ns = min(KS, KST - s0);
+  const int t0 = (blockIdx.x * NW + wave) * R;
+  const h8* x0 = reinterpret_cast<const h8*>(xa);
+  const h8* x1 = reinterpret_cast<const h8*>(xa + ps);
+  h8 areg[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = threadIdx.x + i * 64 * NW;
+    const int pl = e / (KS * 64), st = (e / 64) % KS;
+    if (e < kFrags && st < ns) areg[i] = (pl ? x1 : x0)[(size_t)(s0 + st) * 64 + (e & 63)];
+  }
+  h8 b[KS][R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const long st = map_tile(mp, min(t0 + r, mp.ntiles - 1));
+    const h8* wp = reinterpret_cast<const h8*>(w) + (size_t)st * KST * 64 + lane;
+#pragma unroll
+    for (int u = 0; u < KS; ++u) b[u][r] = wp[(size_t)(s0 + min(u, ns - 1)) * 64];
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = threadIdx.x + i * 64 * NW;
+    const int pl = e / (KS * 64), st = (e / 64) % KS;
+    if (e < kFrags && st < ns) al[pl][st][e & 63] = areg[i];
+  }
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  asm volatile("s_barrier" ::: "memory");
+  f4 acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < KS; ++u) {
+    if (u < ns) {
+      const h8 a = al[0][u][lane], a2 = al[1][u][lane];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        acc[r] = mfma16(a, b[u][r], acc[r]);
+        acc[r] = mfma16(a2, b[u][r], acc[r]);
+      }
+    }
+  }
+  if (t0 >= mp.ntiles) return;
+  float* o = out + (size_t)sp * split_stride;
+  const int j = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = t0 + r, col = t * 16 + n;
+    if (t < mp.ntiles && col < N)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[(size_t)(4 * j + v) * N + col] = acc[r][v];
+  }
+}
+
 // gate/up over the full K with SwiGLU in the epilogue: workgroup g owns
 // ffn tiles [FP·g, FP·g + FP), i.e. FP gate tiles and the FP up tiles
 // (ftiles further on in the stored matrix); its NW waves split K, and their
@@ -197,6 +264,19 @@ void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uin
     k_i4_block<kBlkR, kBlkNW, 2><<<grid, 64 * kBlkNW, 0, st>>>(x, ps, K, c, s, map, N, out, ss);
   else
     k_i4_block<kBlkR, kBlkNW, 4><<<grid, 64 * kBlkNW, 0, st>>>(x, ps, K, c, s, map, N, out, ss);
+}
+
+
+// k_f16_block: one tile a wave, 16 steps (512 columns) a split
+static constexpr int kF16R = 1, kF16NW = 4, kF16KS = 16;
+
+int f16_block_splits(int K) { return (int)cdiv(K / 32, kF16KS); }
+
+void gemm_f16_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t* w,
+                    TileMap map, int N, float* out, long ss) {
+  const dim3 grid(cdiv(map.ntiles, kF16R * kF16NW), f16_block_splits(K));
+  k_f16_block<kF16R, kF16NW, kF16KS><<<grid, 64 * kF16NW, 0, st>>>(
+      reinterpret_cast<const f16*>(xa), ps, K, reinterpret_cast<const f16*>(w), map, N, out, ss);
 }
 
 void gemm_glu(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
