@@ -77,8 +77,9 @@ def main():
     # ------------------------------------------------ settle-bound workload
     n_set = 256 * args.settle_calls
     taps4 = synth.make_taps(g, n_set, seed=0, name="settle_taps", outliers=True, device=dev)
+    calls = args.settle_calls
     for i in range(4):
-        d.settle(0, 256, taps4[256 * i:].data_ptr())
+        d.settle(0, 256, taps4[256 * (i % calls):].data_ptr())
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
@@ -91,7 +92,7 @@ def main():
     log(f"settle: {n_set} rows in {settle_s * 1e3:.2f} ms -> {settle_rows_s / 1e6:.3f} M rows/s")
     d.set_timing(True)
     for i in range(8):
-        d.settle(256 * i, 256, taps4[256 * i:].data_ptr())
+        d.settle(256 * i, 256, taps4[256 * (i % calls):].data_ptr())
     st_settle, _, n_settles = d.stage_times()
     d.set_timing(False)
     del taps4

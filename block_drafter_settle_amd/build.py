@@ -9,9 +9,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdflash.so")
-# source, extra flags: the block pass's int4 kernels keep MFMA results in
-# VGPRs (their results are scaled in VALU at once)
-SOURCES = [("kernels.hip", []), ("skinny.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+# source, extra flags: the block pass's int4 kernels and the attention keep
+# MFMA results in VGPRs (their results are rescaled in VALU at once)
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+SOURCES = [("kernels.hip", []), ("skinny.hip", VGPR_FORM), ("attention.hip", VGPR_FORM),
            ("dflash.cpp", [])]
 
 FLAGS = [

@@ -32,6 +32,7 @@ constexpr int kKsQkv = 2;    // q/k/v, int4: spans (128 columns) per split
 constexpr int kKsO = 2;      // o, int4
 constexpr int kKsDown = 4;   // down, int4
 constexpr int kRKv = 2;      // settle's k/v of every layer, int4
+constexpr int kSettleI4Blocks = 2;  // above this many 16-row blocks the settle's k/v use the f16 halves
 constexpr int kRDebug = 2;   // the debug matvec
 
 thread_local std::string g_create_error;
@@ -154,6 +155,9 @@ struct dflash {
   dfl::SelectScratch sel_sc{};
   // settle scratch
   uint16_t *taps_a = nullptr, *t_a = nullptr;
+  // the settle's keys and values at many rows: Wk/Wv of every layer as two
+  // exact f16 halves, F16T [L·2·kd][2·hs], and the operand [t | t]
+  uint16_t *kvw = nullptr, *t_a2 = nullptr;
   float* tbuf = nullptr;
   long part_floats = 0;
   int stage_cols = 0;  // widest activation the staging buffer holds
@@ -349,6 +353,10 @@ long partial_need(const dflash* d) {
   for (int N : {d->qd, d->kd, d->ffn}) i4b(N, d->hs, 2);
   i4b(d->hs, d->qd, 2);
   i4b(d->hs, d->ffn, 2);
+  for (int mb = kSettleI4Blocks + 1; mb <= kSettleRows / 16; ++mb) {
+    const Split s = split_big(d->L * 2 * d->kd / 16, 2 * d->hs / 32);
+    need = std::max(need, (long)s.S * mb * 16 * d->L * 2 * d->kd);
+  }
   for (int mb = 2; mb <= kSettleRows / 16; ++mb)
     for (int N : {d->hs, d->P, d->rank}) {
       const int K = N == d->hs ? d->tw : d->hs;
@@ -388,7 +396,7 @@ int attn_chunk(long n, int* nchunks) {
     *nchunks = 0;
     return 32;
   }
-  long c = std::max(128L, (n + kMaxChunks - 1) / kMaxChunks);
+  long c = std::max(64L, (n + kMaxChunks - 1) / kMaxChunks);
   c = (c + 31) / 32 * 32;
   *nchunks = (int)((n + c - 1) / c);
   return (int)c;
@@ -556,6 +564,15 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   if (!rc) rc = dev_alloc(d, &d->tbuf, (size_t)kSettleRows * hs, "settle scratch");
   if (!rc) rc = dev_alloc(d, &d->sqp, (size_t)kSettleRows * ((hs + 255) / 256), "norm scratch");
   if (!rc) rc = dev_alloc(d, &d->sel_sc.tab, (size_t)d->top * (1 + 15 * d->top), "selector table");
+  if (!rc) rc = dev_alloc(d, &d->kvw, (size_t)d->L * 2 * d->kd * 2 * hs, "settle k/v weights");
+  if (!rc) rc = dev_alloc(d, &d->t_a2, (size_t)kSettleRows * 2 * hs, "settle scratch");
+  if (!rc) {
+    const int kvt = 2 * d->kd / 16;
+    dfl::i4_planes(d->st, d->qkv.codes, d->qkv.scales,
+                   dfl::TileMap{d->L * kvt, kvt, d->qkv.tiles, d->qd / 16}, d->L * 2 * d->kd, hs,
+                   d->kvw);
+    rc = launch_check(d, "create");
+  }
   if (!rc) rc = hip_check(nullptr, hipDeviceSynchronize(), "create");
   return done(rc);
 }
@@ -627,11 +644,28 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
   // K and V of every layer: the k and v tiles of each layer's q/k/v set
   const int kvt = 2 * d->kd / 16;
   const int N = d->L * 2 * d->kd;
-  const Split sk = split_for(d->L * kvt, kRKv, d->hs / 128, mb, 4);
   const long ssk = (long)mb * 16 * N;
-  dfl::TileMap map{d->L * kvt, kvt, d->qkv.tiles, d->qd / 16};
-  dfl::gemm_i4(st, kRKv, d->t_a, 0, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per, d->part,
-               ssk);
+  Split sk;
+  if (mb > kSettleI4Blocks) {
+    // [t | t] against the two halves of each weight: rows' 16-row blocks
+    // side by side, each block written twice
+    const size_t blk = (size_t)16 * d->hs * sizeof(uint16_t);
+    for (int h = 0; h < 2; ++h) {
+      const int rc = hip_check(d, hipMemcpy2DAsync(reinterpret_cast<char*>(d->t_a2) + h * blk,
+                                                   2 * blk, d->t_a, blk, blk, mb,
+                                                   hipMemcpyDeviceToDevice, st),
+                               "settle");
+      if (rc) return rc;
+    }
+    sk = split_big(d->L * kvt, 2 * d->hs / 32);
+    dfl::gemm_big_f16(st, d->t_a2, 2 * d->hs, mb, d->kvw, dfl::TileMap{d->L * kvt, d->L * kvt, 0, 0},
+                      N, sk.S, sk.per, d->part, ssk);
+  } else {
+    sk = split_for(d->L * kvt, kRKv, d->hs / 128, mb, 4);
+    dfl::TileMap map{d->L * kvt, kvt, d->qkv.tiles, d->qd / 16};
+    dfl::gemm_i4(st, kRKv, d->t_a, 0, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per,
+                 d->part, ssk);
+  }
   tm_mark(d, DFLASH_ST_S_KV);
   dfl::settle_kv(st, d->part, sk.S, ssk, m, d->L, d->kv, d->hd, d->k_norm, d->inv, d->rot_dev,
                  pos0, d->eps, d->sk, d->sv, d->cap, row0);

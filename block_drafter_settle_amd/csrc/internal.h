@@ -132,6 +132,10 @@ void select_all(hipStream_t st, const float* logits, bool have_gmax, int k, int 
                 float* unary, float* score, int* chosen);
 void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,
                 int rows, int K, float* out);
+// int4 rows (map's tiles [0, rows/16)) → F16T [rows][2K]: q·s as two exact
+// f16 halves, hi in columns [0, K), the remainder in [K, 2K).
+void i4_planes(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,
+               int rows, int K, uint16_t* w);
 void sum_rows(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,
               float* out);
 

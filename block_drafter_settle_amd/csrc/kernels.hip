@@ -607,205 +607,6 @@ __global__ __launch_bounds__(64) void k_settle_kv(const float* __restrict__ part
   }
 }
 
-// -------------------------------------------------------------- attention
-
-// Split-context attention (`Drafter::block`'s inner loop). Block (c, g, z):
-// kv head g, its q heads 4z..4z+3, and key chunk c — context keys
-// [c·chunk, min(n, (c+1)·chunk)) of the layer's range, or for c == nchunks
-// the block's own B keys. Each wave keeps one q head's 16 query rows and an
-// online softmax over 32-key steps: S^T = K·Q^T and O^T += V^T·P^T on MFMA.
-// Every operand is an f16 pair (hi, lo = f16 of the rest): q's two A-layout
-// planes (plane 1 at qa + qps), K and V split into two LDS planes, P split
-// in registers; each product takes hi·hi + hi·lo + lo·hi, the dropped lo·lo
-// term lying below f32 rounding. Writes the chunk's (max, sum, O) for the
-// merge.
-template <int HD>
-__global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, long qps,
-                                                   const float* __restrict__ sk,
-                                                   const float* __restrict__ sv,
-                                                   const float* __restrict__ kb,
-                                                   const float* __restrict__ vb, int B, int nh,
-                                                   int kv, int n, long lo_pos, long a, int window,
-                                                   int chunk, int nchunks, float scale,
-                                                   float* __restrict__ pacc,
-                                                   float2* __restrict__ pml) {
-  constexpr int KST = HD + 8;   // LDS row stride of K (halfs)
-  constexpr int VST = 32 + 8;   // LDS row stride of V^T (halfs)
-  constexpr int EPT = HD / 8;   // staged elements per thread per 32 keys
-  __shared__ f16 Ks[2][32 * KST];
-  __shared__ f16 Vt[2][HD * VST];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = blockIdx.x, g = blockIdx.y;
-  const int rep = nh / kv;
-  const int qi = blockIdx.z * 4 + wave;
-  const bool active = qi < rep;
-  const int hq = g * rep + min(qi, rep - 1);
-  const int kd = kv * HD;
-  const bool blk = c == nchunks;
-  const int k_first = blk ? 0 : c * chunk;
-  const int count = blk ? B : min(chunk, n - k_first);
-  const float* kbase = blk ? kb + (size_t)g * HD : sk + (size_t)k_first * kd + (size_t)g * HD;
-  const float* vbase = blk ? vb + (size_t)g * HD : sv + (size_t)k_first * kd + (size_t)g * HD;
-  const long pos_base = lo_pos + k_first;
-
-  h8 qf[HD / 32], ql[HD / 32];
-#pragma unroll
-  for (int s = 0; s < HD / 32; ++s) {
-    const size_t off = (size_t)hq * 16 * HD + ((size_t)s * 64 + lane) * 8;
-    qf[s] = *reinterpret_cast<const h8*>(qa + off);
-    ql[s] = *reinterpret_cast<const h8*>(qa + qps + off);
-  }
-
-  const int r = lane & 15, j = lane >> 4;
-  const long lim = window > 0 ? a + r + 1 - window : LONG_MIN;
-  float m_run = -INFINITY, l_run = 0.f;
-  f4 acc[HD / 16];
-#pragma unroll
-  for (int d = 0; d < HD / 16; ++d) acc[d] = (f4){0.f, 0.f, 0.f, 0.f};
-
-  // staging: thread t copies key t%32, dims (t/32)·EPT .. +EPT
-  const int skey = threadIdx.x & 31, sd0 = (threadIdx.x >> 5) * EPT;
-  float4 kreg[EPT / 4], vreg[EPT / 4];
-  auto fetch = [&](int k0) {
-    const bool ok = k0 + skey < count;
-    const float4* kp = reinterpret_cast<const float4*>(kbase + (size_t)(k0 + skey) * kd + sd0);
-    const float4* vp = reinterpret_cast<const float4*>(vbase + (size_t)(k0 + skey) * kd + sd0);
-#pragma unroll
-    for (int e = 0; e < EPT / 4; ++e) {
-      kreg[e] = ok ? kp[e] : make_float4(0.f, 0.f, 0.f, 0.f);
-      vreg[e] = ok ? vp[e] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  if (count > 0) fetch(0);
-  for (int k0 = 0; k0 < count; k0 += 32) {
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < EPT / 4; ++e) {
-      const float kf[4] = {kreg[e].x, kreg[e].y, kreg[e].z, kreg[e].w};
-      const float vf[4] = {vreg[e].x, vreg[e].y, vreg[e].z, vreg[e].w};
-      h4 khi, klo;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        khi[q] = (f16)kf[q];
-        klo[q] = (f16)(kf[q] - (float)khi[q]);
-        const f16 vh = (f16)vf[q];
-        Vt[0][(sd0 + 4 * e + q) * VST + skey] = vh;
-        Vt[1][(sd0 + 4 * e + q) * VST + skey] = (f16)(vf[q] - (float)vh);
-      }
-      *reinterpret_cast<h4*>(&Ks[0][skey * KST + sd0 + 4 * e]) = khi;
-      *reinterpret_cast<h4*>(&Ks[1][skey * KST + sd0 + 4 * e]) = klo;
-    }
-    __syncthreads();
-    if (k0 + 32 < count) fetch(k0 + 32);
-
-    // scores: st[h][v] = S^T[key 16h + 4j + v][query r]
-    f4 st[2];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      st[hb] = (f4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < HD / 32; ++s) {
-        const int off = (16 * hb + (lane & 15)) * KST + 32 * s + 8 * j;
-        const h8 ka = *reinterpret_cast<const h8*>(&Ks[0][off]);
-        const h8 kl = *reinterpret_cast<const h8*>(&Ks[1][off]);
-        st[hb] = mfma16(ka, qf[s], st[hb]);
-        st[hb] = mfma16(ka, ql[s], st[hb]);
-        st[hb] = mfma16(kl, qf[s], st[hb]);
-      }
-    }
-    float p[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = 16 * (e >> 2) + 4 * j + (e & 3);
-      const int idx = k0 + key;
-      const bool ok = idx < count && (blk || window == 0 || pos_base + idx >= lim);
-      p[e] = ok ? st[e >> 2][e & 3] * scale : -INFINITY;
-      mx = fmaxf(mx, p[e]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float corr = m_new == -INFINITY ? 1.f : expf(m_run - m_new);
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = p[e] == -INFINITY ? 0.f : expf(p[e] - m_new);
-      ps += p[e];
-    }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l_run = l_run * corr + ps;
-    m_run = m_new;
-    h8 pb, pl;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pb[e] = (f16)p[e];
-      pl[e] = (f16)(p[e] - (float)pb[e]);
-    }
-#pragma unroll
-    for (int d = 0; d < HD / 16; ++d) {
-      const int off = (16 * d + (lane & 15)) * VST + 4 * j;
-      const h4 v0 = *reinterpret_cast<const h4*>(&Vt[0][off]);
-      const h4 v1 = *reinterpret_cast<const h4*>(&Vt[0][off + 16]);
-      const h4 w0 = *reinterpret_cast<const h4*>(&Vt[1][off]);
-      const h4 w1 = *reinterpret_cast<const h4*>(&Vt[1][off + 16]);
-      const h8 va = (h8){v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      const h8 vl = (h8){w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      f4 t = mfma16(va, pb, acc[d] * corr);
-      t = mfma16(va, pl, t);
-      acc[d] = mfma16(vl, pb, t);
-    }
-  }
-  if (!active) return;
-  const size_t slot = ((size_t)g * (nchunks + 1) + c) * rep + qi;
-  float* po = pacc + (slot * 16 + r) * HD;
-#pragma unroll
-  for (int d = 0; d < HD / 16; ++d)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) po[16 * d + 4 * j + v] = acc[d][v];
-  if (j == 0) pml[slot * 16 + r] = make_float2(m_run, l_run);
-}
-
-// Softmax-merge of the chunks of one (q head, row) → y in A-layout f16:
-// y = Σ_c acc_c·e^{m_c − M} / Σ_c l_c·e^{m_c − M}, M the largest chunk max.
-// One thread per chunk forms the weights, one thread per dimension sums.
-__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pacc,
-                                                    const float2* __restrict__ pml, int nh,
-                                                    int kv, int hd, int nchunks,
-                                                    f16* __restrict__ ya, long ps) {
-  __shared__ float fw[256], red[4], redl[4];
-  const int hq = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
-  const int rep = nh / kv, g = hq / rep, qi = hq % rep, nc = nchunks + 1;
-  const size_t slot0 = (size_t)g * nc * rep + qi;  // chunk c is slot slot0 + c·rep
-  float2 ml = make_float2(-INFINITY, 0.f);
-  if (t < nc) ml = pml[(slot0 + (size_t)t * rep) * 16 + r];
-  float m = ml.x;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  float M = red[0];
-  for (int w = 1; w < nw; ++w) M = fmaxf(M, red[w]);
-  const float f = (t < nc && ml.x != -INFINITY) ? expf(ml.x - M) : 0.f;
-  if (t < nc) fw[t] = f;
-  const float l = wave_sum(ml.y * f);
-  if (lane == 0) redl[wave] = l;
-  __syncthreads();
-  float L = 0.f;
-  for (int w = 0; w < nw; ++w) L += redl[w];
-  if (t >= hd) return;
-  float y0 = 0.f, y1 = 0.f;
-  int c = 0;
-  for (; c + 2 <= nc; c += 2) {
-    y0 += pacc[((slot0 + (size_t)c * rep) * 16 + r) * hd + t] * fw[c];
-    y1 += pacc[((slot0 + (size_t)(c + 1) * rep) * 16 + r) * hd + t] * fw[c + 1];
-  }
-  if (c < nc) y0 += pacc[((slot0 + (size_t)c * rep) * 16 + r) * hd + t] * fw[c];
-  put_a(ya, ps, a_idx(r, hq * hd + t), (y0 + y1) / L);
-}
-
 // ------------------------------------------------------- top-k, selector
 
 // Orders this wave's LDS accesses (lane 0's writes before every lane's reads).
@@ -1213,6 +1014,36 @@ __global__ void k_dequant_i4(const uint32_t* __restrict__ codes, const uint16_t*
   out[idx] = (float)q * half_bits(sb);
 }
 
+// int4 rows → F16T tiles of 2K columns holding each weight q·s exactly as
+// two halves: columns [0, K) the f16 rounding hi of q·s, columns [K, 2K)
+// the f16 of q·s − hi (q·s has at most 14 significant bits, hi takes 11).
+// A GEMM against [x | x] then sums x·hi + x·lo, the exact dequantised
+// product. One thread per (row, 8 columns) of the low half.
+__global__ void k_i4_planes(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+                            TileMap mp, int rows, int K, f16* __restrict__ w) {
+  const long idx = (long)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (long)rows * (K >> 3)) return;
+  const int row = idx / (K >> 3), k0 = (int)(idx % (K >> 3)) * 8;
+  const int t = row >> 4, n = row & 15, KT = K >> 7;
+  const long st = map_tile(mp, t);
+  const int p = k0 >> 7, u = (k0 >> 5) & 3, j = (k0 >> 3) & 3;
+  const uint32_t word = codes[(((size_t)st * KT + p) * 64 + j * 16 + n) * 4 + u];
+  const float sc = half_bits(scales[(((size_t)st * KT + p) * 16 + n) * 4 + u]);
+  h8 hi, lo;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int pos = (e & 1) ? 16 + 2 * (e - 1) : 2 * e;
+    const float v = (float)((int)((word >> pos) & 15u) - 8) * sc;
+    hi[e] = (f16)v;
+    lo[e] = (f16)(v - (float)hi[e]);
+  }
+  // F16T of the 2K-column matrix: tile t, step s, lane n + 16·j
+  const int KS2 = (2 * K) >> 5, lane = n + 16 * j;
+  h8* wt = reinterpret_cast<h8*>(w) + (size_t)t * KS2 * 64;
+  wt[(size_t)(k0 >> 5) * 64 + lane] = hi;
+  wt[(size_t)((K + k0) >> 5) * 64 + lane] = lo;
+}
+
 __global__ void k_sum_rows(const float* __restrict__ part, int splits, long ss, int rows, int N,
                            float* __restrict__ out) {
   const long idx = (long)blockIdx.x * kThreads + threadIdx.x;
@@ -1369,32 +1200,6 @@ void settle_kv(hipStream_t st, const float* part, int splits, long ss, int rows,
                                    sk, sv, cap, row0);
 }
 
-void attention(hipStream_t st, const uint16_t* qa, long qps, const float* sk, const float* sv,
-               const float* kb, const float* vb, int B, int nh, int kv, int hd, int n,
-               long lo_pos, long a, int window, int chunk, int nchunks, float scale, float* pacc,
-               float* pml) {
-  const int rep = nh / kv;
-  dim3 grid(nchunks + 1, kv, cdiv(rep, 4));
-  const f16* q = reinterpret_cast<const f16*>(qa);
-  float2* ml = reinterpret_cast<float2*>(pml);
-  if (hd == 64)
-    k_attn<64><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, kb, vb, B, nh, kv, n, lo_pos, a, window,
-                                          chunk, nchunks, scale, pacc, ml);
-  else if (hd == 128)
-    k_attn<128><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, kb, vb, B, nh, kv, n, lo_pos, a, window,
-                                           chunk, nchunks, scale, pacc, ml);
-  else
-    k_attn<256><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, kb, vb, B, nh, kv, n, lo_pos, a, window,
-                                           chunk, nchunks, scale, pacc, ml);
-}
-
-void attn_merge(hipStream_t st, const float* pacc, const float* pml, int nh, int kv, int hd,
-                int nchunks, int B, uint16_t* ya, long ps) {
-  dim3 grid(nh, B);
-  k_attn_merge<<<grid, hd, 0, st>>>(pacc, reinterpret_cast<const float2*>(pml), nh, kv, hd, nchunks,
-                                    reinterpret_cast<f16*>(ya), ps);
-}
-
 int topk_slices(int width) { return cdiv(width, 64 * kSliceVPL); }
 
 int topk_cap(int width, int top) {
@@ -1424,6 +1229,12 @@ void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, Ti
                 int rows, int K, float* out) {
   k_dequant_i4<<<cdiv((long)rows * K, kThreads), kThreads, 0, st>>>(
       reinterpret_cast<const uint32_t*>(codes), scales, map, rows, K, out);
+}
+
+void i4_planes(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,
+               int rows, int K, uint16_t* w) {
+  k_i4_planes<<<cdiv((long)rows * (K / 8), kThreads), kThreads, 0, st>>>(
+      reinterpret_cast<const uint32_t*>(codes), scales, map, rows, K, reinterpret_cast<f16*>(w));
 }
 
 void sum_rows(hipStream_t st, const float* part, int splits, long ss, int rows, int N,
