@@ -44,6 +44,11 @@ def main():
     ap.add_argument("--settle-calls", type=int, default=64)
     ap.add_argument("--timing-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB elementwise copy (x*1 into another buffer), the "
+                         "reference kernel for scaling the HBM byte counters")
+    ap.add_argument("--cpu-steps", type=int, default=4,
+                    help="stream steps the CPU oracle baseline runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -73,6 +78,14 @@ def main():
     t0 = time.time()
     d = pkg.Drafter(g, w, max_context=cap, stream=stream)
     log(f"drafter created in {time.time() - t0:.1f}s (store capacity {cap} rows)")
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy probe: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written")
+        del src, dst
 
     # ------------------------------------------------ settle-bound workload
     n_set = 256 * args.settle_calls
@@ -206,7 +219,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(head_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": head_traffic(),
             "us_per_launch": round(head_us, 2),
             "bytes_per_launch": int(head_bytes),
         },
@@ -217,7 +230,7 @@ def main():
             "mfma_frac_call": round(settle_flops / (settle_call_us * 1e-6) / 1e12 /
                                     F16_MFMA_PEAK_TFS, 4),
             "roofline": {
-                "kernel": "k_gemm_f16 (fc, 256 rows)",
+                "kernel": "k_gemm_big_f16 (fc, 256 rows)",
                 "bound": "mfma",
                 "achieved": round(fc_flops / (fc_us * 1e-6) / 1e12, 2),
                 "peak": F16_MFMA_PEAK_TFS,
@@ -231,36 +244,71 @@ def main():
     }
 
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(g, w, synth)
+        res["cpu_baseline"] = cpu_baseline(g, w, synth, args.cpu_steps)
     d.close()
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(g, w, synth):
-    """The CPU oracle on a bounded sample of the stream: one step (8 tap
-    rows settled + one block over a 32768-row context) on the host cores."""
-    import numpy as np
+HEAD_TRAFFIC = os.path.join(ROOT, "profiles", "k_head_27b_stream_traffic.txt")
+KERNELS = os.path.join(ROOT, "block_drafter_settle_amd", "csrc", "kernels.hip")
 
+
+def head_source_sha1():
+    """sha1 of the head kernel's source text (its comment through the row
+    kernels' section line), so a traffic figure taken from counters is only
+    reported for the kernel it was taken on."""
+    import hashlib
+
+    src = open(KERNELS).read()
+    a = src.find("// The head over rows 1..k")
+    b = src.find("// ----------------------------------------------------------- row kernels")
+    if a < 0 or b < a:
+        return None
+    return hashlib.sha1(src[a:b].encode()).hexdigest()
+
+
+def head_traffic():
+    """HBM bytes per k_head launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the plain copy's reading), or
+    None when there is none or the kernel changed since it was taken."""
+    try:
+        fields = dict(l.split(":", 1) for l in open(HEAD_TRAFFIC) if ":" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    if fields.get("kernel_source_sha1", "").strip() != head_source_sha1():
+        return None
+    return int(float(fields["traffic_bytes_per_launch"]))
+
+
+def cpu_baseline(g, w, synth, steps):
+    """The CPU oracle on a bounded sample of the stream: `steps` stream steps
+    (8 tap rows settled + one block over a 32768-row context each) on the
+    host cores."""
     from oracle import oracle
 
     oracle.build()
-    log("cpu baseline: oracle, one stream step ...")
+    log(f"cpu baseline: oracle, {steps} stream steps ...")
     m = oracle.Model(g, w)
     store = [(k.numpy(), v.numpy()) for k, v in synth.make_store(g, 32768, seed=0)]
-    taps = synth.make_taps(g, 8, seed=0, name="stream").numpy()
-    t0 = time.perf_counter()
-    m.settle(taps, 32768)
-    t1 = time.perf_counter()
-    r = m.block(store, 0, 32768, 5, 32768, g["block"] - 1, g["vocab"])
-    m.select(r["logits"], r["hp"], 5)
-    t2 = time.perf_counter()
+    taps = synth.make_taps(g, 8 * steps, seed=0, name="stream").numpy()
+    anchors = synth.uniform_tokens(g, steps, seed=0)
+    t_settle = t_block = 0.0
+    for i in range(steps):
+        t0 = time.perf_counter()
+        m.settle(taps[8 * i:8 * i + 8], 32768 + 8 * i)
+        t1 = time.perf_counter()
+        r = m.block(store, 0, 32768, anchors[i], 32768, g["block"] - 1, g["vocab"])
+        m.select(r["logits"], r["hp"], anchors[i])
+        t2 = time.perf_counter()
+        t_settle += t1 - t0
+        t_block += t2 - t1
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count()))
-    log(f"cpu baseline: settle 8 rows {t1 - t0:.1f}s, block {t2 - t1:.1f}s")
-    return {"value": round(1.0 / (t2 - t0), 4), "unit": "blocks/s", "cores": cores,
+    log(f"cpu baseline: settle {t_settle:.1f}s, block {t_block:.1f}s over {steps} steps")
+    return {"value": round(steps / (t_settle + t_block), 4), "unit": "blocks/s", "cores": cores,
             "kind": "oracle",
-            "sample": "one stream step of the same workload: 8 tap rows settled + one block "
-                      "(32768-position synthetic context, k=15, width=vocab) + selection",
-            "settle_s": round(t1 - t0, 2), "block_s": round(t2 - t1, 2)}
+            "sample": f"{steps} stream steps of the same workload: 8 tap rows settled + one block "
+                      "(32768-position synthetic context, k=15, width=vocab) + selection, each",
+            "settle_s": round(t_settle, 2), "block_s": round(t_block, 2)}
 
 
 if __name__ == "__main__":

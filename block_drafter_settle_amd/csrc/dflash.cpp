@@ -639,24 +639,17 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
   tm_mark(d, DFLASH_ST_S_FC);
   dfl::rowsum_sq(st, d->part, sf.S, ssf, m, d->hs, d->tbuf, d->sqp);
   tm_mark(d, DFLASH_ST_S_NORM);
-  dfl::norm_apply(st, d->tbuf, d->sqp, dfl::row_chunks(d->hs), m, d->hs, d->hidden_norm, d->eps, nullptr, d->t_a, 0);
+  // the K/V product's operand: t, or [t | t] against the two weight halves
+  const bool halves = mb > kSettleI4Blocks;
+  dfl::norm_apply(st, d->tbuf, d->sqp, dfl::row_chunks(d->hs), m, d->hs, d->hidden_norm, d->eps,
+                  nullptr, halves ? d->t_a2 : d->t_a, halves ? -1 : 0);
   tm_mark(d, DFLASH_ST_S_NORM);
   // K and V of every layer: the k and v tiles of each layer's q/k/v set
   const int kvt = 2 * d->kd / 16;
   const int N = d->L * 2 * d->kd;
   const long ssk = (long)mb * 16 * N;
   Split sk;
-  if (mb > kSettleI4Blocks) {
-    // [t | t] against the two halves of each weight: rows' 16-row blocks
-    // side by side, each block written twice
-    const size_t blk = (size_t)16 * d->hs * sizeof(uint16_t);
-    for (int h = 0; h < 2; ++h) {
-      const int rc = hip_check(d, hipMemcpy2DAsync(reinterpret_cast<char*>(d->t_a2) + h * blk,
-                                                   2 * blk, d->t_a, blk, blk, mb,
-                                                   hipMemcpyDeviceToDevice, st),
-                               "settle");
-      if (rc) return rc;
-    }
+  if (halves) {
     sk = split_big(d->L * kvt, 2 * d->hs / 32);
     dfl::gemm_big_f16(st, d->t_a2, 2 * d->hs, mb, d->kvw, dfl::TileMap{d->L * kvt, d->L * kvt, 0, 0},
                       N, sk.S, sk.per, d->part, ssk);

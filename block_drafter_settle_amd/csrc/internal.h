@@ -94,7 +94,8 @@ void head_sel(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t
 void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa, long ps);
 // Row kernels: sqp holds partial sums of squares of each row, row_chunks(N)
 // per row from rowsum_sq and embed (256 channels each), conv1_chunks(hs)
-// per row from conv1; norm_apply takes the producer's count.
+// per row from conv1; norm_apply takes the producer's count. norm_apply
+// with ps < 0 writes one plane of 2N columns, [y | y].
 int row_chunks(int N);
 int conv1_chunks(int hs);
 void rowsum_sq(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,

@@ -398,7 +398,9 @@ __global__ __launch_bounds__(kThreads) void k_rowsum_sq(const float* __restrict_
 // `rms`: y = h·(1/sqrt(Σh²/N + eps))·w for one 256-channel chunk of row r,
 // the row's Σh² gathered from the producer's `nchunk` partial sums (in a
 // fixed order, so every chunk of a row gets the same scale); y to f32 (if
-// x) and to A-layout f16 planes.
+// x) and to A-layout f16 planes. ps < 0 writes instead one plane of 2N
+// columns holding y twice, [y | y] (the operand of a product against two
+// weight halves).
 __global__ __launch_bounds__(kThreads) void k_norm_apply(const float* __restrict__ h,
                                                          const float* __restrict__ sqp,
                                                          int nchunk, int N,
@@ -414,7 +416,13 @@ __global__ __launch_bounds__(kThreads) void k_norm_apply(const float* __restrict
   if (i >= N) return;
   const float y = h[(size_t)r * N + i] * scale * w[i];
   if (x) x[(size_t)r * N + i] = y;
-  put_a(xa, ps, (size_t)(r >> 4) * 16 * N + a_idx(r & 15, i), y);
+  if (ps < 0) {
+    f16* blk = xa + (size_t)(r >> 4) * 16 * 2 * N;
+    blk[a_idx(r & 15, i)] = (f16)y;
+    blk[a_idx(r & 15, i + N)] = (f16)y;
+  } else {
+    put_a(xa, ps, (size_t)(r >> 4) * 16 * N + a_idx(r & 15, i), y);
+  }
 }
 
 // The block's rows [E[anchor], E[mask]…] (f16 → f32) and each chunk's Σh².
