@@ -94,11 +94,14 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
       h4 khi, klo;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        khi[q] = (f16)kf[q];
-        klo[q] = (f16)(kf[q] - (float)khi[q]);
-        const f16 vh = (f16)vf[q];
+        f16 kh, kl;
+        split_f16(kf[q], kh, kl);
+        khi[q] = kh;
+        klo[q] = kl;
+        f16 vh, vl;
+        split_f16(vf[q], vh, vl);
         Vt[0][(sd0 + 4 * e + q) * VST + skey] = vh;
-        Vt[1][(sd0 + 4 * e + q) * VST + skey] = (f16)(vf[q] - (float)vh);
+        Vt[1][(sd0 + 4 * e + q) * VST + skey] = vl;
       }
       *reinterpret_cast<h4*>(&Ks[0][skey * KST + sd0 + 4 * e]) = khi;
       *reinterpret_cast<h4*>(&Ks[1][skey * KST + sd0 + 4 * e]) = klo;
@@ -148,8 +151,10 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
     h8 pb, pl;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pb[e] = (f16)p[e];
-      pl[e] = (f16)(p[e] - (float)pb[e]);
+      f16 h, l;
+      split_f16(p[e], h, l);
+      pb[e] = h;
+      pl[e] = l;
     }
 #pragma unroll
     for (int d = 0; d < HD / 16; ++d) {

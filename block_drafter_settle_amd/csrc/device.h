@@ -25,12 +25,24 @@ __device__ __forceinline__ size_t a_idx(int m, int k) {
   return ((size_t)(k >> 5) * 64 + ((k >> 3) & 3) * 16 + (m & 15)) * 8 + (k & 7);
 }
 
+// v as two f16 halves, hi = f16(v) and lo = f16(v − hi). The empty asm
+// pins v as one rounded f32 first: left free, the compiler may contract the
+// product that makes v into each half differently (an f16-result fma for
+// one, the rounded f32 for the other), and then hi + lo misses v by an
+// ulp of hi.
+__device__ __forceinline__ void split_f16(float v, f16& hi, f16& lo) {
+  asm volatile("" : "+v"(v));
+  hi = (f16)v;
+  lo = (f16)(v - (float)hi);
+}
+
 // Stores v at A-layout index idx: plane 0 its f16 rounding and, when ps (the
 // plane stride in halves) is nonzero, plane 1 the f16 rounding of what is left.
 __device__ __forceinline__ void put_a(f16* xa, long ps, size_t idx, float v) {
-  const f16 hi = (f16)v;
+  f16 hi, lo;
+  split_f16(v, hi, lo);
   xa[idx] = hi;
-  if (ps) xa[ps + idx] = (f16)(v - (float)hi);
+  if (ps) xa[ps + idx] = lo;
 }
 
 __device__ __forceinline__ long map_tile(const TileMap& mp, int t) {

@@ -368,8 +368,10 @@ __global__ __launch_bounds__(kThreads) void k_to_a(const float* __restrict__ x, 
   h8 v, r;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    v[e] = (f16)f[e];
-    r[e] = (f16)(f[e] - (float)v[e]);
+    f16 h, l;
+    split_f16(f[e], h, l);
+    v[e] = h;
+    r[e] = l;
   }
   reinterpret_cast<h8*>(xa + (size_t)mb * 16 * K)[t] = v;
   if (ps) reinterpret_cast<h8*>(xa + ps + (size_t)mb * 16 * K)[t] = r;
@@ -1042,8 +1044,10 @@ __global__ void k_i4_planes(const uint32_t* __restrict__ codes, const uint16_t* 
   for (int e = 0; e < 8; ++e) {
     const int pos = (e & 1) ? 16 + 2 * (e - 1) : 2 * e;
     const float v = (float)((int)((word >> pos) & 15u) - 8) * sc;
-    hi[e] = (f16)v;
-    lo[e] = (f16)(v - (float)hi[e]);
+    f16 h, l;
+    split_f16(v, h, l);
+    hi[e] = h;
+    lo[e] = l;
   }
   // F16T of the 2K-column matrix: tile t, step s, lane n + 16·j
   const int KS2 = (2 * K) >> 5, lane = n + 16 * j;
