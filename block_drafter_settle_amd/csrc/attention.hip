@@ -33,8 +33,10 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
                                                    float* __restrict__ pacc,
                                                    float2* __restrict__ pml) {
   constexpr int KST = HD + 8;   // LDS row stride of K (halfs)
-  constexpr int VST = 32 + 8;   // LDS row stride of V^T (halfs)
-  constexpr int EPT = HD / 8;   // staged elements per thread per 32 keys
+  constexpr int VST = 32 + 4;   // LDS row stride of V^T (halfs): 18 dwords, so 16 rows' 64-bit
+                                // reads fall on distinct banks
+  constexpr int DPT = HD / 16;  // dims a thread stages, for each of its two keys
+  constexpr int EPT = 2 * DPT;  // staged elements per thread per 32 keys, each of K and V
   __shared__ f16 Ks[2][32 * KST];
   __shared__ f16 Vt[2][HD * VST];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -72,39 +74,54 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
 #pragma unroll
   for (int d = 0; d < HD / 16; ++d) acc[d] = (f4){0.f, 0.f, 0.f, 0.f};
 
-  // staging: thread t copies key t%32, dims (t/32)·EPT .. +EPT; two
-  // register sets hold the next two 32-key steps while one is computed
-  const int skey = threadIdx.x & 31, sd0 = (threadIdx.x >> 5) * EPT;
+  // staging: thread t takes keys 2·(t%16) and 2·(t%16)+1, dims (t/16)·DPT ..
+  // +DPT of each, so that V^T takes a key pair a 32-bit store and K a key's
+  // dims in one store; two register sets hold the next two 32-key steps
+  // while one is computed
+  const int kp = threadIdx.x & 15, d0 = (threadIdx.x >> 4) * DPT;
   auto fetch = [&](int k0, float4 (&kreg)[EPT / 4], float4 (&vreg)[EPT / 4]) {
-    const bool ok = k0 + skey < count;
-    const float4* kp = reinterpret_cast<const float4*>(kbase + (size_t)(k0 + skey) * kd + sd0);
-    const float4* vp = reinterpret_cast<const float4*>(vbase + (size_t)(k0 + skey) * kd + sd0);
 #pragma unroll
-    for (int e = 0; e < EPT / 4; ++e) {
-      kreg[e] = ok ? kp[e] : make_float4(0.f, 0.f, 0.f, 0.f);
-      vreg[e] = ok ? vp[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int h = 0; h < 2; ++h) {
+      const int key = k0 + 2 * kp + h;
+      const bool ok = key < count;
+      const float4* kpn = reinterpret_cast<const float4*>(kbase + (size_t)key * kd + d0);
+      const float4* vpn = reinterpret_cast<const float4*>(vbase + (size_t)key * kd + d0);
+#pragma unroll
+      for (int e = 0; e < DPT / 4; ++e) {
+        kreg[h * (DPT / 4) + e] = ok ? kpn[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+        vreg[h * (DPT / 4) + e] = ok ? vpn[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
   };
   auto stage = [&](const float4 (&kreg)[EPT / 4], const float4 (&vreg)[EPT / 4]) {
     __syncthreads();
+    f16 vh[2][DPT], vl[2][DPT];
 #pragma unroll
-    for (int e = 0; e < EPT / 4; ++e) {
-      const float kf[4] = {kreg[e].x, kreg[e].y, kreg[e].z, kreg[e].w};
-      const float vf[4] = {vreg[e].x, vreg[e].y, vreg[e].z, vreg[e].w};
-      h4 khi, klo;
+    for (int h = 0; h < 2; ++h) {
+      f16 kh[DPT], kl[DPT];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f16 kh, kl;
-        split_f16(kf[q], kh, kl);
-        khi[q] = kh;
-        klo[q] = kl;
-        f16 vh, vl;
-        split_f16(vf[q], vh, vl);
-        Vt[0][(sd0 + 4 * e + q) * VST + skey] = vh;
-        Vt[1][(sd0 + 4 * e + q) * VST + skey] = vl;
+      for (int e = 0; e < DPT / 4; ++e) {
+        const float4 kk = kreg[h * (DPT / 4) + e], vv = vreg[h * (DPT / 4) + e];
+        const float kf[4] = {kk.x, kk.y, kk.z, kk.w};
+        const float vf[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          split_f16(kf[q], kh[4 * e + q], kl[4 * e + q]);
+          split_f16(vf[q], vh[h][4 * e + q], vl[h][4 * e + q]);
+        }
       }
-      *reinterpret_cast<h4*>(&Ks[0][skey * KST + sd0 + 4 * e]) = khi;
-      *reinterpret_cast<h4*>(&Ks[1][skey * KST + sd0 + 4 * e]) = klo;
+      f16* k0p = &Ks[0][(2 * kp + h) * KST + d0];
+      f16* k1p = &Ks[1][(2 * kp + h) * KST + d0];
+#pragma unroll
+      for (int e = 0; e < DPT / 4; ++e) {
+        *reinterpret_cast<h4*>(k0p + 4 * e) = (h4){kh[4 * e], kh[4 * e + 1], kh[4 * e + 2], kh[4 * e + 3]};
+        *reinterpret_cast<h4*>(k1p + 4 * e) = (h4){kl[4 * e], kl[4 * e + 1], kl[4 * e + 2], kl[4 * e + 3]};
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) {
+      *reinterpret_cast<h2*>(&Vt[0][(d0 + e) * VST + 2 * kp]) = (h2){vh[0][e], vh[1][e]};
+      *reinterpret_cast<h2*>(&Vt[1][(d0 + e) * VST + 2 * kp]) = (h2){vl[0][e], vl[1][e]};
     }
     __syncthreads();
   };
