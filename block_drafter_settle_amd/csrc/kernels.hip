@@ -873,19 +873,20 @@ __device__ void select_list(const float* rv, const int* ri, int count, int want,
 }
 
 // The first `want` entries in `top_k` order of a row's list of n ≤ kRankMax
-// entries, by rank: an entry's rank is the number of entries better than
-// it (a strict order, indices being distinct), so the entry of rank q < want
-// lands at out[q]. The list is staged in LDS (sv, si); all threads of the
-// block take part.
-static constexpr int kRankMax = 1024;
+// entries, by rank, within one wave: an entry's rank is the number of
+// entries better than it (a strict order, indices being distinct), so the
+// entry of rank q < want lands at out[q]. The list is staged in the wave's
+// LDS (sv, si).
+static constexpr int kRankMax = 512;
 __device__ void rank_select(const float* rv, const int* ri, int n, int want, float* sv, int* si,
                             float* out_v, int* out_i) {
-  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+  const int lane = threadIdx.x & 63;
+  for (int e = lane; e < n; e += 64) {
     sv[e] = rv[e];
     si[e] = ri[e];
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+  wave_lds_sync();
+  for (int e = lane; e < n; e += 64) {
     const float v = sv[e];
     const int i = si[e];
     int rank = 0;
@@ -895,15 +896,16 @@ __device__ void rank_select(const float* rv, const int* ri, int n, int want, flo
       out_i[rank] = i;
     }
   }
-  __syncthreads();
+  wave_lds_sync();
 }
 
 // Row j's top candidates and row j−1's (j ≥ 1, to know the predecessor tp);
 // then the scores of row j's candidates under that predecessor (or the
 // anchor for j = 0, or forced[j]), `select_with`:
 // unary + Σ_q (P[prev][q]·hp[j][q])·C[tok][q]. Block (j, tp); block (j, 0)
-// also writes cand and unary of row j. Lists longer than kRankMax take
-// wave_select passes instead.
+// also writes cand and unary of row j. Wave 0 selects row j and wave 1 row
+// j−1 at the same time; lists longer than kRankMax take wave_select passes
+// instead.
 __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
                                                const int* __restrict__ li,
                                                const int* __restrict__ counters, int cap, int top,
@@ -915,26 +917,23 @@ __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
                                                float* __restrict__ tab) {
   __shared__ float uv[2][32 + 64];
   __shared__ int uc[2][32 + 64];
-  __shared__ float sv[kRankMax];
-  __shared__ int si[kRankMax];
+  __shared__ float sv[2][kRankMax];
+  __shared__ int si[2][kRankMax];
   const int j = blockIdx.x, tp = blockIdx.y, tpn = gridDim.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (j == 0 && tp > 0) return;
-  const int n0 = min(counters[j], cap);
   const bool prev_row = j > 0 && !forced;
-  const int n1 = prev_row ? min(counters[j - 1], cap) : 0;
-  if (n0 <= kRankMax && n1 <= kRankMax) {
-    rank_select(lv + (size_t)j * cap, li + (size_t)j * cap, n0, top, sv, si, uv[0], uc[0]);
-    if (prev_row)
-      rank_select(lv + (size_t)(j - 1) * cap, li + (size_t)(j - 1) * cap, n1, tp + 1, sv, si,
-                  uv[1], uc[1]);
-  } else {
-    const int row = j - wave;  // wave 0: row j, wave 1: row j−1
-    if (wave == 0 || prev_row)
-      select_list(lv + (size_t)row * cap, li + (size_t)row * cap, wave == 0 ? n0 : n1,
-                  wave == 0 ? top : tp + 1, uv[wave], uc[wave]);
-    __syncthreads();
+  const int row = j - wave;  // wave 0: row j, wave 1: row j−1
+  if (wave == 0 || prev_row) {
+    const int n = min(counters[row], cap);
+    const int want = wave == 0 ? top : tp + 1;
+    if (n <= kRankMax)
+      rank_select(lv + (size_t)row * cap, li + (size_t)row * cap, n, want, sv[wave], si[wave],
+                  uv[wave], uc[wave]);
+    else
+      select_list(lv + (size_t)row * cap, li + (size_t)row * cap, n, want, uv[wave], uc[wave]);
   }
+  __syncthreads();
   if (wave == 0 && tp == 0 && lane < top) {
     cand[(size_t)j * top + lane] = uc[0][lane];
     unary[(size_t)j * top + lane] = uv[0][lane];
@@ -976,17 +975,28 @@ __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
 }
 
 // The chain: row by row, the first candidate with the largest score under
-// the predecessor chosen before it. One wave; lane t holds candidate t of
-// the current row (top ≤ 64), and an arg-max over the lanes (the smaller
-// candidate index among equal scores) picks the row's choice.
-__global__ __launch_bounds__(64) void k_chain(const float* __restrict__ tab,
-                                              const int* __restrict__ cand, int k, int top,
-                                              int tpn, float* __restrict__ score,
-                                              int* __restrict__ chosen) {
+// the predecessor chosen before it. The score table is staged in LDS by the
+// whole block (its 16-byte loads issued together), then wave 0 walks the
+// rows: lane t holds candidate t of the current row (top ≤ 64), and an
+// arg-max over the lanes (the smaller candidate index among equal scores)
+// picks the row's choice.
+__global__ __launch_bounds__(kThreads) void k_chain(const float* __restrict__ tab,
+                                                    const int* __restrict__ cand, int k, int top,
+                                                    int tpn, float* __restrict__ score,
+                                                    int* __restrict__ chosen) {
+  extern __shared__ float4 lt4[];
+  const float* lt = reinterpret_cast<const float*>(lt4);
+  const int total = top + (k - 1) * tpn * top;
+  const int n4 = (total + 3) / 4;
+  const float4* t4 = reinterpret_cast<const float4*>(tab);
+#pragma unroll 4
+  for (int e = threadIdx.x; e < n4; e += kThreads) lt4[e] = t4[e];
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
   int tp = 0;
   for (int j = 0; j < k; ++j) {
-    const float* row = tab + (j == 0 ? 0 : top + ((size_t)(j - 1) * tpn + tp) * top);
+    const float* row = lt + (j == 0 ? 0 : top + ((size_t)(j - 1) * tpn + tp) * top);
     const float v = lane < top ? row[lane] : -INFINITY;
     if (lane < top) score[(size_t)j * top + lane] = v;
     // first strictly largest: compare (v, lane) with the smaller lane winning ties;
@@ -1234,7 +1244,8 @@ void select_all(hipStream_t st, const float* logits, bool have_gmax, int k, int 
                                         reinterpret_cast<const f16*>(pbook),
                                         reinterpret_cast<const f16*>(cbook), vocab, anchor,
                                         forced, cand, unary, sc.tab);
-  k_chain<<<1, 64, 0, st>>>(sc.tab, cand, k, top, tpn, score, chosen);
+  const size_t lds = sizeof(float) * ((size_t)(top + (k - 1) * tpn * top + 3) / 4 * 4);
+  k_chain<<<1, kThreads, lds, st>>>(sc.tab, cand, k, top, tpn, score, chosen);
 }
 
 void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,
