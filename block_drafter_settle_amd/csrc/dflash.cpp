@@ -773,8 +773,12 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     dfl::conv0(st, d->x, d->part, spk.S, ssd, mbase, B, hs, d->gs, d->kn, d->xca, psh,
                d->dsum_m);
     tm_mark(d, DFLASH_ST_CONV);
-    dfl::gemm_glu(st, d->xca, psh, hs, d->gu.codes + i4l_gu * 1024 * l,
-                  d->gu.scales + i4l_gu * 64 * l, d->ffn / 16, d->ma, psm);
+    if (dfl::glu_stream_fits(hs))
+      dfl::gemm_glu_stream(st, d->xca, psh, hs, d->gu.codes + i4l_gu * 1024 * l,
+                           d->gu.scales + i4l_gu * 64 * l, d->ffn / 16, d->ma, psm);
+    else
+      dfl::gemm_glu(st, d->xca, psh, hs, d->gu.codes + i4l_gu * 1024 * l,
+                    d->gu.scales + i4l_gu * 64 * l, d->ffn / 16, d->ma, psm);
     tm_mark(d, DFLASH_ST_GLU);
     dfl::gemm_i4_block(st, d->ma, psm, d->ffn, d->down.codes + i4l_dn * 1024 * l,
                        d->down.scales + i4l_dn * 64 * l,

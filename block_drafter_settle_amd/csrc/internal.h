@@ -72,6 +72,13 @@ void gemm_f16_block(hipStream_t st, const uint16_t* xa, long ps, int K, const ui
 // matrix; writes silu(g)·u in A-layout planes (ma, mps).
 void gemm_glu(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
               const uint16_t* scales, int ftiles, uint16_t* ma, long mps);
+
+// gate/up + SwiGLU streamed through one workgroup per tile-pair range
+// (stream.hip), for K ≤ 5120 (40 spans of 128 over eight waves); same
+// operands and output as gemm_glu.
+bool glu_stream_fits(int K);
+void gemm_glu_stream(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
+                     const uint16_t* scales, int ftiles, uint16_t* ma, long mps);
 // Scratch of the selection: gmax [k][ceil(width/256)] column-group maxima,
 // thr [k], counters [16], the candidate lists lv/li [k][topk_cap], and the
 // score table tab [top·(1 + 15·top)].
