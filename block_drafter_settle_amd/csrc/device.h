@@ -45,6 +45,26 @@ __device__ __forceinline__ void put_a(f16* xa, long ps, size_t idx, float v) {
   if (ps) xa[ps + idx] = lo;
 }
 
+// A load that marks its lines non-temporal: weights are read once per pass,
+// and streaming them with this hint keeps them from displacing what is
+// reused (activations, partial sums). Measured here it also raises the
+// sustained read rate of a whole-chip stream. T must be a scalar or an
+// ext_vector_type.
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream(const uint2* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+
 __device__ __forceinline__ long map_tile(const TileMap& mp, int t) {
   return (long)(t / mp.seg) * mp.seg_stride + mp.seg_off + t % mp.seg;
 }

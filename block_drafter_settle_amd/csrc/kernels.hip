@@ -250,20 +250,27 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa
   }
 }
 
+// tiles per wave of the head: eight 16-column tiles share each A fragment
+static constexpr int kHeadR = 8;
+
 // The head over rows 1..k (logits [k][width]) and, in blocks past
 // head_groups, the selector projection of all 16 rows (hp [16][rank]).
 // Head blocks also record, per draft row, the largest logit of each 256
-// columns (gmax [k][head_groups]) for the selection's threshold, and block
-// 0 clears the selection's candidate counters.
+// columns (gmax [k][ceil(width/256)]) for the selection's threshold, and
+// block 0 clears the selection's candidate counters.
 template <int PL>
 __global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, long ps, int K,
                                                    const f16* __restrict__ head, int wtiles,
                                                    int width, int k, float* __restrict__ logits,
                                                    const f16* __restrict__ sel, int stiles,
                                                    int rank, float* __restrict__ hp,
-                                                   int head_groups, float* __restrict__ gmax,
+                                                   int head_groups, int ngroups,
+                                                   float* __restrict__ gmax,
                                                    int* __restrict__ counters) {
-  constexpr int R = 4;
+  static_assert(kHeadR == 4 || kHeadR == 8, "256-column groups are whole waves");
+  constexpr int kWpg = 16 / kHeadR;  // waves per 256 columns
+  constexpr int kGpb = 4 / kWpg;     // 256-column groups per block
+  constexpr int R = kHeadR;
   __shared__ float wm[4][16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool is_sel = (int)blockIdx.x >= head_groups;
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, l
         a[u] = xp[(size_t)(s + u) * 64];
         if (PL == 2) a2[u] = xq[(size_t)(s + u) * 64];
 #pragma unroll
-        for (int r = 0; r < R; ++r) b[u][r] = wp[r][(size_t)(s + u) * 64];
+        for (int r = 0; r < R; ++r) b[u][r] = ld_stream(&wp[r][(size_t)(s + u) * 64]);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, l
       if (PL == 2) a2 = xq[(size_t)s * 64];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const h8 b = wp[r][(size_t)s * 64];
+        const h8 b = ld_stream(&wp[r][(size_t)s * 64]);
         acc[r] = mfma16(a, b, acc[r]);
         if (PL == 2) acc[r] = mfma16(a2, b, acc[r]);
       }
@@ -338,11 +345,14 @@ __global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, l
 #pragma unroll
     for (int v = 0; v < 4; ++v) wm[wave][4 * j + v] = mx[v];
   __syncthreads();
-  if (threadIdx.x < 16) {
-    const int m = threadIdx.x;
-    const float g = fmaxf(fmaxf(wm[0][m], wm[1][m]), fmaxf(wm[2][m], wm[3][m]));
-    if (m >= 1 && m <= k) gmax[(size_t)(m - 1) * head_groups + blockIdx.x] = g;
-    if (blockIdx.x == 0) counters[m] = 0;
+  if (threadIdx.x < 16 * kGpb) {
+    const int m = threadIdx.x & 15, gh = threadIdx.x >> 4;
+    float g = wm[gh * kWpg][m];
+#pragma unroll
+    for (int w = 1; w < kWpg; ++w) g = fmaxf(g, wm[gh * kWpg + w][m]);
+    const int gi = blockIdx.x * kGpb + gh;
+    if (m >= 1 && m <= k && gi < ngroups) gmax[(size_t)(m - 1) * ngroups + gi] = g;
+    if (blockIdx.x == 0 && gh == 0) counters[m] = 0;
   }
 }
 
@@ -1151,16 +1161,18 @@ void gemm_i4(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblo
 void head_sel(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t* head, int width,
               int k, float* logits, const uint16_t* sel, int rank, float* hp, SelectScratch sc) {
   const int wtiles = cdiv(width, 16), stiles = cdiv(rank, 16);
-  const int hg = cdiv(wtiles, 16), sg = cdiv(stiles, 16);
+  const int hg = cdiv(wtiles, 4 * kHeadR), sg = cdiv(stiles, 4 * kHeadR);
   const f16* x = reinterpret_cast<const f16*>(xa);
   const f16* hw = reinterpret_cast<const f16*>(head);
   const f16* sw = reinterpret_cast<const f16*>(sel);
   if (ps)
     k_head<2><<<hg + sg, kThreads, 0, st>>>(x, ps, K, hw, wtiles, width, k, logits, sw, stiles,
-                                            rank, hp, hg, sc.gmax, sc.counters);
+                                            rank, hp, hg, cdiv(width, 256), sc.gmax,
+                                            sc.counters);
   else
     k_head<1><<<hg + sg, kThreads, 0, st>>>(x, 0, K, hw, wtiles, width, k, logits, sw, stiles,
-                                            rank, hp, hg, sc.gmax, sc.counters);
+                                            rank, hp, hg, cdiv(width, 256), sc.gmax,
+                                            sc.counters);
 }
 
 void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa, long ps) {

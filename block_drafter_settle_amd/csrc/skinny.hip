@@ -57,8 +57,8 @@ __global__ __launch_bounds__(64 * NW) void k_i4_block(const f16* __restrict__ xa
 #pragma unroll
     for (int u = 0; u < KS; ++u) {
       const int p = p0 + min(u, np - 1);
-      c[u][r] = cp[(size_t)p * 64];
-      s[u][r] = scp[(size_t)p * 16];
+      c[u][r] = ld_stream(&cp[(size_t)p * 64]);
+      s[u][r] = ld_stream(&scp[(size_t)p * 16]);
     }
   }
 #pragma unroll
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64 * NW) void k_f16_block(const f16* __restrict__ x
     const long st = map_tile(mp, min(t0 + r, mp.ntiles - 1));
     const h8* wp = reinterpret_cast<const h8*>(w) + (size_t)st * KST * 64 + lane;
 #pragma unroll
-    for (int u = 0; u < KS; ++u) b[u][r] = wp[(size_t)(s0 + min(u, ns - 1)) * 64];
+    for (int u = 0; u < KS; ++u) b[u][r] = ld_stream(&wp[(size_t)(s0 + min(u, ns - 1)) * 64]);
   }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -204,10 +204,10 @@ __global__ __launch_bounds__(64 * NW) void k_glu_block(const f16* __restrict__ x
     h8 a0[4], a1[4], b0[4], b1[4];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      c0[r] = cp[r][(size_t)p * 64];
-      c1[r] = cp[r][(size_t)(p + 1) * 64];
-      s0[r] = scp[r][(size_t)p * 16];
-      s1[r] = scp[r][(size_t)(p + 1) * 16];
+      c0[r] = ld_stream(&cp[r][(size_t)p * 64]);
+      c1[r] = ld_stream(&cp[r][(size_t)(p + 1) * 64]);
+      s0[r] = ld_stream(&scp[r][(size_t)p * 16]);
+      s1[r] = ld_stream(&scp[r][(size_t)(p + 1) * 16]);
     }
     load_span<2>(xp, xq, p, a0, b0);
     load_span<2>(xp, xq, p + 1, a1, b1);
@@ -220,8 +220,8 @@ __global__ __launch_bounds__(64 * NW) void k_glu_block(const f16* __restrict__ x
     h8 a0[4], b0[4];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      c0[r] = cp[r][(size_t)p * 64];
-      s0[r] = scp[r][(size_t)p * 16];
+      c0[r] = ld_stream(&cp[r][(size_t)p * 64]);
+      s0[r] = ld_stream(&scp[r][(size_t)p * 16]);
     }
     load_span<2>(xp, xq, p, a0, b0);
     i4_span<R, 2>(c0, s0, a0, b0, acc);

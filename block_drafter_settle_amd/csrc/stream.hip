@@ -73,8 +73,8 @@ __global__ __launch_bounds__(64 * kSW) void k_glu_stream(const f16* __restrict__
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const long tp = (r == 0 ? gg : (long)ftiles + gg) * KT + p;
-        c[u][r] = cp[tp * 64];
-        s[u][r] = sp[tp * 16];
+        c[u][r] = ld_stream(&cp[tp * 64]);
+        s[u][r] = ld_stream(&sp[tp * 16]);
       }
     };
     h8 a0[KSW][4], a1[KSW][4];
