@@ -250,14 +250,15 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa
   }
 }
 
-// tiles per wave of the head: eight 16-column tiles share each A fragment
-static constexpr int kHeadR = 8;
-
 // The head over rows 1..k (logits [k][width]) and, in blocks past
 // head_groups, the selector projection of all 16 rows (hp [16][rank]).
 // Head blocks also record, per draft row, the largest logit of each 256
 // columns (gmax [k][ceil(width/256)]) for the selection's threshold, and
-// block 0 clears the selection's candidate counters.
+// block 0 clears the selection's candidate counters. Each wave covers kHeadR
+// 16-column tiles, which share every A fragment it loads; the weights are
+// read with non-temporal loads.
+static constexpr int kHeadR = 8;
+
 template <int PL>
 __global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, long ps, int K,
                                                    const f16* __restrict__ head, int wtiles,
