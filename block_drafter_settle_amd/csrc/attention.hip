@@ -213,28 +213,34 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
 // Softmax-merge of the chunks of one (q head, row) → y in A-layout f16:
 // y = Σ_c acc_c·2^{m_c − M} / Σ_c l_c·2^{m_c − M}, M the largest chunk max
 // (the chunk states are kept in base 2).
-// One thread per chunk forms the weights, one thread per dimension sums.
+// The threads form the chunk weights (chunks strided over the block), then
+// one thread per dimension sums.
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pacc,
                                                     const float2* __restrict__ pml, int nh,
                                                     int kv, int hd, int nchunks,
                                                     f16* __restrict__ ya, long ps) {
-  __shared__ float fw[256], red[4], redl[4];
+  __shared__ float fw[kAttnMaxChunks + 1], red[4], redl[4];
   const int hq = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
   const int rep = nh / kv, g = hq / rep, qi = hq % rep, nc = nchunks + 1;
   const size_t slot0 = (size_t)g * nc * rep + qi;  // chunk c is slot slot0 + c·rep
-  float2 ml = make_float2(-INFINITY, 0.f);
-  if (t < nc) ml = pml[(slot0 + (size_t)t * rep) * 16 + r];
-  float m = ml.x;
+  auto ml_of = [&](int c) { return pml[(slot0 + (size_t)c * rep) * 16 + r]; };
+  float m = -INFINITY;
+  for (int c = t; c < nc; c += blockDim.x) m = fmaxf(m, ml_of(c).x);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   if (lane == 0) red[wave] = m;
   __syncthreads();
   float M = red[0];
   for (int w = 1; w < nw; ++w) M = fmaxf(M, red[w]);
-  const float f = (t < nc && ml.x != -INFINITY) ? exp2f(ml.x - M) : 0.f;
-  if (t < nc) fw[t] = f;
-  const float l = wave_sum(ml.y * f);
+  float l = 0.f;
+  for (int c = t; c < nc; c += blockDim.x) {
+    const float2 ml = ml_of(c);
+    const float f = ml.x != -INFINITY ? exp2f(ml.x - M) : 0.f;
+    fw[c] = f;
+    l += ml.y * f;
+  }
+  l = wave_sum(l);
   if (lane == 0) redl[wave] = l;
   __syncthreads();
   float L = 0.f;

@@ -158,6 +158,19 @@ __device__ __forceinline__ void load_span(const h8* xp, const h8* xq, int p, h8*
   }
 }
 
+// Workgroup barrier for LDS publication only: waits for this wave's LDS
+// traffic (lgkmcnt 0), then meets. __syncthreads would also wait for every
+// global load in flight (vmcnt 0), draining prefetched weights or K/V.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+  const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
 template <int N_OUT>
 __device__ __forceinline__ void wait_vm() {
   // s_waitcnt vmcnt(N_OUT) with expcnt/lgkmcnt left at their maxima (gfx9 encoding)

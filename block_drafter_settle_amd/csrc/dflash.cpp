@@ -25,7 +25,6 @@ namespace {
 
 constexpr int kSettleRows = 256;     // rows one settle pass takes
 constexpr int kTargetBlocks = 512;   // workgroups a GEMM launch aims for (256 CUs)
-constexpr int kMaxChunks = 64;       // context chunks per kv head in the attention
 // Row tiles per wave of each product (a workgroup covers 4·R tiles of 16).
 constexpr int kRFc = 2;      // settle's fc, f16
 constexpr int kKsQkv = 2;    // q/k/v, int4: spans (128 columns) per split
@@ -396,7 +395,9 @@ int attn_chunk(long n, int* nchunks) {
     *nchunks = 0;
     return 32;
   }
-  long c = std::max(64L, (n + kMaxChunks - 1) / kMaxChunks);
+  // at least 128 keys a chunk: shorter chunks cost more in per-chunk work and
+  // merge traffic than they gain in parallelism
+  long c = std::max(128L, (n + dfl::kAttnMaxChunks - 1) / dfl::kAttnMaxChunks);
   c = (c + 31) / 32 * 32;
   *nchunks = (int)((n + c - 1) / c);
   return (int)c;
@@ -533,7 +534,7 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   if (!rc) rc = dev_alloc(d, &d->sv, store, "context values");
   // ---- scratch
   const int rep = d->nh / d->kv;
-  const size_t slots = (size_t)d->kv * (kMaxChunks + 1) * rep;
+  const size_t slots = (size_t)d->kv * (dfl::kAttnMaxChunks + 1) * rep;
   d->part_floats = partial_need(d);
   const size_t sel_cap = (size_t)dfl::topk_cap(d->V, d->top);
   if (!rc) rc = dev_alloc(d, &d->h, 16 * hs, "scratch");

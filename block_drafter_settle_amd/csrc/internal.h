@@ -123,6 +123,9 @@ void settle_kv(hipStream_t st, const float* part, int splits, long split_stride,
                int layers, int kv, int hd, const float* k_norm, const float* inv_freq,
                const int* rot, long pos0, float eps, float* store_k, float* store_v, long cap,
                long row0);
+// Context chunks per kv head of one attention call; the merge holds one
+// weight per chunk (and one for the block's own rows) in LDS.
+constexpr int kAttnMaxChunks = 64;
 void attention(hipStream_t st, const uint16_t* qa, long qps, const float* sk, const float* sv,
                const float* kb, const float* vb, int B, int nh, int kv, int hd, int n,
                long lo_pos, long a, int window, int chunk, int nchunks, float scale,

@@ -125,12 +125,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_big_f16(const f16* __restr
     else
       fsrc[i] = wg + (size_t)map_tile(mp, min(t0 + f - 16, mp.ntiles - 1)) * KS * 64 + lane;
   }
+  // the weight fragments (read once) are copied non-temporal, the row
+  // fragments (read by every column block) cached; a wave copies only one kind
+  static_assert(16 % kBigPerWave == 0, "a wave copies row or weight fragments");
+  const bool w_wave = wave * kBigPerWave >= 16;
   auto issue = [&](int s) {  // async copies of step s into its stage
     h8* dst = stage + (size_t)((s - s0) % kBigStages) * kBigFrags * 64;
+    if (w_wave) {
 #pragma unroll
-    for (int i = 0; i < kBigPerWave; ++i)
-      __builtin_amdgcn_global_load_lds(fsrc[i] + (size_t)s * 64,
-                                       dst + (wave * kBigPerWave + i) * 64, 16, 0, 0);
+      for (int i = 0; i < kBigPerWave; ++i)
+        __builtin_amdgcn_global_load_lds(fsrc[i] + (size_t)s * 64,
+                                         dst + (wave * kBigPerWave + i) * 64, 16, 0, 2);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kBigPerWave; ++i)
+        __builtin_amdgcn_global_load_lds(fsrc[i] + (size_t)s * 64,
+                                         dst + (wave * kBigPerWave + i) * 64, 16, 0, 0);
+    }
   };
   // wait until this wave's copies of step s are in: at most the copies of
   // the steps issued after it may remain

@@ -69,8 +69,7 @@ __global__ __launch_bounds__(64 * NW) void k_i4_block(const f16* __restrict__ xa
   }
   // LDS writes done, then a bare s_barrier: a __syncthreads here would also
   // wait for the weight loads still in flight
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-  asm volatile("s_barrier" ::: "memory");
+  lds_barrier();
   f4 acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = (f4){0.f, 0.f, 0.f, 0.f};
@@ -137,8 +136,7 @@ __global__ __launch_bounds__(64 * NW) void k_f16_block(const f16* __restrict__ x
     const int pl = e / (KS * 64), st = (e / 64) % KS;
     if (e < kFrags && st < ns) al[pl][st][e & 63] = areg[i];
   }
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-  asm volatile("s_barrier" ::: "memory");
+  lds_barrier();
   f4 acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = (f4){0.f, 0.f, 0.f, 0.f};

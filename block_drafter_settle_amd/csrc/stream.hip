@@ -34,13 +34,6 @@ static constexpr int kSW = 8;     // waves per workgroup
 static constexpr int kGmax = 8;   // tile pairs a workgroup holds in LDS
 static constexpr int kWgs = 256;  // one eight-wave workgroup per compute unit
 
-// LDS publish: wait for this wave's LDS traffic only, then meet. A
-// __syncthreads would also drain the weight loads in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-  asm volatile("s_barrier" ::: "memory");
-}
-
 template <int KSW>
 __global__ __launch_bounds__(64 * kSW) void k_glu_stream(const f16* __restrict__ xa, long ps,
                                                          int K, const uint4* __restrict__ codes,

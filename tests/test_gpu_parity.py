@@ -210,6 +210,9 @@ BLOCK_CASES = [
     (dict(windows=[0, 0], no_rope=[], block=16), (0, 200), 0, 15, 1000),
     (dict(windows=[0, 0], no_rope=[], kv_heads=4), (5, 70), 3, 7, 999),
     (dict(windows=[0, 0], no_rope=[], heads=8, kv_heads=1, head_dim=128), (0, 300), 0, 7, 1000),
+    # 64 context chunks + the block's own rows: more chunk states than merge
+    # threads at head_dim 64
+    (dict(windows=[0, 0], no_rope=[]), (0, 8190), 0, 7, 1000),
 ]
 
 
