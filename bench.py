@@ -177,6 +177,13 @@ def main():
     # settle: the fc GEMM's flops per 256-row launch
     fc_us = st_settle["settle_fc"][0] / st_settle["settle_fc"][1]
     fc_flops = 2.0 * 256 * tw * hs
+    # bytes the fc must move at least: its weight once, the 256 f16 tap rows,
+    # the 256 f32 output rows. At 256 rows the weight stream (hbm) takes longer
+    # at peak than the products (mfma): 244 flop/B is under the chip's
+    # 2.5 PFLOP/s ÷ 8 TB/s = 312 flop/B.
+    fc_bytes = tw * hs * 2 + 256 * tw * 2 + 256 * hs * 4
+    fc_bound = "hbm" if fc_bytes / (HBM_PEAK_GBS * 1e9) >= fc_flops / (F16_MFMA_PEAK_TFS * 1e12) \
+        else "mfma"
     settle_flops = 2.0 * 256 * (tw * hs + L * 2 * kd * hs)
     settle_call_us = sum(v[0] for n, v in st_settle.items() if n.startswith("settle")) / n_settles
 
@@ -231,13 +238,18 @@ def main():
                                     F16_MFMA_PEAK_TFS, 4),
             "roofline": {
                 "kernel": "k_gemm_big_f16 (fc, 256 rows)",
-                "bound": "mfma",
-                "achieved": round(fc_flops / (fc_us * 1e-6) / 1e12, 2),
-                "peak": F16_MFMA_PEAK_TFS,
-                "unit": "TFLOP/s",
-                "frac": round(fc_flops / (fc_us * 1e-6) / 1e12 / F16_MFMA_PEAK_TFS, 4),
+                "bound": fc_bound,
+                "achieved": round(fc_bytes / (fc_us * 1e-6) / 1e9, 1) if fc_bound == "hbm"
+                else round(fc_flops / (fc_us * 1e-6) / 1e12, 2),
+                "peak": HBM_PEAK_GBS if fc_bound == "hbm" else F16_MFMA_PEAK_TFS,
+                "unit": "GB/s" if fc_bound == "hbm" else "TFLOP/s",
+                "frac": round((fc_bytes / (fc_us * 1e-6) / 1e9 / HBM_PEAK_GBS) if fc_bound == "hbm"
+                              else (fc_flops / (fc_us * 1e-6) / 1e12 / F16_MFMA_PEAK_TFS), 4),
                 "traffic": None,
                 "us_per_launch": round(fc_us, 2),
+                "bytes_per_launch": int(fc_bytes),
+                "flops_per_launch": fc_flops,
+                "tflops": round(fc_flops / (fc_us * 1e-6) / 1e12, 2),
             },
         },
         "stages_us": stages,

@@ -88,108 +88,103 @@ __global__ __launch_bounds__(kThreads) void k_gemm_f16(const f16* __restrict__ x
   }
 }
 
-// Many-row GEMM, f16 weights (the settle's fc at up to 256 rows): a block
-// holds all 16 row blocks (256 rows; rows past the input are never
-// written out) against kBigNT row tiles of the weight over its K split.
-// Every 32-column step's fragments (16 A + kBigNT weight, 1 KB each, in
-// their memory layout) are copied global → LDS by the waves' async loads
-// (global_load_lds_dwordx4: lane l's 16 bytes land at dst + 16·l),
-// kBigStages − 1 steps in flight. Wave w multiplies row
-// blocks 4w..4w+3 by all kBigNT tiles. Blocks are numbered split-fastest.
-static constexpr int kBigNT = 16, kBigStages = 4;
-static constexpr int kBigFrags = 16 + kBigNT;      // fragments a step
-static constexpr int kBigPerWave = kBigFrags / 4;  // async loads a wave issues a step
-static_assert(kBigFrags % 4 == 0, "fragments split evenly over the waves");
+// Many-row GEMM, f16 weights (the settle's fc and K/V at up to 256 rows): a
+// block holds all 16 row blocks (256 rows; rows past the input are never
+// written out) against kBigNT weight tiles over its K split. Every 32-column
+// step's fragments (16 row + kBigNT weight, 1 KB each, in their memory
+// layout) are copied global → LDS by the waves' async loads
+// (global_load_lds_dwordx4: lane l's 16 bytes land at dst + 16·l) into a
+// kBigStages ring, kBigStages − 1 steps in flight. The block has eight
+// waves, two on each SIMD, so one wave's products run while the other waits
+// at the step's barrier or on LDS: wave w multiplies row blocks 4(w%4)..+3
+// by weight tiles 8(w/4)..+7. Waves 0–3 copy the row fragments, waves 4–7
+// the weight fragments (non-temporal: read once). Blocks are numbered
+// split-fastest.
+static constexpr int kBigNT = 16, kBigStages = 3, kBigWaves = 8;
+static constexpr int kBigFrags = 16 + kBigNT;              // fragments a step
+static constexpr int kBigPerWave = kBigFrags / kBigWaves;  // async copies a wave issues a step
+static_assert(16 % kBigPerWave == 0, "a wave copies row or weight fragments only");
 
+__device__ __forceinline__ void copy16(const h8* src, h8* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+__device__ __forceinline__ void copy16_nt(const h8* src, h8* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 2);
+}
 
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_big_f16(const f16* __restrict__ xa, int K,
-                                                             int mblocks,
-                                                             const f16* __restrict__ w,
-                                                             TileMap mp, int N, int splits,
-                                                             int sps, float* __restrict__ out,
-                                                             long split_stride) {
+__global__ __launch_bounds__(64 * kBigWaves) void k_gemm_big_f16(const f16* __restrict__ xa, int K,
+                                                                int mblocks,
+                                                                const f16* __restrict__ w,
+                                                                TileMap mp, int N, int splits,
+                                                                int sps, float* __restrict__ out,
+                                                                long split_stride) {
+  constexpr int D = kBigStages - 1;
   extern __shared__ h8 stage[];  // [kBigStages][kBigFrags][64]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rw = wave & 3, cw = wave >> 2;
   const int KS = K >> 5;
   const int sp = blockIdx.x % splits;
-  const int s0 = sp * sps, s1 = min(KS, s0 + sps), nsteps = s1 - s0;
+  const int s0 = sp * sps, s1 = min(KS, s0 + sps);
   const int t0 = (blockIdx.x / splits) * kBigNT;
   const h8* xg = reinterpret_cast<const h8*>(xa);
   const h8* wg = reinterpret_cast<const h8*>(w);
+  const bool w_wave = wave * kBigPerWave >= 16;
   const h8* fsrc[kBigPerWave];  // this wave's fragments, at step 0
 #pragma unroll
   for (int i = 0; i < kBigPerWave; ++i) {
     const int f = wave * kBigPerWave + i;
-    if (f < 16)
-      fsrc[i] = xg + (size_t)f * 2 * K + lane;
-    else
-      fsrc[i] = wg + (size_t)map_tile(mp, min(t0 + f - 16, mp.ntiles - 1)) * KS * 64 + lane;
+    fsrc[i] = f < 16 ? xg + (size_t)f * 2 * K + lane
+                     : wg + (size_t)map_tile(mp, min(t0 + f - 16, mp.ntiles - 1)) * KS * 64 + lane;
   }
-  // the weight fragments (read once) are copied non-temporal, the row
-  // fragments (read by every column block) cached; a wave copies only one kind
-  static_assert(16 % kBigPerWave == 0, "a wave copies row or weight fragments");
-  const bool w_wave = wave * kBigPerWave >= 16;
-  auto issue = [&](int s) {  // async copies of step s into its stage
-    h8* dst = stage + (size_t)((s - s0) % kBigStages) * kBigFrags * 64;
+  // async copies of step s into its stage; past the split's end the last
+  // step is copied again, so that every step issues the same loads
+  auto issue = [&](int s) {
+    const int sc = min(s, s1 - 1);
+    h8* dst = stage + (size_t)(s % kBigStages) * kBigFrags * 64 + (wave * kBigPerWave) * 64;
     if (w_wave) {
 #pragma unroll
-      for (int i = 0; i < kBigPerWave; ++i)
-        __builtin_amdgcn_global_load_lds(fsrc[i] + (size_t)s * 64,
-                                         dst + (wave * kBigPerWave + i) * 64, 16, 0, 2);
+      for (int i = 0; i < kBigPerWave; ++i) copy16_nt(fsrc[i] + (size_t)sc * 64, dst + i * 64);
     } else {
 #pragma unroll
-      for (int i = 0; i < kBigPerWave; ++i)
-        __builtin_amdgcn_global_load_lds(fsrc[i] + (size_t)s * 64,
-                                         dst + (wave * kBigPerWave + i) * 64, 16, 0, 0);
+      for (int i = 0; i < kBigPerWave; ++i) copy16(fsrc[i] + (size_t)sc * 64, dst + i * 64);
     }
   };
-  // wait until this wave's copies of step s are in: at most the copies of
-  // the steps issued after it may remain
-  auto wait_step = [&](int s) {
-    const int later = min(kBigStages - 2, s1 - 1 - s);
-    static_assert(kBigStages <= 4, "waits below cover up to two later steps");
-    if (later >= 2)
-      wait_vm<2 * kBigPerWave>();
-    else if (later == 1)
-      wait_vm<kBigPerWave>();
-    else
-      wait_vm<0>();
-    // every wave's copies of step s are in. A plain s_barrier (a compiler
-    // memory barrier, no wait on vector memory), so later copies stay in
-    // flight.
-    asm volatile("s_barrier" ::: "memory");
-  };
-  f4 acc[4][kBigNT];
+  f4 acc[4][8];
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int t = 0; t < kBigNT; ++t) acc[b][t] = (f4){0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < kBigStages - 1 && i < nsteps; ++i) issue(s0 + i);
+    for (int t = 0; t < 8; ++t) acc[b][t] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < D; ++i) issue(s0 + i);
   for (int s = s0; s < s1; ++s) {
-    wait_step(s);  // the stage of step s−1 is free too
-    if (s + kBigStages - 1 < s1) issue(s + kBigStages - 1);
-    const h8* st = stage + (size_t)((s - s0) % kBigStages) * kBigFrags * 64;
-    h8 bf[kBigNT];
+    // this wave's copies of step s are in (those of the D − 1 later steps
+    // may remain); after the barrier every wave's are, and the stage of
+    // step s − 1 is free for step s + D
+    wait_vm<(D - 1) * kBigPerWave>();
+    lds_barrier();
+    issue(s + D);
+    const h8* st = stage + (size_t)(s % kBigStages) * kBigFrags * 64;
+    h8 af[4], bf[8];
 #pragma unroll
-    for (int t = 0; t < kBigNT; ++t) bf[t] = st[(16 + t) * 64 + lane];
-    // all four row blocks (rows past the input hold padding, never stored)
+    for (int t = 0; t < 8; ++t) bf[t] = st[(16 + cw * 8 + t) * 64 + lane];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const h8 af = st[(wave * 4 + b) * 64 + lane];
+    for (int b = 0; b < 4; ++b) af[b] = st[(rw * 4 + b) * 64 + lane];
 #pragma unroll
-      for (int t = 0; t < kBigNT; ++t) acc[b][t] = mfma16(af, bf[t], acc[b][t]);
-    }
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[b][t] = mfma16(af[b], bf[t], acc[b][t]);
   }
   const int j = lane >> 4, n = lane & 15;
   float* o = out + (size_t)sp * split_stride;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const int mb = wave * 4 + b;
+    const int mb = rw * 4 + b;
     if (mb >= mblocks) continue;
 #pragma unroll
-    for (int t = 0; t < kBigNT; ++t) {
-      const int col = (t0 + t) * 16 + n;
-      if (t0 + t < mp.ntiles && col < N)
+    for (int t = 0; t < 8; ++t) {
+      const int tt = t0 + cw * 8 + t, col = tt * 16 + n;
+      if (tt < mp.ntiles && col < N)
 #pragma unroll
         for (int v = 0; v < 4; ++v) o[(size_t)(mb * 16 + 4 * j + v) * N + col] = acc[b][t][v];
     }
@@ -1133,7 +1128,7 @@ void gemm_big_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const 
                   TileMap map, int N, int splits, int sps, float* out, long ss) {
   const unsigned blocks = cdiv(map.ntiles, kBigNT) * splits;
   const size_t lds = sizeof(h8) * kBigStages * kBigFrags * 64;
-  k_gemm_big_f16<<<blocks, kThreads, lds, st>>>(reinterpret_cast<const f16*>(xa), K, mblocks,
+  k_gemm_big_f16<<<blocks, 64 * kBigWaves, lds, st>>>(reinterpret_cast<const f16*>(xa), K, mblocks,
                                                 reinterpret_cast<const f16*>(w), map, N, splits,
                                                 sps, out, ss);
 }
