@@ -20,6 +20,7 @@ memory before any timed region. The per-kernel rooflines come from the
 library's stage timers (hipEvents on its stream) in a separate timed pass.
 """
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -70,7 +71,7 @@ def main():
     k, width, per_step = g["block"] - 1, g["vocab"], 8
     ctx0 = 32768
     steps, warm = args.steps, args.warmup
-    cap = max(ctx0 + per_step * (warm + steps + args.timing_steps) + 16, 16384 + 256)
+    cap = max(ctx0 + per_step * (warm + steps + 2 * args.timing_steps) + 16, 16384 + 256)
 
     t0 = time.time()
     w = synth.make_weights(g, seed=0, device=dev)
@@ -101,6 +102,15 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     settle_s = ev0.elapsed_time(ev1) / 1e3
+    # per-call times (an events pair around each call), for the median
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.settle_calls)]
+    for i, (a0, a1) in enumerate(cev):
+        a0.record()
+        d.settle(256 * i, 256, taps4[256 * i:].data_ptr())
+        a1.record()
+    torch.cuda.synchronize()
+    settle_call_med_us = float(np.median([a0.elapsed_time(a1) * 1e3 for a0, a1 in cev]))
     settle_rows_s = n_set / settle_s
     log(f"settle: {n_set} rows in {settle_s * 1e3:.2f} ms -> {settle_rows_s / 1e6:.3f} M rows/s")
     d.set_timing(True)
@@ -117,7 +127,7 @@ def main():
         d.settle(256 * c, 256, tp.data_ptr())
     torch.cuda.synchronize()
     log(f"context of {ctx0} positions settled in {time.time() - t0:.1f}s")
-    total = warm + steps + args.timing_steps
+    total = warm + steps + 2 * args.timing_steps
     stream_taps = synth.make_taps(g, per_step * total, seed=0, name="stream", device=dev)
     anchors = synth.uniform_tokens(g, total, seed=0)
     top = g["selector_top"]
@@ -145,9 +155,19 @@ def main():
     value = steps / dt
     log(f"stream: {steps} steps in {dt * 1e3:.1f} ms -> {value:.1f} blocks/s")
 
+    # per-step times over a further stretch (events around each step)
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.timing_steps)]
+    for j, (a0, a1) in enumerate(sev):
+        a0.record()
+        step(warm + steps + j)
+        a1.record()
+    torch.cuda.synchronize()
+    step_med_us = float(np.median([a0.elapsed_time(a1) * 1e3 for a0, a1 in sev]))
+
     # stage timers over a further stretch of the stream
     d.set_timing(True)
-    for i in range(warm + steps, total):
+    for i in range(warm + steps + args.timing_steps, total):
         step(i)
     st_stream, n_blocks, n_str_settles = d.stage_times()
     d.set_timing(False)
@@ -253,7 +273,20 @@ def main():
             },
         },
         "stages_us": stages,
+        "median_us": {"stream_step": round(step_med_us, 2),
+                      "settle_call": round(settle_call_med_us, 2)},
     }
+    # the same rates against what this GPU sustains, measured by two probes
+    # (a streaming read of the head weights; back-to-back f16 MFMAs)
+    read_gbs, mfma_tfs = d.probe_peaks(3)
+    log(f"measured peaks: streaming read {read_gbs:.0f} GB/s, f16 MFMA {mfma_tfs:.0f} TFLOP/s")
+    res["measured_peaks"] = {"hbm_read_gbs": round(read_gbs, 1), "mfma_f16_tfs": round(mfma_tfs, 1)}
+    res["roofline"]["frac_measured"] = round(head_gbs / read_gbs, 4)
+    sr = res["settle"]["roofline"]
+    sr["frac_measured"] = round((sr["achieved"] / read_gbs) if sr["bound"] == "hbm"
+                                else (sr["achieved"] / mfma_tfs), 4)
+    sr["mfma_frac"] = round(sr["tflops"] / F16_MFMA_PEAK_TFS, 4)
+    sr["mfma_frac_measured"] = round(sr["tflops"] / mfma_tfs, 4)
 
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(g, w, synth, args.cpu_steps)
@@ -316,11 +349,38 @@ def cpu_baseline(g, w, synth, steps):
         t_block += t2 - t1
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count()))
     log(f"cpu baseline: settle {t_settle:.1f}s, block {t_block:.1f}s over {steps} steps")
-    return {"value": round(steps / (t_settle + t_block), 4), "unit": "blocks/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{steps} stream steps of the same workload: 8 tap rows settled + one block "
-                      "(32768-position synthetic context, k=15, width=vocab) + selection, each",
-            "settle_s": round(t_settle, 2), "block_s": round(t_block, 2)}
+    res = {"value": round(steps / (t_settle + t_block), 4), "unit": "blocks/s", "cores": cores,
+           "kind": "oracle",
+           "sample": f"{steps} stream steps of the same workload: 8 tap rows settled + one block "
+                     "(32768-position synthetic context, k=15, width=vocab) + selection, each",
+           "settle_s": round(t_settle, 2), "block_s": round(t_block, 2),
+           "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+    # one step more on one thread (the oracle's OpenMP runtime set to 1)
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        t0 = time.perf_counter()
+        m.settle(taps[:8], 32768)
+        r = m.block(store, 0, 32768, anchors[0], 32768, g["block"] - 1, g["vocab"])
+        m.select(r["logits"], r["hp"], anchors[0])
+        t1 = time.perf_counter() - t0
+        gomp.omp_set_num_threads(cores)
+        log(f"cpu baseline: one thread, one step in {t1:.1f}s")
+        res["one_thread"] = {"value": round(1.0 / t1, 4), "unit": "blocks/s", "cores": 1,
+                             "sample": "1 stream step of the same workload"}
+    except OSError as e:
+        log(f"cpu baseline: one-thread run skipped ({e})")
+    return res
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

@@ -66,6 +66,7 @@ _SIGS = {
     "dflash_last_error": ([C.c_void_p], C.c_char_p),
     "dflash_set_timing": ([C.c_void_p, C.c_int], C.c_int),
     "dflash_stage_times": ([C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
+    "dflash_probe_peaks": ([C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p], C.c_int),
     "dflash_debug_dequant": ([C.c_void_p, C.c_int32, C.c_int32, C.c_void_p], C.c_int),
     "dflash_debug_matvec": ([C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int32,
                              C.c_void_p], C.c_int),
@@ -227,6 +228,12 @@ class Drafter:
         b, s = C.c_int64(), C.c_int64()
         _check(lib().dflash_stage_times(self.h, us, n, C.byref(b), C.byref(s)), self.h)
         return {name: (us[i], n[i]) for i, name in enumerate(STAGES)}, b.value, s.value
+
+    def probe_peaks(self, reps: int = 5):
+        """(streaming read GB/s, back-to-back f16 MFMA TFLOP/s) as measured on this GPU."""
+        r, m = C.c_double(), C.c_double()
+        _check(lib().dflash_probe_peaks(self.h, reps, C.byref(r), C.byref(m)), self.h)
+        return r.value, m.value
 
     def debug_dequant(self, layer, which, out_ptr):
         _check(lib().dflash_debug_dequant(self.h, layer, which, out_ptr), self.h)

@@ -578,6 +578,45 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   return done(rc);
 }
 
+int dflash_probe_peaks(dflash_t* d, int32_t reps, double* read_gbs, double* mfma_tfs) {
+  if (!d) return DFLASH_EINVAL;
+  if (reps < 1 || reps > 100 || !read_gbs || !mfma_tfs)
+    return fail(d, DFLASH_EINVAL, "probe_peaks: reps must be in [1, 100], outputs non-null");
+  hipStream_t st = d->st;
+  // the sinks are written only on impossible values; any device word serves
+  uint32_t* usink = reinterpret_cast<uint32_t*>(d->sel_sc.counters);
+  float* fsink = reinterpret_cast<float*>(d->sel_sc.counters);
+  const long bytes = (long)d->V * d->hs * 2 / 16 * 16;
+  constexpr int kWgs = 512, kSteps = 4096;  // two waves on every SIMD
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int rc = hip_check(d, hipEventCreate(&e0), "probe event");
+  if (!rc) rc = hip_check(d, hipEventCreate(&e1), "probe event");
+  float ms_read = 0.f, ms_mfma = 0.f;
+  if (!rc) {
+    dfl::probe_read(st, d->head, bytes, usink);  // warm
+    (void)hipEventRecord(e0, st);
+    for (int i = 0; i < reps; ++i) dfl::probe_read(st, d->head, bytes, usink);
+    (void)hipEventRecord(e1, st);
+    rc = hip_check(d, hipEventSynchronize(e1), "probe read");
+    if (!rc) rc = hip_check(d, hipEventElapsedTime(&ms_read, e0, e1), "probe read time");
+  }
+  if (!rc) {
+    dfl::probe_mfma(st, kWgs, kSteps, fsink);  // warm
+    (void)hipEventRecord(e0, st);
+    for (int i = 0; i < reps; ++i) dfl::probe_mfma(st, kWgs, kSteps, fsink);
+    (void)hipEventRecord(e1, st);
+    rc = hip_check(d, hipEventSynchronize(e1), "probe mfma");
+    if (!rc) rc = hip_check(d, hipEventElapsedTime(&ms_mfma, e0, e1), "probe mfma time");
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (rc) return rc;
+  *read_gbs = (double)bytes * reps / (ms_read * 1e-3) / 1e9;
+  // 4 waves × 32 MFMAs of 16·16·32·2 flops per step
+  *mfma_tfs = (double)kWgs * 4 * kSteps * 32 * 16384.0 * reps / (ms_mfma * 1e-3) / 1e12;
+  return launch_check(d, "probe_peaks");
+}
+
 int dflash_set_timing(dflash_t* d, int on) {
   if (!d) return DFLASH_EINVAL;
   int rc = hip_check(d, hipStreamSynchronize(d->st), "set_timing");

@@ -73,6 +73,11 @@ void gemm_f16_block(hipStream_t st, const uint16_t* xa, long ps, int K, const ui
 void gemm_glu(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
               const uint16_t* scales, int ftiles, uint16_t* ma, long mps);
 
+// Peak probes (kernels.hip): a streaming read of `bytes` (multiple of 16) at
+// p, and `workgroups` × 4 waves of `steps` rounds of 32 back-to-back MFMAs.
+void probe_read(hipStream_t st, const void* p, long bytes, uint32_t* sink);
+void probe_mfma(hipStream_t st, int workgroups, int steps, float* sink);
+
 // gate/up + SwiGLU streamed through one workgroup per tile-pair range
 // (stream.hip), for K ≤ 5120 (40 spans of 128 over eight waves); same
 // operands and output as gemm_glu.

@@ -1092,6 +1092,63 @@ __global__ void k_sum_rows(const float* __restrict__ part, int splits, long ss, 
 
 // ------------------------------------------------------------- launchers
 
+// ---------------------------------------------------------------- probes
+
+// Streaming read: every 16-byte element once, each wave over its own
+// contiguous chunk, eight 1 KB blocks (64 lanes × 16 B) in flight,
+// non-temporal. The xor keeps the loads; sink is written only on an
+// impossible value.
+__global__ __launch_bounds__(kThreads) void k_probe_read(const u32x4* __restrict__ p, long n,
+                                                         uint32_t* __restrict__ sink) {
+  constexpr int U = 8;
+  const int lane = threadIdx.x & 63;
+  const long waves = (long)gridDim.x * (kThreads / 64);
+  const long w = (long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const long per = ((n + waves - 1) / waves + 64 * U - 1) / (64 * U) * (64 * U);
+  const long b0 = w * per, b1 = min(n, b0 + per);
+  uint32_t x = 0;
+  long i = b0 + lane;
+  for (; i + 64 * (U - 1) < b1; i += 64 * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld_stream(p + i + 64 * u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < b1; i += 64) {
+    const u32x4 v = ld_stream(p + i);
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (x == 0x9e3779b9u) sink[0] = x;
+}
+
+// Back-to-back MFMAs: 32 independent accumulators a wave, operands in
+// registers. sink is written only on an impossible value.
+__global__ __launch_bounds__(kThreads) void k_probe_mfma(int steps, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  h8 a[4], b[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) a[r] = (h8){(f16)(1e-3f * (lane + r))};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) b[t] = (h8){(f16)(1e-3f * (lane - t))};
+  f4 acc[4][8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[r][t] = (f4){0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < steps; ++s)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[r][t] = mfma16(a[r], b[t], acc[r][t]);
+  float x = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) x += acc[r][t][0] + acc[r][t][3];
+  if (x == 1234.5f) sink[0] = x;
+}
+
 static inline unsigned cdiv(long a, long b) { return (unsigned)((a + b - 1) / b); }
 
 template <int R, int PL>
@@ -1191,6 +1248,15 @@ void rowsum_sq(hipStream_t st, const float* part, int splits, long ss, int rows,
                float* out, float* sqp) {
   const int nch = cdiv(N, kChunk);
   k_rowsum_sq<<<dim3(nch, rows), kThreads, 0, st>>>(part, splits, ss, N, out, sqp, nch);
+}
+
+// Probe launches; the caller times them (one workgroup of 256 threads is
+// four waves; 512 workgroups place two waves on every SIMD of 256 units).
+void probe_read(hipStream_t st, const void* p, long bytes, uint32_t* sink) {
+  k_probe_read<<<4096, kThreads, 0, st>>>(reinterpret_cast<const u32x4*>(p), bytes / 16, sink);
+}
+void probe_mfma(hipStream_t st, int workgroups, int steps, float* sink) {
+  k_probe_mfma<<<workgroups, kThreads, 0, st>>>(steps, sink);
 }
 
 int row_chunks(int N) { return cdiv(N, kChunk); }

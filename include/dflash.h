@@ -186,6 +186,18 @@ int dflash_set_timing(dflash_t* d, int on);
 int dflash_stage_times(const dflash_t* d, double* us, int64_t* launches, int64_t* blocks,
                        int64_t* settles);
 
+/* Peaks this GPU sustains, to report a kernel's rate against the chip as
+   measured here beside its spec sheet (8 TB/s HBM, 2.5 PFLOP/s dense f16):
+   - read_gbs: a streaming read of the library's own head weights (every
+     byte once a pass; each wave a contiguous chunk with eight 1 KB blocks in
+     flight, non-temporal 16-byte loads, 16 workgroups per compute unit),
+     `reps` passes, in GB/s;
+   - mfma_tfs: back-to-back v_mfma_f32_16x16x32_f16 on register operands,
+     two waves per SIMD, in TFLOP/s.
+   Runs on the library stream, timed with HIP events, and synchronises it.
+   reps in [1, 100]; -1 on a bad argument, -3 on a HIP error. */
+int dflash_probe_peaks(dflash_t* d, int32_t reps, double* read_gbs, double* mfma_tfs);
+
 /* ---- test entry points: each kernel on caller buffers ---------------------- */
 
 /* Matrix ids for the debug entry points (`layer` is ignored for the

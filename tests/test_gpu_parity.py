@@ -2,6 +2,8 @@
 C-ABI. Floating-point outputs must satisfy max|err| ≤ 2e-3·max|ref| per
 tensor and call; integer and index work is compared exactly (candidates and
 chosen tokens where the oracle's margin exceeds that tolerance)."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -243,6 +245,17 @@ def test_block_parity(orc, case):
         check_selection(got, ref["logits"], sel, "block")
     finally:
         d.close()
+
+
+def test_probe_peaks(small):
+    """The peak probes run on a small sidecar (a head buffer far smaller than
+    the probe's grid: most waves get an empty chunk) and return rates."""
+    _, _, d = small
+    read_gbs, mfma_tfs = d.probe_peaks(1)
+    assert math.isfinite(read_gbs) and read_gbs > 0
+    assert math.isfinite(mfma_tfs) and mfma_tfs > 0
+    with pytest.raises(pkg.DflashError):
+        d.probe_peaks(0)
 
 
 def test_block_is_deterministic(small):
