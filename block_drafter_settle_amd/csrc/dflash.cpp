@@ -31,7 +31,7 @@ constexpr int kKsQkv = 2;    // q/k/v, int4: spans (128 columns) per split
 constexpr int kKsO = 2;      // o, int4
 constexpr int kKsDown = 4;   // down, int4
 constexpr int kRKv = 2;      // settle's k/v of every layer, int4
-constexpr int kSettleI4Blocks = 2;  // above this many 16-row blocks the settle's k/v use the f16 halves
+constexpr int kSettleI4Blocks = 2;  // above this many 16-row blocks the settle's k/v use the many-row kernel
 constexpr int kRDebug = 2;   // the debug matvec
 
 thread_local std::string g_create_error;
@@ -50,6 +50,15 @@ Split split_for(int ntiles, int R, int steps, int mblocks, int min_per) {
   S = std::max(1L, std::min<long>(S, std::max(1, steps / min_per)));
   const int per = (int)((steps + S - 1) / S);
   return {(int)((steps + per - 1) / per), per};
+}
+
+// K splits of the settle's many-row K/V kernel (16 weight tiles a block, K in
+// 128-column spans): about one block per CU.
+Split split_kv(int ntiles, int spans) {
+  const long groups = dfl::kv_i4_groups(ntiles);
+  long S = std::max(1L, std::min<long>(256 / groups, spans));
+  const int per = (int)((spans + S - 1) / S);
+  return {(int)((spans + per - 1) / per), per};
 }
 
 // K splits of the many-row f16 GEMM (16 weight tiles a block): about one
@@ -154,9 +163,6 @@ struct dflash {
   dfl::SelectScratch sel_sc{};
   // settle scratch
   uint16_t *taps_a = nullptr, *t_a = nullptr;
-  // the settle's keys and values at many rows: Wk/Wv of every layer as two
-  // exact f16 halves, F16T [L·2·kd][2·hs], and the operand [t | t]
-  uint16_t *kvw = nullptr, *t_a2 = nullptr;
   float* tbuf = nullptr;
   long part_floats = 0;
   int stage_cols = 0;  // widest activation the staging buffer holds
@@ -353,7 +359,7 @@ long partial_need(const dflash* d) {
   i4b(d->hs, d->qd, 2);
   i4b(d->hs, d->ffn, 2);
   for (int mb = kSettleI4Blocks + 1; mb <= kSettleRows / 16; ++mb) {
-    const Split s = split_big(d->L * 2 * d->kd / 16, 2 * d->hs / 32);
+    const Split s = split_kv(d->L * 2 * d->kd / 16, d->hs / 128);
     need = std::max(need, (long)s.S * mb * 16 * d->L * 2 * d->kd);
   }
   for (int mb = 2; mb <= kSettleRows / 16; ++mb)
@@ -565,15 +571,6 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   if (!rc) rc = dev_alloc(d, &d->tbuf, (size_t)kSettleRows * hs, "settle scratch");
   if (!rc) rc = dev_alloc(d, &d->sqp, (size_t)kSettleRows * ((hs + 255) / 256), "norm scratch");
   if (!rc) rc = dev_alloc(d, &d->sel_sc.tab, (size_t)d->top * (1 + 15 * d->top), "selector table");
-  if (!rc) rc = dev_alloc(d, &d->kvw, (size_t)d->L * 2 * d->kd * 2 * hs, "settle k/v weights");
-  if (!rc) rc = dev_alloc(d, &d->t_a2, (size_t)kSettleRows * 2 * hs, "settle scratch");
-  if (!rc) {
-    const int kvt = 2 * d->kd / 16;
-    dfl::i4_planes(d->st, d->qkv.codes, d->qkv.scales,
-                   dfl::TileMap{d->L * kvt, kvt, d->qkv.tiles, d->qd / 16}, d->L * 2 * d->kd, hs,
-                   d->kvw);
-    rc = launch_check(d, "create");
-  }
   if (!rc) rc = hip_check(nullptr, hipDeviceSynchronize(), "create");
   return done(rc);
 }
@@ -679,23 +676,21 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
   tm_mark(d, DFLASH_ST_S_FC);
   dfl::rowsum_sq(st, d->part, sf.S, ssf, m, d->hs, d->tbuf, d->sqp);
   tm_mark(d, DFLASH_ST_S_NORM);
-  // the K/V product's operand: t, or [t | t] against the two weight halves
-  const bool halves = mb > kSettleI4Blocks;
   dfl::norm_apply(st, d->tbuf, d->sqp, dfl::row_chunks(d->hs), m, d->hs, d->hidden_norm, d->eps,
-                  nullptr, halves ? d->t_a2 : d->t_a, halves ? -1 : 0);
+                  nullptr, d->t_a, 0);
   tm_mark(d, DFLASH_ST_S_NORM);
   // K and V of every layer: the k and v tiles of each layer's q/k/v set
   const int kvt = 2 * d->kd / 16;
   const int N = d->L * 2 * d->kd;
   const long ssk = (long)mb * 16 * N;
+  const dfl::TileMap map{d->L * kvt, kvt, d->qkv.tiles, d->qd / 16};
   Split sk;
-  if (halves) {
-    sk = split_big(d->L * kvt, 2 * d->hs / 32);
-    dfl::gemm_big_f16(st, d->t_a2, 2 * d->hs, mb, d->kvw, dfl::TileMap{d->L * kvt, d->L * kvt, 0, 0},
-                      N, sk.S, sk.per, d->part, ssk);
+  if (mb > kSettleI4Blocks) {
+    sk = split_kv(d->L * kvt, d->hs / 128);
+    dfl::gemm_kv_i4(st, d->t_a, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per,
+                    d->part, ssk);
   } else {
     sk = split_for(d->L * kvt, kRKv, d->hs / 128, mb, 4);
-    dfl::TileMap map{d->L * kvt, kvt, d->qkv.tiles, d->qd / 16};
     dfl::gemm_i4(st, kRKv, d->t_a, 0, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per,
                  d->part, ssk);
   }

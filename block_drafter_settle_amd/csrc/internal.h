@@ -73,6 +73,15 @@ void gemm_f16_block(hipStream_t st, const uint16_t* xa, long ps, int K, const ui
 void gemm_glu(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
               const uint16_t* scales, int ftiles, uint16_t* ma, long mps);
 
+// The settle's K/V at many rows straight from int4 codes (kernels.hip): A the
+// single-plane operand of mblocks 16-row blocks (up to 16), K/V tiles through
+// map, K splits of sps spans (128 columns) each; partial sums
+// out[split][mblocks·16][N].
+int kv_i4_groups(int ntiles);
+void gemm_kv_i4(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint8_t* codes,
+                const uint16_t* scales, TileMap map, int N, int splits, int sps, float* out,
+                long ss);
+
 // Peak probes (kernels.hip): a streaming read of `bytes` (multiple of 16) at
 // p, and `workgroups` × 4 waves of `steps` rounds of 32 back-to-back MFMAs.
 void probe_read(hipStream_t st, const void* p, long bytes, uint32_t* sink);
@@ -106,8 +115,7 @@ void head_sel(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t
 void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa, long ps);
 // Row kernels: sqp holds partial sums of squares of each row, row_chunks(N)
 // per row from rowsum_sq and embed (256 channels each), conv1_chunks(hs)
-// per row from conv1; norm_apply takes the producer's count. norm_apply
-// with ps < 0 writes one plane of 2N columns, [y | y].
+// per row from conv1; norm_apply takes the producer's count.
 int row_chunks(int N);
 int conv1_chunks(int hs);
 void rowsum_sq(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,
@@ -148,10 +156,6 @@ void select_all(hipStream_t st, const float* logits, bool have_gmax, int k, int 
                 float* unary, float* score, int* chosen);
 void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,
                 int rows, int K, float* out);
-// int4 rows (map's tiles [0, rows/16)) → F16T [rows][2K]: q·s as two exact
-// f16 halves, hi in columns [0, K), the remainder in [K, 2K).
-void i4_planes(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,
-               int rows, int K, uint16_t* w);
 void sum_rows(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,
               float* out);
 

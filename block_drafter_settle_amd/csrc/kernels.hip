@@ -191,6 +191,132 @@ __global__ __launch_bounds__(64 * kBigWaves) void k_gemm_big_f16(const f16* __re
   }
 }
 
+// The settle's keys and values at many rows, straight from the int4 codes
+// (Wk/Wv of every layer): the block layout of k_gemm_big_f16 (256 rows,
+// 16 weight tiles, eight waves, wave w on row blocks 4(w%4)..+3 and tiles
+// 8(w/4)..+7), with each weight fragment decoded in registers into two
+// exact f16 halves: hi = f16(q·s) (a packed f16 product, rounded once) and
+// lo = q·s − hi (a packed f16 FMA; exact, since q·s has at most 15
+// significant bits and the residual is a multiple of the scale's ulp). The
+// products x·hi + x·lo sum the exact dequantised weight.
+//  - row fragments: every 32-column step through a kKvStages LDS ring (each
+//    wave copies two of the 16), kKvStages − 1 steps ahead;
+//  - codes and scales: every 128-column span into an LDS double buffer (each
+//    wave copies two tiles' codes, non-temporal, and their scales), one span
+//    ahead; each step reads its code word and scale of every tile.
+// Splits fall on span boundaries, so every step of a split is a real one.
+static constexpr int kKvNT = 16, kKvStages = 3;
+
+__global__ __launch_bounds__(64 * kBigWaves) void k_gemm_kv_i4(const f16* __restrict__ xa, int K,
+                                                              int mblocks,
+                                                              const uint4* __restrict__ codes,
+                                                              const uint32_t* __restrict__ scales,
+                                                              TileMap mp, int N, int splits,
+                                                              int sps, float* __restrict__ out,
+                                                              long split_stride) {
+  constexpr int D = kKvStages - 1;
+  static_assert(D == 2, "the waits below count two steps of row copies in flight");
+  __shared__ h8 ast[kKvStages][16][64];   // row fragments of a step
+  __shared__ uint4 cst[2][kKvNT][64];     // codes of a span: tile, lane
+  __shared__ uint32_t sst[2][kKvNT][32];  // scales of a span: tile, (n, pair)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rw = wave & 3, cw = wave >> 2;
+  const int KT = K >> 7;
+  const int sp = blockIdx.x % splits;
+  const int p0 = sp * sps, p1 = min(KT, p0 + sps);
+  const int s1 = 4 * p1;
+  const int t0 = (blockIdx.x / splits) * kKvNT;
+  const h8* xg = reinterpret_cast<const h8*>(xa);
+  const h8* asrc[2];
+  const uint4* csrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    asrc[i] = xg + (size_t)(2 * wave + i) * 2 * K + lane;
+    csrc[i] = codes + (size_t)map_tile(mp, min(t0 + 2 * wave + i, mp.ntiles - 1)) * KT * 64 + lane;
+  }
+  // a dword copy moves 64 dwords: tiles 2w (lanes 0–31) and 2w + 1 (32–63)
+  const uint32_t* ssrc =
+      scales + (size_t)map_tile(mp, min(t0 + 2 * wave + (lane >> 5), mp.ntiles - 1)) * KT * 32 +
+      (lane & 31);
+  auto issue_a = [&](int s) {
+    const int sc = min(s, s1 - 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) copy16(asrc[i] + (size_t)sc * 64, &ast[s % kKvStages][2 * wave + i][0]);
+  };
+  auto issue_c = [&](int p) {
+    const int pc = min(p, p1 - 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds(csrc[i] + (size_t)pc * 64, &cst[p & 1][2 * wave + i][0], 16, 0, 2);
+    __builtin_amdgcn_global_load_lds(ssrc + (size_t)pc * 32, &sst[p & 1][2 * wave][0], 4, 0, 0);
+  };
+  f4 acc[4][8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[b][t] = (f4){0.f, 0.f, 0.f, 0.f};
+  issue_c(p0);
+  issue_a(4 * p0);
+  issue_a(4 * p0 + 1);
+  const int n = lane & 15;
+  const uint32_t* cw32 = reinterpret_cast<const uint32_t*>(&cst[0][0][0]);
+  for (int p = p0; p < p1; ++p) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = 4 * p + u;
+      // this wave's copies of step s (and, at u = 0, of span p) are in: the
+      // copies issued after them may remain (two a step, three more with
+      // each span's codes, issued at its previous span's first step)
+      if (u == 0 || u == 3)
+        wait_vm<2>();
+      else
+        wait_vm<5>();
+      lds_barrier();
+      issue_a(s + D);
+      if (u == 0) issue_c(p + 1);
+      h8 af[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) af[b] = ast[s % kKvStages][rw * 4 + b][lane];
+      // this step's code word and scale of each tile, read from the span's
+      // buffers (rewritten only after the span's last step)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int tile = cw * 8 + t;
+        const uint32_t word = cw32[(((size_t)(p & 1) * kKvNT + tile) * 64 + lane) * 4 + u];
+        const uint32_t sb = sst[p & 1][tile][2 * n + (u >> 1)];
+        const f16 sh = __builtin_bit_cast(f16, (uint16_t)((u & 1) ? (sb >> 16) : (sb & 0xffffu)));
+        const h8 q = unpack_i4(word);
+        const h8 s8 = (h8){sh, sh, sh, sh, sh, sh, sh, sh};
+        const h8 hi = q * s8;
+        const h8 lo = __builtin_elementwise_fma(q, s8, -hi);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          acc[b][t] = mfma16(af[b], hi, acc[b][t]);
+          acc[b][t] = mfma16(af[b], lo, acc[b][t]);
+        }
+        // keep each tile's decode beside its products: decoded halves of all
+        // eight tiles at once would not fit two waves a SIMD
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  const int j = lane >> 4;
+  float* o = out + (size_t)sp * split_stride;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int mb = rw * 4 + b;
+    if (mb >= mblocks) continue;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int tt = t0 + cw * 8 + t, col = tt * 16 + n;
+      if (tt < mp.ntiles && col < N)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[(size_t)(mb * 16 + 4 * j + v) * N + col] = acc[b][t][v];
+    }
+  }
+}
+
 template <int R, int PL>
 __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa, long ps, int K,
                                                       const uint4* __restrict__ codes,
@@ -417,9 +543,7 @@ __global__ __launch_bounds__(kThreads) void k_rowsum_sq(const float* __restrict_
 // `rms`: y = h·(1/sqrt(Σh²/N + eps))·w for one 256-channel chunk of row r,
 // the row's Σh² gathered from the producer's `nchunk` partial sums (in a
 // fixed order, so every chunk of a row gets the same scale); y to f32 (if
-// x) and to A-layout f16 planes. ps < 0 writes instead one plane of 2N
-// columns holding y twice, [y | y] (the operand of a product against two
-// weight halves).
+// x) and to A-layout f16 planes.
 __global__ __launch_bounds__(kThreads) void k_norm_apply(const float* __restrict__ h,
                                                          const float* __restrict__ sqp,
                                                          int nchunk, int N,
@@ -435,13 +559,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_apply(const float* __restrict
   if (i >= N) return;
   const float y = h[(size_t)r * N + i] * scale * w[i];
   if (x) x[(size_t)r * N + i] = y;
-  if (ps < 0) {
-    f16* blk = xa + (size_t)(r >> 4) * 16 * 2 * N;
-    blk[a_idx(r & 15, i)] = (f16)y;
-    blk[a_idx(r & 15, i + N)] = (f16)y;
-  } else {
-    put_a(xa, ps, (size_t)(r >> 4) * 16 * N + a_idx(r & 15, i), y);
-  }
+  put_a(xa, ps, (size_t)(r >> 4) * 16 * N + a_idx(r & 15, i), y);
 }
 
 // The block's rows [E[anchor], E[mask]…] (f16 → f32) and each chunk's Σh².
@@ -1051,38 +1169,6 @@ __global__ void k_dequant_i4(const uint32_t* __restrict__ codes, const uint16_t*
   out[idx] = (float)q * half_bits(sb);
 }
 
-// int4 rows → F16T tiles of 2K columns holding each weight q·s exactly as
-// two halves: columns [0, K) the f16 rounding hi of q·s, columns [K, 2K)
-// the f16 of q·s − hi (q·s has at most 14 significant bits, hi takes 11).
-// A GEMM against [x | x] then sums x·hi + x·lo, the exact dequantised
-// product. One thread per (row, 8 columns) of the low half.
-__global__ void k_i4_planes(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-                            TileMap mp, int rows, int K, f16* __restrict__ w) {
-  const long idx = (long)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (long)rows * (K >> 3)) return;
-  const int row = idx / (K >> 3), k0 = (int)(idx % (K >> 3)) * 8;
-  const int t = row >> 4, n = row & 15, KT = K >> 7;
-  const long st = map_tile(mp, t);
-  const int p = k0 >> 7, u = (k0 >> 5) & 3, j = (k0 >> 3) & 3;
-  const uint32_t word = codes[(((size_t)st * KT + p) * 64 + j * 16 + n) * 4 + u];
-  const float sc = half_bits(scales[(((size_t)st * KT + p) * 16 + n) * 4 + u]);
-  h8 hi, lo;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int pos = (e & 1) ? 16 + 2 * (e - 1) : 2 * e;
-    const float v = (float)((int)((word >> pos) & 15u) - 8) * sc;
-    f16 h, l;
-    split_f16(v, h, l);
-    hi[e] = h;
-    lo[e] = l;
-  }
-  // F16T of the 2K-column matrix: tile t, step s, lane n + 16·j
-  const int KS2 = (2 * K) >> 5, lane = n + 16 * j;
-  h8* wt = reinterpret_cast<h8*>(w) + (size_t)t * KS2 * 64;
-  wt[(size_t)(k0 >> 5) * 64 + lane] = hi;
-  wt[(size_t)((K + k0) >> 5) * 64 + lane] = lo;
-}
-
 __global__ void k_sum_rows(const float* __restrict__ part, int splits, long ss, int rows, int N,
                            float* __restrict__ out) {
   const long idx = (long)blockIdx.x * kThreads + threadIdx.x;
@@ -1179,6 +1265,17 @@ void gemm_f16(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mbl
     pick_f16<2>(st, R, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
   else
     pick_f16<1>(st, R, xa, 0, K, mblocks, w, map, N, splits, sps, out, ss);
+}
+
+int kv_i4_groups(int ntiles) { return (int)cdiv(ntiles, kKvNT); }
+
+void gemm_kv_i4(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint8_t* codes,
+                const uint16_t* scales, TileMap map, int N, int splits, int sps, float* out,
+                long ss) {
+  const unsigned blocks = cdiv(map.ntiles, kKvNT) * splits;
+  k_gemm_kv_i4<<<blocks, 64 * kBigWaves, 0, st>>>(
+      reinterpret_cast<const f16*>(xa), K, mblocks, reinterpret_cast<const uint4*>(codes),
+      reinterpret_cast<const uint32_t*>(scales), map, N, splits, sps, out, ss);
 }
 
 void gemm_big_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
@@ -1337,12 +1434,6 @@ void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, Ti
                 int rows, int K, float* out) {
   k_dequant_i4<<<cdiv((long)rows * K, kThreads), kThreads, 0, st>>>(
       reinterpret_cast<const uint32_t*>(codes), scales, map, rows, K, out);
-}
-
-void i4_planes(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,
-               int rows, int K, uint16_t* w) {
-  k_i4_planes<<<cdiv((long)rows * (K / 8), kThreads), kThreads, 0, st>>>(
-      reinterpret_cast<const uint32_t*>(codes), scales, map, rows, K, reinterpret_cast<f16*>(w));
 }
 
 void sum_rows(hipStream_t st, const float* part, int splits, long ss, int rows, int N,
