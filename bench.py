@@ -165,6 +165,23 @@ def main():
     torch.cuda.synchronize()
     step_med_us = float(np.median([a0.elapsed_time(a1) * 1e3 for a0, a1 in sev]))
 
+    # the head at the pages' CUDA default width (65536 columns) over a short
+    # stretch: the same blocks, fewer head bytes; re-anchored at the same
+    # positions (the store already holds them)
+    w2 = 65536
+    out2 = torch.empty(k, w2, device=dev)
+    p2 = [out2.data_ptr()] + ptrs[1:]
+    n2 = args.timing_steps
+    for i in range(5):
+        d.block(anchors[i], pos, k, w2, *p2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n2):
+        d.block(anchors[i], pos, k, w2, *p2)
+    torch.cuda.synchronize()
+    w2_us = (time.perf_counter() - t0) / n2 * 1e6
+    del out2
+
     # stage timers over a further stretch of the stream
     d.set_timing(True)
     for i in range(warm + steps + args.timing_steps, total):
@@ -273,6 +290,12 @@ def main():
             },
         },
         "stages_us": stages,
+        "block_width_65536": {
+            "blocks_per_s": round(1e6 / w2_us, 1), "us_per_block": round(w2_us, 1),
+            "algorithmic_bytes": int(block_bytes - head_bytes + (w2 * hs * 2 + g["selector_rank"] * hs * 2 + k * w2 * 4)),
+            "hbm_frac": round((block_bytes - head_bytes + (w2 * hs * 2 + g["selector_rank"] * hs * 2 + k * w2 * 4))
+                              / (w2_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "blocks alone (no settle), head and selection over the first 65536 columns"},
         "median_us": {"stream_step": round(step_med_us, 2),
                       "settle_call": round(settle_call_med_us, 2)},
     }
