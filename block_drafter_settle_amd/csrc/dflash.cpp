@@ -30,6 +30,9 @@ constexpr int kRFc = 2;      // settle's fc, f16
 constexpr int kKsQkv = 2;    // q/k/v, int4: spans (128 columns) per split
 constexpr int kKsO = 2;      // o, int4
 constexpr int kKsDown = 4;   // down, int4
+constexpr int kRQkv = 2;     // their row tiles per wave
+constexpr int kRO = 2;
+constexpr int kRDown = 2;
 constexpr int kRKv = 2;      // settle's k/v of every layer, int4
 constexpr int kSettleI4Blocks = 2;  // above this many 16-row blocks the settle's k/v use the many-row kernel
 constexpr int kRDebug = 2;   // the debug matvec
@@ -163,7 +166,6 @@ struct dflash {
   dfl::SelectScratch sel_sc{};
   // settle scratch
   uint16_t *taps_a = nullptr, *t_a = nullptr;
-  float* tbuf = nullptr;
   long part_floats = 0;
   int stage_cols = 0;  // widest activation the staging buffer holds
   int last_k = 0;
@@ -568,9 +570,9 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   d->stage_cols = std::max(std::max(d->tw, d->ffn), std::max(d->qd, hs));
   if (!rc) rc = dev_alloc(d, &d->taps_a, (size_t)kSettleRows * d->stage_cols, "settle scratch");
   if (!rc) rc = dev_alloc(d, &d->t_a, (size_t)kSettleRows * hs, "settle scratch");
-  if (!rc) rc = dev_alloc(d, &d->tbuf, (size_t)kSettleRows * hs, "settle scratch");
   if (!rc) rc = dev_alloc(d, &d->sqp, (size_t)kSettleRows * ((hs + 255) / 256), "norm scratch");
   if (!rc) rc = dev_alloc(d, &d->sel_sc.tab, (size_t)d->top * (1 + 15 * d->top), "selector table");
+  if (!rc) rc = dev_alloc(d, &d->sel_sc.best, (size_t)(1 + 15 * d->top), "selector table");
   if (!rc) rc = hip_check(nullptr, hipDeviceSynchronize(), "create");
   return done(rc);
 }
@@ -674,10 +676,9 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
     dfl::gemm_f16(st, kRFc, d->taps_a, 0, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part,
                   ssf);
   tm_mark(d, DFLASH_ST_S_FC);
-  dfl::rowsum_sq(st, d->part, sf.S, ssf, m, d->hs, d->tbuf, d->sqp);
-  tm_mark(d, DFLASH_ST_S_NORM);
-  dfl::norm_apply(st, d->tbuf, d->sqp, dfl::row_chunks(d->hs), m, d->hs, d->hidden_norm, d->eps,
-                  nullptr, d->t_a, 0);
+  // the hidden norm folded: t ⊙ hidden_norm feeds the K/V projection, and
+  // settle_kv applies each row's rms scale to its output
+  dfl::rowsum_sq(st, d->part, sf.S, ssf, m, d->hs, d->hidden_norm, d->t_a, d->sqp);
   tm_mark(d, DFLASH_ST_S_NORM);
   // K and V of every layer: the k and v tiles of each layer's q/k/v set
   const int kvt = 2 * d->kd / 16;
@@ -696,7 +697,7 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
   }
   tm_mark(d, DFLASH_ST_S_KV);
   dfl::settle_kv(st, d->part, sk.S, ssk, m, d->L, d->kv, d->hd, d->k_norm, d->inv, d->rot_dev,
-                 pos0, d->eps, d->sk, d->sv, d->cap, row0);
+                 pos0, d->eps, d->sqp, d->hs, d->sk, d->sv, d->cap, row0);
   tm_mark(d, DFLASH_ST_S_STORE);
   return launch_check(d, "settle");
 }
@@ -758,23 +759,27 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
   const long psh = 16L * hs, psq = 16L * d->nh * d->hd, psy = 16L * d->qd, psm = 16L * d->ffn;
 
   tm_begin(d);
-  dfl::embed(st, d->embed, anchor, d->mask, B, hs, d->h, d->sqp);
+  // Each sub-layer's rms is folded into its neighbours: the producer of h
+  // (embed, conv1) writes h, its partial sums of squares and h ⊙ gain as the
+  // kernel projection's input; conv0 applies the per-row scale.
+  dfl::embed(st, d->embed, anchor, d->mask, B, hs, d->h, d->sqp, d->in_norm, d->xa, psh);
   tm_mark(d, DFLASH_ST_CONV);
-  dfl::norm_apply(st, d->h, d->sqp, dfl::row_chunks(hs), B, hs, d->in_norm, d->eps, d->x, d->xa, psh);
-  tm_mark(d, DFLASH_ST_CONV);
+  int nch = dfl::row_chunks(hs);  // sums of squares per row: embed's, then conv1's
   for (int l = 0; l < d->L; ++l) {
     const float* ab = d->attn_base + (size_t)l * 2 * d->kn * hs;
     const float* mbase = d->mlp_base + (size_t)l * 2 * d->kn * hs;
+    const float* post = d->post_norm + (size_t)l * hs;
     // attention: conv_in, q/k/v, norms + rotary
     dfl::gemm_f16_block(st, d->xa, psh, hs, d->attn_kproj + l * kp_layer,
                         dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, d->part, ssd);
     tm_mark(d, DFLASH_ST_KPROJ);
-    dfl::conv0(st, d->x, d->part, spk.S, ssd, ab, B, hs, d->gs, d->kn, d->xca, psh, d->dsum_a);
+    dfl::conv0(st, d->h, d->sqp, nch, d->in_norm + (size_t)l * hs, d->eps, d->part, spk.S, ssd, ab,
+               B, hs, d->gs, d->kn, d->xca, psh, d->dsum_a);
     tm_mark(d, DFLASH_ST_CONV);
     dfl::gemm_i4_block(st, d->xca, psh, hs, d->qkv.codes + i4l_qkv * 1024 * l,
                        d->qkv.scales + i4l_qkv * 64 * l,
                        dfl::TileMap{d->qkv.tiles, d->qkv.tiles, 0, 0}, d->qd + 2 * d->kd, sqk.per,
-                       d->part, ssq);
+                       d->part, ssq, kRQkv);
     tm_mark(d, DFLASH_ST_QKV);
     dfl::qkv_post(st, d->part, sqk.S, ssq, B, d->nh, d->kv, d->hd, d->q_norm + (size_t)l * d->hd,
                   d->k_norm + (size_t)l * d->hd, d->inv, a, d->rot[l], d->eps, d->qa, psq, d->kb, d->vb);
@@ -791,22 +796,21 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     tm_mark(d, DFLASH_ST_ATTN);
     dfl::attn_merge(st, d->pacc, d->pml, d->nh, d->kv, d->hd, nchunks, B, d->ya, psy);
     tm_mark(d, DFLASH_ST_ATTN);
-    // o, conv_out into the residual, post-attention norm
+    // o, conv_out into the residual (and the MLP norm's input)
     dfl::gemm_i4_block(st, d->ya, psy, d->qd, d->o.codes + i4l_o * 1024 * l,
                        d->o.scales + i4l_o * 64 * l, dfl::TileMap{d->o.tiles, d->o.tiles, 0, 0},
-                       hs, so.per, d->part, ssh);
+                       hs, so.per, d->part, ssh, kRO);
     tm_mark(d, DFLASH_ST_O);
-    dfl::conv1(st, d->h, d->part, so.S, ssh, d->dsum_a, ab, B, hs, d->gs, d->kn, d->sqp);
-    tm_mark(d, DFLASH_ST_CONV);
-    dfl::norm_apply(st, d->h, d->sqp, nc1, B, hs, d->post_norm + (size_t)l * hs, d->eps, d->x, d->xa,
-                    psh);
+    dfl::conv1(st, d->h, d->part, so.S, ssh, d->dsum_a, ab, B, hs, d->gs, d->kn, d->sqp, post,
+               d->xa, psh);
+    nch = nc1;
     tm_mark(d, DFLASH_ST_CONV);
     // MLP, wrapped the same way
     dfl::gemm_f16_block(st, d->xa, psh, hs, d->mlp_kproj + l * kp_layer,
                         dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, d->part, ssd);
     tm_mark(d, DFLASH_ST_KPROJ);
-    dfl::conv0(st, d->x, d->part, spk.S, ssd, mbase, B, hs, d->gs, d->kn, d->xca, psh,
-               d->dsum_m);
+    dfl::conv0(st, d->h, d->sqp, nch, post, d->eps, d->part, spk.S, ssd, mbase, B, hs, d->gs, d->kn,
+               d->xca, psh, d->dsum_m);
     tm_mark(d, DFLASH_ST_CONV);
     if (dfl::glu_stream_fits(hs))
       dfl::gemm_glu_stream(st, d->xca, psh, hs, d->gu.codes + i4l_gu * 1024 * l,
@@ -817,18 +821,23 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     tm_mark(d, DFLASH_ST_GLU);
     dfl::gemm_i4_block(st, d->ma, psm, d->ffn, d->down.codes + i4l_dn * 1024 * l,
                        d->down.scales + i4l_dn * 64 * l,
-                       dfl::TileMap{d->down.tiles, d->down.tiles, 0, 0}, hs, sdn.per, d->part, ssh);
+                       dfl::TileMap{d->down.tiles, d->down.tiles, 0, 0}, hs, sdn.per, d->part, ssh,
+                       kRDown);
     tm_mark(d, DFLASH_ST_DOWN);
-    const float* next = l + 1 < d->L ? d->in_norm + (size_t)(l + 1) * hs : d->norm;
-    dfl::conv1(st, d->h, d->part, sdn.S, ssh, d->dsum_m, mbase, B, hs, d->gs, d->kn, d->sqp);
-    tm_mark(d, DFLASH_ST_CONV);
-    dfl::norm_apply(st, d->h, d->sqp, nc1, B, hs, next, d->eps, d->x, d->xa, psh);
+    // conv_out into the residual, and the next layer's attention-norm input
+    // (the final norm runs on its own below)
+    const float* next = l + 1 < d->L ? d->in_norm + (size_t)(l + 1) * hs : nullptr;
+    dfl::conv1(st, d->h, d->part, sdn.S, ssh, d->dsum_m, mbase, B, hs, d->gs, d->kn, d->sqp, next,
+               d->xa, psh);
     tm_mark(d, DFLASH_ST_CONV);
     if (d->trace)
       (void)hipMemcpyAsync(d->trace + (size_t)l * B * hs, d->h, sizeof(float) * B * hs,
                            hipMemcpyDeviceToDevice, st);
   }
-  // head over rows 1..k and the selector projection
+  // the final norm (the head's input), then the head over rows 1..k and
+  // the selector projection
+  dfl::norm_apply(st, d->h, d->sqp, nc1, B, hs, d->norm, d->eps, d->x, d->xa, psh);
+  tm_mark(d, DFLASH_ST_CONV);
   float* lg = logits ? logits : d->logits;
   dfl::head_sel(st, d->xa, psh, hs, d->head, width, k, lg, d->sel, d->rank, d->hp, d->sel_sc);
   tm_mark(d, DFLASH_ST_HEAD);

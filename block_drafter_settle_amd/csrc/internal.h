@@ -57,11 +57,12 @@ void gemm_big_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const 
                   long split_stride);
 // The block pass's 16-row int4 GEMM (two planes, ps ≠ 0; skinny.hip):
 // splits of `ks` spans (128 columns) each, i4_block_splits(K, ks) of them;
-// out as gemm_i4. ks is 2 or 4.
+// out as gemm_i4. A wave takes R row tiles: (R, ks) is (2, 2), (2, 4),
+// (2, 8), (4, 2) or (4, 4).
 int i4_block_splits(int K, int ks);
 void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
                    const uint16_t* scales, TileMap map, int N, int ks, float* out,
-                   long split_stride);
+                   long split_stride, int R = 2);
 // The block pass's 16-row f16 GEMM (two planes, ps ≠ 0): f16_block_splits(K)
 // splits of 512 columns; out as gemm_f16.
 int f16_block_splits(int K);
@@ -103,6 +104,7 @@ struct SelectScratch {
   float* lv;
   int* li;
   float* tab;
+  int* best;  // per (row, predecessor) table row: the first candidate of the largest score
 };
 
 // Logits of rows 1..k over head tiles [0, ceil(width/16)) and the selector
@@ -118,24 +120,31 @@ void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa, l
 // per row from conv1; norm_apply takes the producer's count.
 int row_chunks(int N);
 int conv1_chunks(int hs);
+// rowsum_sq: the split-summed settle rows t, their sums of squares, and
+// t ⊙ w as the K/V projection's one-plane operand; settle_kv applies the
+// hidden norm's per-row scale (from sqp, row_chunks(hs) per row).
 void rowsum_sq(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,
-               float* out, float* sqp);
+               const float* w, uint16_t* xa, float* sqp);
 void norm_apply(hipStream_t st, const float* h, const float* sqp, int nchunk, int rows, int N,
                 const float* w, float eps, float* x, uint16_t* xa, long ps);
+// embed and conv1 also write u = h ⊙ w (w: the next norm's gain; conv1
+// skips it for w == nullptr) as A-layout planes, the next kernel
+// projection's input; conv0 applies that norm's per-row scale from sqp.
 void embed(hipStream_t st, const uint16_t* emb, int anchor, int mask, int rows, int hs, float* h,
-           float* sqp);
-void conv0(hipStream_t st, const float* x, const float* dpart, int splits, long split_stride,
-           const float* base, int rows, int hs, int gs, int kn, uint16_t* xca, long ps,
-           float* dsum);
+           float* sqp, const float* w, uint16_t* xa, long ps);
+void conv0(hipStream_t st, const float* h, const float* sqp, int nchunk, const float* w, float eps,
+           const float* dpart, int splits, long split_stride, const float* base, int rows, int hs,
+           int gs, int kn, uint16_t* xca, long ps, float* dsum);
 void conv1(hipStream_t st, float* h, const float* opart, int splits, long split_stride,
-           const float* dsum, const float* base, int rows, int hs, int gs, int kn, float* sqp);
+           const float* dsum, const float* base, int rows, int hs, int gs, int kn, float* sqp,
+           const float* w, uint16_t* xa, long ps);
 void qkv_post(hipStream_t st, const float* part, int splits, long split_stride, int rows, int nh,
               int kv, int hd, const float* q_norm, const float* k_norm, const float* inv_freq,
               long pos0, int rot, float eps, uint16_t* qa, long qps, float* kb, float* vb);
 void settle_kv(hipStream_t st, const float* part, int splits, long split_stride, int rows,
                int layers, int kv, int hd, const float* k_norm, const float* inv_freq,
-               const int* rot, long pos0, float eps, float* store_k, float* store_v, long cap,
-               long row0);
+               const int* rot, long pos0, float eps, const float* sqp, int hs, float* store_k,
+               float* store_v, long cap, long row0);
 // Context chunks per kv head of one attention call; the merge holds one
 // weight per chunk (and one for the block's own rows) in LDS.
 constexpr int kAttnMaxChunks = 64;

@@ -525,16 +525,20 @@ __global__ __launch_bounds__(kThreads) void k_to_a(const float* __restrict__ x, 
 // the rows and each chunk's sum of squares, `k_norm_apply` finishes `rms`.
 static constexpr int kChunk = 256;
 
-// Split-summed rows (the settle's t = fc·taps) and each chunk's Σv².
+// Split-summed rows (the settle's t = fc·taps), each chunk's Σt², and
+// u = t ⊙ w (w: hidden_norm's gain) as the one-plane A-layout operand of the
+// settle's K/V projection; rms's per-row scale is applied to that
+// projection's output (k_settle_kv), so no separate norm pass runs.
 __global__ __launch_bounds__(kThreads) void k_rowsum_sq(const float* __restrict__ part, int splits,
-                                                        long ss, int N, float* __restrict__ out,
+                                                        long ss, int N, const float* __restrict__ w,
+                                                        f16* __restrict__ xa,
                                                         float* __restrict__ sqp, int nchunk) {
   __shared__ float red[4];
   const int r = blockIdx.y, c = blockIdx.x, i = c * kChunk + threadIdx.x;
   float v = 0.f;
   if (i < N) {
     v = sum_splits(part + (size_t)r * N + i, splits, ss);
-    out[(size_t)r * N + i] = v;
+    put_a(xa, 0, (size_t)(r >> 4) * 16 * N + a_idx(r & 15, i), v * w[i]);
   }
   const float sq = block_sum(v * v, red);
   if (threadIdx.x == 0) sqp[(size_t)r * nchunk + c] = sq;
@@ -562,48 +566,106 @@ __global__ __launch_bounds__(kThreads) void k_norm_apply(const float* __restrict
   put_a(xa, ps, (size_t)(r >> 4) * 16 * N + a_idx(r & 15, i), y);
 }
 
-// The block's rows [E[anchor], E[mask]…] (f16 → f32) and each chunk's Σh².
+// The block's rows [E[anchor], E[mask]…] (f16 → f32), each chunk's Σh²,
+// and u = h ⊙ w (w: the first norm's gain) as A-layout f16 planes: the
+// kernel projection takes u, and rms's per-row scale is applied to its
+// product afterwards (k_conv0), so no separate norm pass runs.
 __global__ __launch_bounds__(kThreads) void k_embed(const f16* __restrict__ embed, int anchor,
                                                     int mask, int hs, float* __restrict__ h,
-                                                    float* __restrict__ sqp, int nchunk) {
+                                                    float* __restrict__ sqp, int nchunk,
+                                                    const float* __restrict__ w,
+                                                    f16* __restrict__ xa, long ps) {
   __shared__ float red[4];
   const int r = blockIdx.y, c = blockIdx.x, i = c * kChunk + threadIdx.x;
   float v = 0.f;
   if (i < hs) {
     v = (float)embed[(size_t)(r == 0 ? anchor : mask) * hs + i];
     h[(size_t)r * hs + i] = v;
+    put_a(xa, ps, a_idx(r, i), v * w[i]);
   }
   const float sq = block_sum(v * v, red);
   if (threadIdx.x == 0) sqp[(size_t)r * nchunk + c] = sq;
 }
 
-// Conv stage 0 (`conv`) of row r over a run of whole channel groups:
-// xc[r][i] = Σ_{o ≤ min(kn−1, r)} (base[0][o][i] + d[r][0][o][i/gs])·x[r−o][i].
-// The split-summed kernel projection of these groups, both stages, is kept
-// for stage 1.
-__global__ __launch_bounds__(kThreads) void k_conv0(const float* __restrict__ x,
+// Conv stage 0 (`conv`) of row r over a run of whole channel groups, with
+// the sub-layer's `rms` folded in. The producer of h left each row's
+// partial sums of squares (nchunk of them) and u = h ⊙ w as the kernel
+// projection's input, so with s_q = 1/sqrt(Σh_q²/hs + eps):
+//   x[q][i] = h[q][i]·s_q·w[i]            (the normed rows)
+//   d[r]    = s_r · (Kp·u_r)             (= Kp·x_r)
+//   xc[r][i] = Σ_{o ≤ min(kn−1, r)} (base[0][o][i] + d[r][0][o][i/gs])·x[r−o][i].
+// The split-summed, scaled kernel projection of these groups, both stages,
+// is kept for stage 1.
+__global__ __launch_bounds__(kThreads) void k_conv0(const float* __restrict__ h,
+                                                    const float* __restrict__ sqp, int nchunk,
+                                                    const float* __restrict__ w, float eps,
                                                     const float* __restrict__ dpart, int splits,
                                                     long ss, const float* __restrict__ base,
                                                     int hs, int gs, int kn, int gpw,
                                                     f16* __restrict__ xca, long ps,
                                                     float* __restrict__ dsum) {
   extern __shared__ float dl[];  // [2·kn][ng]
+  __shared__ float sc[16];       // s of rows r − o, o < taps (kn ≤ 16)
   const int r = blockIdx.y;
   const int G = hs / gs, P = 2 * kn * G;
   const int g0 = blockIdx.x * gpw, ng = min(G, g0 + gpw) - g0;
+  const int taps = min(kn, r + 1);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave o sums row r − o's partial sums of squares; every workgroup of a
+  // row sums them in the same order, so all of them get the same scale. The
+  // loads are issued ahead of the projection's split sums below (neither
+  // waits for the other).
+  float q = 0.f;
+  if (wave < taps)
+    for (int c = lane; c < nchunk; c += 64) q += sqp[(size_t)(r - wave) * nchunk + c];
+  // the first channel of this thread: its rows, base taps and gain, loaded
+  // ahead of the barriers
+  constexpr int kPre = 4;
+  const int i0 = g0 * gs + threadIdx.x, iend = (g0 + ng) * gs;
+  const bool pre = i0 < iend;
+  float hx[kPre], bs[kPre], wi = 0.f;
+#pragma unroll
+  for (int o = 0; o < kPre; ++o) {
+    hx[o] = pre && o < taps ? h[(size_t)(r - o) * hs + i0] : 0.f;
+    bs[o] = pre && o < taps ? base[(size_t)o * hs + i0] : 0.f;
+  }
+  if (pre) wi = w[i0];
   for (int e = threadIdx.x; e < 2 * kn * ng; e += kThreads) {
     const int idx = (e / ng) * G + g0 + e % ng;
-    const float v = sum_splits(dpart + (size_t)r * P + idx, splits, ss);
+    dl[e] = sum_splits(dpart + (size_t)r * P + idx, splits, ss);
+  }
+  q = wave_sum(q);
+  if (lane == 0 && wave < taps) sc[wave] = 1.f / sqrtf(q / hs + eps);
+  for (int o = wave + kThreads / 64; o < taps; o += kThreads / 64) {  // kn > 4
+    float q2 = 0.f;
+    for (int c = lane; c < nchunk; c += 64) q2 += sqp[(size_t)(r - o) * nchunk + c];
+    q2 = wave_sum(q2);
+    if (lane == 0) sc[o] = 1.f / sqrtf(q2 / hs + eps);
+  }
+  __syncthreads();
+  const float sr = sc[0];
+  for (int e = threadIdx.x; e < 2 * kn * ng; e += kThreads) {
+    const int idx = (e / ng) * G + g0 + e % ng;
+    const float v = sr * dl[e];
     dl[e] = v;
     dsum[(size_t)r * P + idx] = v;
   }
   __syncthreads();
-  const int taps = min(kn, r + 1);
-  for (int i = g0 * gs + threadIdx.x; i < (g0 + ng) * gs; i += kThreads) {
+  if (pre) {
+    const int g = i0 / gs - g0;
+    float acc = 0.f;
+#pragma unroll
+    for (int o = 0; o < kPre; ++o)
+      if (o < taps) acc += (bs[o] + dl[o * ng + g]) * (hx[o] * sc[o] * wi);
+    for (int o = kPre; o < taps; ++o)
+      acc += (base[(size_t)o * hs + i0] + dl[o * ng + g]) * (h[(size_t)(r - o) * hs + i0] * sc[o] * wi);
+    put_a(xca, ps, a_idx(r, i0), acc);
+  }
+  for (int i = i0 + kThreads; i < iend; i += kThreads) {  // conv groups wider than a block
     const int g = i / gs - g0;
     float acc = 0.f;
     for (int o = 0; o < taps; ++o)
-      acc += (base[(size_t)o * hs + i] + dl[o * ng + g]) * x[(size_t)(r - o) * hs + i];
+      acc += (base[(size_t)o * hs + i] + dl[o * ng + g]) * (h[(size_t)(r - o) * hs + i] * sc[o] * w[i]);
     put_a(xca, ps, a_idx(r, i), acc);
   }
 }
@@ -613,29 +675,48 @@ __global__ __launch_bounds__(kThreads) void k_conv0(const float* __restrict__ x,
 // the split-summed GEMM output. One workgroup per kC1 channels and all
 // rows: thread (c, r) split-sums out[r] at its channel once, and the taps
 // read those sums from LDS. Also each (row, kC1 channels)'s Σh² of the new
-// rows, sqp[r][blockIdx.x].
+// rows, sqp[r][blockIdx.x], and, when w (the next norm's gain) is given,
+// u = h ⊙ w as A-layout f16 planes for the next kernel projection (k_conv0
+// applies that norm's per-row scale).
 static constexpr int kC1 = 32;
 __global__ __launch_bounds__(kC1 * 16) void k_conv1(float* __restrict__ h,
                                                     const float* __restrict__ opart, int splits,
                                                     long ss, const float* __restrict__ dsum,
                                                     const float* __restrict__ base, int rows,
                                                     int hs, int gs, int kn,
-                                                    float* __restrict__ sqp, int nchunk) {
+                                                    float* __restrict__ sqp, int nchunk,
+                                                    const float* __restrict__ w,
+                                                    f16* __restrict__ xa, long ps) {
+  constexpr int kPre = 4;  // taps whose coefficients are loaded ahead of the barrier
   __shared__ float v[16][kC1];
   const int c = threadIdx.x % kC1, r = threadIdx.x / kC1;
   const int i = blockIdx.x * kC1 + c;
   const bool live = r < rows && i < hs;
+  const int G = hs / gs, P = 2 * kn * G, taps = min(kn, r + 1), g = i / gs;
+  const float* b1 = base + (size_t)kn * hs;
+  const float* d1 = dsum + (size_t)r * P + (size_t)kn * G;
+  // this thread's tap coefficients, old h and gain, loaded together with the
+  // split sums (none of them waits for the barrier)
+  float coef[kPre], hold = 0.f, wi = 0.f;
+#pragma unroll
+  for (int o = 0; o < kPre; ++o)
+    coef[o] = live && o < taps ? b1[(size_t)o * hs + i] + d1[o * G + g] : 0.f;
+  if (live) {
+    hold = h[(size_t)r * hs + i];
+    if (w) wi = w[i];
+  }
   v[r][c] = live ? sum_splits(opart + (size_t)r * hs + i, splits, ss) : 0.f;
   __syncthreads();
   float hn = 0.f;
   if (live) {
-    const int G = hs / gs, P = 2 * kn * G, taps = min(kn, r + 1), g = i / gs;
-    const float* b1 = base + (size_t)kn * hs;
-    const float* d1 = dsum + (size_t)r * P + (size_t)kn * G;
     float acc = 0.f;
-    for (int o = 0; o < taps; ++o) acc += (b1[(size_t)o * hs + i] + d1[o * G + g]) * v[r - o][c];
-    hn = h[(size_t)r * hs + i] + acc;
+#pragma unroll
+    for (int o = 0; o < kPre; ++o)
+      if (o < taps) acc += coef[o] * v[r - o][c];
+    for (int o = kPre; o < taps; ++o) acc += (b1[(size_t)o * hs + i] + d1[o * G + g]) * v[r - o][c];
+    hn = hold + acc;
     h[(size_t)r * hs + i] = hn;
+    if (w) put_a(xa, ps, a_idx(r, i), hn * wi);
   }
   // Σh² over the kC1 channels of row r: the kC1 lanes that hold them
   float sq = hn * hn;
@@ -733,7 +814,8 @@ __global__ __launch_bounds__(64) void k_settle_kv(const float* __restrict__ part
                                                   const float* __restrict__ knorm,
                                                   const float* __restrict__ inv,
                                                   const int* __restrict__ rot, long pos0,
-                                                  float eps, float* __restrict__ sk,
+                                                  float eps, const float* __restrict__ sqp,
+                                                  int nchunk, int hs, float* __restrict__ sk,
                                                   float* __restrict__ sv, long cap, long row0) {
   const int r = blockIdx.x, l = blockIdx.y, hh = blockIdx.z;
   const int kd = kv * hd, N = L * 2 * kd, half = hd >> 1;
@@ -741,6 +823,16 @@ __global__ __launch_bounds__(64) void k_settle_kv(const float* __restrict__ part
   const int g = isk ? hh : hh - kv;
   Pairs p = load_pairs(part, splits, ss, (long)r * N + (long)l * 2 * kd + (isk ? 0 : kd) + g * hd,
                        half);
+  // the hidden norm's scale of row r (the projection took t ⊙ w), summed in
+  // the same order by every workgroup of the row
+  float q = 0.f;
+  for (int c = threadIdx.x; c < nchunk; c += 64) q += sqp[(size_t)r * nchunk + c];
+  const float sr = 1.f / sqrtf(wave_sum(q) / hs + eps);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    p.lo[c] *= sr;
+    p.hi[c] *= sr;
+  }
   if (isk) norm_rope(p, hd, knorm + (size_t)l * hd, eps, inv, pos0 + r, rot[l]);
   float* dst = (isk ? sk : sv) + ((size_t)l * cap + row0 + r) * kd + (size_t)g * hd;
 #pragma unroll
@@ -927,6 +1019,7 @@ __device__ __forceinline__ void append(bool take, float v, int idx, int* counter
 __global__ __launch_bounds__(kThreads) void k_collect(const float* __restrict__ logits, int width,
                                                       int top, int nslices,
                                                       const float* __restrict__ thr,
+                                                      const float* __restrict__ gmax, int ngroups,
                                                       int* __restrict__ counters,
                                                       float* __restrict__ lv, int* __restrict__ li,
                                                       int cap) {
@@ -934,6 +1027,12 @@ __global__ __launch_bounds__(kThreads) void k_collect(const float* __restrict__ 
   const int sl = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (sl >= nslices) return;
   const float T = thr[j];
+  // a slice whose 256-column groups all peak below T holds no logit ≥ T:
+  // skip it without reading its logits
+  constexpr int kGroups = 64 * kSliceVPL / 256;
+  const int g = sl * kGroups + lane;
+  const bool hot = lane < kGroups && g < ngroups && gmax[(size_t)j * ngroups + g] >= T;
+  if (!__ballot(hot)) return;
   const int b0 = sl * 64 * kSliceVPL;
   const float* row = logits + (size_t)j * width;
   float v[kSliceVPL];
@@ -1049,7 +1148,7 @@ __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
                                                const f16* __restrict__ cbook, int vocab, int anchor,
                                                const int* __restrict__ forced,
                                                int* __restrict__ cand, float* __restrict__ unary,
-                                               float* __restrict__ tab) {
+                                               float* __restrict__ tab, int* __restrict__ best) {
   __shared__ float uv[2][32 + 64];
   __shared__ int uc[2][32 + 64];
   __shared__ float sv[2][kRankMax];
@@ -1082,74 +1181,80 @@ __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
     const int q = lane + 64 * c;
     pc[c] = (okp && q < rank) ? (float)pbook[(size_t)prev * rank + q] * hp[(size_t)j * rank + q] : 0.f;
   }
-  float* out = tab + (j == 0 ? 0 : top + ((size_t)(j - 1) * tpn + tp) * top);
-  for (int t0 = 0; t0 < top; t0 += 8) {
-    float part[8];
+  const size_t trow = j == 0 ? 0 : 1 + (size_t)(j - 1) * tpn + tp;  // this block's table row
+  float* out = tab + trow * top;
+  // every candidate's codebook row is loaded at once (top ≤ 32): per rank
+  // quarter the 32 loads sit in one basic block, so they are in flight
+  // together rather than in dependent rounds
+  float part[32];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int t = t0 + u;
-      const int tok = t < top ? uc[0][t] : -1;
-      const bool ok = okp && tok >= 0 && tok < vocab;
-      part[u] = 0.f;
+  for (int u = 0; u < 32; ++u) part[u] = 0.f;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int q = lane + 64 * c;
-        if (ok && q < rank) part[u] += pc[c] * (float)cbook[(size_t)tok * rank + q];
-      }
-    }
+  for (int c = 0; c < 4; ++c) {
+    if (64 * c >= rank) break;
+    const int q = lane + 64 * c;
+    const bool qok = q < rank;
+    const int qq = qok ? q : 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int t = t0 + u;
-      const float dot = wave_sum(part[u]);
-      if (lane == 0 && t < top) {
-        const int tok = uc[0][t];
-        out[t] = (okp && tok >= 0 && tok < vocab) ? uv[0][t] + dot : -INFINITY;
-      }
+    for (int u = 0; u < 32; ++u) {
+      const int tok = u < top ? uc[0][u] : -1;
+      const bool ok = okp && qok && tok >= 0 && tok < vocab;
+      const float cb = (float)cbook[(size_t)(ok ? tok : 0) * rank + qq];
+      part[u] += ok ? pc[c] * cb : 0.f;
     }
   }
+  // scores in candidate order; lane 0 also keeps the first strictly
+  // largest (candidate 0 when every score is −∞), the chain's choice for
+  // this predecessor
+  float bv = -INFINITY;
+  int bt = 0;
+#pragma unroll
+  for (int u = 0; u < 32; ++u) {
+    if (u >= top) break;
+    const float dot = wave_sum(part[u]);
+    const int tok = uc[0][u];
+    const float sc = (okp && tok >= 0 && tok < vocab) ? uv[0][u] + dot : -INFINITY;
+    if (sc > bv) {
+      bv = sc;
+      bt = u;
+    }
+    if (lane == 0) out[u] = sc;
+  }
+  if (lane == 0) best[trow] = bt;
 }
 
-// The chain: row by row, the first candidate with the largest score under
-// the predecessor chosen before it. The score table is staged in LDS by the
-// whole block (its 16-byte loads issued together), then wave 0 walks the
-// rows: lane t holds candidate t of the current row (top ≤ 64), and an
-// arg-max over the lanes (the smaller candidate index among equal scores)
-// picks the row's choice.
+// The chain: row by row, the candidate chosen under the predecessor chosen
+// before it. k_pairs already found each (row, predecessor) table row's
+// first largest score, so the walk is a chase through that small index
+// table in LDS (one thread); then the block copies each row's scores under
+// its predecessor and writes the chosen tokens.
 __global__ __launch_bounds__(kThreads) void k_chain(const float* __restrict__ tab,
+                                                    const int* __restrict__ best,
                                                     const int* __restrict__ cand, int k, int top,
                                                     int tpn, float* __restrict__ score,
                                                     int* __restrict__ chosen) {
-  extern __shared__ float4 lt4[];
-  const float* lt = reinterpret_cast<const float*>(lt4);
-  const int total = top + (k - 1) * tpn * top;
-  const int n4 = (total + 3) / 4;
-  const float4* t4 = reinterpret_cast<const float4*>(tab);
-#pragma unroll 4
-  for (int e = threadIdx.x; e < n4; e += kThreads) lt4[e] = t4[e];
+  extern __shared__ int lb[];  // best [1 + (k−1)·tpn], then the walk: table row, choice per row
+  const int nb = 1 + (k - 1) * tpn;
+  int* lrow = lb + nb;
+  int* lch = lrow + k;
+  for (int e = threadIdx.x; e < nb; e += kThreads) lb[e] = best[e];
   __syncthreads();
-  if (threadIdx.x >= 64) return;
-  const int lane = threadIdx.x;
-  int tp = 0;
-  for (int j = 0; j < k; ++j) {
-    const float* row = lt + (j == 0 ? 0 : top + ((size_t)(j - 1) * tpn + tp) * top);
-    const float v = lane < top ? row[lane] : -INFINITY;
-    if (lane < top) score[(size_t)j * top + lane] = v;
-    // first strictly largest: compare (v, lane) with the smaller lane winning ties;
-    // lanes ≥ top never win (candidate 0 wins an all −∞ row)
-    float bv = v;
-    int bl = lane < top ? lane : 64;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float v2 = __shfl_xor(bv, o, 64);
-      const int l2 = __shfl_xor(bl, o, 64);
-      if (v2 > bv || (v2 == bv && l2 < bl)) {
-        bv = v2;
-        bl = l2;
-      }
+  if (threadIdx.x == 0) {
+    int tp = 0;
+    for (int j = 0; j < k; ++j) {
+      const int row = j == 0 ? 0 : 1 + (j - 1) * tpn + tp;
+      const int t = lb[row];
+      lrow[j] = row;
+      lch[j] = t;
+      tp = tpn == 1 ? 0 : t;
     }
-    if (lane == 0) chosen[j] = cand[(size_t)j * top + bl];
-    tp = tpn == 1 ? 0 : bl;
   }
+  __syncthreads();
+  for (int e = threadIdx.x; e < k * top; e += kThreads) {
+    const int j = e / top, t = e - j * top;
+    score[e] = tab[(size_t)lrow[j] * top + t];
+  }
+  if (threadIdx.x < k) chosen[threadIdx.x] = cand[(size_t)threadIdx.x * top + lch[threadIdx.x]];
 }
 
 // --------------------------------------------------------------- debug
@@ -1342,9 +1447,10 @@ void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa, l
 }
 
 void rowsum_sq(hipStream_t st, const float* part, int splits, long ss, int rows, int N,
-               float* out, float* sqp) {
+               const float* w, uint16_t* xa, float* sqp) {
   const int nch = cdiv(N, kChunk);
-  k_rowsum_sq<<<dim3(nch, rows), kThreads, 0, st>>>(part, splits, ss, N, out, sqp, nch);
+  k_rowsum_sq<<<dim3(nch, rows), kThreads, 0, st>>>(part, splits, ss, N, w,
+                                                    reinterpret_cast<f16*>(xa), sqp, nch);
 }
 
 // Probe launches; the caller times them (one workgroup of 256 threads is
@@ -1366,26 +1472,28 @@ void norm_apply(hipStream_t st, const float* h, const float* sqp, int nchunk, in
 }
 
 void embed(hipStream_t st, const uint16_t* emb, int anchor, int mask, int rows, int hs, float* h,
-           float* sqp) {
+           float* sqp, const float* w, uint16_t* xa, long ps) {
   const int nch = cdiv(hs, kChunk);
   k_embed<<<dim3(nch, rows), kThreads, 0, st>>>(reinterpret_cast<const f16*>(emb), anchor, mask,
-                                                hs, h, sqp, nch);
+                                                hs, h, sqp, nch, w, reinterpret_cast<f16*>(xa), ps);
 }
 
-void conv0(hipStream_t st, const float* x, const float* dpart, int splits, long ss,
-           const float* base, int rows, int hs, int gs, int kn, uint16_t* xca, long ps,
-           float* dsum) {
+void conv0(hipStream_t st, const float* h, const float* sqp, int nchunk, const float* w, float eps,
+           const float* dpart, int splits, long ss, const float* base, int rows, int hs, int gs,
+           int kn, uint16_t* xca, long ps, float* dsum) {
   const int G = hs / gs, gpw = std::max(1, kChunk / gs);
   const size_t lds = sizeof(float) * 2 * kn * gpw;
-  k_conv0<<<dim3(cdiv(G, gpw), rows), kThreads, lds, st>>>(x, dpart, splits, ss, base, hs, gs, kn,
-                                                          gpw, reinterpret_cast<f16*>(xca), ps,
-                                                          dsum);
+  k_conv0<<<dim3(cdiv(G, gpw), rows), kThreads, lds, st>>>(h, sqp, nchunk, w, eps, dpart, splits,
+                                                          ss, base, hs, gs, kn, gpw,
+                                                          reinterpret_cast<f16*>(xca), ps, dsum);
 }
 
 void conv1(hipStream_t st, float* h, const float* opart, int splits, long ss, const float* dsum,
-           const float* base, int rows, int hs, int gs, int kn, float* sqp) {
+           const float* base, int rows, int hs, int gs, int kn, float* sqp, const float* w,
+           uint16_t* xa, long ps) {
   const int nch = conv1_chunks(hs);
-  k_conv1<<<nch, kC1 * 16, 0, st>>>(h, opart, splits, ss, dsum, base, rows, hs, gs, kn, sqp, nch);
+  k_conv1<<<nch, kC1 * 16, 0, st>>>(h, opart, splits, ss, dsum, base, rows, hs, gs, kn, sqp, nch,
+                                    w, reinterpret_cast<f16*>(xa), ps);
 }
 
 void qkv_post(hipStream_t st, const float* part, int splits, long ss, int rows, int nh, int kv,
@@ -1398,10 +1506,10 @@ void qkv_post(hipStream_t st, const float* part, int splits, long ss, int rows, 
 
 void settle_kv(hipStream_t st, const float* part, int splits, long ss, int rows, int layers,
                int kv, int hd, const float* k_norm, const float* inv, const int* rot, long pos0,
-               float eps, float* sk, float* sv, long cap, long row0) {
+               float eps, const float* sqp, int hs, float* sk, float* sv, long cap, long row0) {
   dim3 grid(rows, layers, 2 * kv);
   k_settle_kv<<<grid, 64, 0, st>>>(part, splits, ss, layers, kv, hd, k_norm, inv, rot, pos0, eps,
-                                   sk, sv, cap, row0);
+                                   sqp, cdiv(hs, kChunk), hs, sk, sv, cap, row0);
 }
 
 int topk_slices(int width) { return cdiv(width, 64 * kSliceVPL); }
@@ -1419,15 +1527,15 @@ void select_all(hipStream_t st, const float* logits, bool have_gmax, int k, int 
   if (!have_gmax)
     k_rowmax<<<dim3(ngroups, k), kThreads, 0, st>>>(logits, width, ngroups, sc.gmax, sc.counters);
   k_thresh<<<k, kThreads, 0, st>>>(sc.gmax, ngroups, top, sc.thr);
-  k_collect<<<dim3(cdiv(ns, 4), k), kThreads, 0, st>>>(logits, width, top, ns, sc.thr, sc.counters,
-                                                       sc.lv, sc.li, cap);
+  k_collect<<<dim3(cdiv(ns, 4), k), kThreads, 0, st>>>(logits, width, top, ns, sc.thr, sc.gmax,
+                                                       ngroups, sc.counters, sc.lv, sc.li, cap);
   const int tpn = forced ? 1 : top;
   k_pairs<<<dim3(k, tpn), 128, 0, st>>>(sc.lv, sc.li, sc.counters, cap, top, hp, rank,
                                         reinterpret_cast<const f16*>(pbook),
                                         reinterpret_cast<const f16*>(cbook), vocab, anchor,
-                                        forced, cand, unary, sc.tab);
-  const size_t lds = sizeof(float) * ((size_t)(top + (k - 1) * tpn * top + 3) / 4 * 4);
-  k_chain<<<1, kThreads, lds, st>>>(sc.tab, cand, k, top, tpn, score, chosen);
+                                        forced, cand, unary, sc.tab, sc.best);
+  const size_t lds = sizeof(int) * ((size_t)(1 + (k - 1) * tpn) + 2 * k);
+  k_chain<<<1, kThreads, lds, st>>>(sc.tab, sc.best, cand, k, top, tpn, score, chosen);
 }
 
 void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,

@@ -247,21 +247,32 @@ __global__ __launch_bounds__(64 * NW) void k_glu_block(const f16* __restrict__ x
 
 static inline unsigned cdiv(long a, long b) { return (unsigned)((a + b - 1) / b); }
 
-// tiles per workgroup and spans per split of k_i4_block
-static constexpr int kBlkR = 2, kBlkNW = 4;
+// waves per workgroup of k_i4_block; tiles a wave (R) and spans a split
+// (ks) are the caller's
+static constexpr int kBlkNW = 4;
 
 int i4_block_splits(int K, int ks) { return (int)cdiv(K / 128, ks); }
 
+template <int R, int KS>
+static void launch_i4_block(hipStream_t st, const f16* x, long ps, int K, const uint4* c,
+                            const uint2* s, TileMap map, int N, float* out, long ss) {
+  const dim3 grid(cdiv(map.ntiles, R * kBlkNW), i4_block_splits(K, KS));
+  k_i4_block<R, kBlkNW, KS><<<grid, 64 * kBlkNW, 0, st>>>(x, ps, K, c, s, map, N, out, ss);
+}
+
 void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
-                   const uint16_t* scales, TileMap map, int N, int ks, float* out, long ss) {
-  const dim3 grid(cdiv(map.ntiles, kBlkR * kBlkNW), i4_block_splits(K, ks));
+                   const uint16_t* scales, TileMap map, int N, int ks, float* out, long ss, int R) {
   const f16* x = reinterpret_cast<const f16*>(xa);
   const uint4* c = reinterpret_cast<const uint4*>(codes);
   const uint2* s = reinterpret_cast<const uint2*>(scales);
-  if (ks == 2)
-    k_i4_block<kBlkR, kBlkNW, 2><<<grid, 64 * kBlkNW, 0, st>>>(x, ps, K, c, s, map, N, out, ss);
-  else
-    k_i4_block<kBlkR, kBlkNW, 4><<<grid, 64 * kBlkNW, 0, st>>>(x, ps, K, c, s, map, N, out, ss);
+  if (R == 4) {
+    if (ks == 2) launch_i4_block<4, 2>(st, x, ps, K, c, s, map, N, out, ss);
+    else launch_i4_block<4, 4>(st, x, ps, K, c, s, map, N, out, ss);
+  } else {
+    if (ks == 2) launch_i4_block<2, 2>(st, x, ps, K, c, s, map, N, out, ss);
+    else if (ks == 8) launch_i4_block<2, 8>(st, x, ps, K, c, s, map, N, out, ss);
+    else launch_i4_block<2, 4>(st, x, ps, K, c, s, map, N, out, ss);
+  }
 }
 
 
