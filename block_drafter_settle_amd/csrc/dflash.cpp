@@ -27,9 +27,9 @@ constexpr int kSettleRows = 256;     // rows one settle pass takes
 constexpr int kTargetBlocks = 512;   // workgroups a GEMM launch aims for (256 CUs)
 // Row tiles per wave of each product (a workgroup covers 4·R tiles of 16).
 constexpr int kRFc = 2;      // settle's fc, f16
-constexpr int kKsQkv = 2;    // q/k/v, int4: spans (128 columns) per split
+constexpr int kKsQkv = 8;    // q/k/v, int4: spans (128 columns) per split
 constexpr int kKsO = 2;      // o, int4
-constexpr int kKsDown = 4;   // down, int4
+constexpr int kKsDown = 8;   // down, int4
 constexpr int kRQkv = 2;     // their row tiles per wave
 constexpr int kRO = 2;
 constexpr int kRDown = 2;
