@@ -89,18 +89,41 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// Σ_s p[s·ss] over the K splits of a GEMM, four independent chains so the
-// loads are in flight together (fixed order: the same splits give the same sum).
+// Σ_s p[s·ss] over the K splits of a GEMM, in four chains (split s into
+// chain s % 4 for every whole group of four, the rest into chain 0), in a
+// fixed order: the same splits give the same sum. Up to 16 loads are issued
+// before any add, so a sum over ≤ 16 splits costs one memory round trip
+// (a chain of dependent adds would hold each load until the previous one).
 __device__ __forceinline__ float sum_splits(const float* __restrict__ p, int splits, long ss) {
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   int s = 0;
-  for (; s + 4 <= splits; s += 4) {
-    a0 += p[(size_t)s * ss];
-    a1 += p[(size_t)(s + 1) * ss];
-    a2 += p[(size_t)(s + 2) * ss];
-    a3 += p[(size_t)(s + 3) * ss];
+  for (; s + 16 <= splits; s += 16) {
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = p[(size_t)(s + e) * ss];
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      a0 += v[e];
+      a1 += v[e + 1];
+      a2 += v[e + 2];
+      a3 += v[e + 3];
+    }
   }
-  for (; s < splits; ++s) a0 += p[(size_t)s * ss];
+  const int rem = splits - s, full = rem & ~3;
+  float v[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = e < rem ? p[(size_t)(s + e) * ss] : 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; e += 4)
+    if (e < full) {
+      a0 += v[e];
+      a1 += v[e + 1];
+      a2 += v[e + 2];
+      a3 += v[e + 3];
+    }
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if (e >= full && e < rem) a0 += v[e];
   return (a0 + a1) + (a2 + a3);
 }
 

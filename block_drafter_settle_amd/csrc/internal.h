@@ -57,8 +57,8 @@ void gemm_big_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const 
                   long split_stride);
 // The block pass's 16-row int4 GEMM (two planes, ps ≠ 0; skinny.hip):
 // splits of `ks` spans (128 columns) each, i4_block_splits(K, ks) of them;
-// out as gemm_i4. A wave takes R row tiles: (R, ks) is (2, 2), (2, 4),
-// (2, 8), (4, 2) or (4, 4).
+// out as gemm_i4. A wave takes R row tiles: R is 2 with ks 2, 4, 5, 6 or 8,
+// or 4 with ks 2, 4, 5 or 6.
 int i4_block_splits(int K, int ks);
 void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
                    const uint16_t* scales, TileMap map, int N, int ks, float* out,

@@ -24,8 +24,8 @@ namespace dfl {
 
 // ------------------------------------------------------------------ GEMMs
 
-// Skinny GEMM, f16 weights: each wave owns R row tiles over its K split;
-// PL activation planes, plane 1 at xa + ps.
+// Skinny GEMM, f16 weights (read non-temporal: once a pass): each wave owns R
+// row tiles over its K split; PL activation planes, plane 1 at xa + ps.
 template <int R, int PL>
 __global__ __launch_bounds__(kThreads) void k_gemm_f16(const f16* __restrict__ xa, long ps, int K,
                                                        const f16* __restrict__ w, TileMap mp,
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_f16(const f16* __restrict__ x
       a[u] = xp[(size_t)(s + u) * 64];
       if (PL == 2) a2[u] = xq[(size_t)(s + u) * 64];
 #pragma unroll
-      for (int r = 0; r < R; ++r) b[u][r] = wp[r][(size_t)(s + u) * 64];
+      for (int r = 0; r < R; ++r) b[u][r] = ld_stream(&wp[r][(size_t)(s + u) * 64]);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_f16(const f16* __restrict__ x
     if (PL == 2) a2 = xq[(size_t)s * 64];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const h8 b = wp[r][(size_t)s * 64];
+      const h8 b = ld_stream(&wp[r][(size_t)s * 64]);
       acc[r] = mfma16(a, b, acc[r]);
       if (PL == 2) acc[r] = mfma16(a2, b, acc[r]);
     }
@@ -349,10 +349,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa
     h8 a0[4], a1[4], b0[4], b1[4];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      c0[r] = cp[r][(size_t)p * 64];
-      c1[r] = cp[r][(size_t)(p + 1) * 64];
-      s0[r] = scp[r][(size_t)p * 16];
-      s1[r] = scp[r][(size_t)(p + 1) * 16];
+      c0[r] = ld_stream(&cp[r][(size_t)p * 64]);
+      c1[r] = ld_stream(&cp[r][(size_t)(p + 1) * 64]);
+      s0[r] = ld_stream(&scp[r][(size_t)p * 16]);
+      s1[r] = ld_stream(&scp[r][(size_t)(p + 1) * 16]);
     }
     load_span<PL>(xp, xq, p, a0, b0);
     load_span<PL>(xp, xq, p + 1, a1, b1);
@@ -365,8 +365,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa
     h8 a0[4], b0[4];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      c0[r] = cp[r][(size_t)p * 64];
-      s0[r] = scp[r][(size_t)p * 16];
+      c0[r] = ld_stream(&cp[r][(size_t)p * 64]);
+      s0[r] = ld_stream(&scp[r][(size_t)p * 16]);
     }
     load_span<PL>(xp, xq, p, a0, b0);
     i4_span<R, PL>(c0, s0, a0, b0, acc);
@@ -616,8 +616,16 @@ __global__ __launch_bounds__(kThreads) void k_conv0(const float* __restrict__ h,
   // loads are issued ahead of the projection's split sums below (neither
   // waits for the other).
   float q = 0.f;
-  if (wave < taps)
-    for (int c = lane; c < nchunk; c += 64) q += sqp[(size_t)(r - wave) * nchunk + c];
+  if (wave < taps) {
+    // four loads in flight a round (hs/32 ≤ 256 partials take one round)
+    const float* sq = sqp + (size_t)(r - wave) * nchunk;
+    for (int c = lane; c < nchunk; c += 256) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = c + 64 * e < nchunk ? sq[c + 64 * e] : 0.f;
+      q += ((v[0] + v[1]) + v[2]) + v[3];
+    }
+  }
   // the first channel of this thread: its rows, base taps and gain, loaded
   // ahead of the barriers
   constexpr int kPre = 4;
@@ -1191,7 +1199,7 @@ __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
   for (int u = 0; u < 32; ++u) part[u] = 0.f;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    if (64 * c >= rank) break;
+    if (64 * c >= rank) continue;  // uniform
     const int q = lane + 64 * c;
     const bool qok = q < rank;
     const int qq = qok ? q : 0;
@@ -1360,8 +1368,10 @@ static void pick_f16(hipStream_t st, int R, const uint16_t* xa, long ps, int K, 
     launch_f16<1, PL>(st, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
   else if (R == 2)
     launch_f16<2, PL>(st, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
-  else
+  else if (R == 4)
     launch_f16<4, PL>(st, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
+  else
+    launch_f16<8, PL>(st, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
 }
 
 void gemm_f16(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblocks,

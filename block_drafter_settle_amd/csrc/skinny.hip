@@ -266,12 +266,20 @@ void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uin
   const uint4* c = reinterpret_cast<const uint4*>(codes);
   const uint2* s = reinterpret_cast<const uint2*>(scales);
   if (R == 4) {
-    if (ks == 2) launch_i4_block<4, 2>(st, x, ps, K, c, s, map, N, out, ss);
-    else launch_i4_block<4, 4>(st, x, ps, K, c, s, map, N, out, ss);
+    switch (ks) {
+      case 2: launch_i4_block<4, 2>(st, x, ps, K, c, s, map, N, out, ss); break;
+      case 5: launch_i4_block<4, 5>(st, x, ps, K, c, s, map, N, out, ss); break;
+      case 6: launch_i4_block<4, 6>(st, x, ps, K, c, s, map, N, out, ss); break;
+      default: launch_i4_block<4, 4>(st, x, ps, K, c, s, map, N, out, ss); break;
+    }
   } else {
-    if (ks == 2) launch_i4_block<2, 2>(st, x, ps, K, c, s, map, N, out, ss);
-    else if (ks == 8) launch_i4_block<2, 8>(st, x, ps, K, c, s, map, N, out, ss);
-    else launch_i4_block<2, 4>(st, x, ps, K, c, s, map, N, out, ss);
+    switch (ks) {
+      case 2: launch_i4_block<2, 2>(st, x, ps, K, c, s, map, N, out, ss); break;
+      case 5: launch_i4_block<2, 5>(st, x, ps, K, c, s, map, N, out, ss); break;
+      case 6: launch_i4_block<2, 6>(st, x, ps, K, c, s, map, N, out, ss); break;
+      case 8: launch_i4_block<2, 8>(st, x, ps, K, c, s, map, N, out, ss); break;
+      default: launch_i4_block<2, 4>(st, x, ps, K, c, s, map, N, out, ss); break;
+    }
   }
 }
 
