@@ -79,22 +79,25 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
   // dims in one store; two register sets hold the next two 32-key steps
   // while one is computed
   const int kp = threadIdx.x & 15, d0 = (threadIdx.x >> 4) * DPT;
+  // Keys past the chunk's end read the chunk's last row instead (their
+  // scores are masked, so they weigh 0 against finite values): no load sits
+  // in a branch, and the loads of the steps ahead stay in flight across the
+  // LDS-only barriers below.
   auto fetch = [&](int k0, float4 (&kreg)[EPT / 4], float4 (&vreg)[EPT / 4]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int key = k0 + 2 * kp + h;
-      const bool ok = key < count;
+      const int key = min(k0 + 2 * kp + h, count - 1);
       const float4* kpn = reinterpret_cast<const float4*>(kbase + (size_t)key * kd + d0);
       const float4* vpn = reinterpret_cast<const float4*>(vbase + (size_t)key * kd + d0);
 #pragma unroll
       for (int e = 0; e < DPT / 4; ++e) {
-        kreg[h * (DPT / 4) + e] = ok ? kpn[e] : make_float4(0.f, 0.f, 0.f, 0.f);
-        vreg[h * (DPT / 4) + e] = ok ? vpn[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+        kreg[h * (DPT / 4) + e] = kpn[e];
+        vreg[h * (DPT / 4) + e] = vpn[e];
       }
     }
   };
   auto stage = [&](const float4 (&kreg)[EPT / 4], const float4 (&vreg)[EPT / 4]) {
-    __syncthreads();
+    lds_barrier();
     f16 vh[2][DPT], vl[2][DPT];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
       *reinterpret_cast<h2*>(&Vt[0][(d0 + e) * VST + 2 * kp]) = (h2){vh[0][e], vh[1][e]};
       *reinterpret_cast<h2*>(&Vt[1][(d0 + e) * VST + 2 * kp]) = (h2){vl[0][e], vl[1][e]};
     }
-    __syncthreads();
+    lds_barrier();
   };
   auto compute = [&](int k0) {
     // scores: st[h][v] = S^T[key 16h + 4j + v][query r]
@@ -187,16 +190,19 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
       acc[d] = mfma16(vl, pb, t);
     }
   };
+  // 64 keys a round, in two 32-key steps, each fetched two steps ahead. A
+  // step wholly past the chunk's end changes nothing: its scores are all
+  // masked, so the correction factor is exactly 1 and P is 0.
   float4 ka[EPT / 4], va[EPT / 4], kb2[EPT / 4], vb2[EPT / 4];
-  if (count > 0) fetch(0, ka, va);
-  if (count > 32) fetch(32, kb2, vb2);
-  for (int k0 = 0; k0 < count; k0 += 64) {
-    stage(ka, va);
-    if (k0 + 64 < count) fetch(k0 + 64, ka, va);
-    compute(k0);
-    if (k0 + 32 < count) {
+  if (count > 0) {
+    fetch(0, ka, va);
+    fetch(32, kb2, vb2);
+    for (int k0 = 0; k0 < count; k0 += 64) {
+      stage(ka, va);
+      fetch(k0 + 64, ka, va);
+      compute(k0);
       stage(kb2, vb2);
-      if (k0 + 96 < count) fetch(k0 + 96, kb2, vb2);
+      fetch(k0 + 96, kb2, vb2);
       compute(k0 + 32);
     }
   }
