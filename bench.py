@@ -225,6 +225,9 @@ def main():
     settle_call_us = sum(v[0] for n, v in st_settle.items() if n.startswith("settle")) / n_settles
 
     stages = {n: round(st_stream[n][0] / n_blocks, 2) for n in block_stages}
+    # the stream's own 8-row settles, per call
+    stages["stream_settle"] = round(sum(v[0] for n, v in st_stream.items() if n.startswith("settle"))
+                                    / max(n_str_settles, 1), 2)
     stages.update({n: round(st_settle[n][0] / n_settles, 2) for n in st_settle
                    if n.startswith("settle")})
     res = {
