@@ -181,6 +181,17 @@ def main():
     torch.cuda.synchronize()
     w2_us = (time.perf_counter() - t0) / n2 * 1e6
     del out2
+    # blocks alone at the full width over the same stretch: the block pass's
+    # own throughput, with no settle between blocks and no stage timers
+    for i in range(5):
+        d.block(anchors[i], pos, k, width, *ptrs)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n2):
+        d.block(anchors[i], pos, k, width, *ptrs)
+    torch.cuda.synchronize()
+    bo_us = (time.perf_counter() - t0) / n2 * 1e6
+    pos_bo = pos
 
     # stage timers over a further stretch of the stream
     d.set_timing(True)
@@ -202,15 +213,18 @@ def main():
     ffn = g["intermediate"]
     i4 = L * (qd * hs + 2 * kd * hs + hs * qd + 3 * ffn * hs) * (0.5 + 2 / 32)
     kproj = L * 2 * (2 * g["conv_kernel"] * hs // g["conv_group"]) * hs * 2
-    a_end = pos
-    kv_rows = 0
-    for l in range(L):
-        wdw = g["windows"][l]
-        hi = a_end
-        lo = max(0, a_end + 1 - wdw) if wdw > 0 else 0
-        kv_rows += hi - lo
-    block_bytes = (i4 + kproj + head_bytes + kv_rows * kd * 4 * 2 +
-                   k * (1 + top) * g["selector_rank"] * 2 + 2 * hs * 2)
+    def block_bytes_at(a_end):
+        kv_rows = 0
+        for l in range(L):
+            wdw = g["windows"][l]
+            lo = max(0, a_end + 1 - wdw) if wdw > 0 else 0
+            kv_rows += a_end - lo
+        return (i4 + kproj + head_bytes + kv_rows * kd * 4 * 2 +
+                k * (1 + top) * g["selector_rank"] * 2 + 2 * hs * 2)
+    block_bytes = block_bytes_at(pos)
+    bo_bytes = block_bytes_at(pos_bo)
+    # the same blocks with the head over the first 65536 columns
+    w2_bytes = bo_bytes - head_bytes + (w2 * hs * 2 + g["selector_rank"] * hs * 2 + k * w2 * 4)
     # settle: the fc GEMM's flops per 256-row launch
     fc_us = st_settle["settle_fc"][0] / st_settle["settle_fc"][1]
     fc_flops = 2.0 * 256 * tw * hs
@@ -254,10 +268,13 @@ def main():
             "settle_rows_per_step": per_step,
         },
         "block_only": {
-            "blocks_per_s": round(1e6 / block_us, 1),
-            "us_per_block": round(block_us, 1),
-            "algorithmic_bytes": int(block_bytes),
-            "hbm_frac": round(block_bytes / (block_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "blocks_per_s": round(1e6 / bo_us, 1),
+            "us_per_block": round(bo_us, 1),
+            "algorithmic_bytes": int(bo_bytes),
+            "hbm_frac": round(bo_bytes / (bo_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "blocks alone at the full width, back to back (no settle between, no "
+                    "stage timers); stage_timer_us is the same pass under per-kernel events",
+            "stage_timer_us": round(block_us, 1),
         },
         "roofline": {
             "kernel": "k_head (head logits over the vocabulary + selector projection)",
@@ -295,9 +312,8 @@ def main():
         "stages_us": stages,
         "block_width_65536": {
             "blocks_per_s": round(1e6 / w2_us, 1), "us_per_block": round(w2_us, 1),
-            "algorithmic_bytes": int(block_bytes - head_bytes + (w2 * hs * 2 + g["selector_rank"] * hs * 2 + k * w2 * 4)),
-            "hbm_frac": round((block_bytes - head_bytes + (w2 * hs * 2 + g["selector_rank"] * hs * 2 + k * w2 * 4))
-                              / (w2_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": int(w2_bytes),
+            "hbm_frac": round(w2_bytes / (w2_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "note": "blocks alone (no settle), head and selection over the first 65536 columns"},
         "median_us": {"stream_step": round(step_med_us, 2),
                       "settle_call": round(settle_call_med_us, 2)},

@@ -557,7 +557,6 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   if (!rc) rc = dev_alloc(d, &d->logits, (size_t)16 * d->V, "logits");
   if (!rc) rc = dev_alloc(d, &d->hp, 16 * d->rank, "selector projection");
   if (!rc) rc = dev_alloc(d, &d->sel_sc.gmax, (size_t)16 * ((d->V + 255) / 256), "selection");
-  if (!rc) rc = dev_alloc(d, &d->sel_sc.thr, 16, "selection");
   if (!rc) rc = dev_alloc(d, &d->sel_sc.counters, 16, "selection");
   if (!rc) rc = dev_alloc(d, &d->sel_sc.lv, 16 * sel_cap, "selection candidates");
   if (!rc) rc = dev_alloc(d, &d->sel_sc.li, 16 * sel_cap, "selection candidates");

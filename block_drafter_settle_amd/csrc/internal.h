@@ -99,7 +99,6 @@ void gemm_glu_stream(hipStream_t st, const uint16_t* xa, long ps, int K, const u
 // score table tab [top·(1 + 15·top)].
 struct SelectScratch {
   float* gmax;
-  float* thr;
   int* counters;
   float* lv;
   int* li;

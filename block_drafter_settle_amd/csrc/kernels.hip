@@ -913,12 +913,13 @@ __device__ void wave_select(float (&v)[VPL], int (&ix)[VPL], int want, float* ou
   }
 }
 
-// Selection of the top `top` logits of a row, exactly, in three steps:
-//   k_thresh   T = the top-th largest of the row's 256-column maxima; at
+// Selection of the top `top` logits of a row, exactly, in two launches:
+//   k_collect  T = the top-th largest of the row's 256-column maxima (at
 //              least `top` logits are ≥ T, and only the < top column groups
-//              whose maximum exceeds T can hold logits > T;
-//   k_collect  every logit > T, and of the logits equal to T the first `top`
-//              by index in each 2048-column slice, into the row's list;
+//              whose maximum exceeds T can hold logits > T), found by every
+//              workgroup of the row alike; then every logit > T, and of the
+//              logits equal to T the first `top` by index in each
+//              2048-column slice, into the row's list;
 //   k_pairs    the exact top `top` of that list (it holds the row's top
 //              `top` by construction), then the selector's scores.
 static constexpr int kSliceVPL = 32;  // a collect wave covers 64·32 = 2048 columns
@@ -950,27 +951,24 @@ __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// T of each row: the top-th largest of its ngroups column-group maxima, by a
+// T of a row: the top-th largest of its ngroups column-group maxima, by a
 // radix select over the maxima's order keys, eight bits a pass from the top:
-// each pass counts the candidates still matching the chosen prefix per
-// next byte, and a suffix scan over the 256 counts picks the byte holding
-// the top-th largest. One workgroup per row.
+// each pass counts the candidates still matching the chosen prefix per next
+// byte, and a suffix scan over the 256 counts picks the byte holding the
+// top-th largest. All kThreads threads of the block call it; every thread
+// gets T.
 static constexpr int kThreshPer = 8;  // maxima per thread: ngroups ≤ 2048
-__global__ __launch_bounds__(kThreads) void k_thresh(const float* __restrict__ gmax, int ngroups,
-                                                     int top, float* __restrict__ thr) {
+__device__ float row_threshold(const float* __restrict__ gm, int ngroups, int top) {
   __shared__ int hist[256];
   __shared__ int wsum[4];
   __shared__ uint32_t sel[2];  // chosen byte, rank still wanted inside it
-  const int j = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  if (ngroups < top) {  // fewer groups than candidates: every logit is one
-    if (t == 0) thr[j] = -INFINITY;
-    return;
-  }
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (ngroups < top) return -INFINITY;  // fewer groups than candidates: every logit is one
   uint32_t key[kThreshPer];
 #pragma unroll
   for (int u = 0; u < kThreshPer; ++u) {
     const int e = t + kThreads * u;
-    key[u] = e < ngroups ? order_key(gmax[(size_t)j * ngroups + e]) : 0u;
+    key[u] = e < ngroups ? order_key(gm[e]) : 0u;
   }
   uint32_t prefix = 0, mask = 0;
   int want = top;  // rank (1-based) of the wanted key among those matching prefix
@@ -1005,7 +1003,7 @@ __global__ __launch_bounds__(kThreads) void k_thresh(const float* __restrict__ g
     want = (int)sel[1];
     __syncthreads();
   }
-  if (t == 0) thr[j] = key_float(prefix);
+  return key_float(prefix);
 }
 
 // Append (value, index) for the lanes with `take`, in lane order, to row j's list.
@@ -1026,15 +1024,16 @@ __device__ __forceinline__ void append(bool take, float v, int idx, int* counter
 
 __global__ __launch_bounds__(kThreads) void k_collect(const float* __restrict__ logits, int width,
                                                       int top, int nslices,
-                                                      const float* __restrict__ thr,
                                                       const float* __restrict__ gmax, int ngroups,
                                                       int* __restrict__ counters,
                                                       float* __restrict__ lv, int* __restrict__ li,
                                                       int cap) {
   const int lane = threadIdx.x & 63, j = blockIdx.y;
   const int sl = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // every workgroup of row j finds the same T (the whole block, before any
+  // wave leaves)
+  const float T = row_threshold(gmax + (size_t)j * ngroups, ngroups, top);
   if (sl >= nslices) return;
-  const float T = thr[j];
   // a slice whose 256-column groups all peak below T holds no logit ≥ T:
   // skip it without reading its logits
   constexpr int kGroups = 64 * kSliceVPL / 256;
@@ -1536,9 +1535,8 @@ void select_all(hipStream_t st, const float* logits, bool have_gmax, int k, int 
   const int ngroups = cdiv(width, 256), ns = topk_slices(width), cap = topk_cap(width, top);
   if (!have_gmax)
     k_rowmax<<<dim3(ngroups, k), kThreads, 0, st>>>(logits, width, ngroups, sc.gmax, sc.counters);
-  k_thresh<<<k, kThreads, 0, st>>>(sc.gmax, ngroups, top, sc.thr);
-  k_collect<<<dim3(cdiv(ns, 4), k), kThreads, 0, st>>>(logits, width, top, ns, sc.thr, sc.gmax,
-                                                       ngroups, sc.counters, sc.lv, sc.li, cap);
+  k_collect<<<dim3(cdiv(ns, 4), k), kThreads, 0, st>>>(logits, width, top, ns, sc.gmax, ngroups,
+                                                       sc.counters, sc.lv, sc.li, cap);
   const int tpn = forced ? 1 : top;
   k_pairs<<<dim3(k, tpn), 128, 0, st>>>(sc.lv, sc.li, sc.counters, cap, top, hp, rank,
                                         reinterpret_cast<const f16*>(pbook),
