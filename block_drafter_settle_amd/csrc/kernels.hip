@@ -193,8 +193,8 @@ __global__ __launch_bounds__(64 * kBigWaves) void k_gemm_big_f16(const f16* __re
 
 // The settle's keys and values at many rows, straight from the int4 codes
 // (Wk/Wv of every layer): the block layout of k_gemm_big_f16 (256 rows,
-// 16 weight tiles, eight waves, wave w on row blocks 4(w%4)..+3 and tiles
-// 8(w/4)..+7), with each weight fragment decoded in registers into two
+// 16 weight tiles, eight waves; here wave w multiplies all 16 row blocks by
+// tiles 2w and 2w + 1), with each weight fragment decoded in registers into two
 // exact f16 halves: hi = f16(q·s) (a packed f16 product, rounded once) and
 // lo = q·s − hi (a packed f16 FMA; exact, since q·s has at most 15
 // significant bits and the residual is a multiple of the scale's ulp). The
@@ -206,6 +206,13 @@ __global__ __launch_bounds__(64 * kBigWaves) void k_gemm_big_f16(const f16* __re
 //    ahead; each step reads its code word and scale of every tile.
 // Splits fall on span boundaries, so every step of a split is a real one.
 static constexpr int kKvNT = 16, kKvStages = 3;
+// row blocks and weight tiles a wave multiplies (kKvRB·kKvTW = 32 of the
+// block's 16 × 16): each of the block's tiles is decoded by 16/kKvRB waves.
+// Every row block a wave and two tiles each, so that each tile is decoded
+// once: measured 66 → 64 µs a 256-row call against four row blocks × eight
+// tiles (each tile decoded by four waves) and 64 µs for eight × four.
+static constexpr int kKvRB = 16, kKvTW = 2;
+static_assert(kKvRB * kKvTW == 32 && 16 % kKvRB == 0, "eight waves cover 16 row blocks x 16 tiles");
 
 __global__ __launch_bounds__(64 * kBigWaves) void k_gemm_kv_i4(const f16* __restrict__ xa, int K,
                                                               int mblocks,
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(64 * kBigWaves) void k_gemm_kv_i4(const f16* __rest
   __shared__ uint32_t sst[2][kKvNT][32];  // scales of a span: tile, (n, pair)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rw = wave & 3, cw = wave >> 2;
+  const int rw = wave % (16 / kKvRB), cw = wave / (16 / kKvRB);
   const int KT = K >> 7;
   const int sp = blockIdx.x % splits;
   const int p0 = sp * sps, p1 = min(KT, p0 + sps);
@@ -251,11 +258,11 @@ __global__ __launch_bounds__(64 * kBigWaves) void k_gemm_kv_i4(const f16* __rest
       __builtin_amdgcn_global_load_lds(csrc[i] + (size_t)pc * 64, &cst[p & 1][2 * wave + i][0], 16, 0, 2);
     __builtin_amdgcn_global_load_lds(ssrc + (size_t)pc * 32, &sst[p & 1][2 * wave][0], 4, 0, 0);
   };
-  f4 acc[4][8];
+  f4 acc[kKvRB][kKvTW];
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int b = 0; b < kKvRB; ++b)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[b][t] = (f4){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < kKvTW; ++t) acc[b][t] = (f4){0.f, 0.f, 0.f, 0.f};
   issue_c(p0);
   issue_a(4 * p0);
   issue_a(4 * p0 + 1);
@@ -275,14 +282,14 @@ __global__ __launch_bounds__(64 * kBigWaves) void k_gemm_kv_i4(const f16* __rest
       lds_barrier();
       issue_a(s + D);
       if (u == 0) issue_c(p + 1);
-      h8 af[4];
+      h8 af[kKvRB];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) af[b] = ast[s % kKvStages][rw * 4 + b][lane];
+      for (int b = 0; b < kKvRB; ++b) af[b] = ast[s % kKvStages][rw * kKvRB + b][lane];
       // this step's code word and scale of each tile, read from the span's
       // buffers (rewritten only after the span's last step)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int tile = cw * 8 + t;
+      for (int t = 0; t < kKvTW; ++t) {
+        const int tile = cw * kKvTW + t;
         const uint32_t word = cw32[(((size_t)(p & 1) * kKvNT + tile) * 64 + lane) * 4 + u];
         const uint32_t sb = sst[p & 1][tile][2 * n + (u >> 1)];
         const f16 sh = __builtin_bit_cast(f16, (uint16_t)((u & 1) ? (sb >> 16) : (sb & 0xffffu)));
@@ -291,12 +298,13 @@ __global__ __launch_bounds__(64 * kBigWaves) void k_gemm_kv_i4(const f16* __rest
         const h8 hi = q * s8;
         const h8 lo = __builtin_elementwise_fma(q, s8, -hi);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < kKvRB; ++b) {
           acc[b][t] = mfma16(af[b], hi, acc[b][t]);
           acc[b][t] = mfma16(af[b], lo, acc[b][t]);
         }
-        // keep each tile's decode beside its products: decoded halves of all
-        // eight tiles at once would not fit two waves a SIMD
+        // keep each tile's decode beside its products (the decoded halves of
+        // all of a wave's tiles at once need more registers than two waves a
+        // SIMD leave)
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -304,12 +312,12 @@ __global__ __launch_bounds__(64 * kBigWaves) void k_gemm_kv_i4(const f16* __rest
   const int j = lane >> 4;
   float* o = out + (size_t)sp * split_stride;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int mb = rw * 4 + b;
+  for (int b = 0; b < kKvRB; ++b) {
+    const int mb = rw * kKvRB + b;
     if (mb >= mblocks) continue;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int tt = t0 + cw * 8 + t, col = tt * 16 + n;
+    for (int t = 0; t < kKvTW; ++t) {
+      const int tt = t0 + cw * kKvTW + t, col = tt * 16 + n;
       if (tt < mp.ntiles && col < N)
 #pragma unroll
         for (int v = 0; v < 4; ++v) o[(size_t)(mb * 16 + 4 * j + v) * N + col] = acc[b][t][v];
