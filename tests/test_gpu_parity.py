@@ -215,6 +215,13 @@ BLOCK_CASES = [
     # 64 context chunks + the block's own rows: more chunk states than merge
     # threads at head_dim 64
     (dict(windows=[0, 0], no_rope=[]), (0, 8190), 0, 7, 1000),
+    # conv kernels other than 4 taps: one tap; more taps than the conv
+    # kernels load ahead of their barrier (4), with wider groups; a tap for
+    # every block row
+    (dict(windows=[0, 0], no_rope=[], conv_kernel=1), (0, 50), 0, 7, 1000),
+    (dict(windows=[0, 7], no_rope=[], conv_kernel=6, conv_group=8), (10, 60), 0, 7, 1000),
+    (dict(windows=[0, 0], no_rope=[1], block=16, conv_kernel=16, conv_group=16), (0, 100), 0, 15,
+     1000),
 ]
 
 
