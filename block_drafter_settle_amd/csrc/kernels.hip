@@ -529,8 +529,10 @@ __global__ __launch_bounds__(kThreads) void k_to_a(const float* __restrict__ x, 
 }
 
 // The row kernels below split each row into chunks of kChunk channels, one
-// workgroup per (chunk, row). A norm is two launches: the producer writes
-// the rows and each chunk's sum of squares, `k_norm_apply` finishes `rms`.
+// workgroup per (chunk, row). The producer of a row writes each chunk's sum
+// of squares; `rms` is then finished by its consumer (k_conv0 and
+// k_settle_kv scale the projection of h ⊙ gain) or, for the final norm
+// before the head, by `k_norm_apply`.
 static constexpr int kChunk = 256;
 
 // Split-summed rows (the settle's t = fc·taps), each chunk's Σt², and
