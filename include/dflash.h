@@ -160,7 +160,7 @@ const char* dflash_last_error(const dflash_t* d);
    (and the calls no longer overlap the host). Stages, in order: */
 enum {
   DFLASH_ST_KPROJ = 0,  /* kernel projections (both conv sets), f16 GEMM */
-  DFLASH_ST_CONV,       /* embedding, row convolutions, norms */
+  DFLASH_ST_CONV,       /* embedding, row convolutions (the norms folded in), final norm */
   DFLASH_ST_QKV,        /* q/k/v int4 GEMM */
   DFLASH_ST_QKPOST,     /* q/k norms + rotary */
   DFLASH_ST_ATTN,       /* attention chunks + merge */
@@ -171,7 +171,8 @@ enum {
   DFLASH_ST_SELECT,     /* top-k + selector chain */
   DFLASH_ST_S_TAPS,     /* settle: tap rows to f16 */
   DFLASH_ST_S_FC,       /* settle: fc f16 GEMM */
-  DFLASH_ST_S_NORM,     /* settle: hidden norm */
+  DFLASH_ST_S_NORM,     /* settle: fc split sums + hidden norm input (its scale is applied by
+                           the store stage) */
   DFLASH_ST_S_KV,       /* settle: all layers' K/V int4 GEMM */
   DFLASH_ST_S_STORE,    /* settle: k norm + rotary + store append */
   DFLASH_STAGES
