@@ -1,19 +1,25 @@
 #!/usr/bin/env python
 """Throughput of the DFlash 2 drafter's forward pass on one MI355X.
 
-Workload (synthetic, seeded; weights random-init of the 27B-target-shaped
-sidecar: hidden 5120, intermediate 17408, 5 layers, 32/8 heads, head_dim
-128, vocab 248320, block 16, 5 taps (tap width 25600), windows
-[2048 x4, 0], layer 4 without rotary; int4 q/k/v/o/gate/up/down, f16 fc,
-kernel projections, head, selector):
+Workloads (synthetic, seeded; random-init sidecars of the stated shapes,
+int4 q/k/v/o/gate/up/down, f16 fc, kernel projections, head, selector):
 
-  stream  32768 context positions settled first (untimed); then each step
-          settles the next 8 tap rows and runs one block at the next anchor
-          (k = 15 draft rows, head width = the vocabulary, a uniform anchor
-          token). `value` = steps per second = draft blocks per second,
-          the 8-row settle included.
-  settle  16384 tap rows (N(0,1), 1 % of the channels x20) settled in 64
-          calls of 256 rows: settle rows per second.
+  27b stream (the headline `value`)  the 27B-target-shaped sidecar (hidden
+          5120, intermediate 17408, 5 layers, 32/8 heads, head_dim 128, vocab
+          248320, block 16, 5 taps = tap width 25600, windows [2048 x4, 0],
+          layer 4 without rotary): 32768 context positions settled first
+          (untimed); then each step settles the next 8 tap rows and runs one
+          block at the next anchor (k = 15 draft rows, head width = the
+          vocabulary, a uniform anchor token). `value` = steps per second =
+          draft blocks per second, the 8-row settle included.
+  27b settle  the same sidecar: 16384 tap rows (N(0,1), 1 % of the channels
+          x20) settled in 64 calls of 256 rows: settle rows per second.
+  4b      the Qwen3-4B-shaped sidecar (hidden 2560, intermediate 9728, vocab
+          151936): 4096 rows settled in 16 calls of 256 (timed: rows/s), then
+          200 blocks at a = 4096 (timed: blocks/s).
+  27b long  the 27B sidecar with every window 0, vocab 262144, top 32, rank
+          128: 131071 positions settled (untimed), then 200 steps of one new
+          row settled and one block at a = 131072 + i.
 
 One JSON line on stdout; progress on stderr. Inputs are resident in device
 memory before any timed region. The per-kernel rooflines come from the
@@ -50,6 +56,10 @@ def main():
                          "reference kernel for scaling the HBM byte counters")
     ap.add_argument("--cpu-steps", type=int, default=4,
                     help="stream steps the CPU oracle baseline runs")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 4B and long-context legs")
+    ap.add_argument("--blocks-4b", type=int, default=200)
+    ap.add_argument("--steps-long", type=int, default=200)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -207,22 +217,7 @@ def main():
     # read once, the logits written once
     head_bytes = width * hs * 2 + g["selector_rank"] * hs * 2 + k * width * 4
     head_gbs = head_bytes / (head_us * 1e-6) / 1e9
-    # whole block: int4 weights + scales, f16 kernel projections, head,
-    # selector, visible context K/V, gathered codebook rows, embedding rows
-    qd = g["heads"] * g["head_dim"]
-    ffn = g["intermediate"]
-    i4 = L * (qd * hs + 2 * kd * hs + hs * qd + 3 * ffn * hs) * (0.5 + 2 / 32)
-    kproj = L * 2 * (2 * g["conv_kernel"] * hs // g["conv_group"]) * hs * 2
-    def block_bytes_at(a_end):
-        kv_rows = 0
-        for l in range(L):
-            wdw = g["windows"][l]
-            lo = max(0, a_end + 1 - wdw) if wdw > 0 else 0
-            kv_rows += a_end - lo
-        return (i4 + kproj + head_bytes + kv_rows * kd * 4 * 2 +
-                k * (1 + top) * g["selector_rank"] * 2 + 2 * hs * 2)
-    block_bytes = block_bytes_at(pos)
-    bo_bytes = block_bytes_at(pos_bo)
+    bo_bytes = block_bytes(g, 0, pos_bo, width, k)
     # the same blocks with the head over the first 65536 columns
     w2_bytes = bo_bytes - head_bytes + (w2 * hs * 2 + g["selector_rank"] * hs * 2 + k * w2 * 4)
     # settle: the fc GEMM's flops per 256-row launch
@@ -235,7 +230,7 @@ def main():
     fc_bytes = tw * hs * 2 + 256 * tw * 2 + 256 * hs * 4
     fc_bound = "hbm" if fc_bytes / (HBM_PEAK_GBS * 1e9) >= fc_flops / (F16_MFMA_PEAK_TFS * 1e12) \
         else "mfma"
-    settle_flops = 2.0 * 256 * (tw * hs + L * 2 * kd * hs)
+    call_flops = settle_flops(g, 256)
     settle_call_us = sum(v[0] for n, v in st_settle.items() if n.startswith("settle")) / n_settles
 
     stages = {n: round(st_stream[n][0] / n_blocks, 2) for n in block_stages}
@@ -291,7 +286,7 @@ def main():
             "workload": "27b_settle: 16384 tap rows (1% channels x20) in 64 calls of 256 rows",
             "rows_per_s": round(settle_rows_s, 1),
             "us_per_call": round(settle_call_us, 2),
-            "mfma_frac_call": round(settle_flops / (settle_call_us * 1e-6) / 1e12 /
+            "mfma_frac_call": round(call_flops / (settle_call_us * 1e-6) / 1e12 /
                                     F16_MFMA_PEAK_TFS, 4),
             "roofline": {
                 "kernel": "k_gemm_big_f16 (fc, 256 rows)",
@@ -330,10 +325,204 @@ def main():
     sr["mfma_frac"] = round(sr["tflops"] / F16_MFMA_PEAK_TFS, 4)
     sr["mfma_frac_measured"] = round(sr["tflops"] / mfma_tfs, 4)
 
+    cpu = None
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(g, w, synth, args.cpu_steps)
+        cpu = cpu_baseline(g, w, synth, args.cpu_steps)
     d.close()
+    del w, d
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        res["qwen3_4b"] = leg_4b(pkg, synth, dev, stream, args.blocks_4b)
+        torch.cuda.empty_cache()
+        res["t27b_long"], long_w = leg_long(pkg, synth, dev, stream, args.steps_long)
+        torch.cuda.empty_cache()
+        if cpu is not None:
+            cpu["t27b_long_block"] = cpu_long_block(synth, long_w)
+        del long_w
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
+
+
+def block_bytes(g, first, a, width, k):
+    """Algorithmic bytes of one block at anchor position a over a context
+    starting at `first` (settled through a): int4 weights with their scales,
+    f16 kernel projections, the head rows read and the logits written, the
+    selector projection, the visible K/V rows of every layer, the gathered
+    codebook rows and the two embedding rows."""
+    hs, L = g["hidden"], g["layers"]
+    kd = g["kv_heads"] * g["head_dim"]
+    qd = g["heads"] * g["head_dim"]
+    ffn = g["intermediate"]
+    rank, top = g["selector_rank"], g["selector_top"]
+    i4 = L * (qd * hs + 2 * kd * hs + hs * qd + 3 * ffn * hs) * (0.5 + 2 / 32)
+    kproj = L * 2 * (2 * g["conv_kernel"] * hs // g["conv_group"]) * hs * 2
+    head = width * hs * 2 + rank * hs * 2 + k * width * 4
+    kv_rows = 0
+    for l in range(L):
+        wdw = g["windows"][l]
+        lo = max(first, a + 1 - wdw) if wdw > 0 else first
+        kv_rows += max(0, a - lo)
+    return i4 + kproj + head + kv_rows * kd * 4 * 2 + k * (1 + top) * rank * 2 + 2 * hs * 2
+
+
+def settle_flops(g, rows):
+    """The settle's products: fc (tap width x hidden) and every layer's K and
+    V (2 x kv_heads*head_dim x hidden), a multiply-add each, per row."""
+    hs, tw = g["hidden"], g["n_taps"] * g["hidden"]
+    kd = g["kv_heads"] * g["head_dim"]
+    return 2.0 * rows * (tw * hs + g["layers"] * 2 * kd * hs)
+
+
+def _events(n):
+    import torch
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+
+
+def leg_4b(pkg, synth, dev, stream, nblocks):
+    """The 4B-shaped sidecar: 4096 rows settled in 16 calls of 256, then
+    nblocks blocks at a = 4096 (width = vocab, k = 15)."""
+    import numpy as np
+    import torch
+
+    g = synth.geometry("qwen3_4b")
+    t0 = time.time()
+    w = synth.make_weights(g, seed=0, device=dev)
+    d = pkg.Drafter(g, w, max_context=4096 + 256, stream=stream)
+    del w
+    log(f"4b: sidecar ready in {time.time() - t0:.1f}s")
+    calls, n = 16, 4096
+    taps = synth.make_taps(g, n, seed=0, name="settle_taps", outliers=True, device=dev)
+    for i in range(4):  # warm
+        d.settle(0, 256, taps[256 * i:].data_ptr())
+    torch.cuda.synchronize()
+    e0, e1 = _events(1)[0]
+    e0.record()
+    for i in range(calls):
+        d.settle(256 * i, 256, taps[256 * i:].data_ptr())
+    e1.record()
+    torch.cuda.synchronize()
+    settle_s = e0.elapsed_time(e1) / 1e3
+    k, width, top = g["block"] - 1, g["vocab"], g["selector_top"]
+    out = [torch.empty(k, width, device=dev), torch.empty(k, top, dtype=torch.int32, device=dev),
+           torch.empty(k, top, device=dev), torch.empty(k, top, device=dev),
+           torch.empty(k, dtype=torch.int32, device=dev)]
+    ptrs = [t.data_ptr() for t in out]
+    anchors = synth.uniform_tokens(g, nblocks + 10, seed=0)
+    for i in range(10):
+        d.block(anchors[i], n, k, width, *ptrs)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(nblocks):
+        d.block(anchors[10 + i], n, k, width, *ptrs)
+    torch.cuda.synchronize()
+    blk_s = time.perf_counter() - t0
+    d.set_timing(True)
+    for i in range(20):
+        d.block(anchors[i], n, k, width, *ptrs)
+    st, nb, _ = d.stage_times()
+    d.set_timing(False)
+    d.close()
+    bb = block_bytes(g, 0, n, width, k)
+    us = blk_s / nblocks * 1e6
+    sfl = settle_flops(g, n)
+    log(f"4b: settle {n / settle_s / 1e6:.3f} M rows/s; blocks {nblocks / blk_s:.1f}/s")
+    return {
+        "workload": "4b: Qwen3-4B-shaped sidecar (hidden 2560, ffn 9728, 5 layers, 32/8 heads, "
+                    "hd 128, vocab 151936, block 16, tap width 12800, windows 0); 4096 rows "
+                    "settled in 16 calls of 256, then blocks at a=4096 (k=15, width=vocab)",
+        "blocks_per_s": round(nblocks / blk_s, 1), "us_per_block": round(us, 1),
+        "blocks": nblocks, "algorithmic_bytes": int(bb),
+        "hbm_frac": round(bb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "settle_rows_per_s": round(n / settle_s, 1),
+        "settle_us_per_call": round(settle_s / calls * 1e6, 2),
+        "settle_mfma_frac": round(sfl / settle_s / 1e12 / F16_MFMA_PEAK_TFS, 4),
+        "stages_us": {s_: round(v[0] / nb, 2) for s_, v in st.items()
+                      if not s_.startswith("settle") and v[1]},
+    }
+
+
+def leg_long(pkg, synth, dev, stream, steps):
+    """The long-context sidecar: 131071 positions settled (untimed), then
+    `steps` steps of one row settled + one block at a = 131072 + i."""
+    import torch
+
+    g = synth.geometry("t27b_long")
+    t0 = time.time()
+    w = synth.make_weights(g, seed=0, device=dev)
+    ctx0 = 131071
+    d = pkg.Drafter(g, w, max_context=ctx0 + steps + 40, stream=stream)
+    log(f"long: sidecar ready in {time.time() - t0:.1f}s")
+    t0 = time.time()
+    for c in range((ctx0 + 255) // 256):
+        m = min(256, ctx0 - 256 * c)
+        tp = synth.make_taps(g, m, seed=0, name=f"long_context.{c}", device=dev)
+        d.settle(256 * c, m, tp.data_ptr())
+    torch.cuda.synchronize()
+    log(f"long: {ctx0} positions settled in {time.time() - t0:.1f}s")
+    k, width, top = g["block"] - 1, g["vocab"], g["selector_top"]
+    out = [torch.empty(k, width, device=dev), torch.empty(k, top, dtype=torch.int32, device=dev),
+           torch.empty(k, top, device=dev), torch.empty(k, top, device=dev),
+           torch.empty(k, dtype=torch.int32, device=dev)]
+    ptrs = [t.data_ptr() for t in out]
+    warm = 10
+    total = warm + steps + 20
+    taps = synth.make_taps(g, total, seed=0, name="long_stream", device=dev)
+    anchors = synth.uniform_tokens(g, total, seed=1)
+    pos = ctx0
+
+    def step(i):
+        nonlocal pos
+        d.settle(pos, 1, taps[i:].data_ptr())
+        pos += 1
+        d.block(anchors[i], pos, k, width, *ptrs)
+
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    a_first = pos + 1
+    t0 = time.perf_counter()
+    for i in range(warm, warm + steps):
+        step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    a_last = pos
+    # blocks alone at the last anchor (no settle between)
+    t0 = time.perf_counter()
+    for i in range(20):
+        d.block(anchors[i], pos, k, width, *ptrs)
+    torch.cuda.synchronize()
+    bo_us = (time.perf_counter() - t0) / 20 * 1e6
+    d.set_timing(True)
+    for i in range(warm + steps, total):
+        step(i)
+    st, nb, _ = d.stage_times()
+    d.set_timing(False)
+    d.close()
+    del d
+    bytes_mean = sum(block_bytes(g, 0, a, width, k) for a in range(a_first, a_last + 1)) / steps
+    bo_bytes = block_bytes(g, 0, pos, width, k)
+    step_us = dt / steps * 1e6
+    kd = g["kv_heads"] * g["head_dim"]
+    attn_us = st["attention"][0] / nb
+    kv_bytes = g["layers"] * pos * kd * 8
+    log(f"long: {steps / dt:.1f} steps/s, blocks alone {1e6 / bo_us:.1f}/s")
+    res = {
+        "workload": "27b_long: 27B sidecar, every window 0 (layer 4 no_rope), vocab 262144, "
+                    "top 32, rank 128; 131071 positions settled, then per step 1 row settled "
+                    "+ one block at a=131072+i (k=15, width=vocab)",
+        "steps_per_s": round(steps / dt, 1), "us_per_step": round(step_us, 1), "steps": steps,
+        "block_only": {"blocks_per_s": round(1e6 / bo_us, 1), "us_per_block": round(bo_us, 1),
+                       "algorithmic_bytes": int(bo_bytes),
+                       "hbm_frac": round(bo_bytes / (bo_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "step_hbm_frac": round(bytes_mean / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "attention": {"us_per_block": round(attn_us, 1), "kv_bytes": int(kv_bytes),
+                      "hbm_frac": round(kv_bytes / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "note": "attention chunks + merge of all 5 layers over the whole context"},
+        "stages_us": {s_: round(v[0] / nb, 2) for s_, v in st.items() if v[1]},
+    }
+    return res, (g, w)
 
 
 HEAD_TRAFFIC = os.path.join(ROOT, "profiles", "k_head_27b_stream_traffic.txt")
@@ -397,7 +586,16 @@ def cpu_baseline(g, w, synth, steps):
                      "(32768-position synthetic context, k=15, width=vocab) + selection, each",
            "settle_s": round(t_settle, 2), "block_s": round(t_block, 2),
            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
-    # one step more on one thread (the oracle's OpenMP runtime set to 1)
+    # the settle unit: one 256-row call of the settle workload's tap rows
+    st4 = synth.make_taps(g, 256, seed=0, name="settle_taps", outliers=True).numpy()
+    t0 = time.perf_counter()
+    m.settle(st4, 0)
+    t4 = time.perf_counter() - t0
+    log(f"cpu baseline: one 256-row settle call in {t4:.2f}s")
+    res["settle"] = {"value": round(256 / t4, 1), "unit": "rows/s", "cores": cores,
+                     "sample": "one 256-row settle call of the 27b settle workload"}
+    # one step more on one thread (the oracle's OpenMP runtime set to 1), and
+    # 16 settle rows on one thread
     try:
         gomp = ctypes.CDLL("libgomp.so.1")
         gomp.omp_set_num_threads(1)
@@ -406,13 +604,40 @@ def cpu_baseline(g, w, synth, steps):
         r = m.block(store, 0, 32768, anchors[0], 32768, g["block"] - 1, g["vocab"])
         m.select(r["logits"], r["hp"], anchors[0])
         t1 = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        m.settle(st4[:16], 0)
+        t5 = time.perf_counter() - t0
         gomp.omp_set_num_threads(cores)
-        log(f"cpu baseline: one thread, one step in {t1:.1f}s")
+        log(f"cpu baseline: one thread, one step in {t1:.1f}s, 16 settle rows in {t5:.1f}s")
         res["one_thread"] = {"value": round(1.0 / t1, 4), "unit": "blocks/s", "cores": 1,
                              "sample": "1 stream step of the same workload"}
+        res["settle"]["one_thread"] = {"value": round(16 / t5, 2), "unit": "rows/s", "cores": 1,
+                                       "sample": "16 rows of the 256-row call"}
     except OSError as e:
         log(f"cpu baseline: one-thread run skipped ({e})")
     return res
+
+
+def cpu_long_block(synth, gw):
+    """The oracle on one block of the long-context workload: a 131072-position
+    synthetic context (drawn on the GPU, copied to the host), all cores."""
+    import torch
+    from oracle import oracle
+
+    g, w = gw
+    ctx = 131072
+    store = [(k_.cpu().numpy(), v_.cpu().numpy())
+             for k_, v_ in synth.make_store(g, ctx, seed=0, device=torch.device("cuda:0"))]
+    m = oracle.Model(g, w)
+    anchor = synth.uniform_tokens(g, 1, seed=1)[0]
+    t0 = time.perf_counter()
+    r = m.block(store, 0, ctx, anchor, ctx, g["block"] - 1, g["vocab"])
+    m.select(r["logits"], r["hp"], anchor)
+    t1 = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count()))
+    log(f"cpu baseline: one long-context block in {t1:.1f}s")
+    return {"value": round(1.0 / t1, 4), "unit": "blocks/s", "cores": cores,
+            "sample": "one block of the 27b long workload (131072 positions) + selection"}
 
 
 def cpu_model():

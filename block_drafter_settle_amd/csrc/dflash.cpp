@@ -25,17 +25,11 @@ namespace {
 
 constexpr int kSettleRows = 256;     // rows one settle pass takes
 constexpr int kTargetBlocks = 512;   // workgroups a GEMM launch aims for (256 CUs)
-// Row tiles per wave of each product (a workgroup covers 4·R tiles of 16).
-constexpr int kRFc = 2;      // settle's fc, f16
+constexpr int kR = 2;        // row tiles per wave of the skinny GEMMs (8 a workgroup)
 constexpr int kKsQkv = 8;    // q/k/v, int4: spans (128 columns) per split
 constexpr int kKsO = 2;      // o, int4
 constexpr int kKsDown = 8;   // down, int4
-constexpr int kRQkv = 2;     // their row tiles per wave
-constexpr int kRO = 2;
-constexpr int kRDown = 2;
-constexpr int kRKv = 2;      // settle's k/v of every layer, int4
 constexpr int kSettleI4Blocks = 2;  // above this many 16-row blocks the settle's k/v use the many-row kernel
-constexpr int kRDebug = 2;   // the debug matvec
 
 thread_local std::string g_create_error;
 
@@ -282,6 +276,9 @@ const char* validate(const dflash_geometry* g, const dflash_weights* w) {
   if (g->conv_group <= 0 || g->hidden % g->conv_group) return "hidden % conv_group";
   if (g->conv_kernel < 1 || g->conv_kernel > g->block) return "conv_kernel must be in [1, block]";
   if (g->hidden <= 0 || g->hidden % 128) return "hidden must be a multiple of 128";
+  // gate/up streams each wave's share of K through registers: at most 40
+  // spans of 128 columns over eight waves
+  if (!dfl::glu_stream_fits(g->hidden)) return "hidden must be at most 5120";
   if (g->intermediate <= 0 || g->intermediate % 128) return "intermediate must be a multiple of 128";
   if ((g->heads * g->head_dim) % 128) return "heads*head_dim must be a multiple of 128";
   if (2L * g->conv_kernel * (g->hidden / g->conv_group) > 16384)
@@ -373,13 +370,13 @@ long partial_need(const dflash* d) {
       need = std::max(need, (long)s2.S * mb * 16 * N);
     }
   for (int mb = 1; mb <= kSettleRows / 16; ++mb) {
-    f16(d->hs, d->tw, mb, kRFc);
-    i4(d->L * 2 * d->kd, d->hs, mb, kRKv);
-    for (int N : {d->hs, d->P, d->rank}) f16(N, d->hs, mb, kRDebug);
-    f16(d->hs, d->tw, mb, kRDebug);
-    for (int N : {d->qd, d->kd, d->ffn}) i4(N, d->hs, mb, kRDebug);
-    i4(d->hs, d->qd, mb, kRDebug);
-    i4(d->hs, d->ffn, mb, kRDebug);
+    f16(d->hs, d->tw, mb, kR);
+    i4(d->L * 2 * d->kd, d->hs, mb, kR);
+    for (int N : {d->hs, d->P, d->rank}) f16(N, d->hs, mb, kR);
+    f16(d->hs, d->tw, mb, kR);
+    for (int N : {d->qd, d->kd, d->ffn}) i4(N, d->hs, mb, kR);
+    i4(d->hs, d->qd, mb, kR);
+    i4(d->hs, d->ffn, mb, kR);
   }
   return need;
 }
@@ -667,12 +664,12 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
   // t = fc · taps (f32 partials), then rms by hidden_norm into A-layout
   const dfl::TileMap fmap{d->hs / 16, d->hs / 16, 0, 0};
   const Split sf = mb > 1 ? split_big(d->hs / 16, d->tw / 32)
-                          : split_for(d->hs / 16, kRFc, d->tw / 32, mb, 16);
+                          : split_for(d->hs / 16, kR, d->tw / 32, mb, 16);
   const long ssf = (long)mb * 16 * d->hs;
   if (mb > 1)
     dfl::gemm_big_f16(st, d->taps_a, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part, ssf);
   else
-    dfl::gemm_f16(st, kRFc, d->taps_a, 0, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part,
+    dfl::gemm_f16(st, d->taps_a, 0, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part,
                   ssf);
   tm_mark(d, DFLASH_ST_S_FC);
   // the hidden norm folded: t ⊙ hidden_norm feeds the K/V projection, and
@@ -690,8 +687,8 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
     dfl::gemm_kv_i4(st, d->t_a, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per,
                     d->part, ssk);
   } else {
-    sk = split_for(d->L * kvt, kRKv, d->hs / 128, mb, 4);
-    dfl::gemm_i4(st, kRKv, d->t_a, 0, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per,
+    sk = split_for(d->L * kvt, kR, d->hs / 128, mb, 4);
+    dfl::gemm_i4(st, d->t_a, 0, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per,
                  d->part, ssk);
   }
   tm_mark(d, DFLASH_ST_S_KV);
@@ -716,18 +713,28 @@ int dflash_settle(dflash_t* d, int64_t first_pos, int32_t n, const float* taps) 
   if (len + (long)n > d->cap)
     return fail(d, DFLASH_ENOMEM, "settle: %ld rows do not fit the store (max_context %ld)",
                 len + (long)n, d->cap);
-  d->first = first;
-  d->len = len;
-  if (n == 0) return DFLASH_OK;
-  tm_begin(d);
-  for (int done = 0; done < n; done += kSettleRows) {
-    const int m = std::min(kSettleRows, n - done);
-    const int rc = settle_pass(d, taps + (size_t)done * d->tw, m, first_pos + done, len + done);
-    if (rc) return rc;
-    d->len = len + done + m;
+  // The span is committed only once every pass has been enqueued. After a
+  // HIP error part of the rows may have been written, so the span keeps only
+  // what the call cannot have touched: the old rows before first_pos, or
+  // nothing when the rule restarted the context.
+  if (n > 0) {
+    tm_begin(d);
+    for (int done = 0; done < n; done += kSettleRows) {
+      const int m = std::min(kSettleRows, n - done);
+      const int rc = settle_pass(d, taps + (size_t)done * d->tw, m, first_pos + done, len + done);
+      if (rc) {
+        if (first != d->first)
+          d->len = 0;
+        else
+          d->len = std::min(d->len, len);
+        return rc;
+      }
+    }
+    tm_end(d);
+    d->tm.settles += d->tm.on;
   }
-  tm_end(d);
-  d->tm.settles += d->tm.on;
+  d->first = first;
+  d->len = len + n;
   return DFLASH_OK;
 }
 
@@ -778,7 +785,7 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     dfl::gemm_i4_block(st, d->xca, psh, hs, d->qkv.codes + i4l_qkv * 1024 * l,
                        d->qkv.scales + i4l_qkv * 64 * l,
                        dfl::TileMap{d->qkv.tiles, d->qkv.tiles, 0, 0}, d->qd + 2 * d->kd, sqk.per,
-                       d->part, ssq, kRQkv);
+                       d->part, ssq);
     tm_mark(d, DFLASH_ST_QKV);
     dfl::qkv_post(st, d->part, sqk.S, ssq, B, d->nh, d->kv, d->hd, d->q_norm + (size_t)l * d->hd,
                   d->k_norm + (size_t)l * d->hd, d->inv, a, d->rot[l], d->eps, d->qa, psq, d->kb, d->vb);
@@ -798,7 +805,7 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     // o, conv_out into the residual (and the MLP norm's input)
     dfl::gemm_i4_block(st, d->ya, psy, d->qd, d->o.codes + i4l_o * 1024 * l,
                        d->o.scales + i4l_o * 64 * l, dfl::TileMap{d->o.tiles, d->o.tiles, 0, 0},
-                       hs, so.per, d->part, ssh, kRO);
+                       hs, so.per, d->part, ssh);
     tm_mark(d, DFLASH_ST_O);
     dfl::conv1(st, d->h, d->part, so.S, ssh, d->dsum_a, ab, B, hs, d->gs, d->kn, d->sqp, post,
                d->xa, psh);
@@ -811,17 +818,12 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     dfl::conv0(st, d->h, d->sqp, nch, post, d->eps, d->part, spk.S, ssd, mbase, B, hs, d->gs, d->kn,
                d->xca, psh, d->dsum_m);
     tm_mark(d, DFLASH_ST_CONV);
-    if (dfl::glu_stream_fits(hs))
-      dfl::gemm_glu_stream(st, d->xca, psh, hs, d->gu.codes + i4l_gu * 1024 * l,
-                           d->gu.scales + i4l_gu * 64 * l, d->ffn / 16, d->ma, psm);
-    else
-      dfl::gemm_glu(st, d->xca, psh, hs, d->gu.codes + i4l_gu * 1024 * l,
-                    d->gu.scales + i4l_gu * 64 * l, d->ffn / 16, d->ma, psm);
+    dfl::gemm_glu_stream(st, d->xca, psh, hs, d->gu.codes + i4l_gu * 1024 * l,
+                         d->gu.scales + i4l_gu * 64 * l, d->ffn / 16, d->ma, psm);
     tm_mark(d, DFLASH_ST_GLU);
     dfl::gemm_i4_block(st, d->ma, psm, d->ffn, d->down.codes + i4l_dn * 1024 * l,
                        d->down.scales + i4l_dn * 64 * l,
-                       dfl::TileMap{d->down.tiles, d->down.tiles, 0, 0}, hs, sdn.per, d->part, ssh,
-                       kRDown);
+                       dfl::TileMap{d->down.tiles, d->down.tiles, 0, 0}, hs, sdn.per, d->part, ssh);
     tm_mark(d, DFLASH_ST_DOWN);
     // conv_out into the residual, and the next layer's attention-norm input
     // (the final norm runs on its own below)
@@ -926,16 +928,16 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
   // at m ≤ 16 an int4 matrix takes the block pass's kernel (two-span splits)
   const Split s = is_i4 && mb == 1 ? Split{dfl::i4_block_splits(cols, 2), 2}
                   : mb == 1        ? Split{dfl::f16_block_splits(cols), 0}
-                  : is_i4          ? split_for(map.ntiles, kRDebug, cols / 128, mb, 4)
+                  : is_i4          ? split_for(map.ntiles, kR, cols / 128, mb, 4)
                   : mb > 1         ? split_big(map.ntiles, cols / 32)
-                                   : split_for(map.ntiles, kRDebug, cols / 32, mb, 16);
+                                   : split_for(map.ntiles, kR, cols / 32, mb, 16);
   const long ss = (long)mb * 16 * rows;
   if ((long)s.S * ss > d->part_floats) return fail(d, DFLASH_EINVAL, "matvec: partials too large");
   if (is_i4 && mb == 1)
     dfl::gemm_i4_block(d->st, d->taps_a, ps, cols, static_cast<const uint8_t*>(codes), scales, map,
                        rows, 2, d->part, ss);
   else if (is_i4)
-    dfl::gemm_i4(d->st, kRDebug, d->taps_a, ps, cols, mb, static_cast<const uint8_t*>(codes), scales, map, rows,
+    dfl::gemm_i4(d->st, d->taps_a, ps, cols, mb, static_cast<const uint8_t*>(codes), scales, map, rows,
                  s.S, s.per, d->part, ss);
   else if (mb > 1)
     dfl::gemm_big_f16(d->st, d->taps_a, cols, mb, static_cast<const uint16_t*>(codes), map, rows,

@@ -43,11 +43,10 @@ struct TileMap {
 };
 
 // GEMM launches: out[split][mb·16 + m][col] partial sums (f32), col < N.
-// R = row tiles per wave (1, 2 or 4); a workgroup covers 4·R tiles.
-void gemm_f16(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblocks,
-              const uint16_t* w, TileMap map, int N, int splits, int steps_per_split, float* out,
-              long split_stride);
-void gemm_i4(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblocks,
+// Two row tiles a wave; a workgroup covers 8 tiles.
+void gemm_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks, const uint16_t* w,
+              TileMap map, int N, int splits, int steps_per_split, float* out, long split_stride);
+void gemm_i4(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks,
              const uint8_t* codes, const uint16_t* scales, TileMap map, int N, int splits,
              int spans_per_split, float* out, long split_stride);
 // Many-row f16 GEMM (mblocks ≤ 16 row blocks at once, 16 weight tiles per
@@ -56,24 +55,17 @@ void gemm_big_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const 
                   TileMap map, int N, int splits, int steps_per_split, float* out,
                   long split_stride);
 // The block pass's 16-row int4 GEMM (two planes, ps ≠ 0; skinny.hip):
-// splits of `ks` spans (128 columns) each, i4_block_splits(K, ks) of them;
-// out as gemm_i4. A wave takes R row tiles: R is 2 with ks 2, 4, 5, 6 or 8,
-// or 4 with ks 2, 4, 5 or 6.
+// splits of `ks` spans (128 columns) each, ks 2 or 8, i4_block_splits(K, ks)
+// of them; out as gemm_i4. Two row tiles a wave, four waves a workgroup.
 int i4_block_splits(int K, int ks);
 void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
                    const uint16_t* scales, TileMap map, int N, int ks, float* out,
-                   long split_stride, int R = 2);
+                   long split_stride);
 // The block pass's 16-row f16 GEMM (two planes, ps ≠ 0): f16_block_splits(K)
 // splits of 512 columns; out as gemm_f16.
 int f16_block_splits(int K);
 void gemm_f16_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t* w,
                     TileMap map, int N, float* out, long split_stride);
-// gate/up with the SwiGLU epilogue at 16 rows, two planes in (xa, ps):
-// gate tiles [0, ftiles), up tiles [ftiles, 2·ftiles) of one stored
-// matrix; writes silu(g)·u in A-layout planes (ma, mps).
-void gemm_glu(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
-              const uint16_t* scales, int ftiles, uint16_t* ma, long mps);
-
 // The settle's K/V at many rows straight from int4 codes (kernels.hip): A the
 // single-plane operand of mblocks 16-row blocks (up to 16), K/V tiles through
 // map, K splits of sps spans (128 columns) each; partial sums
@@ -88,9 +80,11 @@ void gemm_kv_i4(hipStream_t st, const uint16_t* xa, int K, int mblocks, const ui
 void probe_read(hipStream_t st, const void* p, long bytes, uint32_t* sink);
 void probe_mfma(hipStream_t st, int workgroups, int steps, float* sink);
 
-// gate/up + SwiGLU streamed through one workgroup per tile-pair range
-// (stream.hip), for K ≤ 5120 (40 spans of 128 over eight waves); same
-// operands and output as gemm_glu.
+// gate/up with the SwiGLU epilogue at 16 rows, two planes in (xa, ps),
+// streamed through one workgroup per tile-pair range (stream.hip), for
+// K ≤ 5120 (40 spans of 128 over eight waves): gate tiles [0, ftiles), up
+// tiles [ftiles, 2·ftiles) of one stored matrix; writes silu(g)·u in
+// A-layout planes (ma, mps).
 bool glu_stream_fits(int K);
 void gemm_glu_stream(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
                      const uint16_t* scales, int ftiles, uint16_t* ma, long mps);

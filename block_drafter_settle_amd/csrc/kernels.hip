@@ -1369,26 +1369,14 @@ static void launch_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int m
                                                ss);
 }
 
-template <int PL>
-static void pick_f16(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblocks,
-                     const uint16_t* w, TileMap map, int N, int splits, int sps, float* out,
-                     long ss) {
-  if (R == 1)
-    launch_f16<1, PL>(st, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
-  else if (R == 2)
-    launch_f16<2, PL>(st, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
-  else if (R == 4)
-    launch_f16<4, PL>(st, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
-  else
-    launch_f16<8, PL>(st, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
-}
-
-void gemm_f16(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblocks,
-              const uint16_t* w, TileMap map, int N, int splits, int sps, float* out, long ss) {
+// The skinny f16 and int4 GEMMs (the 8-row settle, the debug matvec) run two
+// row tiles a wave.
+void gemm_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks, const uint16_t* w,
+              TileMap map, int N, int splits, int sps, float* out, long ss) {
   if (ps)
-    pick_f16<2>(st, R, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
+    launch_f16<2, 2>(st, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
   else
-    pick_f16<1>(st, R, xa, 0, K, mblocks, w, map, N, splits, sps, out, ss);
+    launch_f16<2, 1>(st, xa, 0, K, mblocks, w, map, N, splits, sps, out, ss);
 }
 
 int kv_i4_groups(int ntiles) { return (int)cdiv(ntiles, kKvNT); }
@@ -1422,25 +1410,12 @@ static void launch_i4(hipStream_t st, const uint16_t* xa, long ps, int K, int mb
                                               out, ss);
 }
 
-template <int PL>
-static void pick_i4(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblocks,
-                    const uint8_t* codes, const uint16_t* scales, TileMap map, int N, int splits,
-                    int pps, float* out, long ss) {
-  if (R == 1)
-    launch_i4<1, PL>(st, xa, ps, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
-  else if (R == 2)
-    launch_i4<2, PL>(st, xa, ps, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
-  else
-    launch_i4<4, PL>(st, xa, ps, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
-}
-
-void gemm_i4(hipStream_t st, int R, const uint16_t* xa, long ps, int K, int mblocks,
-             const uint8_t* codes, const uint16_t* scales, TileMap map, int N, int splits, int pps,
-             float* out, long ss) {
+void gemm_i4(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks, const uint8_t* codes,
+             const uint16_t* scales, TileMap map, int N, int splits, int pps, float* out, long ss) {
   if (ps)
-    pick_i4<2>(st, R, xa, ps, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
+    launch_i4<2, 2>(st, xa, ps, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
   else
-    pick_i4<1>(st, R, xa, 0, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
+    launch_i4<2, 1>(st, xa, 0, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
 }
 
 void head_sel(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t* head, int width,

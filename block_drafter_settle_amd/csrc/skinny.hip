@@ -1,14 +1,13 @@
-// The block pass's int4 projections (q/k/v, o, down and the gate/up pair
-// with SwiGLU) at 16 rows with two activation planes.
+// The block pass's 16-row projections with two activation planes: the int4
+// q/k/v, o and down, and the f16 kernel projections.
 //
 // These kernels are compiled on their own with MFMA results in VGPRs
 // (-mllvm -amdgpu-mfma-vgpr-form): every MFMA result is scaled by its
 // group's f16 scale in VALU right away, which in the accumulator-register
 // form costs a v_accvgpr_read per element.
 //
-// `mlp` (silu(a) = a/(1+e^−a), the product with up) and the projections
-// are defined on the docs.rs page "cortiq_engine/dflash.rs" (cortiq-engine
-// 0.8.78), `Drafter::block`.
+// The projections are those of `Drafter::block` on the docs.rs page
+// "cortiq_engine/dflash.rs" (cortiq-engine 0.8.78).
 #include "device.h"
 #include "internal.h"
 
@@ -163,88 +162,6 @@ __global__ __launch_bounds__(64 * NW) void k_f16_block(const f16* __restrict__ x
   }
 }
 
-// gate/up over the full K with SwiGLU in the epilogue: workgroup g owns
-// ffn tiles [FP·g, FP·g + FP), i.e. FP gate tiles and the FP up tiles
-// (ftiles further on in the stored matrix); its NW waves split K, and their
-// partial sums meet in LDS, where wave 0 finishes silu(g)·u into the A-layout
-// planes of the down projection (ma, mps).
-template <int FP, int NW>
-__global__ __launch_bounds__(64 * NW) void k_glu_block(const f16* __restrict__ xa, long ps, int K,
-                                                       const uint4* __restrict__ codes,
-                                                       const uint2* __restrict__ scales,
-                                                       int ftiles, f16* __restrict__ ma,
-                                                       long mps) {
-  constexpr int R = 2 * FP;
-  __shared__ f4 red[NW - 1][R][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int KT = K >> 7;
-  const int ft0 = blockIdx.x * FP;
-  const int per = (KT + NW - 1) / NW;
-  const int p0 = wave * per, p1 = min(KT, p0 + per);
-  const h8* xp = reinterpret_cast<const h8*>(xa) + lane;
-  const h8* xq = reinterpret_cast<const h8*>(xa + ps) + lane;
-  const uint4* cp[R];
-  const uint2* scp[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int f = min(ft0 + (r % FP), ftiles - 1);
-    const long st = r < FP ? f : ftiles + f;
-    cp[r] = codes + (size_t)st * KT * 64 + lane;
-    scp[r] = scales + (size_t)st * KT * 16 + (lane & 15);
-  }
-  f4 acc[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = (f4){0.f, 0.f, 0.f, 0.f};
-  int p = p0;
-  for (; p + 2 <= p1; p += 2) {
-    uint4 c0[R], c1[R];
-    uint2 s0[R], s1[R];
-    h8 a0[4], a1[4], b0[4], b1[4];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      c0[r] = ld_stream(&cp[r][(size_t)p * 64]);
-      c1[r] = ld_stream(&cp[r][(size_t)(p + 1) * 64]);
-      s0[r] = ld_stream(&scp[r][(size_t)p * 16]);
-      s1[r] = ld_stream(&scp[r][(size_t)(p + 1) * 16]);
-    }
-    load_span<2>(xp, xq, p, a0, b0);
-    load_span<2>(xp, xq, p + 1, a1, b1);
-    i4_span<R, 2>(c0, s0, a0, b0, acc);
-    i4_span<R, 2>(c1, s1, a1, b1, acc);
-  }
-  if (p < p1) {
-    uint4 c0[R];
-    uint2 s0[R];
-    h8 a0[4], b0[4];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      c0[r] = ld_stream(&cp[r][(size_t)p * 64]);
-      s0[r] = ld_stream(&scp[r][(size_t)p * 16]);
-    }
-    load_span<2>(xp, xq, p, a0, b0);
-    i4_span<R, 2>(c0, s0, a0, b0, acc);
-  }
-  if (wave > 0)
-#pragma unroll
-    for (int r = 0; r < R; ++r) red[wave - 1][r][lane] = acc[r];
-  __syncthreads();
-  if (wave > 0) return;
-#pragma unroll
-  for (int w = 0; w < NW - 1; ++w)
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] += red[w][r][lane];
-  const int j = lane >> 4, n = lane & 15;
-#pragma unroll
-  for (int f = 0; f < FP; ++f) {
-    if (ft0 + f >= ftiles) break;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float g = acc[f][v];
-      put_a(ma, mps, a_idx(4 * j + v, (ft0 + f) * 16 + n), g / (1.f + expf(-g)) * acc[FP + f][v]);
-    }
-  }
-}
-
 static inline unsigned cdiv(long a, long b) { return (unsigned)((a + b - 1) / b); }
 
 // waves per workgroup of k_i4_block; tiles a wave (R) and spans a split
@@ -261,26 +178,14 @@ static void launch_i4_block(hipStream_t st, const f16* x, long ps, int K, const 
 }
 
 void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
-                   const uint16_t* scales, TileMap map, int N, int ks, float* out, long ss, int R) {
+                   const uint16_t* scales, TileMap map, int N, int ks, float* out, long ss) {
   const f16* x = reinterpret_cast<const f16*>(xa);
   const uint4* c = reinterpret_cast<const uint4*>(codes);
   const uint2* s = reinterpret_cast<const uint2*>(scales);
-  if (R == 4) {
-    switch (ks) {
-      case 2: launch_i4_block<4, 2>(st, x, ps, K, c, s, map, N, out, ss); break;
-      case 5: launch_i4_block<4, 5>(st, x, ps, K, c, s, map, N, out, ss); break;
-      case 6: launch_i4_block<4, 6>(st, x, ps, K, c, s, map, N, out, ss); break;
-      default: launch_i4_block<4, 4>(st, x, ps, K, c, s, map, N, out, ss); break;
-    }
-  } else {
-    switch (ks) {
-      case 2: launch_i4_block<2, 2>(st, x, ps, K, c, s, map, N, out, ss); break;
-      case 5: launch_i4_block<2, 5>(st, x, ps, K, c, s, map, N, out, ss); break;
-      case 6: launch_i4_block<2, 6>(st, x, ps, K, c, s, map, N, out, ss); break;
-      case 8: launch_i4_block<2, 8>(st, x, ps, K, c, s, map, N, out, ss); break;
-      default: launch_i4_block<2, 4>(st, x, ps, K, c, s, map, N, out, ss); break;
-    }
-  }
+  if (ks == 2)
+    launch_i4_block<2, 2>(st, x, ps, K, c, s, map, N, out, ss);
+  else
+    launch_i4_block<2, 8>(st, x, ps, K, c, s, map, N, out, ss);
 }
 
 
@@ -295,14 +200,6 @@ void gemm_f16_block(hipStream_t st, const uint16_t* xa, long ps, int K, const ui
   const dim3 grid(cdiv(map.ntiles, kF16R * kF16NW), f16_block_splits(K));
   k_f16_block<kF16R, kF16NW, kF16KS><<<grid, 64 * kF16NW, 0, st>>>(
       reinterpret_cast<const f16*>(xa), ps, K, reinterpret_cast<const f16*>(w), map, N, out, ss);
-}
-
-void gemm_glu(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
-              const uint16_t* scales, int ftiles, uint16_t* ma, long mps) {
-  constexpr int FP = 2, NW = 4;
-  k_glu_block<FP, NW><<<cdiv(ftiles, FP), 64 * NW, 0, st>>>(
-      reinterpret_cast<const f16*>(xa), ps, K, reinterpret_cast<const uint4*>(codes),
-      reinterpret_cast<const uint2*>(scales), ftiles, reinterpret_cast<f16*>(ma), mps);
 }
 
 }  // namespace dfl

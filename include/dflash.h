@@ -15,7 +15,10 @@
  *     invalid argument or geometry, DFLASH_ENOMEM (-2) for device memory or
  *     store capacity (max_context) exhausted, DFLASH_EHIP (-3) for a HIP
  *     runtime error. The message is kept for dflash_last_error. Arguments
- *     are checked before any launch, and a call that fails changes no state.
+ *     are checked before any launch, and a call they reject changes no
+ *     state. After DFLASH_EHIP (a launch failed: the device is usually
+ *     unusable then) the settled span keeps only rows the call cannot have
+ *     written (see dflash_settle).
  *   - "dev" pointers are device memory the caller owns (e.g. torch tensors'
  *     data_ptr on the same GPU); "host" pointers are host memory.
  *   - Work is enqueued on the stream given at create and is asynchronous:
@@ -69,7 +72,7 @@ typedef struct {
    > 0, block in [2, 16], n_taps > 0, kv_heads > 0, heads % kv_heads == 0,
    head_dim in {64, 128, 256}, conv_group > 0, hidden % conv_group == 0,
    conv_kernel in [1, block], hidden, intermediate and heads*head_dim
-   multiples of 128, 1 ≤ selector_top ≤ 32, selector_top ≤ vocab,
+   multiples of 128, hidden ≤ 5120, 1 ≤ selector_top ≤ 32, selector_top ≤ vocab,
    vocab ≤ 262144, selector_rank in [1, 256], 0 ≤ mask_token < vocab, every window ≥ 0,
    max_context ≥ 1. */
 typedef struct {
@@ -112,7 +115,11 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
    context is cut at first_pos and the rows appended; otherwise (an empty
    context, a gap, or first_pos < first) it restarts at first_pos. n = 0 only
    applies the rule. Fails with DFLASH_ENOMEM if the rows would not fit
-   max_context. Any n is accepted and taken 256 rows at a time. */
+   max_context (nothing changed). Any n is accepted and taken 256 rows at a
+   time; the new span is committed once every pass has been enqueued. If a
+   launch fails (DFLASH_EHIP) the span becomes [first, min(first+len,
+   first_pos)) when the rule kept the old first position, and empty when it
+   restarted the context. */
 int dflash_settle(dflash_t* d, int64_t first_pos, int32_t n, const float* taps);
 
 /* Block pass (`Drafter::block` + the head + `select_with`): rows

@@ -50,7 +50,7 @@ def _try_create(**over):
     dict(layers=0), dict(block=1), dict(block=17), dict(kv_heads=3), dict(head_dim=48),
     dict(conv_group=3), dict(hidden=96), dict(intermediate=200), dict(selector_top=0),
     dict(selector_top=33), dict(selector_rank=0), dict(mask_token=64), dict(conv_kernel=0),
-    dict(n_taps=0),
+    dict(n_taps=0), dict(hidden=5248),
 ])
 def test_invalid_geometry_is_rejected_on_the_host(over):
     e = _try_create(**over)

@@ -1,8 +1,10 @@
 """Parity at the full sidecar sizes, in the launch configuration the
-benchmark times, on outputs the CPU oracle can afford: whole blocks over a
-synthetic context store (loaded through the debug entry, so no oracle input
-comes from the GPU), and sampled rows of 256-row and 8-row settles (each
-settled row depends only on its tap row and position)."""
+benchmark times: whole blocks over a synthetic context store (loaded through
+the debug entry, so no oracle input comes from the GPU), every row of 256-row
+and 8-row settles, and the 27B stream's own composition end to end (a
+library-settled context longer than the layers' windows, then the stream's
+8-row settle and a block), the oracle settling its own context from the same
+tap rows."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +12,7 @@ import torch
 import block_drafter_settle_amd as pkg
 from block_drafter_settle_amd import synth
 
-from test_gpu_parity import REL, check_selection, close, run_block
+from test_gpu_parity import REL, check_selection, close, forced_select, run_block
 
 pytestmark = pytest.mark.gpu
 
@@ -70,35 +72,83 @@ def test_full_block_over_synthetic_store(orc, name, ctx, k):
         close(got["logits"], ref["logits"], f"{name} logits")
         close(got["hp"], ref["hp"], f"{name} hp")
         sel = m.select(ref["logits"], ref["hp"], anchor)
-        check_selection(got, ref["logits"], sel, name)
+        check_selection(got, ref["logits"], sel, name,
+                        forced=forced_select(d, g, got, k, width, anchor))
     finally:
         d.close()
 
 
-@pytest.mark.parametrize("name", ["t27b", "qwen3_4b"])
-def test_full_settle_sampled_rows(orc, name):
-    g, w = sidecar(name)
+def _store_rows(d, g, n, row0=0):
     dev = _dev()
     kd = g["kv_heads"] * g["head_dim"]
+    ks = [torch.empty(n, kd, device=dev) for _ in range(g["layers"])]
+    vs = [torch.empty(n, kd, device=dev) for _ in range(g["layers"])]
+    for l in range(g["layers"]):
+        d.debug_read_store(l, row0, n, ks[l].data_ptr(), vs[l].data_ptr())
+    d.sync()
+    return [k.cpu().numpy() for k in ks], [v.cpu().numpy() for v in vs]
+
+
+@pytest.mark.parametrize("name", ["t27b", "qwen3_4b"])
+def test_full_settle_every_row(orc, name):
+    """Every row of a 256-row settle (the many-row kernels; tap rows with
+    outlier channels) and of an 8-row settle (the stream's kernels)."""
+    g, w = sidecar(name)
+    dev = _dev()
     d = drafter(g, w, 300)
     try:
         m = orc.Model(g, w)
         for n, first, outl in ((256, 32768, True), (8, 40000, False)):
             taps = synth.make_taps(g, n, seed=n, outliers=outl, device=dev)
             d.settle(first, n, taps.data_ptr())
-            ks = [torch.empty(n, kd, device=dev) for _ in range(g["layers"])]
-            vs = [torch.empty(n, kd, device=dev) for _ in range(g["layers"])]
+            ks, vs = _store_rows(d, g, n)
+            print(f"{name}: settle of {n} rows at {first}, every row against the oracle",
+                  flush=True)
+            K, V = m.settle(taps.cpu().numpy(), first)
             for l in range(g["layers"]):
-                d.debug_read_store(l, 0, n, ks[l].data_ptr(), vs[l].data_ptr())
-            d.sync()
-            rows = sorted({0, n // 2, n - 1})
-            host_taps = taps.cpu().numpy()
-            print(f"{name}: settle of {n} rows at {first}, oracle rows {rows}", flush=True)
-            for r in rows:
-                K, V = m.settle(host_taps[r:r + 1], first + r)
-                for l in range(g["layers"]):
-                    close(ks[l][r].cpu().numpy(), K[l, 0], f"{name} K l{l} row {r}")
-                    close(vs[l][r].cpu().numpy(), V[l, 0], f"{name} V l{l} row {r}")
+                close(ks[l], K[l], f"{name} settle {n} K layer {l}")
+                close(vs[l], V[l], f"{name} settle {n} V layer {l}")
+    finally:
+        d.close()
+
+
+def test_27b_stream_end_to_end(orc):
+    """The 27B stream's composition: 2304 positions settled through the
+    library (nine 256-row passes: longer than the 2048-position windows),
+    then the next 8 rows (the stream's 8-row settle), then a block at the new
+    end, width = vocabulary. The oracle settles the same tap rows itself; the
+    store, the block's rows, logits, selector projections and selection are
+    compared."""
+    g, w = sidecar("t27b")
+    dev = _dev()
+    n0, n1, first = 2304, 8, 1000
+    d = drafter(g, w, n0 + n1 + 16)
+    try:
+        taps = synth.make_taps(g, n0 + n1, seed=11, name="e2e", device=dev)
+        d.settle(first, n0, taps.data_ptr())
+        d.settle(first + n0, n1, taps[n0:].data_ptr())
+        assert d.span() == (first, first + n0 + n1)
+        a = first + n0 + n1
+        anchor, k, width = synth.uniform_tokens(g, 1, seed=12)[0], g["block"] - 1, g["vocab"]
+        got = run_block(d, g, anchor, a, k, width)
+        ks, vs = _store_rows(d, g, n0 + n1)
+        host_taps = taps.cpu().numpy()
+        del taps
+        m = orc.Model(g, w)
+        print(f"t27b end to end: oracle settles {n0 + n1} rows", flush=True)
+        K, V = m.settle(host_taps, first)
+        for l in range(g["layers"]):
+            close(ks[l], K[l], f"t27b e2e store K layer {l}")
+            close(vs[l], V[l], f"t27b e2e store V layer {l}")
+        print(f"t27b end to end: oracle block at a={a}", flush=True)
+        ref = m.block([(K[l], V[l]) for l in range(g["layers"])], first, n0 + n1, anchor, a, k,
+                      width)
+        close(got["hidden"], ref["hidden"], "t27b e2e hidden")
+        close(got["logits"], ref["logits"], "t27b e2e logits")
+        close(got["hp"], ref["hp"], "t27b e2e hp")
+        sel = m.select(ref["logits"], ref["hp"], anchor)
+        check_selection(got, ref["logits"], sel, "t27b e2e",
+                        forced=forced_select(d, g, got, k, width, anchor))
     finally:
         d.close()
 

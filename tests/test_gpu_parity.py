@@ -10,6 +10,7 @@ import torch
 
 import block_drafter_settle_amd as pkg
 from block_drafter_settle_amd import synth
+from margins import record
 
 pytestmark = pytest.mark.gpu
 
@@ -27,8 +28,9 @@ def close(got, ref, what, rel=REL):
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     tol = rel * np.abs(ref).max()
-    err = np.abs(got - ref).max()
+    err = np.abs(got - ref).max() if got.size else 0.0
     print(f"{what}: max|err| {err:.3e} tol {tol:.3e}", flush=True)
+    record(what, err, tol)
     assert err <= tol, f"{what}: max|err| {err:.3e} > {tol:.3e}"
 
 
@@ -54,9 +56,31 @@ def run_block(d, g, anchor, a, k, width):
     return {n: t.cpu().numpy() for n, t in out.items()}
 
 
-def check_selection(got, ref_logits, ref_sel, what):
-    """Candidates where the oracle's neighbouring gaps exceed τ; chosen
-    tokens and scores along the chain while it agrees."""
+def _check_chain_rows(got, ref_sel, rows, stau, what):
+    """Scores (within stau) and chosen tokens (where the oracle's best score
+    leads the second by more than stau) of the given rows, wherever the
+    candidate lists agree."""
+    compared = 0
+    for j in rows:
+        if not np.array_equal(got["cand"][j], ref_sel["cand"][j]):
+            continue
+        err = np.abs(got["score"][j] - ref_sel["score"][j]).max()
+        record(f"{what} score row {j}", err, stau)
+        assert err <= stau, f"{what} score row {j}: max|err| {err:.3e} > {stau:.3e}"
+        s = np.sort(ref_sel["score"][j])[::-1]
+        if s.size < 2 or s[0] - s[1] > stau:
+            assert got["chosen"][j] == ref_sel["chosen"][j], (what, "chosen", j)
+        compared += 1
+    return compared
+
+
+def check_selection(got, ref_logits, ref_sel, what, forced=None):
+    """Candidates where the oracle's neighbouring gaps exceed τ; scores and
+    chosen tokens along the chain while it agrees. After the first row where
+    the chains part (a candidate list or a chosen token differs), the later
+    rows are compared under the oracle's chain: `forced(prev)` re-runs the
+    GPU selection on its own logits and projections with each row's
+    predecessor forced to the oracle's choice before it."""
     tau = REL * np.abs(ref_logits).max()
     k, top = ref_sel["cand"].shape
     for j in range(k):
@@ -66,18 +90,50 @@ def check_selection(got, ref_logits, ref_sel, what):
             hi_gap = row[t - 1] - row[t] if t > 0 else np.inf
             if lo_gap > tau and hi_gap > tau:
                 assert got["cand"][j, t] == ref_sel["cand"][j, t], (what, j, t)
-    # the chain: compare while every earlier chosen token agrees
     stau = REL * np.abs(ref_sel["score"]).max()
+    part = k
     for j in range(k):
-        if not np.array_equal(got["cand"][j], ref_sel["cand"][j]):
+        if (not np.array_equal(got["cand"][j], ref_sel["cand"][j])
+                or got["chosen"][j] != ref_sel["chosen"][j]):
+            part = j
             break
-        err = np.abs(got["score"][j] - ref_sel["score"][j]).max()
-        assert err <= stau, f"{what} score row {j}: max|err| {err:.3e} > {stau:.3e}"
-        s = np.sort(ref_sel["score"][j])[::-1]
-        if s.size < 2 or s[0] - s[1] > stau:
-            assert got["chosen"][j] == ref_sel["chosen"][j], (what, "chosen", j)
-        if got["chosen"][j] != ref_sel["chosen"][j]:
-            break
+    _check_chain_rows(got, ref_sel, range(min(part + 1, k)), stau, what)
+    if part + 1 < k and forced is not None:
+        prev = np.concatenate([[0], ref_sel["chosen"][:-1]]).astype(np.int32)
+        again = forced(prev)
+        n = _check_chain_rows(again, ref_sel, range(part + 1, k), stau, what + " (forced chain)")
+        print(f"{what}: chains part at row {part}; {n} later rows compared under the oracle's "
+              "chain", flush=True)
+    return part
+
+
+def forced_select(d, g, got, k, width, anchor):
+    """The GPU selection on the block's own logits and selector projections,
+    with every row's predecessor forced (`dflash_debug_select`)."""
+    dev = _dev()
+    top = g["selector_top"]
+
+    def run(prev):
+        lg = torch.tensor(got["logits"], device=dev)
+        hp = torch.tensor(got["hp"], device=dev)
+        fp = torch.tensor(prev, dtype=torch.int32, device=dev)
+        out = dict(cand=torch.empty(k, top, dtype=torch.int32, device=dev),
+                   unary=torch.empty(k, top, device=dev), score=torch.empty(k, top, device=dev),
+                   chosen=torch.empty(k, dtype=torch.int32, device=dev))
+        d.debug_select(lg.data_ptr(), hp.data_ptr(), k, width, anchor, fp.data_ptr(),
+                       out["cand"].data_ptr(), out["unary"].data_ptr(), out["score"].data_ptr(),
+                       out["chosen"].data_ptr())
+        d.sync()
+        return {n: t.cpu().numpy() for n, t in out.items()}
+
+    return run
+
+
+def strengthen_codebooks(w, seed=1, std=0.5):
+    """Codebooks large enough for the selector to reorder the candidates."""
+    rng = np.random.default_rng(seed)
+    for name in ("pred_book", "succ_book"):
+        w[name] = (rng.standard_normal(w[name].shape) * std).astype(np.float16).view(np.uint16)
 
 
 # ------------------------------------------------------------------ pieces
@@ -222,14 +278,31 @@ BLOCK_CASES = [
     (dict(windows=[0, 7], no_rope=[], conv_kernel=6, conv_group=8), (10, 60), 0, 7, 1000),
     (dict(windows=[0, 0], no_rope=[1], block=16, conv_kernel=16, conv_group=16), (0, 100), 0, 15,
      1000),
+    # head_dim 256 (two pairs a lane in the q/k norm and rotary, the widest
+    # attention tiles), with a window and a no-rope layer
+    (dict(windows=[0, 9], no_rope=[1], heads=4, kv_heads=2, head_dim=256), (3, 90), 0, 7, 1000),
+    (dict(windows=[0, 0], no_rope=[], heads=2, kv_heads=1, head_dim=256, block=16), (0, 300), 0,
+     15, 1000),
+    # codebooks strong enough for the selector to reorder candidates
+    (dict(windows=[0, 5], no_rope=[], _strong=True), (0, 80), 0, 7, 1000),
+    (dict(windows=[0, 0], no_rope=[], block=16, vocab=3000, mask_token=2999, _strong=True),
+     (7, 120), 0, 15, 3000),
 ]
 
 
 @pytest.mark.parametrize("case", BLOCK_CASES)
 def test_block_parity(orc, case):
     over, (first, length), da, k, width = case
+    over = dict(over)
+    strong = over.pop("_strong", False)
     g = synth.small_geometry(**over)
-    w, d = make(g, seed=2, max_context=max(length, 1) + 8)
+    if strong:
+        w = synth.make_weights(g, seed=2)
+        strengthen_codebooks(w)
+        d = pkg.Drafter(g, w, max_context=max(length, 1) + 8,
+                        stream=torch.cuda.current_stream(_dev()).cuda_stream)
+    else:
+        w, d = make(g, seed=2, max_context=max(length, 1) + 8)
     try:
         dev = _dev()
         m = orc.Model(g, w)
@@ -245,11 +318,15 @@ def test_block_parity(orc, case):
         anchor = 123
         got = run_block(d, g, anchor, a, k, width)
         ref = m.block(store, first, length, anchor, a, k, width)
-        close(got["hidden"], ref["hidden"], "hidden")
-        close(got["logits"], ref["logits"], "logits")
-        close(got["hp"], ref["hp"], "hp")
+        tag = f"block {over} ctx {length}"
+        close(got["hidden"], ref["hidden"], tag + " hidden")
+        close(got["logits"], ref["logits"], tag + " logits")
+        close(got["hp"], ref["hp"], tag + " hp")
         sel = m.select(ref["logits"], ref["hp"], anchor)
-        check_selection(got, ref["logits"], sel, "block")
+        check_selection(got, ref["logits"], sel, tag,
+                        forced=forced_select(d, g, got, k, width, anchor))
+        if strong:  # the selector must have reordered something
+            assert np.any(sel["chosen"] != sel["plain"]), "codebooks too weak to reorder"
     finally:
         d.close()
 
@@ -285,11 +362,7 @@ def test_select_parity(orc, strong):
     try:
         dev = _dev()
         if strong:  # codebooks large enough for the selector to reorder
-            rng = np.random.default_rng(1)
-            w["pred_book"] = (rng.standard_normal(w["pred_book"].shape) * 0.5).astype(
-                np.float16).view(np.uint16)
-            w["succ_book"] = (rng.standard_normal(w["succ_book"].shape) * 0.5).astype(
-                np.float16).view(np.uint16)
+            strengthen_codebooks(w)
             d.close()
             d = pkg.Drafter(g, w, max_context=8, stream=torch.cuda.current_stream(dev).cuda_stream)
         rng = np.random.default_rng(2)
