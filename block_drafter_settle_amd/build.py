@@ -9,11 +9,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdflash.so")
-# source, extra flags: the block pass's int4 kernels and the attention keep
-# MFMA results in VGPRs (their results are rescaled in VALU at once)
+# source, extra flags: the int4 kernels and the attention keep MFMA results in
+# VGPRs (their results are rescaled in VALU at once)
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 SOURCES = [("kernels.hip", []), ("skinny.hip", VGPR_FORM), ("stream.hip", VGPR_FORM),
-           ("attention.hip", VGPR_FORM), ("dflash.cpp", [])]
+           ("attention.hip", VGPR_FORM), ("settle.hip", VGPR_FORM), ("dflash.cpp", [])]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

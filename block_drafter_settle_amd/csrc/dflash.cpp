@@ -564,8 +564,9 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   if (!rc) rc = dev_alloc(d, &d->ya, 2 * 16 * d->qd, "scratch");
   if (!rc) rc = dev_alloc(d, &d->ma, 2 * 16 * d->ffn, "scratch");
   d->stage_cols = std::max(std::max(d->tw, d->ffn), std::max(d->qd, hs));
-  if (!rc) rc = dev_alloc(d, &d->taps_a, (size_t)kSettleRows * d->stage_cols, "settle scratch");
-  if (!rc) rc = dev_alloc(d, &d->t_a, (size_t)kSettleRows * hs, "settle scratch");
+  // the settle's operands, two planes of 256 rows each
+  if (!rc) rc = dev_alloc(d, &d->taps_a, 2 * (size_t)kSettleRows * d->stage_cols, "settle scratch");
+  if (!rc) rc = dev_alloc(d, &d->t_a, 2 * (size_t)kSettleRows * hs, "settle scratch");
   if (!rc) rc = dev_alloc(d, &d->sqp, (size_t)kSettleRows * ((hs + 255) / 256), "norm scratch");
   if (!rc) rc = dev_alloc(d, &d->sel_sc.tab, (size_t)d->top * (1 + 15 * d->top), "selector table");
   if (!rc) rc = dev_alloc(d, &d->sel_sc.best, (size_t)(1 + 15 * d->top), "selector table");
@@ -659,7 +660,12 @@ int dflash_truncate(dflash_t* d, int64_t pos) {
 static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0) {
   hipStream_t st = d->st;
   const int mb = (m + 15) / 16;
-  dfl::to_a(st, taps, d->tw, m, d->tw, d->taps_a, 0);
+  // every activation operand carries two f16 planes (hi and the rest): the
+  // settled keys and values feed every later block, whose layers amplify
+  // their error, so single-plane f16 rounding (1e-3 of the largest K/V
+  // entry) is not enough end to end
+  const long pst = (long)kSettleRows * d->tw, psh = (long)kSettleRows * d->hs;
+  dfl::to_a(st, taps, d->tw, m, d->tw, d->taps_a, pst);
   tm_mark(d, DFLASH_ST_S_TAPS);
   // t = fc · taps (f32 partials), then rms by hidden_norm into A-layout
   const dfl::TileMap fmap{d->hs / 16, d->hs / 16, 0, 0};
@@ -667,14 +673,14 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
                           : split_for(d->hs / 16, kR, d->tw / 32, mb, 16);
   const long ssf = (long)mb * 16 * d->hs;
   if (mb > 1)
-    dfl::gemm_big_f16(st, d->taps_a, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part, ssf);
+    dfl::gemm_big_f16(st, d->taps_a, pst, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part,
+                      ssf);
   else
-    dfl::gemm_f16(st, d->taps_a, 0, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part,
-                  ssf);
+    dfl::gemm_f16(st, d->taps_a, pst, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part, ssf);
   tm_mark(d, DFLASH_ST_S_FC);
   // the hidden norm folded: t ⊙ hidden_norm feeds the K/V projection, and
   // settle_kv applies each row's rms scale to its output
-  dfl::rowsum_sq(st, d->part, sf.S, ssf, m, d->hs, d->hidden_norm, d->t_a, d->sqp);
+  dfl::rowsum_sq(st, d->part, sf.S, ssf, m, d->hs, d->hidden_norm, d->t_a, psh, d->sqp);
   tm_mark(d, DFLASH_ST_S_NORM);
   // K and V of every layer: the k and v tiles of each layer's q/k/v set
   const int kvt = 2 * d->kd / 16;
@@ -684,11 +690,11 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
   Split sk;
   if (mb > kSettleI4Blocks) {
     sk = split_kv(d->L * kvt, d->hs / 128);
-    dfl::gemm_kv_i4(st, d->t_a, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per,
+    dfl::gemm_kv_i4(st, d->t_a, psh, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per,
                     d->part, ssk);
   } else {
     sk = split_for(d->L * kvt, kR, d->hs / 128, mb, 4);
-    dfl::gemm_i4(st, d->t_a, 0, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per,
+    dfl::gemm_i4(st, d->t_a, psh, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per,
                  d->part, ssk);
   }
   tm_mark(d, DFLASH_ST_S_KV);
@@ -922,8 +928,8 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
   if (rc) return rc;
   if (cols > d->stage_cols) return fail(d, DFLASH_EINVAL, "matvec: matrix wider than the staging buffer");
   const int mb = (m + 15) / 16;
-  // the block's operands (m ≤ 16) carry two planes, the settle's one
-  const long ps = m <= 16 ? 16L * cols : 0;
+  // two planes, as every operand of the block and the settle
+  const long ps = (long)kSettleRows * cols;
   dfl::to_a(d->st, x, cols, m, cols, d->taps_a, ps);
   // at m ≤ 16 an int4 matrix takes the block pass's kernel (two-span splits)
   const Split s = is_i4 && mb == 1 ? Split{dfl::i4_block_splits(cols, 2), 2}
@@ -940,7 +946,7 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
     dfl::gemm_i4(d->st, d->taps_a, ps, cols, mb, static_cast<const uint8_t*>(codes), scales, map, rows,
                  s.S, s.per, d->part, ss);
   else if (mb > 1)
-    dfl::gemm_big_f16(d->st, d->taps_a, cols, mb, static_cast<const uint16_t*>(codes), map, rows,
+    dfl::gemm_big_f16(d->st, d->taps_a, ps, cols, mb, static_cast<const uint16_t*>(codes), map, rows,
                       s.S, s.per, d->part, ss);
   else
     dfl::gemm_f16_block(d->st, d->taps_a, ps, cols, static_cast<const uint16_t*>(codes), map, rows,

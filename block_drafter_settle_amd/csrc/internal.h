@@ -50,10 +50,11 @@ void gemm_i4(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks,
              const uint8_t* codes, const uint16_t* scales, TileMap map, int N, int splits,
              int spans_per_split, float* out, long split_stride);
 // Many-row f16 GEMM (mblocks ≤ 16 row blocks at once, 16 weight tiles per
-// block, async copies into a 4-stage LDS ring; one plane); out as gemm_f16.
-void gemm_big_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
-                  TileMap map, int N, int splits, int steps_per_split, float* out,
-                  long split_stride);
+// block, async copies into a 3-stage LDS ring), one plane (ps = 0) or two
+// (plane 1 at xa + ps, ps a multiple of 8); out as gemm_f16.
+void gemm_big_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks,
+                  const uint16_t* w, TileMap map, int N, int splits, int steps_per_split,
+                  float* out, long split_stride);
 // The block pass's 16-row int4 GEMM (two planes, ps ≠ 0; skinny.hip):
 // splits of `ks` spans (128 columns) each, ks 2 or 8, i4_block_splits(K, ks)
 // of them; out as gemm_i4. Two row tiles a wave, four waves a workgroup.
@@ -66,14 +67,14 @@ void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uin
 int f16_block_splits(int K);
 void gemm_f16_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t* w,
                     TileMap map, int N, float* out, long split_stride);
-// The settle's K/V at many rows straight from int4 codes (kernels.hip): A the
-// single-plane operand of mblocks 16-row blocks (up to 16), K/V tiles through
-// map, K splits of sps spans (128 columns) each; partial sums
-// out[split][mblocks·16][N].
+// The settle's K/V at many rows straight from int4 codes (settle.hip): A the
+// two-plane operand (plane 1 at xa + ps) of mblocks 16-row blocks (up to 16),
+// K/V tiles through map, K splits of sps spans (128 columns) each; partial
+// sums out[split][mblocks·16][N].
 int kv_i4_groups(int ntiles);
-void gemm_kv_i4(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint8_t* codes,
-                const uint16_t* scales, TileMap map, int N, int splits, int sps, float* out,
-                long ss);
+void gemm_kv_i4(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks,
+                const uint8_t* codes, const uint16_t* scales, TileMap map, int N, int splits,
+                int sps, float* out, long ss);
 
 // Peak probes (kernels.hip): a streaming read of `bytes` (multiple of 16) at
 // p, and `workgroups` × 4 waves of `steps` rounds of 32 back-to-back MFMAs.
@@ -114,10 +115,11 @@ void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa, l
 int row_chunks(int N);
 int conv1_chunks(int hs);
 // rowsum_sq: the split-summed settle rows t, their sums of squares, and
-// t ⊙ w as the K/V projection's one-plane operand; settle_kv applies the
-// hidden norm's per-row scale (from sqp, row_chunks(hs) per row).
+// t ⊙ w as the K/V projection's two-plane operand (plane 1 at xa + ps);
+// settle_kv applies the hidden norm's per-row scale (from sqp,
+// row_chunks(hs) per row).
 void rowsum_sq(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,
-               const float* w, uint16_t* xa, float* sqp);
+               const float* w, uint16_t* xa, long ps, float* sqp);
 void norm_apply(hipStream_t st, const float* h, const float* sqp, int nchunk, int rows, int N,
                 const float* w, float eps, float* x, uint16_t* xa, long ps);
 // embed and conv1 also write u = h ⊙ w (w: the next norm's gain; conv1

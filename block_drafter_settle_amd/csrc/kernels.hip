@@ -88,22 +88,28 @@ __global__ __launch_bounds__(kThreads) void k_gemm_f16(const f16* __restrict__ x
   }
 }
 
-// Many-row GEMM, f16 weights (the settle's fc and K/V at up to 256 rows): a
-// block holds all 16 row blocks (256 rows; rows past the input are never
-// written out) against kBigNT weight tiles over its K split. Every 32-column
-// step's fragments (16 row + kBigNT weight, 1 KB each, in their memory
+// Many-row GEMM, f16 weights (the settle's fc at up to 256 rows, and the
+// f16 matrices of the debug product above 16 rows): a block
+// holds all 16 row blocks (256 rows; rows past the input are never written
+// out) of PL activation planes against kBigNT weight tiles over its K split,
+// both planes' products summed into one accumulator. Every 32-column step's
+// fragments (16·PL row + kBigNT weight fragments, 1 KB each, in their memory
 // layout) are copied global → LDS by the waves' async loads
 // (global_load_lds_dwordx4: lane l's 16 bytes land at dst + 16·l) into a
 // kBigStages ring, kBigStages − 1 steps in flight. The block has eight
 // waves, two on each SIMD, so one wave's products run while the other waits
 // at the step's barrier or on LDS: wave w multiplies row blocks 4(w%4)..+3
-// by weight tiles 8(w/4)..+7. Waves 0–3 copy the row fragments, waves 4–7
-// the weight fragments (non-temporal: read once). Blocks are numbered
-// split-fastest.
+// (every plane) by weight tiles 8(w/4)..+7. Each wave copies
+// (16·PL + kBigNT)/8 fragments a step, the weight fragments non-temporal
+// (read once). Blocks are numbered split-fastest.
 static constexpr int kBigNT = 16, kBigStages = 3, kBigWaves = 8;
-static constexpr int kBigFrags = 16 + kBigNT;              // fragments a step
-static constexpr int kBigPerWave = kBigFrags / kBigWaves;  // async copies a wave issues a step
-static_assert(16 % kBigPerWave == 0, "a wave copies row or weight fragments only");
+template <int PL>
+struct Big {
+  static constexpr int kFrags = 16 * PL + kBigNT;         // fragments a step
+  static constexpr int kPerWave = kFrags / kBigWaves;     // async copies a wave issues a step
+  static_assert(kFrags % kBigWaves == 0, "every wave copies as many fragments");
+  static constexpr size_t kLds = sizeof(h8) * kBigStages * kFrags * 64;
+};
 
 __device__ __forceinline__ void copy16(const h8* src, h8* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
@@ -112,14 +118,17 @@ __device__ __forceinline__ void copy16_nt(const h8* src, h8* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 2);
 }
 
-__global__ __launch_bounds__(64 * kBigWaves) void k_gemm_big_f16(const f16* __restrict__ xa, int K,
-                                                                int mblocks,
+template <int PL>
+__global__ __launch_bounds__(64 * kBigWaves) void k_gemm_big_f16(const f16* __restrict__ xa, long ps,
+                                                                int K, int mblocks,
                                                                 const f16* __restrict__ w,
                                                                 TileMap mp, int N, int splits,
                                                                 int sps, float* __restrict__ out,
                                                                 long split_stride) {
+  using C = Big<PL>;
   constexpr int D = kBigStages - 1;
-  extern __shared__ h8 stage[];  // [kBigStages][kBigFrags][64]
+  constexpr int NA = 16 * PL;    // row fragments a step
+  extern __shared__ h8 stage[];  // [kBigStages][C::kFrags][64]: row fragments (plane, block), then weight tiles
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rw = wave & 3, cw = wave >> 2;
@@ -129,25 +138,24 @@ __global__ __launch_bounds__(64 * kBigWaves) void k_gemm_big_f16(const f16* __re
   const int t0 = (blockIdx.x / splits) * kBigNT;
   const h8* xg = reinterpret_cast<const h8*>(xa);
   const h8* wg = reinterpret_cast<const h8*>(w);
-  const bool w_wave = wave * kBigPerWave >= 16;
-  const h8* fsrc[kBigPerWave];  // this wave's fragments, at step 0
+  const h8* fsrc[C::kPerWave];  // this wave's fragments, at step 0
 #pragma unroll
-  for (int i = 0; i < kBigPerWave; ++i) {
-    const int f = wave * kBigPerWave + i;
-    fsrc[i] = f < 16 ? xg + (size_t)f * 2 * K + lane
-                     : wg + (size_t)map_tile(mp, min(t0 + f - 16, mp.ntiles - 1)) * KS * 64 + lane;
+  for (int i = 0; i < C::kPerWave; ++i) {
+    const int f = wave * C::kPerWave + i;
+    fsrc[i] = f < NA ? xg + (size_t)(f / 16) * (ps / 8) + (size_t)(f % 16) * 2 * K + lane
+                     : wg + (size_t)map_tile(mp, min(t0 + f - NA, mp.ntiles - 1)) * KS * 64 + lane;
   }
   // async copies of step s into its stage; past the split's end the last
   // step is copied again, so that every step issues the same loads
   auto issue = [&](int s) {
     const int sc = min(s, s1 - 1);
-    h8* dst = stage + (size_t)(s % kBigStages) * kBigFrags * 64 + (wave * kBigPerWave) * 64;
-    if (w_wave) {
+    h8* dst = stage + (size_t)(s % kBigStages) * C::kFrags * 64 + (wave * C::kPerWave) * 64;
 #pragma unroll
-      for (int i = 0; i < kBigPerWave; ++i) copy16_nt(fsrc[i] + (size_t)sc * 64, dst + i * 64);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kBigPerWave; ++i) copy16(fsrc[i] + (size_t)sc * 64, dst + i * 64);
+    for (int i = 0; i < C::kPerWave; ++i) {
+      if (wave * C::kPerWave + i >= NA)  // uniform: weight fragments are read once
+        copy16_nt(fsrc[i] + (size_t)sc * 64, dst + i * 64);
+      else
+        copy16(fsrc[i] + (size_t)sc * 64, dst + i * 64);
     }
   };
   f4 acc[4][8];
@@ -161,19 +169,23 @@ __global__ __launch_bounds__(64 * kBigWaves) void k_gemm_big_f16(const f16* __re
     // this wave's copies of step s are in (those of the D − 1 later steps
     // may remain); after the barrier every wave's are, and the stage of
     // step s − 1 is free for step s + D
-    wait_vm<(D - 1) * kBigPerWave>();
+    wait_vm<(D - 1) * C::kPerWave>();
     lds_barrier();
     issue(s + D);
-    const h8* st = stage + (size_t)(s % kBigStages) * kBigFrags * 64;
-    h8 af[4], bf[8];
+    const h8* st = stage + (size_t)(s % kBigStages) * C::kFrags * 64;
+    h8 bf[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) bf[t] = st[(16 + cw * 8 + t) * 64 + lane];
+    for (int t = 0; t < 8; ++t) bf[t] = st[(NA + cw * 8 + t) * 64 + lane];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) af[b] = st[(rw * 4 + b) * 64 + lane];
+    for (int p = 0; p < PL; ++p) {
+      h8 af[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 4; ++b) af[b] = st[(p * 16 + rw * 4 + b) * 64 + lane];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc[b][t] = mfma16(af[b], bf[t], acc[b][t]);
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[b][t] = mfma16(af[b], bf[t], acc[b][t]);
+    }
   }
   const int j = lane >> 4, n = lane & 15;
   float* o = out + (size_t)sp * split_stride;
@@ -184,140 +196,6 @@ __global__ __launch_bounds__(64 * kBigWaves) void k_gemm_big_f16(const f16* __re
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int tt = t0 + cw * 8 + t, col = tt * 16 + n;
-      if (tt < mp.ntiles && col < N)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) o[(size_t)(mb * 16 + 4 * j + v) * N + col] = acc[b][t][v];
-    }
-  }
-}
-
-// The settle's keys and values at many rows, straight from the int4 codes
-// (Wk/Wv of every layer): the block layout of k_gemm_big_f16 (256 rows,
-// 16 weight tiles, eight waves; here wave w multiplies all 16 row blocks by
-// tiles 2w and 2w + 1), with each weight fragment decoded in registers into two
-// exact f16 halves: hi = f16(q·s) (a packed f16 product, rounded once) and
-// lo = q·s − hi (a packed f16 FMA; exact, since q·s has at most 15
-// significant bits and the residual is a multiple of the scale's ulp). The
-// products x·hi + x·lo sum the exact dequantised weight.
-//  - row fragments: every 32-column step through a kKvStages LDS ring (each
-//    wave copies two of the 16), kKvStages − 1 steps ahead;
-//  - codes and scales: every 128-column span into an LDS double buffer (each
-//    wave copies two tiles' codes, non-temporal, and their scales), one span
-//    ahead; each step reads its code word and scale of every tile.
-// Splits fall on span boundaries, so every step of a split is a real one.
-static constexpr int kKvNT = 16, kKvStages = 3;
-// row blocks and weight tiles a wave multiplies (kKvRB·kKvTW = 32 of the
-// block's 16 × 16): each of the block's tiles is decoded by 16/kKvRB waves.
-// Every row block a wave and two tiles each, so that each tile is decoded
-// once: measured 66 → 64 µs a 256-row call against four row blocks × eight
-// tiles (each tile decoded by four waves) and 64 µs for eight × four.
-static constexpr int kKvRB = 16, kKvTW = 2;
-static_assert(kKvRB * kKvTW == 32 && 16 % kKvRB == 0, "eight waves cover 16 row blocks x 16 tiles");
-
-__global__ __launch_bounds__(64 * kBigWaves) void k_gemm_kv_i4(const f16* __restrict__ xa, int K,
-                                                              int mblocks,
-                                                              const uint4* __restrict__ codes,
-                                                              const uint32_t* __restrict__ scales,
-                                                              TileMap mp, int N, int splits,
-                                                              int sps, float* __restrict__ out,
-                                                              long split_stride) {
-  constexpr int D = kKvStages - 1;
-  static_assert(D == 2, "the waits below count two steps of row copies in flight");
-  __shared__ h8 ast[kKvStages][16][64];   // row fragments of a step
-  __shared__ uint4 cst[2][kKvNT][64];     // codes of a span: tile, lane
-  __shared__ uint32_t sst[2][kKvNT][32];  // scales of a span: tile, (n, pair)
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rw = wave % (16 / kKvRB), cw = wave / (16 / kKvRB);
-  const int KT = K >> 7;
-  const int sp = blockIdx.x % splits;
-  const int p0 = sp * sps, p1 = min(KT, p0 + sps);
-  const int s1 = 4 * p1;
-  const int t0 = (blockIdx.x / splits) * kKvNT;
-  const h8* xg = reinterpret_cast<const h8*>(xa);
-  const h8* asrc[2];
-  const uint4* csrc[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    asrc[i] = xg + (size_t)(2 * wave + i) * 2 * K + lane;
-    csrc[i] = codes + (size_t)map_tile(mp, min(t0 + 2 * wave + i, mp.ntiles - 1)) * KT * 64 + lane;
-  }
-  // a dword copy moves 64 dwords: tiles 2w (lanes 0–31) and 2w + 1 (32–63)
-  const uint32_t* ssrc =
-      scales + (size_t)map_tile(mp, min(t0 + 2 * wave + (lane >> 5), mp.ntiles - 1)) * KT * 32 +
-      (lane & 31);
-  auto issue_a = [&](int s) {
-    const int sc = min(s, s1 - 1);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) copy16(asrc[i] + (size_t)sc * 64, &ast[s % kKvStages][2 * wave + i][0]);
-  };
-  auto issue_c = [&](int p) {
-    const int pc = min(p, p1 - 1);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_global_load_lds(csrc[i] + (size_t)pc * 64, &cst[p & 1][2 * wave + i][0], 16, 0, 2);
-    __builtin_amdgcn_global_load_lds(ssrc + (size_t)pc * 32, &sst[p & 1][2 * wave][0], 4, 0, 0);
-  };
-  f4 acc[kKvRB][kKvTW];
-#pragma unroll
-  for (int b = 0; b < kKvRB; ++b)
-#pragma unroll
-    for (int t = 0; t < kKvTW; ++t) acc[b][t] = (f4){0.f, 0.f, 0.f, 0.f};
-  issue_c(p0);
-  issue_a(4 * p0);
-  issue_a(4 * p0 + 1);
-  const int n = lane & 15;
-  const uint32_t* cw32 = reinterpret_cast<const uint32_t*>(&cst[0][0][0]);
-  for (int p = p0; p < p1; ++p) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = 4 * p + u;
-      // this wave's copies of step s (and, at u = 0, of span p) are in: the
-      // copies issued after them may remain (two a step, three more with
-      // each span's codes, issued at its previous span's first step)
-      if (u == 0 || u == 3)
-        wait_vm<2>();
-      else
-        wait_vm<5>();
-      lds_barrier();
-      issue_a(s + D);
-      if (u == 0) issue_c(p + 1);
-      h8 af[kKvRB];
-#pragma unroll
-      for (int b = 0; b < kKvRB; ++b) af[b] = ast[s % kKvStages][rw * kKvRB + b][lane];
-      // this step's code word and scale of each tile, read from the span's
-      // buffers (rewritten only after the span's last step)
-#pragma unroll
-      for (int t = 0; t < kKvTW; ++t) {
-        const int tile = cw * kKvTW + t;
-        const uint32_t word = cw32[(((size_t)(p & 1) * kKvNT + tile) * 64 + lane) * 4 + u];
-        const uint32_t sb = sst[p & 1][tile][2 * n + (u >> 1)];
-        const f16 sh = __builtin_bit_cast(f16, (uint16_t)((u & 1) ? (sb >> 16) : (sb & 0xffffu)));
-        const h8 q = unpack_i4(word);
-        const h8 s8 = (h8){sh, sh, sh, sh, sh, sh, sh, sh};
-        const h8 hi = q * s8;
-        const h8 lo = __builtin_elementwise_fma(q, s8, -hi);
-#pragma unroll
-        for (int b = 0; b < kKvRB; ++b) {
-          acc[b][t] = mfma16(af[b], hi, acc[b][t]);
-          acc[b][t] = mfma16(af[b], lo, acc[b][t]);
-        }
-        // keep each tile's decode beside its products (the decoded halves of
-        // all of a wave's tiles at once need more registers than two waves a
-        // SIMD leave)
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-  const int j = lane >> 4;
-  float* o = out + (size_t)sp * split_stride;
-#pragma unroll
-  for (int b = 0; b < kKvRB; ++b) {
-    const int mb = rw * kKvRB + b;
-    if (mb >= mblocks) continue;
-#pragma unroll
-    for (int t = 0; t < kKvTW; ++t) {
-      const int tt = t0 + cw * kKvTW + t, col = tt * 16 + n;
       if (tt < mp.ntiles && col < N)
 #pragma unroll
         for (int v = 0; v < 4; ++v) o[(size_t)(mb * 16 + 4 * j + v) * N + col] = acc[b][t][v];
@@ -536,19 +414,19 @@ __global__ __launch_bounds__(kThreads) void k_to_a(const float* __restrict__ x, 
 static constexpr int kChunk = 256;
 
 // Split-summed rows (the settle's t = fc·taps), each chunk's Σt², and
-// u = t ⊙ w (w: hidden_norm's gain) as the one-plane A-layout operand of the
-// settle's K/V projection; rms's per-row scale is applied to that
+// u = t ⊙ w (w: hidden_norm's gain) as the two-plane A-layout operand of the
+// settle's K/V projection (plane 1 at xa + ps); rms's per-row scale is applied to that
 // projection's output (k_settle_kv), so no separate norm pass runs.
 __global__ __launch_bounds__(kThreads) void k_rowsum_sq(const float* __restrict__ part, int splits,
                                                         long ss, int N, const float* __restrict__ w,
-                                                        f16* __restrict__ xa,
+                                                        f16* __restrict__ xa, long ps,
                                                         float* __restrict__ sqp, int nchunk) {
   __shared__ float red[4];
   const int r = blockIdx.y, c = blockIdx.x, i = c * kChunk + threadIdx.x;
   float v = 0.f;
   if (i < N) {
     v = sum_splits(part + (size_t)r * N + i, splits, ss);
-    put_a(xa, 0, (size_t)(r >> 4) * 16 * N + a_idx(r & 15, i), v * w[i]);
+    put_a(xa, ps, (size_t)(r >> 4) * 16 * N + a_idx(r & 15, i), v * w[i]);
   }
   const float sq = block_sum(v * v, red);
   if (threadIdx.x == 0) sqp[(size_t)r * nchunk + c] = sq;
@@ -1379,24 +1257,23 @@ void gemm_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks, c
     launch_f16<2, 1>(st, xa, 0, K, mblocks, w, map, N, splits, sps, out, ss);
 }
 
-int kv_i4_groups(int ntiles) { return (int)cdiv(ntiles, kKvNT); }
-
-void gemm_kv_i4(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint8_t* codes,
-                const uint16_t* scales, TileMap map, int N, int splits, int sps, float* out,
-                long ss) {
-  const unsigned blocks = cdiv(map.ntiles, kKvNT) * splits;
-  k_gemm_kv_i4<<<blocks, 64 * kBigWaves, 0, st>>>(
-      reinterpret_cast<const f16*>(xa), K, mblocks, reinterpret_cast<const uint4*>(codes),
-      reinterpret_cast<const uint32_t*>(scales), map, N, splits, sps, out, ss);
-}
-
-void gemm_big_f16(hipStream_t st, const uint16_t* xa, int K, int mblocks, const uint16_t* w,
-                  TileMap map, int N, int splits, int sps, float* out, long ss) {
+void gemm_big_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks,
+                  const uint16_t* w, TileMap map, int N, int splits, int sps, float* out,
+                  long ss) {
   const unsigned blocks = cdiv(map.ntiles, kBigNT) * splits;
-  const size_t lds = sizeof(h8) * kBigStages * kBigFrags * 64;
-  k_gemm_big_f16<<<blocks, 64 * kBigWaves, lds, st>>>(reinterpret_cast<const f16*>(xa), K, mblocks,
-                                                reinterpret_cast<const f16*>(w), map, N, splits,
-                                                sps, out, ss);
+  const f16* x = reinterpret_cast<const f16*>(xa);
+  const f16* wt = reinterpret_cast<const f16*>(w);
+  // the two-plane ring takes 144 KB of the compute unit's 160 KB LDS
+  static const hipError_t lds_ok = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_gemm_big_f16<2>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)Big<2>::kLds);
+  (void)lds_ok;  // a refusal surfaces as the launch's error
+  if (ps)
+    k_gemm_big_f16<2><<<blocks, 64 * kBigWaves, Big<2>::kLds, st>>>(x, ps, K, mblocks, wt, map, N,
+                                                                     splits, sps, out, ss);
+  else
+    k_gemm_big_f16<1><<<blocks, 64 * kBigWaves, Big<1>::kLds, st>>>(x, 0, K, mblocks, wt, map, N,
+                                                                     splits, sps, out, ss);
 }
 
 template <int R, int PL>
@@ -1441,10 +1318,10 @@ void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa, l
 }
 
 void rowsum_sq(hipStream_t st, const float* part, int splits, long ss, int rows, int N,
-               const float* w, uint16_t* xa, float* sqp) {
+               const float* w, uint16_t* xa, long ps, float* sqp) {
   const int nch = cdiv(N, kChunk);
   k_rowsum_sq<<<dim3(nch, rows), kThreads, 0, st>>>(part, splits, ss, N, w,
-                                                    reinterpret_cast<f16*>(xa), sqp, nch);
+                                                    reinterpret_cast<f16*>(xa), ps, sqp, nch);
 }
 
 // Probe launches; the caller times them (one workgroup of 256 threads is
