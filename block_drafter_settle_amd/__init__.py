@@ -59,6 +59,8 @@ _SIGS = {
     "dflash_settle": ([C.c_void_p, C.c_int64, C.c_int32, C.c_void_p], C.c_int),
     "dflash_block": ([C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
                       C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
+    "dflash_block_noalloc": ([C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
+                              C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
     "dflash_truncate": ([C.c_void_p, C.c_int64], C.c_int),
     "dflash_span": ([C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
     "dflash_sync": ([C.c_void_p], C.c_int),
@@ -119,6 +121,10 @@ def dflash_settle(h, first_pos, n, taps):
 
 def dflash_block(h, anchor, a, k, width, logits, cand, unary, score, chosen):
     return lib().dflash_block(h, anchor, a, k, width, logits, cand, unary, score, chosen)
+
+
+def dflash_block_noalloc(h, anchor, a, k, width, logits, cand, unary, score, chosen):
+    return lib().dflash_block_noalloc(h, anchor, a, k, width, logits, cand, unary, score, chosen)
 
 
 def dflash_truncate(h, pos):
@@ -207,6 +213,11 @@ class Drafter:
               score_ptr, chosen_ptr):
         _check(lib().dflash_block(self.h, anchor, a, k, width, logits_ptr, cand_ptr, unary_ptr,
                                   score_ptr, chosen_ptr), self.h)
+
+    def block_noalloc(self, anchor: int, a: int, k: int, width: int, logits_ptr, cand_ptr,
+                      unary_ptr, score_ptr, chosen_ptr):
+        _check(lib().dflash_block_noalloc(self.h, anchor, a, k, width, logits_ptr, cand_ptr,
+                                          unary_ptr, score_ptr, chosen_ptr), self.h)
 
     def truncate(self, pos: int):
         _check(lib().dflash_truncate(self.h, pos), self.h)

@@ -15,8 +15,10 @@
 #include <cstdio>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <string>
 #include <thread>
+#include <type_traits>
 #include <vector>
 
 #include "internal.h"
@@ -124,6 +126,16 @@ void repack_i4(const dflash_i4& m, int N, int K, uint8_t* codes, uint16_t* scale
 
 }  // namespace
 
+// Per-call scratch of the block pass: activations, GEMM and attention
+// partial results, the selection's lists and counters.
+struct BlockScratch {
+  float *h = nullptr, *x = nullptr, *dsum_a = nullptr, *dsum_m = nullptr, *kb = nullptr,
+        *vb = nullptr, *pacc = nullptr, *pml = nullptr, *part = nullptr, *logits = nullptr,
+        *hp = nullptr, *sqp = nullptr;
+  uint16_t *xa = nullptr, *xca = nullptr, *qa = nullptr, *ya = nullptr, *ma = nullptr;
+  dfl::SelectScratch sel{};
+};
+
 struct I4Set {  // one int4 product of every layer, tiles [layer][tiles][K/128]
   uint8_t* codes = nullptr;
   uint16_t* scales = nullptr;
@@ -151,14 +163,12 @@ struct dflash {
   // context store
   float *sk = nullptr, *sv = nullptr;
   long first = 0, len = 0;
-  // block scratch
-  float *h = nullptr, *x = nullptr, *dsum_a = nullptr, *dsum_m = nullptr, *kb = nullptr,
-        *vb = nullptr, *pacc = nullptr, *pml = nullptr, *part = nullptr, *logits = nullptr,
-        *hp = nullptr;
-  uint16_t *xa = nullptr, *xca = nullptr, *qa = nullptr, *ya = nullptr, *ma = nullptr;
-  float* sqp = nullptr;
-  dfl::SelectScratch sel_sc{};
-  // settle scratch
+  int dev = 0;  // the device the handle was created on
+  // block scratch (the handle's own; dflash_block_noalloc carves the same set
+  // from the library's static array instead)
+  BlockScratch bs;
+  // settle scratch (part and sqp are shared with bs)
+  float *part = nullptr, *sqp = nullptr;
   uint16_t *taps_a = nullptr, *t_a = nullptr;
   long part_floats = 0;
   int stage_cols = 0;  // widest activation the staging buffer holds
@@ -408,6 +418,92 @@ int attn_chunk(long n, int* nchunks) {
   return (int)c;
 }
 
+// ---- the static scratch of dflash_block_noalloc
+
+// Bytes of the library's static scratch on each GPU: a block pass's per-call
+// scratch of the 27B-shaped sidecar takes about 26 MB of it.
+constexpr size_t kNoallocScratchBytes = DFLASH_NOALLOC_SCRATCH_BYTES;
+
+}  // namespace
+
+// The file-scope device array dflash_block_noalloc takes its scratch from.
+// In host code its name is only a stand-in: its device address is looked up
+// once per device (hipGetSymbolAddress) and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+bool g_scratch_tried[kMaxDevices] = {};
+
+// Look the array's address up on device `dev` (current), once.
+void scratch_init(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_tried[dev]) return;
+  g_scratch_tried[dev] = true;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess)
+    g_scratch[dev] = p;
+  else
+    (void)hipGetLastError();
+}
+
+void* scratch_ptr(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch[dev];
+}
+
+// Lay the block pass's scratch out from base (256-byte aligned pieces); with
+// base == nullptr only count. Returns the bytes taken. The logits are the
+// caller's (no scratch copy).
+size_t carve_block_scratch(const dflash* d, uint8_t* base, BlockScratch* out) {
+  size_t off = 0;
+  auto take = [&](auto** p, size_t count) {
+    using T = std::remove_pointer_t<std::remove_reference_t<decltype(*p)>>;
+    off = (off + 255) / 256 * 256;
+    if (base) *p = reinterpret_cast<T*>(base + off);
+    off += count * sizeof(T);
+  };
+  BlockScratch tmp;
+  BlockScratch& b = out ? *out : tmp;
+  const size_t hs = d->hs;
+  long part = 0;
+  part = std::max(part, (long)dfl::f16_block_splits(d->hs) * 16 * d->P);
+  part = std::max(part, (long)dfl::i4_block_splits(d->hs, kKsQkv) * 16 * (d->qd + 2 * d->kd));
+  part = std::max(part, (long)dfl::i4_block_splits(d->qd, kKsO) * 16 * d->hs);
+  part = std::max(part, (long)dfl::i4_block_splits(d->ffn, kKsDown) * 16 * d->hs);
+  const size_t slots = (size_t)d->kv * (dfl::kAttnMaxChunks + 1) * (d->nh / d->kv);
+  const size_t cap = (size_t)dfl::topk_cap(d->V, d->top);
+  take(&b.h, 16 * hs);
+  take(&b.x, 16 * hs);
+  take(&b.dsum_a, 16 * (size_t)d->P);
+  take(&b.dsum_m, 16 * (size_t)d->P);
+  take(&b.kb, 16 * (size_t)d->kd);
+  take(&b.vb, 16 * (size_t)d->kd);
+  take(&b.pacc, slots * 16 * d->hd);
+  take(&b.pml, slots * 16 * 2);
+  take(&b.part, (size_t)part);
+  take(&b.hp, 16 * (size_t)d->rank);
+  take(&b.sqp, 16 * (size_t)std::max(dfl::row_chunks(d->hs), dfl::conv1_chunks(d->hs)));
+  take(&b.xa, 2 * 16 * hs);
+  take(&b.xca, 2 * 16 * hs);
+  take(&b.qa, 2 * (size_t)d->nh * 16 * d->hd);
+  take(&b.ya, 2 * 16 * (size_t)d->qd);
+  take(&b.ma, 2 * 16 * (size_t)d->ffn);
+  take(&b.sel.gmax, 16 * (size_t)((d->V + 255) / 256));
+  take(&b.sel.counters, 16);
+  take(&b.sel.lv, 16 * cap);
+  take(&b.sel.li, 16 * cap);
+  take(&b.sel.tab, (size_t)d->top * (1 + 15 * d->top));
+  take(&b.sel.best, (size_t)(1 + 15 * d->top));
+  b.logits = nullptr;
+  return off;
+}
+
 }  // namespace
 
 // ====================================================================== API
@@ -542,35 +638,43 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   const size_t slots = (size_t)d->kv * (dfl::kAttnMaxChunks + 1) * rep;
   d->part_floats = partial_need(d);
   const size_t sel_cap = (size_t)dfl::topk_cap(d->V, d->top);
-  if (!rc) rc = dev_alloc(d, &d->h, 16 * hs, "scratch");
-  if (!rc) rc = dev_alloc(d, &d->x, 16 * hs, "scratch");
-  if (!rc) rc = dev_alloc(d, &d->dsum_a, 16 * d->P, "scratch");
-  if (!rc) rc = dev_alloc(d, &d->dsum_m, 16 * d->P, "scratch");
-  if (!rc) rc = dev_alloc(d, &d->kb, 16 * d->kd, "scratch");
-  if (!rc) rc = dev_alloc(d, &d->vb, 16 * d->kd, "scratch");
-  if (!rc) rc = dev_alloc(d, &d->pacc, slots * 16 * d->hd, "attention partials");
-  if (!rc) rc = dev_alloc(d, &d->pml, slots * 16 * 2, "attention partials");
+  BlockScratch& b = d->bs;
+  if (!rc) rc = dev_alloc(d, &b.h, 16 * hs, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.x, 16 * hs, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.dsum_a, 16 * d->P, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.dsum_m, 16 * d->P, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.kb, 16 * d->kd, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.vb, 16 * d->kd, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.pacc, slots * 16 * d->hd, "attention partials");
+  if (!rc) rc = dev_alloc(d, &b.pml, slots * 16 * 2, "attention partials");
   if (!rc) rc = dev_alloc(d, &d->part, d->part_floats, "GEMM partials");
-  if (!rc) rc = dev_alloc(d, &d->logits, (size_t)16 * d->V, "logits");
-  if (!rc) rc = dev_alloc(d, &d->hp, 16 * d->rank, "selector projection");
-  if (!rc) rc = dev_alloc(d, &d->sel_sc.gmax, (size_t)16 * ((d->V + 255) / 256), "selection");
-  if (!rc) rc = dev_alloc(d, &d->sel_sc.counters, 16, "selection");
-  if (!rc) rc = dev_alloc(d, &d->sel_sc.lv, 16 * sel_cap, "selection candidates");
-  if (!rc) rc = dev_alloc(d, &d->sel_sc.li, 16 * sel_cap, "selection candidates");
+  b.part = d->part;
+  if (!rc) rc = dev_alloc(d, &b.logits, (size_t)16 * d->V, "logits");
+  if (!rc) rc = dev_alloc(d, &b.hp, 16 * d->rank, "selector projection");
+  if (!rc) rc = dev_alloc(d, &b.sel.gmax, (size_t)16 * ((d->V + 255) / 256), "selection");
+  if (!rc) rc = dev_alloc(d, &b.sel.counters, 16, "selection");
+  if (!rc) rc = dev_alloc(d, &b.sel.lv, 16 * sel_cap, "selection candidates");
+  if (!rc) rc = dev_alloc(d, &b.sel.li, 16 * sel_cap, "selection candidates");
   // the block's activation operands, two planes each
-  if (!rc) rc = dev_alloc(d, &d->xa, 2 * 16 * hs, "scratch");
-  if (!rc) rc = dev_alloc(d, &d->xca, 2 * 16 * hs, "scratch");
-  if (!rc) rc = dev_alloc(d, &d->qa, 2 * (size_t)d->nh * 16 * d->hd, "scratch");
-  if (!rc) rc = dev_alloc(d, &d->ya, 2 * 16 * d->qd, "scratch");
-  if (!rc) rc = dev_alloc(d, &d->ma, 2 * 16 * d->ffn, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.xa, 2 * 16 * hs, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.xca, 2 * 16 * hs, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.qa, 2 * (size_t)d->nh * 16 * d->hd, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.ya, 2 * 16 * d->qd, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.ma, 2 * 16 * d->ffn, "scratch");
   d->stage_cols = std::max(std::max(d->tw, d->ffn), std::max(d->qd, hs));
   // the settle's operands, two planes of 256 rows each
   if (!rc) rc = dev_alloc(d, &d->taps_a, 2 * (size_t)kSettleRows * d->stage_cols, "settle scratch");
   if (!rc) rc = dev_alloc(d, &d->t_a, 2 * (size_t)kSettleRows * hs, "settle scratch");
-  if (!rc) rc = dev_alloc(d, &d->sqp, (size_t)kSettleRows * ((hs + 255) / 256), "norm scratch");
-  if (!rc) rc = dev_alloc(d, &d->sel_sc.tab, (size_t)d->top * (1 + 15 * d->top), "selector table");
-  if (!rc) rc = dev_alloc(d, &d->sel_sc.best, (size_t)(1 + 15 * d->top), "selector table");
+  if (!rc)
+    rc = dev_alloc(d, &d->sqp,
+                   (size_t)std::max(kSettleRows * dfl::row_chunks(hs), 16 * dfl::conv1_chunks(hs)),
+                   "norm scratch");
+  b.sqp = d->sqp;
+  if (!rc) rc = dev_alloc(d, &b.sel.tab, (size_t)d->top * (1 + 15 * d->top), "selector table");
+  if (!rc) rc = dev_alloc(d, &b.sel.best, (size_t)(1 + 15 * d->top), "selector table");
   if (!rc) rc = hip_check(nullptr, hipDeviceSynchronize(), "create");
+  if (!rc) rc = hip_check(nullptr, hipGetDevice(&d->dev), "create: current device");
+  if (!rc) scratch_init(d->dev);
   return done(rc);
 }
 
@@ -580,8 +684,8 @@ int dflash_probe_peaks(dflash_t* d, int32_t reps, double* read_gbs, double* mfma
     return fail(d, DFLASH_EINVAL, "probe_peaks: reps must be in [1, 100], outputs non-null");
   hipStream_t st = d->st;
   // the sinks are written only on impossible values; any device word serves
-  uint32_t* usink = reinterpret_cast<uint32_t*>(d->sel_sc.counters);
-  float* fsink = reinterpret_cast<float*>(d->sel_sc.counters);
+  uint32_t* usink = reinterpret_cast<uint32_t*>(d->bs.sel.counters);
+  float* fsink = reinterpret_cast<float*>(d->bs.sel.counters);
   const long bytes = (long)d->V * d->hs * 2 / 16 * 16;
   constexpr int kWgs = 512, kSteps = 4096;  // two waves on every SIMD
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -744,15 +848,23 @@ int dflash_settle(dflash_t* d, int64_t first_pos, int32_t n, const float* taps) 
   return DFLASH_OK;
 }
 
-int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t width, float* logits,
-                 int32_t* cand, float* unary, float* score, int32_t* chosen) {
-  if (!d) return DFLASH_EINVAL;
+// Argument checks shared by the block entry points.
+static int block_args(dflash* d, int32_t anchor, int64_t a, int32_t k, int32_t width,
+                      const int32_t* cand, const float* unary, const float* score,
+                      const int32_t* chosen) {
   if (k < 1 || k >= d->B) return fail(d, DFLASH_EINVAL, "block: k must be in [1, block)");
   if (width < d->top || width > d->V)
     return fail(d, DFLASH_EINVAL, "block: width must be in [selector_top, vocab]");
   if (anchor < 0 || anchor >= d->V) return fail(d, DFLASH_EINVAL, "block: anchor outside the vocabulary");
   if (a < 0) return fail(d, DFLASH_EINVAL, "block: a must be >= 0");
   if (!cand || !unary || !score || !chosen) return fail(d, DFLASH_EINVAL, "block: null output");
+  return DFLASH_OK;
+}
+
+// The block pass on the scratch set b (arguments already checked).
+static int block_pass(dflash* d, const BlockScratch& b, int32_t anchor, int64_t a, int32_t k,
+                      int32_t width, float* logits, int32_t* cand, float* unary, float* score,
+                      int32_t* chosen) {
   hipStream_t st = d->st;
   const int hs = d->hs, B = d->B;
   const float scale = std::pow((float)d->hd, -0.5f);
@@ -774,7 +886,7 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
   // Each sub-layer's rms is folded into its neighbours: the producer of h
   // (embed, conv1) writes h, its partial sums of squares and h ⊙ gain as the
   // kernel projection's input; conv0 applies the per-row scale.
-  dfl::embed(st, d->embed, anchor, d->mask, B, hs, d->h, d->sqp, d->in_norm, d->xa, psh);
+  dfl::embed(st, d->embed, anchor, d->mask, B, hs, b.h, b.sqp, d->in_norm, b.xa, psh);
   tm_mark(d, DFLASH_ST_CONV);
   int nch = dfl::row_chunks(hs);  // sums of squares per row: embed's, then conv1's
   for (int l = 0; l < d->L; ++l) {
@@ -782,19 +894,19 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     const float* mbase = d->mlp_base + (size_t)l * 2 * d->kn * hs;
     const float* post = d->post_norm + (size_t)l * hs;
     // attention: conv_in, q/k/v, norms + rotary
-    dfl::gemm_f16_block(st, d->xa, psh, hs, d->attn_kproj + l * kp_layer,
-                        dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, d->part, ssd);
+    dfl::gemm_f16_block(st, b.xa, psh, hs, d->attn_kproj + l * kp_layer,
+                        dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, b.part, ssd);
     tm_mark(d, DFLASH_ST_KPROJ);
-    dfl::conv0(st, d->h, d->sqp, nch, d->in_norm + (size_t)l * hs, d->eps, d->part, spk.S, ssd, ab,
-               B, hs, d->gs, d->kn, d->xca, psh, d->dsum_a);
+    dfl::conv0(st, b.h, b.sqp, nch, d->in_norm + (size_t)l * hs, d->eps, b.part, spk.S, ssd, ab,
+               B, hs, d->gs, d->kn, b.xca, psh, b.dsum_a);
     tm_mark(d, DFLASH_ST_CONV);
-    dfl::gemm_i4_block(st, d->xca, psh, hs, d->qkv.codes + i4l_qkv * 1024 * l,
+    dfl::gemm_i4_block(st, b.xca, psh, hs, d->qkv.codes + i4l_qkv * 1024 * l,
                        d->qkv.scales + i4l_qkv * 64 * l,
                        dfl::TileMap{d->qkv.tiles, d->qkv.tiles, 0, 0}, d->qd + 2 * d->kd, sqk.per,
-                       d->part, ssq);
+                       b.part, ssq);
     tm_mark(d, DFLASH_ST_QKV);
-    dfl::qkv_post(st, d->part, sqk.S, ssq, B, d->nh, d->kv, d->hd, d->q_norm + (size_t)l * d->hd,
-                  d->k_norm + (size_t)l * d->hd, d->inv, a, d->rot[l], d->eps, d->qa, psq, d->kb, d->vb);
+    dfl::qkv_post(st, b.part, sqk.S, ssq, B, d->nh, d->kv, d->hd, d->q_norm + (size_t)l * d->hd,
+                  d->k_norm + (size_t)l * d->hd, d->inv, a, d->rot[l], d->eps, b.qa, psq, b.kb, b.vb);
     tm_mark(d, DFLASH_ST_QKPOST);
     // attention over the layer's context range and the block's rows
     long lo, n;
@@ -802,60 +914,89 @@ int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t widt
     int nchunks = 0;
     const int chunk = attn_chunk(n, &nchunks);
     const size_t lrow = (size_t)l * d->cap + (lo - d->first);
-    dfl::attention(st, d->qa, psq, d->sk + lrow * d->kd, d->sv + lrow * d->kd, d->kb, d->vb, B, d->nh,
-                   d->kv, d->hd, (int)n, lo, a, d->windows[l], chunk, nchunks, scale, d->pacc,
-                   d->pml);
+    dfl::attention(st, b.qa, psq, d->sk + lrow * d->kd, d->sv + lrow * d->kd, b.kb, b.vb, B, d->nh,
+                   d->kv, d->hd, (int)n, lo, a, d->windows[l], chunk, nchunks, scale, b.pacc,
+                   b.pml);
     tm_mark(d, DFLASH_ST_ATTN);
-    dfl::attn_merge(st, d->pacc, d->pml, d->nh, d->kv, d->hd, nchunks, B, d->ya, psy);
+    dfl::attn_merge(st, b.pacc, b.pml, d->nh, d->kv, d->hd, nchunks, B, b.ya, psy);
     tm_mark(d, DFLASH_ST_ATTN);
     // o, conv_out into the residual (and the MLP norm's input)
-    dfl::gemm_i4_block(st, d->ya, psy, d->qd, d->o.codes + i4l_o * 1024 * l,
+    dfl::gemm_i4_block(st, b.ya, psy, d->qd, d->o.codes + i4l_o * 1024 * l,
                        d->o.scales + i4l_o * 64 * l, dfl::TileMap{d->o.tiles, d->o.tiles, 0, 0},
-                       hs, so.per, d->part, ssh);
+                       hs, so.per, b.part, ssh);
     tm_mark(d, DFLASH_ST_O);
-    dfl::conv1(st, d->h, d->part, so.S, ssh, d->dsum_a, ab, B, hs, d->gs, d->kn, d->sqp, post,
-               d->xa, psh);
+    dfl::conv1(st, b.h, b.part, so.S, ssh, b.dsum_a, ab, B, hs, d->gs, d->kn, b.sqp, post,
+               b.xa, psh);
     nch = nc1;
     tm_mark(d, DFLASH_ST_CONV);
     // MLP, wrapped the same way
-    dfl::gemm_f16_block(st, d->xa, psh, hs, d->mlp_kproj + l * kp_layer,
-                        dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, d->part, ssd);
+    dfl::gemm_f16_block(st, b.xa, psh, hs, d->mlp_kproj + l * kp_layer,
+                        dfl::TileMap{d->ptiles, d->ptiles, 0, 0}, d->P, b.part, ssd);
     tm_mark(d, DFLASH_ST_KPROJ);
-    dfl::conv0(st, d->h, d->sqp, nch, post, d->eps, d->part, spk.S, ssd, mbase, B, hs, d->gs, d->kn,
-               d->xca, psh, d->dsum_m);
+    dfl::conv0(st, b.h, b.sqp, nch, post, d->eps, b.part, spk.S, ssd, mbase, B, hs, d->gs, d->kn,
+               b.xca, psh, b.dsum_m);
     tm_mark(d, DFLASH_ST_CONV);
-    dfl::gemm_glu_stream(st, d->xca, psh, hs, d->gu.codes + i4l_gu * 1024 * l,
-                         d->gu.scales + i4l_gu * 64 * l, d->ffn / 16, d->ma, psm);
+    dfl::gemm_glu_stream(st, b.xca, psh, hs, d->gu.codes + i4l_gu * 1024 * l,
+                         d->gu.scales + i4l_gu * 64 * l, d->ffn / 16, b.ma, psm);
     tm_mark(d, DFLASH_ST_GLU);
-    dfl::gemm_i4_block(st, d->ma, psm, d->ffn, d->down.codes + i4l_dn * 1024 * l,
+    dfl::gemm_i4_block(st, b.ma, psm, d->ffn, d->down.codes + i4l_dn * 1024 * l,
                        d->down.scales + i4l_dn * 64 * l,
-                       dfl::TileMap{d->down.tiles, d->down.tiles, 0, 0}, hs, sdn.per, d->part, ssh);
+                       dfl::TileMap{d->down.tiles, d->down.tiles, 0, 0}, hs, sdn.per, b.part, ssh);
     tm_mark(d, DFLASH_ST_DOWN);
     // conv_out into the residual, and the next layer's attention-norm input
     // (the final norm runs on its own below)
     const float* next = l + 1 < d->L ? d->in_norm + (size_t)(l + 1) * hs : nullptr;
-    dfl::conv1(st, d->h, d->part, sdn.S, ssh, d->dsum_m, mbase, B, hs, d->gs, d->kn, d->sqp, next,
-               d->xa, psh);
+    dfl::conv1(st, b.h, b.part, sdn.S, ssh, b.dsum_m, mbase, B, hs, d->gs, d->kn, b.sqp, next,
+               b.xa, psh);
     tm_mark(d, DFLASH_ST_CONV);
     if (d->trace)
-      (void)hipMemcpyAsync(d->trace + (size_t)l * B * hs, d->h, sizeof(float) * B * hs,
+      (void)hipMemcpyAsync(d->trace + (size_t)l * B * hs, b.h, sizeof(float) * B * hs,
                            hipMemcpyDeviceToDevice, st);
   }
   // the final norm (the head's input), then the head over rows 1..k and
   // the selector projection
-  dfl::norm_apply(st, d->h, d->sqp, nc1, B, hs, d->norm, d->eps, d->x, d->xa, psh);
+  dfl::norm_apply(st, b.h, b.sqp, nc1, B, hs, d->norm, d->eps, b.x, b.xa, psh);
   tm_mark(d, DFLASH_ST_CONV);
-  float* lg = logits ? logits : d->logits;
-  dfl::head_sel(st, d->xa, psh, hs, d->head, width, k, lg, d->sel, d->rank, d->hp, d->sel_sc);
+  float* lg = logits ? logits : b.logits;
+  dfl::head_sel(st, b.xa, psh, hs, d->head, width, k, lg, d->sel, d->rank, b.hp, b.sel);
   tm_mark(d, DFLASH_ST_HEAD);
-  dfl::select_all(st, lg, true, k, width, d->top, d->hp + d->rank, d->rank, d->pbook, d->cbook,
-                  d->V, anchor, nullptr, d->sel_sc, cand, unary, score, chosen);
+  dfl::select_all(st, lg, true, k, width, d->top, b.hp + d->rank, d->rank, d->pbook, d->cbook,
+                  d->V, anchor, nullptr, b.sel, cand, unary, score, chosen);
   tm_mark(d, DFLASH_ST_SELECT);
-  d->last_k = k;
   const int rc = launch_check(d, "block");
   tm_end(d);
   d->tm.blocks += d->tm.on;
   return rc;
+}
+
+int dflash_block(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t width, float* logits,
+                 int32_t* cand, float* unary, float* score, int32_t* chosen) {
+  if (!d) return DFLASH_EINVAL;
+  if (int rc = block_args(d, anchor, a, k, width, cand, unary, score, chosen)) return rc;
+  const int rc = block_pass(d, d->bs, anchor, a, k, width, logits, cand, unary, score, chosen);
+  d->last_k = k;
+  return rc;
+}
+
+int dflash_block_noalloc(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int32_t width,
+                         float* logits, int32_t* cand, float* unary, float* score,
+                         int32_t* chosen) {
+  if (!d) return DFLASH_EINVAL;
+  if (int rc = block_args(d, anchor, a, k, width, cand, unary, score, chosen)) return rc;
+  if (!logits) return fail(d, DFLASH_EINVAL, "block_noalloc: logits must be a caller buffer");
+  const size_t need = carve_block_scratch(d, nullptr, nullptr);
+  if (need > kNoallocScratchBytes)
+    return fail(d, DFLASH_EINVAL,
+                "block_noalloc: this geometry needs %zu bytes of scratch, more than the %zu the "
+                "library holds",
+                need, kNoallocScratchBytes);
+  void* base = scratch_ptr(d->dev);
+  if (!base)
+    return fail(d, DFLASH_EHIP, "block_noalloc: the static scratch of device %d is unavailable",
+                d->dev);
+  BlockScratch b;
+  carve_block_scratch(d, static_cast<uint8_t*>(base), &b);
+  return block_pass(d, b, anchor, a, k, width, logits, cand, unary, score, chosen);
 }
 
 // --------------------------------------------------------------- debug
@@ -995,11 +1136,11 @@ int dflash_debug_last_block(dflash_t* d, float* hidden, float* hp) {
   if (!d) return DFLASH_EINVAL;
   int rc = DFLASH_OK;
   if (hidden)
-    rc = hip_check(d, hipMemcpyAsync(hidden, d->x, (size_t)d->B * d->hs * 4, hipMemcpyDeviceToDevice,
+    rc = hip_check(d, hipMemcpyAsync(hidden, d->bs.x, (size_t)d->B * d->hs * 4, hipMemcpyDeviceToDevice,
                                      d->st),
                    "last_block");
   if (!rc && hp && d->last_k)
-    rc = hip_check(d, hipMemcpyAsync(hp, d->hp + d->rank, (size_t)d->last_k * d->rank * 4,
+    rc = hip_check(d, hipMemcpyAsync(hp, d->bs.hp + d->rank, (size_t)d->last_k * d->rank * 4,
                                      hipMemcpyDeviceToDevice, d->st),
                    "last_block");
   return rc;
@@ -1019,7 +1160,7 @@ int dflash_debug_select(dflash_t* d, const float* logits, const float* hp, int32
   if (width < d->top || width > d->V) return fail(d, DFLASH_EINVAL, "select: bad width");
   if (anchor < 0 || anchor >= d->V) return fail(d, DFLASH_EINVAL, "select: bad anchor");
   dfl::select_all(d->st, logits, false, k, width, d->top, hp, d->rank, d->pbook, d->cbook, d->V,
-                  anchor, forced_prev, d->sel_sc, cand, unary, score, chosen);
+                  anchor, forced_prev, d->bs.sel, cand, unary, score, chosen);
   return launch_check(d, "select");
 }
 

@@ -142,6 +142,24 @@ int dflash_settle(dflash_t* d, int64_t first_pos, int32_t n, const float* taps);
 int dflash_block(dflash_t* d, int32_t anchor_token, int64_t a, int32_t k, int32_t width,
                  float* logits, int32_t* cand, float* unary, float* score, int32_t* chosen);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+   capture, tight serving loops, harnesses that forbid allocation): the block
+   pass of dflash_block, same arguments and results, except that `logits`
+   must be a caller buffer (dev f32 [k][width], not NULL). Its per-call
+   scratch (activations, partial sums, attention states, candidate lists)
+   comes from one static array of the library on each GPU, 48 MiB
+   (`DFLASH_NOALLOC_SCRATCH_BYTES`), held until the process ends; the call
+   itself allocates nothing. A geometry whose scratch exceeds it fails with
+   DFLASH_EINVAL (the 27B-shaped sidecar takes about 26 MB). Every call on a
+   GPU shares that GPU's array and leaves its contents behind: calls that
+   overlap on one GPU (from any handle, on any stream) race, so they must be
+   ordered. The dflash_debug_* reads of the last block reflect the last
+   dflash_block, not this call. */
+#define DFLASH_NOALLOC_SCRATCH_BYTES (48u << 20)
+int dflash_block_noalloc(dflash_t* d, int32_t anchor_token, int64_t a, int32_t k, int32_t width,
+                         float* logits, int32_t* cand, float* unary, float* score,
+                         int32_t* chosen);
+
 /* Forget the context from position pos on (`truncate`). */
 int dflash_truncate(dflash_t* d, int64_t pos);
 
