@@ -61,11 +61,14 @@ Split split_kv(int ntiles, int spans) {
 }
 
 // K splits of the many-row f16 GEMM (16 weight tiles a block): about one
-// block per CU, every split keeping at least 16 steps (512 columns).
+// block per CU, every split keeping at least 16 steps (512 columns) and an
+// even number of them (the kernel takes its steps in pairs; `steps`, K/32,
+// is even since K is a multiple of 128).
 Split split_big(int ntiles, int steps) {
   const long groups = (ntiles + 15) / 16;
   long S = std::max(1L, std::min<long>(256 / groups, steps / 16));
-  const int per = (int)((steps + S - 1) / S);
+  int per = (int)((steps + S - 1) / S);
+  per += per & 1;
   return {(int)((steps + per - 1) / per), per};
 }
 

@@ -50,8 +50,8 @@ void gemm_i4(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks,
              const uint8_t* codes, const uint16_t* scales, TileMap map, int N, int splits,
              int spans_per_split, float* out, long split_stride);
 // Many-row f16 GEMM (mblocks ≤ 16 row blocks at once, 16 weight tiles per
-// block, async copies into a 3-stage LDS ring), one plane (ps = 0) or two
-// (plane 1 at xa + ps, ps a multiple of 8); out as gemm_f16.
+// block, async copies into a 3-stage LDS ring), two planes (plane 1 at
+// xa + ps, ps a multiple of 8); out as gemm_f16.
 void gemm_big_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks,
                   const uint16_t* w, TileMap map, int N, int splits, int steps_per_split,
                   float* out, long split_stride);

@@ -88,47 +88,36 @@ __global__ __launch_bounds__(kThreads) void k_gemm_f16(const f16* __restrict__ x
   }
 }
 
-// Many-row GEMM, f16 weights (the settle's fc at up to 256 rows, and the
-// f16 matrices of the debug product above 16 rows): a block
-// holds all 16 row blocks (256 rows; rows past the input are never written
-// out) of PL activation planes against kBigNT weight tiles over its K split,
-// both planes' products summed into one accumulator. Every 32-column step's
-// fragments (16·PL row + kBigNT weight fragments, 1 KB each, in their memory
-// layout) are copied global → LDS by the waves' async loads
-// (global_load_lds_dwordx4: lane l's 16 bytes land at dst + 16·l) into a
-// kBigStages ring, kBigStages − 1 steps in flight. The block has eight
-// waves, two on each SIMD, so one wave's products run while the other waits
-// at the step's barrier or on LDS: wave w multiplies row blocks 4(w%4)..+3
-// (every plane) by weight tiles 8(w/4)..+7. Each wave copies
-// (16·PL + kBigNT)/8 fragments a step, the weight fragments non-temporal
-// (read once). Blocks are numbered split-fastest.
+// Many-row GEMM, f16 weights, two activation planes (the settle's fc at up
+// to 256 rows, and the f16 matrices of the debug product above 16 rows). A
+// block holds all 16 row blocks (256 rows; rows past the input are never
+// written out) of both planes against kBigNT weight tiles over its K split;
+// both planes' products go into one accumulator.
+//  - Eight waves, two on each SIMD, each with a 4 × 8-tile accumulator:
+//    wave w multiplies row blocks 4(w%4)..+3 of both planes by weight tiles
+//    8(w/4)..+7, 64 MFMAs a 32-column step.
+//  - Every step's 48 fragments (32 row, 16 weight; 1 KB each, in their
+//    memory layout) are copied global → LDS by the waves' async loads
+//    (global_load_lds_dwordx4: lane l's 16 bytes land at dst + 16·l), six a
+//    wave, into a three-stage ring, two steps ahead; one barrier a step.
+//  - A step reads its eight weight fragments, then runs eight groups of
+//    eight MFMAs (one row fragment against the eight weight fragments), each
+//    group's row fragment read one group ahead: only a couple of LDS reads
+//    are in flight, so the MFMAs wait on none but the one they use (with a
+//    whole step's reads in flight, the 4-bit LDS counter forces a wait for
+//    all of them, and a single wave per SIMD with 256 accumulators leaves the
+//    register allocator no room: both measured at half the MFMA rate).
+// Blocks are numbered split-fastest.
 static constexpr int kBigNT = 16, kBigStages = 3, kBigWaves = 8;
-template <int PL>
-struct Big {
-  static constexpr int kFrags = 16 * PL + kBigNT;         // fragments a step
-  static constexpr int kPerWave = kFrags / kBigWaves;     // async copies a wave issues a step
-  static_assert(kFrags % kBigWaves == 0, "every wave copies as many fragments");
-  static constexpr size_t kLds = sizeof(h8) * kBigStages * kFrags * 64;
-};
+static constexpr int kBigFrags = 2 * 16 + kBigNT;            // fragments a step
+static constexpr int kBigPerWave = kBigFrags / kBigWaves;    // async copies a wave issues a step
+static constexpr size_t kBigLds = sizeof(h8) * kBigStages * kBigFrags * 64;  // 144 KB
+static_assert(kBigFrags % kBigWaves == 0, "every wave copies as many fragments");
 
-__device__ __forceinline__ void copy16(const h8* src, h8* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-}
-__device__ __forceinline__ void copy16_nt(const h8* src, h8* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 2);
-}
-
-template <int PL>
-__global__ __launch_bounds__(64 * kBigWaves) void k_gemm_big_f16(const f16* __restrict__ xa, long ps,
-                                                                int K, int mblocks,
-                                                                const f16* __restrict__ w,
-                                                                TileMap mp, int N, int splits,
-                                                                int sps, float* __restrict__ out,
-                                                                long split_stride) {
-  using C = Big<PL>;
-  constexpr int D = kBigStages - 1;
-  constexpr int NA = 16 * PL;    // row fragments a step
-  extern __shared__ h8 stage[];  // [kBigStages][C::kFrags][64]: row fragments (plane, block), then weight tiles
+__global__ __launch_bounds__(64 * kBigWaves) void k_gemm_big_f16(const f16* __restrict__ xa, long ps, int K, int mblocks,
+                    const f16* __restrict__ w, TileMap mp, int N, int splits, int sps,
+                    float* __restrict__ out, long split_stride) {
+  extern __shared__ h8 stage[];  // [kBigStages][kBigFrags][64]: row fragments (plane, block), then weight tiles
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rw = wave & 3, cw = wave >> 2;
@@ -138,53 +127,49 @@ __global__ __launch_bounds__(64 * kBigWaves) void k_gemm_big_f16(const f16* __re
   const int t0 = (blockIdx.x / splits) * kBigNT;
   const h8* xg = reinterpret_cast<const h8*>(xa);
   const h8* wg = reinterpret_cast<const h8*>(w);
-  const h8* fsrc[C::kPerWave];  // this wave's fragments, at step 0
+  const h8* fsrc[kBigPerWave];  // this wave's fragments at step 0 (uniform)
 #pragma unroll
-  for (int i = 0; i < C::kPerWave; ++i) {
-    const int f = wave * C::kPerWave + i;
-    fsrc[i] = f < NA ? xg + (size_t)(f / 16) * (ps / 8) + (size_t)(f % 16) * 2 * K + lane
-                     : wg + (size_t)map_tile(mp, min(t0 + f - NA, mp.ntiles - 1)) * KS * 64 + lane;
+  for (int i = 0; i < kBigPerWave; ++i) {
+    const int f = wave * kBigPerWave + i;
+    fsrc[i] = f < 32 ? xg + (size_t)(f / 16) * (ps / 8) + (size_t)(f % 16) * 2 * K
+                     : wg + (size_t)map_tile(mp, min(t0 + f - 32, mp.ntiles - 1)) * KS * 64;
   }
   // async copies of step s into its stage; past the split's end the last
   // step is copied again, so that every step issues the same loads
   auto issue = [&](int s) {
     const int sc = min(s, s1 - 1);
-    h8* dst = stage + (size_t)(s % kBigStages) * C::kFrags * 64 + (wave * C::kPerWave) * 64;
+    h8* dst = stage + (size_t)(s % kBigStages) * kBigFrags * 64 + (wave * kBigPerWave) * 64;
 #pragma unroll
-    for (int i = 0; i < C::kPerWave; ++i) {
-      if (wave * C::kPerWave + i >= NA)  // uniform: weight fragments are read once
-        copy16_nt(fsrc[i] + (size_t)sc * 64, dst + i * 64);
-      else
-        copy16(fsrc[i] + (size_t)sc * 64, dst + i * 64);
-    }
+    for (int i = 0; i < kBigPerWave; ++i)
+      __builtin_amdgcn_global_load_lds(fsrc[i] + (size_t)sc * 64 + lane, dst + i * 64, 16, 0, 0);
   };
   f4 acc[4][8];
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[b][t] = (f4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < D; ++i) issue(s0 + i);
+  issue(s0);
+  issue(s0 + 1);
   for (int s = s0; s < s1; ++s) {
-    // this wave's copies of step s are in (those of the D − 1 later steps
-    // may remain); after the barrier every wave's are, and the stage of
-    // step s − 1 is free for step s + D
-    wait_vm<(D - 1) * C::kPerWave>();
+    // the copies of steps up to s + 1 are issued: once this wave's of step
+    // s are in (those of s + 1 may remain), the barrier makes the stage of
+    // s complete and every wave's reads of step s − 1 done, so its stage
+    // takes the copies two steps ahead
+    wait_vm<kBigPerWave>();
     lds_barrier();
-    issue(s + D);
-    const h8* st = stage + (size_t)(s % kBigStages) * C::kFrags * 64;
-    h8 bf[8];
+    issue(s + 2);
+    const h8* st = stage + (size_t)(s % kBigStages) * kBigFrags * 64;
+    h8 bf[8], af[2];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) bf[t] = st[(NA + cw * 8 + t) * 64 + lane];
+    for (int t = 0; t < 8; ++t) bf[t] = st[(32 + cw * 8 + t) * 64 + lane];
+    af[0] = st[(rw * 4) * 64 + lane];
 #pragma unroll
-    for (int p = 0; p < PL; ++p) {
-      h8 af[4];
+    for (int g = 0; g < 8; ++g) {  // group g: plane g / 4, row block 4·rw + g % 4
+      if (g + 1 < 8) af[(g + 1) & 1] = st[(((g + 1) / 4) * 16 + rw * 4 + (g + 1) % 4) * 64 + lane];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) af[b] = st[(p * 16 + rw * 4 + b) * 64 + lane];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[b][t] = mfma16(af[b], bf[t], acc[b][t]);
+      for (int t = 0; t < 8; ++t) acc[g % 4][t] = mfma16(af[g & 1], bf[t], acc[g % 4][t]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   const int j = lane >> 4, n = lane & 15;
@@ -1261,19 +1246,14 @@ void gemm_big_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int mblock
                   const uint16_t* w, TileMap map, int N, int splits, int sps, float* out,
                   long ss) {
   const unsigned blocks = cdiv(map.ntiles, kBigNT) * splits;
-  const f16* x = reinterpret_cast<const f16*>(xa);
-  const f16* wt = reinterpret_cast<const f16*>(w);
-  // the two-plane ring takes 144 KB of the compute unit's 160 KB LDS
+  // the ring takes 144 KB of the compute unit's 160 KB LDS
   static const hipError_t lds_ok = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_gemm_big_f16<2>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)Big<2>::kLds);
+      reinterpret_cast<const void*>(&k_gemm_big_f16), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)kBigLds);
   (void)lds_ok;  // a refusal surfaces as the launch's error
-  if (ps)
-    k_gemm_big_f16<2><<<blocks, 64 * kBigWaves, Big<2>::kLds, st>>>(x, ps, K, mblocks, wt, map, N,
-                                                                     splits, sps, out, ss);
-  else
-    k_gemm_big_f16<1><<<blocks, 64 * kBigWaves, Big<1>::kLds, st>>>(x, 0, K, mblocks, wt, map, N,
-                                                                     splits, sps, out, ss);
+  k_gemm_big_f16<<<blocks, 64 * kBigWaves, kBigLds, st>>>(
+      reinterpret_cast<const f16*>(xa), ps, K, mblocks, reinterpret_cast<const f16*>(w), map, N,
+      splits, sps, out, ss);
 }
 
 template <int R, int PL>
