@@ -169,26 +169,30 @@ void orc_conv(int rows, int hidden, int conv_group, int conv_kernel, int stage, 
 
 /* ----------------------------------------------------------- attention */
 
-/* One layer's attention, as `Drafter::block` runs it. Context rows come
-   from the store (row i = position first + i, [kv][hd] binary32 per row).
-   The layer reads positions [lo, hi): hi = min(a, first+len) (never below
-   first), lo = first, or for a window w > 0 the clamp of a+1−w into
-   [first, hi]. Block row r at position a+r further hides context positions
-   below a+r+1−w. Every row sees all block rows (not causal). Scores are
-   scale·q·k with scale = hd^−½; a softmax over the visible keys weights the
-   values, the block's rows summed first and the context's added. */
+/* One layer's attention, as `Drafter::block` runs it. The layer holds the
+   context positions [first + dropped, first + len) (`Ctx::dropped`: rows
+   that fell out of its window and were let go); store row i is position
+   first + dropped + i, [kv][hd] binary32 per row. The layer reads positions
+   [lo, hi): hi = min(a, first+len) (never below the first held position
+   base = first + dropped), lo = base, or for a window w > 0 the clamp of
+   a+1−w into [base, hi]. Block row r at position a+r further hides context
+   positions below a+r+1−w. Every row sees all block rows (not causal).
+   Scores are scale·q·k with scale = hd^−½; a softmax over the visible keys
+   weights the values, the block's rows summed first and the context's
+   added. */
 void orc_attention(int rows, int heads, int kv_heads, int hd, const double* q, const double* k,
                    const double* v, const float* store_k, const float* store_v, long first,
-                   long len, long a, int window, double* y) {
+                   long len, long dropped, long a, int window, double* y) {
   const int rep = heads / kv_heads;
   const double scale = 1.0 / sqrt((double)hd);
+  const long base = first + dropped;
   long hi = a < first + len ? a : first + len;
-  if (hi < first) hi = first;
-  long lo = first;
+  if (hi < base) hi = base;
+  long lo = base;
   if (window > 0) {
     lo = a + 1 - window;
     if (lo < 0) lo = 0;
-    if (lo < first) lo = first;
+    if (lo < base) lo = base;
     if (lo > hi) lo = hi;
   }
   const long n = hi - lo;
@@ -210,7 +214,7 @@ void orc_attention(int rows, int heads, int kv_heads, int hd, const double* q, c
           s[p - lo] = -INFINITY;
           continue;
         }
-        const float* kr = store_k + (p - first) * row_stride + (long)g * hd;
+        const float* kr = store_k + (p - base) * row_stride + (long)g * hd;
         double dot = 0.0;
         for (int e = 0; e < hd; ++e) dot += qv[e] * (double)kr[e];
         s[p - lo] = scale * dot;
@@ -235,7 +239,7 @@ void orc_attention(int rows, int heads, int kv_heads, int hd, const double* q, c
         double blk = 0.0, ctx = 0.0;
         for (int b = 0; b < rows; ++b) blk += s[n + b] * v[((size_t)b * kv_heads + g) * hd + e];
         for (long p = lo; p < hi; ++p)
-          ctx += s[p - lo] * (double)store_v[(p - first) * row_stride + (long)g * hd + e];
+          ctx += s[p - lo] * (double)store_v[(p - base) * row_stride + (long)g * hd + e];
         out[e] = blk + ctx;
       }
     }
@@ -297,12 +301,13 @@ static void add_into(double* h, const double* d, long count) {
 /* `Drafter::block` from the rows [E[anchor], E[mask]…] at positions a, a+1, …,
    followed by the head over the first `width` vocabulary rows and the
    selector's projection, both of rows 1..k after the last norm:
-   logits [k][width], hp [k][rank]. `hidden` (or NULL) receives every row
-   after the last norm, `trace` (or NULL) the residual rows after each
-   layer, [layers][block][hidden]. */
+   logits [k][width], hp [k][rank]. Layer l's store holds positions
+   [first + dropped[l], first + len) (dropped NULL: none dropped). `hidden`
+   (or NULL) receives every row after the last norm, `trace` (or NULL) the
+   residual rows after each layer, [layers][block][hidden]. */
 int orc_block(const orc_model* m, const float* const* store_k, const float* const* store_v,
-              long first, long len, int anchor, long a, int k, int width, double* logits,
-              double* hp, double* hidden, double* trace) {
+              long first, long len, const long* dropped, int anchor, long a, int k, int width,
+              double* logits, double* hp, double* hidden, double* trace) {
   init_f16();
   const int hs = m->hidden, B = m->block, nh = m->heads, kv = m->kv_heads, hd = m->head_dim;
   const int ffn = m->intermediate, qd = nh * hd, kd = kv * hd;
@@ -344,8 +349,8 @@ int orc_block(const orc_model* m, const float* const* store_k, const float* cons
       orc_rotate(q, B, nh, hd, pos, inv);
       orc_rotate(kk, B, kv, hd, pos, inv);
     }
-    orc_attention(B, nh, kv, hd, q, kk, vv, store_k[l], store_v[l], first, len, a,
-                  m->windows[l], y);
+    orc_attention(B, nh, kv, hd, q, kk, vv, store_k[l], store_v[l], first, len,
+                  dropped ? dropped[l] : 0, a, m->windows[l], y);
     orc_apply_q4(&L->o, hs, qd, y, B, tmp);
     orc_conv(B, hs, gs, kn, 1, L->attn_base, d, tmp, xc);
     add_into(h, xc, (long)B * hs);

@@ -71,11 +71,11 @@ void orc_apply_f16(const uint16_t* w, int rows, int cols, const double* x, int m
 void orc_apply_q4(const orc_q4* w, int rows, int cols, const double* x, int m, double* y);
 void orc_attention(int rows, int heads, int kv_heads, int hd, const double* q, const double* k,
                    const double* v, const float* store_k, const float* store_v, long first,
-                   long len, long a, int window, double* y);
+                   long len, long dropped, long a, int window, double* y);
 int orc_settle(const orc_model* m, const float* taps, int n, long pos0, float* k_out, float* v_out);
 int orc_block(const orc_model* m, const float* const* store_k, const float* const* store_v,
-              long first, long len, int anchor, long a, int k, int width, double* logits,
-              double* hp, double* hidden, double* trace);
+              long first, long len, const long* dropped, int anchor, long a, int k, int width,
+              double* logits, double* hp, double* hidden, double* trace);
 void orc_top_k(const double* x, long n, int k, double* val, int* idx);
 void orc_select(const orc_model* m, const double* logits, int width, const double* hp, int k,
                 int anchor, const int* forced_prev, int* cand, double* unary, double* score,

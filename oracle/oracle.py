@@ -66,10 +66,10 @@ def lib():
         L.orc_conv.argtypes = [i, i, i, i, i, vp, vp, vp, vp]
         L.orc_apply_f16.argtypes = [vp, i, i, vp, i, vp]
         L.orc_apply_q4.argtypes = [vp, i, i, vp, i, vp]
-        L.orc_attention.argtypes = [i, i, i, i, vp, vp, vp, vp, vp, l, l, l, i, vp]
+        L.orc_attention.argtypes = [i, i, i, i, vp, vp, vp, vp, vp, l, l, l, l, i, vp]
         L.orc_settle.argtypes = [vp, vp, i, l, vp, vp]
         L.orc_settle.restype = i
-        L.orc_block.argtypes = [vp, vp, vp, l, l, i, l, i, i, vp, vp, vp, vp]
+        L.orc_block.argtypes = [vp, vp, vp, l, l, vp, i, l, i, i, vp, vp, vp, vp]
         L.orc_block.restype = i
         L.orc_top_k.argtypes = [vp, l, i, vp, vp]
         L.orc_select.argtypes = [vp, vp, i, vp, i, i, vp, vp, vp, vp, vp, vp]
@@ -149,8 +149,9 @@ class Model:
         return k, v
 
     def block(self, store, first: int, length: int, anchor: int, a: int, k: int, width: int,
-              trace: bool = False):
-        """store: per layer (K, V) f32 [rows ≥ length][kv*hd]. Returns dict of
+              trace: bool = False, dropped=None):
+        """store: per layer (K, V) f32 [rows][kv*hd], row i = position
+        first + dropped[l] + i (dropped None: all zero). Returns dict of
         logits [k][width], hp [k][rank], hidden [block][hidden] (float64)."""
         g = self.g
         ks = [_c(s[0], np.float32) for s in store]
@@ -161,8 +162,10 @@ class Model:
         hp = np.zeros((k, g["selector_rank"]))
         hidden = np.zeros((g["block"], g["hidden"]))
         tr = np.zeros((g["layers"], g["block"], g["hidden"])) if trace else None
-        rc = lib().orc_block(self.ptr, kp, vp, first, length, anchor, a, k, width, _p(logits),
-                             _p(hp), _p(hidden), _p(tr) if trace else None)
+        dr = None if dropped is None else _c(dropped, np.int64)
+        rc = lib().orc_block(self.ptr, kp, vp, first, length, _p(dr) if dr is not None else None,
+                             anchor, a, k, width, _p(logits), _p(hp), _p(hidden),
+                             _p(tr) if trace else None)
         assert rc == 0, rc
         out = dict(logits=logits, hp=hp, hidden=hidden)
         if trace:
@@ -254,14 +257,16 @@ def apply_q4(codes: np.ndarray, scale: np.ndarray, x: np.ndarray) -> np.ndarray:
     return y
 
 
-def attention(q, k, v, store_k, store_v, first, length, a, window, heads, kv_heads, hd):
-    """q [rows][heads*hd], k/v [rows][kv*hd], store [≥length][kv*hd] f32."""
+def attention(q, k, v, store_k, store_v, first, length, a, window, heads, kv_heads, hd,
+              dropped=0):
+    """q [rows][heads*hd], k/v [rows][kv*hd], store [rows][kv*hd] f32 (row i
+    = position first + dropped + i)."""
     q, k, v = f64(q), f64(k), f64(v)
     sk, sv = _c(store_k, np.float32), _c(store_v, np.float32)
     rows = q.shape[0]
     y = np.zeros_like(q)
     lib().orc_attention(rows, heads, kv_heads, hd, _p(q), _p(k), _p(v), _p(sk), _p(sv), first,
-                        length, a, window, _p(y))
+                        length, dropped, a, window, _p(y))
     return y
 
 
