@@ -88,6 +88,7 @@ def main():
     log(f"weights generated in {time.time() - t0:.1f}s")
     t0 = time.time()
     d = pkg.Drafter(g, w, max_context=cap, stream=stream)
+    d.reserve(cap)  # the full layer's store at its final size: no store moves later
     log(f"drafter created in {time.time() - t0:.1f}s (store capacity {cap} rows)")
 
     if args.calibrate_copy:
@@ -390,6 +391,7 @@ def leg_4b(pkg, synth, dev, stream, nblocks):
     t0 = time.time()
     w = synth.make_weights(g, seed=0, device=dev)
     d = pkg.Drafter(g, w, max_context=4096 + 256, stream=stream)
+    d.reserve(4096 + 256)
     del w
     log(f"4b: sidecar ready in {time.time() - t0:.1f}s")
     calls, n = 16, 4096
@@ -453,6 +455,7 @@ def leg_long(pkg, synth, dev, stream, steps):
     w = synth.make_weights(g, seed=0, device=dev)
     ctx0 = 131071
     d = pkg.Drafter(g, w, max_context=ctx0 + steps + 40, stream=stream)
+    d.reserve(ctx0 + steps + 40)
     log(f"long: sidecar ready in {time.time() - t0:.1f}s")
     t0 = time.time()
     for c in range((ctx0 + 255) // 256):

@@ -61,6 +61,10 @@ _SIGS = {
                       C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
     "dflash_block_noalloc": ([C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
                               C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
+    "dflash_queue": ([C.c_void_p, C.c_int64, C.c_int32, C.c_void_p], C.c_int),
+    "dflash_flush": ([C.c_void_p], C.c_int),
+    "dflash_reserve": ([C.c_void_p, C.c_int64], C.c_int),
+    "dflash_state": ([C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
     "dflash_truncate": ([C.c_void_p, C.c_int64], C.c_int),
     "dflash_span": ([C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
     "dflash_sync": ([C.c_void_p], C.c_int),
@@ -125,6 +129,22 @@ def dflash_block(h, anchor, a, k, width, logits, cand, unary, score, chosen):
 
 def dflash_block_noalloc(h, anchor, a, k, width, logits, cand, unary, score, chosen):
     return lib().dflash_block_noalloc(h, anchor, a, k, width, logits, cand, unary, score, chosen)
+
+
+def dflash_queue(h, first_pos, n, taps):
+    return lib().dflash_queue(h, first_pos, n, taps)
+
+
+def dflash_flush(h):
+    return lib().dflash_flush(h)
+
+
+def dflash_reserve(h, rows):
+    return lib().dflash_reserve(h, rows)
+
+
+def dflash_state(h, first_p, settled_p, waiting_p, dropped_p):
+    return lib().dflash_state(h, first_p, settled_p, waiting_p, dropped_p)
 
 
 def dflash_truncate(h, pos):
@@ -218,6 +238,22 @@ class Drafter:
                       unary_ptr, score_ptr, chosen_ptr):
         _check(lib().dflash_block_noalloc(self.h, anchor, a, k, width, logits_ptr, cand_ptr,
                                           unary_ptr, score_ptr, chosen_ptr), self.h)
+
+    def queue(self, first_pos: int, n: int, taps_ptr: int):
+        _check(lib().dflash_queue(self.h, first_pos, n, taps_ptr), self.h)
+
+    def flush(self):
+        _check(lib().dflash_flush(self.h), self.h)
+
+    def reserve(self, rows: int):
+        _check(lib().dflash_reserve(self.h, rows), self.h)
+
+    def state(self):
+        """(first, settled rows, waiting rows, [dropped rows of each layer])."""
+        f, s, w = C.c_int64(), C.c_int64(), C.c_int64()
+        dr = (C.c_int64 * self.g["layers"])()
+        _check(lib().dflash_state(self.h, C.byref(f), C.byref(s), C.byref(w), dr), self.h)
+        return f.value, s.value, w.value, list(dr)
 
     def truncate(self, pos: int):
         _check(lib().dflash_truncate(self.h, pos), self.h)

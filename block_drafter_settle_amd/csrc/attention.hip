@@ -14,7 +14,8 @@ namespace dfl {
 // Split-context attention (`Drafter::block`'s inner loop). Block (c, g, z):
 // kv head g, its q heads 4z..4z+3, and key chunk c — context keys
 // [c·chunk, min(n, (c+1)·chunk)) of the layer's range, or for c == nchunks
-// the block's own B keys. Each wave keeps one q head's 16 query rows and an
+// the block's own B keys. The context keys sit in the layer's ring of cap
+// rows from row s0 on, wrapping at most once. Each wave keeps one q head's 16 query rows and an
 // online softmax over 32-key steps: S^T = K·Q^T and O^T += V^T·P^T on MFMA.
 // Every operand is an f16 pair (hi, lo = f16 of the rest): q's two A-layout
 // planes (plane 1 at qa + qps), K and V split into two LDS planes, P split
@@ -25,8 +26,8 @@ namespace dfl {
 template <int HD>
 __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, long qps,
                                                    const float* __restrict__ sk,
-                                                   const float* __restrict__ sv,
-                                                   const float* __restrict__ kb,
+                                                   const float* __restrict__ sv, long cap,
+                                                   long s0, const float* __restrict__ kb,
                                                    const float* __restrict__ vb, int B, int nh,
                                                    int kv, int n, long lo_pos, long a, int window,
                                                    int chunk, int nchunks, float scale,
@@ -49,8 +50,12 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
   const bool blk = c == nchunks;
   const int k_first = blk ? 0 : c * chunk;
   const int count = blk ? B : min(chunk, n - k_first);
-  const float* kbase = blk ? kb + (size_t)g * HD : sk + (size_t)k_first * kd + (size_t)g * HD;
-  const float* vbase = blk ? vb + (size_t)g * HD : sv + (size_t)k_first * kd + (size_t)g * HD;
+  const float* kbase = (blk ? kb : sk) + (size_t)g * HD;
+  const float* vbase = (blk ? vb : sv) + (size_t)g * HD;
+  // ring row of the chunk's first key (s0 < cap and k_first < n ≤ cap)
+  const long wrap = blk ? LONG_MAX : cap;
+  long row_first = blk ? 0 : s0 + k_first;
+  if (row_first >= wrap) row_first -= wrap;
   const long pos_base = lo_pos + k_first;
 
   h8 qf[HD / 32], ql[HD / 32];
@@ -87,8 +92,10 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int key = min(k0 + 2 * kp + h, count - 1);
-      const float4* kpn = reinterpret_cast<const float4*>(kbase + (size_t)key * kd + d0);
-      const float4* vpn = reinterpret_cast<const float4*>(vbase + (size_t)key * kd + d0);
+      long row = row_first + key;
+      if (row >= wrap) row -= wrap;
+      const float4* kpn = reinterpret_cast<const float4*>(kbase + (size_t)row * kd + d0);
+      const float4* vpn = reinterpret_cast<const float4*>(vbase + (size_t)row * kd + d0);
 #pragma unroll
       for (int e = 0; e < DPT / 4; ++e) {
         kreg[h * (DPT / 4) + e] = kpn[e];
@@ -269,22 +276,22 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 static inline unsigned cdiv(long a, long b) { return (unsigned)((a + b - 1) / b); }
 
 void attention(hipStream_t st, const uint16_t* qa, long qps, const float* sk, const float* sv,
-               const float* kb, const float* vb, int B, int nh, int kv, int hd, int n,
-               long lo_pos, long a, int window, int chunk, int nchunks, float scale, float* pacc,
-               float* pml) {
+               long cap, long s0, const float* kb, const float* vb, int B, int nh, int kv,
+               int hd, int n, long lo_pos, long a, int window, int chunk, int nchunks,
+               float scale, float* pacc, float* pml) {
   const int rep = nh / kv;
   dim3 grid(nchunks + 1, kv, cdiv(rep, 4));
   const f16* q = reinterpret_cast<const f16*>(qa);
   float2* ml = reinterpret_cast<float2*>(pml);
   if (hd == 64)
-    k_attn<64><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, kb, vb, B, nh, kv, n, lo_pos, a, window,
-                                          chunk, nchunks, scale, pacc, ml);
+    k_attn<64><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, cap, s0, kb, vb, B, nh, kv, n, lo_pos,
+                                           a, window, chunk, nchunks, scale, pacc, ml);
   else if (hd == 128)
-    k_attn<128><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, kb, vb, B, nh, kv, n, lo_pos, a, window,
-                                           chunk, nchunks, scale, pacc, ml);
+    k_attn<128><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, cap, s0, kb, vb, B, nh, kv, n, lo_pos,
+                                            a, window, chunk, nchunks, scale, pacc, ml);
   else
-    k_attn<256><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, kb, vb, B, nh, kv, n, lo_pos, a, window,
-                                           chunk, nchunks, scale, pacc, ml);
+    k_attn<256><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, cap, s0, kb, vb, B, nh, kv, n, lo_pos,
+                                            a, window, chunk, nchunks, scale, pacc, ml);
 }
 
 void attn_merge(hipStream_t st, const float* pacc, const float* pml, int nh, int kv, int hd,

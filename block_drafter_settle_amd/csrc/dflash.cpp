@@ -32,6 +32,10 @@ constexpr int kKsQkv = 8;    // q/k/v, int4: spans (128 columns) per split
 constexpr int kKsO = 2;      // o, int4
 constexpr int kKsDown = 8;   // down, int4
 constexpr int kSettleI4Blocks = 2;  // above this many 16-row blocks the settle's k/v use the many-row kernel
+// `queue_context`: at most kPendingRows rows wait (as many as the widest
+// window plus kBlockSlack when every layer is windowed); past that the
+// oldest go through in multiples of kContextChunk rows
+constexpr long kPendingRows = 512, kContextChunk = 64, kBlockSlack = 256;
 
 thread_local std::string g_create_error;
 
@@ -152,7 +156,7 @@ struct dflash {
   std::vector<int> windows, rot;
   double theta;
   float eps;
-  long cap;
+  long maxctx;  // rows a layer may hold at most
   hipStream_t st;
   // weights
   uint16_t *fc = nullptr, *sel = nullptr, *pbook = nullptr, *cbook = nullptr, *embed = nullptr,
@@ -163,9 +167,19 @@ struct dflash {
   int* rot_dev = nullptr;
   I4Set qkv, o, gu, down;
   int ptiles;  // kernel-projection row tiles
-  // context store
-  float *sk = nullptr, *sv = nullptr;
+  // the context (`Ctx`): settled positions first .. first+len; per layer a
+  // ring store of the rows it still holds; tap rows that wait to be settled
   long first = 0, len = 0;
+  struct LayerStore {
+    float *k = nullptr, *v = nullptr;  // cap rows; position p at row (p − first) mod cap
+    long cap = 0;
+    long limit = 0;    // most rows the layer may hold (a windowed layer's ring is this big)
+    long dropped = 0;  // settled rows the layer no longer holds (`Ctx::dropped`)
+  };
+  std::vector<LayerStore> ls;
+  dfl::StoreSlot* tab = nullptr;  // every layer's (k, v, cap), for the settle's store kernel
+  float* pq = nullptr;            // waiting tap rows: a ring of pcap rows from row phead
+  long pcap = 0, phead = 0, pend = 0;
   int dev = 0;  // the device the handle was created on
   // block scratch (the handle's own; dflash_block_noalloc carves the same set
   // from the library's static array instead)
@@ -395,10 +409,10 @@ long partial_need(const dflash* d) {
 }
 
 void layer_range(const dflash* d, int l, long a, long* lo, long* n) {
-  // `block_dev`: base = first (the store keeps every settled row);
+  // `block_dev`: base = first + dropped (the layer's first held position);
   // hi = min(a, first+len), never below base; a window w > 0 starts the
   // layer at a+1−w, clamped into [base, hi].
-  const long base = d->first;
+  const long base = d->first + d->ls[l].dropped;
   long hi = std::min(a, d->first + d->len);
   hi = std::max(hi, base);
   long l0 = base;
@@ -406,6 +420,147 @@ void layer_range(const dflash* d, int l, long a, long* lo, long* n) {
   if (w > 0) l0 = std::min(std::max(std::max(a + 1 - w, 0L), base), hi);
   *lo = l0;
   *n = hi - l0;
+}
+
+// ---- the context lifecycle (`queue_context`, `settle`, `settle_rows`,
+// `truncate`, `Dev::reserve`)
+
+// The device table of the layers' stores, after a store moved.
+// (err: the handle that keeps the message, nullptr while creating)
+int upload_tab(dflash* d, dflash* err) {
+  std::vector<dfl::StoreSlot> t(d->L);
+  for (int l = 0; l < d->L; ++l) t[l] = {d->ls[l].k, d->ls[l].v, std::max(1L, d->ls[l].cap)};
+  return hip_check(err, hipMemcpy(d->tab, t.data(), t.size() * sizeof t[0], hipMemcpyHostToDevice),
+                   "context table");
+}
+
+// The context's bookkeeping alone: the position rule and the window drop
+// are worked out on a copy, checked, and only then committed.
+struct CtxState {
+  long first, len, pend, phead;
+  std::vector<long> dropped;
+};
+
+CtxState state_of(const dflash* d) {
+  CtxState s{d->first, d->len, d->pend, d->phead, {}};
+  for (const auto& l : d->ls) s.dropped.push_back(l.dropped);
+  return s;
+}
+
+void commit(dflash* d, const CtxState& s) {
+  d->first = s.first;
+  d->len = s.len;
+  d->pend = s.pend;
+  d->phead = s.phead;
+  for (int l = 0; l < d->L; ++l) d->ls[l].dropped = s.dropped[l];
+}
+
+// `truncate`: forget positions from pos on, waiting rows included.
+void truncate_state(CtxState& s, long pos) {
+  s.pend = std::min(s.pend, std::max(0L, pos - (s.first + s.len)));
+  const long keep = std::min(std::max(0L, pos - s.first), s.len);
+  for (long& dr : s.dropped) dr = std::min(dr, keep);
+  s.len = keep;
+}
+
+// The position rule of `queue_context`: rows at a held or waiting position
+// cut the context there; a gap, or a position before first, restarts it.
+void position_rule(CtxState& s, long pos) {
+  if (pos > s.first + s.len + s.pend || pos < s.first) {
+    truncate_state(s, 0);
+    s.first = pos;
+    s.phead = 0;
+  } else {
+    truncate_state(s, pos);
+  }
+}
+
+// One `settle_rows` call of n rows on the bookkeeping: the rows join, then a
+// windowed layer that holds more than twice its window keeps the last
+// window's rows. False if a layer would hold more rows than it may (a
+// windowed layer's peak inside the call is what it holds after it).
+bool settle_state(const dflash* d, CtxState& s, long n) {
+  s.len += n;
+  for (int l = 0; l < d->L; ++l) {
+    const long w = d->windows[l];
+    long held = s.len - s.dropped[l];
+    if (w > 0 && held > 2 * w) {
+      s.dropped[l] += held - w;
+      held = w;
+    }
+    if (held > d->ls[l].limit) return false;
+  }
+  return true;
+}
+
+// Room for `rows` rows in every full layer (`Dev::reserve`): a store that is
+// too small grows to max(rows, 2·cap, 4096) rows, at most max_context, and
+// keeps what it held. Synchronises the stream when a store moves.
+int reserve(dflash* d, long rows) {
+  if (rows > d->maxctx)
+    return fail(d, DFLASH_ENOMEM, "%ld rows do not fit a layer's store (max_context %ld)", rows,
+                d->maxctx);
+  bool moved = false;
+  for (int l = 0; l < d->L; ++l) {
+    auto& S = d->ls[l];
+    if (d->windows[l] > 0 || rows <= S.cap) continue;
+    const long cap = std::min(std::max(std::max(rows, 2 * S.cap), 4096L), d->maxctx);
+    const size_t bytes = (size_t)cap * d->kd * sizeof(float);
+    float *nk = nullptr, *nv = nullptr;
+    if (hipMalloc(&nk, bytes) != hipSuccess || hipMalloc(&nv, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      if (nk) (void)hipFree(nk);
+      return fail(d, DFLASH_ENOMEM, "device memory for layer %d's context (%zu bytes)", l,
+                  2 * bytes);
+    }
+    // a full layer holds positions first .. first+len at rows 0 .. len
+    const size_t held = (size_t)std::min(d->len, S.cap) * d->kd * sizeof(float);
+    int rc = DFLASH_OK;
+    if (held)
+      rc = hip_check(d, hipMemcpyAsync(nk, S.k, held, hipMemcpyDeviceToDevice, d->st), "reserve");
+    if (!rc && held)
+      rc = hip_check(d, hipMemcpyAsync(nv, S.v, held, hipMemcpyDeviceToDevice, d->st), "reserve");
+    if (!rc) rc = hip_check(d, hipStreamSynchronize(d->st), "reserve");
+    if (rc) {
+      (void)hipFree(nk);
+      (void)hipFree(nv);
+      return rc;
+    }
+    if (S.k) (void)hipFree(S.k);
+    if (S.v) (void)hipFree(S.v);
+    S.k = nk;
+    S.v = nv;
+    S.cap = cap;
+    moved = true;
+  }
+  return moved ? upload_tab(d, d) : DFLASH_OK;
+}
+
+// A launch failed while rows were being settled: what the layers hold can
+// no longer be told, so the context is emptied (first stays).
+void lose_context(dflash* d) {
+  d->len = 0;
+  d->pend = 0;
+  d->phead = 0;
+  for (auto& l : d->ls) l.dropped = 0;
+}
+
+// The rows of one `settle_rows` call: up to three runs of consecutive tap
+// rows, in order (the waiting ring's two pieces, then the caller's rows).
+struct Runs {
+  const float* p[3] = {nullptr, nullptr, nullptr};
+  long n[3] = {0, 0, 0};
+  int k = 0;
+  void add(const float* q, long m) {
+    if (m > 0) p[k] = q, n[k++] = m;
+  }
+};
+
+// Runs of the waiting rows [from, from+count) of the ring.
+void add_waiting(const dflash* d, Runs& r, long from, long count) {
+  const long i = (d->phead + from) % d->pcap, a = std::min(count, d->pcap - i);
+  r.add(d->pq + (size_t)i * d->tw, a);
+  r.add(d->pq, count - a);
 }
 
 int attn_chunk(long n, int* nchunks) {
@@ -522,6 +677,10 @@ void dflash_destroy(dflash_t* d) {
   (void)hipStreamSynchronize(d->st);
   for (hipEvent_t e : d->tm.ev) (void)hipEventDestroy(e);
   for (void* p : d->allocs) (void)hipFree(p);
+  for (auto& l : d->ls) {
+    if (l.k) (void)hipFree(l.k);
+    if (l.v) (void)hipFree(l.v);
+  }
   delete d;
 }
 
@@ -553,7 +712,7 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
   d->P = 2 * d->kn * d->G;
   d->theta = g->rope_theta;
   d->eps = (float)g->eps;
-  d->cap = g->max_context;
+  d->maxctx = g->max_context;
   d->st = static_cast<hipStream_t>(stream);
   d->windows.assign(g->windows, g->windows + d->L);
   for (int l = 0; l < d->L; ++l) d->rot.push_back(g->rotary[l] ? 1 : 0);
@@ -632,10 +791,31 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
     rc = upload(d, &d->inv, inv.data(), inv.size(), "rotary frequencies");
   }
   if (!rc) rc = upload(d, &d->rot_dev, d->rot.data(), d->rot.size(), "rotary flags");
-  // ---- context store
-  const size_t store = (size_t)L * d->cap * d->kd;
-  if (!rc) rc = dev_alloc(d, &d->sk, store, "context keys");
-  if (!rc) rc = dev_alloc(d, &d->sv, store, "context values");
+  // ---- context: a windowed layer's ring of min(2·window, max_context) rows
+  // now; a full layer's store grows as rows come (`Dev::reserve`); the
+  // waiting rows' ring
+  d->ls.resize(L);
+  for (int l = 0; l < L && !rc; ++l) {
+    auto& S = d->ls[l];
+    const long w = d->windows[l];
+    S.limit = w > 0 ? std::min(2 * w, d->maxctx) : d->maxctx;
+    if (w > 0) {
+      const size_t bytes = (size_t)S.limit * d->kd * sizeof(float);
+      if (hipMalloc(&S.k, bytes) != hipSuccess || hipMalloc(&S.v, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        rc = fail(nullptr, DFLASH_ENOMEM, "device memory for layer %d's context (%zu bytes)", l,
+                  2 * bytes);
+      }
+      S.cap = S.limit;
+    }
+  }
+  if (!rc) rc = dev_alloc(d, &d->tab, L, "context table");
+  if (!rc) rc = upload_tab(d, nullptr);
+  d->pcap = kPendingRows;
+  if (std::all_of(d->windows.begin(), d->windows.end(), [](int w) { return w > 0; }))
+    d->pcap = std::max(kPendingRows,
+                       (long)*std::max_element(d->windows.begin(), d->windows.end()) + kBlockSlack);
+  if (!rc) rc = dev_alloc(d, &d->pq, (size_t)d->pcap * d->tw, "waiting rows");
   // ---- scratch
   const int rep = d->nh / d->kv;
   const size_t slots = (size_t)d->kv * (dfl::kAttnMaxChunks + 1) * rep;
@@ -753,18 +933,38 @@ int dflash_sync(dflash_t* d) {
 int dflash_span(const dflash_t* d, int64_t* first, int64_t* end) {
   if (!d || !first || !end) return DFLASH_EINVAL;
   *first = d->first;
-  *end = d->first + d->len;
+  *end = d->first + d->len + d->pend;
+  return DFLASH_OK;
+}
+
+int dflash_state(const dflash_t* d, int64_t* first, int64_t* settled, int64_t* waiting,
+                 int64_t* dropped) {
+  if (!d || !first || !settled || !waiting) return DFLASH_EINVAL;
+  *first = d->first;
+  *settled = d->len;
+  *waiting = d->pend;
+  if (dropped)
+    for (int l = 0; l < d->L; ++l) dropped[l] = d->ls[l].dropped;
   return DFLASH_OK;
 }
 
 int dflash_truncate(dflash_t* d, int64_t pos) {
   if (!d) return DFLASH_EINVAL;
-  d->len = std::max(0L, std::min(d->len, (long)pos - d->first));
+  CtxState s = state_of(d);
+  truncate_state(s, std::max<int64_t>(pos, 0));
+  commit(d, s);
   return DFLASH_OK;
 }
 
-// One settle pass of m ≤ 256 rows at store row `row0`, positions pos0.. .
-static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0) {
+int dflash_reserve(dflash_t* d, int64_t rows) {
+  if (!d) return DFLASH_EINVAL;
+  if (rows < 0) return fail(d, DFLASH_EINVAL, "reserve: rows must be >= 0");
+  return reserve(d, rows);
+}
+
+// One settle pass of m ≤ 256 rows at positions pos0.. (store rows
+// pos0 − first ..) of a settle call that ends at store row row_end.
+static int settle_pass(dflash* d, const dfl::RowSrc& taps, int m, long pos0, long row_end) {
   hipStream_t st = d->st;
   const int mb = (m + 15) / 16;
   // every activation operand carries two f16 planes (hi and the rest): the
@@ -772,7 +972,7 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
   // their error, so single-plane f16 rounding (1e-3 of the largest K/V
   // entry) is not enough end to end
   const long pst = (long)kSettleRows * d->tw, psh = (long)kSettleRows * d->hs;
-  dfl::to_a(st, taps, d->tw, m, d->tw, d->taps_a, pst);
+  dfl::to_a(st, taps, m, d->tw, d->taps_a, pst);
   tm_mark(d, DFLASH_ST_S_TAPS);
   // t = fc · taps (f32 partials), then rms by hidden_norm into A-layout
   const dfl::TileMap fmap{d->hs / 16, d->hs / 16, 0, 0};
@@ -806,49 +1006,135 @@ static int settle_pass(dflash* d, const float* taps, int m, long pos0, long row0
   }
   tm_mark(d, DFLASH_ST_S_KV);
   dfl::settle_kv(st, d->part, sk.S, ssk, m, d->L, d->kv, d->hd, d->k_norm, d->inv, d->rot_dev,
-                 pos0, d->eps, d->sqp, d->hs, d->sk, d->sv, d->cap, row0);
+                 pos0, d->eps, d->sqp, d->hs, d->tab, pos0 - d->first,
+                 row_end);
   tm_mark(d, DFLASH_ST_S_STORE);
   return launch_check(d, "settle");
 }
 
+// One `settle_rows` call: the rows at positions first+len.., 256 a pass,
+// then the window drop.
+static int settle_call(dflash* d, const Runs& r) {
+  const long n = r.n[0] + r.n[1] + r.n[2];
+  if (n == 0) return DFLASH_OK;
+  tm_begin(d);
+  for (long done = 0; done < n; done += kSettleRows) {
+    const int m = (int)std::min<long>(kSettleRows, n - done);
+    // this pass's rows, as runs of r
+    const float* p[3] = {nullptr, nullptr, nullptr};
+    long c[3] = {0, 0, 0};
+    int k = 0;
+    long skip = done, need = m;
+    for (int i = 0; i < r.k && need > 0; ++i) {
+      if (skip >= r.n[i]) {
+        skip -= r.n[i];
+        continue;
+      }
+      const long take = std::min(r.n[i] - skip, need);
+      p[k] = r.p[i] + (size_t)skip * d->tw;
+      c[k++] = take;
+      need -= take;
+      skip = 0;
+    }
+    const dfl::RowSrc src{{p[0], k > 1 ? p[1] : p[0], k > 2 ? p[2] : p[0]}, (int)c[0], (int)c[1],
+                          (long)d->tw};
+    const int rc = settle_pass(d, src, m, d->first + d->len + done, d->len + n);
+    if (rc) {
+      lose_context(d);
+      return rc;
+    }
+  }
+  tm_end(d);
+  d->tm.settles += d->tm.on;
+  CtxState s = state_of(d);
+  settle_state(d, s, n);
+  commit(d, s);
+  return DFLASH_OK;
+}
+
+// `queue_context` (all = false: the rows past the waiting limit settle, the
+// rest wait) and `push_context` (all = true: every row settles).
+static int push_rows(dflash* d, int64_t pos, int32_t n, const float* taps, bool all,
+                     const char* what) {
+  if (n < 0 || pos < 0) return fail(d, DFLASH_EINVAL, "%s: n and first_pos must be >= 0", what);
+  if (n > 0 && !taps) return fail(d, DFLASH_EINVAL, "%s: null taps", what);
+  CtxState s = state_of(d);
+  position_rule(s, pos);
+  const long total = s.pend + n;
+  const long over =
+      total > d->pcap
+          ? std::min((total - d->pcap + kContextChunk - 1) / kContextChunk * kContextChunk, total)
+          : 0;
+  // what the layers hold after the calls this makes (for a queue, also after
+  // the later settle of what waits) must fit them
+  CtxState t = s;
+  if ((over && !settle_state(d, t, over)) || (total > over && !settle_state(d, t, total - over)))
+    return fail(d, DFLASH_ENOMEM,
+                "%s: the context would hold more rows than a layer's store (max_context %ld)", what,
+                d->maxctx);
+  if (int rc = reserve(d, t.len)) return rc;
+  commit(d, s);
+  long used = 0;  // caller rows settled so far
+  if (over) {
+    Runs r;
+    const long a = std::min(over, d->pend);
+    add_waiting(d, r, 0, a);
+    r.add(taps, over - a);
+    d->phead = (d->phead + a) % d->pcap;
+    d->pend -= a;
+    used = over - a;
+    if (int rc = settle_call(d, r)) return rc;
+  }
+  if (all) {
+    Runs r;
+    add_waiting(d, r, 0, d->pend);
+    r.add(taps + (size_t)used * d->tw, n - used);
+    d->pend = 0;
+    d->phead = 0;
+    return settle_call(d, r);
+  }
+  // the caller's other rows wait: into the ring after the waiting ones
+  long left = n - used;
+  const float* src = taps + (size_t)used * d->tw;
+  while (left > 0) {
+    const long i = (d->phead + d->pend) % d->pcap, c = std::min(left, d->pcap - i);
+    const int rc = hip_check(d,
+                             hipMemcpyAsync(d->pq + (size_t)i * d->tw, src, (size_t)c * d->tw * 4,
+                                            hipMemcpyDeviceToDevice, d->st),
+                             what);
+    if (rc) {
+      lose_context(d);
+      return rc;
+    }
+    d->pend += c;
+    src += (size_t)c * d->tw;
+    left -= c;
+  }
+  return DFLASH_OK;
+}
+
 int dflash_settle(dflash_t* d, int64_t first_pos, int32_t n, const float* taps) {
   if (!d) return DFLASH_EINVAL;
-  if (n < 0 || first_pos < 0) return fail(d, DFLASH_EINVAL, "settle: n and first_pos must be >= 0");
-  if (n > 0 && !taps) return fail(d, DFLASH_EINVAL, "settle: null taps");
-  // position rule of `queue_context`
-  long first = d->first, len = d->len;
-  if (len == 0 || first_pos > first + len || first_pos < first) {
-    first = first_pos;
-    len = 0;
-  } else {
-    len = first_pos - first;
-  }
-  if (len + (long)n > d->cap)
-    return fail(d, DFLASH_ENOMEM, "settle: %ld rows do not fit the store (max_context %ld)",
-                len + (long)n, d->cap);
-  // The span is committed only once every pass has been enqueued. After a
-  // HIP error part of the rows may have been written, so the span keeps only
-  // what the call cannot have touched: the old rows before first_pos, or
-  // nothing when the rule restarted the context.
-  if (n > 0) {
-    tm_begin(d);
-    for (int done = 0; done < n; done += kSettleRows) {
-      const int m = std::min(kSettleRows, n - done);
-      const int rc = settle_pass(d, taps + (size_t)done * d->tw, m, first_pos + done, len + done);
-      if (rc) {
-        if (first != d->first)
-          d->len = 0;
-        else
-          d->len = std::min(d->len, len);
-        return rc;
-      }
-    }
-    tm_end(d);
-    d->tm.settles += d->tm.on;
-  }
-  d->first = first;
-  d->len = len + n;
-  return DFLASH_OK;
+  return push_rows(d, first_pos, n, taps, true, "settle");
+}
+
+int dflash_queue(dflash_t* d, int64_t first_pos, int32_t n, const float* taps) {
+  if (!d) return DFLASH_EINVAL;
+  return push_rows(d, first_pos, n, taps, false, "queue");
+}
+
+int dflash_flush(dflash_t* d) {
+  if (!d) return DFLASH_EINVAL;
+  if (d->pend == 0) return DFLASH_OK;
+  CtxState t = state_of(d);
+  if (!settle_state(d, t, d->pend))
+    return fail(d, DFLASH_ENOMEM, "flush: the context would not fit a layer's store");
+  if (int rc = reserve(d, t.len)) return rc;
+  Runs r;
+  add_waiting(d, r, 0, d->pend);
+  d->pend = 0;
+  d->phead = 0;
+  return settle_call(d, r);
 }
 
 // Argument checks shared by the block entry points.
@@ -861,6 +1147,9 @@ static int block_args(dflash* d, int32_t anchor, int64_t a, int32_t k, int32_t w
   if (anchor < 0 || anchor >= d->V) return fail(d, DFLASH_EINVAL, "block: anchor outside the vocabulary");
   if (a < 0) return fail(d, DFLASH_EINVAL, "block: a must be >= 0");
   if (!cand || !unary || !score || !chosen) return fail(d, DFLASH_EINVAL, "block: null output");
+  if (d->pend)
+    return fail(d, DFLASH_EINVAL, "block: %ld rows wait to become context (dflash_flush first)",
+                d->pend);
   return DFLASH_OK;
 }
 
@@ -916,10 +1205,10 @@ static int block_pass(dflash* d, const BlockScratch& b, int32_t anchor, int64_t 
     layer_range(d, l, a, &lo, &n);
     int nchunks = 0;
     const int chunk = attn_chunk(n, &nchunks);
-    const size_t lrow = (size_t)l * d->cap + (lo - d->first);
-    dfl::attention(st, b.qa, psq, d->sk + lrow * d->kd, d->sv + lrow * d->kd, b.kb, b.vb, B, d->nh,
-                   d->kv, d->hd, (int)n, lo, a, d->windows[l], chunk, nchunks, scale, b.pacc,
-                   b.pml);
+    const auto& S = d->ls[l];
+    const long s0 = S.cap ? (lo - d->first) % S.cap : 0;
+    dfl::attention(st, b.qa, psq, S.k, S.v, S.cap, s0, b.kb, b.vb, B, d->nh, d->kv, d->hd, (int)n,
+                   lo, a, d->windows[l], chunk, nchunks, scale, b.pacc, b.pml);
     tm_mark(d, DFLASH_ST_ATTN);
     dfl::attn_merge(st, b.pacc, b.pml, d->nh, d->kv, d->hd, nchunks, B, b.ya, psy);
     tm_mark(d, DFLASH_ST_ATTN);
@@ -1099,39 +1388,62 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
   return launch_check(d, "matvec");
 }
 
+// Copies n rows of a layer's ring from ring row r0 on (wrapping) to or from
+// a linear buffer.
+static int ring_copy(dflash* d, float* ring, long cap, long r0, float* lin, long n, bool out,
+                     const char* what) {
+  const size_t row = (size_t)d->kd * sizeof(float);
+  for (long done = 0; done < n;) {
+    const long r = (r0 + done) % cap, c = std::min(n - done, cap - r);
+    float* rp = ring + (size_t)r * d->kd;
+    float* lp = lin + (size_t)done * d->kd;
+    const int rc = hip_check(d,
+                             hipMemcpyAsync(out ? lp : rp, out ? rp : lp, c * row,
+                                            hipMemcpyDeviceToDevice, d->st),
+                             what);
+    if (rc) return rc;
+    done += c;
+  }
+  return DFLASH_OK;
+}
+
 int dflash_debug_read_store(dflash_t* d, int32_t layer, int64_t row0, int64_t n, float* k_out,
                             float* v_out) {
   if (!d || !k_out || !v_out) return DFLASH_EINVAL;
-  if (layer < 0 || layer >= d->L || row0 < 0 || n < 0 || row0 + n > d->cap)
-    return fail(d, DFLASH_EINVAL, "read_store: range outside the store");
-  const size_t off = ((size_t)layer * d->cap + row0) * d->kd, bytes = (size_t)n * d->kd * 4;
-  int rc = hip_check(d, hipMemcpyAsync(k_out, d->sk + off, bytes, hipMemcpyDeviceToDevice, d->st),
-                     "read_store");
-  if (!rc)
-    rc = hip_check(d, hipMemcpyAsync(v_out, d->sv + off, bytes, hipMemcpyDeviceToDevice, d->st),
-                   "read_store");
+  if (layer < 0 || layer >= d->L || n < 0 || row0 < d->ls[layer].dropped || row0 + n > d->len)
+    return fail(d, DFLASH_EINVAL, "read_store: rows the layer does not hold");
+  auto& S = d->ls[layer];
+  int rc = ring_copy(d, S.k, S.cap, row0, k_out, n, true, "read_store");
+  if (!rc) rc = ring_copy(d, S.v, S.cap, row0, v_out, n, true, "read_store");
   return rc;
 }
 
 int dflash_debug_load_store(dflash_t* d, int64_t first, int64_t len, const float* const* k,
                             const float* const* v) {
   if (!d || !k || !v) return DFLASH_EINVAL;
-  if (first < 0 || len < 0 || len > d->cap) return fail(d, DFLASH_EINVAL, "load_store: bad range");
+  if (first < 0 || len < 0) return fail(d, DFLASH_EINVAL, "load_store: bad range");
   for (int l = 0; l < d->L; ++l) {
     if (len && (!k[l] || !v[l])) return fail(d, DFLASH_EINVAL, "load_store: null layer pointer");
   }
-  const size_t bytes = (size_t)len * d->kd * 4;
-  for (int l = 0; l < d->L && len; ++l) {
-    const size_t off = (size_t)l * d->cap * d->kd;
-    int rc = hip_check(d, hipMemcpyAsync(d->sk + off, k[l], bytes, hipMemcpyDeviceToDevice, d->st),
-                       "load_store");
+  // as one settle_rows call of len rows on an empty context at first
+  CtxState s{first, 0, 0, 0, std::vector<long>(d->L, 0)};
+  if (!settle_state(d, s, len))
+    return fail(d, DFLASH_ENOMEM, "load_store: %ld rows do not fit a layer's store", (long)len);
+  if (int rc = reserve(d, s.len)) return rc;
+  commit(d, s);
+  for (int l = 0; l < d->L; ++l) {
+    auto& S = d->ls[l];
+    const long dr = S.dropped, held = len - dr;
+    int rc = ring_copy(d, S.k, S.cap, dr, const_cast<float*>(k[l]) + (size_t)dr * d->kd, held,
+                       false, "load_store");
     if (!rc)
-      rc = hip_check(d, hipMemcpyAsync(d->sv + off, v[l], bytes, hipMemcpyDeviceToDevice, d->st),
+      rc = ring_copy(d, S.v, S.cap, dr, const_cast<float*>(v[l]) + (size_t)dr * d->kd, held, false,
                      "load_store");
-    if (rc) return rc;
+    if (rc) {
+      lose_context(d);
+      return rc;
+    }
   }
-  d->first = first;
-  d->len = len;
   return DFLASH_OK;
 }
 

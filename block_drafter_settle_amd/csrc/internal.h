@@ -108,6 +108,16 @@ void head_sel(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t
               int width, int k, float* logits, const uint16_t* sel, int rank, float* hp,
               SelectScratch sc);
 
+// Rows 0..m of an operand taken from up to three runs of consecutive rows
+// (ld floats apart): rows [0, n0) from p[0], [n0, n0 + n1) from p[1], the
+// rest from p[2] (a settle's rows may wait in a ring and follow from the
+// caller's buffer).
+struct RowSrc {
+  const float* p[3];
+  int n0, n1;
+  long ld;
+};
+void to_a(hipStream_t st, const RowSrc& x, int m, int K, uint16_t* xa, long ps);
 void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa, long ps);
 // Row kernels: sqp holds partial sums of squares of each row, row_chunks(N)
 // per row from rowsum_sq and embed (256 channels each), conv1_chunks(hs)
@@ -136,17 +146,29 @@ void conv1(hipStream_t st, float* h, const float* opart, int splits, long split_
 void qkv_post(hipStream_t st, const float* part, int splits, long split_stride, int rows, int nh,
               int kv, int hd, const float* q_norm, const float* k_norm, const float* inv_freq,
               long pos0, int rot, float eps, uint16_t* qa, long qps, float* kb, float* vb);
+// A layer's context store: a ring of cap rows of [kv_heads][head_dim] f32
+// keys and values; position p sits at row (p − first) mod cap.
+struct StoreSlot {
+  float* k;
+  float* v;
+  long cap;
+};
+// row0 = pos0 − first; row_end: one past the settle call's last row (rows
+// below row_end − cap of a layer are not written to it); tab: the layers'
+// stores (device memory).
 void settle_kv(hipStream_t st, const float* part, int splits, long split_stride, int rows,
                int layers, int kv, int hd, const float* k_norm, const float* inv_freq,
-               const int* rot, long pos0, float eps, const float* sqp, int hs, float* store_k,
-               float* store_v, long cap, long row0);
+               const int* rot, long pos0, float eps, const float* sqp, int hs,
+               const StoreSlot* tab, long row0, long row_end);
 // Context chunks per kv head of one attention call; the merge holds one
 // weight per chunk (and one for the block's own rows) in LDS.
 constexpr int kAttnMaxChunks = 64;
+// sk, sv: the layer's ring of cap rows; its n keys of positions lo_pos..
+// start at ring row s0 and wrap at most once.
 void attention(hipStream_t st, const uint16_t* qa, long qps, const float* sk, const float* sv,
-               const float* kb, const float* vb, int B, int nh, int kv, int hd, int n,
-               long lo_pos, long a, int window, int chunk, int nchunks, float scale,
-               float* pacc, float* pml);
+               long cap, long s0, const float* kb, const float* vb, int B, int nh, int kv,
+               int hd, int n, long lo_pos, long a, int window, int chunk, int nchunks,
+               float scale, float* pacc, float* pml);
 void attn_merge(hipStream_t st, const float* pacc, const float* pml, int nh, int kv, int hd,
                 int nchunks, int B, uint16_t* ya, long ps);
 // Selection (`top_k` + `select_with`) on logits [k][width] and hp rows

@@ -364,8 +364,8 @@ __global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, l
 
 // f32 rows → A-layout f16 (plane 1 at xa + ps when ps is nonzero); one
 // thread per 8 columns of one row.
-__global__ __launch_bounds__(kThreads) void k_to_a(const float* __restrict__ x, long ld, int m,
-                                                   int K, f16* __restrict__ xa, long ps) {
+__global__ __launch_bounds__(kThreads) void k_to_a(RowSrc x, int m, int K, f16* __restrict__ xa,
+                                                   long ps) {
   const int mb = blockIdx.y;
   const long t = (long)blockIdx.x * kThreads + threadIdx.x;
   if (t >= (long)(K >> 3) * 16) return;
@@ -374,7 +374,11 @@ __global__ __launch_bounds__(kThreads) void k_to_a(const float* __restrict__ x, 
   const int row = mb * 16 + i;
   float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (row < m) {
-    const float4* p = reinterpret_cast<const float4*>(x + (size_t)row * ld + s * 32 + j * 8);
+    const int r1 = row - x.n0, r2 = r1 - x.n1;
+    const float* src = r1 < 0 ? x.p[0] + (size_t)row * x.ld
+                       : r2 < 0 ? x.p[1] + (size_t)r1 * x.ld
+                                : x.p[2] + (size_t)r2 * x.ld;
+    const float4* p = reinterpret_cast<const float4*>(src + s * 32 + j * 8);
     const float4 lo = p[0], hi = p[1];
     f[0] = lo.x, f[1] = lo.y, f[2] = lo.z, f[3] = lo.w;
     f[4] = hi.x, f[5] = hi.y, f[6] = hi.z, f[7] = hi.w;
@@ -696,9 +700,15 @@ __global__ __launch_bounds__(64) void k_settle_kv(const float* __restrict__ part
                                                   const float* __restrict__ inv,
                                                   const int* __restrict__ rot, long pos0,
                                                   float eps, const float* __restrict__ sqp,
-                                                  int nchunk, int hs, float* __restrict__ sk,
-                                                  float* __restrict__ sv, long cap, long row0) {
+                                                  int nchunk, int hs,
+                                                  const StoreSlot* __restrict__ tab, long row0,
+                                                  long row_end) {
   const int r = blockIdx.x, l = blockIdx.y, hh = blockIdx.z;
+  const StoreSlot so = tab[l];
+  // a row that a later row of the same settle call takes the ring place of
+  // (cap rows on) is not written: it would race with that row in this launch,
+  // and the layer does not keep it
+  if (row0 + r < row_end - so.cap) return;
   const int kd = kv * hd, N = L * 2 * kd, half = hd >> 1;
   const bool isk = hh < kv;
   const int g = isk ? hh : hh - kv;
@@ -715,7 +725,7 @@ __global__ __launch_bounds__(64) void k_settle_kv(const float* __restrict__ part
     p.hi[c] *= sr;
   }
   if (isk) norm_rope(p, hd, knorm + (size_t)l * hd, eps, inv, pos0 + r, rot[l]);
-  float* dst = (isk ? sk : sv) + ((size_t)l * cap + row0 + r) * kd + (size_t)g * hd;
+  float* dst = (isk ? so.k : so.v) + (size_t)((row0 + r) % so.cap) * kd + (size_t)g * hd;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int i = threadIdx.x + 64 * c;
@@ -1292,9 +1302,13 @@ void head_sel(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t
                                             sc.counters);
 }
 
-void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa, long ps) {
+void to_a(hipStream_t st, const RowSrc& x, int m, int K, uint16_t* xa, long ps) {
   dim3 grid(cdiv((long)(K / 8) * 16, kThreads), cdiv(m, 16));
-  k_to_a<<<grid, kThreads, 0, st>>>(x, ld, m, K, reinterpret_cast<f16*>(xa), ps);
+  k_to_a<<<grid, kThreads, 0, st>>>(x, m, K, reinterpret_cast<f16*>(xa), ps);
+}
+
+void to_a(hipStream_t st, const float* x, long ld, int m, int K, uint16_t* xa, long ps) {
+  to_a(st, RowSrc{{x, x, x}, m, 0, ld}, m, K, xa, ps);
 }
 
 void rowsum_sq(hipStream_t st, const float* part, int splits, long ss, int rows, int N,
@@ -1357,10 +1371,11 @@ void qkv_post(hipStream_t st, const float* part, int splits, long ss, int rows, 
 
 void settle_kv(hipStream_t st, const float* part, int splits, long ss, int rows, int layers,
                int kv, int hd, const float* k_norm, const float* inv, const int* rot, long pos0,
-               float eps, const float* sqp, int hs, float* sk, float* sv, long cap, long row0) {
+               float eps, const float* sqp, int hs, const StoreSlot* tab, long row0,
+               long row_end) {
   dim3 grid(rows, layers, 2 * kv);
   k_settle_kv<<<grid, 64, 0, st>>>(part, splits, ss, layers, kv, hd, k_norm, inv, rot, pos0, eps,
-                                   sqp, cdiv(hs, kChunk), hs, sk, sv, cap, row0);
+                                   sqp, cdiv(hs, kChunk), hs, tab, row0, row_end);
 }
 
 int topk_slices(int width) { return cdiv(width, 64 * kSliceVPL); }

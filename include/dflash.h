@@ -13,12 +13,12 @@
  * Conventions for every entry point:
  *   - Return 0 on success or a negative code: DFLASH_EINVAL (-1) for an
  *     invalid argument or geometry, DFLASH_ENOMEM (-2) for device memory or
- *     store capacity (max_context) exhausted, DFLASH_EHIP (-3) for a HIP
- *     runtime error. The message is kept for dflash_last_error. Arguments
- *     are checked before any launch, and a call they reject changes no
- *     state. After DFLASH_EHIP (a launch failed: the device is usually
- *     unusable then) the settled span keeps only rows the call cannot have
- *     written (see dflash_settle).
+ *     a layer's store capacity (max_context) exhausted, DFLASH_EHIP (-3) for
+ *     a HIP runtime error. The message is kept for dflash_last_error.
+ *     Arguments and capacity are checked before any launch, and a call they
+ *     reject changes no state. After DFLASH_EHIP from a call that settles
+ *     or moves context rows (a launch failed: the device is usually unusable
+ *     then) the context is empty: span [first, first).
  *   - "dev" pointers are device memory the caller owns (e.g. torch tensors'
  *     data_ptr on the same GPU); "host" pointers are host memory.
  *   - Work is enqueued on the stream given at create and is asynchronous:
@@ -81,7 +81,9 @@ typedef struct {
   const int32_t* windows; /* host [layers]: positions a block row sees back, 0 = all */
   const uint8_t* rotary;  /* host [layers]: 1 = rotary queries and keys, 0 = `no_rope` */
   double rope_theta, eps;
-  int64_t max_context; /* rows the context store holds (positions first .. first+max_context) */
+  int64_t max_context; /* most context rows one layer holds: a layer without a window
+                          holds every settled row, so the settled span is at most this
+                          long; a windowed layer holds at most min(2·window, max_context) */
 } dflash_geometry;
 
 typedef struct {
@@ -98,29 +100,60 @@ typedef struct {
 
 /* Build a drafter: validate the geometry, copy every weight to device memory
    (int4 and f16 matrices repacked into the kernels' tile layouts), allocate
-   the f32 context store ([layer][max_context][kv_heads][head_dim], keys and
-   values) and all scratch. Synchronous: the caller may free every host array
+   each windowed layer's context ring (min(2·window, max_context) rows of f32
+   [kv_heads][head_dim] keys and values: the rows a layer holds never exceed
+   that, see dflash_settle), the ring of waiting tap rows (see dflash_queue)
+   and all scratch. A layer without a window gets its store as rows come
+   (dflash_reserve). Synchronous: the caller may free every host array
    once it returns. `stream` is a hipStream_t (NULL = the null stream) that
    every later call enqueues on. On failure *out is NULL and
    dflash_last_error(NULL) has the message. */
 int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* stream,
                   dflash_t** out);
 
-/* Context settle (`settle_rows`; `Dev::settle`): n joined tap rows
-   (dev f32 [n][n_taps*hidden], row r = position first_pos + r, taps in the
-   order of the geometry's taps) become context: t = rms(fc·row, hidden_norm);
-   per layer K = rot(rms(Wk·t per kv head, k_norm), position) (no rotation
-   on a no-rope layer), V = Wv·t, stored f32.
-   Position rule (`queue_context`): with first ≤ first_pos ≤ first+len the
-   context is cut at first_pos and the rows appended; otherwise (an empty
-   context, a gap, or first_pos < first) it restarts at first_pos. n = 0 only
-   applies the rule. Fails with DFLASH_ENOMEM if the rows would not fit
-   max_context (nothing changed). Any n is accepted and taken 256 rows at a
-   time; the new span is committed once every pass has been enqueued. If a
-   launch fails (DFLASH_EHIP) the span becomes [first, min(first+len,
-   first_pos)) when the rule kept the old first position, and empty when it
-   restarted the context. */
+/* Context settle (`push_context`: `queue_context` then `settle`; the rows
+   themselves as `settle_rows` and `Dev::settle` make them): n joined tap
+   rows (dev f32 [n][n_taps*hidden], row r = position first_pos + r, taps in
+   the order of the geometry's taps) become context, after any rows that
+   wait (dflash_queue): t = rms(fc·row, hidden_norm); per layer K =
+   rot(rms(Wk·t per kv head, k_norm), position) (no rotation on a no-rope
+   layer), V = Wv·t, stored f32.
+   Position rule (`queue_context`): with first ≤ first_pos ≤ the span's end
+   (waiting rows included) the context is cut at first_pos and the rows
+   appended; otherwise (a gap, or first_pos < first) it restarts at
+   first_pos. n = 0 only applies the rule (and settles what waits).
+   The rows are settled by `settle_rows` calls, 256 rows a pass: when more
+   than the waiting limit (see dflash_queue) would wait, first the oldest
+   rows past it (a multiple of 64), then the rest. After each call a layer
+   with window w > 0 that holds more than 2w rows keeps only the last w
+   (`Ctx::dropped`): a block sees no further back than its window, so a
+   block at the end of the context is unchanged by the drop. Fails with
+   DFLASH_ENOMEM (nothing changed) if a layer would hold more rows than
+   max_context or its store cannot grow. */
 int dflash_settle(dflash_t* d, int64_t first_pos, int32_t n, const float* taps);
+
+/* Queue rows without settling them (`queue_context`): the position rule of
+   dflash_settle, then the rows wait in the library's ring (copied from the
+   caller's buffer, which may be reused once the stream passes this call).
+   At most 512 rows wait (`PENDING_ROWS`; when every layer is windowed,
+   max(512, widest window + 256): `BLOCK_SLACK`); past that the oldest
+   settle at once, as many as bring the waiting rows to the limit, rounded
+   up to a multiple of 64 (`CONTEXT_CHUNK`). dflash_block fails while rows
+   wait. Errors as dflash_settle; also fails with DFLASH_ENOMEM if the rows
+   that would then wait could not be settled later. */
+int dflash_queue(dflash_t* d, int64_t first_pos, int32_t n, const float* taps);
+
+/* Settle every waiting row (`settle`), one `settle_rows` call. */
+int dflash_flush(dflash_t* d);
+
+/* Room for `rows` context rows in every layer without a window
+   (`Dev::reserve`): a store that is too small grows to max(rows, 2·its
+   rows, 4096), at most max_context, keeping what it holds (the stream is
+   synchronised when a store moves). The settle calls reserve by themselves;
+   a caller that knows its context length may reserve up front so that no
+   later call moves a store. DFLASH_ENOMEM if rows > max_context or the
+   memory cannot be had (nothing changed). */
+int dflash_reserve(dflash_t* d, int64_t rows);
 
 /* Block pass (`Drafter::block` + the head + `select_with`): rows
    [embed[anchor_token], embed[mask_token] × (block−1)] at positions a, a+1, …
@@ -138,7 +171,8 @@ int dflash_settle(dflash_t* d, int64_t first_pos, int32_t n, const float* taps);
      score   dev f32   [k][selector_top] their selector scores
      chosen  dev int32 [k] the first candidate with the largest score.
    Requires 1 ≤ k < block, selector_top ≤ width ≤ vocab,
-   0 ≤ anchor_token < vocab, a ≥ 0. */
+   0 ≤ anchor_token < vocab, a ≥ 0, and no waiting rows. A layer's context
+   range starts at its first held position, first + dropped (`block_dev`). */
 int dflash_block(dflash_t* d, int32_t anchor_token, int64_t a, int32_t k, int32_t width,
                  float* logits, int32_t* cand, float* unary, float* score, int32_t* chosen);
 
@@ -160,11 +194,19 @@ int dflash_block_noalloc(dflash_t* d, int32_t anchor_token, int64_t a, int32_t k
                          float* logits, int32_t* cand, float* unary, float* score,
                          int32_t* chosen);
 
-/* Forget the context from position pos on (`truncate`). */
+/* Forget the context from position pos on (`truncate`), waiting rows
+   included; a layer that had dropped rows past pos holds none. */
 int dflash_truncate(dflash_t* d, int64_t pos);
 
-/* The settled span: *first and one past the last settled position. */
+/* The span (`span`): *first and one past the last position, waiting rows
+   included (`next_position`). */
 int dflash_span(const dflash_t* d, int64_t* first, int64_t* end);
+
+/* The context's bookkeeping: first position, settled rows, waiting rows,
+   and (dropped non-NULL: host int64 [layers]) each layer's dropped rows, so
+   that layer l holds positions first + dropped[l] .. first + settled. */
+int dflash_state(const dflash_t* d, int64_t* first, int64_t* settled, int64_t* waiting,
+                 int64_t* dropped);
 
 /* Wait for every call enqueued so far. */
 int dflash_sync(dflash_t* d);
@@ -239,19 +281,21 @@ enum {
 int dflash_debug_dequant(dflash_t* d, int32_t layer, int32_t which, float* out);
 
 /* y = W·x with the product path's GEMM kernels: x dev f32 [m][cols],
-   y dev f32 [m][rows], m in [1, 256]. x enters as the block pass's
-   operands do for m <= 16 (two f16 planes, hi and the rest) and as the
-   settle's do above (one f16 plane). */
+   y dev f32 [m][rows], m in [1, 256]. x enters as every operand of the
+   block and settle passes does: two f16 planes, hi and the rest. */
 int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* x, int32_t m,
                         float* y);
 
-/* Copy rows [row0, row0+n) of layer's store (row i = position first+i):
+/* Copy the rows of positions first+row0 .. first+row0+n−1 from layer's
+   store (rows the layer holds: dropped ≤ row0, row0 + n ≤ settled):
    k_out, v_out dev f32 [n][kv_heads*head_dim]. */
 int dflash_debug_read_store(dflash_t* d, int32_t layer, int64_t row0, int64_t n, float* k_out,
                             float* v_out);
 
-/* Replace the context with `len` given rows at positions first..first+len−1:
-   k[l], v[l] (host array of `layers` dev pointers) dev f32 [len][kv*hd]. */
+/* Replace the context with `len` given rows at positions first..first+len−1,
+   as if one settle had made them on an empty context (waiting rows go;
+   each windowed layer then drops rows as after a settle): k[l], v[l] (host
+   array of `layers` dev pointers) dev f32 [len][kv*hd]. */
 int dflash_debug_load_store(dflash_t* d, int64_t first, int64_t len, const float* const* k,
                             const float* const* v);
 

@@ -192,31 +192,46 @@ def test_matvec_parity(small, orc, m):
 
 # ------------------------------------------------------------------ settle
 
-def _read_store(d, g, rows, row0=0):
+def held_store(d, g):
+    """The rows each layer holds (positions first + dropped .. first + settled)."""
     dev = _dev()
     kd = g["kv_heads"] * g["head_dim"]
+    _, settled, _, dropped = d.state()
     out = []
     for l in range(g["layers"]):
-        k = torch.empty(rows, kd, device=dev)
-        v = torch.empty(rows, kd, device=dev)
-        d.debug_read_store(l, row0, rows, k.data_ptr(), v.data_ptr())
-        out.append((k, v))
+        n = settled - dropped[l]
+        k = torch.empty(max(n, 1), kd, device=dev)
+        v = torch.empty(max(n, 1), kd, device=dev)
+        d.debug_read_store(l, dropped[l], n, k.data_ptr(), v.data_ptr())
+        out.append((k[:n], v[:n]))
     d.sync()
     return [(k.cpu().numpy(), v.cpu().numpy()) for k, v in out]
 
 
+def same_state(d, ctx):
+    """The library's bookkeeping equals the oracle context's, exactly."""
+    first, settled, waiting, dropped = d.state()
+    assert (first, settled, waiting, dropped) == (ctx.first, ctx.len, ctx.pending.shape[0],
+                                                  list(ctx.dropped)), (d.state(), ctx.span())
+    assert d.span() == ctx.span()
+
+
 @pytest.mark.parametrize("n,first", [(1, 0), (40, 100), (300, 7)])
 def test_settle_parity(small, orc, n, first):
+    from oracle.context import Context
+
     g, w, d = small
     dev = _dev()
     taps = synth.make_taps(g, n, seed=n)
     d.settle(first, n, taps.to(dev).data_ptr())
     assert d.span() == (first, first + n)
-    got = _read_store(d, g, n)
-    K, V = orc.Model(g, w).settle(taps.numpy(), first)
+    ctx = Context(orc.Model(g, w))
+    ctx.push(first, taps.numpy())
+    same_state(d, ctx)
+    got = held_store(d, g)
     for l in range(g["layers"]):
-        close(got[l][0], K[l], f"settle K layer {l}")
-        close(got[l][1], V[l], f"settle V layer {l}")
+        close(got[l][0], ctx.k[l], f"settle K layer {l}")
+        close(got[l][1], ctx.v[l], f"settle V layer {l}")
 
 
 def test_settle_position_rule(small):
@@ -247,13 +262,15 @@ def test_rewind_resettle_equals_fresh(small):
     taps = synth.make_taps(g, 24, seed=8).to(dev)
     other = synth.make_taps(g, 24, seed=9).to(dev)
     d.settle(0, 24, taps.data_ptr())
-    fresh = _read_store(d, g, 24)
+    fresh, st_fresh = held_store(d, g), d.state()
     d.settle(0, 24, other.data_ptr())
     d.settle(10, 14, taps[10:].data_ptr())
-    mixed = _read_store(d, g, 24)
+    mixed = held_store(d, g)
+    assert d.state() == st_fresh
     for l in range(g["layers"]):
-        assert np.array_equal(fresh[l][0][10:], mixed[l][0][10:])
-        assert np.array_equal(fresh[l][1][10:], mixed[l][1][10:])
+        keep = max(0, 10 - st_fresh[3][l])  # held rows at positions ≥ 10
+        assert np.array_equal(fresh[l][0][keep:], mixed[l][0][keep:])
+        assert np.array_equal(fresh[l][1][keep:], mixed[l][1][keep:])
 
 
 # ------------------------------------------------------------------- block
@@ -304,20 +321,20 @@ def test_block_parity(orc, case):
     else:
         w, d = make(g, seed=2, max_context=max(length, 1) + 8)
     try:
+        from oracle.context import Context
+
         dev = _dev()
         m = orc.Model(g, w)
+        ctx = Context(m)
         if length:
             taps = synth.make_taps(g, length, seed=3)
             d.settle(first, length, taps.to(dev).data_ptr())
-            K, V = m.settle(taps.numpy(), first)
-            store = [(K[l], V[l]) for l in range(g["layers"])]
-        else:
-            store = [(np.zeros((1, g["kv_heads"] * g["head_dim"]), np.float32),) * 2
-                     for _ in range(g["layers"])]
+            ctx.push(first, taps.numpy())
+        same_state(d, ctx)
         a = first + length + da
         anchor = 123
         got = run_block(d, g, anchor, a, k, width)
-        ref = m.block(store, first, length, anchor, a, k, width)
+        ref = ctx.block(anchor, a, k, width)
         tag = f"block {over} ctx {length}"
         close(got["hidden"], ref["hidden"], tag + " hidden")
         close(got["logits"], ref["logits"], tag + " logits")
