@@ -74,7 +74,11 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev).cuda_stream
+    # one side stream for everything (torch's work and events included): a
+    # block can then also be captured into a graph on it
+    side = torch.cuda.Stream(dev)
+    torch.cuda.set_stream(side)
+    stream = side.cuda_stream
     g = synth.geometry("t27b")
     hs, V, tw, L = g["hidden"], g["vocab"], synth.tap_width(g), g["layers"]
     kd = g["kv_heads"] * g["head_dim"]
@@ -203,6 +207,19 @@ def main():
     torch.cuda.synchronize()
     bo_us = (time.perf_counter() - t0) / n2 * 1e6
     pos_bo = pos
+    # the same block as one submission: captured into a graph once, replayed
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=side, capture_error_mode="thread_local"):
+        d.block(anchors[0], pos, k, width, *ptrs)
+    for i in range(5):
+        gr.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n2):
+        gr.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t0) / n2 * 1e6
+    del gr
 
     # stage timers over a further stretch of the stream
     d.set_timing(True)
@@ -271,6 +288,9 @@ def main():
             "note": "blocks alone at the full width, back to back (no settle between, no "
                     "stage timers); stage_timer_us is the same pass under per-kernel events",
             "stage_timer_us": round(block_us, 1),
+            "graph_replay_us": round(graph_us, 1),
+            "graph_note": "the same block captured once into a HIP graph and replayed "
+                          "(one submission a block)",
         },
         "roofline": {
             "kernel": "k_head (head logits over the vocabulary + selector projection)",

@@ -28,9 +28,10 @@ namespace {
 constexpr int kSettleRows = 256;     // rows one settle pass takes
 constexpr int kTargetBlocks = 512;   // workgroups a GEMM launch aims for (256 CUs)
 constexpr int kR = 2;        // row tiles per wave of the skinny GEMMs (8 a workgroup)
-constexpr int kKsQkv = 8;    // q/k/v, int4: spans (128 columns) per split
-constexpr int kKsO = 2;      // o, int4
-constexpr int kKsDown = 8;   // down, int4
+// the block's int4 GEMMs: row tiles a wave and spans (128 columns) a split
+constexpr int kRQkv = 2, kKsQkv = 8;    // q/k/v
+constexpr int kRO = 2, kKsO = 2;        // o
+constexpr int kRDown = 2, kKsDown = 8;  // down
 constexpr int kSettleI4Blocks = 2;  // above this many 16-row blocks the settle's k/v use the many-row kernel
 // `queue_context`: at most kPendingRows rows wait (as many as the widest
 // window plus kBlockSlack when every layer is windowed); past that the
@@ -1194,8 +1195,8 @@ static int block_pass(dflash* d, const BlockScratch& b, int32_t anchor, int64_t 
     tm_mark(d, DFLASH_ST_CONV);
     dfl::gemm_i4_block(st, b.xca, psh, hs, d->qkv.codes + i4l_qkv * 1024 * l,
                        d->qkv.scales + i4l_qkv * 64 * l,
-                       dfl::TileMap{d->qkv.tiles, d->qkv.tiles, 0, 0}, d->qd + 2 * d->kd, sqk.per,
-                       b.part, ssq);
+                       dfl::TileMap{d->qkv.tiles, d->qkv.tiles, 0, 0}, d->qd + 2 * d->kd, kRQkv,
+                       sqk.per, b.part, ssq);
     tm_mark(d, DFLASH_ST_QKV);
     dfl::qkv_post(st, b.part, sqk.S, ssq, B, d->nh, d->kv, d->hd, d->q_norm + (size_t)l * d->hd,
                   d->k_norm + (size_t)l * d->hd, d->inv, a, d->rot[l], d->eps, b.qa, psq, b.kb, b.vb);
@@ -1215,7 +1216,7 @@ static int block_pass(dflash* d, const BlockScratch& b, int32_t anchor, int64_t 
     // o, conv_out into the residual (and the MLP norm's input)
     dfl::gemm_i4_block(st, b.ya, psy, d->qd, d->o.codes + i4l_o * 1024 * l,
                        d->o.scales + i4l_o * 64 * l, dfl::TileMap{d->o.tiles, d->o.tiles, 0, 0},
-                       hs, so.per, b.part, ssh);
+                       hs, kRO, so.per, b.part, ssh);
     tm_mark(d, DFLASH_ST_O);
     dfl::conv1(st, b.h, b.part, so.S, ssh, b.dsum_a, ab, B, hs, d->gs, d->kn, b.sqp, post,
                b.xa, psh);
@@ -1233,7 +1234,8 @@ static int block_pass(dflash* d, const BlockScratch& b, int32_t anchor, int64_t 
     tm_mark(d, DFLASH_ST_GLU);
     dfl::gemm_i4_block(st, b.ma, psm, d->ffn, d->down.codes + i4l_dn * 1024 * l,
                        d->down.scales + i4l_dn * 64 * l,
-                       dfl::TileMap{d->down.tiles, d->down.tiles, 0, 0}, hs, sdn.per, b.part, ssh);
+                       dfl::TileMap{d->down.tiles, d->down.tiles, 0, 0}, hs, kRDown, sdn.per, b.part,
+                       ssh);
     tm_mark(d, DFLASH_ST_DOWN);
     // conv_out into the residual, and the next layer's attention-norm input
     // (the final norm runs on its own below)
@@ -1374,7 +1376,7 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
   if ((long)s.S * ss > d->part_floats) return fail(d, DFLASH_EINVAL, "matvec: partials too large");
   if (is_i4 && mb == 1)
     dfl::gemm_i4_block(d->st, d->taps_a, ps, cols, static_cast<const uint8_t*>(codes), scales, map,
-                       rows, 2, d->part, ss);
+                       rows, 2, 2, d->part, ss);
   else if (is_i4)
     dfl::gemm_i4(d->st, d->taps_a, ps, cols, mb, static_cast<const uint8_t*>(codes), scales, map, rows,
                  s.S, s.per, d->part, ss);

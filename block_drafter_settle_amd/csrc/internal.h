@@ -56,11 +56,12 @@ void gemm_big_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int mblock
                   const uint16_t* w, TileMap map, int N, int splits, int steps_per_split,
                   float* out, long split_stride);
 // The block pass's 16-row int4 GEMM (two planes, ps ≠ 0; skinny.hip):
-// splits of `ks` spans (128 columns) each, ks 2 or 8, i4_block_splits(K, ks)
-// of them; out as gemm_i4. Two row tiles a wave, four waves a workgroup.
+// splits of `ks` spans (128 columns) each, i4_block_splits(K, ks) of them;
+// out as gemm_i4. R row tiles a wave, four waves a workgroup; (R, ks) one of
+// (1, 4), (2, 2), (2, 4), (2, 8), (4, 4).
 int i4_block_splits(int K, int ks);
 void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
-                   const uint16_t* scales, TileMap map, int N, int ks, float* out,
+                   const uint16_t* scales, TileMap map, int N, int R, int ks, float* out,
                    long split_stride);
 // The block pass's 16-row f16 GEMM (two planes, ps ≠ 0): f16_block_splits(K)
 // splits of 512 columns; out as gemm_f16.

@@ -178,13 +178,20 @@ static void launch_i4_block(hipStream_t st, const f16* x, long ps, int K, const 
 }
 
 void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
-                   const uint16_t* scales, TileMap map, int N, int ks, float* out, long ss) {
+                   const uint16_t* scales, TileMap map, int N, int R, int ks, float* out,
+                   long ss) {
   const f16* x = reinterpret_cast<const f16*>(xa);
   const uint4* c = reinterpret_cast<const uint4*>(codes);
   const uint2* s = reinterpret_cast<const uint2*>(scales);
-  if (ks == 2)
+  if (R == 1 && ks == 4)
+    launch_i4_block<1, 4>(st, x, ps, K, c, s, map, N, out, ss);
+  else if (R == 2 && ks == 2)
     launch_i4_block<2, 2>(st, x, ps, K, c, s, map, N, out, ss);
-  else
+  else if (R == 2 && ks == 4)
+    launch_i4_block<2, 4>(st, x, ps, K, c, s, map, N, out, ss);
+  else if (R == 4 && ks == 4)
+    launch_i4_block<4, 4>(st, x, ps, K, c, s, map, N, out, ss);
+  else  // (2, 8)
     launch_i4_block<2, 8>(st, x, ps, K, c, s, map, N, out, ss);
 }
 
