@@ -58,6 +58,7 @@ def main():
                     help="stream steps the CPU oracle baseline runs")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 4B and long-context legs")
+    ap.add_argument("--no-batch", action="store_true", help="skip the batched-blocks leg")
     ap.add_argument("--blocks-4b", type=int, default=200)
     ap.add_argument("--steps-long", type=int, default=200)
     args = ap.parse_args()
@@ -221,6 +222,11 @@ def main():
     graph_us = (time.perf_counter() - t0) / n2 * 1e6
     del gr
 
+    # batched blocks: B handles sharing the weights, each over its own
+    # 32768-position context (the lead is this stream's handle)
+    batched = {} if args.no_batch else leg_batch(pkg, synth, dev, stream, d, g, ctx0, pos, k,
+                                                 width, anchors, n2)
+
     # stage timers over a further stretch of the stream
     d.set_timing(True)
     for i in range(warm + steps + args.timing_steps, total):
@@ -292,6 +298,7 @@ def main():
             "graph_note": "the same block captured once into a HIP graph and replayed "
                           "(one submission a block)",
         },
+        "batched": batched,
         "roofline": {
             "kernel": "k_head (head logits over the vocabulary + selector projection)",
             "bound": "hbm",
@@ -385,6 +392,80 @@ def block_bytes(g, first, a, width, k):
         lo = max(first, a + 1 - wdw) if wdw > 0 else first
         kv_rows += max(0, a - lo)
     return i4 + kproj + head + kv_rows * kd * 4 * 2 + k * (1 + top) * rank * 2 + 2 * hs * 2
+
+
+def batch_bytes(g, seqs, width, k):
+    """Algorithmic bytes of one batched pass: the weights once, and each
+    sequence's own K/V rows, logits, codebook and embedding rows. seqs:
+    (first, a) per sequence."""
+    one = [block_bytes(g, f, a, width, k) for f, a in seqs]
+    hs, rank, top = g["hidden"], g["selector_rank"], g["selector_top"]
+    own = [block_bytes(g, f, a, width, k) - block_bytes(g, 0, 0, width, k) +
+           k * width * 4 + k * (1 + top) * rank * 2 + 2 * hs * 2 for f, a in seqs]
+    return one[0] - own[0] + sum(own)
+
+
+def block_flops(g, width, k, nseq):
+    """Products of nseq blocks: every layer's projections on the block's 16
+    rows, the head on rows 1..k and the selector projection on all 16."""
+    hs, L = g["hidden"], g["layers"]
+    kd, qd = g["kv_heads"] * g["head_dim"], g["heads"] * g["head_dim"]
+    ffn, rows = g["intermediate"], g["block"]
+    kp = 2 * (2 * g["conv_kernel"] * hs // g["conv_group"]) * hs
+    per_layer = qd * hs + 2 * kd * hs + hs * qd + 3 * ffn * hs + kp
+    return nseq * 2.0 * (rows * L * per_layer + k * width * hs + rows * g["selector_rank"] * hs)
+
+
+def leg_batch(pkg, synth, dev, stream, lead, g, ctx0, lead_pos, k, width, anchors, nb):
+    """Batched blocks at B = 2, 4, 8: the lead plus B−1 context handles on the
+    same weights, each holding a synthetic 32768-position store; nb passes
+    each, timed back to back."""
+    import torch
+
+    store = synth.make_store(g, ctx0, seed=7, device=dev)
+    others = []
+    for i in range(7):
+        o = pkg.Drafter.context_of(lead, ctx0 + 64, stream)
+        o.debug_load_store(0, ctx0, [x[0].data_ptr() for x in store],
+                           [x[1].data_ptr() for x in store])
+        others.append(o)
+    del store
+    top = g["selector_top"]
+    res = {}
+    for nseq in (2, 4, 8):
+        ds = [lead] + others[:nseq - 1]
+        out = [torch.empty(nseq, k, width, device=dev),
+               torch.empty(nseq, k, top, dtype=torch.int32, device=dev),
+               torch.empty(nseq, k, top, device=dev), torch.empty(nseq, k, top, device=dev),
+               torch.empty(nseq, k, dtype=torch.int32, device=dev)]
+        ptrs = [t.data_ptr() for t in out]
+        pos = [lead_pos] + [ctx0] * (nseq - 1)
+        firsts = [0] * nseq
+        for i in range(3):
+            pkg.block_batch(ds, anchors[i:i + nseq], pos, k, width, *ptrs)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(nb):
+            pkg.block_batch(ds, anchors[i:i + nseq], pos, k, width, *ptrs)
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) / nb * 1e6
+        by = batch_bytes(g, list(zip(firsts, pos)), width, k)
+        fl = block_flops(g, width, k, nseq)
+        res[f"B{nseq}"] = {
+            "blocks_per_s": round(nseq * 1e6 / us, 1), "us_per_batch": round(us, 1),
+            "algorithmic_bytes": int(by), "hbm_frac": round(by / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_flops": fl,
+            "mfma_frac": round(fl / (us * 1e-6) / 1e12 / F16_MFMA_PEAK_TFS, 4),
+        }
+        log(f"batch of {nseq}: {us:.1f} us a pass -> {nseq * 1e6 / us:.1f} blocks/s")
+        del out
+    for o in others:
+        o.close()
+    res["workload"] = ("27b_batch: B sequences on the 27B-shaped sidecar's shared weights, each "
+                       "over its own 32768-position context (the stream's, then synthetic "
+                       "stores), one dflash_block_batch pass drafting all B blocks (k=15, "
+                       "width=vocab); the weights are read once a pass")
+    return res
 
 
 def settle_flops(g, rows):

@@ -61,6 +61,9 @@ _SIGS = {
                       C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
     "dflash_block_noalloc": ([C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
                               C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
+    "dflash_create_context": ([C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p], C.c_int),
+    "dflash_block_batch": ([C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                            C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
     "dflash_queue": ([C.c_void_p, C.c_int64, C.c_int32, C.c_void_p], C.c_int),
     "dflash_flush": ([C.c_void_p], C.c_int),
     "dflash_reserve": ([C.c_void_p, C.c_int64], C.c_int),
@@ -129,6 +132,27 @@ def dflash_block(h, anchor, a, k, width, logits, cand, unary, score, chosen):
 
 def dflash_block_noalloc(h, anchor, a, k, width, logits, cand, unary, score, chosen):
     return lib().dflash_block_noalloc(h, anchor, a, k, width, logits, cand, unary, score, chosen)
+
+
+def dflash_create_context(model, max_context, stream, out_p):
+    return lib().dflash_create_context(model, max_context, stream, out_p)
+
+
+def dflash_block_batch(hs_p, nseq, anchors_p, a_p, k, width, logits, cand, unary, score, chosen):
+    return lib().dflash_block_batch(hs_p, nseq, anchors_p, a_p, k, width, logits, cand, unary,
+                                    score, chosen)
+
+
+def block_batch(drafters, anchors, a, k, width, logits_ptr, cand_ptr, unary_ptr, score_ptr,
+                chosen_ptr):
+    """dflash_block_batch over Drafter handles that share weights (the first
+    leads); outputs are sequence-major device buffers."""
+    n = len(drafters)
+    hs = (C.c_void_p * n)(*[x.h.value for x in drafters])
+    an = (C.c_int32 * n)(*[int(x) for x in anchors])
+    ap = (C.c_int64 * n)(*[int(x) for x in a])
+    _check(lib().dflash_block_batch(hs, n, an, ap, k, width, logits_ptr, cand_ptr, unary_ptr,
+                                    score_ptr, chosen_ptr), drafters[0].h)
 
 
 def dflash_queue(h, first_pos, n, taps):
@@ -213,6 +237,18 @@ class Drafter:
         _check(rc, None)
         self.h = h
         del keep
+
+    @classmethod
+    def context_of(cls, model: "Drafter", max_context: int, stream: int = 0) -> "Drafter":
+        """A handle sharing `model`'s weights with a context of its own
+        (dflash_create_context)."""
+        self = cls.__new__(cls)
+        self.g = model.g
+        self.h = None
+        h = C.c_void_p()
+        _check(lib().dflash_create_context(model.h, int(max_context), stream, C.byref(h)), None)
+        self.h = h
+        return self
 
     def close(self):
         if self.h:

@@ -13,7 +13,8 @@ LIB = os.path.join(HERE, "libdflash.so")
 # VGPRs (their results are rescaled in VALU at once)
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 SOURCES = [("kernels.hip", []), ("skinny.hip", VGPR_FORM), ("stream.hip", VGPR_FORM),
-           ("attention.hip", VGPR_FORM), ("settle.hip", VGPR_FORM), ("dflash.cpp", [])]
+           ("attention.hip", VGPR_FORM), ("settle.hip", VGPR_FORM), ("batch.hip", VGPR_FORM),
+           ("dflash.cpp", [])]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

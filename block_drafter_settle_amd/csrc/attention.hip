@@ -23,14 +23,17 @@ namespace dfl {
 // term lying below f32 rounding. The softmax runs in base 2 (scores times
 // log2 e, exp2 as one v_exp_f32). Writes the chunk's (max, sum, O) for the
 // merge, the max in base-2 units.
+// Batched blocks: blockIdx.z = nzq·s + z for sequence s, whose call is
+// seqs.s[s] (its own store, range and chunking); its queries at
+// qa + s·nh·16·hd, its block rows' keys and values at kb, vb + s·16·kd,
+// its chunk states at pacc, pml + s·nh·(kAttnMaxChunks + 1)·16·(hd, 1).
+// A chunk index past the sequence's own chunks leaves at once.
 template <int HD>
 __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, long qps,
-                                                   const float* __restrict__ sk,
-                                                   const float* __restrict__ sv, long cap,
-                                                   long s0, const float* __restrict__ kb,
+                                                   AttnSeqs seqs, int nzq,
+                                                   const float* __restrict__ kb,
                                                    const float* __restrict__ vb, int B, int nh,
-                                                   int kv, int n, long lo_pos, long a, int window,
-                                                   int chunk, int nchunks, float scale,
+                                                   int kv, int window, float scale,
                                                    float* __restrict__ pacc,
                                                    float2* __restrict__ pml) {
   constexpr int KST = HD + 8;   // LDS row stride of K (halfs)
@@ -42,11 +45,23 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
   __shared__ f16 Vt[2][HD * VST];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = blockIdx.x, g = blockIdx.y;
+  const int sq = blockIdx.z / nzq;
+  const AttnSeq& cs = seqs.s[sq];
+  const int n = cs.n, chunk = cs.chunk, nchunks = cs.nchunks;
+  if (c > nchunks) return;  // whole workgroup
+  const float* __restrict__ sk = cs.sk;
+  const float* __restrict__ sv = cs.sv;
+  const long cap = cs.cap, s0 = cs.s0, lo_pos = cs.lo, a = cs.a;
   const int rep = nh / kv;
-  const int qi = blockIdx.z * 4 + wave;
+  const int qi = (blockIdx.z % nzq) * 4 + wave;
   const bool active = qi < rep;
   const int hq = g * rep + min(qi, rep - 1);
   const int kd = kv * HD;
+  qa += (size_t)sq * nh * 16 * HD;
+  kb += (size_t)sq * 16 * kd;
+  vb += (size_t)sq * 16 * kd;
+  pacc += (size_t)sq * nh * (kAttnMaxChunks + 1) * 16 * HD;
+  pml += (size_t)sq * nh * (kAttnMaxChunks + 1) * 16;
   const bool blk = c == nchunks;
   const int k_first = blk ? 0 : c * chunk;
   const int count = blk ? B : min(chunk, n - k_first);
@@ -230,10 +245,15 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
 // one thread per dimension sums.
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pacc,
                                                     const float2* __restrict__ pml, int nh,
-                                                    int kv, int hd, int nchunks,
+                                                    int kv, int hd, SeqChunks sc,
                                                     f16* __restrict__ ya, long ps) {
   __shared__ float fw[kAttnMaxChunks + 1], red[4], redl[4];
   const int hq = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
+  // sequence sq (blockIdx.z): its chunk states and its A-layout block of y
+  const int sq = blockIdx.z, nchunks = sc.n[sq];
+  pacc += (size_t)sq * nh * (kAttnMaxChunks + 1) * 16 * hd;
+  pml += (size_t)sq * nh * (kAttnMaxChunks + 1) * 16;
+  ya += (size_t)sq * 16 * nh * hd;
   const int lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
   const int rep = nh / kv, g = hq / rep, qi = hq % rep, nc = nchunks + 1;
   const size_t slot0 = (size_t)g * nc * rep + qi;  // chunk c is slot slot0 + c·rep
@@ -275,29 +295,32 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 
 static inline unsigned cdiv(long a, long b) { return (unsigned)((a + b - 1) / b); }
 
-void attention(hipStream_t st, const uint16_t* qa, long qps, const float* sk, const float* sv,
-               long cap, long s0, const float* kb, const float* vb, int B, int nh, int kv,
-               int hd, int n, long lo_pos, long a, int window, int chunk, int nchunks,
+void attention(hipStream_t st, const uint16_t* qa, long qps, const AttnSeqs& seqs, int nseq,
+               const float* kb, const float* vb, int B, int nh, int kv, int hd, int window,
                float scale, float* pacc, float* pml) {
-  const int rep = nh / kv;
-  dim3 grid(nchunks + 1, kv, cdiv(rep, 4));
+  const int rep = nh / kv, nzq = cdiv(rep, 4);
+  int maxc = 0;
+  for (int i = 0; i < nseq; ++i) maxc = std::max(maxc, seqs.s[i].nchunks);
+  dim3 grid(maxc + 1, kv, nzq * nseq);
   const f16* q = reinterpret_cast<const f16*>(qa);
   float2* ml = reinterpret_cast<float2*>(pml);
   if (hd == 64)
-    k_attn<64><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, cap, s0, kb, vb, B, nh, kv, n, lo_pos,
-                                           a, window, chunk, nchunks, scale, pacc, ml);
+    k_attn<64><<<grid, kThreads, 0, st>>>(q, qps, seqs, nzq, kb, vb, B, nh, kv, window, scale,
+                                           pacc, ml);
   else if (hd == 128)
-    k_attn<128><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, cap, s0, kb, vb, B, nh, kv, n, lo_pos,
-                                            a, window, chunk, nchunks, scale, pacc, ml);
+    k_attn<128><<<grid, kThreads, 0, st>>>(q, qps, seqs, nzq, kb, vb, B, nh, kv, window, scale,
+                                            pacc, ml);
   else
-    k_attn<256><<<grid, kThreads, 0, st>>>(q, qps, sk, sv, cap, s0, kb, vb, B, nh, kv, n, lo_pos,
-                                            a, window, chunk, nchunks, scale, pacc, ml);
+    k_attn<256><<<grid, kThreads, 0, st>>>(q, qps, seqs, nzq, kb, vb, B, nh, kv, window, scale,
+                                            pacc, ml);
 }
 
 void attn_merge(hipStream_t st, const float* pacc, const float* pml, int nh, int kv, int hd,
-                int nchunks, int B, uint16_t* ya, long ps) {
-  dim3 grid(nh, B);
-  k_attn_merge<<<grid, hd, 0, st>>>(pacc, reinterpret_cast<const float2*>(pml), nh, kv, hd, nchunks,
+                const AttnSeqs& seqs, int nseq, int B, uint16_t* ya, long ps) {
+  dim3 grid(nh, B, nseq);
+  SeqChunks sc{};
+  for (int i = 0; i < nseq; ++i) sc.n[i] = seqs.s[i].nchunks;
+  k_attn_merge<<<grid, hd, 0, st>>>(pacc, reinterpret_cast<const float2*>(pml), nh, kv, hd, sc,
                                     reinterpret_cast<f16*>(ya), ps);
 }
 

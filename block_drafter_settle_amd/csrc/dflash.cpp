@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstring>
 #include <functional>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <thread>
@@ -75,6 +76,18 @@ Split split_big(int ntiles, int steps) {
   int per = (int)((steps + S - 1) / S);
   per += per & 1;
   return {(int)((steps + per - 1) / per), per};
+}
+
+// K splits of a batched product (16 weight tiles a workgroup): as many
+// workgroups as run at once without a second round (two a compute unit at
+// 4 row blocks, one at 8: their LDS), at most 8 splits (each split writes
+// a whole [rows][N] partial).
+Split split_mb(int ntiles, int units, int MB) {
+  const long groups = dfl::mb_groups(ntiles);
+  const long slots = MB == 4 ? 512 : 256;
+  const long S = std::max(1L, std::min<long>(std::min<long>(8, units), slots / groups));
+  const int per = (int)((units + S - 1) / S);
+  return {(units + per - 1) / per, per};
 }
 
 void parallel_for(long n, const std::function<void(long)>& f) {
@@ -151,6 +164,28 @@ struct I4Set {  // one int4 product of every layer, tiles [layer][tiles][K/128]
   long layer_tiles() const { return tiles; }
 };
 
+// The device weights, shared by every handle made from them (a handle and
+// the contexts made from it with dflash_create_context); freed with the last.
+struct WeightOwner {
+  std::vector<void*> allocs;
+  ~WeightOwner() {
+    for (void* p : allocs) (void)hipFree(p);
+  }
+};
+
+// Scratch of batched blocks (dflash_block_batch), the lead handle's, sized
+// for dfl::kMaxSeq sequences (8 A-layout row blocks) at its first batched
+// call.
+struct BatchScratch {
+  float *h = nullptr, *dsum_a = nullptr, *dsum_m = nullptr, *kb = nullptr, *vb = nullptr,
+        *pacc = nullptr, *pml = nullptr, *part = nullptr, *logits = nullptr, *hp = nullptr,
+        *sqp = nullptr;
+  uint16_t *xa = nullptr, *xca = nullptr, *qa = nullptr, *ya = nullptr, *ma = nullptr;
+  dfl::SelectScratch sel[dfl::kMaxSeq]{};
+  long part_floats = 0;
+  bool ready = false;
+};
+
 struct dflash {
   // geometry
   int hs, ffn, L, nh, kv, hd, V, B, mask, gs, kn, rank, top, ntaps, tw, qd, kd, G, P;
@@ -192,7 +227,10 @@ struct dflash {
   int stage_cols = 0;  // widest activation the staging buffer holds
   int last_k = 0;
   float* trace = nullptr;  // per-layer residual copies (debug)
-  std::vector<void*> allocs;
+  std::vector<void*> allocs;     // the handle's own device buffers (not the weights)
+  std::shared_ptr<WeightOwner> wown;
+  BatchScratch bb;
+  hipEvent_t order = nullptr;  // orders a batched call against this handle's stream
   std::string err;
   struct Timing {
     bool on = false;
@@ -677,12 +715,89 @@ void dflash_destroy(dflash_t* d) {
   if (!d) return;
   (void)hipStreamSynchronize(d->st);
   for (hipEvent_t e : d->tm.ev) (void)hipEventDestroy(e);
+  if (d->order) (void)hipEventDestroy(d->order);
   for (void* p : d->allocs) (void)hipFree(p);
   for (auto& l : d->ls) {
     if (l.k) (void)hipFree(l.k);
     if (l.v) (void)hipFree(l.v);
   }
   delete d;
+}
+
+// Everything a handle owns beyond the weights: its context stores, the
+// waiting rows' ring and the scratch of both passes. Errors go to the
+// create error (the handle is not out yet).
+static int alloc_state(dflash* d) {
+  int rc = DFLASH_OK;
+  const int L = d->L, hs = d->hs;
+  // ---- context: a windowed layer's ring of min(2·window, max_context) rows
+  // now; a full layer's store grows as rows come (`Dev::reserve`); the
+  // waiting rows' ring
+  d->ls.resize(L);
+  for (int l = 0; l < L && !rc; ++l) {
+    auto& S = d->ls[l];
+    const long w = d->windows[l];
+    S.limit = w > 0 ? std::min(2 * w, d->maxctx) : d->maxctx;
+    if (w > 0) {
+      const size_t bytes = (size_t)S.limit * d->kd * sizeof(float);
+      if (hipMalloc(&S.k, bytes) != hipSuccess || hipMalloc(&S.v, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        rc = fail(nullptr, DFLASH_ENOMEM, "device memory for layer %d's context (%zu bytes)", l,
+                  2 * bytes);
+      }
+      S.cap = S.limit;
+    }
+  }
+  if (!rc) rc = dev_alloc(d, &d->tab, L, "context table");
+  if (!rc) rc = upload_tab(d, nullptr);
+  d->pcap = kPendingRows;
+  if (std::all_of(d->windows.begin(), d->windows.end(), [](int w) { return w > 0; }))
+    d->pcap = std::max(kPendingRows,
+                       (long)*std::max_element(d->windows.begin(), d->windows.end()) + kBlockSlack);
+  if (!rc) rc = dev_alloc(d, &d->pq, (size_t)d->pcap * d->tw, "waiting rows");
+  // ---- scratch
+  const int rep = d->nh / d->kv;
+  const size_t slots = (size_t)d->kv * (dfl::kAttnMaxChunks + 1) * rep;
+  d->part_floats = partial_need(d);
+  const size_t sel_cap = (size_t)dfl::topk_cap(d->V, d->top);
+  BlockScratch& b = d->bs;
+  if (!rc) rc = dev_alloc(d, &b.h, 16 * hs, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.x, 16 * hs, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.dsum_a, 16 * d->P, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.dsum_m, 16 * d->P, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.kb, 16 * d->kd, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.vb, 16 * d->kd, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.pacc, slots * 16 * d->hd, "attention partials");
+  if (!rc) rc = dev_alloc(d, &b.pml, slots * 16 * 2, "attention partials");
+  if (!rc) rc = dev_alloc(d, &d->part, d->part_floats, "GEMM partials");
+  b.part = d->part;
+  if (!rc) rc = dev_alloc(d, &b.logits, (size_t)16 * d->V, "logits");
+  if (!rc) rc = dev_alloc(d, &b.hp, 16 * d->rank, "selector projection");
+  if (!rc) rc = dev_alloc(d, &b.sel.gmax, (size_t)16 * ((d->V + 255) / 256), "selection");
+  if (!rc) rc = dev_alloc(d, &b.sel.counters, 16, "selection");
+  if (!rc) rc = dev_alloc(d, &b.sel.lv, 16 * sel_cap, "selection candidates");
+  if (!rc) rc = dev_alloc(d, &b.sel.li, 16 * sel_cap, "selection candidates");
+  // the block's activation operands, two planes each
+  if (!rc) rc = dev_alloc(d, &b.xa, 2 * 16 * hs, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.xca, 2 * 16 * hs, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.qa, 2 * (size_t)d->nh * 16 * d->hd, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.ya, 2 * 16 * d->qd, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.ma, 2 * 16 * d->ffn, "scratch");
+  d->stage_cols = std::max(std::max(d->tw, d->ffn), std::max(d->qd, hs));
+  // the settle's operands, two planes of 256 rows each
+  if (!rc) rc = dev_alloc(d, &d->taps_a, 2 * (size_t)kSettleRows * d->stage_cols, "settle scratch");
+  if (!rc) rc = dev_alloc(d, &d->t_a, 2 * (size_t)kSettleRows * hs, "settle scratch");
+  if (!rc)
+    rc = dev_alloc(d, &d->sqp,
+                   (size_t)std::max(kSettleRows * dfl::row_chunks(hs), 16 * dfl::conv1_chunks(hs)),
+                   "norm scratch");
+  b.sqp = d->sqp;
+  if (!rc) rc = dev_alloc(d, &b.sel.tab, (size_t)d->top * (1 + 15 * d->top), "selector table");
+  if (!rc) rc = dev_alloc(d, &b.sel.best, (size_t)(1 + 15 * d->top), "selector table");
+  if (!rc) rc = hip_check(nullptr, hipDeviceSynchronize(), "create");
+  if (!rc) rc = hip_check(nullptr, hipGetDevice(&d->dev), "create: current device");
+  if (!rc) scratch_init(d->dev);
+  return rc;
 }
 
 int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* stream,
@@ -792,73 +907,13 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
     rc = upload(d, &d->inv, inv.data(), inv.size(), "rotary frequencies");
   }
   if (!rc) rc = upload(d, &d->rot_dev, d->rot.data(), d->rot.size(), "rotary flags");
-  // ---- context: a windowed layer's ring of min(2·window, max_context) rows
-  // now; a full layer's store grows as rows come (`Dev::reserve`); the
-  // waiting rows' ring
-  d->ls.resize(L);
-  for (int l = 0; l < L && !rc; ++l) {
-    auto& S = d->ls[l];
-    const long w = d->windows[l];
-    S.limit = w > 0 ? std::min(2 * w, d->maxctx) : d->maxctx;
-    if (w > 0) {
-      const size_t bytes = (size_t)S.limit * d->kd * sizeof(float);
-      if (hipMalloc(&S.k, bytes) != hipSuccess || hipMalloc(&S.v, bytes) != hipSuccess) {
-        (void)hipGetLastError();
-        rc = fail(nullptr, DFLASH_ENOMEM, "device memory for layer %d's context (%zu bytes)", l,
-                  2 * bytes);
-      }
-      S.cap = S.limit;
-    }
+  // the weights are shared by every handle made from this one
+  // (dflash_create_context): they move to their own owner
+  if (!rc) {
+    d->wown = std::make_shared<WeightOwner>();
+    d->wown->allocs.swap(d->allocs);
   }
-  if (!rc) rc = dev_alloc(d, &d->tab, L, "context table");
-  if (!rc) rc = upload_tab(d, nullptr);
-  d->pcap = kPendingRows;
-  if (std::all_of(d->windows.begin(), d->windows.end(), [](int w) { return w > 0; }))
-    d->pcap = std::max(kPendingRows,
-                       (long)*std::max_element(d->windows.begin(), d->windows.end()) + kBlockSlack);
-  if (!rc) rc = dev_alloc(d, &d->pq, (size_t)d->pcap * d->tw, "waiting rows");
-  // ---- scratch
-  const int rep = d->nh / d->kv;
-  const size_t slots = (size_t)d->kv * (dfl::kAttnMaxChunks + 1) * rep;
-  d->part_floats = partial_need(d);
-  const size_t sel_cap = (size_t)dfl::topk_cap(d->V, d->top);
-  BlockScratch& b = d->bs;
-  if (!rc) rc = dev_alloc(d, &b.h, 16 * hs, "scratch");
-  if (!rc) rc = dev_alloc(d, &b.x, 16 * hs, "scratch");
-  if (!rc) rc = dev_alloc(d, &b.dsum_a, 16 * d->P, "scratch");
-  if (!rc) rc = dev_alloc(d, &b.dsum_m, 16 * d->P, "scratch");
-  if (!rc) rc = dev_alloc(d, &b.kb, 16 * d->kd, "scratch");
-  if (!rc) rc = dev_alloc(d, &b.vb, 16 * d->kd, "scratch");
-  if (!rc) rc = dev_alloc(d, &b.pacc, slots * 16 * d->hd, "attention partials");
-  if (!rc) rc = dev_alloc(d, &b.pml, slots * 16 * 2, "attention partials");
-  if (!rc) rc = dev_alloc(d, &d->part, d->part_floats, "GEMM partials");
-  b.part = d->part;
-  if (!rc) rc = dev_alloc(d, &b.logits, (size_t)16 * d->V, "logits");
-  if (!rc) rc = dev_alloc(d, &b.hp, 16 * d->rank, "selector projection");
-  if (!rc) rc = dev_alloc(d, &b.sel.gmax, (size_t)16 * ((d->V + 255) / 256), "selection");
-  if (!rc) rc = dev_alloc(d, &b.sel.counters, 16, "selection");
-  if (!rc) rc = dev_alloc(d, &b.sel.lv, 16 * sel_cap, "selection candidates");
-  if (!rc) rc = dev_alloc(d, &b.sel.li, 16 * sel_cap, "selection candidates");
-  // the block's activation operands, two planes each
-  if (!rc) rc = dev_alloc(d, &b.xa, 2 * 16 * hs, "scratch");
-  if (!rc) rc = dev_alloc(d, &b.xca, 2 * 16 * hs, "scratch");
-  if (!rc) rc = dev_alloc(d, &b.qa, 2 * (size_t)d->nh * 16 * d->hd, "scratch");
-  if (!rc) rc = dev_alloc(d, &b.ya, 2 * 16 * d->qd, "scratch");
-  if (!rc) rc = dev_alloc(d, &b.ma, 2 * 16 * d->ffn, "scratch");
-  d->stage_cols = std::max(std::max(d->tw, d->ffn), std::max(d->qd, hs));
-  // the settle's operands, two planes of 256 rows each
-  if (!rc) rc = dev_alloc(d, &d->taps_a, 2 * (size_t)kSettleRows * d->stage_cols, "settle scratch");
-  if (!rc) rc = dev_alloc(d, &d->t_a, 2 * (size_t)kSettleRows * hs, "settle scratch");
-  if (!rc)
-    rc = dev_alloc(d, &d->sqp,
-                   (size_t)std::max(kSettleRows * dfl::row_chunks(hs), 16 * dfl::conv1_chunks(hs)),
-                   "norm scratch");
-  b.sqp = d->sqp;
-  if (!rc) rc = dev_alloc(d, &b.sel.tab, (size_t)d->top * (1 + 15 * d->top), "selector table");
-  if (!rc) rc = dev_alloc(d, &b.sel.best, (size_t)(1 + 15 * d->top), "selector table");
-  if (!rc) rc = hip_check(nullptr, hipDeviceSynchronize(), "create");
-  if (!rc) rc = hip_check(nullptr, hipGetDevice(&d->dev), "create: current device");
-  if (!rc) scratch_init(d->dev);
+  if (!rc) rc = alloc_state(d);
   return done(rc);
 }
 
@@ -1179,7 +1234,9 @@ static int block_pass(dflash* d, const BlockScratch& b, int32_t anchor, int64_t 
   // Each sub-layer's rms is folded into its neighbours: the producer of h
   // (embed, conv1) writes h, its partial sums of squares and h ⊙ gain as the
   // kernel projection's input; conv0 applies the per-row scale.
-  dfl::embed(st, d->embed, anchor, d->mask, B, hs, b.h, b.sqp, d->in_norm, b.xa, psh);
+  const int anchors[1] = {anchor};
+  const long apos[1] = {(long)a};
+  dfl::embed(st, d->embed, anchors, 1, d->mask, B, hs, b.h, b.sqp, d->in_norm, b.xa, psh);
   tm_mark(d, DFLASH_ST_CONV);
   int nch = dfl::row_chunks(hs);  // sums of squares per row: embed's, then conv1's
   for (int l = 0; l < d->L; ++l) {
@@ -1199,7 +1256,8 @@ static int block_pass(dflash* d, const BlockScratch& b, int32_t anchor, int64_t 
                        sqk.per, b.part, ssq);
     tm_mark(d, DFLASH_ST_QKV);
     dfl::qkv_post(st, b.part, sqk.S, ssq, B, d->nh, d->kv, d->hd, d->q_norm + (size_t)l * d->hd,
-                  d->k_norm + (size_t)l * d->hd, d->inv, a, d->rot[l], d->eps, b.qa, psq, b.kb, b.vb);
+                  d->k_norm + (size_t)l * d->hd, d->inv, apos, 1, d->rot[l], d->eps, b.qa, psq,
+                  b.kb, b.vb);
     tm_mark(d, DFLASH_ST_QKPOST);
     // attention over the layer's context range and the block's rows
     long lo, n;
@@ -1207,11 +1265,13 @@ static int block_pass(dflash* d, const BlockScratch& b, int32_t anchor, int64_t 
     int nchunks = 0;
     const int chunk = attn_chunk(n, &nchunks);
     const auto& S = d->ls[l];
-    const long s0 = S.cap ? (lo - d->first) % S.cap : 0;
-    dfl::attention(st, b.qa, psq, S.k, S.v, S.cap, s0, b.kb, b.vb, B, d->nh, d->kv, d->hd, (int)n,
-                   lo, a, d->windows[l], chunk, nchunks, scale, b.pacc, b.pml);
+    dfl::AttnSeqs as{};
+    as.s[0] = {S.k, S.v, S.cap, S.cap ? (lo - d->first) % S.cap : 0, lo, (long)a, (int)n, chunk,
+               nchunks};
+    dfl::attention(st, b.qa, psq, as, 1, b.kb, b.vb, B, d->nh, d->kv, d->hd, d->windows[l], scale,
+                   b.pacc, b.pml);
     tm_mark(d, DFLASH_ST_ATTN);
-    dfl::attn_merge(st, b.pacc, b.pml, d->nh, d->kv, d->hd, nchunks, B, b.ya, psy);
+    dfl::attn_merge(st, b.pacc, b.pml, d->nh, d->kv, d->hd, as, 1, B, b.ya, psy);
     tm_mark(d, DFLASH_ST_ATTN);
     // o, conv_out into the residual (and the MLP norm's input)
     dfl::gemm_i4_block(st, b.ya, psy, d->qd, d->o.codes + i4l_o * 1024 * l,
@@ -1291,6 +1351,285 @@ int dflash_block_noalloc(dflash_t* d, int32_t anchor, int64_t a, int32_t k, int3
   BlockScratch b;
   carve_block_scratch(d, static_cast<uint8_t*>(base), &b);
   return block_pass(d, b, anchor, a, k, width, logits, cand, unary, score, chosen);
+}
+
+// ------------------------------------------------------- batched blocks
+
+int dflash_create_context(const dflash_t* model, int64_t max_context, void* stream,
+                          dflash_t** out) {
+  if (!out) return fail(nullptr, DFLASH_EINVAL, "null output handle");
+  *out = nullptr;
+  g_create_error.clear();
+  if (!model) return fail(nullptr, DFLASH_EINVAL, "create_context: null model handle");
+  if (max_context < 1) return fail(nullptr, DFLASH_EINVAL, "create_context: max_context must be >= 1");
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != model->dev)
+    return fail(nullptr, DFLASH_EINVAL, "create_context: the model's device (%d) must be current",
+                model->dev);
+  // the geometry and the weights (shared), then a state of its own
+  dflash* d = new dflash(*model);
+  d->allocs.clear();
+  d->ls.clear();
+  d->tab = nullptr;
+  d->pq = nullptr;
+  d->pcap = d->phead = d->pend = 0;
+  d->first = d->len = 0;
+  d->bs = BlockScratch{};
+  d->part = d->sqp = nullptr;
+  d->taps_a = d->t_a = nullptr;
+  d->part_floats = 0;
+  d->stage_cols = 0;
+  d->last_k = 0;
+  d->trace = nullptr;
+  d->bb = BatchScratch{};
+  d->order = nullptr;
+  d->err.clear();
+  d->tm = dflash::Timing{};
+  d->st = static_cast<hipStream_t>(stream);
+  d->maxctx = max_context;
+  const int rc = alloc_state(d);
+  if (rc) {
+    if (g_create_error.empty()) g_create_error = "create_context failed";
+    dflash_destroy(d);
+    return rc;
+  }
+  *out = d;
+  return DFLASH_OK;
+}
+
+// The lead handle's batch scratch, for up to dfl::kMaxSeq sequences.
+static int batch_scratch(dflash* d) {
+  BatchScratch& b = d->bb;
+  if (b.ready) return DFLASH_OK;
+  const size_t R = 16 * dfl::kMaxSeq, hs = d->hs;
+  const size_t slots = (size_t)dfl::kMaxSeq * d->nh * (dfl::kAttnMaxChunks + 1);
+  // the largest split partial of any batched product
+  long part = 0;
+  auto f16p = [&](int N, int K) {
+    const Split s = split_mb((N + 15) / 16, K / 32, 4);
+    part = std::max(part, (long)s.S * (long)R * N);
+  };
+  auto i4p = [&](int N, int K) {
+    const Split s = split_mb(N / 16, K / 128, 4);
+    part = std::max(part, (long)s.S * (long)R * N);
+  };
+  f16p(d->P, d->hs);
+  f16p(d->rank, d->hs);
+  i4p(d->qd + 2 * d->kd, d->hs);
+  i4p(d->hs, d->qd);
+  i4p(2 * d->ffn, d->hs);
+  i4p(d->hs, d->ffn);
+  b.part_floats = part;
+  const size_t sel_cap = (size_t)dfl::topk_cap(d->V, d->top);
+  int rc = DFLASH_OK;
+  auto take = [&](auto** p, size_t count, const char* what) {
+    if (!rc) rc = dev_alloc(d, p, count, what);
+  };
+  take(&b.h, R * hs, "batch scratch");
+  take(&b.sqp, R * (size_t)std::max(dfl::row_chunks(d->hs), dfl::conv1_chunks(d->hs)), "batch scratch");
+  take(&b.dsum_a, R * d->P, "batch scratch");
+  take(&b.dsum_m, R * d->P, "batch scratch");
+  take(&b.kb, R * d->kd, "batch scratch");
+  take(&b.vb, R * d->kd, "batch scratch");
+  take(&b.pacc, slots * 16 * d->hd, "batch attention partials");
+  take(&b.pml, slots * 16 * 2, "batch attention partials");
+  take(&b.part, (size_t)part, "batch partials");
+  take(&b.logits, R * d->V, "batch logits");
+  take(&b.hp, R * d->rank, "batch selector projection");
+  take(&b.xa, 2 * R * hs, "batch scratch");
+  take(&b.xca, 2 * R * hs, "batch scratch");
+  take(&b.qa, 2 * R * d->qd, "batch scratch");
+  take(&b.ya, 2 * R * d->qd, "batch scratch");
+  take(&b.ma, 2 * R * d->ffn, "batch scratch");
+  for (int s = 0; s < dfl::kMaxSeq; ++s) {
+    auto& sc = b.sel[s];
+    take(&sc.gmax, (size_t)16 * ((d->V + 255) / 256), "batch selection");
+    take(&sc.counters, 16, "batch selection");
+    take(&sc.lv, 16 * sel_cap, "batch selection");
+    take(&sc.li, 16 * sel_cap, "batch selection");
+    take(&sc.tab, (size_t)d->top * (1 + 15 * d->top), "batch selection");
+    take(&sc.best, (size_t)(1 + 15 * d->top), "batch selection");
+  }
+  if (rc) return fail(d, rc, "block_batch: %s", g_create_error.c_str());
+  b.ready = true;
+  return DFLASH_OK;
+}
+
+// The batched pass on the lead's stream and scratch (arguments checked).
+static int block_batch_pass(dflash* const* ds, int nseq, const int32_t* anchors,
+                            const int64_t* apos, int32_t k, int32_t width, float* logits,
+                            int32_t* cand, float* unary, float* score, int32_t* chosen) {
+  dflash* d = ds[0];
+  BatchScratch& b = d->bb;
+  hipStream_t st = d->st;
+  const int MB = nseq <= 4 ? 4 : 8, R = 16 * MB;
+  const int hs = d->hs, B = d->B;
+  const float scale = std::pow((float)d->hd, -0.5f);
+  const long psh = (long)R * hs, psq = (long)R * d->qd, psm = (long)R * d->ffn;
+  const size_t kp_layer = (size_t)d->ptiles * 16 * hs;
+  const size_t i4l_qkv = (size_t)d->qkv.tiles * (hs / 128);
+  const size_t i4l_o = (size_t)d->o.tiles * (d->qd / 128);
+  const size_t i4l_gu = (size_t)d->gu.tiles * (hs / 128);
+  const size_t i4l_dn = (size_t)d->down.tiles * (d->ffn / 128);
+  const int nc1 = dfl::conv1_chunks(hs);
+  int anc[dfl::kMaxSeq];
+  long pos[dfl::kMaxSeq];
+  for (int s = 0; s < nseq; ++s) {
+    anc[s] = anchors[s];
+    pos[s] = (long)apos[s];
+  }
+  const Split skp = split_mb(d->ptiles, hs / 32, MB);
+  const Split sqk = split_mb(d->qkv.tiles, hs / 128, MB);
+  const Split so = split_mb(d->o.tiles, d->qd / 128, MB);
+  const Split sgu = split_mb(d->gu.tiles, hs / 128, MB);
+  const Split sdn = split_mb(d->down.tiles, d->ffn / 128, MB);
+  const long ssd = (long)R * d->P, ssq = (long)R * (d->qd + 2 * d->kd), ssh = (long)R * hs,
+             ssg = (long)R * 2 * d->ffn;
+  const dfl::TileMap kpmap{d->ptiles, d->ptiles, 0, 0};
+
+  tm_begin(d);
+  dfl::embed(st, d->embed, anc, nseq, d->mask, B, hs, b.h, b.sqp, d->in_norm, b.xa, psh);
+  tm_mark(d, DFLASH_ST_CONV);
+  int nch = dfl::row_chunks(hs);
+  for (int l = 0; l < d->L; ++l) {
+    const float* ab = d->attn_base + (size_t)l * 2 * d->kn * hs;
+    const float* mbase = d->mlp_base + (size_t)l * 2 * d->kn * hs;
+    const float* post = d->post_norm + (size_t)l * hs;
+    dfl::gemm_mb_f16(st, b.xa, psh, hs, MB, nseq, d->attn_kproj + l * kp_layer, kpmap, d->P,
+                     skp.S, skp.per, b.part, ssd);
+    tm_mark(d, DFLASH_ST_KPROJ);
+    dfl::conv0(st, b.h, b.sqp, nch, d->in_norm + (size_t)l * hs, d->eps, b.part, skp.S, ssd, ab, B,
+               hs, d->gs, d->kn, b.xca, psh, b.dsum_a, nseq);
+    tm_mark(d, DFLASH_ST_CONV);
+    dfl::gemm_mb_i4(st, b.xca, psh, hs, MB, nseq, d->qkv.codes + i4l_qkv * 1024 * l,
+                    d->qkv.scales + i4l_qkv * 64 * l,
+                    dfl::TileMap{d->qkv.tiles, d->qkv.tiles, 0, 0}, d->qd + 2 * d->kd, sqk.S,
+                    sqk.per, b.part, ssq);
+    tm_mark(d, DFLASH_ST_QKV);
+    dfl::qkv_post(st, b.part, sqk.S, ssq, B, d->nh, d->kv, d->hd, d->q_norm + (size_t)l * d->hd,
+                  d->k_norm + (size_t)l * d->hd, d->inv, pos, nseq, d->rot[l], d->eps, b.qa, psq,
+                  b.kb, b.vb);
+    tm_mark(d, DFLASH_ST_QKPOST);
+    // each sequence's own context range of this layer, in its own store
+    dfl::AttnSeqs as{};
+    for (int s = 0; s < nseq; ++s) {
+      const dflash* e = ds[s];
+      long lo, n;
+      layer_range(e, l, pos[s], &lo, &n);
+      int nchunks = 0;
+      const int chunk = attn_chunk(n, &nchunks);
+      const auto& S = e->ls[l];
+      as.s[s] = {S.k, S.v, S.cap, S.cap ? (lo - e->first) % S.cap : 0, lo, pos[s], (int)n, chunk,
+                 nchunks};
+    }
+    dfl::attention(st, b.qa, psq, as, nseq, b.kb, b.vb, B, d->nh, d->kv, d->hd, d->windows[l],
+                   scale, b.pacc, b.pml);
+    dfl::attn_merge(st, b.pacc, b.pml, d->nh, d->kv, d->hd, as, nseq, B, b.ya, psq);
+    tm_mark(d, DFLASH_ST_ATTN);
+    dfl::gemm_mb_i4(st, b.ya, psq, d->qd, MB, nseq, d->o.codes + i4l_o * 1024 * l,
+                    d->o.scales + i4l_o * 64 * l, dfl::TileMap{d->o.tiles, d->o.tiles, 0, 0}, hs,
+                    so.S, so.per, b.part, ssh);
+    tm_mark(d, DFLASH_ST_O);
+    dfl::conv1(st, b.h, b.part, so.S, ssh, b.dsum_a, ab, B, hs, d->gs, d->kn, b.sqp, post, b.xa,
+               psh, nseq);
+    nch = nc1;
+    tm_mark(d, DFLASH_ST_CONV);
+    dfl::gemm_mb_f16(st, b.xa, psh, hs, MB, nseq, d->mlp_kproj + l * kp_layer, kpmap, d->P, skp.S,
+                     skp.per, b.part, ssd);
+    tm_mark(d, DFLASH_ST_KPROJ);
+    dfl::conv0(st, b.h, b.sqp, nch, post, d->eps, b.part, skp.S, ssd, mbase, B, hs, d->gs, d->kn,
+               b.xca, psh, b.dsum_m, nseq);
+    tm_mark(d, DFLASH_ST_CONV);
+    dfl::gemm_mb_i4(st, b.xca, psh, hs, MB, nseq, d->gu.codes + i4l_gu * 1024 * l,
+                    d->gu.scales + i4l_gu * 64 * l, dfl::TileMap{d->gu.tiles, d->gu.tiles, 0, 0},
+                    2 * d->ffn, sgu.S, sgu.per, b.part, ssg);
+    dfl::glu_act(st, b.part, sgu.S, ssg, B, nseq, d->ffn, b.ma, psm);
+    tm_mark(d, DFLASH_ST_GLU);
+    dfl::gemm_mb_i4(st, b.ma, psm, d->ffn, MB, nseq, d->down.codes + i4l_dn * 1024 * l,
+                    d->down.scales + i4l_dn * 64 * l,
+                    dfl::TileMap{d->down.tiles, d->down.tiles, 0, 0}, hs, sdn.S, sdn.per, b.part,
+                    ssh);
+    tm_mark(d, DFLASH_ST_DOWN);
+    const float* next = l + 1 < d->L ? d->in_norm + (size_t)(l + 1) * hs : nullptr;
+    dfl::conv1(st, b.h, b.part, sdn.S, ssh, b.dsum_m, mbase, B, hs, d->gs, d->kn, b.sqp, next,
+               b.xa, psh, nseq);
+    tm_mark(d, DFLASH_ST_CONV);
+  }
+  dfl::norm_apply(st, b.h, b.sqp, nc1, B, hs, d->norm, d->eps, nullptr, b.xa, psh, nseq);
+  tm_mark(d, DFLASH_ST_CONV);
+  // the head over every row of every block, then the selector projection
+  const int wtiles = (width + 15) / 16, stiles = (d->rank + 15) / 16;
+  dfl::gemm_mb_f16(st, b.xa, psh, hs, MB, nseq, d->head, dfl::TileMap{wtiles, wtiles, 0, 0}, width,
+                   1, hs / 32, b.logits, (long)R * width);
+  const Split ssel = split_mb(stiles, hs / 32, MB);
+  dfl::gemm_mb_f16(st, b.xa, psh, hs, MB, nseq, d->sel, dfl::TileMap{stiles, stiles, 0, 0},
+                   d->rank, ssel.S, ssel.per, b.part, (long)R * d->rank);
+  dfl::sum_rows(st, b.part, ssel.S, (long)R * d->rank, R, d->rank, b.hp);
+  tm_mark(d, DFLASH_ST_HEAD);
+  // each sequence's selection on its rows 1..k
+  for (int s = 0; s < nseq; ++s) {
+    const float* lg = b.logits + (size_t)(16 * s + 1) * width;
+    const size_t co = (size_t)s * k * d->top;
+    dfl::select_all(st, lg, false, k, width, d->top, b.hp + (size_t)(16 * s + 1) * d->rank,
+                    d->rank, d->pbook, d->cbook, d->V, anc[s], nullptr, b.sel[s], cand + co,
+                    unary + co, score + co, chosen + (size_t)s * k);
+    if (logits)
+      (void)hipMemcpyAsync(logits + (size_t)s * k * width, lg, sizeof(float) * k * width,
+                           hipMemcpyDeviceToDevice, st);
+  }
+  tm_mark(d, DFLASH_ST_SELECT);
+  const int rc = launch_check(d, "block_batch");
+  tm_end(d);
+  d->tm.blocks += d->tm.on;
+  return rc;
+}
+
+int dflash_block_batch(dflash_t* const* ds, int32_t nseq, const int32_t* anchors,
+                       const int64_t* a, int32_t k, int32_t width, float* logits, int32_t* cand,
+                       float* unary, float* score, int32_t* chosen) {
+  if (!ds || !ds[0]) return DFLASH_EINVAL;
+  dflash* d = ds[0];
+  if (nseq < 1 || nseq > dfl::kMaxSeq)
+    return fail(d, DFLASH_EINVAL, "block_batch: nseq must be in [1, %d]", dfl::kMaxSeq);
+  if (!anchors || !a) return fail(d, DFLASH_EINVAL, "block_batch: null anchors or positions");
+  if (int rc = block_args(d, anchors[0], a[0], k, width, cand, unary, score, chosen)) return rc;
+  for (int s = 1; s < nseq; ++s) {
+    const dflash* e = ds[s];
+    if (!e) return fail(d, DFLASH_EINVAL, "block_batch: null handle %d", s);
+    if (e->wown != d->wown)
+      return fail(d, DFLASH_EINVAL, "block_batch: handle %d does not share the lead's weights", s);
+    if (e->pend)
+      return fail(d, DFLASH_EINVAL, "block_batch: handle %d has rows waiting (dflash_flush first)",
+                  s);
+    if (anchors[s] < 0 || anchors[s] >= d->V)
+      return fail(d, DFLASH_EINVAL, "block_batch: anchor %d outside the vocabulary", s);
+    if (a[s] < 0) return fail(d, DFLASH_EINVAL, "block_batch: a must be >= 0");
+  }
+  if (int rc = batch_scratch(d)) return rc;
+  // the other handles' streams: the batch waits for what they enqueued,
+  // and they wait for the batch
+  for (int s = 1; s < nseq; ++s) {
+    dflash* e = ds[s];
+    if (e->st == d->st) continue;
+    if (!e->order && hip_check(e, hipEventCreateWithFlags(&e->order, hipEventDisableTiming),
+                               "block_batch: event"))
+      return fail(d, DFLASH_EHIP, "block_batch: %s", e->err.c_str());
+    if (hipEventRecord(e->order, e->st) != hipSuccess ||
+        hipStreamWaitEvent(d->st, e->order, 0) != hipSuccess)
+      return fail(d, DFLASH_EHIP, "block_batch: ordering against handle %d's stream", s);
+  }
+  const int rc = block_batch_pass(ds, nseq, anchors, a, k, width, logits, cand, unary, score,
+                                  chosen);
+  if (rc) return rc;
+  if (!d->order && hip_check(d, hipEventCreateWithFlags(&d->order, hipEventDisableTiming),
+                             "block_batch: event"))
+    return DFLASH_EHIP;
+  if (hipEventRecord(d->order, d->st) != hipSuccess)
+    return fail(d, DFLASH_EHIP, "block_batch: recording the batch's end");
+  for (int s = 1; s < nseq; ++s)
+    if (ds[s]->st != d->st && hipStreamWaitEvent(ds[s]->st, d->order, 0) != hipSuccess)
+      return fail(d, DFLASH_EHIP, "block_batch: ordering handle %d's stream after the batch", s);
+  return DFLASH_OK;
 }
 
 // --------------------------------------------------------------- debug

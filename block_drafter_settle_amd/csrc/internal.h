@@ -131,22 +131,36 @@ int conv1_chunks(int hs);
 // row_chunks(hs) per row).
 void rowsum_sq(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,
                const float* w, uint16_t* xa, long ps, float* sqp);
+// The block kernels below take `nseq` sequences' blocks at once (batched
+// blocks): sequence s owns rows 16s..16s+15 of every row-major buffer
+// (its `rows` block rows first), A-layout block s of every operand, and
+// qa + s·nh·16·hd of the attention's queries.
+constexpr int kMaxSeq = 8;
+struct SeqTok {
+  int t[kMaxSeq];
+};
+struct SeqPos {
+  long a[kMaxSeq];
+};
 void norm_apply(hipStream_t st, const float* h, const float* sqp, int nchunk, int rows, int N,
-                const float* w, float eps, float* x, uint16_t* xa, long ps);
+                const float* w, float eps, float* x, uint16_t* xa, long ps, int nseq = 1);
 // embed and conv1 also write u = h ⊙ w (w: the next norm's gain; conv1
 // skips it for w == nullptr) as A-layout planes, the next kernel
 // projection's input; conv0 applies that norm's per-row scale from sqp.
-void embed(hipStream_t st, const uint16_t* emb, int anchor, int mask, int rows, int hs, float* h,
-           float* sqp, const float* w, uint16_t* xa, long ps);
+// anchors: host [nseq].
+void embed(hipStream_t st, const uint16_t* emb, const int* anchors, int nseq, int mask, int rows,
+           int hs, float* h, float* sqp, const float* w, uint16_t* xa, long ps);
 void conv0(hipStream_t st, const float* h, const float* sqp, int nchunk, const float* w, float eps,
            const float* dpart, int splits, long split_stride, const float* base, int rows, int hs,
-           int gs, int kn, uint16_t* xca, long ps, float* dsum);
+           int gs, int kn, uint16_t* xca, long ps, float* dsum, int nseq = 1);
 void conv1(hipStream_t st, float* h, const float* opart, int splits, long split_stride,
            const float* dsum, const float* base, int rows, int hs, int gs, int kn, float* sqp,
-           const float* w, uint16_t* xa, long ps);
+           const float* w, uint16_t* xa, long ps, int nseq = 1);
+// pos: host [nseq], each sequence's block position a
 void qkv_post(hipStream_t st, const float* part, int splits, long split_stride, int rows, int nh,
               int kv, int hd, const float* q_norm, const float* k_norm, const float* inv_freq,
-              long pos0, int rot, float eps, uint16_t* qa, long qps, float* kb, float* vb);
+              const long* pos, int nseq, int rot, float eps, uint16_t* qa, long qps, float* kb,
+              float* vb);
 // A layer's context store: a ring of cap rows of [kv_heads][head_dim] f32
 // keys and values; position p sits at row (p − first) mod cap.
 struct StoreSlot {
@@ -164,14 +178,28 @@ void settle_kv(hipStream_t st, const float* part, int splits, long split_stride,
 // Context chunks per kv head of one attention call; the merge holds one
 // weight per chunk (and one for the block's own rows) in LDS.
 constexpr int kAttnMaxChunks = 64;
-// sk, sv: the layer's ring of cap rows; its n keys of positions lo_pos..
-// start at ring row s0 and wrap at most once.
-void attention(hipStream_t st, const uint16_t* qa, long qps, const float* sk, const float* sv,
-               long cap, long s0, const float* kb, const float* vb, int B, int nh, int kv,
-               int hd, int n, long lo_pos, long a, int window, int chunk, int nchunks,
+// One sequence's attention over a layer: sk, sv its ring of cap rows,
+// whose n keys of positions lo.. start at ring row s0 and wrap at most
+// once; a its block position; the keys in nchunks chunks of `chunk`.
+struct AttnSeq {
+  const float* sk;
+  const float* sv;
+  long cap, s0, lo, a;
+  int n, chunk, nchunks;
+};
+struct AttnSeqs {
+  AttnSeq s[kMaxSeq];
+};
+struct SeqChunks {
+  int n[kMaxSeq];
+};
+// pacc, pml: nseq·nh·(kAttnMaxChunks + 1)·16 chunk states (hd floats, and a
+// float pair, each)
+void attention(hipStream_t st, const uint16_t* qa, long qps, const AttnSeqs& seqs, int nseq,
+               const float* kb, const float* vb, int B, int nh, int kv, int hd, int window,
                float scale, float* pacc, float* pml);
 void attn_merge(hipStream_t st, const float* pacc, const float* pml, int nh, int kv, int hd,
-                int nchunks, int B, uint16_t* ya, long ps);
+                const AttnSeqs& seqs, int nseq, int B, uint16_t* ya, long ps);
 // Selection (`top_k` + `select_with`) on logits [k][width] and hp rows
 // [k][rank]: cand/unary, the score table and the chain (score, chosen).
 // have_gmax: the head kernel already wrote the column-group maxima.
@@ -181,6 +209,20 @@ void select_all(hipStream_t st, const float* logits, bool have_gmax, int k, int 
                 const float* hp, int rank, const uint16_t* pbook, const uint16_t* cbook,
                 int vocab, int anchor, const int* forced, SelectScratch sc, int* cand,
                 float* unary, float* score, int* chosen);
+// Batched blocks (batch.hip): products of MB·16 rows (MB = 4 or 8 A-layout
+// row blocks, the first `mblocks` written out) in splits of sps spans
+// (int4) or steps (f16), 16 weight tiles a workgroup; out as gemm_i4.
+int mb_groups(int ntiles);
+void gemm_mb_i4(hipStream_t st, const uint16_t* xa, long ps, int K, int MB, int mblocks,
+                const uint8_t* codes, const uint16_t* scales, TileMap map, int N, int splits,
+                int sps, float* out, long split_stride);
+void gemm_mb_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int MB, int mblocks,
+                 const uint16_t* w, TileMap map, int N, int splits, int sps, float* out,
+                 long split_stride);
+// silu(gate)·up of the split-summed batched gate/up product [rows of nseq
+// sequences][2·ffn] into the down projection's A-layout planes
+void glu_act(hipStream_t st, const float* part, int splits, long split_stride, int rows, int nseq,
+             int ffn, uint16_t* ma, long mps);
 void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,
                 int rows, int K, float* out);
 void sum_rows(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,

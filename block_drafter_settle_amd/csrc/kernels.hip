@@ -432,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_apply(const float* __restrict
                                                          float* __restrict__ x,
                                                          f16* __restrict__ xa, long ps) {
   __shared__ float red[4];
-  const int r = blockIdx.y, c = blockIdx.x, i = c * kChunk + threadIdx.x;
+  const int r = 16 * blockIdx.z + blockIdx.y, c = blockIdx.x, i = c * kChunk + threadIdx.x;
   float part = 0.f;
   for (int q = threadIdx.x; q < nchunk; q += kThreads) part += sqp[(size_t)r * nchunk + q];
   const float ss = block_sum(part, red);
@@ -447,21 +447,23 @@ __global__ __launch_bounds__(kThreads) void k_norm_apply(const float* __restrict
 // and u = h ⊙ w (w: the first norm's gain) as A-layout f16 planes: the
 // kernel projection takes u, and rms's per-row scale is applied to its
 // product afterwards (k_conv0), so no separate norm pass runs.
-__global__ __launch_bounds__(kThreads) void k_embed(const f16* __restrict__ embed, int anchor,
+__global__ __launch_bounds__(kThreads) void k_embed(const f16* __restrict__ embed, SeqTok tok,
                                                     int mask, int hs, float* __restrict__ h,
                                                     float* __restrict__ sqp, int nchunk,
                                                     const float* __restrict__ w,
                                                     f16* __restrict__ xa, long ps) {
   __shared__ float red[4];
-  const int r = blockIdx.y, c = blockIdx.x, i = c * kChunk + threadIdx.x;
+  // block row m of sequence s (its rows are 16s..16s+15, its A-layout block s)
+  const int m = blockIdx.y, sq = blockIdx.z, r = 16 * sq + m;
+  const int c = blockIdx.x, i = c * kChunk + threadIdx.x;
   float v = 0.f;
   if (i < hs) {
-    v = (float)embed[(size_t)(r == 0 ? anchor : mask) * hs + i];
+    v = (float)embed[(size_t)(m == 0 ? tok.t[sq] : mask) * hs + i];
     h[(size_t)r * hs + i] = v;
-    put_a(xa, ps, a_idx(r, i), v * w[i]);
+    put_a(xa, ps, (size_t)sq * 16 * hs + a_idx(m, i), v * w[i]);
   }
-  const float sq = block_sum(v * v, red);
-  if (threadIdx.x == 0) sqp[(size_t)r * nchunk + c] = sq;
+  const float ssq = block_sum(v * v, red);
+  if (threadIdx.x == 0) sqp[(size_t)r * nchunk + c] = ssq;
 }
 
 // Conv stage 0 (`conv`) of row r over a run of whole channel groups, with
@@ -483,10 +485,11 @@ __global__ __launch_bounds__(kThreads) void k_conv0(const float* __restrict__ h,
                                                     float* __restrict__ dsum) {
   extern __shared__ float dl[];  // [2·kn][ng]
   __shared__ float sc[16];       // s of rows r − o, o < taps (kn ≤ 16)
-  const int r = blockIdx.y;
+  // block row m of sequence sq: row r of every row-major buffer
+  const int m = blockIdx.y, sq = blockIdx.z, r = 16 * sq + m;
   const int G = hs / gs, P = 2 * kn * G;
   const int g0 = blockIdx.x * gpw, ng = min(G, g0 + gpw) - g0;
-  const int taps = min(kn, r + 1);
+  const int taps = min(kn, m + 1);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // wave o sums row r − o's partial sums of squares; every workgroup of a
   // row sums them in the same order, so all of them get the same scale. The
@@ -495,11 +498,11 @@ __global__ __launch_bounds__(kThreads) void k_conv0(const float* __restrict__ h,
   float q = 0.f;
   if (wave < taps) {
     // four loads in flight a round (hs/32 ≤ 256 partials take one round)
-    const float* sq = sqp + (size_t)(r - wave) * nchunk;
+    const float* sqr = sqp + (size_t)(r - wave) * nchunk;
     for (int c = lane; c < nchunk; c += 256) {
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = c + 64 * e < nchunk ? sq[c + 64 * e] : 0.f;
+      for (int e = 0; e < 4; ++e) v[e] = c + 64 * e < nchunk ? sqr[c + 64 * e] : 0.f;
       q += ((v[0] + v[1]) + v[2]) + v[3];
     }
   }
@@ -544,14 +547,14 @@ __global__ __launch_bounds__(kThreads) void k_conv0(const float* __restrict__ h,
       if (o < taps) acc += (bs[o] + dl[o * ng + g]) * (hx[o] * sc[o] * wi);
     for (int o = kPre; o < taps; ++o)
       acc += (base[(size_t)o * hs + i0] + dl[o * ng + g]) * (h[(size_t)(r - o) * hs + i0] * sc[o] * wi);
-    put_a(xca, ps, a_idx(r, i0), acc);
+    put_a(xca, ps, (size_t)sq * 16 * hs + a_idx(m, i0), acc);
   }
   for (int i = i0 + kThreads; i < iend; i += kThreads) {  // conv groups wider than a block
     const int g = i / gs - g0;
     float acc = 0.f;
     for (int o = 0; o < taps; ++o)
       acc += (base[(size_t)o * hs + i] + dl[o * ng + g]) * (h[(size_t)(r - o) * hs + i] * sc[o] * w[i]);
-    put_a(xca, ps, a_idx(r, i), acc);
+    put_a(xca, ps, (size_t)sq * 16 * hs + a_idx(m, i), acc);
   }
 }
 
@@ -574,10 +577,11 @@ __global__ __launch_bounds__(kC1 * 16) void k_conv1(float* __restrict__ h,
                                                     f16* __restrict__ xa, long ps) {
   constexpr int kPre = 4;  // taps whose coefficients are loaded ahead of the barrier
   __shared__ float v[16][kC1];
-  const int c = threadIdx.x % kC1, r = threadIdx.x / kC1;
+  // block row m of sequence sq (blockIdx.y): row r of every row-major buffer
+  const int c = threadIdx.x % kC1, m = threadIdx.x / kC1, sq = blockIdx.y, r = 16 * sq + m;
   const int i = blockIdx.x * kC1 + c;
-  const bool live = r < rows && i < hs;
-  const int G = hs / gs, P = 2 * kn * G, taps = min(kn, r + 1), g = i / gs;
+  const bool live = m < rows && i < hs;
+  const int G = hs / gs, P = 2 * kn * G, taps = min(kn, m + 1), g = i / gs;
   const float* b1 = base + (size_t)kn * hs;
   const float* d1 = dsum + (size_t)r * P + (size_t)kn * G;
   // this thread's tap coefficients, old h and gain, loaded together with the
@@ -590,24 +594,24 @@ __global__ __launch_bounds__(kC1 * 16) void k_conv1(float* __restrict__ h,
     hold = h[(size_t)r * hs + i];
     if (w) wi = w[i];
   }
-  v[r][c] = live ? sum_splits(opart + (size_t)r * hs + i, splits, ss) : 0.f;
+  v[m][c] = live ? sum_splits(opart + (size_t)r * hs + i, splits, ss) : 0.f;
   __syncthreads();
   float hn = 0.f;
   if (live) {
     float acc = 0.f;
 #pragma unroll
     for (int o = 0; o < kPre; ++o)
-      if (o < taps) acc += coef[o] * v[r - o][c];
-    for (int o = kPre; o < taps; ++o) acc += (b1[(size_t)o * hs + i] + d1[o * G + g]) * v[r - o][c];
+      if (o < taps) acc += coef[o] * v[m - o][c];
+    for (int o = kPre; o < taps; ++o) acc += (b1[(size_t)o * hs + i] + d1[o * G + g]) * v[m - o][c];
     hn = hold + acc;
     h[(size_t)r * hs + i] = hn;
-    if (w) put_a(xa, ps, a_idx(r, i), hn * wi);
+    if (w) put_a(xa, ps, (size_t)sq * 16 * hs + a_idx(m, i), hn * wi);
   }
   // Σh² over the kC1 channels of row r: the kC1 lanes that hold them
-  float sq = hn * hn;
+  float q2 = hn * hn;
 #pragma unroll
-  for (int o = kC1 / 2; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
-  if (c == 0 && r < rows) sqp[(size_t)r * nchunk + blockIdx.x] = sq;
+  for (int o = kC1 / 2; o > 0; o >>= 1) q2 += __shfl_xor(q2, o, 64);
+  if (c == 0 && m < rows) sqp[(size_t)r * nchunk + blockIdx.x] = q2;
 }
 
 // One head of one row: split-summed values at columns col0 + i and
@@ -667,23 +671,25 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ part,
                                                  long ss, int nh, int kv, int hd,
                                                  const float* __restrict__ qn,
                                                  const float* __restrict__ kn,
-                                                 const float* __restrict__ inv, long pos0,
+                                                 const float* __restrict__ inv, SeqPos pos,
                                                  int rot, float eps, f16* __restrict__ qa,
                                                  long qps, float* __restrict__ kb,
                                                  float* __restrict__ vb) {
-  const int r = blockIdx.x, hh = blockIdx.y;
+  // block row m of sequence sq (rows 16sq.. of part, kb, vb; its q heads at
+  // qa + sq·nh·16·hd), at position a_sq + m
+  const int m = blockIdx.x, hh = blockIdx.y, sq = blockIdx.z, r = 16 * sq + m;
   const int qd = nh * hd, kd = kv * hd, N = qd + 2 * kd, half = hd >> 1;
   const int col0 = hh < nh ? hh * hd : (hh < nh + kv ? qd + (hh - nh) * hd : qd + kd + (hh - nh - kv) * hd);
   Pairs p = load_pairs(part, splits, ss, (long)r * N + col0, half);
-  if (hh < nh + kv) norm_rope(p, hd, hh < nh ? qn : kn, eps, inv, pos0 + r, rot);
+  if (hh < nh + kv) norm_rope(p, hd, hh < nh ? qn : kn, eps, inv, pos.a[sq] + m, rot);
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int i = threadIdx.x + 64 * c;
     if (i >= half) continue;
     if (hh < nh) {
-      f16* q = qa + (size_t)hh * 16 * hd;
-      put_a(q, qps, a_idx(r, i), p.lo[c]);
-      put_a(q, qps, a_idx(r, i + half), p.hi[c]);
+      f16* q = qa + ((size_t)sq * nh + hh) * 16 * hd;
+      put_a(q, qps, a_idx(m, i), p.lo[c]);
+      put_a(q, qps, a_idx(m, i + half), p.hi[c]);
     } else {
       float* dst = hh < nh + kv ? kb + (size_t)r * kd + (hh - nh) * hd
                                 : vb + (size_t)r * kd + (hh - nh - kv) * hd;
@@ -1331,41 +1337,46 @@ int row_chunks(int N) { return cdiv(N, kChunk); }
 int conv1_chunks(int hs) { return cdiv(hs, kC1); }
 
 void norm_apply(hipStream_t st, const float* h, const float* sqp, int nchunk, int rows, int N,
-                const float* w, float eps, float* x, uint16_t* xa, long ps) {
-  k_norm_apply<<<dim3(cdiv(N, kChunk), rows), kThreads, 0, st>>>(h, sqp, nchunk, N, w, eps, x,
-                                                                 reinterpret_cast<f16*>(xa), ps);
+                const float* w, float eps, float* x, uint16_t* xa, long ps, int nseq) {
+  k_norm_apply<<<dim3(cdiv(N, kChunk), rows, nseq), kThreads, 0, st>>>(
+      h, sqp, nchunk, N, w, eps, x, reinterpret_cast<f16*>(xa), ps);
 }
 
-void embed(hipStream_t st, const uint16_t* emb, int anchor, int mask, int rows, int hs, float* h,
-           float* sqp, const float* w, uint16_t* xa, long ps) {
+void embed(hipStream_t st, const uint16_t* emb, const int* anchors, int nseq, int mask, int rows,
+           int hs, float* h, float* sqp, const float* w, uint16_t* xa, long ps) {
   const int nch = cdiv(hs, kChunk);
-  k_embed<<<dim3(nch, rows), kThreads, 0, st>>>(reinterpret_cast<const f16*>(emb), anchor, mask,
-                                                hs, h, sqp, nch, w, reinterpret_cast<f16*>(xa), ps);
+  SeqTok tok{};
+  for (int i = 0; i < nseq; ++i) tok.t[i] = anchors[i];
+  k_embed<<<dim3(nch, rows, nseq), kThreads, 0, st>>>(reinterpret_cast<const f16*>(emb), tok,
+                                                      mask, hs, h, sqp, nch, w,
+                                                      reinterpret_cast<f16*>(xa), ps);
 }
 
 void conv0(hipStream_t st, const float* h, const float* sqp, int nchunk, const float* w, float eps,
            const float* dpart, int splits, long ss, const float* base, int rows, int hs, int gs,
-           int kn, uint16_t* xca, long ps, float* dsum) {
+           int kn, uint16_t* xca, long ps, float* dsum, int nseq) {
   const int G = hs / gs, gpw = std::max(1, kChunk / gs);
   const size_t lds = sizeof(float) * 2 * kn * gpw;
-  k_conv0<<<dim3(cdiv(G, gpw), rows), kThreads, lds, st>>>(h, sqp, nchunk, w, eps, dpart, splits,
-                                                          ss, base, hs, gs, kn, gpw,
-                                                          reinterpret_cast<f16*>(xca), ps, dsum);
+  k_conv0<<<dim3(cdiv(G, gpw), rows, nseq), kThreads, lds, st>>>(
+      h, sqp, nchunk, w, eps, dpart, splits, ss, base, hs, gs, kn, gpw,
+      reinterpret_cast<f16*>(xca), ps, dsum);
 }
 
 void conv1(hipStream_t st, float* h, const float* opart, int splits, long ss, const float* dsum,
            const float* base, int rows, int hs, int gs, int kn, float* sqp, const float* w,
-           uint16_t* xa, long ps) {
+           uint16_t* xa, long ps, int nseq) {
   const int nch = conv1_chunks(hs);
-  k_conv1<<<nch, kC1 * 16, 0, st>>>(h, opart, splits, ss, dsum, base, rows, hs, gs, kn, sqp, nch,
-                                    w, reinterpret_cast<f16*>(xa), ps);
+  k_conv1<<<dim3(nch, nseq), kC1 * 16, 0, st>>>(h, opart, splits, ss, dsum, base, rows, hs, gs, kn,
+                                                sqp, nch, w, reinterpret_cast<f16*>(xa), ps);
 }
 
 void qkv_post(hipStream_t st, const float* part, int splits, long ss, int rows, int nh, int kv,
-              int hd, const float* q_norm, const float* k_norm, const float* inv, long pos0,
-              int rot, float eps, uint16_t* qa, long qps, float* kb, float* vb) {
-  dim3 grid(rows, nh + 2 * kv);
-  k_qkv_post<<<grid, 64, 0, st>>>(part, splits, ss, nh, kv, hd, q_norm, k_norm, inv, pos0, rot, eps,
+              int hd, const float* q_norm, const float* k_norm, const float* inv, const long* pos,
+              int nseq, int rot, float eps, uint16_t* qa, long qps, float* kb, float* vb) {
+  dim3 grid(rows, nh + 2 * kv, nseq);
+  SeqPos sp{};
+  for (int i = 0; i < nseq; ++i) sp.a[i] = pos[i];
+  k_qkv_post<<<grid, 64, 0, st>>>(part, splits, ss, nh, kv, hd, q_norm, k_norm, inv, sp, rot, eps,
                                   reinterpret_cast<f16*>(qa), qps, kb, vb);
 }
 

@@ -194,6 +194,36 @@ int dflash_block_noalloc(dflash_t* d, int32_t anchor_token, int64_t a, int32_t k
                          float* logits, int32_t* cand, float* unary, float* score,
                          int32_t* chosen);
 
+/* ---- batched blocks ------------------------------------------------------ */
+
+/* A handle on the same weights as `model` (device memory shared, not copied)
+   with a context of its own: one per sequence for dflash_block_batch. Same
+   geometry except max_context; `stream` as in dflash_create. The model's
+   device must be current. Weights live until the last handle that shares
+   them is destroyed. On failure *out is NULL and dflash_last_error(NULL)
+   has the message. */
+int dflash_create_context(const dflash_t* model, int64_t max_context, void* stream,
+                          dflash_t** out);
+
+/* The block pass of dflash_block for nseq (1..8) handles that share weights
+   at once, each over its own context: the rows of all their blocks go
+   through every weight matrix together (16 rows a sequence, padded to 4 or
+   8 sequences), so each weight is read once for the batch (the pages'
+   narrow/wide split: `mm` and `many` take a block's few rows on one kernel
+   and many rows on another). d: host [nseq] handles, d[0] the lead (its
+   stream runs the batch; the others' streams are ordered before and after
+   it by events); anchors, a: host [nseq]. k and width as dflash_block, for
+   every sequence. Outputs, dev, sequence-major: logits [nseq][k][width]
+   (NULL: not written; copied from the batch's own buffer), cand, unary,
+   score [nseq][k][selector_top], chosen [nseq][k]. Results equal
+   dflash_block's on each handle to the parity tolerance (sums run in
+   another order). The lead allocates its batch scratch at the first call.
+   DFLASH_EINVAL for arguments dflash_block rejects, a handle that does not
+   share the lead's weights, or rows waiting on any handle. */
+int dflash_block_batch(dflash_t* const* d, int32_t nseq, const int32_t* anchors, const int64_t* a,
+                       int32_t k, int32_t width, float* logits, int32_t* cand, float* unary,
+                       float* score, int32_t* chosen);
+
 /* Forget the context from position pos on (`truncate`), waiting rows
    included; a layer that had dropped rows past pos holds none. */
 int dflash_truncate(dflash_t* d, int64_t pos);
