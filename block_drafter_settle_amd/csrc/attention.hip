@@ -11,7 +11,9 @@
 
 namespace dfl {
 
-// Split-context attention (`Drafter::block`'s inner loop). Block (c, g, z):
+// Split-context attention (`Drafter::block`'s inner loop). Block (g, c, z)
+// (kv heads fastest: the workgroups that run together read all kv heads of
+// the same context rows, whole rows of the store):
 // kv head g, its q heads 4z..4z+3, and key chunk c — context keys
 // [c·chunk, min(n, (c+1)·chunk)) of the layer's range, or for c == nchunks
 // the block's own B keys. The context keys sit in the layer's ring of cap
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
   __shared__ f16 Ks[2][32 * KST];
   __shared__ f16 Vt[2][HD * VST];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = blockIdx.x, g = blockIdx.y;
+  const int g = blockIdx.x, c = blockIdx.y;
   const int sq = blockIdx.z / nzq;
   const AttnSeq& cs = seqs.s[sq];
   const int n = cs.n, chunk = cs.chunk, nchunks = cs.nchunks;
@@ -301,7 +303,7 @@ void attention(hipStream_t st, const uint16_t* qa, long qps, const AttnSeqs& seq
   const int rep = nh / kv, nzq = cdiv(rep, 4);
   int maxc = 0;
   for (int i = 0; i < nseq; ++i) maxc = std::max(maxc, seqs.s[i].nchunks);
-  dim3 grid(maxc + 1, kv, nzq * nseq);
+  dim3 grid(kv, maxc + 1, nzq * nseq);
   const f16* q = reinterpret_cast<const f16*>(qa);
   float2* ml = reinterpret_cast<float2*>(pml);
   if (hd == 64)
