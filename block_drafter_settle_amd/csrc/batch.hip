@@ -25,11 +25,14 @@ namespace dfl {
 static constexpr int kMbWaves = 8, kMbNT = 16, kMbStages = 3, kMbAhead = kMbStages - 1;
 
 // int4 weights (I4T tiles): the tiles' codes and scales of every 128-column
-// span go to LDS too (a double buffer, one span ahead: the settle's
-// many-row K/V kernel's scheme; wave w copies tiles 2w, 2w + 1). Each step
-// is one scale group: t = a_hi·q + a_lo·q on the exact integer codes, then
-// acc += s·t in f32. Copies past the split's end repeat its last step or
-// span (same data into a slot no step still reads).
+// span go to LDS too (a double buffer, one span ahead; wave w copies tiles
+// 2w, 2w + 1), and each wave reads its four tiles' codes and scales of a
+// span into registers once. Each step is one scale group: t = a_hi·q +
+// a_lo·q on the exact integer codes, then acc += s·t in f32. A step holds
+// few products, so the row fragments run four steps ahead in a five-stage
+// ring (copies from L2 take longer than two steps). Copies past the
+// split's end repeat its last step or span (same data into a slot no step
+// still reads).
 // (The bodies are device templates behind one plain kernel per MB: a
 // kernel template whose body holds these copy builtins gets no host stub.)
 template <int MB>
@@ -41,8 +44,9 @@ __device__ __forceinline__ void mb_i4(const f16* __restrict__ xa, long ps, int K
   constexpr int CA = 2 * MB / kMbWaves;  // row-fragment copies a wave a step
   constexpr int CC = 3;                  // code and scale copies a wave a span
   static_assert(CA >= 1 && 2 * MB % kMbWaves == 0, "every wave copies as many row fragments");
-  static_assert(kMbAhead == 2, "the waits below count two steps of row fragments in flight");
-  __shared__ h8 ast[kMbStages][2][MB][64];
+  constexpr int ST = 5, AH = ST - 1;  // row-fragment ring stages, steps ahead
+  static_assert(AH == 4, "the waits below count four steps of row fragments in flight");
+  __shared__ h8 ast[ST][2][MB][64];
   __shared__ uint4 cst[2][kMbNT][64];
   __shared__ uint32_t sst[2][kMbNT][32];
   const int lane = threadIdx.x & 63;
@@ -73,7 +77,7 @@ __device__ __forceinline__ void mb_i4(const f16* __restrict__ xa, long ps, int K
     for (int i = 0; i < CA; ++i) {
       const int f = wave * CA + i;
       __builtin_amdgcn_global_load_lds(asrc[i] + (size_t)sc * 64,
-                                       &ast[s % kMbStages][f / MB][f % MB][0], 16, 0, 0);
+                                       &ast[s % ST][f / MB][f % MB][0], 16, 0, 0);
     }
   };
   auto issue_c = [&](int p) {
@@ -91,34 +95,44 @@ __device__ __forceinline__ void mb_i4(const f16* __restrict__ xa, long ps, int K
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[b][t] = (f4){0.f, 0.f, 0.f, 0.f};
   issue_c(p0);
-  issue_a(4 * p0);
-  issue_a(4 * p0 + 1);
+#pragma unroll
+  for (int i = 0; i < AH; ++i) issue_a(4 * p0 + i);
   const int n = lane & 15;
-  const uint32_t* cw32 = reinterpret_cast<const uint32_t*>(&cst[0][0][0]);
+  uint4 cw[4];
+  uint2 sw[4];
   for (int p = p0; p < p1; ++p) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int s = 4 * p + u;
-      // this wave's copies of step s (and, at u = 0, of span p) are in; the
-      // ones issued after them may remain (step s + 1's, and at u = 1, 2
-      // also the next span's codes and scales, issued at u = 0)
-      if (u == 0 || u == 3)
-        wait_vm<CA>();
+      // Issue order: span p0's codes, the row fragments of steps 4p0 ..
+      // 4p0 + 3, then for every step t those of t + 4 and, when t starts
+      // span q, the codes of span q + 1. Once this wave's copies of step s
+      // and of span p are in, what was issued after them may remain: three
+      // steps of row fragments, plus (past a span's first step) the next
+      // span's codes.
+      if (u == 0)
+        wait_vm<3 * CA>();
       else
-        wait_vm<CA + CC>();
+        wait_vm<3 * CA + CC>();
       lds_barrier();
-      issue_a(s + kMbAhead);
-      if (u == 0) issue_c(p + 1);
+      issue_a(s + AH);
+      if (u == 0) {
+        issue_c(p + 1);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          cw[t] = cst[p & 1][4 * tg + t][lane];
+          sw[t] = *reinterpret_cast<const uint2*>(&sst[p & 1][4 * tg + t][2 * n]);
+        }
+      }
       h8 q[4];
       float sc[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int tile = 4 * tg + t;
-        q[t] = unpack_i4(cw32[(((size_t)(p & 1) * kMbNT + tile) * 64 + lane) * 4 + u]);
-        const uint32_t sb = sst[p & 1][tile][2 * n + (u >> 1)];
+        q[t] = unpack_i4(u == 0 ? cw[t].x : u == 1 ? cw[t].y : u == 2 ? cw[t].z : cw[t].w);
+        const uint32_t sb = u < 2 ? sw[t].x : sw[t].y;
         sc[t] = half_bits((u & 1) ? (sb >> 16) : sb);
       }
-      const int st = s % kMbStages;
+      const int st = s % ST;
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
         const h8 a0 = ast[st][0][rg * RB + b][lane];
