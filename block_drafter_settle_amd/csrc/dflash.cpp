@@ -181,7 +181,7 @@ struct BatchScratch {
         *pacc = nullptr, *pml = nullptr, *part = nullptr, *logits = nullptr, *hp = nullptr,
         *sqp = nullptr;
   uint16_t *xa = nullptr, *xca = nullptr, *qa = nullptr, *ya = nullptr, *ma = nullptr;
-  dfl::SelectScratch sel[dfl::kMaxSeq]{};
+  dfl::SelectScratch sel{};  // kMaxSeq sets (select_batch)
   long part_floats = 0;
   bool ready = false;
 };
@@ -1441,15 +1441,13 @@ static int batch_scratch(dflash* d) {
   take(&b.qa, 2 * R * d->qd, "batch scratch");
   take(&b.ya, 2 * R * d->qd, "batch scratch");
   take(&b.ma, 2 * R * d->ffn, "batch scratch");
-  for (int s = 0; s < dfl::kMaxSeq; ++s) {
-    auto& sc = b.sel[s];
-    take(&sc.gmax, (size_t)16 * ((d->V + 255) / 256), "batch selection");
-    take(&sc.counters, 16, "batch selection");
-    take(&sc.lv, 16 * sel_cap, "batch selection");
-    take(&sc.li, 16 * sel_cap, "batch selection");
-    take(&sc.tab, (size_t)d->top * (1 + 15 * d->top), "batch selection");
-    take(&sc.best, (size_t)(1 + 15 * d->top), "batch selection");
-  }
+  const size_t S = dfl::kMaxSeq;
+  take(&b.sel.gmax, S * 16 * ((d->V + 255) / 256), "batch selection");
+  take(&b.sel.counters, S * 16, "batch selection");
+  take(&b.sel.lv, S * 16 * sel_cap, "batch selection");
+  take(&b.sel.li, S * 16 * sel_cap, "batch selection");
+  take(&b.sel.tab, S * d->top * (1 + 15 * d->top), "batch selection");
+  take(&b.sel.best, S * (1 + 15 * d->top), "batch selection");
   if (rc) return fail(d, rc, "block_batch: %s", g_create_error.c_str());
   b.ready = true;
   return DFLASH_OK;
@@ -1566,17 +1564,14 @@ static int block_batch_pass(dflash* const* ds, int nseq, const int32_t* anchors,
                    d->rank, ssel.S, ssel.per, b.part, (long)R * d->rank);
   dfl::sum_rows(st, b.part, ssel.S, (long)R * d->rank, R, d->rank, b.hp);
   tm_mark(d, DFLASH_ST_HEAD);
-  // each sequence's selection on its rows 1..k
-  for (int s = 0; s < nseq; ++s) {
-    const float* lg = b.logits + (size_t)(16 * s + 1) * width;
-    const size_t co = (size_t)s * k * d->top;
-    dfl::select_all(st, lg, false, k, width, d->top, b.hp + (size_t)(16 * s + 1) * d->rank,
-                    d->rank, d->pbook, d->cbook, d->V, anc[s], nullptr, b.sel[s], cand + co,
-                    unary + co, score + co, chosen + (size_t)s * k);
-    if (logits)
-      (void)hipMemcpyAsync(logits + (size_t)s * k * width, lg, sizeof(float) * k * width,
+  // every sequence's selection on its rows 1..k, in one set of launches
+  dfl::select_batch(st, nseq, b.logits + width, 16L * width, false, k, width, d->top,
+                    b.hp + d->rank, 16L * d->rank, d->rank, d->pbook, d->cbook, d->V, anc,
+                    nullptr, b.sel, cand, unary, score, chosen);
+  if (logits)
+    (void)hipMemcpy2DAsync(logits, sizeof(float) * k * width, b.logits + width,
+                           sizeof(float) * 16 * width, sizeof(float) * k * width, nseq,
                            hipMemcpyDeviceToDevice, st);
-  }
   tm_mark(d, DFLASH_ST_SELECT);
   const int rc = launch_check(d, "block_batch");
   tm_end(d);

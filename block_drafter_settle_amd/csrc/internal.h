@@ -209,6 +209,17 @@ void select_all(hipStream_t st, const float* logits, bool have_gmax, int k, int 
                 const float* hp, int rank, const uint16_t* pbook, const uint16_t* cbook,
                 int vocab, int anchor, const int* forced, SelectScratch sc, int* cand,
                 float* unary, float* score, int* chosen);
+// nseq sequences' selections at once (batched blocks): sequence s's logits
+// rows at logits + s·lseq, its projections at hp + s·hseq, its anchor
+// anchors[s] (host), scratch set s of sc (sized for nseq sets: 16·ceil(
+// width/256) maxima, 16 counters, 16·topk_cap lists, top·(1 + 15·top)
+// table entries and 1 + 15·top best indices a set), outputs at s·k·top
+// (cand, unary, score) and s·k (chosen). No forced chain when nseq > 1.
+void select_batch(hipStream_t st, int nseq, const float* logits, long lseq, bool have_gmax, int k,
+                  int width, int top, const float* hp, long hseq, int rank,
+                  const uint16_t* pbook, const uint16_t* cbook, int vocab, const int* anchors,
+                  const int* forced, SelectScratch sc, int* cand, float* unary, float* score,
+                  int* chosen);
 // Batched blocks (batch.hip): products of MB·16 rows (MB = 4 or 8 A-layout
 // row blocks, the first `mblocks` written out) in splits of sps spans
 // (int4) or steps (f16), 16 weight tiles a workgroup; out as gemm_i4.

@@ -817,9 +817,13 @@ static constexpr int kSliceVPL = 32;  // a collect wave covers 64·32 = 2048 col
 // logits do not come from the head kernel); block (0, 0) clears the counters.
 __global__ __launch_bounds__(kThreads) void k_rowmax(const float* __restrict__ logits, int width,
                                                      int ngroups, float* __restrict__ gmax,
-                                                     int* __restrict__ counters) {
+                                                     int* __restrict__ counters, long lseq) {
   __shared__ float red[4];
   const int g = blockIdx.x, j = blockIdx.y, c = g * 256 + threadIdx.x;
+  // sequence blockIdx.z of a batched selection: its logits and its scratch
+  logits += blockIdx.z * lseq;
+  gmax += (size_t)blockIdx.z * 16 * ngroups;
+  counters += blockIdx.z * 16;
   float v = c < width ? logits[(size_t)j * width + c] : -INFINITY;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -916,8 +920,13 @@ __global__ __launch_bounds__(kThreads) void k_collect(const float* __restrict__ 
                                                       const float* __restrict__ gmax, int ngroups,
                                                       int* __restrict__ counters,
                                                       float* __restrict__ lv, int* __restrict__ li,
-                                                      int cap) {
+                                                      int cap, long lseq) {
   const int lane = threadIdx.x & 63, j = blockIdx.y;
+  logits += blockIdx.z * lseq;
+  gmax += (size_t)blockIdx.z * 16 * ngroups;
+  counters += blockIdx.z * 16;
+  lv += (size_t)blockIdx.z * 16 * cap;
+  li += (size_t)blockIdx.z * 16 * cap;
   const int sl = blockIdx.x * 4 + (threadIdx.x >> 6);
   // every workgroup of row j finds the same T (the whole block, before any
   // wave leaves)
@@ -1041,7 +1050,8 @@ __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
                                                const int* __restrict__ counters, int cap, int top,
                                                const float* __restrict__ hp, int rank,
                                                const f16* __restrict__ pbook,
-                                               const f16* __restrict__ cbook, int vocab, int anchor,
+                                               const f16* __restrict__ cbook, int vocab,
+                                               SeqTok anchors, long hseq,
                                                const int* __restrict__ forced,
                                                int* __restrict__ cand, float* __restrict__ unary,
                                                float* __restrict__ tab, int* __restrict__ best) {
@@ -1050,6 +1060,17 @@ __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
   __shared__ float sv[2][kRankMax];
   __shared__ int si[2][kRankMax];
   const int j = blockIdx.x, tp = blockIdx.y, tpn = gridDim.y;
+  // sequence sq of a batched selection: its lists, projections, table and
+  // outputs
+  const int sq = blockIdx.z, k = gridDim.x, anchor = anchors.t[sq];
+  lv += (size_t)sq * 16 * cap;
+  li += (size_t)sq * 16 * cap;
+  counters += sq * 16;
+  hp += sq * hseq;
+  cand += (size_t)sq * k * top;
+  unary += (size_t)sq * k * top;
+  tab += (size_t)sq * top * (1 + 15 * top);
+  best += (size_t)sq * (1 + 15 * top);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (j == 0 && tp > 0) return;
   const bool prev_row = j > 0 && !forced;
@@ -1130,6 +1151,12 @@ __global__ __launch_bounds__(kThreads) void k_chain(const float* __restrict__ ta
                                                     int tpn, float* __restrict__ score,
                                                     int* __restrict__ chosen) {
   extern __shared__ int lb[];  // best [1 + (k−1)·tpn], then the walk: table row, choice per row
+  // sequence blockIdx.z of a batched selection
+  tab += (size_t)blockIdx.z * top * (1 + 15 * top);
+  best += (size_t)blockIdx.z * (1 + 15 * top);
+  cand += (size_t)blockIdx.z * k * top;
+  score += (size_t)blockIdx.z * k * top;
+  chosen += (size_t)blockIdx.z * k;
   const int nb = 1 + (k - 1) * tpn;
   int* lrow = lb + nb;
   int* lch = lrow + k;
@@ -1400,18 +1427,32 @@ void select_all(hipStream_t st, const float* logits, bool have_gmax, int k, int 
                 const float* hp, int rank, const uint16_t* pbook, const uint16_t* cbook,
                 int vocab, int anchor, const int* forced, SelectScratch sc, int* cand,
                 float* unary, float* score, int* chosen) {
+  select_batch(st, 1, logits, 0, have_gmax, k, width, top, hp, 0, rank, pbook, cbook, vocab,
+               &anchor, forced, sc, cand, unary, score, chosen);
+}
+
+void select_batch(hipStream_t st, int nseq, const float* logits, long lseq, bool have_gmax, int k,
+                  int width, int top, const float* hp, long hseq, int rank,
+                  const uint16_t* pbook, const uint16_t* cbook, int vocab, const int* anchors,
+                  const int* forced, SelectScratch sc, int* cand, float* unary, float* score,
+                  int* chosen) {
   const int ngroups = cdiv(width, 256), ns = topk_slices(width), cap = topk_cap(width, top);
+  SeqTok an{};
+  for (int i = 0; i < nseq; ++i) an.t[i] = anchors[i];
   if (!have_gmax)
-    k_rowmax<<<dim3(ngroups, k), kThreads, 0, st>>>(logits, width, ngroups, sc.gmax, sc.counters);
-  k_collect<<<dim3(cdiv(ns, 4), k), kThreads, 0, st>>>(logits, width, top, ns, sc.gmax, ngroups,
-                                                       sc.counters, sc.lv, sc.li, cap);
+    k_rowmax<<<dim3(ngroups, k, nseq), kThreads, 0, st>>>(logits, width, ngroups, sc.gmax,
+                                                          sc.counters, lseq);
+  k_collect<<<dim3(cdiv(ns, 4), k, nseq), kThreads, 0, st>>>(logits, width, top, ns, sc.gmax,
+                                                             ngroups, sc.counters, sc.lv, sc.li,
+                                                             cap, lseq);
   const int tpn = forced ? 1 : top;
-  k_pairs<<<dim3(k, tpn), 128, 0, st>>>(sc.lv, sc.li, sc.counters, cap, top, hp, rank,
-                                        reinterpret_cast<const f16*>(pbook),
-                                        reinterpret_cast<const f16*>(cbook), vocab, anchor,
-                                        forced, cand, unary, sc.tab, sc.best);
+  k_pairs<<<dim3(k, tpn, nseq), 128, 0, st>>>(sc.lv, sc.li, sc.counters, cap, top, hp, rank,
+                                              reinterpret_cast<const f16*>(pbook),
+                                              reinterpret_cast<const f16*>(cbook), vocab, an,
+                                              hseq, forced, cand, unary, sc.tab, sc.best);
   const size_t lds = sizeof(int) * ((size_t)(1 + (k - 1) * tpn) + 2 * k);
-  k_chain<<<1, kThreads, lds, st>>>(sc.tab, sc.best, cand, k, top, tpn, score, chosen);
+  k_chain<<<dim3(1, 1, nseq), kThreads, lds, st>>>(sc.tab, sc.best, cand, k, top, tpn, score,
+                                                   chosen);
 }
 
 void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, TileMap map,
