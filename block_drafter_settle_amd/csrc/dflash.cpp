@@ -78,14 +78,23 @@ Split split_big(int ntiles, int steps) {
   return {(int)((steps + per - 1) / per), per};
 }
 
-// K splits of a batched product (16 weight tiles a workgroup): as many
-// workgroups as run at once without a second round (two a compute unit at
-// 4 row blocks, one at 8: their LDS), at most 8 splits (each split writes
-// a whole [rows][N] partial).
+// K splits of a batched product (16 weight tiles a workgroup): the count
+// that finishes soonest when the workgroups run in rounds of `slots` (two a
+// compute unit at 4 row blocks, one at 8: their LDS), i.e. the least
+// rounds / S, at most 8 splits (each split writes a whole [rows][N]
+// partial); the smaller S among near ties.
 Split split_mb(int ntiles, int units, int MB) {
   const long groups = dfl::mb_groups(ntiles);
   const long slots = MB == 4 ? 512 : 256;
-  const long S = std::max(1L, std::min<long>(std::min<long>(8, units), slots / groups));
+  long S = 1;
+  double best = 1e30;
+  for (long c = 1; c <= std::min<long>(8, units); ++c) {
+    const double t = (double)((groups * c + slots - 1) / slots) / c;
+    if (t < best * 0.9) {
+      best = t;
+      S = c;
+    }
+  }
   const int per = (int)((units + S - 1) / S);
   return {(units + per - 1) / per, per};
 }
