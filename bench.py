@@ -512,7 +512,7 @@ def leg_4b(pkg, synth, dev, stream, nblocks):
            torch.empty(k, top, device=dev), torch.empty(k, top, device=dev),
            torch.empty(k, dtype=torch.int32, device=dev)]
     ptrs = [t.data_ptr() for t in out]
-    anchors = synth.uniform_tokens(g, nblocks + 10, seed=0)
+    anchors = synth.uniform_tokens(g, max(nblocks, 10) + 10, seed=0)  # 10 warm, 20 timed stages
     for i in range(10):
         d.block(anchors[i], n, k, width, *ptrs)
     torch.cuda.synchronize()

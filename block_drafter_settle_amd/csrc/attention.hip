@@ -20,29 +20,28 @@ namespace dfl {
 // rows from row s0 on, wrapping at most once. Each wave keeps one q head's 16 query rows and an
 // online softmax over 32-key steps: S^T = K·Q^T and O^T += V^T·P^T on MFMA.
 // Every operand is an f16 pair (hi, lo = f16 of the rest): q's two A-layout
-// planes (plane 1 at qa + qps), K and V split into two LDS planes, P split
-// in registers; each product takes hi·hi + hi·lo + lo·hi, the dropped lo·lo
+// planes (plane 1 at qa + qps), K and V as the store keeps them (per kv
+// head, rows of hi [hd] then lo [hd]) staged into two LDS planes each, P
+// split in registers; each product takes hi·hi + hi·lo + lo·hi, the dropped lo·lo
 // term lying below f32 rounding. The softmax runs in base 2 (scores times
 // log2 e, exp2 as one v_exp_f32). Writes the chunk's (max, sum, O) for the
 // merge, the max in base-2 units.
 // Batched blocks: blockIdx.z = nzq·s + z for sequence s, whose call is
 // seqs.s[s] (its own store, range and chunking); its queries at
-// qa + s·nh·16·hd, its block rows' keys and values at kb, vb + s·16·kd,
+// qa + s·nh·16·hd, its block rows' keys and values at kb, vb + s·16·2kd halves,
 // its chunk states at pacc, pml + s·nh·(kAttnMaxChunks + 1)·16·(hd, 1).
 // A chunk index past the sequence's own chunks leaves at once.
 template <int HD>
 __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, long qps,
                                                    AttnSeqs seqs, int nzq,
-                                                   const float* __restrict__ kb,
-                                                   const float* __restrict__ vb, int B, int nh,
+                                                   const f16* __restrict__ kb,
+                                                   const f16* __restrict__ vb, int B, int nh,
                                                    int kv, int window, float scale,
                                                    float* __restrict__ pacc,
                                                    float2* __restrict__ pml) {
   constexpr int KST = HD + 8;   // LDS row stride of K (halfs)
   constexpr int VST = 32 + 4;   // LDS row stride of V^T (halfs): 18 dwords, so 16 rows' 64-bit
                                 // reads fall on distinct banks
-  constexpr int DPT = HD / 16;  // dims a thread stages, for each of its two keys
-  constexpr int EPT = 2 * DPT;  // staged elements per thread per 32 keys, each of K and V
   __shared__ f16 Ks[2][32 * KST];
   __shared__ f16 Vt[2][HD * VST];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -51,8 +50,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
   const AttnSeq& cs = seqs.s[sq];
   const int n = cs.n, chunk = cs.chunk, nchunks = cs.nchunks;
   if (c > nchunks) return;  // whole workgroup
-  const float* __restrict__ sk = cs.sk;
-  const float* __restrict__ sv = cs.sv;
+  const f16* __restrict__ sk = reinterpret_cast<const f16*>(cs.sk);
+  const f16* __restrict__ sv = reinterpret_cast<const f16*>(cs.sv);
   const long cap = cs.cap, s0 = cs.s0, lo_pos = cs.lo, a = cs.a;
   const int rep = nh / kv;
   const int qi = (blockIdx.z % nzq) * 4 + wave;
@@ -60,15 +59,16 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
   const int hq = g * rep + min(qi, rep - 1);
   const int kd = kv * HD;
   qa += (size_t)sq * nh * 16 * HD;
-  kb += (size_t)sq * 16 * kd;
-  vb += (size_t)sq * 16 * kd;
+  kb += (size_t)sq * 16 * 2 * kd;
+  vb += (size_t)sq * 16 * 2 * kd;
   pacc += (size_t)sq * nh * (kAttnMaxChunks + 1) * 16 * HD;
   pml += (size_t)sq * nh * (kAttnMaxChunks + 1) * 16;
   const bool blk = c == nchunks;
   const int k_first = blk ? 0 : c * chunk;
   const int count = blk ? B : min(chunk, n - k_first);
-  const float* kbase = (blk ? kb : sk) + (size_t)g * HD;
-  const float* vbase = (blk ? vb : sv) + (size_t)g * HD;
+  // kv head g's rows: its ring of cap rows in the store, or the block's 16
+  const f16* kbase = blk ? kb + (size_t)g * 16 * 2 * HD : sk + (size_t)g * cap * 2 * HD;
+  const f16* vbase = blk ? vb + (size_t)g * 16 * 2 * HD : sv + (size_t)g * cap * 2 * HD;
   // ring row of the chunk's first key (s0 < cap and k_first < n ≤ cap)
   const long wrap = blk ? LONG_MAX : cap;
   long row_first = blk ? 0 : s0 + k_first;
@@ -96,59 +96,47 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
 #pragma unroll
   for (int d = 0; d < HD / 16; ++d) acc[d] = (f4){0.f, 0.f, 0.f, 0.f};
 
-  // staging: thread t takes keys 2·(t%16) and 2·(t%16)+1, dims (t/16)·DPT ..
-  // +DPT of each, so that V^T takes a key pair a 32-bit store and K a key's
-  // dims in one store; two register sets hold the next two 32-key steps
-  // while one is computed
-  const int kp = threadIdx.x & 15, d0 = (threadIdx.x >> 4) * DPT;
+  // Staging: a kv head's row is 2·HD halves (hi, then lo), NPL 16-byte
+  // pieces a plane. Thread t stages piece jp of key pairs q, q + QP, ..:
+  // q = lane mod QP, jp = lane / QP + (64 / QP)·wave, so a load instruction
+  // covers whole 128-byte runs of QP rows, and for a V^T dims row the lanes
+  // with one jp write consecutive key pairs. NSET register sets (set entry
+  // 2·pass + key of the pair) hold the next NSET 32-key steps while one is
+  // computed.
+  constexpr int QP = 1024 / HD;   // key pairs a pass: 16 pairs (32 keys) in HD / 64 passes
+  constexpr int NPASS = HD / 64;
+  constexpr int NPL = HD / 8;
+  const int q = lane % QP, jp = lane / QP + (64 / QP) * wave;
+  const int spl = jp / NPL, dd = (jp % NPL) * 8;
   // Keys past the chunk's end read the chunk's last row instead (their
   // scores are masked, so they weigh 0 against finite values): no load sits
   // in a branch, and the loads of the steps ahead stay in flight across the
   // LDS-only barriers below.
-  auto fetch = [&](int k0, float4 (&kreg)[EPT / 4], float4 (&vreg)[EPT / 4]) {
+  auto fetch = [&](int k0, h8 (&kreg)[2 * NPASS], h8 (&vreg)[2 * NPASS]) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int key = min(k0 + 2 * kp + h, count - 1);
-      long row = row_first + key;
-      if (row >= wrap) row -= wrap;
-      const float4* kpn = reinterpret_cast<const float4*>(kbase + (size_t)row * kd + d0);
-      const float4* vpn = reinterpret_cast<const float4*>(vbase + (size_t)row * kd + d0);
+    for (int ps = 0; ps < NPASS; ++ps)
 #pragma unroll
-      for (int e = 0; e < DPT / 4; ++e) {
-        kreg[h * (DPT / 4) + e] = kpn[e];
-        vreg[h * (DPT / 4) + e] = vpn[e];
+      for (int h = 0; h < 2; ++h) {
+        const int key = min(k0 + 2 * (q + QP * ps) + h, count - 1);
+        long row = row_first + key;
+        if (row >= wrap) row -= wrap;
+        const size_t off = (size_t)row * 2 * HD + spl * HD + dd;
+        kreg[2 * ps + h] = *reinterpret_cast<const h8*>(kbase + off);
+        vreg[2 * ps + h] = *reinterpret_cast<const h8*>(vbase + off);
       }
-    }
   };
-  auto stage = [&](const float4 (&kreg)[EPT / 4], const float4 (&vreg)[EPT / 4]) {
+  auto stage = [&](const h8 (&kreg)[2 * NPASS], const h8 (&vreg)[2 * NPASS]) {
     lds_barrier();
-    f16 vh[2][DPT], vl[2][DPT];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f16 kh[DPT], kl[DPT];
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int kk = 2 * (q + QP * ps);
 #pragma unroll
-      for (int e = 0; e < DPT / 4; ++e) {
-        const float4 kk = kreg[h * (DPT / 4) + e], vv = vreg[h * (DPT / 4) + e];
-        const float kf[4] = {kk.x, kk.y, kk.z, kk.w};
-        const float vf[4] = {vv.x, vv.y, vv.z, vv.w};
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<h8*>(&Ks[spl][(kk + h) * KST + dd]) = kreg[2 * ps + h];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          split_f16(kf[q], kh[4 * e + q], kl[4 * e + q]);
-          split_f16(vf[q], vh[h][4 * e + q], vl[h][4 * e + q]);
-        }
-      }
-      f16* k0p = &Ks[0][(2 * kp + h) * KST + d0];
-      f16* k1p = &Ks[1][(2 * kp + h) * KST + d0];
-#pragma unroll
-      for (int e = 0; e < DPT / 4; ++e) {
-        *reinterpret_cast<h4*>(k0p + 4 * e) = (h4){kh[4 * e], kh[4 * e + 1], kh[4 * e + 2], kh[4 * e + 3]};
-        *reinterpret_cast<h4*>(k1p + 4 * e) = (h4){kl[4 * e], kl[4 * e + 1], kl[4 * e + 2], kl[4 * e + 3]};
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < DPT; ++e) {
-      *reinterpret_cast<h2*>(&Vt[0][(d0 + e) * VST + 2 * kp]) = (h2){vh[0][e], vh[1][e]};
-      *reinterpret_cast<h2*>(&Vt[1][(d0 + e) * VST + 2 * kp]) = (h2){vl[0][e], vl[1][e]};
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<h2*>(&Vt[spl][(dd + e) * VST + kk]) =
+            (h2){vreg[2 * ps][e], vreg[2 * ps + 1][e]};
     }
     lds_barrier();
   };
@@ -214,20 +202,22 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
       acc[d] = mfma16(vl, pb, t);
     }
   };
-  // 64 keys a round, in two 32-key steps, each fetched two steps ahead. A
-  // step wholly past the chunk's end changes nothing: its scores are all
-  // masked, so the correction factor is exactly 1 and P is 0.
-  float4 ka[EPT / 4], va[EPT / 4], kb2[EPT / 4], vb2[EPT / 4];
+  // NSET register sets of 32-key steps: each step is fetched NSET steps
+  // ahead, so that NSET steps of K/V rows are in flight while one is
+  // computed. Steps past the chunk's end are fetched (the clamped last row)
+  // and staged but not computed. (Three sets were measured no faster.)
+  constexpr int NSET = 2;
+  h8 kr[NSET][2 * NPASS], vr[NSET][2 * NPASS];
   if (count > 0) {
-    fetch(0, ka, va);
-    fetch(32, kb2, vb2);
-    for (int k0 = 0; k0 < count; k0 += 64) {
-      stage(ka, va);
-      fetch(k0 + 64, ka, va);
-      compute(k0);
-      stage(kb2, vb2);
-      fetch(k0 + 96, kb2, vb2);
-      compute(k0 + 32);
+#pragma unroll
+    for (int i = 0; i < NSET; ++i) fetch(32 * i, kr[i], vr[i]);
+    for (int k0 = 0; k0 < count; k0 += 32 * NSET) {
+#pragma unroll
+      for (int i = 0; i < NSET; ++i) {
+        stage(kr[i], vr[i]);
+        fetch(k0 + 32 * (i + NSET), kr[i], vr[i]);
+        if (k0 + 32 * i < count) compute(k0 + 32 * i);
+      }
     }
   }
   if (!active) return;
@@ -298,22 +288,24 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 static inline unsigned cdiv(long a, long b) { return (unsigned)((a + b - 1) / b); }
 
 void attention(hipStream_t st, const uint16_t* qa, long qps, const AttnSeqs& seqs, int nseq,
-               const float* kb, const float* vb, int B, int nh, int kv, int hd, int window,
+               const uint16_t* kb, const uint16_t* vb, int B, int nh, int kv, int hd, int window,
                float scale, float* pacc, float* pml) {
   const int rep = nh / kv, nzq = cdiv(rep, 4);
   int maxc = 0;
   for (int i = 0; i < nseq; ++i) maxc = std::max(maxc, seqs.s[i].nchunks);
   dim3 grid(kv, maxc + 1, nzq * nseq);
   const f16* q = reinterpret_cast<const f16*>(qa);
+  const f16* k16 = reinterpret_cast<const f16*>(kb);
+  const f16* v16 = reinterpret_cast<const f16*>(vb);
   float2* ml = reinterpret_cast<float2*>(pml);
   if (hd == 64)
-    k_attn<64><<<grid, kThreads, 0, st>>>(q, qps, seqs, nzq, kb, vb, B, nh, kv, window, scale,
+    k_attn<64><<<grid, kThreads, 0, st>>>(q, qps, seqs, nzq, k16, v16, B, nh, kv, window, scale,
                                            pacc, ml);
   else if (hd == 128)
-    k_attn<128><<<grid, kThreads, 0, st>>>(q, qps, seqs, nzq, kb, vb, B, nh, kv, window, scale,
+    k_attn<128><<<grid, kThreads, 0, st>>>(q, qps, seqs, nzq, k16, v16, B, nh, kv, window, scale,
                                             pacc, ml);
   else
-    k_attn<256><<<grid, kThreads, 0, st>>>(q, qps, seqs, nzq, kb, vb, B, nh, kv, window, scale,
+    k_attn<256><<<grid, kThreads, 0, st>>>(q, qps, seqs, nzq, k16, v16, B, nh, kv, window, scale,
                                             pacc, ml);
 }
 

@@ -36,6 +36,14 @@ __device__ __forceinline__ void split_f16(float v, f16& hi, f16& lo) {
   lo = (f16)(v - (float)hi);
 }
 
+// Stores v's f16 pair in a key/value row: hi at row[i], lo at row[kd + i].
+__device__ __forceinline__ void put_pair(f16* row, int kd, int i, float v) {
+  f16 hi, lo;
+  split_f16(v, hi, lo);
+  row[i] = hi;
+  row[kd + i] = lo;
+}
+
 // Stores v at A-layout index idx: plane 0 its f16 rounding and, when ps (the
 // plane stride in halves) is nonzero, plane 1 the f16 rounding of what is left.
 __device__ __forceinline__ void put_a(f16* xa, long ps, size_t idx, float v) {

@@ -159,10 +159,10 @@ void repack_i4(const dflash_i4& m, int N, int K, uint8_t* codes, uint16_t* scale
 // Per-call scratch of the block pass: activations, GEMM and attention
 // partial results, the selection's lists and counters.
 struct BlockScratch {
-  float *h = nullptr, *x = nullptr, *dsum_a = nullptr, *dsum_m = nullptr, *kb = nullptr,
-        *vb = nullptr, *pacc = nullptr, *pml = nullptr, *part = nullptr, *logits = nullptr,
-        *hp = nullptr, *sqp = nullptr;
+  float *h = nullptr, *x = nullptr, *dsum_a = nullptr, *dsum_m = nullptr, *pacc = nullptr,
+        *pml = nullptr, *part = nullptr, *logits = nullptr, *hp = nullptr, *sqp = nullptr;
   uint16_t *xa = nullptr, *xca = nullptr, *qa = nullptr, *ya = nullptr, *ma = nullptr;
+  uint16_t *kb = nullptr, *vb = nullptr;  // the block's keys and values, f16-pair rows
   dfl::SelectScratch sel{};
 };
 
@@ -186,10 +186,10 @@ struct WeightOwner {
 // for dfl::kMaxSeq sequences (8 A-layout row blocks) at its first batched
 // call.
 struct BatchScratch {
-  float *h = nullptr, *dsum_a = nullptr, *dsum_m = nullptr, *kb = nullptr, *vb = nullptr,
-        *pacc = nullptr, *pml = nullptr, *part = nullptr, *logits = nullptr, *hp = nullptr,
-        *sqp = nullptr;
+  float *h = nullptr, *dsum_a = nullptr, *dsum_m = nullptr, *pacc = nullptr, *pml = nullptr,
+        *part = nullptr, *logits = nullptr, *hp = nullptr, *sqp = nullptr;
   uint16_t *xa = nullptr, *xca = nullptr, *qa = nullptr, *ya = nullptr, *ma = nullptr;
+  uint16_t *kb = nullptr, *vb = nullptr;
   dfl::SelectScratch sel{};  // kMaxSeq sets (select_batch)
   long part_floats = 0;
   bool ready = false;
@@ -216,7 +216,9 @@ struct dflash {
   // ring store of the rows it still holds; tap rows that wait to be settled
   long first = 0, len = 0;
   struct LayerStore {
-    float *k = nullptr, *v = nullptr;  // cap rows; position p at row (p − first) mod cap
+    // rings of cap rows of f16 pairs, kv head major ([kv][cap][hi hd | lo
+    // hd], 4·kd bytes a row); position p at row (p − first) mod cap
+    uint16_t *k = nullptr, *v = nullptr;
     long cap = 0;
     long limit = 0;    // most rows the layer may hold (a windowed layer's ring is this big)
     long dropped = 0;  // settled rows the layer no longer holds (`Ctx::dropped`)
@@ -266,6 +268,9 @@ int fail(dflash* d, int code, const char* fmt, ...) {
     g_create_error = buf;
   return code;
 }
+
+// Bytes of one store row: kd keys (or values), each as its f16 pair.
+size_t store_row_bytes(const dflash* d) { return 2 * (size_t)d->kd * sizeof(uint16_t); }
 
 int hip_check(dflash* d, hipError_t e, const char* what) {
   if (e == hipSuccess) return DFLASH_OK;
@@ -553,21 +558,27 @@ int reserve(dflash* d, long rows) {
     auto& S = d->ls[l];
     if (d->windows[l] > 0 || rows <= S.cap) continue;
     const long cap = std::min(std::max(std::max(rows, 2 * S.cap), 4096L), d->maxctx);
-    const size_t bytes = (size_t)cap * d->kd * sizeof(float);
-    float *nk = nullptr, *nv = nullptr;
+    const size_t bytes = (size_t)cap * store_row_bytes(d);
+    uint16_t *nk = nullptr, *nv = nullptr;
     if (hipMalloc(&nk, bytes) != hipSuccess || hipMalloc(&nv, bytes) != hipSuccess) {
       (void)hipGetLastError();
       if (nk) (void)hipFree(nk);
       return fail(d, DFLASH_ENOMEM, "device memory for layer %d's context (%zu bytes)", l,
                   2 * bytes);
     }
-    // a full layer holds positions first .. first+len at rows 0 .. len
-    const size_t held = (size_t)std::min(d->len, S.cap) * d->kd * sizeof(float);
+    // a full layer holds positions first .. first+len at rows 0 .. len of
+    // every kv head's ring
+    const size_t hrow = store_row_bytes(d) / d->kv;  // one kv head's row
+    const size_t held = (size_t)std::min(d->len, S.cap) * hrow;
     int rc = DFLASH_OK;
     if (held)
-      rc = hip_check(d, hipMemcpyAsync(nk, S.k, held, hipMemcpyDeviceToDevice, d->st), "reserve");
+      rc = hip_check(d, hipMemcpy2DAsync(nk, cap * hrow, S.k, S.cap * hrow, held, d->kv,
+                                         hipMemcpyDeviceToDevice, d->st),
+                     "reserve");
     if (!rc && held)
-      rc = hip_check(d, hipMemcpyAsync(nv, S.v, held, hipMemcpyDeviceToDevice, d->st), "reserve");
+      rc = hip_check(d, hipMemcpy2DAsync(nv, cap * hrow, S.v, S.cap * hrow, held, d->kv,
+                                         hipMemcpyDeviceToDevice, d->st),
+                     "reserve");
     if (!rc) rc = hip_check(d, hipStreamSynchronize(d->st), "reserve");
     if (rc) {
       (void)hipFree(nk);
@@ -688,8 +699,8 @@ size_t carve_block_scratch(const dflash* d, uint8_t* base, BlockScratch* out) {
   take(&b.x, 16 * hs);
   take(&b.dsum_a, 16 * (size_t)d->P);
   take(&b.dsum_m, 16 * (size_t)d->P);
-  take(&b.kb, 16 * (size_t)d->kd);
-  take(&b.vb, 16 * (size_t)d->kd);
+  take(&b.kb, 2 * 16 * (size_t)d->kd);
+  take(&b.vb, 2 * 16 * (size_t)d->kd);
   take(&b.pacc, slots * 16 * d->hd);
   take(&b.pml, slots * 16 * 2);
   take(&b.part, (size_t)part);
@@ -748,7 +759,7 @@ static int alloc_state(dflash* d) {
     const long w = d->windows[l];
     S.limit = w > 0 ? std::min(2 * w, d->maxctx) : d->maxctx;
     if (w > 0) {
-      const size_t bytes = (size_t)S.limit * d->kd * sizeof(float);
+      const size_t bytes = (size_t)S.limit * store_row_bytes(d);
       if (hipMalloc(&S.k, bytes) != hipSuccess || hipMalloc(&S.v, bytes) != hipSuccess) {
         (void)hipGetLastError();
         rc = fail(nullptr, DFLASH_ENOMEM, "device memory for layer %d's context (%zu bytes)", l,
@@ -774,8 +785,8 @@ static int alloc_state(dflash* d) {
   if (!rc) rc = dev_alloc(d, &b.x, 16 * hs, "scratch");
   if (!rc) rc = dev_alloc(d, &b.dsum_a, 16 * d->P, "scratch");
   if (!rc) rc = dev_alloc(d, &b.dsum_m, 16 * d->P, "scratch");
-  if (!rc) rc = dev_alloc(d, &b.kb, 16 * d->kd, "scratch");
-  if (!rc) rc = dev_alloc(d, &b.vb, 16 * d->kd, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.kb, 2 * 16 * d->kd, "scratch");
+  if (!rc) rc = dev_alloc(d, &b.vb, 2 * 16 * d->kd, "scratch");
   if (!rc) rc = dev_alloc(d, &b.pacc, slots * 16 * d->hd, "attention partials");
   if (!rc) rc = dev_alloc(d, &b.pml, slots * 16 * 2, "attention partials");
   if (!rc) rc = dev_alloc(d, &d->part, d->part_floats, "GEMM partials");
@@ -1438,8 +1449,8 @@ static int batch_scratch(dflash* d) {
   take(&b.sqp, R * (size_t)std::max(dfl::row_chunks(d->hs), dfl::conv1_chunks(d->hs)), "batch scratch");
   take(&b.dsum_a, R * d->P, "batch scratch");
   take(&b.dsum_m, R * d->P, "batch scratch");
-  take(&b.kb, R * d->kd, "batch scratch");
-  take(&b.vb, R * d->kd, "batch scratch");
+  take(&b.kb, 2 * R * d->kd, "batch scratch");
+  take(&b.vb, 2 * R * d->kd, "batch scratch");
   take(&b.pacc, slots * 16 * d->hd, "batch attention partials");
   take(&b.pml, slots * 16 * 2, "batch attention partials");
   take(&b.part, (size_t)part, "batch partials");
@@ -1735,21 +1746,12 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
 
 // Copies n rows of a layer's ring from ring row r0 on (wrapping) to or from
 // a linear buffer.
-static int ring_copy(dflash* d, float* ring, long cap, long r0, float* lin, long n, bool out,
+// f32 rows lin [n][kd] to (out = false) or from (out = true) rows r0 .. of
+// a layer's ring
+static int ring_copy(dflash* d, uint16_t* ring, long cap, long r0, float* lin, long n, bool out,
                      const char* what) {
-  const size_t row = (size_t)d->kd * sizeof(float);
-  for (long done = 0; done < n;) {
-    const long r = (r0 + done) % cap, c = std::min(n - done, cap - r);
-    float* rp = ring + (size_t)r * d->kd;
-    float* lp = lin + (size_t)done * d->kd;
-    const int rc = hip_check(d,
-                             hipMemcpyAsync(out ? lp : rp, out ? rp : lp, c * row,
-                                            hipMemcpyDeviceToDevice, d->st),
-                             what);
-    if (rc) return rc;
-    done += c;
-  }
-  return DFLASH_OK;
+  dfl::store_rows(d->st, ring, cap, r0, lin, n, d->kv, d->hd, out);
+  return hip_check(d, hipGetLastError(), what);
 }
 
 int dflash_debug_read_store(dflash_t* d, int32_t layer, int64_t row0, int64_t n, float* k_out,

@@ -159,15 +159,25 @@ void conv1(hipStream_t st, float* h, const float* opart, int splits, long split_
 // pos: host [nseq], each sequence's block position a
 void qkv_post(hipStream_t st, const float* part, int splits, long split_stride, int rows, int nh,
               int kv, int hd, const float* q_norm, const float* k_norm, const float* inv_freq,
-              const long* pos, int nseq, int rot, float eps, uint16_t* qa, long qps, float* kb,
-              float* vb);
-// A layer's context store: a ring of cap rows of [kv_heads][head_dim] f32
-// keys and values; position p sits at row (p − first) mod cap.
+              const long* pos, int nseq, int rot, float eps, uint16_t* qa, long qps, uint16_t* kb,
+              uint16_t* vb);
+// Keys and values are kept as f16 pairs, kv head major: the head_dim f32
+// values x of one kv head of one row are 2·head_dim halves, hi = f16(x) for
+// all head_dim, then lo = f16(x − hi) (the bytes of the f32 values), and a
+// buffer of R rows holds kv head g's rows at [g][R][2·head_dim]. A layer's
+// context store is such a ring of R = cap rows for the keys and one for the
+// values; position p sits at row (p − first) mod cap. The block's own rows
+// (kb, vb) are R = 16 rows a sequence.
 struct StoreSlot {
-  float* k;
-  float* v;
+  uint16_t* k;
+  uint16_t* v;
   long cap;
 };
+// Conversion between f32 rows and a ring's rows (debug reads and loads of
+// the store): rows r0 .. r0+n−1 of the ring (each at row index mod cap) from
+// (out = false) or to (out = true) lin, dev f32 [n][kv·hd].
+void store_rows(hipStream_t st, uint16_t* ring, long cap, long r0, float* lin, long n, int kv,
+                int hd, bool out);
 // row0 = pos0 − first; row_end: one past the settle call's last row (rows
 // below row_end − cap of a layer are not written to it); tab: the layers'
 // stores (device memory).
@@ -182,8 +192,8 @@ constexpr int kAttnMaxChunks = 64;
 // whose n keys of positions lo.. start at ring row s0 and wrap at most
 // once; a its block position; the keys in nchunks chunks of `chunk`.
 struct AttnSeq {
-  const float* sk;
-  const float* sv;
+  const uint16_t* sk;
+  const uint16_t* sv;
   long cap, s0, lo, a;
   int n, chunk, nchunks;
 };
@@ -196,7 +206,7 @@ struct SeqChunks {
 // pacc, pml: nseq·nh·(kAttnMaxChunks + 1)·16 chunk states (hd floats, and a
 // float pair, each)
 void attention(hipStream_t st, const uint16_t* qa, long qps, const AttnSeqs& seqs, int nseq,
-               const float* kb, const float* vb, int B, int nh, int kv, int hd, int window,
+               const uint16_t* kb, const uint16_t* vb, int B, int nh, int kv, int hd, int window,
                float scale, float* pacc, float* pml);
 void attn_merge(hipStream_t st, const float* pacc, const float* pml, int nh, int kv, int hd,
                 const AttnSeqs& seqs, int nseq, int B, uint16_t* ya, long ps);

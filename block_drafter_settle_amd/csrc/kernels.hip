@@ -666,15 +666,16 @@ __device__ __forceinline__ void norm_rope(Pairs& p, int hd, const float* gain, f
 }
 
 // Block q/k/v: split-summed, q and k normed per head and rotated to a+r;
-// q in A-layout per head for the attention, k and v f32 [16][kd].
+// q in A-layout per head for the attention, k and v as f16 pairs in the
+// store's form, [kv][16][hi hd | lo hd] a sequence.
 __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ part, int splits,
                                                  long ss, int nh, int kv, int hd,
                                                  const float* __restrict__ qn,
                                                  const float* __restrict__ kn,
                                                  const float* __restrict__ inv, SeqPos pos,
                                                  int rot, float eps, f16* __restrict__ qa,
-                                                 long qps, float* __restrict__ kb,
-                                                 float* __restrict__ vb) {
+                                                 long qps, f16* __restrict__ kb,
+                                                 f16* __restrict__ vb) {
   // block row m of sequence sq (rows 16sq.. of part, kb, vb; its q heads at
   // qa + sq·nh·16·hd), at position a_sq + m
   const int m = blockIdx.x, hh = blockIdx.y, sq = blockIdx.z, r = 16 * sq + m;
@@ -691,10 +692,11 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ part,
       put_a(q, qps, a_idx(m, i), p.lo[c]);
       put_a(q, qps, a_idx(m, i + half), p.hi[c]);
     } else {
-      float* dst = hh < nh + kv ? kb + (size_t)r * kd + (hh - nh) * hd
-                                : vb + (size_t)r * kd + (hh - nh - kv) * hd;
-      dst[i] = p.lo[c];
-      dst[i + half] = p.hi[c];
+      const int g = hh < nh + kv ? hh - nh : hh - nh - kv;
+      f16* dst = (hh < nh + kv ? kb : vb) + (size_t)sq * 16 * 2 * kd +
+                 ((size_t)g * 16 + m) * 2 * hd;
+      put_pair(dst, hd, i, p.lo[c]);
+      put_pair(dst, hd, i + half, p.hi[c]);
     }
   }
 }
@@ -731,14 +733,31 @@ __global__ __launch_bounds__(64) void k_settle_kv(const float* __restrict__ part
     p.hi[c] *= sr;
   }
   if (isk) norm_rope(p, hd, knorm + (size_t)l * hd, eps, inv, pos0 + r, rot[l]);
-  float* dst = (isk ? so.k : so.v) + (size_t)((row0 + r) % so.cap) * kd + (size_t)g * hd;
+  f16* dst = reinterpret_cast<f16*>(isk ? so.k : so.v) +
+             ((size_t)g * so.cap + (row0 + r) % so.cap) * 2 * hd;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int i = threadIdx.x + 64 * c;
     if (i >= half) continue;
-    dst[i] = p.lo[c];
-    dst[i + half] = p.hi[c];
+    put_pair(dst, hd, i, p.lo[c]);
+    put_pair(dst, hd, i + half, p.hi[c]);
   }
+}
+
+// Rows r0 .. r0+n−1 of a ring of f16-pair rows against f32 rows: one thread
+// per value; out: x = hi + lo into lin, else the pair of lin's x.
+__global__ __launch_bounds__(kThreads) void k_store_rows(f16* __restrict__ ring, long cap, long r0,
+                                                         float* __restrict__ lin, long n, int kv,
+                                                         int hd, int out) {
+  const long kd = (long)kv * hd, e = (long)blockIdx.x * kThreads + threadIdx.x;
+  if (e >= n * kd) return;
+  const long i = e / kd;
+  const int c = (int)(e - i * kd), g = c / hd, x = c - g * hd;
+  f16* row = ring + ((size_t)g * cap + (r0 + i) % cap) * 2 * hd;
+  if (out)
+    lin[e] = (float)row[x] + (float)row[hd + x];
+  else
+    put_pair(row, hd, x, lin[e]);
 }
 
 // ------------------------------------------------------- top-k, selector
@@ -1399,12 +1418,13 @@ void conv1(hipStream_t st, float* h, const float* opart, int splits, long ss, co
 
 void qkv_post(hipStream_t st, const float* part, int splits, long ss, int rows, int nh, int kv,
               int hd, const float* q_norm, const float* k_norm, const float* inv, const long* pos,
-              int nseq, int rot, float eps, uint16_t* qa, long qps, float* kb, float* vb) {
+              int nseq, int rot, float eps, uint16_t* qa, long qps, uint16_t* kb, uint16_t* vb) {
   dim3 grid(rows, nh + 2 * kv, nseq);
   SeqPos sp{};
   for (int i = 0; i < nseq; ++i) sp.a[i] = pos[i];
   k_qkv_post<<<grid, 64, 0, st>>>(part, splits, ss, nh, kv, hd, q_norm, k_norm, inv, sp, rot, eps,
-                                  reinterpret_cast<f16*>(qa), qps, kb, vb);
+                                  reinterpret_cast<f16*>(qa), qps, reinterpret_cast<f16*>(kb),
+                                  reinterpret_cast<f16*>(vb));
 }
 
 void settle_kv(hipStream_t st, const float* part, int splits, long ss, int rows, int layers,
@@ -1414,6 +1434,13 @@ void settle_kv(hipStream_t st, const float* part, int splits, long ss, int rows,
   dim3 grid(rows, layers, 2 * kv);
   k_settle_kv<<<grid, 64, 0, st>>>(part, splits, ss, layers, kv, hd, k_norm, inv, rot, pos0, eps,
                                    sqp, cdiv(hs, kChunk), hs, tab, row0, row_end);
+}
+
+void store_rows(hipStream_t st, uint16_t* ring, long cap, long r0, float* lin, long n, int kv,
+                int hd, bool out) {
+  if (n <= 0) return;
+  k_store_rows<<<cdiv(n * kv * hd, kThreads), kThreads, 0, st>>>(
+      reinterpret_cast<f16*>(ring), cap, r0, lin, n, kv, hd, out ? 1 : 0);
 }
 
 int topk_slices(int width) { return cdiv(width, 64 * kSliceVPL); }
