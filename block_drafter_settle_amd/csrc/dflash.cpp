@@ -1744,10 +1744,8 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
   return launch_check(d, "matvec");
 }
 
-// Copies n rows of a layer's ring from ring row r0 on (wrapping) to or from
-// a linear buffer.
 // f32 rows lin [n][kd] to (out = false) or from (out = true) rows r0 .. of
-// a layer's ring
+// a layer's ring (wrapping)
 static int ring_copy(dflash* d, uint16_t* ring, long cap, long r0, float* lin, long n, bool out,
                      const char* what) {
   dfl::store_rows(d->st, ring, cap, r0, lin, n, d->kv, d->hd, out);

@@ -1057,17 +1057,20 @@ __device__ void rank_select(const float* rv, const int* ri, int n, int want, flo
   wave_lds_sync();
 }
 
-// Row j's top candidates and row j−1's (j ≥ 1, to know the predecessor tp);
-// then the scores of row j's candidates under that predecessor (or the
-// anchor for j = 0, or forced[j]), `select_with`:
-// unary + Σ_q (P[prev][q]·hp[j][q])·C[tok][q]. Block (j, tp); block (j, 0)
-// also writes cand and unary of row j. Wave 0 selects row j and wave 1 row
-// j−1 at the same time; lists longer than kRankMax take wave_select passes
-// instead.
-__global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
+// Row j's top candidates and row j−1's (j ≥ 1: its candidates are row j's
+// predecessors), then the scores of row j's candidates under every
+// predecessor (or the anchor for j = 0, or forced[j]), `select_with`:
+// unary + Σ_q (P[prev][q]·hp[j][q])·C[tok][q]. One block per row: wave 0
+// selects row j and wave 1 row j−1 at the same time (lists longer than
+// kRankMax take wave_select passes instead); the predecessors' P rows times
+// hp[j], and the candidates' C rows, are staged in LDS once; each thread
+// then forms whole dot products, and each table row's first largest score
+// (the chain's choice for that predecessor) is found in the block.
+static constexpr int kSelTop = 32, kSelRank = 256;
+__global__ __launch_bounds__(256) void k_pairs(const float* __restrict__ lv,
                                                const int* __restrict__ li,
                                                const int* __restrict__ counters, int cap, int top,
-                                               const float* __restrict__ hp, int rank,
+                                               int tpn, const float* __restrict__ hp, int rank,
                                                const f16* __restrict__ pbook,
                                                const f16* __restrict__ cbook, int vocab,
                                                SeqTok anchors, long hseq,
@@ -1078,10 +1081,13 @@ __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
   __shared__ int uc[2][32 + 64];
   __shared__ float sv[2][kRankMax];
   __shared__ int si[2][kRankMax];
-  const int j = blockIdx.x, tp = blockIdx.y, tpn = gridDim.y;
+  __shared__ float ph[kSelTop][kSelRank];       // P[prev_p]·hp[j]
+  __shared__ uint32_t cw[kSelTop][kSelRank / 2 + 1];  // C[tok_u] as f16 pairs (odd row stride)
+  __shared__ float sc[kSelTop][kSelTop + 1];
+  const int j = blockIdx.x, k = gridDim.x;
   // sequence sq of a batched selection: its lists, projections, table and
   // outputs
-  const int sq = blockIdx.z, k = gridDim.x, anchor = anchors.t[sq];
+  const int sq = blockIdx.z, anchor = anchors.t[sq];
   lv += (size_t)sq * 16 * cap;
   li += (size_t)sq * 16 * cap;
   counters += sq * 16;
@@ -1090,73 +1096,70 @@ __global__ __launch_bounds__(128) void k_pairs(const float* __restrict__ lv,
   unary += (size_t)sq * k * top;
   tab += (size_t)sq * top * (1 + 15 * top);
   best += (size_t)sq * (1 + 15 * top);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (j == 0 && tp > 0) return;
+  const int t = threadIdx.x, wave = t >> 6;
   const bool prev_row = j > 0 && !forced;
-  const int row = j - wave;  // wave 0: row j, wave 1: row j−1
-  if (wave == 0 || prev_row) {
+  const int np = j == 0 ? 1 : tpn;  // predecessors: this row's table rows
+  if (wave == 0 || (wave == 1 && prev_row)) {
+    const int row = j - wave;
     const int n = min(counters[row], cap);
-    const int want = wave == 0 ? top : tp + 1;
     if (n <= kRankMax)
-      rank_select(lv + (size_t)row * cap, li + (size_t)row * cap, n, want, sv[wave], si[wave],
+      rank_select(lv + (size_t)row * cap, li + (size_t)row * cap, n, top, sv[wave], si[wave],
                   uv[wave], uc[wave]);
     else
-      select_list(lv + (size_t)row * cap, li + (size_t)row * cap, n, want, uv[wave], uc[wave]);
+      select_list(lv + (size_t)row * cap, li + (size_t)row * cap, n, top, uv[wave], uc[wave]);
   }
   __syncthreads();
-  if (wave == 0 && tp == 0 && lane < top) {
-    cand[(size_t)j * top + lane] = uc[0][lane];
-    unary[(size_t)j * top + lane] = uv[0][lane];
+  if (t < top) {
+    cand[(size_t)j * top + t] = uc[0][t];
+    unary[(size_t)j * top + t] = uv[0][t];
   }
-  if (wave != 0) return;
-  const int prev = j == 0 ? anchor : (forced ? forced[j] : uc[1][tp]);
-  const bool okp = prev >= 0 && prev < vocab;
-  float pc[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int q = lane + 64 * c;
-    pc[c] = (okp && q < rank) ? (float)pbook[(size_t)prev * rank + q] * hp[(size_t)j * rank + q] : 0.f;
+  for (int e = t; e < np * rank; e += 256) {
+    const int pi = e / rank, q = e - pi * rank;
+    const int prev = j == 0 ? anchor : (forced ? forced[j] : uc[1][pi]);
+    const bool ok = prev >= 0 && prev < vocab;
+    ph[pi][q] = ok ? (float)pbook[(size_t)prev * rank + q] * hp[(size_t)j * rank + q] : 0.f;
   }
-  const size_t trow = j == 0 ? 0 : 1 + (size_t)(j - 1) * tpn + tp;  // this block's table row
-  float* out = tab + trow * top;
-  // every candidate's codebook row is loaded at once (top ≤ 32): per rank
-  // quarter the 32 loads sit in one basic block, so they are in flight
-  // together rather than in dependent rounds
-  float part[32];
-#pragma unroll
-  for (int u = 0; u < 32; ++u) part[u] = 0.f;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if (64 * c >= rank) continue;  // uniform
-    const int q = lane + 64 * c;
-    const bool qok = q < rank;
-    const int qq = qok ? q : 0;
-#pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      const int tok = u < top ? uc[0][u] : -1;
-      const bool ok = okp && qok && tok >= 0 && tok < vocab;
-      const float cb = (float)cbook[(size_t)(ok ? tok : 0) * rank + qq];
-      part[u] += ok ? pc[c] * cb : 0.f;
-    }
-  }
-  // scores in candidate order; lane 0 also keeps the first strictly
-  // largest (candidate 0 when every score is −∞), the chain's choice for
-  // this predecessor
-  float bv = -INFINITY;
-  int bt = 0;
-#pragma unroll
-  for (int u = 0; u < 32; ++u) {
-    if (u >= top) break;
-    const float dot = wave_sum(part[u]);
+  const int rh = (rank + 1) >> 1;
+  for (int e = t; e < top * rh; e += 256) {
+    const int u = e / rh, q = 2 * (e - u * rh);
     const int tok = uc[0][u];
-    const float sc = (okp && tok >= 0 && tok < vocab) ? uv[0][u] + dot : -INFINITY;
-    if (sc > bv) {
-      bv = sc;
-      bt = u;
-    }
-    if (lane == 0) out[u] = sc;
+    const bool ok = tok >= 0 && tok < vocab;
+    const f16* cr = cbook + (size_t)(ok ? tok : 0) * rank;
+    const f16 c0 = ok ? cr[q] : (f16)0.f, c1 = ok && q + 1 < rank ? cr[q + 1] : (f16)0.f;
+    cw[u][q >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, c0) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, c1) << 16);
   }
-  if (lane == 0) best[trow] = bt;
+  __syncthreads();
+  // entry (p, u): threads of a wave share p and take consecutive u
+  for (int e = t; e < np * top; e += 256) {
+    const int pi = e / top, u = e - pi * top;
+    const int prev = j == 0 ? anchor : (forced ? forced[j] : uc[1][pi]);
+    const int tok = uc[0][u];
+    float d0 = 0.f, d1 = 0.f;
+    for (int q2 = 0; q2 < rh; ++q2) {
+      const uint32_t w = cw[u][q2];
+      d0 += ph[pi][2 * q2] * half_bits(w);
+      d1 += (2 * q2 + 1 < rank ? ph[pi][2 * q2 + 1] : 0.f) * half_bits(w >> 16);
+    }
+    const bool ok = prev >= 0 && prev < vocab && tok >= 0 && tok < vocab;
+    const float score = ok ? uv[0][u] + (d0 + d1) : -INFINITY;
+    sc[pi][u] = score;
+    const size_t trow = j == 0 ? 0 : 1 + (size_t)(j - 1) * tpn + pi;
+    tab[trow * top + u] = score;
+  }
+  __syncthreads();
+  // each table row's first strictly largest score (candidate 0 when every
+  // score is −∞)
+  for (int pi = t; pi < np; pi += 256) {
+    float bv = -INFINITY;
+    int bt = 0;
+    for (int u = 0; u < top; ++u)
+      if (sc[pi][u] > bv) {
+        bv = sc[pi][u];
+        bt = u;
+      }
+    best[j == 0 ? 0 : 1 + (size_t)(j - 1) * tpn + pi] = bt;
+  }
 }
 
 // The chain: row by row, the candidate chosen under the predecessor chosen
@@ -1473,10 +1476,10 @@ void select_batch(hipStream_t st, int nseq, const float* logits, long lseq, bool
                                                              ngroups, sc.counters, sc.lv, sc.li,
                                                              cap, lseq);
   const int tpn = forced ? 1 : top;
-  k_pairs<<<dim3(k, tpn, nseq), 128, 0, st>>>(sc.lv, sc.li, sc.counters, cap, top, hp, rank,
-                                              reinterpret_cast<const f16*>(pbook),
-                                              reinterpret_cast<const f16*>(cbook), vocab, an,
-                                              hseq, forced, cand, unary, sc.tab, sc.best);
+  k_pairs<<<dim3(k, 1, nseq), 256, 0, st>>>(sc.lv, sc.li, sc.counters, cap, top, tpn, hp, rank,
+                                            reinterpret_cast<const f16*>(pbook),
+                                            reinterpret_cast<const f16*>(cbook), vocab, an, hseq,
+                                            forced, cand, unary, sc.tab, sc.best);
   const size_t lds = sizeof(int) * ((size_t)(1 + (k - 1) * tpn) + 2 * k);
   k_chain<<<dim3(1, 1, nseq), kThreads, lds, st>>>(sc.tab, sc.best, cand, k, top, tpn, score,
                                                    chosen);

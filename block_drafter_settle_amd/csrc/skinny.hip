@@ -183,15 +183,12 @@ void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uin
   const f16* x = reinterpret_cast<const f16*>(xa);
   const uint4* c = reinterpret_cast<const uint4*>(codes);
   const uint2* s = reinterpret_cast<const uint2*>(scales);
-  if (R == 1 && ks == 4)
-    launch_i4_block<1, 4>(st, x, ps, K, c, s, map, N, out, ss);
-  else if (R == 2 && ks == 2)
+  // the shapes the callers use: (2, 2) for o and the debug matvec, (2, 8)
+  // for q/k/v and down
+  (void)R;
+  if (ks == 2)
     launch_i4_block<2, 2>(st, x, ps, K, c, s, map, N, out, ss);
-  else if (R == 2 && ks == 4)
-    launch_i4_block<2, 4>(st, x, ps, K, c, s, map, N, out, ss);
-  else if (R == 4 && ks == 4)
-    launch_i4_block<4, 4>(st, x, ps, K, c, s, map, N, out, ss);
-  else  // (2, 8)
+  else
     launch_i4_block<2, 8>(st, x, ps, K, c, s, map, N, out, ss);
 }
 
