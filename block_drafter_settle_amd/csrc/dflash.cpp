@@ -82,13 +82,14 @@ Split split_big(int ntiles, int steps) {
 // that finishes soonest when the workgroups run in rounds of `slots` (two a
 // compute unit at 4 row blocks, one at 8: their LDS), i.e. the least
 // rounds / S, at most 8 splits (each split writes a whole [rows][N]
-// partial); the smaller S among near ties.
+// partial; caps of 16 and 32 were not faster consistently across boxes);
+// the smaller S among near ties.
 Split split_mb(int ntiles, int units, int MB) {
   const long groups = dfl::mb_groups(ntiles);
-  const long slots = MB == 4 ? 512 : 256;
+  const long slots = MB == 4 ? 512 : 256, cap = 8;
   long S = 1;
   double best = 1e30;
-  for (long c = 1; c <= std::min<long>(8, units); ++c) {
+  for (long c = 1; c <= std::min<long>(cap, units); ++c) {
     const double t = (double)((groups * c + slots - 1) / slots) / c;
     if (t < best * 0.9) {
       best = t;
@@ -1424,14 +1425,16 @@ static int batch_scratch(dflash* d) {
   const size_t R = 16 * dfl::kMaxSeq, hs = d->hs;
   const size_t slots = (size_t)dfl::kMaxSeq * d->nh * (dfl::kAttnMaxChunks + 1);
   // the largest split partial of any batched product
+  // (a pass of B sequences runs MB = 4 or 8 row blocks, 16·MB rows, with the
+  // splits split_mb gives at that MB)
   long part = 0;
   auto f16p = [&](int N, int K) {
-    const Split s = split_mb((N + 15) / 16, K / 32, 4);
-    part = std::max(part, (long)s.S * (long)R * N);
+    for (int MB : {4, 8})
+      part = std::max(part, (long)split_mb((N + 15) / 16, K / 32, MB).S * 16 * MB * N);
   };
   auto i4p = [&](int N, int K) {
-    const Split s = split_mb(N / 16, K / 128, 4);
-    part = std::max(part, (long)s.S * (long)R * N);
+    for (int MB : {4, 8})
+      part = std::max(part, (long)split_mb(N / 16, K / 128, MB).S * 16 * MB * N);
   };
   f16p(d->P, d->hs);
   f16p(d->rank, d->hs);
