@@ -16,7 +16,14 @@ initialisation of such a drafter):
     norm gains and base kernels: f32;
   - tap rows: N(0, 1) f32, optionally with a fixed set of channels scaled
     (1 % of the tap width, x20, for the settle-bound workload);
-  - context stores for block-only tests: N(0, 1) f32 keys and values.
+  - context stores for block-only tests: N(0, 1) f32 keys and values;
+  - router subspaces (`make_subspace`): an orthonormal basis of `rank` rows
+    (the Q factor of an N(0, 1) [hidden][rank] matrix, rows of its
+    transpose) and a mean of N(0, 0.25/hidden) values (norm about 0.5), both
+    rounded to f16 as a sidecar holds them; target rows (`make_route_rows`):
+    N(0, 1), or, for a share of them, a point of a given subspace near the
+    unit sphere (its mean plus N(0, 0.75/rank) coordinates along its basis
+    rows) plus N(0, noise) jitter.
 
 Weight preparation (`quantize_int4`) is the offline conversion the pages
 leave to their converter: scale = f16(max|w| / 7) per 32-column group,
@@ -195,3 +202,32 @@ def uniform_tokens(g: dict, n: int, seed: int = 0, name: str = "anchors") -> lis
     gen = torch.Generator(device="cpu")
     gen.manual_seed(_seed(seed, name))
     return torch.randint(0, g["vocab"], (n,), generator=gen).tolist()
+
+
+def make_subspace(hidden: int, rank: int, seed: int = 0, name: str = "route.block"):
+    """A router subspace as a sidecar holds it: (mean f16 [hidden], basis f16
+    [rank][hidden], rank), torch float16 on the CPU."""
+    mean = _normal(seed, name + ".mean", (hidden,), 0.5 / math.sqrt(hidden), "cpu")
+    if rank:
+        a = _normal(seed, name + ".basis", (hidden, rank), 1.0, "cpu").double()
+        q, _ = torch.linalg.qr(a)
+        basis = q.T.contiguous().float()
+    else:
+        basis = torch.zeros(0, hidden)
+    return mean.to(torch.float16), basis.to(torch.float16), rank
+
+
+def make_route_rows(hidden: int, m: int, seed: int = 0, near=None, share: float = 0.0,
+                    noise: float = 0.01, name: str = "route.rows") -> torch.Tensor:
+    """m target rows f32 [m][hidden]: N(0, 1); the first round(share·m) of
+    them instead a point of subspace `near` (its mean plus N(0, 0.75/rank)
+    coordinates along its basis rows) plus N(0, noise) jitter."""
+    x = _normal(seed, name, (m, hidden), 1.0, "cpu")
+    k = int(round(share * m))
+    if near is not None and k:
+        mean, basis, rank = near
+        coef = _normal(seed, name + ".coef", (k, rank), math.sqrt(0.75 / max(rank, 1)), "cpu")
+        jit = _normal(seed, name + ".jitter", (k, hidden), noise, "cpu")
+        x[:k] = mean.float() + coef @ basis.float() + jit
+    return x
+
