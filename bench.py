@@ -352,6 +352,7 @@ def main():
                                 else (sr["achieved"] / mfma_tfs), 4)
     sr["mfma_frac"] = round(sr["tflops"] / F16_MFMA_PEAK_TFS, 4)
     sr["mfma_frac_measured"] = round(sr["tflops"] / mfma_tfs, 4)
+    res["router"] = leg_route(synth, dev, d, hs)
 
     cpu = None
     if not args.no_cpu:
@@ -414,6 +415,39 @@ def block_flops(g, width, k, nseq):
     kp = 2 * (2 * g["conv_kernel"] * hs // g["conv_group"]) * hs
     per_layer = qd * hs + 2 * kd * hs + hs * qd + 3 * ffn * hs + kp
     return nseq * 2.0 * (rows * L * per_layer + k * width * hs + rows * g["selector_rank"] * hs)
+
+
+def leg_route(synth, dev, d, hs, rank=64, calls=500):
+    """The router margin (dflash_route_margin) of m = 1 and 8 target rows
+    against two synthetic rank-64 subspaces, back to back on the handle's
+    stream."""
+    import torch
+
+    blk_h = synth.make_subspace(hs, rank, seed=9)
+    blk = [blk_h[0].to(dev), blk_h[1].to(dev)]
+    chn = [t.to(dev) for t in synth.make_subspace(hs, rank, seed=9, name="route.chain")[:2]]
+    bp = (blk[0].data_ptr(), blk[1].data_ptr(), rank)
+    cp = (chn[0].data_ptr(), chn[1].data_ptr(), rank)
+    out = {"workload": f"router: Route::margin of m target rows (hidden {hs}) against two "
+                       f"synthetic rank-{rank} subspaces (f16 mean and basis)"}
+    for m in (1, 8):
+        rows = synth.make_route_rows(hs, m, seed=10, near=blk_h, share=0.5).to(dev)
+        mg = torch.empty(m, device=dev)
+        for _ in range(20):
+            d.route_margin(rows.data_ptr(), m, bp, cp, mg.data_ptr())
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(calls):
+            d.route_margin(rows.data_ptr(), m, bp, cp, mg.data_ptr())
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / calls
+        nbytes = m * hs * 4 + 2 * (hs + rank * hs) * 2 + m * 4
+        out[f"m{m}"] = {"us_per_call": round(us, 2), "algorithmic_bytes": nbytes,
+                        "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 5)}
+        log(f"router: m={m}: {us:.2f} us a call")
+    return out
 
 
 def leg_batch(pkg, synth, dev, stream, lead, g, ctx0, lead_pos, k, width, anchors, nb):

@@ -64,6 +64,8 @@ _SIGS = {
     "dflash_create_context": ([C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p], C.c_int),
     "dflash_block_batch": ([C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                             C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
+    "dflash_route_margin": ([C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                             C.c_int32, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p], C.c_int),
     "dflash_queue": ([C.c_void_p, C.c_int64, C.c_int32, C.c_void_p], C.c_int),
     "dflash_flush": ([C.c_void_p], C.c_int),
     "dflash_reserve": ([C.c_void_p, C.c_int64], C.c_int),
@@ -274,6 +276,12 @@ class Drafter:
                       unary_ptr, score_ptr, chosen_ptr):
         _check(lib().dflash_block_noalloc(self.h, anchor, a, k, width, logits_ptr, cand_ptr,
                                           unary_ptr, score_ptr, chosen_ptr), self.h)
+
+    def route_margin(self, rows_ptr, m: int, block, chain, margin_ptr):
+        """dflash_route_margin: block and chain are (mean_ptr, basis_ptr,
+        rank) of device f16 buffers; rows and margin device f32."""
+        _check(lib().dflash_route_margin(self.h, rows_ptr, m, block[0], block[1], block[2],
+                                         chain[0], chain[1], chain[2], margin_ptr), self.h)
 
     def queue(self, first_pos: int, n: int, taps_ptr: int):
         _check(lib().dflash_queue(self.h, first_pos, n, taps_ptr), self.h)

@@ -14,6 +14,7 @@ LIB = os.path.join(HERE, "libdflash.so")
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 SOURCES = [("kernels.hip", []), ("skinny.hip", VGPR_FORM), ("stream.hip", VGPR_FORM),
            ("attention.hip", VGPR_FORM), ("settle.hip", VGPR_FORM), ("batch.hip", VGPR_FORM),
+           ("route.hip", []),
            ("dflash.cpp", [])]
 
 FLAGS = [

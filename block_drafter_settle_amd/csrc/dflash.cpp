@@ -239,6 +239,7 @@ struct dflash {
   int stage_cols = 0;  // widest activation the staging buffer holds
   int last_k = 0;
   float* trace = nullptr;  // per-layer residual copies (debug)
+  float *rt_coef = nullptr, *rt_nrm = nullptr, *rt_part = nullptr;  // router margin scratch
   std::vector<void*> allocs;     // the handle's own device buffers (not the weights)
   std::shared_ptr<WeightOwner> wown;
   BatchScratch bb;
@@ -815,6 +816,13 @@ static int alloc_state(dflash* d) {
   b.sqp = d->sqp;
   if (!rc) rc = dev_alloc(d, &b.sel.tab, (size_t)d->top * (1 + 15 * d->top), "selector table");
   if (!rc) rc = dev_alloc(d, &b.sel.best, (size_t)(1 + 15 * d->top), "selector table");
+  if (!rc)
+    rc = dev_alloc(d, &d->rt_coef, (size_t)dfl::kRouteMaxRows * 2 * dfl::kRouteMaxRank,
+                   "router scratch");
+  if (!rc) rc = dev_alloc(d, &d->rt_nrm, (size_t)dfl::kRouteMaxRows * 2, "router scratch");
+  if (!rc)
+    rc = dev_alloc(d, &d->rt_part, (size_t)dfl::kRouteMaxRows * 2 * dfl::route_chunks(hs),
+                   "router scratch");
   if (!rc) rc = hip_check(nullptr, hipDeviceSynchronize(), "create");
   if (!rc) rc = hip_check(nullptr, hipGetDevice(&d->dev), "create: current device");
   if (!rc) scratch_init(d->dev);
@@ -1648,6 +1656,24 @@ int dflash_block_batch(dflash_t* const* ds, int32_t nseq, const int32_t* anchors
     if (ds[s]->st != d->st && hipStreamWaitEvent(ds[s]->st, d->order, 0) != hipSuccess)
       return fail(d, DFLASH_EHIP, "block_batch: ordering handle %d's stream after the batch", s);
   return DFLASH_OK;
+}
+
+int dflash_route_margin(dflash_t* d, const float* rows, int32_t m, const uint16_t* block_mean,
+                        const uint16_t* block_basis, int32_t block_rank,
+                        const uint16_t* chain_mean, const uint16_t* chain_basis,
+                        int32_t chain_rank, float* margin) {
+  if (!d) return DFLASH_EINVAL;
+  if (!rows || !block_mean || !chain_mean || !margin || (block_rank && !block_basis) ||
+      (chain_rank && !chain_basis))
+    return fail(d, DFLASH_EINVAL, "route_margin: null pointer");
+  if (m < 1 || m > dfl::kRouteMaxRows)
+    return fail(d, DFLASH_EINVAL, "route_margin: m must be in [1, %d]", dfl::kRouteMaxRows);
+  if (block_rank < 0 || block_rank > dfl::kRouteMaxRank || chain_rank < 0 ||
+      chain_rank > dfl::kRouteMaxRank)
+    return fail(d, DFLASH_EINVAL, "route_margin: ranks must be in [0, %d]", dfl::kRouteMaxRank);
+  dfl::route_margin(d->st, rows, m, d->hs, block_mean, block_basis, block_rank, chain_mean,
+                    chain_basis, chain_rank, d->rt_coef, d->rt_nrm, d->rt_part, margin);
+  return launch_check(d, "route_margin");
 }
 
 // --------------------------------------------------------------- debug

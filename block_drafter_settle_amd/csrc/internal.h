@@ -249,4 +249,15 @@ void dequant_i4(hipStream_t st, const uint8_t* codes, const uint16_t* scales, Ti
 void sum_rows(hipStream_t st, const float* part, int splits, long split_stride, int rows, int N,
               float* out);
 
+// Router margin (route.hip): rows dev f32 [m][hidden], each subspace's mean
+// f16 [hidden] and basis f16 [rank][hidden]; scratch coef
+// [kRouteMaxRows][2][kRouteMaxRank], nrm [kRouteMaxRows][2], part
+// [kRouteMaxRows][2][route_chunks(hidden)]; margin dev f32 [m].
+constexpr int kRouteMaxRows = 64, kRouteMaxRank = 256, kRouteMaxHidden = 5120;
+int route_chunks(int hidden);
+void route_margin(hipStream_t st, const float* rows, int m, int hidden, const uint16_t* bmean,
+                  const uint16_t* bbasis, int brank, const uint16_t* cmean,
+                  const uint16_t* cbasis, int crank, float* coef, float* nrm, float* part,
+                  float* margin);
+
 }  // namespace dfl

@@ -224,6 +224,27 @@ int dflash_block_batch(dflash_t* const* d, int32_t nseq, const int32_t* anchors,
                        int32_t k, int32_t width, float* logits, int32_t* cand, float* unary,
                        float* score, int32_t* chosen);
 
+/* ---- router ---------------------------------------------------------------- */
+
+/* The router margin (`Route::margin` on the docs.rs page
+   "cortiq_engine/dflash.rs"): which drafter a round is for. For each of m
+   target rows x at the tip (dev f32 [m][hidden], the handle's hidden),
+   u = x / max(‖x‖, 1e-12); for each subspace (mean dev f16 [hidden], basis
+   dev f16 [rank][hidden] row-major, as the sidecar's fit holds them)
+   err = ‖d − Σ_{r<rank} ⟨d, b_r⟩ b_r‖₂ with d = u − mean (the page names
+   this reconstruction error without printing it: the residual's norm after
+   removing d's components along the basis rows, the distance to the affine
+   subspace for orthonormal rows); margin[i] = err(chain) − err(block),
+   dev f32 [m]: above zero the round is the block drafter's. Requires
+   1 ≤ m ≤ 64, ranks in [0, 256] (a basis may be NULL at rank 0). Runs on
+   the handle's stream with the handle's own scratch (calls on one handle
+   are ordered by its stream); changes no state. DFLASH_EINVAL for null
+   pointers or sizes out of range. */
+int dflash_route_margin(dflash_t* d, const float* rows, int32_t m, const uint16_t* block_mean,
+                        const uint16_t* block_basis, int32_t block_rank,
+                        const uint16_t* chain_mean, const uint16_t* chain_basis,
+                        int32_t chain_rank, float* margin);
+
 /* Forget the context from position pos on (`truncate`), waiting rows
    included; a layer that had dropped rows past pos holds none. */
 int dflash_truncate(dflash_t* d, int64_t pos);
