@@ -7,6 +7,11 @@
 // the residual's norm after removing the components along the basis rows);
 // margin = err(chain) − err(block).
 //
+// Grids put the row last (blockIdx.y) and the (subspace, basis part) first,
+// padded to a multiple of 8: consecutive workgroups go to the 8 XCDs in
+// turn, so every row's workgroup for one part of a basis lands on the same
+// XCD and the basis is fetched into its L2 once, not once per row.
+//
 // Three launches, all sums in a fixed order:
 //   k_route_coef   block (row, subspace, 16 basis rows): ‖x‖, d in LDS, and
 //                  each wave's four c_r (a lane takes 8 channels a step, in
@@ -46,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void k_route_coef(const float* __restrict
                                                          float* __restrict__ nrm) {
   __shared__ float d[kRouteMaxHidden];
   __shared__ float red[4];
-  const int m = blockIdx.x, s = blockIdx.y, z = blockIdx.z;
+  const int m = blockIdx.y, s = blockIdx.x & 1, z = blockIdx.x >> 1;
   const RouteSub& sub = route_sub(blk, chn, s);
   const float* row = rows + (size_t)m * hidden;
   const float n = route_norm(row, hidden, red);
@@ -83,7 +88,8 @@ __global__ __launch_bounds__(kThreads) void k_route_resid(const float* __restric
                                                           float* __restrict__ part, int nchunk) {
   __shared__ float c[kRouteMaxRank];
   __shared__ float red[4];
-  const int m = blockIdx.x, s = blockIdx.y, ch = blockIdx.z;
+  const int m = blockIdx.y, s = blockIdx.x & 1, ch = blockIdx.x >> 1;
+  if (ch >= nchunk) return;  // padding of the grid (whole workgroup)
   const RouteSub& sub = route_sub(blk, chn, s);
   for (int r = threadIdx.x; r < sub.rank; r += kThreads)
     c[r] = coef[(size_t)(m * 2 + s) * kRouteMaxRank + r];
@@ -136,9 +142,11 @@ void route_margin(hipStream_t st, const float* rows, int m, int hidden, const ui
                    crank};
   const int rz = std::max(1, (int)cdiv(std::max(brank, crank), kRouteRowsPerBlock));
   const int nchunk = route_chunks(hidden);
-  k_route_coef<<<dim3(m, 2, rz), kThreads, 0, st>>>(rows, hidden, b, c, coef, nrm);
-  k_route_resid<<<dim3(m, 2, nchunk), kThreads, 0, st>>>(rows, hidden, b, c, coef, nrm, part,
-                                                         nchunk);
+  const unsigned pad8 = 8;
+  k_route_coef<<<dim3(cdiv(2 * rz, pad8) * pad8, m), kThreads, 0, st>>>(rows, hidden, b, c, coef,
+                                                                       nrm);
+  k_route_resid<<<dim3(cdiv(2 * nchunk, pad8) * pad8, m), kThreads, 0, st>>>(
+      rows, hidden, b, c, coef, nrm, part, nchunk);
   k_route_final<<<m, 64, 0, st>>>(part, nchunk, margin);
 }
 
