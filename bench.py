@@ -282,7 +282,7 @@ def main():
                         "[2048x4,0], layer 4 no_rope), 32768 settled positions, each step settles "
                         "8 new tap rows then drafts one block (k=15, width=vocab) at the next anchor",
             "weights": "int4 g32 f16-scale q/k/v/o/gate/up/down; f16 fc/kproj/head/selector; "
-                       "f32 context KV; f16 MFMA operands, f32 accumulate",
+                       "f32 context K/V held as f16 hi/lo pairs; f16 MFMA operands, f32 accumulate",
             "block_rows": g["block"], "k": k, "width": width, "context": ctx0,
             "settle_rows_per_step": per_step,
         },
@@ -325,7 +325,7 @@ def main():
                 "unit": "GB/s" if fc_bound == "hbm" else "TFLOP/s",
                 "frac": round((fc_bytes / (fc_us * 1e-6) / 1e9 / HBM_PEAK_GBS) if fc_bound == "hbm"
                               else (fc_flops / (fc_us * 1e-6) / 1e12 / F16_MFMA_PEAK_TFS), 4),
-                "traffic": None,
+                "traffic": fc_traffic(),
                 "us_per_launch": round(fc_us, 2),
                 "bytes_per_launch": int(fc_bytes),
                 "flops_per_launch": fc_flops,
@@ -681,17 +681,43 @@ def head_source_sha1():
     return hashlib.sha1(src[a:b].encode()).hexdigest()
 
 
-def head_traffic():
-    """HBM bytes per k_head launch from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, each scaled by the plain copy's reading), or
-    None when there is none or the kernel changed since it was taken."""
+def _source_sha1(start, end):
+    """sha1 of kernels.hip's text from the line `start` to the line `end`."""
+    import hashlib
+
+    src = open(KERNELS).read()
+    a = src.find(start)
+    b = src.find(end, a + 1)
+    if a < 0 or b < a:
+        return None
+    return hashlib.sha1(src[a:b].encode()).hexdigest()
+
+
+def _traffic(path, sha):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, each scaled by the plain copy's reading), or None when there
+    is none or the kernel changed since it was taken."""
     try:
-        fields = dict(l.split(":", 1) for l in open(HEAD_TRAFFIC) if ":" in l and not l.startswith("#"))
+        fields = dict(l.split(":", 1) for l in open(path) if ":" in l and not l.startswith("#"))
     except OSError:
         return None
-    if fields.get("kernel_source_sha1", "").strip() != head_source_sha1():
+    if sha is None or fields.get("kernel_source_sha1", "").strip() != sha:
         return None
     return int(float(fields["traffic_bytes_per_launch"]))
+
+
+def head_traffic():
+    return _traffic(HEAD_TRAFFIC, head_source_sha1())
+
+
+FC_TRAFFIC = os.path.join(ROOT, "profiles", "k_gemm_big_f16_27b_settle_traffic.txt")
+
+
+def fc_traffic():
+    """The settle fc kernel's (k_gemm_big_f16 at 256 rows) counter traffic."""
+    return _traffic(FC_TRAFFIC, _source_sha1(
+        "// Many-row GEMM, f16 weights, two activation planes",
+        "template <int R, int PL>\n__global__ __launch_bounds__(kThreads) void k_gemm_i4("))
 
 
 def cpu_baseline(g, w, synth, steps):
