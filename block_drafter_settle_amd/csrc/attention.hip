@@ -45,11 +45,13 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
   __shared__ f16 Ks[2][32 * KST];
   __shared__ f16 Vt[2][HD * VST];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = blockIdx.x, c = blockIdx.y;
+  // the block's own keys first (y = 0, a short workgroup that then does not
+  // trail the context chunks), then context chunk y − 1
+  const int g = blockIdx.x, c = blockIdx.y == 0 ? seqs.s[blockIdx.z / nzq].nchunks : blockIdx.y - 1;
   const int sq = blockIdx.z / nzq;
   const AttnSeq& cs = seqs.s[sq];
   const int n = cs.n, chunk = cs.chunk, nchunks = cs.nchunks;
-  if (c > nchunks) return;  // whole workgroup
+  if (blockIdx.y > 0 && c >= nchunks) return;  // whole workgroup
   const f16* __restrict__ sk = reinterpret_cast<const f16*>(cs.sk);
   const f16* __restrict__ sv = reinterpret_cast<const f16*>(cs.sv);
   const long cap = cs.cap, s0 = cs.s0, lo_pos = cs.lo, a = cs.a;
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
 // y = Σ_c acc_c·2^{m_c − M} / Σ_c l_c·2^{m_c − M}, M the largest chunk max
 // (the chunk states are kept in base 2).
 // The threads form the chunk weights (chunks strided over the block), then
-// one thread per dimension sums.
+// 256 / hd groups of hd threads each sum a strided share of the chunks.
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pacc,
                                                     const float2* __restrict__ pml, int nh,
                                                     int kv, int hd, SeqChunks sc,
@@ -270,19 +272,25 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   __syncthreads();
   float L = 0.f;
   for (int w = 0; w < nw; ++w) L += redl[w];
-  if (t >= hd) return;
-  float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
-  const float* pc = pacc + (slot0 * 16 + r) * hd + t;
+  // thread (grp, d): dimension d of chunks grp, grp + G, … (G = blockDim / hd
+  // groups), eight loads in flight; the groups' sums meet in LDS in order
+  const int G = blockDim.x / hd, grp = t / hd, d = t - grp * hd;
+  const float* pc = pacc + (slot0 * 16 + r) * hd + d;
   const size_t cs = (size_t)rep * 16 * hd;  // chunk stride
-  int c = 0;
-  for (; c + 4 <= nc; c += 4) {
-    y0 += pc[(size_t)c * cs] * fw[c];
-    y1 += pc[(size_t)(c + 1) * cs] * fw[c + 1];
-    y2 += pc[(size_t)(c + 2) * cs] * fw[c + 2];
-    y3 += pc[(size_t)(c + 3) * cs] * fw[c + 3];
-  }
-  for (; c < nc; ++c) y0 += pc[(size_t)c * cs] * fw[c];
-  put_a(ya, ps, a_idx(r, hq * hd + t), ((y0 + y1) + (y2 + y3)) / L);
+  float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int c = grp;
+  for (; c + 7 * G < nc; c += 8 * G)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] += pc[(size_t)(c + k * G) * cs] * fw[c + k * G];
+  for (int k = 0; c < nc; c += G, ++k) y[k & 7] += pc[(size_t)c * cs] * fw[c];
+  const float ys = ((y[0] + y[1]) + (y[2] + y[3])) + ((y[4] + y[5]) + (y[6] + y[7]));
+  __shared__ float part[256];
+  part[t] = ys;
+  __syncthreads();
+  if (grp) return;
+  float yt = part[d];
+  for (int q = 1; q < G; ++q) yt += part[q * hd + d];
+  put_a(ya, ps, a_idx(r, hq * hd + d), yt / L);
 }
 
 static inline unsigned cdiv(long a, long b) { return (unsigned)((a + b - 1) / b); }
@@ -314,8 +322,8 @@ void attn_merge(hipStream_t st, const float* pacc, const float* pml, int nh, int
   dim3 grid(nh, B, nseq);
   SeqChunks sc{};
   for (int i = 0; i < nseq; ++i) sc.n[i] = seqs.s[i].nchunks;
-  k_attn_merge<<<grid, hd, 0, st>>>(pacc, reinterpret_cast<const float2*>(pml), nh, kv, hd, sc,
-                                    reinterpret_cast<f16*>(ya), ps);
+  k_attn_merge<<<grid, 256, 0, st>>>(pacc, reinterpret_cast<const float2*>(pml), nh, kv, hd, sc,
+                                     reinterpret_cast<f16*>(ya), ps);
 }
 
 }  // namespace dfl

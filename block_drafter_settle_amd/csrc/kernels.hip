@@ -1113,21 +1113,71 @@ __global__ __launch_bounds__(256) void k_pairs(const float* __restrict__ lv,
     cand[(size_t)j * top + t] = uc[0][t];
     unary[(size_t)j * top + t] = uv[0][t];
   }
-  for (int e = t; e < np * rank; e += 256) {
-    const int pi = e / rank, q = e - pi * rank;
-    const int prev = j == 0 ? anchor : (forced ? forced[j] : uc[1][pi]);
-    const bool ok = prev >= 0 && prev < vocab;
-    ph[pi][q] = ok ? (float)pbook[(size_t)prev * rank + q] * hp[(size_t)j * rank + q] : 0.f;
-  }
   const int rh = (rank + 1) >> 1;
-  for (int e = t; e < top * rh; e += 256) {
-    const int u = e / rh, q = 2 * (e - u * rh);
-    const int tok = uc[0][u];
-    const bool ok = tok >= 0 && tok < vocab;
-    const f16* cr = cbook + (size_t)(ok ? tok : 0) * rank;
-    const f16 c0 = ok ? cr[q] : (f16)0.f, c1 = ok && q + 1 < rank ? cr[q + 1] : (f16)0.f;
-    cw[u][q >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, c0) |
-                    ((uint32_t)__builtin_bit_cast(uint16_t, c1) << 16);
+  if ((rank & 7) == 0) {
+    // 16-byte pieces of the rows (8 values), every thread's loads issued
+    // before any is used: one round trip for the codebook gathers
+    constexpr int kMaxPer = kSelTop * kSelRank / 8 / 256;  // pieces a thread, at most
+    const int r8 = rank >> 3;
+    uint4 pv[kMaxPer], cv[kMaxPer];
+    float4 h0[kMaxPer], h1[kMaxPer];
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      const int e = t + 256 * i;
+      if (e < np * r8) {
+        const int pi = e / r8, q0 = 8 * (e - pi * r8);
+        const int prev = j == 0 ? anchor : (forced ? forced[j] : uc[1][pi]);
+        const bool ok = prev >= 0 && prev < vocab;
+        pv[i] = ok ? *reinterpret_cast<const uint4*>(pbook + (size_t)prev * rank + q0)
+                   : make_uint4(0, 0, 0, 0);
+        h0[i] = *reinterpret_cast<const float4*>(hp + (size_t)j * rank + q0);
+        h1[i] = *reinterpret_cast<const float4*>(hp + (size_t)j * rank + q0 + 4);
+      }
+      if (e < top * r8) {
+        const int u = e / r8, q0 = 8 * (e - u * r8);
+        const int tok = uc[0][u];
+        cv[i] = tok >= 0 && tok < vocab
+                    ? *reinterpret_cast<const uint4*>(cbook + (size_t)tok * rank + q0)
+                    : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      const int e = t + 256 * i;
+      if (e < np * r8) {
+        const int pi = e / r8, q0 = 8 * (e - pi * r8);
+        const uint32_t w[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+        const float hv[8] = {h0[i].x, h0[i].y, h0[i].z, h0[i].w, h1[i].x, h1[i].y, h1[i].z, h1[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          ph[pi][q0 + 2 * k] = half_bits(w[k]) * hv[2 * k];
+          ph[pi][q0 + 2 * k + 1] = half_bits(w[k] >> 16) * hv[2 * k + 1];
+        }
+      }
+      if (e < top * r8) {
+        const int u = e / r8, q2 = 4 * (e - u * r8);
+        cw[u][q2] = cv[i].x;
+        cw[u][q2 + 1] = cv[i].y;
+        cw[u][q2 + 2] = cv[i].z;
+        cw[u][q2 + 3] = cv[i].w;
+      }
+    }
+  } else {
+    for (int e = t; e < np * 2 * rh; e += 256) {  // an odd rank's last pair padded with 0
+      const int pi = e / (2 * rh), q = e - pi * 2 * rh;
+      const int prev = j == 0 ? anchor : (forced ? forced[j] : uc[1][pi]);
+      const bool ok = q < rank && prev >= 0 && prev < vocab;
+      ph[pi][q] = ok ? (float)pbook[(size_t)prev * rank + q] * hp[(size_t)j * rank + q] : 0.f;
+    }
+    for (int e = t; e < top * rh; e += 256) {
+      const int u = e / rh, q = 2 * (e - u * rh);
+      const int tok = uc[0][u];
+      const bool ok = tok >= 0 && tok < vocab;
+      const f16* cr = cbook + (size_t)(ok ? tok : 0) * rank;
+      const f16 c0 = ok ? cr[q] : (f16)0.f, c1 = ok && q + 1 < rank ? cr[q + 1] : (f16)0.f;
+      cw[u][q >> 1] = (uint32_t)__builtin_bit_cast(uint16_t, c0) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, c1) << 16);
+    }
   }
   __syncthreads();
   // entry (p, u): threads of a wave share p and take consecutive u
@@ -1135,14 +1185,24 @@ __global__ __launch_bounds__(256) void k_pairs(const float* __restrict__ lv,
     const int pi = e / top, u = e - pi * top;
     const int prev = j == 0 ? anchor : (forced ? forced[j] : uc[1][pi]);
     const int tok = uc[0][u];
-    float d0 = 0.f, d1 = 0.f;
-    for (int q2 = 0; q2 < rh; ++q2) {
+    // eight partial sums, so that the LDS reads of four pairs are in flight
+    float dp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int q2 = 0;
+    for (; q2 + 4 <= rh; q2 += 4)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w = cw[u][q2 + k];
+        dp[2 * k] += ph[pi][2 * (q2 + k)] * half_bits(w);
+        dp[2 * k + 1] += ph[pi][2 * (q2 + k) + 1] * half_bits(w >> 16);
+      }
+    for (int k = 0; q2 < rh; ++q2, ++k) {
       const uint32_t w = cw[u][q2];
-      d0 += ph[pi][2 * q2] * half_bits(w);
-      d1 += (2 * q2 + 1 < rank ? ph[pi][2 * q2 + 1] : 0.f) * half_bits(w >> 16);
+      dp[2 * k] += ph[pi][2 * q2] * half_bits(w);
+      dp[2 * k + 1] += ph[pi][2 * q2 + 1] * half_bits(w >> 16);
     }
+    const float dot = ((dp[0] + dp[1]) + (dp[2] + dp[3])) + ((dp[4] + dp[5]) + (dp[6] + dp[7]));
     const bool ok = prev >= 0 && prev < vocab && tok >= 0 && tok < vocab;
-    const float score = ok ? uv[0][u] + (d0 + d1) : -INFINITY;
+    const float score = ok ? uv[0][u] + dot : -INFINITY;
     sc[pi][u] = score;
     const size_t trow = j == 0 ? 0 : 1 + (size_t)(j - 1) * tpn + pi;
     tab[trow * top + u] = score;
