@@ -100,9 +100,9 @@ typedef struct {
 
 /* Build a drafter: validate the geometry, copy every weight to device memory
    (int4 and f16 matrices repacked into the kernels' tile layouts), allocate
-   each windowed layer's context ring (min(2·window, max_context) rows of f32
-   [kv_heads][head_dim] keys and values: the rows a layer holds never exceed
-   that, see dflash_settle), the ring of waiting tap rows (see dflash_queue)
+   each windowed layer's context ring (min(2·window, max_context) rows of
+   [kv_heads][head_dim] f32 keys and values, each held as its f16 pair: the
+   rows a layer holds never exceed that, see dflash_settle), the ring of waiting tap rows (see dflash_queue)
    and all scratch. A layer without a window gets its store as rows come
    (dflash_reserve). Synchronous: the caller may free every host array
    once it returns. `stream` is a hipStream_t (NULL = the null stream) that
@@ -117,7 +117,8 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* strea
    the order of the geometry's taps) become context, after any rows that
    wait (dflash_queue): t = rms(fc·row, hidden_norm); per layer K =
    rot(rms(Wk·t per kv head, k_norm), position) (no rotation on a no-rope
-   layer), V = Wv·t, stored f32.
+   layer), V = Wv·t, stored as f32 values (each held as its f16 pair
+   hi = f16(x), lo = f16(x − hi), the form the attention multiplies).
    Position rule (`queue_context`): with first ≤ first_pos ≤ the span's end
    (waiting rows included) the context is cut at first_pos and the rows
    appended; otherwise (a gap, or first_pos < first) it restarts at
@@ -339,14 +340,17 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
 
 /* Copy the rows of positions first+row0 .. first+row0+n−1 from layer's
    store (rows the layer holds: dropped ≤ row0, row0 + n ≤ settled):
-   k_out, v_out dev f32 [n][kv_heads*head_dim]. */
+   k_out, v_out dev f32 [n][kv_heads*head_dim]. The store keeps each f32
+   value x as its f16 pair (hi = f16(x), lo = f16(x − hi)), the form the
+   attention multiplies; a read returns hi + lo. */
 int dflash_debug_read_store(dflash_t* d, int32_t layer, int64_t row0, int64_t n, float* k_out,
                             float* v_out);
 
 /* Replace the context with `len` given rows at positions first..first+len−1,
    as if one settle had made them on an empty context (waiting rows go;
    each windowed layer then drops rows as after a settle): k[l], v[l] (host
-   array of `layers` dev pointers) dev f32 [len][kv*hd]. */
+   array of `layers` dev pointers) dev f32 [len][kv*hd], each value stored
+   as its f16 pair like a settled one. */
 int dflash_debug_load_store(dflash_t* d, int64_t first, int64_t len, const float* const* k,
                             const float* const* v);
 
