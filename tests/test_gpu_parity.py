@@ -372,9 +372,12 @@ def test_block_is_deterministic(small):
 
 # ----------------------------------------------------------------- select
 
+# (top, rank): the staged codebook rows in 16-byte pieces (rank a multiple of
+# 8), at the largest top and rank; and the element-wise path (rank 20)
+@pytest.mark.parametrize("top,rank", [(16, 32), (32, 256), (7, 20)])
 @pytest.mark.parametrize("strong", [False, True])
-def test_select_parity(orc, strong):
-    g = synth.small_geometry(vocab=5000, mask_token=4999, selector_top=16, selector_rank=32)
+def test_select_parity(orc, strong, top, rank):
+    g = synth.small_geometry(vocab=5000, mask_token=4999, selector_top=top, selector_rank=rank)
     w, d = make(g, seed=6, max_context=8)
     try:
         dev = _dev()

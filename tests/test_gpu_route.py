@@ -65,7 +65,7 @@ def _rows(hidden, m, blk, chn, seed):
 
 @pytest.mark.parametrize("hidden,m,rb,rc", [(256, 1, 16, 16), (256, 7, 0, 5), (256, 64, 256, 3),
                                            (256, 12, 40, 40), (5120, 8, 64, 64),
-                                           (5120, 3, 17, 200)])
+                                           (5120, 3, 17, 200), (5120, 64, 256, 256)])
 def test_route_margin_matches_oracle(hidden, m, rb, rc):
     d = _handle(hidden)
     try:
