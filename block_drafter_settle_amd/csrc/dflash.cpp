@@ -633,6 +633,11 @@ int attn_chunk(long n, int* nchunks) {
   // merge traffic than they gain in parallelism
   long c = std::max(128L, (n + dfl::kAttnMaxChunks - 1) / dfl::kAttnMaxChunks);
   c = (c + 31) / 32 * 32;
+  // Longer chunks take an odd number of 32-key steps: the workgroups walk
+  // their chunks in step, and chunks a power of two of rows apart would have
+  // them all at the same offset within equal-sized address blocks at once
+  // (measured: a pure read of the pattern goes from 6.57 to 6.92 TB/s).
+  if (c > 128 && (c / 32) % 2 == 0) c += 32;
   *nchunks = (int)((n + c - 1) / c);
   return (int)c;
 }

@@ -288,6 +288,9 @@ BLOCK_CASES = [
     # 64 context chunks + the block's own rows: more chunk states than merge
     # threads at head_dim 64
     (dict(windows=[0, 0], no_rope=[]), (0, 8190), 0, 7, 1000),
+    # chunks longer than 128 keys take an odd number of 32-key steps (352
+    # here: 57 chunks, the last one short)
+    (dict(windows=[0, 0], no_rope=[]), (0, 20000), 0, 7, 1000),
     # conv kernels other than 4 taps: one tap; more taps than the conv
     # kernels load ahead of their barrier (4), with wider groups; a tap for
     # every block row
