@@ -257,12 +257,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa
 // head_groups, the selector projection of all 16 rows (hp [16][rank]).
 // Head blocks also record, per draft row, the largest logit of each 256
 // columns (gmax [k][ceil(width/256)]) for the selection's threshold, and
-// block 0 clears the selection's candidate counters. Each wave covers kHeadR
-// 16-column tiles, which share every A fragment it loads; the weights are
-// read with non-temporal loads.
-static constexpr int kHeadR = 8;
-
-template <int PL>
+// block 0 clears the selection's candidate counters. Each wave covers R
+// 16-column tiles, which share every A fragment it loads, and keeps 32 weight
+// fragments in flight (32 / R steps of its R tiles); the weights are read
+// with non-temporal loads.
+template <int PL, int R>
 __global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, long ps, int K,
                                                    const f16* __restrict__ head, int wtiles,
                                                    int width, int k, float* __restrict__ logits,
@@ -271,10 +270,10 @@ __global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, l
                                                    int head_groups, int ngroups,
                                                    float* __restrict__ gmax,
                                                    int* __restrict__ counters) {
-  static_assert(kHeadR == 4 || kHeadR == 8, "256-column groups are whole waves");
-  constexpr int kWpg = 16 / kHeadR;  // waves per 256 columns
+  static_assert(R == 4 || R == 8, "256-column groups are whole waves");
+  constexpr int kWpg = 16 / R;  // waves per 256 columns
   constexpr int kGpb = 4 / kWpg;     // 256-column groups per block
-  constexpr int R = kHeadR;
+  constexpr int U = 32 / R;     // steps a round
   __shared__ float wm[4][16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool is_sel = (int)blockIdx.x >= head_groups;
@@ -294,17 +293,17 @@ __global__ __launch_bounds__(kThreads) void k_head(const f16* __restrict__ xa, l
     for (int r = 0; r < R; ++r)
       wp[r] = reinterpret_cast<const h8*>(w) + (size_t)min(t0 + r, ntiles - 1) * KS * 64 + lane;
     int s = 0;
-    for (; s + 4 <= KS; s += 4) {
-      h8 a[4], a2[4], b[4][R];
+    for (; s + U <= KS; s += U) {
+      h8 a[U], a2[U], b[U][R];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < U; ++u) {
         a[u] = xp[(size_t)(s + u) * 64];
         if (PL == 2) a2[u] = xq[(size_t)(s + u) * 64];
 #pragma unroll
         for (int r = 0; r < R; ++r) b[u][r] = ld_stream(&wp[r][(size_t)(s + u) * 64]);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           acc[r] = mfma16(a[u], b[u][r], acc[r]);
@@ -1400,21 +1399,40 @@ void gemm_i4(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks, co
     launch_i4<2, 1>(st, xa, 0, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
 }
 
+// Eight tiles a wave need at least this many workgroups (one a compute
+// unit); a narrower head (a shortlisted width: 65536 columns give 128) takes
+// four tiles a wave and twice the workgroups, which measured 912 -> 842 us a
+// 27B block at width 65536.
+static constexpr int kHeadMinGroups = 256;
+
 void head_sel(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t* head, int width,
               int k, float* logits, const uint16_t* sel, int rank, float* hp, SelectScratch sc) {
   const int wtiles = cdiv(width, 16), stiles = cdiv(rank, 16);
-  const int hg = cdiv(wtiles, 4 * kHeadR), sg = cdiv(stiles, 4 * kHeadR);
   const f16* x = reinterpret_cast<const f16*>(xa);
   const f16* hw = reinterpret_cast<const f16*>(head);
   const f16* sw = reinterpret_cast<const f16*>(sel);
-  if (ps)
-    k_head<2><<<hg + sg, kThreads, 0, st>>>(x, ps, K, hw, wtiles, width, k, logits, sw, stiles,
-                                            rank, hp, hg, cdiv(width, 256), sc.gmax,
-                                            sc.counters);
-  else
-    k_head<1><<<hg + sg, kThreads, 0, st>>>(x, 0, K, hw, wtiles, width, k, logits, sw, stiles,
-                                            rank, hp, hg, cdiv(width, 256), sc.gmax,
-                                            sc.counters);
+  // eight tiles a wave while that still gives every compute unit a
+  // workgroup, else four (a shortlisted width)
+  const bool r8 = cdiv(wtiles, 4 * 8) >= kHeadMinGroups;
+  const int R = r8 ? 8 : 4;
+  const int hg = cdiv(wtiles, 4 * R), sg = cdiv(stiles, 4 * R);
+  const unsigned g = hg + sg;
+  const int ng = cdiv(width, 256);
+  if (ps) {
+    if (r8)
+      k_head<2, 8><<<g, kThreads, 0, st>>>(x, ps, K, hw, wtiles, width, k, logits, sw, stiles,
+                                           rank, hp, hg, ng, sc.gmax, sc.counters);
+    else
+      k_head<2, 4><<<g, kThreads, 0, st>>>(x, ps, K, hw, wtiles, width, k, logits, sw, stiles,
+                                           rank, hp, hg, ng, sc.gmax, sc.counters);
+  } else {
+    if (r8)
+      k_head<1, 8><<<g, kThreads, 0, st>>>(x, 0, K, hw, wtiles, width, k, logits, sw, stiles,
+                                           rank, hp, hg, ng, sc.gmax, sc.counters);
+    else
+      k_head<1, 4><<<g, kThreads, 0, st>>>(x, 0, K, hw, wtiles, width, k, logits, sw, stiles,
+                                           rank, hp, hg, ng, sc.gmax, sc.counters);
+  }
 }
 
 void to_a(hipStream_t st, const RowSrc& x, int m, int K, uint16_t* xa, long ps) {

@@ -39,9 +39,12 @@ def drafter(g, w, cap):
     return pkg.Drafter(g, w, max_context=cap, stream=torch.cuda.current_stream(_dev()).cuda_stream)
 
 
-@pytest.mark.parametrize("name,ctx,k", [("t27b", 32768, 15), ("qwen3_4b", 4096, 15),
-                                        ("t27b_long", 131072, 15)])
-def test_full_block_over_synthetic_store(orc, name, ctx, k):
+# width None: the full vocabulary; 65536: the shortlisted head (the first
+# 65536 columns), which runs the head at four tiles a wave
+@pytest.mark.parametrize("name,ctx,k,width", [("t27b", 32768, 15, None), ("t27b", 32768, 15, 65536),
+                                              ("qwen3_4b", 4096, 15, None),
+                                              ("t27b_long", 131072, 15, None)])
+def test_full_block_over_synthetic_store(orc, name, ctx, k, width):
     g, w = sidecar(name)
     dev = _dev()
     store = synth.make_store(g, ctx, seed=1, device=dev)
@@ -52,8 +55,9 @@ def test_full_block_over_synthetic_store(orc, name, ctx, k):
                            [s[1].data_ptr() for s in store])
         a = first + ctx
         anchor = synth.uniform_tokens(g, 1, seed=3)[0]
-        width = g["vocab"]
-        print(f"{name}: block at a={a} over {ctx} positions, width {width}", flush=True)
+        width = width or g["vocab"]
+        tag = name if width == g["vocab"] else f"{name} width {width}"
+        print(f"{tag}: block at a={a} over {ctx} positions, width {width}", flush=True)
         trace = torch.zeros(g["layers"], g["block"], g["hidden"], device=dev)
         d.debug_set_trace(trace.data_ptr())
         got = run_block(d, g, anchor, a, k, width)
@@ -68,11 +72,11 @@ def test_full_block_over_synthetic_store(orc, name, ctx, k):
             print(f"{name} layer {l}: residual max|ref| {np.abs(ref['trace'][l]).max():.3e} "
                   f"max|err| {e.max():.3e} rows {np.round(e.max(axis=1) / np.abs(ref['trace'][l]).max(), 5).tolist()}",
                   flush=True)
-        close(got["hidden"], ref["hidden"], f"{name} hidden")
-        close(got["logits"], ref["logits"], f"{name} logits")
-        close(got["hp"], ref["hp"], f"{name} hp")
+        close(got["hidden"], ref["hidden"], f"{tag} hidden")
+        close(got["logits"], ref["logits"], f"{tag} logits")
+        close(got["hp"], ref["hp"], f"{tag} hp")
         sel = m.select(ref["logits"], ref["hp"], anchor)
-        check_selection(got, ref["logits"], sel, name,
+        check_selection(got, ref["logits"], sel, tag,
                         forced=forced_select(d, g, got, k, width, anchor))
     finally:
         d.close()
