@@ -434,6 +434,7 @@ long partial_need(const dflash* d) {
     need = std::max(need, (long)dfl::i4_block_splits(K, ks) * 16 * N);
   };
   i4b(d->qd + 2 * d->kd, d->hs, kKsQkv);
+  i4b(d->L * 2 * d->kd, d->hs, kKsQkv);  // a one-block settle's K/V
   i4b(d->hs, d->qd, kKsO);
   i4b(d->hs, d->ffn, kKsDown);
   for (int N : {d->qd, d->kd, d->ffn}) i4b(N, d->hs, 2);
@@ -1066,14 +1067,16 @@ static int settle_pass(dflash* d, const dfl::RowSrc& taps, int m, long pos0, lon
   tm_mark(d, DFLASH_ST_S_TAPS);
   // t = fc · taps (f32 partials), then rms by hidden_norm into A-layout
   const dfl::TileMap fmap{d->hs / 16, d->hs / 16, 0, 0};
+  // one 16-row block (the stream's few-row settles): the block pass's
+  // 16-row kernels, every weight load of a workgroup issued at once
   const Split sf = mb > 1 ? split_big(d->hs / 16, d->tw / 32)
-                          : split_for(d->hs / 16, kR, d->tw / 32, mb, 16);
+                          : Split{dfl::f16_block_splits(d->tw), 0};
   const long ssf = (long)mb * 16 * d->hs;
   if (mb > 1)
     dfl::gemm_big_f16(st, d->taps_a, pst, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part,
                       ssf);
   else
-    dfl::gemm_f16(st, d->taps_a, pst, d->tw, mb, d->fc, fmap, d->hs, sf.S, sf.per, d->part, ssf);
+    dfl::gemm_f16_block(st, d->taps_a, pst, d->tw, d->fc, fmap, d->hs, d->part, ssf);
   tm_mark(d, DFLASH_ST_S_FC);
   // the hidden norm folded: t ⊙ hidden_norm feeds the K/V projection, and
   // settle_kv applies each row's rms scale to its output
@@ -1089,10 +1092,14 @@ static int settle_pass(dflash* d, const dfl::RowSrc& taps, int m, long pos0, lon
     sk = split_kv(d->L * kvt, d->hs / 128);
     dfl::gemm_kv_i4(st, d->t_a, psh, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per,
                     d->part, ssk);
-  } else {
+  } else if (mb > 1) {
     sk = split_for(d->L * kvt, kR, d->hs / 128, mb, 4);
     dfl::gemm_i4(st, d->t_a, psh, d->hs, mb, d->qkv.codes, d->qkv.scales, map, N, sk.S, sk.per,
                  d->part, ssk);
+  } else {
+    sk = {dfl::i4_block_splits(d->hs, kKsQkv), 0};
+    dfl::gemm_i4_block(st, d->t_a, psh, d->hs, d->qkv.codes, d->qkv.scales, map, N, 2, kKsQkv,
+                       d->part, ssk);
   }
   tm_mark(d, DFLASH_ST_S_KV);
   dfl::settle_kv(st, d->part, sk.S, ssk, m, d->L, d->kv, d->hd, d->k_norm, d->inv, d->rot_dev,
