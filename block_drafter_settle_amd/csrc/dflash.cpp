@@ -416,10 +416,6 @@ int upload_i4(dflash* d, I4Set& s, int l, std::initializer_list<std::pair<const 
 // Largest GEMM partial buffer (floats) any call can need.
 long partial_need(const dflash* d) {
   long need = 0;
-  auto f16 = [&](int N, int K, int mb, int R) {
-    const Split s = split_for((N + 15) / 16, R, K / 32, mb, 16);
-    need = std::max(need, (long)s.S * mb * 16 * N);
-  };
   auto i4 = [&](int N, int K, int mb, int R) {
     const Split s = split_for(N / 16, R, K / 128, mb, 4);
     need = std::max(need, (long)s.S * mb * 16 * N);
@@ -453,10 +449,7 @@ long partial_need(const dflash* d) {
       need = std::max(need, (long)s2.S * mb * 16 * N);
     }
   for (int mb = 1; mb <= kSettleRows / 16; ++mb) {
-    f16(d->hs, d->tw, mb, kR);
     i4(d->L * 2 * d->kd, d->hs, mb, kR);
-    for (int N : {d->hs, d->P, d->rank}) f16(N, d->hs, mb, kR);
-    f16(d->hs, d->tw, mb, kR);
     for (int N : {d->qd, d->kd, d->ffn}) i4(N, d->hs, mb, kR);
     i4(d->hs, d->qd, mb, kR);
     i4(d->hs, d->ffn, mb, kR);
@@ -1765,8 +1758,7 @@ int dflash_debug_matvec(dflash_t* d, int32_t layer, int32_t which, const float* 
   const Split s = is_i4 && mb == 1 ? Split{dfl::i4_block_splits(cols, 2), 2}
                   : mb == 1        ? Split{dfl::f16_block_splits(cols), 0}
                   : is_i4          ? split_for(map.ntiles, kR, cols / 128, mb, 4)
-                  : mb > 1         ? split_big(map.ntiles, cols / 32)
-                                   : split_for(map.ntiles, kR, cols / 32, mb, 16);
+                                   : split_big(map.ntiles, cols / 32);
   const long ss = (long)mb * 16 * rows;
   if ((long)s.S * ss > d->part_floats) return fail(d, DFLASH_EINVAL, "matvec: partials too large");
   if (is_i4 && mb == 1)

@@ -43,28 +43,27 @@ struct TileMap {
 };
 
 // GEMM launches: out[split][mb·16 + m][col] partial sums (f32), col < N.
-// Two row tiles a wave; a workgroup covers 8 tiles.
-void gemm_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks, const uint16_t* w,
-              TileMap map, int N, int splits, int steps_per_split, float* out, long split_stride);
+// gemm_i4: the int4 GEMM of 17–32 rows (and the debug product's): two row
+// tiles a wave, a workgroup covers 8 tiles.
 void gemm_i4(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks,
              const uint8_t* codes, const uint16_t* scales, TileMap map, int N, int splits,
              int spans_per_split, float* out, long split_stride);
 // Many-row f16 GEMM (mblocks ≤ 16 row blocks at once, 16 weight tiles per
 // block, async copies into a 3-stage LDS ring), two planes (plane 1 at
-// xa + ps, ps a multiple of 8); out as gemm_f16.
+// xa + ps, ps a multiple of 8); out as gemm_i4.
 void gemm_big_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks,
                   const uint16_t* w, TileMap map, int N, int splits, int steps_per_split,
                   float* out, long split_stride);
 // The block pass's 16-row int4 GEMM (two planes, ps ≠ 0; skinny.hip):
 // splits of `ks` spans (128 columns) each, i4_block_splits(K, ks) of them;
-// out as gemm_i4. R row tiles a wave, four waves a workgroup; (R, ks) one of
-// (1, 4), (2, 2), (2, 4), (2, 8), (4, 4).
+// out as gemm_i4. R row tiles a wave, four waves a workgroup; (R, ks) is
+// (2, 2) or (2, 8).
 int i4_block_splits(int K, int ks);
 void gemm_i4_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint8_t* codes,
                    const uint16_t* scales, TileMap map, int N, int R, int ks, float* out,
                    long split_stride);
 // The block pass's 16-row f16 GEMM (two planes, ps ≠ 0): f16_block_splits(K)
-// splits of 512 columns; out as gemm_f16.
+// splits of 512 columns; out as gemm_i4.
 int f16_block_splits(int K);
 void gemm_f16_block(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t* w,
                     TileMap map, int N, float* out, long split_stride);

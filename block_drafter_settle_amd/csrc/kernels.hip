@@ -24,70 +24,6 @@ namespace dfl {
 
 // ------------------------------------------------------------------ GEMMs
 
-// Skinny GEMM, f16 weights (read non-temporal: once a pass): each wave owns R
-// row tiles over its K split; PL activation planes, plane 1 at xa + ps.
-template <int R, int PL>
-__global__ __launch_bounds__(kThreads) void k_gemm_f16(const f16* __restrict__ xa, long ps, int K,
-                                                       const f16* __restrict__ w, TileMap mp,
-                                                       int N, int sps, float* __restrict__ out,
-                                                       long split_stride) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int KS = K >> 5;
-  const int sp = blockIdx.y, mb = blockIdx.z;
-  const int s0 = sp * sps, s1 = min(KS, s0 + sps);
-  const int t0 = (blockIdx.x * 4 + wave) * R;
-  if (t0 >= mp.ntiles) return;
-  const h8* xp = reinterpret_cast<const h8*>(xa + (size_t)mb * 16 * K) + lane;
-  const h8* xq = reinterpret_cast<const h8*>(xa + ps * (PL - 1) + (size_t)mb * 16 * K) + lane;
-  const h8* wp[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int t = min(t0 + r, mp.ntiles - 1);
-    wp[r] = reinterpret_cast<const h8*>(w) + (size_t)map_tile(mp, t) * KS * 64 + lane;
-  }
-  f4 acc[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = (f4){0.f, 0.f, 0.f, 0.f};
-  int s = s0;
-  for (; s + 4 <= s1; s += 4) {
-    h8 a[4], a2[4], b[4][R];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a[u] = xp[(size_t)(s + u) * 64];
-      if (PL == 2) a2[u] = xq[(size_t)(s + u) * 64];
-#pragma unroll
-      for (int r = 0; r < R; ++r) b[u][r] = ld_stream(&wp[r][(size_t)(s + u) * 64]);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        acc[r] = mfma16(a[u], b[u][r], acc[r]);
-        if (PL == 2) acc[r] = mfma16(a2[u], b[u][r], acc[r]);
-      }
-  }
-  for (; s < s1; ++s) {
-    const h8 a = xp[(size_t)s * 64];
-    h8 a2;
-    if (PL == 2) a2 = xq[(size_t)s * 64];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const h8 b = ld_stream(&wp[r][(size_t)s * 64]);
-      acc[r] = mfma16(a, b, acc[r]);
-      if (PL == 2) acc[r] = mfma16(a2, b, acc[r]);
-    }
-  }
-  float* o = out + (size_t)sp * split_stride + (size_t)mb * 16 * N;
-  const int j = lane >> 4, n = lane & 15;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int t = t0 + r, col = t * 16 + n;
-    if (t < mp.ntiles && col < N)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) o[(size_t)(4 * j + v) * N + col] = acc[r][v];
-  }
-}
-
 // Many-row GEMM, f16 weights, two activation planes (the settle's fc at up
 // to 256 rows, and the f16 matrices of the debug product above 16 rows). A
 // block holds all 16 row blocks (256 rows; rows past the input are never
@@ -1345,26 +1281,6 @@ __global__ __launch_bounds__(kThreads) void k_probe_mfma(int steps, float* __res
 }
 
 static inline unsigned cdiv(long a, long b) { return (unsigned)((a + b - 1) / b); }
-
-template <int R, int PL>
-static void launch_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks,
-                       const uint16_t* w, TileMap map, int N, int splits, int sps, float* out,
-                       long ss) {
-  dim3 grid(cdiv(map.ntiles, 4 * R), splits, mblocks);
-  k_gemm_f16<R, PL><<<grid, kThreads, 0, st>>>(reinterpret_cast<const f16*>(xa), ps, K,
-                                               reinterpret_cast<const f16*>(w), map, N, sps, out,
-                                               ss);
-}
-
-// The skinny f16 and int4 GEMMs (the 8-row settle, the debug matvec) run two
-// row tiles a wave.
-void gemm_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks, const uint16_t* w,
-              TileMap map, int N, int splits, int sps, float* out, long ss) {
-  if (ps)
-    launch_f16<2, 2>(st, xa, ps, K, mblocks, w, map, N, splits, sps, out, ss);
-  else
-    launch_f16<2, 1>(st, xa, 0, K, mblocks, w, map, N, splits, sps, out, ss);
-}
 
 void gemm_big_f16(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks,
                   const uint16_t* w, TileMap map, int N, int splits, int sps, float* out,
