@@ -29,6 +29,8 @@ namespace dfl {
 static constexpr int kKvNT = 16, kKvStages = 3, kKvWaves = 8;
 static constexpr int kKvA = 32 / kKvWaves;  // row fragments a wave copies a step
 static constexpr int kKvC = 3;              // copies a wave issues a span for its codes and scales
+static constexpr size_t kKvLds =
+    16 * (kKvStages * 2 * 16 * 64 + 2 * kKvNT * 64) + 4 * 2 * kKvNT * 32;  // 132 KB
 
 __global__ __launch_bounds__(64 * kKvWaves) void k_gemm_kv_i4(const f16* __restrict__ xa, long ps,
                                                              int K, int mblocks,
@@ -39,9 +41,17 @@ __global__ __launch_bounds__(64 * kKvWaves) void k_gemm_kv_i4(const f16* __restr
                                                              long split_stride) {
   constexpr int D = kKvStages - 1;
   static_assert(D == 2, "the waits below count two steps of row copies in flight");
-  __shared__ h8 ast[kKvStages][2][16][64];  // row fragments of a step: plane, row block, lane
-  __shared__ uint4 cst[2][kKvNT][64];       // codes of a span: tile, lane
-  __shared__ uint32_t sst[2][kKvNT][32];    // scales of a span: tile, (n, pair)
+  // one dynamic LDS block (kKvLds bytes): row-fragment ring ast[stage][plane]
+  // [row block][lane], codes cst[buffer][tile][lane], scales sst[buffer]
+  // [tile][(n, pair)]. The waits below order the async copies and the LDS
+  // reads. (Into static __shared__ arrays the compiler also waited for every
+  // copy in flight before each LDS read, draining the ring every step: the
+  // K/V stage of a 256-row settle took 83 against 71 us.)
+  extern __shared__ uint4 kv_lds[];
+  auto ast = reinterpret_cast<h8(*)[2][16][64]>(kv_lds);
+  auto cst = reinterpret_cast<uint4(*)[kKvNT][64]>(kv_lds + kKvStages * 2 * 16 * 64);
+  auto sst = reinterpret_cast<uint32_t(*)[kKvNT][32]>(kv_lds + kKvStages * 2 * 16 * 64 +
+                                                      2 * kKvNT * 64);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rw = wave & 1, cw = wave >> 1;
@@ -130,6 +140,7 @@ __global__ __launch_bounds__(64 * kKvWaves) void k_gemm_kv_i4(const f16* __restr
       }
     }
   }
+  wait_vm<0>();  // the copies issued past the split's end land before the workgroup leaves
   const int j = lane >> 4;
   float* o = out + (size_t)sp * split_stride;
 #pragma unroll
@@ -154,7 +165,11 @@ void gemm_kv_i4(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks,
                 const uint8_t* codes, const uint16_t* scales, TileMap map, int N, int splits,
                 int sps, float* out, long ss) {
   const unsigned blocks = cdiv(map.ntiles, kKvNT) * splits;
-  k_gemm_kv_i4<<<blocks, 64 * kKvWaves, 0, st>>>(
+  static const hipError_t lds_ok = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_gemm_kv_i4), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)kKvLds);
+  (void)lds_ok;
+  k_gemm_kv_i4<<<blocks, 64 * kKvWaves, kKvLds, st>>>(
       reinterpret_cast<const f16*>(xa), ps, K, mblocks, reinterpret_cast<const uint4*>(codes),
       reinterpret_cast<const uint32_t*>(scales), map, N, splits, sps, out, ss);
 }
