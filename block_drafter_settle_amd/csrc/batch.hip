@@ -35,6 +35,15 @@ static constexpr int kMbWaves = 8, kMbNT = 16, kMbStages = 3, kMbAhead = kMbStag
 // still reads).
 // (The bodies are device templates behind one plain kernel per MB: a
 // kernel template whose body holds these copy builtins gets no host stub.)
+static constexpr int kMbI4Stages = 5;  // row-fragment ring stages of mb_i4
+
+// LDS of mb_i4<MB>: the ring's stages of both planes' MB row fragments, two
+// spans of 16 tiles' codes and their scales
+static constexpr size_t mb_i4_lds(int MB) {
+  return sizeof(h8) * (kMbI4Stages * 2 * MB * 64 + 2 * kMbNT * 64) +
+         sizeof(uint32_t) * 2 * kMbNT * 32;
+}
+
 template <int MB>
 __device__ __forceinline__ void mb_i4(const f16* __restrict__ xa, long ps, int K,
                                       const uint4* __restrict__ codes,
@@ -44,11 +53,17 @@ __device__ __forceinline__ void mb_i4(const f16* __restrict__ xa, long ps, int K
   constexpr int CA = 2 * MB / kMbWaves;  // row-fragment copies a wave a step
   constexpr int CC = 3;                  // code and scale copies a wave a span
   static_assert(CA >= 1 && 2 * MB % kMbWaves == 0, "every wave copies as many row fragments");
-  constexpr int ST = 5, AH = ST - 1;  // row-fragment ring stages, steps ahead
+  constexpr int ST = kMbI4Stages, AH = ST - 1;  // row-fragment ring stages, steps ahead
   static_assert(AH == 4, "the waits below count four steps of row fragments in flight");
-  __shared__ h8 ast[ST][2][MB][64];
-  __shared__ uint4 cst[2][kMbNT][64];
-  __shared__ uint32_t sst[2][kMbNT][32];
+  // one dynamic LDS block (mb_i4_lds(MB) bytes): the row-fragment ring
+  // ast[stage][plane][row block][lane], codes cst[buffer][tile][lane] and
+  // scales sst[buffer][tile][(n, pair)]. The waits below order the async
+  // copies and the LDS reads (into static __shared__ arrays the compiler also
+  // waited for every copy in flight before each LDS read, draining the ring).
+  extern __shared__ h8 stage[];
+  auto ast = reinterpret_cast<h8(*)[2][MB][64]>(stage);
+  auto cst = reinterpret_cast<uint4(*)[kMbNT][64]>(stage + ST * 2 * MB * 64);
+  auto sst = reinterpret_cast<uint32_t(*)[kMbNT][32]>(stage + ST * 2 * MB * 64 + 2 * kMbNT * 64);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int KT = K >> 7;
@@ -277,19 +292,28 @@ static inline unsigned cdiv(long a, long b) { return (unsigned)((a + b - 1) / b)
 
 int mb_groups(int ntiles) { return (int)cdiv(ntiles, kMbNT); }
 
+
 void gemm_mb_i4(hipStream_t st, const uint16_t* xa, long ps, int K, int MB, int mblocks,
                 const uint8_t* codes, const uint16_t* scales, TileMap map, int N, int splits,
                 int sps, float* out, long ss) {
+  static const bool attr = [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mb_i4_8),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)mb_i4_lds(8));
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mb_i4_4),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)mb_i4_lds(4));
+    return true;
+  }();
+  (void)attr;
   const unsigned blocks = cdiv(map.ntiles, kMbNT) * splits;
   const f16* x = reinterpret_cast<const f16*>(xa);
   const uint4* c = reinterpret_cast<const uint4*>(codes);
   const uint32_t* s = reinterpret_cast<const uint32_t*>(scales);
   if (MB == 8)
-    k_mb_i4_8<<<blocks, 64 * kMbWaves, 0, st>>>(x, ps, K, c, s, map, N, mblocks, splits, sps, out,
-                                                ss);
+    k_mb_i4_8<<<blocks, 64 * kMbWaves, mb_i4_lds(8), st>>>(x, ps, K, c, s, map, N, mblocks, splits,
+                                                          sps, out, ss);
   else
-    k_mb_i4_4<<<blocks, 64 * kMbWaves, 0, st>>>(x, ps, K, c, s, map, N, mblocks, splits, sps, out,
-                                                ss);
+    k_mb_i4_4<<<blocks, 64 * kMbWaves, mb_i4_lds(4), st>>>(x, ps, K, c, s, map, N, mblocks, splits,
+                                                          sps, out, ss);
 }
 
 static constexpr size_t mb_f16_lds(int MB) { return sizeof(h8) * kMbStages * (2 * MB + kMbNT) * 64; }
