@@ -1307,12 +1307,10 @@ static void launch_i4(hipStream_t st, const uint16_t* xa, long ps, int K, int mb
                                               out, ss);
 }
 
+// every caller passes two planes (ps ≠ 0)
 void gemm_i4(hipStream_t st, const uint16_t* xa, long ps, int K, int mblocks, const uint8_t* codes,
              const uint16_t* scales, TileMap map, int N, int splits, int pps, float* out, long ss) {
-  if (ps)
-    launch_i4<2, 2>(st, xa, ps, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
-  else
-    launch_i4<2, 1>(st, xa, 0, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
+  launch_i4<2, 2>(st, xa, ps, K, mblocks, codes, scales, map, N, splits, pps, out, ss);
 }
 
 // Eight tiles a wave need at least this many workgroups (one a compute
@@ -1334,21 +1332,13 @@ void head_sel(hipStream_t st, const uint16_t* xa, long ps, int K, const uint16_t
   const int hg = cdiv(wtiles, 4 * R), sg = cdiv(stiles, 4 * R);
   const unsigned g = hg + sg;
   const int ng = cdiv(width, 256);
-  if (ps) {
-    if (r8)
-      k_head<2, 8><<<g, kThreads, 0, st>>>(x, ps, K, hw, wtiles, width, k, logits, sw, stiles,
-                                           rank, hp, hg, ng, sc.gmax, sc.counters);
-    else
-      k_head<2, 4><<<g, kThreads, 0, st>>>(x, ps, K, hw, wtiles, width, k, logits, sw, stiles,
-                                           rank, hp, hg, ng, sc.gmax, sc.counters);
-  } else {
-    if (r8)
-      k_head<1, 8><<<g, kThreads, 0, st>>>(x, 0, K, hw, wtiles, width, k, logits, sw, stiles,
-                                           rank, hp, hg, ng, sc.gmax, sc.counters);
-    else
-      k_head<1, 4><<<g, kThreads, 0, st>>>(x, 0, K, hw, wtiles, width, k, logits, sw, stiles,
-                                           rank, hp, hg, ng, sc.gmax, sc.counters);
-  }
+  // two planes (ps ≠ 0), as every caller passes
+  if (r8)
+    k_head<2, 8><<<g, kThreads, 0, st>>>(x, ps, K, hw, wtiles, width, k, logits, sw, stiles, rank,
+                                         hp, hg, ng, sc.gmax, sc.counters);
+  else
+    k_head<2, 4><<<g, kThreads, 0, st>>>(x, ps, K, hw, wtiles, width, k, logits, sw, stiles, rank,
+                                         hp, hg, ng, sc.gmax, sc.counters);
 }
 
 void to_a(hipStream_t st, const RowSrc& x, int m, int K, uint16_t* xa, long ps) {
