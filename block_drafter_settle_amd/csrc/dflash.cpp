@@ -81,12 +81,13 @@ Split split_big(int ntiles, int steps) {
 // K splits of a batched product (16 weight tiles a workgroup): the count
 // that finishes soonest when the workgroups run in rounds of `slots` (two a
 // compute unit at 4 row blocks, one at 8: their LDS), i.e. the least
-// rounds / S, at most 8 splits (each split writes a whole [rows][N]
-// partial; caps of 16 and 32 were not faster consistently across boxes);
-// the smaller S among near ties.
+// rounds / S, the smaller S among near ties. At most 8 splits at 4 row
+// blocks and 16 at 8 (each split writes a whole [rows][N] partial): with the
+// int4 ring no longer drained every step, 16 at 8 blocks measured 3201 ->
+// 3103 us a B = 8 pass and 16 at 4 blocks 2034 -> 2100 us for B = 4 (one box).
 Split split_mb(int ntiles, int units, int MB) {
   const long groups = dfl::mb_groups(ntiles);
-  const long slots = MB == 4 ? 512 : 256, cap = 8;
+  const long slots = MB == 4 ? 512 : 256, cap = MB == 8 ? 16 : 8;
   long S = 1;
   double best = 1e30;
   for (long c = 1; c <= std::min<long>(cap, units); ++c) {
