@@ -42,8 +42,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
   constexpr int KST = HD + 8;   // LDS row stride of K (halfs)
   constexpr int VST = 32 + 4;   // LDS row stride of V^T (halfs): 18 dwords, so 16 rows' 64-bit
                                 // reads fall on distinct banks
-  __shared__ f16 Ks[2][32 * KST];
-  __shared__ f16 Vt[2][HD * VST];
+  __shared__ f16 Ks[2][2][32 * KST];  // [buffer][plane]
+  __shared__ f16 Vt[2][2][HD * VST];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // the block's own keys first (y = 0, a short workgroup that then does not
   // trail the context chunks), then context chunk y − 1
@@ -129,22 +129,21 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
         vreg[2 * ps + h] = __builtin_nontemporal_load(reinterpret_cast<const h8*>(vbase + off));
       }
   };
-  auto stage = [&](const h8 (&kreg)[2 * NPASS], const h8 (&vreg)[2 * NPASS]) {
-    lds_barrier();
+  auto stage = [&](const h8 (&kreg)[2 * NPASS], const h8 (&vreg)[2 * NPASS], int b) {
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
       const int kk = 2 * (q + QP * ps);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<h8*>(&Ks[spl][(kk + h) * KST + dd]) = kreg[2 * ps + h];
+        *reinterpret_cast<h8*>(&Ks[b][spl][(kk + h) * KST + dd]) = kreg[2 * ps + h];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<h2*>(&Vt[spl][(dd + e) * VST + kk]) =
+        *reinterpret_cast<h2*>(&Vt[b][spl][(dd + e) * VST + kk]) =
             (h2){vreg[2 * ps][e], vreg[2 * ps + 1][e]};
     }
     lds_barrier();
   };
-  auto compute = [&](int k0) {
+  auto compute = [&](int k0, int b) {
     // scores: st[h][v] = S^T[key 16h + 4j + v][query r]
     f4 st[2];
 #pragma unroll
@@ -153,8 +152,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
 #pragma unroll
       for (int s = 0; s < HD / 32; ++s) {
         const int off = (16 * hb + (lane & 15)) * KST + 32 * s + 8 * j;
-        const h8 ka = *reinterpret_cast<const h8*>(&Ks[0][off]);
-        const h8 kl = *reinterpret_cast<const h8*>(&Ks[1][off]);
+        const h8 ka = *reinterpret_cast<const h8*>(&Ks[b][0][off]);
+        const h8 kl = *reinterpret_cast<const h8*>(&Ks[b][1][off]);
         st[hb] = mfma16(ka, qf[s], st[hb]);
         st[hb] = mfma16(ka, ql[s], st[hb]);
         st[hb] = mfma16(kl, qf[s], st[hb]);
@@ -195,10 +194,10 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
 #pragma unroll
     for (int d = 0; d < HD / 16; ++d) {
       const int off = (16 * d + (lane & 15)) * VST + 4 * j;
-      const h4 v0 = *reinterpret_cast<const h4*>(&Vt[0][off]);
-      const h4 v1 = *reinterpret_cast<const h4*>(&Vt[0][off + 16]);
-      const h4 w0 = *reinterpret_cast<const h4*>(&Vt[1][off]);
-      const h4 w1 = *reinterpret_cast<const h4*>(&Vt[1][off + 16]);
+      const h4 v0 = *reinterpret_cast<const h4*>(&Vt[b][0][off]);
+      const h4 v1 = *reinterpret_cast<const h4*>(&Vt[b][0][off + 16]);
+      const h4 w0 = *reinterpret_cast<const h4*>(&Vt[b][1][off]);
+      const h4 w1 = *reinterpret_cast<const h4*>(&Vt[b][1][off + 16]);
       const h8 va = (h8){v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       const h8 vl = (h8){w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
       f4 t = mfma16(va, pb, acc[d] * corr);
@@ -210,7 +209,11 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
   // ahead, so that NSET steps of K/V rows are in flight while one is
   // computed. Steps past the chunk's end are fetched (the clamped last row)
   // and staged but not computed. (Three sets were measured no faster.)
+  // Step s is staged into LDS buffer s mod 2 and published by one barrier;
+  // that buffer's last readers, step s − 2's computes, all finished before
+  // the barrier that published step s − 1.
   constexpr int NSET = 2;
+  static_assert(NSET == 2, "a step's LDS buffer is its set index");
   h8 kr[NSET][2 * NPASS], vr[NSET][2 * NPASS];
   if (count > 0) {
 #pragma unroll
@@ -218,9 +221,9 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
     for (int k0 = 0; k0 < count; k0 += 32 * NSET) {
 #pragma unroll
       for (int i = 0; i < NSET; ++i) {
-        stage(kr[i], vr[i]);
+        stage(kr[i], vr[i], i);  // step k0/32 + i, its parity i (k0 a multiple of 64)
         fetch(k0 + 32 * (i + NSET), kr[i], vr[i]);
-        if (k0 + 32 * i < count) compute(k0 + 32 * i);
+        if (k0 + 32 * i < count) compute(k0 + 32 * i, i);
       }
     }
   }
