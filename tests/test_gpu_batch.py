@@ -123,6 +123,48 @@ def test_batch_27b_two_sequences(orc):
         lead.close()
 
 
+def test_batch_27b_eight_sequences(orc):
+    """The 27B-shaped sidecar at eight sequences (8 row blocks, the products
+    split up to 16 ways): contexts of 40 to 320 rows at different starts;
+    three sequences against the oracle, all eight against dflash_block on the
+    same handle."""
+    g = synth.geometry("t27b")
+    dev = _dev()
+    w = synth.make_weights(g, seed=0, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    lead = pkg.Drafter(g, w, max_context=512, stream=stream)
+    ds = [lead] + [pkg.Drafter.context_of(lead, 512, stream) for _ in range(7)]
+    try:
+        m = orc.Model(g, w)
+        del w
+        spans = [(13 * i, 40 * (i + 1)) for i in range(8)]
+        taps_host, pos = [], []
+        for i, (first, n) in enumerate(spans):
+            taps = synth.make_taps(g, n, seed=80 + i, device=dev)
+            ds[i].settle(first, n, taps.data_ptr())
+            taps_host.append(taps.cpu().numpy())
+            pos.append(first + n)
+        anchors = [int(x) for x in synth.uniform_tokens(g, 8, seed=81)]
+        k, width = 15, g["vocab"]
+        got = _batch(ds, anchors, pos, k, width, g)
+        for i in range(8):
+            one = run_block(ds[i], g, anchors[i], pos[i], k, width)
+            close(got["logits"][i], one["logits"], f"t27b batch of 8, seq {i} against its own block")
+        for i in (0, 3, 7):
+            print(f"t27b batch of 8: oracle block of sequence {i}", flush=True)
+            ctx = Context(m)
+            ctx.push(spans[i][0], taps_host[i])
+            ref = ctx.block(anchors[i], pos[i], k, width)
+            close(got["logits"][i], ref["logits"], f"t27b batch of 8, seq {i} logits")
+            sel = m.select(ref["logits"], ref["hp"], anchors[i])
+            check_selection({n: got[n][i] for n in ("cand", "score", "chosen")}, ref["logits"],
+                            sel, f"t27b batch of 8, seq {i}")
+    finally:
+        for d in ds[1:]:
+            d.close()
+        lead.close()
+
+
 def test_batch_rejections():
     g = synth.small_geometry()
     w = synth.make_weights(g, seed=42)
