@@ -216,7 +216,13 @@ def same_state(d, ctx):
     assert d.span() == ctx.span()
 
 
-@pytest.mark.parametrize("n,first", [(1, 0), (40, 100), (300, 7)])
+# row counts where the kernels change: one 16-row block (the 16-row block
+# kernels), 17 and 32 rows (the many-row fc, the small-row int4 K/V), 33
+# rows (the many-row K/V), a full 256-row call, and more than one call.
+# The handle is shared: each start lies past the previous span's end or at
+# or before its first position, so every case settles a fresh context.
+@pytest.mark.parametrize("n,first", [(1, 0), (16, 3), (17, 0), (32, 50), (33, 90), (40, 200),
+                                     (256, 0), (300, 400)])
 def test_settle_parity(small, orc, n, first):
     from oracle.context import Context
 
