@@ -361,8 +361,11 @@ def main():
     del w, d
     torch.cuda.empty_cache()
     if not args.no_extra:
-        res["qwen3_4b"] = leg_4b(pkg, synth, dev, stream, args.blocks_4b)
+        res["qwen3_4b"], w4 = leg_4b(pkg, synth, dev, stream, args.blocks_4b)
         torch.cuda.empty_cache()
+        if cpu is not None:
+            cpu["qwen3_4b"] = cpu_4b(synth, w4)
+        del w4
         res["t27b_long"], long_w = leg_long(pkg, synth, dev, stream, args.steps_long)
         torch.cuda.empty_cache()
         if cpu is not None:
@@ -527,7 +530,6 @@ def leg_4b(pkg, synth, dev, stream, nblocks):
     w = synth.make_weights(g, seed=0, device=dev)
     d = pkg.Drafter(g, w, max_context=4096 + 256, stream=stream)
     d.reserve(4096 + 256)
-    del w
     log(f"4b: sidecar ready in {time.time() - t0:.1f}s")
     calls, n = 16, 4096
     taps = synth.make_taps(g, n, seed=0, name="settle_taps", outliers=True, device=dev)
@@ -565,7 +567,7 @@ def leg_4b(pkg, synth, dev, stream, nblocks):
     us = blk_s / nblocks * 1e6
     sfl = settle_flops(g, n)
     log(f"4b: settle {n / settle_s / 1e6:.3f} M rows/s; blocks {nblocks / blk_s:.1f}/s")
-    return {
+    res = {
         "workload": "4b: Qwen3-4B-shaped sidecar (hidden 2560, ffn 9728, 5 layers, 32/8 heads, "
                     "hd 128, vocab 151936, block 16, tap width 12800, windows 0); 4096 rows "
                     "settled in 16 calls of 256, then blocks at a=4096 (k=15, width=vocab)",
@@ -578,6 +580,7 @@ def leg_4b(pkg, synth, dev, stream, nblocks):
         "stages_us": {s_: round(v[0] / nb, 2) for s_, v in st.items()
                       if not s_.startswith("settle") and v[1]},
     }
+    return res, (g, w)
 
 
 def leg_long(pkg, synth, dev, stream, steps):
@@ -780,6 +783,37 @@ def cpu_baseline(g, w, synth, steps):
     except OSError as e:
         log(f"cpu baseline: one-thread run skipped ({e})")
     return res
+
+
+def cpu_4b(synth, gw, device="cuda:0"):
+    """The oracle on the 4B-shaped sidecar's unit: one 256-row settle call,
+    then 3 blocks at a = 4096 over a 4096-position synthetic context (drawn on
+    the GPU, copied to the host), all cores."""
+    import torch
+    from oracle import oracle
+
+    g, w = gw
+    m = oracle.Model(g, w)
+    taps = synth.make_taps(g, 256, seed=0, name="settle_taps", outliers=True).numpy()
+    t0 = time.perf_counter()
+    m.settle(taps, 0)
+    ts = time.perf_counter() - t0
+    ctx = 4096
+    store = [(k_.cpu().numpy(), v_.cpu().numpy())
+             for k_, v_ in synth.make_store(g, ctx, seed=0, device=torch.device(device))]
+    anchors = synth.uniform_tokens(g, 3, seed=0)
+    t0 = time.perf_counter()
+    for anchor in anchors:
+        r = m.block(store, 0, ctx, anchor, ctx, g["block"] - 1, g["vocab"])
+        m.select(r["logits"], r["hp"], anchor)
+    tb = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count()))
+    log(f"cpu baseline: 4b settle call in {ts:.2f}s, 3 blocks in {tb:.1f}s")
+    return {"value": round(3 / tb, 4), "unit": "blocks/s", "cores": cores,
+            "sample": "3 blocks of the 4b workload at a=4096 (4096-position synthetic context, "
+                      "k=15, width=vocab) + selection",
+            "settle": {"value": round(256 / ts, 1), "unit": "rows/s", "cores": cores,
+                       "sample": "one 256-row settle call of the 4b workload"}}
 
 
 def cpu_long_block(synth, gw):
