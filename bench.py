@@ -357,6 +357,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(g, w, synth, args.cpu_steps)
+        cpu["tiny"] = cpu_tiny(synth)
     d.close()
     del w, d
     torch.cuda.empty_cache()
@@ -783,6 +784,28 @@ def cpu_baseline(g, w, synth, steps):
     except OSError as e:
         log(f"cpu baseline: one-thread run skipped ({e})")
     return res
+
+
+def cpu_tiny(synth):
+    """The oracle on the tiny sidecar whole: 128 tap rows settled, then one
+    block at a = 128 over them (k = block - 1, width = vocab)."""
+    from oracle import oracle
+
+    g = synth.geometry("tiny")
+    w = synth.make_weights(g, seed=0)
+    m = oracle.Model(g, w)
+    n = 128
+    taps = synth.make_taps(g, n, seed=0).numpy()
+    anchor = 17
+    t0 = time.perf_counter()
+    K, V = m.settle(taps, 0)
+    r = m.block([(K[l], V[l]) for l in range(g["layers"])], 0, n, anchor, n, g["block"] - 1,
+                g["vocab"])
+    m.select(r["logits"], r["hp"], anchor)
+    t = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count()))
+    return {"value": round(1.0 / t, 2), "unit": "runs/s", "cores": cores,
+            "sample": "the tiny sidecar whole: 128 rows settled + one block + selection"}
 
 
 def cpu_4b(synth, gw, device="cuda:0"):
