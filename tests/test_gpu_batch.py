@@ -147,6 +147,9 @@ def test_batch_27b_eight_sequences(orc):
         anchors = [int(x) for x in synth.uniform_tokens(g, 8, seed=81)]
         k, width = 15, g["vocab"]
         got = _batch(ds, anchors, pos, k, width, g)
+        again = _batch(ds, anchors, pos, k, width, g)  # the same pass twice: the same bits
+        for n in got:
+            assert np.array_equal(got[n], again[n]), n
         for i in range(8):
             one = run_block(ds[i], g, anchors[i], pos[i], k, width)
             close(got["logits"][i], one["logits"], f"t27b batch of 8, seq {i} against its own block")

@@ -116,6 +116,32 @@ def test_full_settle_every_row(orc, name):
         d.close()
 
 
+def test_27b_repeat_bit_identical():
+    """The same work twice gives the same bits: a 256-row settle (the fc and
+    K/V kernels with their async-copy rings) re-settled at the same position,
+    and a block over it. A missing wait between an async copy and its reader
+    would show here as a difference between the two runs."""
+    g, w = sidecar("t27b")
+    dev = _dev()
+    d = drafter(g, w, 600)
+    try:
+        taps = synth.make_taps(g, 512, seed=5, outliers=True, device=dev)
+        anchor = synth.uniform_tokens(g, 1, seed=6)[0]
+        runs = []
+        for _ in range(2):
+            d.settle(100, 512, taps.data_ptr())  # a rewind to 100 on the second run
+            ks, vs = _store_rows(d, g, 512)
+            got = run_block(d, g, anchor, 612, 15, g["vocab"])
+            runs.append((ks, vs, got))
+        (k0, v0, b0), (k1, v1, b1) = runs
+        for l in range(g["layers"]):
+            assert np.array_equal(k0[l], k1[l]) and np.array_equal(v0[l], v1[l]), l
+        for n in ("logits", "hidden", "hp", "cand", "score", "chosen"):
+            assert np.array_equal(b0[n], b1[n]), n
+    finally:
+        d.close()
+
+
 def test_27b_stream_end_to_end(orc):
     """The 27B stream's composition: 2304 positions settled through the
     library (nine 256-row passes: longer than the 2048-position windows),
