@@ -148,15 +148,34 @@ __device__ __forceinline__ void mb_i4(const f16* __restrict__ xa, long ps, int K
         sc[t] = half_bits((u & 1) ? (sb >> 16) : sb);
       }
       const int st = s % ST;
+      if (MB == 8) {
+        // every product of the step first, then their scaling: the MFMAs
+        // run back to back instead of waiting on the FMAs that free one
+        // temporary (same operations, same order: the same bits)
+        f4 v[RB][4];
 #pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        const h8 a0 = ast[st][0][rg * RB + b][lane];
-        const h8 a1 = ast[st][1][rg * RB + b][lane];
+        for (int b = 0; b < RB; ++b) {
+          const h8 a0 = ast[st][0][rg * RB + b][lane];
+          const h8 a1 = ast[st][1][rg * RB + b][lane];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          f4 v = mfma16(a0, q[t], (f4){0.f, 0.f, 0.f, 0.f});
-          v = mfma16(a1, q[t], v);
-          acc[b][t] += sc[t] * v;
+          for (int t = 0; t < 4; ++t)
+            v[b][t] = mfma16(a1, q[t], mfma16(a0, q[t], (f4){0.f, 0.f, 0.f, 0.f}));
+        }
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[b][t] += sc[t] * v[b][t];
+      } else {
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          const h8 a0 = ast[st][0][rg * RB + b][lane];
+          const h8 a1 = ast[st][1][rg * RB + b][lane];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            f4 v = mfma16(a0, q[t], (f4){0.f, 0.f, 0.f, 0.f});
+            v = mfma16(a1, q[t], v);
+            acc[b][t] += sc[t] * v;
+          }
         }
       }
     }
