@@ -81,7 +81,7 @@ __global__ __launch_bounds__(64 * NW) void k_i4_block(const f16* __restrict__ xa
         a[q] = al[0][u * 4 + q][lane];
         b[q] = al[1][u * 4 + q][lane];
       }
-      i4_span<R, 2>(c[u], s[u], a, b, acc);
+      i4_span_deferred<R, 2>(c[u], s[u], a, b, acc);
     }
   }
   if (t0 >= mp.ntiles) return;
