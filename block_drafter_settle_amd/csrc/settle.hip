@@ -131,12 +131,15 @@ __global__ __launch_bounds__(64 * kKvWaves) void k_gemm_kv_i4(const f16* __restr
       for (int b = 0; b < 8; ++b) {
         const h8 a0 = ast[st][0][rw * 8 + b][lane];
         const h8 a1 = ast[st][1][rw * 8 + b][lane];
+        // a row block's four products first, then their scaling (same
+        // operations and order): the MFMAs do not each wait on the FMAs
+        // that free one temporary
+        f4 v[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          f4 v = mfma16(a0, q[t], (f4){0.f, 0.f, 0.f, 0.f});
-          v = mfma16(a1, q[t], v);
-          acc[b][t] += sc[t] * v;
-        }
+        for (int t = 0; t < 4; ++t)
+          v[t] = mfma16(a1, q[t], mfma16(a0, q[t], (f4){0.f, 0.f, 0.f, 0.f}));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[b][t] += sc[t] * v[t];
       }
     }
   }
