@@ -206,6 +206,29 @@ __device__ __forceinline__ void i4_span_deferred(const uint4* c, const uint2* sc
     for (int r = 0; r < R; ++r) acc[r] += s[u][r] * t[u][r];
 }
 
+// i4_span with each step's R products formed before their scalings (the
+// same operations in the same order): R temporaries instead of one.
+template <int R, int PL>
+__device__ __forceinline__ void i4_span_step(const uint4* c, const uint2* sc, const h8* a,
+                                             const h8* a2, f4* acc) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    f4 t[R];
+    float s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t word = u == 0 ? c[r].x : u == 1 ? c[r].y : u == 2 ? c[r].z : c[r].w;
+      const uint32_t sb = u < 2 ? sc[r].x : sc[r].y;
+      s[r] = half_bits((u & 1) ? (sb >> 16) : sb);
+      const h8 q = unpack_i4(word);
+      t[r] = mfma16(a[u], q, (f4){0.f, 0.f, 0.f, 0.f});
+      if (PL == 2) t[r] = mfma16(a2[u], q, t[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] += s[r] * t[r];
+  }
+}
+
 // The A fragments of span p: four steps of each plane.
 template <int PL>
 __device__ __forceinline__ void load_span(const h8* xp, const h8* xq, int p, h8* a, h8* a2) {

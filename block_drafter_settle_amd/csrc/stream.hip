@@ -97,7 +97,7 @@ __global__ __launch_bounds__(64 * kSW) void k_glu_stream(const f16* __restrict__
       f4 acc[2] = {(f4){0.f, 0.f, 0.f, 0.f}, (f4){0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int u = 0; u < KSW; ++u) {
-        i4_span<2, 2>(c[u], s[u], a0[u], a1[u], acc);
+        i4_span_step<2, 2>(c[u], s[u], a0[u], a1[u], acc);
         issue(g + 1, u);
       }
       red[g - g0][0][wave][lane] = acc[0];
