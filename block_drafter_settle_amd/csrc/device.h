@@ -160,29 +160,11 @@ __device__ __forceinline__ h8 unpack_i4(uint32_t w) {
 }
 
 // One 128-column span of R int4 tiles against four A-layout steps of PL
-// planes (a, a2).
-template <int R, int PL>
-__device__ __forceinline__ void i4_span(const uint4* c, const uint2* sc, const h8* a, const h8* a2,
-                                        f4* acc) {
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint32_t word = u == 0 ? c[r].x : u == 1 ? c[r].y : u == 2 ? c[r].z : c[r].w;
-      const uint32_t sb = u < 2 ? sc[r].x : sc[r].y;
-      const float s = half_bits((u & 1) ? (sb >> 16) : sb);
-      const h8 q = unpack_i4(word);
-      f4 t = mfma16(a[u], q, (f4){0.f, 0.f, 0.f, 0.f});
-      if (PL == 2) t = mfma16(a2[u], q, t);
-      acc[r] += s * t;
-    }
-  }
-}
-
-// i4_span with every product of the span formed first and the group
-// scalings applied after, in the same order (the same bits): the MFMAs run
-// back to back instead of each waiting on the FMAs that free a temporary.
-// Costs 16·R more VGPRs.
+// planes (a, a2): per step and tile t = a·q (+ a2·q) on MFMA with the codes q
+// as exact f16 integers, then acc += s·t with the group's scale s. Every
+// product of the span is formed first and the scalings applied after, in the
+// same order: the MFMAs run back to back instead of each waiting on the FMAs
+// that free a temporary. Costs 16·R more VGPRs than i4_span_step.
 template <int R, int PL>
 __device__ __forceinline__ void i4_span_deferred(const uint4* c, const uint2* sc, const h8* a,
                                                  const h8* a2, f4* acc) {
@@ -206,8 +188,8 @@ __device__ __forceinline__ void i4_span_deferred(const uint4* c, const uint2* sc
     for (int r = 0; r < R; ++r) acc[r] += s[u][r] * t[u][r];
 }
 
-// i4_span with each step's R products formed before their scalings (the
-// same operations in the same order): R temporaries instead of one.
+// As i4_span_deferred, each step's R products formed before their scalings
+// (R temporaries).
 template <int R, int PL>
 __device__ __forceinline__ void i4_span_step(const uint4* c, const uint2* sc, const h8* a,
                                              const h8* a2, f4* acc) {

@@ -163,8 +163,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa
     }
     load_span<PL>(xp, xq, p, a0, b0);
     load_span<PL>(xp, xq, p + 1, a1, b1);
-    i4_span<R, PL>(c0, s0, a0, b0, acc);
-    i4_span<R, PL>(c1, s1, a1, b1, acc);
+    i4_span_step<R, PL>(c0, s0, a0, b0, acc);
+    i4_span_step<R, PL>(c1, s1, a1, b1, acc);
   }
   if (p < p1) {
     uint4 c0[R];
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i4(const f16* __restrict__ xa
       s0[r] = ld_stream(&scp[r][(size_t)p * 16]);
     }
     load_span<PL>(xp, xq, p, a0, b0);
-    i4_span<R, PL>(c0, s0, a0, b0, acc);
+    i4_span_step<R, PL>(c0, s0, a0, b0, acc);
   }
   float* o = out + (size_t)sp * split_stride + (size_t)mb * 16 * N;
   const int j = lane >> 4, n = lane & 15;
