@@ -240,8 +240,8 @@ __global__ __launch_bounds__(kThreads) void k_attn(const f16* __restrict__ qa, l
 // Softmax-merge of the chunks of one (q head, row) → y in A-layout f16:
 // y = Σ_c acc_c·2^{m_c − M} / Σ_c l_c·2^{m_c − M}, M the largest chunk max
 // (the chunk states are kept in base 2).
-// The threads form the chunk weights (chunks strided over the block), then
-// 256 / hd groups of hd threads each sum a strided share of the chunks.
+// Thread t forms chunk t's weight, then 256 / hd groups of hd threads each
+// sum a strided share of the chunks.
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pacc,
                                                     const float2* __restrict__ pml, int nh,
                                                     int kv, int hd, SeqChunks sc,
@@ -256,9 +256,18 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   const int lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
   const int rep = nh / kv, g = hq / rep, qi = hq % rep, nc = nchunks + 1;
   const size_t slot0 = (size_t)g * nc * rep + qi;  // chunk c is slot slot0 + c·rep
-  auto ml_of = [&](int c) { return pml[(slot0 + (size_t)c * rep) * 16 + r]; };
-  float m = -INFINITY;
-  for (int c = t; c < nc; c += blockDim.x) m = fmaxf(m, ml_of(c).x);
+  // one chunk a thread (nc ≤ kAttnMaxChunks + 1 ≤ 256): its (m, l) is loaded
+  // once, together with the first eight partial outputs this thread sums
+  // below, so those loads overlap the two reductions
+  static_assert(kAttnMaxChunks + 1 <= 256, "one chunk a thread");
+  const float2 mlt = t < nc ? pml[(slot0 + (size_t)t * rep) * 16 + r] : make_float2(-INFINITY, 0.f);
+  const int G = blockDim.x / hd, grp = t / hd, d = t - grp * hd;
+  const float* pc = pacc + (slot0 * 16 + r) * hd + d;
+  const size_t cs = (size_t)rep * 16 * hd;  // chunk stride
+  float pre[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) pre[k] = grp + k * G < nc ? pc[(size_t)(grp + k * G) * cs] : 0.f;
+  float m = mlt.x;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   if (lane == 0) red[wave] = m;
@@ -266,11 +275,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   float M = red[0];
   for (int w = 1; w < nw; ++w) M = fmaxf(M, red[w]);
   float l = 0.f;
-  for (int c = t; c < nc; c += blockDim.x) {
-    const float2 ml = ml_of(c);
-    const float f = ml.x != -INFINITY ? exp2f(ml.x - M) : 0.f;
-    fw[c] = f;
-    l += ml.y * f;
+  if (t < nc) {
+    const float f = mlt.x != -INFINITY ? exp2f(mlt.x - M) : 0.f;
+    fw[t] = f;
+    l = mlt.y * f;
   }
   l = wave_sum(l);
   if (lane == 0) redl[wave] = l;
@@ -279,15 +287,21 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   for (int w = 0; w < nw; ++w) L += redl[w];
   // thread (grp, d): dimension d of chunks grp, grp + G, … (G = blockDim / hd
   // groups), eight loads in flight; the groups' sums meet in LDS in order
-  const int G = blockDim.x / hd, grp = t / hd, d = t - grp * hd;
-  const float* pc = pacc + (slot0 * 16 + r) * hd + d;
-  const size_t cs = (size_t)rep * 16 * hd;  // chunk stride
   float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   int c = grp;
-  for (; c + 7 * G < nc; c += 8 * G)
+  if (c + 7 * G < nc) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) y[k] += pc[(size_t)(c + k * G) * cs] * fw[c + k * G];
-  for (int k = 0; c < nc; c += G, ++k) y[k & 7] += pc[(size_t)c * cs] * fw[c];
+    for (int k = 0; k < 8; ++k) y[k] += pre[k] * fw[c + k * G];
+    c += 8 * G;
+    for (; c + 7 * G < nc; c += 8 * G)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[k] += pc[(size_t)(c + k * G) * cs] * fw[c + k * G];
+    for (int k = 0; c < nc; c += G, ++k) y[k & 7] += pc[(size_t)c * cs] * fw[c];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (c + k * G < nc) y[k] += pre[k] * fw[c + k * G];
+  }
   const float ys = ((y[0] + y[1]) + (y[2] + y[3])) + ((y[4] + y[5]) + (y[6] + y[7]));
   __shared__ float part[256];
   part[t] = ys;
